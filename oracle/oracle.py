@@ -1,0 +1,69 @@
+"""Python access to the CPU oracle.  TEST INFRASTRUCTURE ONLY.
+
+``topk_ragged_oracle`` runs the C++ oracle (``oracle_topk.cpp``: per-row
+nth_element under the order "larger value first, then lower index", chosen
+indices sorted ascending, -1 padding).
+
+Source of the op: vLLM persistent_topk pages -- PR #54110 ("low shared
+memory fallback"), its code excerpt: the per-row decode top-K takes the
+logits, next_n, the lengths, the output and both logits strides, and next_n
+is the second dimension of a 2-D lengths tensor, else 1; PR #41189 (deadlock
+fix), its code excerpt: fp32 logits in, int32 indices out.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle_topk.so")
+_lib = None
+
+
+def load_library():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build_oracle
+            build_oracle.build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.oracle_topk_ragged.argtypes = [
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32]
+        lib.oracle_topk_ragged.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _next_n_of(lengths: np.ndarray) -> int:
+    # PR #54110 excerpt: a 2-D lengths tensor [batch, next_n] is the
+    # multi-token layout, a 1-D one is plain decode (next_n = 1).
+    return int(lengths.shape[1]) if lengths.ndim == 2 else 1
+
+
+def topk_ragged_oracle(scores: np.ndarray, lengths: np.ndarray, K: int,
+                       next_n: int | None = None, threads: int = 0) -> np.ndarray:
+    """int32 [num_rows, K]: per row, the indices of the K best of the first
+    lengths[r] scores ("best": larger value, then lower index), ascending,
+    padded with -1.  Raises on a NaN inside a valid prefix (out of contract).
+    """
+    scores = np.ascontiguousarray(scores, dtype=np.float32)
+    assert scores.ndim == 2
+    lengths = np.asarray(lengths)
+    if next_n is None:
+        next_n = _next_n_of(lengths)
+    flat = np.ascontiguousarray(lengths.reshape(-1), dtype=np.int32)
+    num_rows, stride = scores.shape
+    assert flat.shape[0] == num_rows, "one length per row"
+    out = np.empty((num_rows, K), dtype=np.int32)
+    lib = load_library()
+    rc = lib.oracle_topk_ragged(scores.ctypes.data, stride, flat.ctypes.data, num_rows,
+                                next_n, K, out.ctypes.data, int(threads))
+    if rc == -2:
+        raise ValueError("NaN inside a valid prefix: outside the op's contract")
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (rc={rc})")
+    return out
