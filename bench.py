@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Benchmark: ragged per-row top-2048 on one MI355X.
+
+One step = one topk_ragged launch over the whole prefill-shaped batch (4096
+rows, row_stride 65536, lengths 61440+i, K=2048, N(0,1) plus a per-row offset
+U(-4,4)), inputs already resident in HBM.  Prints one JSON line:
+rows/s as `value`, effective HBM GB/s (valid fp32 score bytes / time) and its
+fraction of the 8 TB/s peak, the roofline of the kernel, the CPU oracle timed
+on a bounded sample of the same rows, and per-launch figures for the other
+workloads (timed over rotating input copies so the 256 MB last-level cache
+cannot serve them).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "rows/sec + effective HBM GB/s (fraction of peak) for ragged per-row top-2048"
+KERNEL_SRC = os.path.join(ROOT, "row_radix_top_amd", "csrc", "topk_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_hbm_traffic.json")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+
+
+def algorithmic_bytes(lengths: np.ndarray, row_stride: int, K: int) -> tuple[int, int]:
+    """(valid score bytes, algorithmic bytes): every valid fp32 score read
+    once, plus K int32 indices written and one int32 length read per row."""
+    n = np.clip(lengths.reshape(-1).astype(np.int64), 0, row_stride)
+    valid = int(4 * n.sum())
+    rows = n.size
+    return valid, valid + rows * (4 * K + 4)
+
+
+def time_launches(fn, n: int):
+    """Average ms per launch over n back-to-back launches (HIP events on the
+    launch stream, which is torch's current stream)."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(n):
+        fn(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / n
+
+
+def measured_traffic(per_launch_alg: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float):
+    """Time the CPU oracle (as is) on the first rows of the same workload."""
+    from oracle import topk_ragged_oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    probe = min(64, w.num_rows)
+    topk_ragged_oracle(w.scores[:8], w.flat_lengths[:8], w.K, threads=threads)  # warm
+    t0 = time.perf_counter()
+    topk_ragged_oracle(w.scores[:probe], w.flat_lengths[:probe], w.K, threads=threads)
+    t_probe = time.perf_counter() - t0
+    rows = int(min(w.num_rows, max(probe, probe * budget_s / max(t_probe, 1e-6))))
+    t0 = time.perf_counter()
+    topk_ragged_oracle(w.scores[:rows], w.flat_lengths[:rows], w.K, threads=threads)
+    t = time.perf_counter() - t0
+    valid, _ = algorithmic_bytes(w.flat_lengths[:rows], w.row_stride, w.K)
+    return {
+        "value": rows / t,
+        "unit": "rows/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"first {rows} of {w.num_rows} rows of the same workload, {t:.2f} s, "
+                  f"{valid / t / 1e9:.2f} effective GB/s",
+    }
+
+
+def bench_other(name: str, copies_bytes: int = 1 << 30, launches: int = 200):
+    """Per-launch time of another workload over rotating input copies."""
+    import torch
+    import row_radix_top_amd as rrt
+    from row_radix_top_amd import workloads
+    w = workloads.make_workload(name)
+    dev = torch.device("cuda:0")
+    one = torch.from_numpy(w.scores).to(dev)
+    ncopy = max(1, min(1024, copies_bytes // max(1, one.numel() * 4)))
+    pool = torch.empty((ncopy,) + tuple(one.shape), dtype=torch.float32, device=dev)
+    pool.copy_(one.unsqueeze(0).expand_as(pool))
+    L = torch.from_numpy(w.flat_lengths).to(dev)
+    out = torch.empty((w.num_rows, w.K), dtype=torch.int32, device=dev)
+    ws = rrt.new_workspace(rrt.workspace_size(w.num_rows, w.row_stride, w.K, device=dev), dev)
+    plan = rrt.query_plan(pool[0], w.K)
+
+    def launch(i):
+        rrt.topk_ragged(pool[i % ncopy], L, w.K, out=out, workspace=ws, next_n=w.next_n)
+
+    for i in range(min(20, ncopy)):
+        launch(i)
+    ms = time_launches(launch, launches)
+    valid, _ = algorithmic_bytes(w.flat_lengths, w.row_stride, w.K)
+    res = {
+        "us_per_launch": round(ms * 1e3, 3),
+        "rows_per_s": w.num_rows / (ms * 1e-3),
+        "effective_GBps": round(valid / (ms * 1e-3) / 1e9, 1),
+        "frac_of_hbm_peak": round(valid / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "rotating_copies": ncopy,
+        "path": plan["path"], "grid": plan["grid"], "wg_per_row": plan["wg_per_row"],
+    }
+    del pool, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true", help="skip the other workloads")
+    ap.add_argument("--check", action="store_true", help="compare sampled rows with the oracle")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); rows are independent, "
+              "so more GPUs would each run this same kernel on their own block of rows.", file=sys.stderr)
+        return 2
+
+    import torch
+    import row_radix_top_amd as rrt
+    from row_radix_top_amd import binding, workloads
+
+    binding.load()  # fail loudly if the HIP library is missing
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+
+    log(f"generating workload {args.workload}")
+    w = workloads.make_workload(args.workload)
+    scores = torch.from_numpy(w.scores).to(dev)
+    lengths = torch.from_numpy(w.flat_lengths).to(dev)
+    out = torch.empty((w.num_rows, w.K), dtype=torch.int32, device=dev)
+    nbytes = rrt.workspace_size(w.num_rows, w.row_stride, w.K, device=dev)
+    ws = rrt.new_workspace(nbytes, dev)
+    plan = rrt.query_plan(scores, w.K)
+    log(f"plan {plan}")
+
+    def step(_i=0):
+        rrt.topk_ragged(scores, lengths, w.K, out=out, workspace=ws, next_n=w.next_n)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms_ev = time_launches(step, args.steps)
+    wall = time.perf_counter() - t0
+    log(f"{args.steps} steps: {ms_ev:.4f} ms/step (events), wall {wall:.3f} s")
+
+    if args.check:
+        from oracle import topk_ragged_oracle
+        rows = np.linspace(0, w.num_rows - 1, 64).astype(int)
+        exp = topk_ragged_oracle(w.scores[rows], w.flat_lengths[rows], w.K)
+        got = out.cpu().numpy()[rows]
+        assert np.array_equal(got, exp), "bench output differs from the oracle"
+        log("sampled rows match the oracle")
+
+    valid, alg = algorithmic_bytes(w.flat_lengths, w.row_stride, w.K)
+    sec = ms_ev * 1e-3
+    rows_per_s = w.num_rows / sec
+    eff = valid / sec / 1e9
+    achieved = alg / sec / 1e9
+    traffic = measured_traffic(alg)
+    result = {
+        "metric": METRIC,
+        "value": rows_per_s,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_ev,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.description,
+            "num_rows": w.num_rows, "row_stride": w.row_stride, "K": w.K, "next_n": w.next_n,
+            "parallelism": "single GPU",
+        },
+        "effective_GBps": round(eff, 1),
+        "frac_of_hbm_peak": round(eff / HBM_PEAK_GBPS, 4),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": f"topk_single_kernel<{plan['kmax']},{plan['vec']}>" if plan["path"] == 1
+                      else f"topk_multi_kernel<{plan['kmax']},{plan['vec']}>",
+            "algorithmic_bytes_per_launch": alg,
+        },
+        "plan": {k: plan[k] for k in ("path", "grid", "wg_per_row", "kmax", "vec", "resident_cap")},
+    }
+
+    if not args.no_others:
+        others = {}
+        for name in ("small", "decode", "mtp", "long_k1024", "long_k2048"):
+            log(f"timing {name}")
+            others[name] = bench_other(name)
+        result["workloads"] = others
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,190 @@
+/*
+ * topk_ragged.h -- ragged per-row top-K on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (vLLM persistent_topk pages: PR #54110 "low shared memory
+ * fallback", its csrc/libtorch_stable/topk.cu excerpt, which passes logits,
+ * next_n, lengths, the output and both logits strides to the per-row decode
+ * top-K; PR #41189 "cooperative barrier deadlock fix", its csrc/topk.cu
+ * excerpt, which hands fp32 logits to the top-K and gets int32 indices back):
+ *
+ *   for every row r of an fp32 score matrix, return the int32 column indices
+ *   of the K largest scores among the first lengths[r] entries.
+ *
+ * The pages leave three things open; this library fixes them so that exactly
+ * one output is correct:
+ *   - ties: of two equal scores the lower index wins (IEEE equality, so -0.0
+ *     and +0.0 are equal);
+ *   - order: the chosen indices are written in ascending index order;
+ *   - short rows: when lengths[r] < K the row is padded with -1.
+ *
+ * All pointers given to topk_ragged are DEVICE pointers owned by the caller.
+ * The library never allocates device memory, never synchronises and never
+ * issues a host memset on the launch path, so a launch can be captured in a
+ * hipGraph and replayed.  Every call is asynchronous on `stream`; the device
+ * is the stream's device.  Device properties and kernel occupancies are
+ * queried once per device and cached.
+ *
+ * Return values are topk_status codes.  On failure a description is
+ * available from topk_ragged_last_error() (thread-local).  A kernel that
+ * faults reports at the caller's next synchronisation, like any HIP op.
+ */
+#ifndef TOPK_RAGGED_H
+#define TOPK_RAGGED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TOPK_OK = 0,
+  TOPK_EINVAL = -1,          /* bad pointer, size, stride, next_n or alignment */
+  TOPK_EUNSUPPORTED_K = -2,  /* K outside [1, TOPK_RAGGED_MAX_K] */
+  TOPK_EWORKSPACE = -3,      /* the plan needs a workspace and none was given */
+  TOPK_EDEVICE = -4,         /* a HIP runtime query failed */
+  TOPK_ELAUNCH = -5          /* the kernel launch reported an error */
+} topk_status;
+
+#define TOPK_RAGGED_MAX_K 2048
+/* Rows whose stride exceeds this may be split over several workgroups that
+ * cooperate through the workspace (the pages' RADIX_THRESHOLD of 32K with a
+ * strict comparison: PR #41189 page, csrc/topk.cu excerpt and review notes). */
+#define TOPK_RAGGED_RADIX_THRESHOLD 32768
+
+/*
+ * topk_ragged -- the hot path.
+ *
+ *   scores     fp32, row r starts at scores + r * row_stride (elements), column
+ *              stride 1.  Only entries [0, lengths[r]) of row r are read.
+ *   row_stride elements between row starts, >= 1.
+ *   lengths    int32, num_rows entries, one per row.  Multi-token layouts
+ *              ([batch, next_n] row-major, PR #54110 page, topk.cu excerpt)
+ *              are passed flattened: row b*next_n + j belongs to batch b.
+ *              A length outside [0, row_stride] is clamped into it.
+ *   num_rows   >= 0; 0 is a successful no-op.
+ *   next_n     >= 1 and divides num_rows.  It groups rows and never changes
+ *              which indices are chosen.
+ *   K          1 <= K <= TOPK_RAGGED_MAX_K.
+ *   out_idx    int32 [num_rows, K] contiguous, 4-byte aligned.  Row r gets
+ *              min(K, n_r) ascending indices then -1s.
+ *   workspace  device memory of at least topk_ragged_workspace_size() bytes
+ *              for the same (num_rows, row_stride, K) and device, zeroed once
+ *              by topk_ragged_workspace_init().  Every launch returns it to
+ *              all-zero before it ends (in-kernel cleanup), so no per-call
+ *              memset is needed.  May be NULL when the size is 0.
+ *   stream     HIP stream (NULL = the current device's null stream).
+ *
+ * Concurrent launches that share a workspace race; give each stream its own.
+ * If a launch fails or a cooperative wait times out (see
+ * topk_ragged_workspace_status) the workspace contents are undefined:
+ * initialise it again before reuse.
+ */
+int topk_ragged(const float* scores, int64_t row_stride, const int32_t* lengths,
+                int32_t num_rows, int32_t next_n, int32_t K, int32_t* out_idx,
+                void* workspace, hipStream_t stream);
+
+/* Bytes of workspace topk_ragged needs for this shape on the stream's device.
+ * *bytes = 0 means no workspace is used (rows at or under the radix
+ * threshold, or enough rows to give every workgroup a row of its own). */
+int topk_ragged_workspace_size(int32_t num_rows, int64_t row_stride, int32_t K,
+                               hipStream_t stream, size_t* bytes);
+
+/* One-time zeroing of a freshly allocated workspace, asynchronous on stream
+ * (a small fill kernel, not a memset node).  Not needed between launches. */
+int topk_ragged_workspace_init(void* workspace, size_t bytes, hipStream_t stream);
+
+/* Diagnostic text for the last failing call on this host thread ("" if none). */
+const char* topk_ragged_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Planning, overrides and diagnostics.  These expose the launch decision so
+ * that it can be tested without a GPU and forced down each code path.
+ * ------------------------------------------------------------------------- */
+
+/* Device facts the planner uses.  occupancy_* are workgroups per CU of the
+ * exact kernel instance that would run (PR #41189 page, implementation
+ * notes: query the instance actually launched, not a sibling). */
+typedef struct {
+  int32_t num_cus;
+  int32_t occupancy_single;  /* one workgroup per row kernel */
+  int32_t occupancy_multi;   /* several workgroups per row kernel */
+  int32_t max_lds_per_block;
+} topk_device_props;
+
+typedef enum {
+  TOPK_PATH_NONE = 0,    /* num_rows == 0 */
+  TOPK_PATH_SINGLE = 1,  /* one workgroup owns a row; persistent grid over rows */
+  TOPK_PATH_MULTI = 2    /* wg_per_row workgroups split a row, merge through the workspace */
+} topk_path;
+
+typedef struct {
+  int32_t path;           /* topk_path */
+  int32_t kmax;           /* kernel instance: K rounded up to 256/512/1024/2048 */
+  int32_t vec;            /* fp32 elements per load: 4, 2 or 1 */
+  int32_t block;          /* threads per workgroup */
+  int32_t grid;           /* workgroups launched */
+  int32_t wg_per_row;     /* G (1 on the single path) */
+  int64_t chunk;          /* elements of a row per workgroup (multi path) */
+  int32_t resident_cap;   /* num_cus * occupancy of the chosen kernel */
+  int32_t headroom;       /* slots left free when workgroups wait on each other */
+  int32_t lds_bytes;      /* static LDS per workgroup */
+  int32_t fell_back;      /* 1 if a requested multi plan could not be made co-resident */
+  int32_t reserved;
+  uint64_t workspace_bytes;
+} topk_plan;
+
+typedef struct {
+  int32_t force_path;        /* 0 auto, TOPK_PATH_SINGLE or TOPK_PATH_MULTI */
+  int32_t force_wg_per_row;  /* 0 auto, else G for the multi path */
+  int32_t max_grid;          /* 0 auto, else cap on the single path's persistent grid */
+  int32_t force_vec;         /* 0 auto, else 1, 2 or 4 (must suit the alignment) */
+  int64_t force_chunk;       /* 0 auto, else elements per workgroup (multiple of 4) */
+  uint32_t spin_limit;       /* 0 default; bound on a cooperative wait (polls) */
+  int32_t min_chunk;         /* 0 default; smallest per-workgroup chunk the planner picks */
+} topk_overrides;
+
+/* Pure planning function (host only, no GPU needed).  vec_allowed is the
+ * widest load the pointer/stride alignment permits (4, 2 or 1).  ov may be
+ * NULL. */
+int topk_ragged_plan(const topk_device_props* props, int32_t num_rows, int64_t row_stride,
+                     int32_t K, int32_t vec_allowed, const topk_overrides* ov,
+                     topk_plan* plan);
+
+/* The plan topk_ragged / topk_ragged_ex would use for these arguments on the
+ * stream's device (queries and caches occupancy). */
+int topk_ragged_query_plan(const float* scores, int32_t num_rows, int64_t row_stride,
+                           int32_t K, const topk_overrides* ov, hipStream_t stream,
+                           topk_plan* plan);
+
+/* Workspace bytes for the plan chosen under overrides ov. */
+int topk_ragged_workspace_size_ex(const float* scores, int32_t num_rows, int64_t row_stride,
+                                  int32_t K, const topk_overrides* ov, hipStream_t stream,
+                                  size_t* bytes);
+
+/* topk_ragged with planner overrides (testing and benchmarking). */
+int topk_ragged_ex(const float* scores, int64_t row_stride, const int32_t* lengths,
+                   int32_t num_rows, int32_t next_n, int32_t K, int32_t* out_idx,
+                   void* workspace, hipStream_t stream, const topk_overrides* ov);
+
+/* Error bits a kernel left in the workspace header (synchronises stream):
+ * bit 0: a cooperative wait hit its spin limit; bit 1: a threshold search
+ * found the histogram inconsistent.  0 = healthy. */
+int topk_ragged_workspace_status(const void* workspace, hipStream_t stream, uint32_t* flags);
+
+/* Key-transform probe (testing only): keys[i] = the device's order-preserving
+ * uint32 key of the fp32 bit pattern bits[i], for i < n.  Both arrays are
+ * device memory; asynchronous on stream. */
+int topk_ragged_debug_keys(const uint32_t* bits, uint32_t* keys, int64_t n, hipStream_t stream);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int topk_ragged_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOPK_RAGGED_H */

@@ -1,0 +1,425 @@
+// Host side of the C ABI: argument checks, the launch planner, cached device
+// facts and kernel launches.  No allocation, no memset and no synchronisation
+// on the launch path, so a call can be captured in a hipGraph.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+
+#include "topk_internal.h"
+#include "topk_ragged.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+constexpr int64_t kDefaultMinChunk = 8192;
+
+int kmax_for(int K) {
+  if (K <= 256) return 256;
+  if (K <= 512) return 512;
+  if (K <= 1024) return 1024;
+  return 2048;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool verbose() {
+  static const bool v = [] {
+    const char* e = std::getenv("TOPK_RAGGED_VERBOSE");
+    return e != nullptr && e[0] == '1';
+  }();
+  return v;
+}
+
+std::string describe(const topk_plan& p) {
+  char buf[512];
+  std::snprintf(buf, sizeof(buf),
+                "path=%d kmax=%d vec=%d block=%d grid=%d wg_per_row=%d chunk=%lld "
+                "resident_cap=%d headroom=%d lds=%d fell_back=%d workspace=%llu",
+                p.path, p.kmax, p.vec, p.block, p.grid, p.wg_per_row, (long long)p.chunk,
+                p.resident_cap, p.headroom, p.lds_bytes, p.fell_back,
+                (unsigned long long)p.workspace_bytes);
+  return buf;
+}
+
+// ---------------------------------------------------------------------------
+// Device facts, cached per device (the stream's device, looked up per call,
+// so a cached value can never belong to another device).
+// ---------------------------------------------------------------------------
+struct DevInfo {
+  int num_cus = 0;
+  int max_lds_block = 0;
+  std::map<std::tuple<int, int, int>, int> occ;  // (path, kmax, vec) -> WGs per CU
+};
+
+std::mutex g_mu;
+std::map<int, DevInfo> g_dev;
+
+int stream_device(hipStream_t stream, int* dev) {
+  hipError_t e = stream == nullptr ? hipGetDevice(dev) : hipStreamGetDevice(stream, dev);
+  if (e != hipSuccess)
+    return fail(TOPK_EDEVICE, std::string("cannot find the stream's device: ") + hipGetErrorString(e));
+  return TOPK_OK;
+}
+
+int device_info(int dev, DevInfo** out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_dev.find(dev);
+  if (it == g_dev.end()) {
+    DevInfo d;
+    hipError_t e = hipDeviceGetAttribute(&d.num_cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+      e = hipDeviceGetAttribute(&d.max_lds_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess)
+      return fail(TOPK_EDEVICE, std::string("device attribute query failed: ") + hipGetErrorString(e));
+    it = g_dev.emplace(dev, d).first;
+  }
+  *out = &it->second;
+  return TOPK_OK;
+}
+
+// Occupancy of the exact instance that will be launched.
+int occupancy(int dev, DevInfo* d, int path, int kmax, int vec, int* occ) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  const auto key = std::make_tuple(path, kmax, vec);
+  auto it = d->occ.find(key);
+  if (it != d->occ.end()) {
+    *occ = it->second;
+    return TOPK_OK;
+  }
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+  int o = 0;
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, rrt::kernel_ptr(path, kmax, vec), rrt::kBlock, 0);
+  if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
+  if (e != hipSuccess) {
+    char buf[256];
+    std::snprintf(buf, sizeof(buf), "occupancy query failed (path=%d kmax=%d vec=%d): %s", path, kmax,
+                  vec, hipGetErrorString(e));
+    return fail(TOPK_EDEVICE, buf);
+  }
+  d->occ[key] = o;
+  *occ = o;
+  return TOPK_OK;
+}
+
+int vec_allowed_for(const float* scores, int64_t row_stride) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(scores);
+  if (a % 16 == 0 && row_stride % 4 == 0) return 4;
+  if (a % 8 == 0 && row_stride % 2 == 0) return 2;
+  return 1;
+}
+
+int chosen_vec(int vec_allowed, const topk_overrides* ov, int* vec) {
+  int v = vec_allowed;
+  if (ov != nullptr && ov->force_vec != 0) {
+    if (ov->force_vec != 1 && ov->force_vec != 2 && ov->force_vec != 4)
+      return fail(TOPK_EINVAL, "force_vec must be 1, 2 or 4");
+    if (ov->force_vec > vec_allowed)
+      return fail(TOPK_EINVAL, "force_vec is wider than the scores pointer/stride alignment allows");
+    v = ov->force_vec;
+  }
+  *vec = v;
+  return TOPK_OK;
+}
+
+// Fills props for the instances (kmax, vec) of both paths on device dev.
+int real_props(int dev, int kmax, int vec, topk_device_props* props) {
+  DevInfo* d = nullptr;
+  int rc = device_info(dev, &d);
+  if (rc != TOPK_OK) return rc;
+  std::memset(props, 0, sizeof(*props));
+  props->num_cus = d->num_cus;
+  props->max_lds_per_block = d->max_lds_block;
+  rc = occupancy(dev, d, 1, kmax, vec, &props->occupancy_single);
+  if (rc == TOPK_OK) rc = occupancy(dev, d, 2, kmax, vec, &props->occupancy_multi);
+  return rc;
+}
+
+int check_common(int32_t num_rows, int64_t row_stride, int32_t K) {
+  if (num_rows < 0) return fail(TOPK_EINVAL, "num_rows must be >= 0");
+  if (row_stride < 1 || row_stride > INT32_MAX)
+    return fail(TOPK_EINVAL, "row_stride must be in [1, 2^31 - 1]");
+  if (K < 1 || K > TOPK_RAGGED_MAX_K) {
+    char buf[128];
+    std::snprintf(buf, sizeof(buf), "K=%d outside [1, %d]", K, TOPK_RAGGED_MAX_K);
+    return fail(TOPK_EUNSUPPORTED_K, buf);
+  }
+  return TOPK_OK;
+}
+
+int plan_for_call(const float* scores, int32_t num_rows, int64_t row_stride, int32_t K,
+                  const topk_overrides* ov, hipStream_t stream, int* dev_out, topk_plan* plan) {
+  int rc = check_common(num_rows, row_stride, K);
+  if (rc != TOPK_OK) return rc;
+  const int va = vec_allowed_for(scores, row_stride);
+  int vec = 4;
+  rc = chosen_vec(va, ov, &vec);
+  if (rc != TOPK_OK) return rc;
+  int dev = 0;
+  rc = stream_device(stream, &dev);
+  if (rc != TOPK_OK) return rc;
+  topk_device_props props;
+  rc = real_props(dev, kmax_for(K), vec, &props);
+  if (rc != TOPK_OK) return rc;
+  if (dev_out) *dev_out = dev;
+  return topk_ragged_plan(&props, num_rows, row_stride, K, va, ov, plan);
+}
+
+}  // namespace
+
+extern "C" {
+
+int topk_ragged_plan(const topk_device_props* props, int32_t num_rows, int64_t row_stride, int32_t K,
+                     int32_t vec_allowed, const topk_overrides* ov, topk_plan* plan) {
+  if (props == nullptr || plan == nullptr) return fail(TOPK_EINVAL, "null props or plan");
+  std::memset(plan, 0, sizeof(*plan));
+  int rc = check_common(num_rows, row_stride, K);
+  if (rc != TOPK_OK) return rc;
+  if (vec_allowed != 1 && vec_allowed != 2 && vec_allowed != 4)
+    return fail(TOPK_EINVAL, "vec_allowed must be 1, 2 or 4");
+  if (props->num_cus < 1) return fail(TOPK_EDEVICE, "device reports no compute units");
+  int vec = 4;
+  rc = chosen_vec(vec_allowed, ov, &vec);
+  if (rc != TOPK_OK) return rc;
+
+  plan->kmax = kmax_for(K);
+  plan->vec = vec;
+  plan->block = rrt::kBlock;
+  plan->wg_per_row = 1;
+  if (num_rows == 0) {
+    plan->path = TOPK_PATH_NONE;
+    return TOPK_OK;
+  }
+  const int want = ov != nullptr ? ov->force_path : 0;
+  if (want != 0 && want != TOPK_PATH_SINGLE && want != TOPK_PATH_MULTI)
+    return fail(TOPK_EINVAL, "force_path must be 0, 1 or 2");
+
+  // Several workgroups per row only pay off when rows are long (the pages'
+  // 32K radix threshold, strict) and too few to occupy the GPU one per
+  // workgroup.  row_stride stands in for the longest length, which lives on
+  // the device.
+  const bool long_rows = row_stride > TOPK_RAGGED_RADIX_THRESHOLD;
+  if (want == TOPK_PATH_MULTI || (want == 0 && long_rows)) {
+    const int occ = props->occupancy_multi;
+    if (occ < 1) {
+      if (want == TOPK_PATH_MULTI) return fail(TOPK_EDEVICE, "multi-workgroup kernel cannot be resident");
+    } else {
+      // Workgroups of one row wait for each other, so all of them must be
+      // resident at once.  Keep headroom for slots another kernel may hold
+      // (PR #41189 page: a CU's worth when occupancy > 1, else one slot).
+      const int64_t cap = (int64_t)props->num_cus * occ;
+      int64_t headroom = occ > 1 ? props->num_cus : 1;
+      int64_t avail = cap;
+      if (avail >= headroom + 2)
+        avail -= headroom;
+      else
+        headroom = 0;
+      const int64_t min_chunk = (ov != nullptr && ov->min_chunk > 0) ? ov->min_chunk : kDefaultMinChunk;
+      int64_t G = 0, chunk = 0;
+      if (ov != nullptr && ov->force_chunk > 0) {
+        if (ov->force_chunk % 4 != 0) return fail(TOPK_EINVAL, "force_chunk must be a multiple of 4");
+        chunk = ov->force_chunk;
+        G = ceil_div(row_stride, chunk);
+      } else {
+        if (ov != nullptr && ov->force_wg_per_row > 0) {
+          G = ov->force_wg_per_row;
+        } else {
+          G = ceil_div(row_stride, min_chunk);
+          const int64_t by_slots = avail / num_rows;
+          if (by_slots < G) G = by_slots;
+          if (G > rrt::kMaxGroup) G = rrt::kMaxGroup;
+        }
+        if (G >= 1) {
+          // Automatic chunks are whole tiles; a requested G keeps its count
+          // (chunks only need 4-element alignment).
+          const uint64_t align = (ov != nullptr && ov->force_wg_per_row > 0) ? 4 : rrt::kTile;
+          chunk = (int64_t)rrt::round_up((uint64_t)ceil_div(row_stride, G), align);
+          G = ceil_div(row_stride, chunk);
+        }
+      }
+      if (G > rrt::kMaxGroup) {
+        char buf[160];
+        std::snprintf(buf, sizeof(buf), "wg_per_row=%lld exceeds %d", (long long)G, rrt::kMaxGroup);
+        return fail(TOPK_EINVAL, buf);
+      }
+      const bool usable = want == TOPK_PATH_MULTI ? G >= 1 : G >= 2;
+      if (usable) {
+        const int64_t grid = (int64_t)num_rows * G;
+        if (grid <= avail) {
+          const rrt::GroupLayout lay = rrt::group_layout((int)G, rrt::cap_of(plan->kmax));
+          plan->path = TOPK_PATH_MULTI;
+          plan->wg_per_row = (int)G;
+          plan->chunk = chunk;
+          plan->grid = (int)grid;
+          plan->resident_cap = (int)cap;
+          plan->headroom = (int)headroom;
+          plan->lds_bytes = rrt::lds_bytes_of(2, plan->kmax);
+          plan->workspace_bytes = rrt::kWsHeader + (uint64_t)num_rows * lay.bytes;
+          return TOPK_OK;
+        }
+        // Not co-resident: waiting workgroups could deadlock.  Fall back to
+        // one workgroup per row, which never waits (PR #41189 page).
+        plan->fell_back = 1;
+      } else if (want == TOPK_PATH_MULTI) {
+        plan->fell_back = 1;
+      }
+    }
+  }
+
+  const int occ = props->occupancy_single;
+  if (occ < 1) return fail(TOPK_EDEVICE, "single-workgroup kernel cannot be resident");
+  const int64_t cap = (int64_t)props->num_cus * occ;
+  int64_t grid = num_rows < cap ? num_rows : cap;
+  if (ov != nullptr && ov->max_grid > 0 && grid > ov->max_grid) grid = ov->max_grid;
+  plan->path = TOPK_PATH_SINGLE;
+  plan->wg_per_row = 1;
+  plan->chunk = row_stride;
+  plan->grid = (int)grid;
+  plan->resident_cap = (int)cap;
+  plan->headroom = 0;
+  plan->lds_bytes = rrt::lds_bytes_of(1, plan->kmax);
+  plan->workspace_bytes = 0;
+  return TOPK_OK;
+}
+
+int topk_ragged_query_plan(const float* scores, int32_t num_rows, int64_t row_stride, int32_t K,
+                           const topk_overrides* ov, hipStream_t stream, topk_plan* plan) {
+  if (plan == nullptr) return fail(TOPK_EINVAL, "null plan");
+  return plan_for_call(scores, num_rows, row_stride, K, ov, stream, nullptr, plan);
+}
+
+int topk_ragged_workspace_size_ex(const float* scores, int32_t num_rows, int64_t row_stride, int32_t K,
+                                  const topk_overrides* ov, hipStream_t stream, size_t* bytes) {
+  if (bytes == nullptr) return fail(TOPK_EINVAL, "null bytes");
+  topk_plan plan;
+  const int rc = plan_for_call(scores, num_rows, row_stride, K, ov, stream, nullptr, &plan);
+  if (rc != TOPK_OK) return rc;
+  *bytes = (size_t)plan.workspace_bytes;
+  return TOPK_OK;
+}
+
+int topk_ragged_workspace_size(int32_t num_rows, int64_t row_stride, int32_t K, hipStream_t stream,
+                               size_t* bytes) {
+  // The workspace size does not depend on load width; plan as if 16-byte aligned.
+  return topk_ragged_workspace_size_ex(reinterpret_cast<const float*>(uintptr_t(256)), num_rows, row_stride,
+                                       K, nullptr, stream, bytes);
+}
+
+int topk_ragged_workspace_init(void* workspace, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return TOPK_OK;
+  if (workspace == nullptr) return fail(TOPK_EINVAL, "null workspace with nonzero size");
+  if (reinterpret_cast<uintptr_t>(workspace) % 4 != 0 || bytes % 4 != 0)
+    return fail(TOPK_EINVAL, "workspace must be 4-byte aligned and a multiple of 4 bytes");
+  const uint64_t words = bytes / 4;
+  uint32_t* p = static_cast<uint32_t*>(workspace);
+  uint64_t w = words;
+  void* args[] = {&p, &w};
+  const uint64_t blocks64 = (words + 255) / 256;
+  const unsigned blocks = (unsigned)(blocks64 < 4096 ? blocks64 : 4096);
+  hipError_t e = hipLaunchKernel(rrt::zero_kernel_ptr(), dim3(blocks), dim3(256), args, 0, stream);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return fail(TOPK_ELAUNCH, std::string("workspace init: ") + hipGetErrorString(e));
+  return TOPK_OK;
+}
+
+int topk_ragged_ex(const float* scores, int64_t row_stride, const int32_t* lengths, int32_t num_rows,
+                   int32_t next_n, int32_t K, int32_t* out_idx, void* workspace, hipStream_t stream,
+                   const topk_overrides* ov) {
+  if (num_rows < 0) return fail(TOPK_EINVAL, "num_rows must be >= 0");
+  if (next_n < 1) return fail(TOPK_EINVAL, "next_n must be >= 1");
+  if (num_rows % next_n != 0) return fail(TOPK_EINVAL, "num_rows must be a multiple of next_n");
+  int rc = check_common(num_rows, row_stride, K);
+  if (rc != TOPK_OK) return rc;
+  if (num_rows == 0) return TOPK_OK;
+  if (scores == nullptr || lengths == nullptr || out_idx == nullptr)
+    return fail(TOPK_EINVAL, "null scores, lengths or out_idx");
+  if (reinterpret_cast<uintptr_t>(out_idx) % 4 != 0 || reinterpret_cast<uintptr_t>(lengths) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(scores) % 4 != 0)
+    return fail(TOPK_EINVAL, "scores, lengths and out_idx must be 4-byte aligned");
+  topk_plan plan;
+  rc = plan_for_call(scores, num_rows, row_stride, K, ov, stream, nullptr, &plan);
+  if (rc != TOPK_OK) return rc;
+  if (plan.workspace_bytes > 0 && workspace == nullptr)
+    return fail(TOPK_EWORKSPACE, "this launch needs a workspace of " + std::to_string(plan.workspace_bytes) +
+                                     " bytes (" + describe(plan) + ")");
+  if (plan.workspace_bytes > 0 && reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(TOPK_EINVAL, "workspace must be 256-byte aligned");
+
+  rrt::KernelParams kp{};
+  kp.scores = scores;
+  kp.lengths = lengths;
+  kp.out = out_idx;
+  kp.ws = static_cast<uint8_t*>(workspace);
+  kp.row_stride = row_stride;
+  kp.chunk = plan.chunk;
+  kp.group_bytes = plan.path == TOPK_PATH_MULTI
+                       ? rrt::group_layout(plan.wg_per_row, rrt::cap_of(plan.kmax)).bytes
+                       : 0;
+  kp.num_rows = num_rows;
+  kp.K = K;
+  kp.wg_per_row = plan.wg_per_row;
+  kp.spin_limit = (ov != nullptr && ov->spin_limit > 0) ? ov->spin_limit : rrt::kDefaultSpin;
+
+  if (verbose()) std::fprintf(stderr, "[topk_ragged] rows=%d stride=%lld K=%d %s\n", num_rows,
+                              (long long)row_stride, K, describe(plan).c_str());
+  void* args[] = {&kp};
+  const void* fn = rrt::kernel_ptr(plan.path, plan.kmax, plan.vec);
+  hipError_t e = hipLaunchKernel(fn, dim3(plan.grid), dim3(plan.block), args, 0, stream);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) {
+    char buf[640];
+    std::snprintf(buf, sizeof(buf), "kernel launch failed: %s (K=%d %s)", hipGetErrorString(e), K,
+                  describe(plan).c_str());
+    return fail(TOPK_ELAUNCH, buf);
+  }
+  return TOPK_OK;
+}
+
+int topk_ragged(const float* scores, int64_t row_stride, const int32_t* lengths, int32_t num_rows,
+                int32_t next_n, int32_t K, int32_t* out_idx, void* workspace, hipStream_t stream) {
+  return topk_ragged_ex(scores, row_stride, lengths, num_rows, next_n, K, out_idx, workspace, stream, nullptr);
+}
+
+const char* topk_ragged_last_error(void) { return g_last_error.c_str(); }
+
+int topk_ragged_workspace_status(const void* workspace, hipStream_t stream, uint32_t* flags) {
+  if (flags == nullptr) return fail(TOPK_EINVAL, "null flags");
+  *flags = 0;
+  if (workspace == nullptr) return TOPK_OK;
+  hipError_t e = hipMemcpyAsync(flags, workspace, sizeof(uint32_t), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(TOPK_EDEVICE, std::string("workspace status: ") + hipGetErrorString(e));
+  return TOPK_OK;
+}
+
+int topk_ragged_debug_keys(const uint32_t* bits, uint32_t* keys, int64_t n, hipStream_t stream) {
+  if (n < 0) return fail(TOPK_EINVAL, "n must be >= 0");
+  if (n == 0) return TOPK_OK;
+  if (bits == nullptr || keys == nullptr) return fail(TOPK_EINVAL, "null bits or keys");
+  const int64_t blocks = (n + 255) / 256;
+  if (blocks > INT32_MAX) return fail(TOPK_EINVAL, "n too large");
+  void* args[] = {&bits, &keys, &n};
+  hipError_t e = hipLaunchKernel(rrt::keys_kernel_ptr(), dim3((unsigned)blocks), dim3(256), args, 0, stream);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return fail(TOPK_ELAUNCH, std::string("keys kernel: ") + hipGetErrorString(e));
+  return TOPK_OK;
+}
+
+int topk_ragged_version(void) { return 100; }
+
+}  // extern "C"

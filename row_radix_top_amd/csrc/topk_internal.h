@@ -1,0 +1,71 @@
+// Internal constants and launch parameters shared by the host launcher and
+// the gfx950 kernels.  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rrt {
+
+constexpr int kBlock = 256;                 // threads per workgroup (4 wave64)
+constexpr int kWaves = kBlock / 64;
+constexpr int kElems = 8;                   // fp32 elements per thread per tile
+constexpr int kTile = kBlock * kElems;      // 2048 elements streamed per tile
+constexpr int kBins = 2048;                 // 11-bit radix digit
+constexpr int kMaxGroup = 64;               // most workgroups that may share a row
+constexpr uint32_t kDefaultSpin = 1u << 24; // polls before a cooperative wait gives up
+
+// Candidate buffer capacity of a kernel instance: room for the KMAX kept
+// entries plus one full tile, so a tile always fits after a compaction.
+constexpr int cap_of(int kmax) { return kmax + kTile; }
+
+// Workspace: a 256-byte header (word 0: error bits) followed by one block per
+// row of the multi-workgroup path.
+constexpr uint64_t kWsHeader = 256;
+constexpr uint32_t kErrSpin = 1u;
+constexpr uint32_t kErrSearch = 2u;
+
+// Per-row block layout (bytes from the block start):
+//   0    arrival counter (u32)
+//   128  exit counter (u32)
+//   256  per-workgroup slots, 4 x u32 each: [above digit 1, above digit 2, list length, -]
+//   ...  digit-1 histogram, 2048 x u32
+//   ...  digit-2 histogram, 2048 x u32
+//   ...  per-workgroup lists, cap x u32 each
+struct GroupLayout {
+  uint64_t slots, h1, h2, lists, bytes;
+};
+
+inline constexpr uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+inline constexpr GroupLayout group_layout(int wg_per_row, int cap) {
+  GroupLayout L{};
+  L.slots = 256;
+  L.h1 = L.slots + round_up(16ull * (uint64_t)wg_per_row, 256);
+  L.h2 = L.h1 + 4ull * kBins;
+  L.lists = L.h2 + 4ull * kBins;
+  L.bytes = round_up(L.lists + 4ull * (uint64_t)cap * (uint64_t)wg_per_row, 256);
+  return L;
+}
+
+struct KernelParams {
+  const float* scores;
+  const int32_t* lengths;
+  int32_t* out;
+  uint8_t* ws;
+  int64_t row_stride;
+  int64_t chunk;         // multi path: row elements per workgroup (multiple of 4)
+  uint64_t group_bytes;  // multi path: bytes per row block in the workspace
+  int32_t num_rows;
+  int32_t K;
+  int32_t wg_per_row;    // multi path: G
+  uint32_t spin_limit;
+};
+
+// Kernel lookup for the host side.  path: 1 single, 2 multi.
+const void* kernel_ptr(int path, int kmax, int vec);
+const void* zero_kernel_ptr();
+const void* keys_kernel_ptr();
+int lds_bytes_of(int path, int kmax);
+
+}  // namespace rrt

@@ -1,0 +1,157 @@
+"""Host-side tests (no GPU): the C-ABI library loads and exports every symbol
+the public header declares, and the launch planner's residency and fallback
+rules hold for made-up device properties.
+
+The fake-device planner tests stand in for the low-shared-memory fallback
+test that the PR #54110 page says was added and then dropped: instead of
+mocking a device they call the pure planning function with chosen CU counts
+and occupancies.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import row_radix_top_amd as rrt
+from row_radix_top_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "topk_ragged.h")
+
+
+def header_functions() -> list[str]:
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(topk_ragged\w*)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = binding.load()
+    names = header_functions()
+    assert len(names) >= 10, names
+    assert set(names) == set(binding.EXPORTED), "binding and header disagree"
+    for n in names:
+        assert hasattr(lib, n), n
+    assert binding.version() >= 100
+
+
+def test_library_carries_gfx950_code():
+    blob = open(binding.LIB_PATH, "rb").read()
+    assert b"gfx950" in blob
+
+
+def test_plan_single_path_for_short_rows():
+    p = rrt.plan_for_props(256, 3, 3, 64, 32768, 2048)
+    assert p["path"] == rrt.PATH_SINGLE and p["workspace_bytes"] == 0
+    assert p["grid"] == 64 and p["headroom"] == 0 and p["kmax"] == 2048
+    # At the threshold exactly: still one workgroup per row (strict ">").
+    p = rrt.plan_for_props(256, 3, 3, 2, 32768, 1024)
+    assert p["path"] == rrt.PATH_SINGLE
+    p = rrt.plan_for_props(256, 3, 3, 2, 32769, 1024)
+    assert p["path"] == rrt.PATH_MULTI
+
+
+def test_plan_many_long_rows_use_persistent_single_path():
+    p = rrt.plan_for_props(256, 3, 3, 4096, 65536, 2048)
+    assert p["path"] == rrt.PATH_SINGLE
+    assert p["grid"] == 768 == p["resident_cap"]
+    p = rrt.plan_for_props(256, 3, 3, 4096, 65536, 2048, max_grid=100)
+    assert p["grid"] == 100
+
+
+@pytest.mark.parametrize("cus,occ", [(256, 1), (256, 2), (256, 3), (256, 4), (80, 2), (4, 1), (1, 1)])
+@pytest.mark.parametrize("rows,stride", [(16, 131072), (64, 65536), (1, 1 << 20), (3, 40000), (300, 65536)])
+def test_plan_multi_is_always_coresident(cus, occ, rows, stride):
+    p = rrt.plan_for_props(cus, occ, occ, rows, stride, 2048)
+    cap = cus * occ
+    if p["path"] == rrt.PATH_MULTI:
+        headroom = cus if occ > 1 else 1
+        assert p["headroom"] == headroom
+        assert p["grid"] == rows * p["wg_per_row"]
+        assert p["grid"] <= cap - headroom, p
+        assert p["wg_per_row"] >= 2
+        assert p["chunk"] % 2048 == 0
+        assert (p["wg_per_row"] - 1) * p["chunk"] < stride <= p["wg_per_row"] * p["chunk"]
+        assert p["workspace_bytes"] > 0
+    else:
+        assert p["path"] == rrt.PATH_SINGLE
+        assert p["workspace_bytes"] == 0
+        assert p["grid"] <= cap
+
+
+def test_plan_forced_multi_that_cannot_be_resident_falls_back():
+    # 64 rows x 16 workgroups cannot be resident on 8 CUs with occupancy 1.
+    p = rrt.plan_for_props(8, 1, 1, 64, 65536, 2048, force_path=2, force_wg_per_row=16)
+    assert p["path"] == rrt.PATH_SINGLE and p["fell_back"] == 1 and p["workspace_bytes"] == 0
+    p = rrt.plan_for_props(256, 2, 2, 4, 65536, 2048, force_path=2, force_wg_per_row=4)
+    assert p["path"] == rrt.PATH_MULTI and p["wg_per_row"] == 4
+
+
+def test_plan_headroom_only_when_there_is_room():
+    # One CU, occupancy 1: no room for headroom plus a group -> no headroom,
+    # and a group of 2 cannot be resident -> single path.
+    p = rrt.plan_for_props(1, 1, 1, 1, 65536, 2048)
+    assert p["path"] == rrt.PATH_SINGLE
+    p = rrt.plan_for_props(4, 1, 1, 1, 65536, 2048)
+    assert p["path"] == rrt.PATH_MULTI and p["headroom"] == 1 and p["grid"] <= 3
+
+
+def test_plan_single_when_multi_kernel_cannot_run():
+    p = rrt.plan_for_props(256, 2, 0, 4, 131072, 2048)
+    assert p["path"] == rrt.PATH_SINGLE
+
+
+def test_plan_kmax_and_vec():
+    for K, kmax in [(1, 256), (256, 256), (257, 512), (512, 512), (1000, 1024), (2048, 2048)]:
+        assert rrt.plan_for_props(256, 2, 2, 4, 8192, K)["kmax"] == kmax
+    assert rrt.plan_for_props(256, 2, 2, 4, 8192, 64, vec_allowed=2)["vec"] == 2
+    assert rrt.plan_for_props(256, 2, 2, 4, 8192, 64, vec_allowed=4, force_vec=1)["vec"] == 1
+    with pytest.raises(rrt.TopKError):
+        rrt.plan_for_props(256, 2, 2, 4, 8192, 64, vec_allowed=2, force_vec=4)
+
+
+def test_plan_rejects_bad_arguments():
+    with pytest.raises(rrt.TopKError) as e:
+        rrt.plan_for_props(256, 2, 2, 4, 8192, 0)
+    assert e.value.code == -2
+    with pytest.raises(rrt.TopKError) as e:
+        rrt.plan_for_props(256, 2, 2, 4, 8192, 2049)
+    assert e.value.code == -2 and "2049" in str(e.value)
+    with pytest.raises(rrt.TopKError) as e:
+        rrt.plan_for_props(256, 2, 2, -1, 8192, 10)
+    assert e.value.code == -1
+    with pytest.raises(rrt.TopKError):
+        rrt.plan_for_props(256, 2, 2, 4, 0, 10)
+    with pytest.raises(rrt.TopKError):
+        rrt.plan_for_props(256, 2, 2, 4, 100000, 10, force_path=2, force_chunk=6)
+    p = rrt.plan_for_props(256, 2, 2, 0, 8192, 10)
+    assert p["path"] == rrt.PATH_NONE
+
+
+def test_launch_argument_errors_need_no_gpu():
+    # Argument checks happen before any HIP call.
+    lib = binding.load()
+    out = ctypes.c_void_p(256)
+    assert lib.topk_ragged(None, 10, None, -1, 1, 4, None, None, None) == -1
+    assert lib.topk_ragged(None, 10, None, 4, 3, 4, None, None, None) == -1  # 4 % 3 != 0
+    assert lib.topk_ragged(None, 10, None, 4, 0, 4, None, None, None) == -1
+    assert lib.topk_ragged(None, 10, None, 0, 1, 4, None, None, None) == 0   # no-op
+    assert lib.topk_ragged(ctypes.c_void_p(256), 10, ctypes.c_void_p(256), 4, 1, 0, out, None, None) == -2
+    assert "K=0" in binding.last_error()
+    assert lib.topk_ragged(None, 10, ctypes.c_void_p(256), 4, 1, 4, out, None, None) == -1
+    assert lib.topk_ragged(ctypes.c_void_p(256), 10, ctypes.c_void_p(256), 4, 1, 4, ctypes.c_void_p(258),
+                           None, None) == -1
+
+
+def test_plan_forced_group_sizes_are_kept():
+    for G in (1, 2, 3, 5, 7, 16, 31, 32):
+        p = rrt.plan_for_props(256, 3, 3, 16, 131072, 2048, force_path=2, force_wg_per_row=G)
+        assert p["path"] == rrt.PATH_MULTI and p["wg_per_row"] == G, (G, p)
+        assert p["chunk"] % 4 == 0
+    # 16 x 64 = 1024 workgroups exceed 768 slots less 256 of headroom.
+    p = rrt.plan_for_props(256, 3, 3, 16, 131072, 2048, force_path=2, force_wg_per_row=64)
+    assert p["path"] == rrt.PATH_SINGLE and p["fell_back"] == 1

@@ -1,0 +1,223 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle,
+element by element (int32 indices, padding included).  Bit-exact is the bar:
+the output is integer and the selection rule makes it unique.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import row_radix_top_amd as rrt
+from oracle import topk_ragged_oracle
+from row_radix_top_amd import workloads
+from tests.gpu_util import assert_same, note, require_gpu, run_gpu
+from tests.pins import check_invariants
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+# ---------------------------------------------------------------------------
+# Key transform: every fp32 bit pattern
+# ---------------------------------------------------------------------------
+
+def test_key_transform_exhaustive():
+    """Walk all 2^32 patterns in IEEE value order (-NaNs, -inf .. -0, +0 ..
+    +inf, +NaNs): keys must rise strictly, except -0 -> +0 which are equal."""
+    import torch
+    dev = torch.device("cuda:0")
+    chunk = 1 << 27
+    # Negative floats in increasing value: bits 0xFFFFFFFF down to 0x80000000.
+    # Non-negative floats in increasing value: 0x00000000 up to 0x7FFFFFFF.
+    prev_last = None
+    for neg in (True, False):
+        for c in range(0, 1 << 31, chunk):
+            ar = torch.arange(c, c + chunk, dtype=torch.int64, device=dev)
+            bits = (0xFFFFFFFF - ar) if neg else ar
+            bits32 = (bits - (bits >= (1 << 31)).to(torch.int64) * (1 << 32)).to(torch.int32)
+            keys = rrt.debug_keys(bits32).to(torch.int64) & 0xFFFFFFFF
+            d = keys[1:] - keys[:-1]
+            assert bool((d > 0).all()), f"keys not increasing near chunk {c} neg={neg}"
+            if prev_last is not None:
+                step = int(keys[0].item()) - prev_last
+                if neg is False and c == 0:
+                    assert step == 0, "-0.0 and +0.0 must share a key"
+                else:
+                    assert step > 0
+            prev_last = int(keys[-1].item())
+    # -0.0 and +0.0 -> 0x80000000; -inf -> 0x007FFFFF; +inf -> 0xFF800000.
+    probe = torch.tensor([0x80000000 - (1 << 32), 0, 0xFF800000 - (1 << 32), 0x7F800000],
+                         dtype=torch.int32, device=dev)
+    k = (rrt.debug_keys(probe).to(torch.int64) & 0xFFFFFFFF).tolist()
+    assert k == [0x80000000, 0x80000000, 0x007FFFFF, 0xFF800000]
+
+
+# ---------------------------------------------------------------------------
+# The five workloads (the long-row one at both K), full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["small", "decode", "mtp", "long_k1024", "long_k2048", "prefill"])
+def test_workload_parity(name):
+    w = workloads.make_workload(name)
+    exp = topk_ragged_oracle(w.scores, w.lengths, w.K)
+    got, plan = run_gpu(w.scores, w.lengths, w.K, tag=name)
+    assert_same(got, exp, name)
+    if name in ("mtp", "long_k1024", "long_k2048"):
+        assert plan["path"] == rrt.PATH_MULTI, plan
+    if name == "prefill":
+        assert plan["path"] == rrt.PATH_SINGLE and plan["grid"] < w.num_rows, plan
+
+
+@pytest.mark.parametrize("name", ["mtp", "long_k1024", "long_k2048"])
+def test_long_rows_one_workgroup_per_row(name):
+    # The same long rows with the cooperative path switched off.
+    w = workloads.make_workload(name)
+    exp = topk_ragged_oracle(w.scores, w.lengths, w.K)
+    got, plan = run_gpu(w.scores, w.lengths, w.K, tag=name + "/single", force_path=1)
+    assert plan["path"] == rrt.PATH_SINGLE
+    assert_same(got, exp, name + " single path")
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 5, 16, 31, 64])
+def test_long_rows_group_sizes(G):
+    w = workloads.make_workload("long_k2048")
+    exp = topk_ragged_oracle(w.scores, w.lengths, w.K)
+    got, plan = run_gpu(w.scores, w.lengths, w.K, tag=f"long G={G}", force_path=2, force_wg_per_row=G)
+    if plan["path"] == rrt.PATH_MULTI:
+        assert plan["wg_per_row"] == G
+    else:
+        # Not co-resident on this device: the planner must have fallen back.
+        assert plan["fell_back"] == 1 and 16 * G > plan["resident_cap"] - plan["headroom"]
+    assert_same(got, exp, f"G={G}")
+
+
+@pytest.mark.parametrize("grid", [1, 3, 64, 200])
+def test_persistent_grid_caps(grid):
+    w = workloads.make_workload("decode")
+    exp = topk_ragged_oracle(w.scores, w.lengths, w.K)
+    got, plan = run_gpu(w.scores, w.lengths, w.K, tag=f"decode grid={grid}", max_grid=grid)
+    assert plan["grid"] == min(grid, w.num_rows)
+    assert_same(got, exp, f"grid={grid}")
+
+
+def test_decode_short_rows_and_next_n():
+    w = workloads.make_workload("mtp")
+    got2d, _ = run_gpu(w.scores, w.lengths, w.K, tag="mtp 2-D lengths")
+    got1d, _ = run_gpu(w.scores, w.flat_lengths, w.K, next_n=1, tag="mtp 1-D lengths")
+    assert np.array_equal(got2d, got1d)
+    w = workloads.make_workload("decode")
+    got, _ = run_gpu(w.scores, w.lengths, w.K, tag="decode invariants")
+    for r in range(w.num_rows):
+        check_invariants(w.scores[r], int(w.flat_lengths[r]), w.K, got[r])
+
+
+# ---------------------------------------------------------------------------
+# Edge rows: every length class, special values, both paths, narrow loads
+# ---------------------------------------------------------------------------
+
+EDGE_DISTS = ["normal", "levels", "const", "inc", "dec", "signed_zero", "denorm", "inf"]
+
+
+@pytest.mark.parametrize("dist", EDGE_DISTS)
+@pytest.mark.parametrize("K", [1, 7, 300, 1024, 2048])
+def test_edge_rows_single_path(dist, K):
+    stride = 9000
+    lens = [0, 1, K - 1, K, K + 1, stride, 2047, 2048, 2049, 4097, 6143, 8191, 8999, -5, 99999]
+    lens = [min(max(v, -5), 99999) for v in lens]
+    s, L = workloads.random_rows(1000 + K, len(lens), stride, lens, dist=dist, levels=3)
+    exp = topk_ragged_oracle(s, L, K)
+    got, _ = run_gpu(s, L, K, tag=f"edge {dist} K={K}")
+    assert_same(got, exp, f"{dist} K={K}")
+
+
+@pytest.mark.parametrize("dist", EDGE_DISTS)
+@pytest.mark.parametrize("K", [5, 2048])
+def test_edge_rows_multi_path(dist, K):
+    stride = 40000
+    lens = [0, 1, K, K + 1, 2049, 8192, 8193, 16384 + 3, 39999, 40000]
+    s, L = workloads.random_rows(2000 + K, len(lens), stride, lens, dist=dist, levels=4)
+    exp = topk_ragged_oracle(s, L, K)
+    for G in (2, 5):
+        got, plan = run_gpu(s, L, K, tag=f"edge-multi {dist} K={K} G={G}", force_path=2,
+                            force_wg_per_row=G)
+        assert plan["path"] == rrt.PATH_MULTI
+        assert_same(got, exp, f"multi {dist} K={K} G={G}")
+
+
+@pytest.mark.parametrize("offset,stride", [(1, 5001), (2, 5002), (3, 5003), (0, 5003), (0, 5002)])
+def test_narrow_loads(offset, stride):
+    lens = [stride, stride - 1, 4099, 3000, 17]
+    s, L = workloads.random_rows(77 + offset, len(lens), stride, lens, dist="levels", levels=50)
+    for K in (16, 2048):
+        exp = topk_ragged_oracle(s, L, K)
+        got, plan = run_gpu(s, L, K, offset=offset, tag=f"narrow off={offset} stride={stride}")
+        want_vec = 4 if (offset % 4 == 0 and stride % 4 == 0) else (2 if offset % 2 == 0 and stride % 2 == 0 else 1)
+        assert plan["vec"] == want_vec
+        assert_same(got, exp, f"offset={offset} stride={stride} K={K}")
+
+
+def test_forced_vec_widths():
+    s, L = workloads.random_rows(5, 6, 12000, [12000, 11999, 5000, 2048, 2049, 1], dist="normal")
+    exp = topk_ragged_oracle(s, L, 777)
+    for vec in (1, 2, 4):
+        for path in (1, 2):
+            got, plan = run_gpu(s, L, 777, tag=f"vec={vec} path={path}", force_vec=vec, force_path=path,
+                                force_wg_per_row=3 if path == 2 else 0)
+            assert plan["vec"] == vec
+            assert_same(got, exp, f"vec={vec} path={path}")
+
+
+def test_all_ties_long_rows():
+    # Constant rows far longer than the candidate buffer: every element ties.
+    s, L = workloads.random_rows(9, 4, 131072, [131072, 100000, 65537, 2049], dist="const")
+    for K in (1, 2048):
+        exp = topk_ragged_oracle(s, L, K)
+        got, _ = run_gpu(s, L, K, tag=f"const auto K={K}")
+        assert_same(got, exp, f"const K={K}")
+        got, _ = run_gpu(s, L, K, tag=f"const single K={K}", force_path=1)
+        assert_same(got, exp, f"const single K={K}")
+
+
+def test_increasing_rows_refill_every_tile():
+    # Every new tile beats the whole buffer: the worst case for compaction.
+    s, L = workloads.random_rows(3, 3, 70000, [70000, 65536, 33333], dist="inc")
+    exp = topk_ragged_oracle(s, L, 2048)
+    for path in (1, 2):
+        got, _ = run_gpu(s, L, 2048, tag=f"inc path={path}", force_path=path)
+        assert_same(got, exp, f"inc path={path}")
+
+
+def test_many_rows_random_lengths():
+    rng = np.random.default_rng(31)
+    lens = rng.integers(0, 20000, size=700)
+    s, L = workloads.random_rows(31, 700, 20000, lens, dist="normal")
+    for K in (64, 513, 2048):
+        exp = topk_ragged_oracle(s, L, K)
+        got, _ = run_gpu(s, L, K, tag=f"700 rows K={K}")
+        assert_same(got, exp, f"700 rows K={K}")
+
+
+# ---------------------------------------------------------------------------
+# Errors reported by the launch path on the device
+# ---------------------------------------------------------------------------
+
+def test_missing_workspace_is_an_error():
+    import torch
+    dev = torch.device("cuda:0")
+    s = torch.zeros(16, 131072, device=dev)
+    L = torch.full((16,), 131072, dtype=torch.int32, device=dev)
+    assert rrt.workspace_size(16, 131072, 2048, device=dev) > 0
+    with pytest.raises(rrt.TopKError) as e:
+        rrt.topk_ragged(s, L, 2048)
+    assert e.value.code == -3 and "workspace" in str(e.value)
+    assert rrt.workspace_size(4, 8192, 512, device=dev) == 0
+    s = torch.zeros(4, 8192, device=dev)
+    out = rrt.topk_ragged(s, torch.full((4,), 8192, dtype=torch.int32, device=dev), 512)
+    torch.cuda.synchronize()
+    assert out[0].tolist() == list(range(512))
+    note("errors ok")
