@@ -12,12 +12,14 @@ constexpr int kWaves = kBlock / 64;
 constexpr int kElems = 8;                   // fp32 elements per thread per tile
 constexpr int kTile = kBlock * kElems;      // 2048 elements streamed per tile
 constexpr int kBins = 2048;                 // 11-bit radix digit
+constexpr int kPrefetch = 4;                // register ring of tiles per thread
 constexpr int kMaxGroup = 64;               // most workgroups that may share a row
 constexpr uint32_t kDefaultSpin = 1u << 24; // polls before a cooperative wait gives up
 
 // Candidate buffer capacity of a kernel instance: room for the KMAX kept
-// entries plus one full tile, so a tile always fits after a compaction.
-constexpr int cap_of(int kmax) { return kmax + kTile; }
+// entries plus one full tile, so a tile always fits after a compaction;
+// rounded up to 1024 so every thread owns a whole number of uint4s.
+constexpr int cap_of(int kmax) { return (kmax + kTile + 1023) / 1024 * 1024; }
 
 // Workspace: a 256-byte header (word 0: error bits) followed by one block per
 // row of the multi-workgroup path.

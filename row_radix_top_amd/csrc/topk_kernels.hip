@@ -8,24 +8,31 @@
 // Design (not the pages' CUDA design, which is prior art):
 //
 // * Streaming filter.  A workgroup walks its row (or its chunk of a row) once,
-//   in 2048-element tiles of coalesced vector loads.  It keeps an
-//   index-ordered candidate buffer in LDS and a lower bound L on the key of
-//   the K-th best element seen so far; an element is appended only if its key
-//   is >= L.  When a tile would overflow the buffer, the buffer is compacted
-//   to exactly its K best entries (radix select below) and L rises to just
-//   above the K-th best key.  Later elements equal to that key can never win
-//   (every kept entry has a lower index), so the buffer never fills with
-//   ties.  Each score is read from HBM exactly once.
+//   in 2048-element tiles of coalesced vector loads kept in flight by a
+//   register ring.  It keeps an index-ordered candidate buffer in LDS and a
+//   lower bound L on the key of the K-th best element seen so far; an element
+//   is appended only if its key is >= L, which costs one IEEE compare per
+//   element.  When a tile would overflow the buffer, the buffer is compacted
+//   to exactly its K best entries and L rises to just above the K-th best key.
+//   Later elements equal to that key can never win (every kept entry has a
+//   lower index), so the buffer never fills with ties.  Each score is read
+//   from HBM exactly once.
 //
-// * Radix select in LDS.  The buffer is held in registers (cap/256 entries per
-//   thread) while 11/11/10-bit digit histograms are built with LDS atomics;
-//   one wavefront scans each histogram from the top with a lane prefix scan
-//   to find the threshold digit.  Ties at the final 32-bit key go to the
-//   lower buffer position, which is the lower index.
+// * Running histogram.  Every appended key also bumps an 11-bit (top digit)
+//   LDS histogram of the buffer, so the first radix pass of every selection
+//   is already done; after a compaction the histogram is corrected bin-wise
+//   (bins below the threshold digit empty, the threshold bin holds the number
+//   of entries kept from it).
 //
-// * Ordered emit.  Wavefront ballots and mbcnt give each lane its rank inside
-//   the wave; per-wave counts exchanged through LDS give the rest.  Output is
-//   written in ascending index order with no sort.
+// * Radix select.  Later digits (11 then 10 bits) are histogrammed with LDS
+//   atomics over the register-held buffer; one wavefront scans a histogram
+//   from the top with DPP prefix sums to find the threshold digit.  Ties at
+//   the final 32-bit key go to the lower buffer position, the lower index.
+//
+// * Ordered emit.  Each thread owns a contiguous slice of the buffer; one
+//   workgroup prefix sum of the per-thread (greater, equal) counts gives every
+//   chosen entry its output rank, so output is written in ascending index
+//   order with no sort.
 //
 // * Multi-workgroup rows.  G workgroups each filter a contiguous chunk, then
 //   merge digit histograms in the workspace with agent-scope atomics across
@@ -50,7 +57,7 @@
 namespace rrt {
 
 // ---------------------------------------------------------------------------
-// Bit-level helpers
+// Bit-level and wavefront helpers
 // ---------------------------------------------------------------------------
 
 // Order-preserving key: negative floats -> ~bits, non-negative -> bits | sign.
@@ -68,6 +75,17 @@ __device__ __forceinline__ float key_floor(uint32_t L) {
   return __uint_as_float(u);
 }
 
+// Acceptance threshold as a float: x >= accept_floor(L) <=> key(x) >= L.
+__device__ __forceinline__ float accept_floor(uint32_t L) {
+  return L >= 0x00800000u ? key_floor(L) : -__builtin_inff();
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// Pointers into LDS (address space 3), so out-of-line helpers address it with
+// ds_* instructions directly.
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) u32x4 lds_u4;
+
 __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
 // Number of set bits of m in lanes below this one.
@@ -77,14 +95,21 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
 
 __device__ __forceinline__ uint32_t popc64(uint64_t m) { return (uint32_t)__popcll(m); }
 
+// Inclusive prefix sum over the 64 lanes with DPP row shifts and row
+// broadcasts (no LDS traffic).
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
-  }
-  return v;
+  int x = (int)v;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return (uint32_t)x;
+}
+
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, int lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -94,184 +119,237 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
 template <int KMAX>
 struct Shape {
   static constexpr int kCap = cap_of(KMAX);
-  static constexpr int kSlots = kCap / kBlock;  // buffer entries per thread in registers
-  static_assert(kCap % kBlock == 0, "capacity must tile the workgroup");
+  static constexpr int kSlots = kCap / kBlock;  // buffer entries owned per thread
+  static_assert(kCap % kBlock == 0 && kSlots % 4 == 0, "capacity must tile the workgroup in uint4s");
   static_assert(kCap < 65536, "packed 16-bit counts");
 };
 
 template <int KMAX>
 struct __align__(16) Smem {
-  uint32_t key[Shape<KMAX>::kCap];
-  uint32_t idx[Shape<KMAX>::kCap];
-  uint32_t hist[kBins];
+  uint32_t key[Shape<KMAX>::kCap];  // candidate keys, index order
+  uint32_t idx[Shape<KMAX>::kCap];  // their column indices
+  uint32_t hist1[kBins];            // top-digit histogram of the buffer, kept current
+  uint32_t hist2[kBins];            // scratch histogram for later digits (zero between uses)
   uint32_t tile_cnt[2][kElems][kWaves];
-  uint32_t rank_cnt[Shape<KMAX>::kSlots][kWaves];
+  uint32_t wsum[kWaves];
   uint32_t res[4];
   uint32_t acc[8];
 };
 
 // ---------------------------------------------------------------------------
 // Threshold search: wavefront 0 finds the bin holding the krem-th largest
-// entry, counting down from the top bin, then leaves the histogram zeroed.
-// res = {bin, entries in bins above it, entries in the bin, ok}.  Kept out of
-// line: inlined, its rotated LDS addresses are hoisted out of the row loop
-// and pinned in registers for the whole kernel.
+// entry, counting down from the top bin; with ZERO it leaves the histogram
+// zeroed.  res = {bin, entries in bins above it, entries in the bin, ok}.
+// Kept out of line: inlined, its per-lane LDS addresses are hoisted out of
+// the row loop and pinned in registers for the whole kernel.
 // ---------------------------------------------------------------------------
-template <int NB>
-__device__ __noinline__ void wave_search(uint32_t* hist, uint32_t krem, uint32_t* res) {
-  constexpr int kPer = NB / 64;
+template <int NB, bool ZERO>
+__device__ __noinline__ void wave_search(lds_u32* hist, uint32_t krem, lds_u32* res) {
+  constexpr int kPer = NB / 64;  // bins per lane-group: 32 or 16
+  constexpr int kVec = kPer / 4;
   const int lane = threadIdx.x & 63;
-  const int q = 63 - lane;  // lane 0 owns the highest group of bins
-  uint32_t* grp = hist + q * kPer;
+  // Lane l owns group 63 - l, so lane order is descending bin order.
+  lds_u4* grp = (lds_u4*)(hist + (63 - lane) * kPer);
   uint32_t s = 0;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) s += grp[(i + lane) & (kPer - 1)];  // rotated: no bank conflicts
+  for (int c = 0; c < kVec; ++c) {
+    const u32x4 v = grp[(c + lane) & (kVec - 1)];  // rotated start: spreads the banks
+    s += v.x + v.y + v.z + v.w;
+  }
   const uint32_t incl = wave_incl_scan(s);
-  const uint32_t excl = incl - s;
-  if (incl >= krem && excl < krem) {
-    uint32_t acc = excl;
-    for (int i = kPer - 1; i >= 0; --i) {
-      const uint32_t v = grp[i];
-      if (acc + v >= krem) {
-        res[0] = (uint32_t)(q * kPer + i);
-        res[1] = acc;
-        res[2] = v;
-        res[3] = 1u;
-        break;
-      }
-      acc += v;
+  const uint64_t reach = ballot(incl >= krem);
+  if (reach == 0) {  // fewer than krem entries: inconsistent histogram
+    if (lane == 0) {
+      res[0] = 0u;
+      res[1] = 0u;
+      res[2] = lane_value(incl, 63);
+      res[3] = 0u;
+    }
+  } else {
+    // The first lane whose running count reaches krem owns the threshold
+    // group; its bins are scanned by as many lanes, top bin first.
+    const int lc = __builtin_ctzll(reach);
+    const uint32_t before = lane_value(incl, lc) - lane_value(s, lc);
+    const int qc = 63 - lc;
+    const uint32_t v = lane < kPer ? hist[qc * kPer + (kPer - 1 - lane)] : 0u;
+    const uint32_t in2 = wave_incl_scan(v) + before;
+    const uint64_t reach2 = ballot(lane < kPer && in2 >= krem);
+    const int l2 = __builtin_ctzll(reach2);
+    if (lane == l2) {
+      res[0] = (uint32_t)(qc * kPer + (kPer - 1 - l2));
+      res[1] = in2 - v;
+      res[2] = v;
+      res[3] = 1u;
     }
   }
-  const uint32_t total = __shfl(incl, 63, 64);
-  if (lane == 0 && total < krem) {
-    res[0] = 0u;
-    res[1] = 0u;
-    res[2] = total;
-    res[3] = 0u;
-  }
+  if (ZERO) {
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) grp[(i + lane) & (kPer - 1)] = 0u;
+    for (int c = 0; c < kVec; ++c) grp[(c + lane) & (kVec - 1)] = u32x4{0u, 0u, 0u, 0u};
+  }
 }
+
+template <int NB, bool ZERO>
+__device__ __forceinline__ void search(uint32_t* hist, uint32_t krem, uint32_t* res) {
+  if (threadIdx.x < 64) wave_search<NB, ZERO>((lds_u32*)hist, krem, (lds_u32*)res);
+}
+
+// Exclusive prefix sum of v over the workgroup in thread order; *total gets
+// the sum.  Contains one barrier.
+template <int KMAX>
+__device__ __forceinline__ uint32_t block_excl_scan(Smem<KMAX>& sm, uint32_t v, uint32_t* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_scan(v);
+  if (lane == 63) sm.wsum[w] = incl;
+  __syncthreads();
+  const uint4 ws = *reinterpret_cast<const uint4*>(sm.wsum);
+  *total = ws.x + ws.y + ws.z + ws.w;
+  const uint32_t before = (w > 0 ? ws.x : 0u) + (w > 1 ? ws.y : 0u) + (w > 2 ? ws.z : 0u);
+  return before + incl - v;
+}
+
+// ---------------------------------------------------------------------------
+// Selection over the candidate buffer
+// ---------------------------------------------------------------------------
 
 struct Sel {
   uint32_t prefix;  // decided key bits
   uint32_t pmask;   // which bits are decided
-  uint32_t krem;    // entries equal to prefix (under pmask) still to take, lowest position first
+  uint32_t krem;    // entries equal to prefix (under pmask) to take, lowest position first
   uint32_t ok;
+  uint32_t b1;      // threshold top digit
+  uint32_t krem1;   // entries taken from bin b1
 };
 
-// Radix select over the register-held buffer: the keep best entries are those
-// with (key & pmask) > prefix, plus the first krem (by position) with
-// (key & pmask) == prefix.  Requires keep <= number of valid entries.
+// Thread t owns buffer positions [t*S, t*S + S); loads keys and indices.
 template <int KMAX>
-__device__ Sel radix_select(Smem<KMAX>& sm, const uint32_t (&k)[Shape<KMAX>::kSlots], uint32_t cnt,
-                            uint32_t keep) {
+__device__ __forceinline__ void load_owned(const Smem<KMAX>& sm, uint32_t (&k)[Shape<KMAX>::kSlots],
+                                           uint32_t (&ix)[Shape<KMAX>::kSlots]) {
   constexpr int S = Shape<KMAX>::kSlots;
-  const int t = threadIdx.x;
-  Sel r{0u, 0u, keep, 1u};
+  const uint32_t base = threadIdx.x * S;
 #pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+  for (int q = 0; q < S / 4; ++q) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(&sm.key[base + 4 * q]);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(&sm.idx[base + 4 * q]);
+    k[4 * q + 0] = a.x;
+    k[4 * q + 1] = a.y;
+    k[4 * q + 2] = a.z;
+    k[4 * q + 3] = a.w;
+    ix[4 * q + 0] = b.x;
+    ix[4 * q + 1] = b.y;
+    ix[4 * q + 2] = b.z;
+    ix[4 * q + 3] = b.w;
+  }
+}
+
+// The keep best of the cnt buffer entries (keys in registers, contiguous
+// ownership): those with (key & pmask) > prefix plus the first krem with
+// (key & pmask) == prefix.  hist1 must be the top-digit histogram of the
+// buffer; it is read, not changed.  hist2 is left zeroed.  keep <= cnt.
+template <int KMAX>
+__device__ Sel select_keep(Smem<KMAX>& sm, const uint32_t (&k)[Shape<KMAX>::kSlots], uint32_t cnt,
+                           uint32_t keep) {
+  constexpr int S = Shape<KMAX>::kSlots;
+  const uint32_t base = threadIdx.x * S;
+  Sel r;
+  search<2048, false>(sm.hist1, keep, sm.res);
+  __syncthreads();
+  r.b1 = sm.res[0];
+  r.ok = sm.res[3];
+  r.krem = keep - sm.res[1];
+  r.krem1 = r.krem;
+  r.prefix = r.b1 << 21;
+  r.pmask = 0xffe00000u;
+  uint32_t in_bin = sm.res[2];
 #pragma unroll
-    for (int j = 0; j < S; ++j) {
-      const uint32_t p = (uint32_t)(t + j * kBlock);
-      if (p < cnt && (k[j] & r.pmask) == r.prefix) atomicAdd(&sm.hist[(k[j] >> shift) & dmask], 1u);
-    }
+  for (int pass = 1; pass < 3; ++pass) {
+    if (in_bin == r.krem) break;  // every entry of the bin is taken
+    const int shift = pass == 1 ? 10 : 0;
+    const uint32_t dmask = pass == 1 ? 2047u : 1023u;
+#pragma unroll
+    for (int j = 0; j < S; ++j)
+      if (base + j < cnt && (k[j] & r.pmask) == r.prefix) atomicAdd(&sm.hist2[(k[j] >> shift) & dmask], 1u);
     __syncthreads();
-    if (t < 64) {
-      if (pass == 2)
-        wave_search<1024>(sm.hist, r.krem, sm.res);
-      else
-        wave_search<2048>(sm.hist, r.krem, sm.res);
-    }
+    if (pass == 1)
+      search<2048, true>(sm.hist2, r.krem, sm.res);
+    else
+      search<1024, true>(sm.hist2, r.krem, sm.res);
     __syncthreads();
-    const uint32_t b = sm.res[0], above = sm.res[1], in_bin = sm.res[2];
     r.ok &= sm.res[3];
-    r.krem -= above;
-    r.prefix |= b << shift;
+    r.krem -= sm.res[1];
+    r.prefix |= sm.res[0] << shift;
     r.pmask |= dmask << shift;
-    if (in_bin == r.krem) break;  // every entry of the bin is taken: no further digit needed
+    in_bin = sm.res[2];
   }
   return r;
 }
 
-// Ordered emit of the entries chosen by s.  An entry's rank counts chosen
-// entries before it in buffer order; gt_base / eq_base add counts from
-// earlier chunks of the row (multi path); take_eq bounds the row-wide number
-// of entries equal to the prefix that are taken.  Writes idx to out[rank]
-// when out != nullptr, otherwise (key, idx) back to the LDS buffer.  Ranks at
-// or above limit are dropped (only reachable with an inconsistent workspace).
-// Flags are recomputed after the barrier rather than kept live across it.
+// Writes the chosen entries in buffer order.  An entry is chosen if
+// (key & pmask) > prefix, or if it equals prefix and fewer than take_eq
+// equal entries precede it (gt_base / eq_base count greater / equal entries
+// of earlier chunks of the row).  Its rank = earlier greater entries +
+// min(earlier equal entries, take_eq).  Ranks >= limit are dropped (only
+// reachable with an inconsistent workspace).  To LDS (key, idx) when out is
+// null, else idx to out[rank].  Contains one barrier.
 template <int KMAX>
-__device__ void ordered_emit(Smem<KMAX>& sm, const uint32_t (&k)[Shape<KMAX>::kSlots],
-                             const uint32_t (&ix)[Shape<KMAX>::kSlots], uint32_t cnt, const Sel& s,
-                             uint32_t gt_base, uint32_t eq_base, uint32_t take_eq, int32_t* out,
-                             uint32_t limit) {
+__device__ __forceinline__ void emit_chosen(Smem<KMAX>& sm, const uint32_t (&k)[Shape<KMAX>::kSlots],
+                                            const uint32_t (&ix)[Shape<KMAX>::kSlots], uint32_t cnt,
+                                            uint32_t prefix, uint32_t pmask, uint32_t gt_base,
+                                            uint32_t eq_base, uint32_t take_eq, int32_t* out,
+                                            uint32_t limit) {
   constexpr int S = Shape<KMAX>::kSlots;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const uint32_t base = threadIdx.x * S;
+  uint32_t packed = 0;
 #pragma unroll
   for (int j = 0; j < S; ++j) {
-    const bool valid = (uint32_t)(t + j * kBlock) < cnt;
-    const uint32_t km = k[j] & s.pmask;
-    const uint32_t cg = popc64(ballot(valid && km > s.prefix));
-    const uint32_t ce = popc64(ballot(valid && km == s.prefix));
-    if (lane == 0) sm.rank_cnt[j][w] = cg | (ce << 16);
+    const bool valid = base + j < cnt;
+    const uint32_t km = k[j] & pmask;
+    packed += (valid && km > prefix) ? 1u : 0u;
+    packed += (valid && km == prefix) ? 0x10000u : 0u;
   }
-  __syncthreads();
-  uint32_t run = 0;
+  uint32_t total;
+  const uint32_t excl = block_excl_scan(sm, packed, &total);
+  uint32_t g = gt_base + (excl & 0xffffu);
+  uint32_t e = eq_base + (excl >> 16);
 #pragma unroll
   for (int j = 0; j < S; ++j) {
-    const bool valid = (uint32_t)(t + j * kBlock) < cnt;
-    const uint32_t km = k[j] & s.pmask;
-    const bool gt = valid && km > s.prefix;
-    const bool eq = valid && km == s.prefix;
-    const uint32_t pg = lanes_below(ballot(gt));
-    const uint32_t pe = lanes_below(ballot(eq));
-    const uint4 v = *reinterpret_cast<const uint4*>(sm.rank_cnt[j]);
-    const uint32_t before = (w > 0 ? v.x : 0u) + (w > 1 ? v.y : 0u) + (w > 2 ? v.z : 0u);
-    const uint32_t base = run + before;
-    run += v.x + v.y + v.z + v.w;
-    const uint32_t gtb = gt_base + (base & 0xffffu) + pg;
-    const uint32_t eqb = eq_base + (base >> 16) + pe;
-    if (gt || (eq && eqb < take_eq)) {
-      const uint32_t pos = gtb + (eqb < take_eq ? eqb : take_eq);
-      if (pos < limit) {
-        if (out != nullptr) {
-          out[pos] = (int32_t)ix[j];
-        } else {
-          sm.key[pos] = k[j];
-          sm.idx[pos] = ix[j];
-        }
+    const bool valid = base + j < cnt;
+    const uint32_t km = k[j] & pmask;
+    const bool gt = valid && km > prefix;
+    const bool eq = valid && km == prefix;
+    const bool take = gt || (eq && e < take_eq);
+    const uint32_t pos = g + (e < take_eq ? e : take_eq);
+    if (take && pos < limit) {
+      if (out != nullptr) {
+        out[pos] = (int32_t)ix[j];
+      } else {
+        sm.key[pos] = k[j];
+        sm.idx[pos] = ix[j];
       }
     }
+    g += gt ? 1u : 0u;
+    e += eq ? 1u : 0u;
   }
 }
 
+// Compacts the buffer (cnt > keep entries) to its keep best, index order
+// kept, corrects the running histogram and returns the raised acceptance
+// bound.  Arguments and result go by value: as an out-of-line call, a
+// by-reference counter would live in scratch, and every scratch reload waits
+// on all outstanding prefetches.
 template <int KMAX>
-__device__ __forceinline__ void load_buffer(const Smem<KMAX>& sm, uint32_t cnt,
-                                            uint32_t (&k)[Shape<KMAX>::kSlots],
-                                            uint32_t (&ix)[Shape<KMAX>::kSlots]) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int j = 0; j < Shape<KMAX>::kSlots; ++j) {
-    const uint32_t p = (uint32_t)(t + j * kBlock);
-    k[j] = p < cnt ? sm.key[p] : 0u;
-    ix[j] = p < cnt ? sm.idx[p] : 0u;
-  }
-}
-
-// Compacts the LDS buffer to its keep best entries (index order kept) and
-// raises the acceptance bound L.
-template <int KMAX>
-__device__ void compact(Smem<KMAX>& sm, uint32_t& cnt, uint32_t keep, uint32_t& L) {
+__device__ __noinline__ uint32_t compact(Smem<KMAX>& sm, uint32_t cnt, uint32_t keep, uint32_t L) {
   constexpr int S = Shape<KMAX>::kSlots;
   uint32_t k[S], ix[S];
-  load_buffer<KMAX>(sm, cnt, k, ix);
-  const Sel s = radix_select<KMAX>(sm, k, cnt, keep);
-  ordered_emit<KMAX>(sm, k, ix, cnt, s, 0u, 0u, s.krem, nullptr, (uint32_t)Shape<KMAX>::kCap);
+  load_owned<KMAX>(sm, k, ix);
+  const Sel s = select_keep<KMAX>(sm, k, cnt, keep);
+  emit_chosen<KMAX>(sm, k, ix, cnt, s.prefix, s.pmask, 0u, 0u, s.krem, nullptr,
+                    (uint32_t)Shape<KMAX>::kCap);
+  // Kept entries: bins above b1 unchanged, krem1 from bin b1, none below.
+  for (uint32_t i = threadIdx.x; i < (uint32_t)kBins; i += kBlock) {
+    if (i < s.b1) sm.hist1[i] = 0u;
+    if (i == s.b1) sm.hist1[i] = s.krem1;
+  }
   __syncthreads();
-  cnt = keep;
   // Every element still to come has a higher index than all kept entries, so
   // it must beat the K-th best key strictly to matter.  When the K-th best key
   // is known only to its top bits, accept anything from that prefix up.
@@ -280,7 +358,20 @@ __device__ void compact(Smem<KMAX>& sm, uint32_t& cnt, uint32_t keep, uint32_t& 
     Ln = s.prefix == 0xffffffffu ? 0xffffffffu : s.prefix + 1u;
   else
     Ln = s.prefix;
-  L = Ln > L ? Ln : L;
+  return Ln > L ? Ln : L;
+}
+
+// The K best of the buffer, written to out in index order; the running
+// histogram is cleared for the next row.
+template <int KMAX>
+__device__ __noinline__ void final_select(Smem<KMAX>& sm, uint32_t cnt, uint32_t K, int32_t* out) {
+  constexpr int S = Shape<KMAX>::kSlots;
+  uint32_t k[S], ix[S];
+  load_owned<KMAX>(sm, k, ix);
+  const Sel s = select_keep<KMAX>(sm, k, cnt, K);
+  emit_chosen<KMAX>(sm, k, ix, cnt, s.prefix, s.pmask, 0u, 0u, s.krem, out, K);
+  for (uint32_t i = threadIdx.x; i < (uint32_t)kBins; i += kBlock) sm.hist1[i] = 0u;
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -288,67 +379,53 @@ __device__ void compact(Smem<KMAX>& sm, uint32_t& cnt, uint32_t keep, uint32_t& 
 // ---------------------------------------------------------------------------
 
 template <int VEC>
-__device__ __forceinline__ void load_tile(const float* __restrict__ rowp, uint32_t c1, uint32_t p0,
+__device__ __forceinline__ void load_full(const float* __restrict__ rowp, uint32_t p0, float (&x)[kElems]) {
+  const uint32_t t = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < kElems / VEC; ++u) {
+    const uint32_t pos = p0 + (uint32_t)u * (kBlock * VEC) + t * VEC;
+    if constexpr (VEC == 4) {
+      const float4 v = *reinterpret_cast<const float4*>(rowp + pos);
+      x[u * 4 + 0] = v.x;
+      x[u * 4 + 1] = v.y;
+      x[u * 4 + 2] = v.z;
+      x[u * 4 + 3] = v.w;
+    } else if constexpr (VEC == 2) {
+      const float2 v = *reinterpret_cast<const float2*>(rowp + pos);
+      x[u * 2 + 0] = v.x;
+      x[u * 2 + 1] = v.y;
+    } else {
+      x[u] = rowp[pos];
+    }
+  }
+}
+
+// The partial last tile: per-element bounds checks, nothing read at or past c1.
+template <int VEC>
+__device__ __forceinline__ void load_tail(const float* __restrict__ rowp, uint32_t c1, uint32_t p0,
                                           float (&x)[kElems]) {
   const uint32_t t = threadIdx.x;
 #pragma unroll
   for (int u = 0; u < kElems / VEC; ++u) {
     const uint32_t pos = p0 + (uint32_t)u * (kBlock * VEC) + t * VEC;
-    if (pos + VEC <= c1) {
-      if constexpr (VEC == 4) {
-        const float4 v = *reinterpret_cast<const float4*>(rowp + pos);
-        x[u * 4 + 0] = v.x;
-        x[u * 4 + 1] = v.y;
-        x[u * 4 + 2] = v.z;
-        x[u * 4 + 3] = v.w;
-      } else if constexpr (VEC == 2) {
-        const float2 v = *reinterpret_cast<const float2*>(rowp + pos);
-        x[u * 2 + 0] = v.x;
-        x[u * 2 + 1] = v.y;
-      } else {
-        x[u] = rowp[pos];
-      }
-    } else {
 #pragma unroll
-      for (int c = 0; c < VEC; ++c) x[u * VEC + c] = (pos + c < c1) ? rowp[pos + c] : 0.0f;
-    }
+    for (int c = 0; c < VEC; ++c) x[u * VEC + c] = (pos + c < c1) ? rowp[pos + c] : 0.0f;
   }
-}
-
-// Bit e of the result: element e of this thread's tile slice is in range and
-// passes the acceptance bound (key >= L, evaluated as an IEEE compare).
-template <int VEC>
-__device__ __forceinline__ uint32_t tile_flags(const float (&x)[kElems], uint32_t p0, uint32_t c1,
-                                               uint32_t L) {
-  const uint32_t t = threadIdx.x;
-  const bool on = L >= 0x00800000u;
-  const float bf = key_floor(L);
-  uint32_t f = 0;
-#pragma unroll
-  for (int u = 0; u < kElems / VEC; ++u) {
-#pragma unroll
-    for (int c = 0; c < VEC; ++c) {
-      const uint32_t pos = p0 + (uint32_t)u * (kBlock * VEC) + t * VEC + c;
-      const bool a = pos < c1 && (!on || x[u * VEC + c] >= bf);
-      f |= (a ? 1u : 0u) << (u * VEC + c);
-    }
-  }
-  return f;
 }
 
 // Per-wave counts of accepted elements for each load slot go through LDS
-// (double-buffered by par); returns the tile total and each slot's offset for
-// this wave.
+// (double-buffered by par); returns the tile total and this wave's offset
+// for each slot.
 template <int KMAX, int VEC>
-__device__ __forceinline__ uint32_t tile_exchange(Smem<KMAX>& sm, uint32_t f, int& par,
+__device__ __forceinline__ uint32_t tile_exchange(Smem<KMAX>& sm, const bool (&a)[kElems], int& par,
                                                   uint32_t (&off)[kElems / VEC]) {
   constexpr int NL = kElems / VEC;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
   for (int u = 0; u < NL; ++u) {
     uint32_t c = 0;
 #pragma unroll
-    for (int cc = 0; cc < VEC; ++cc) c += popc64(ballot((f >> (u * VEC + cc)) & 1u));
+    for (int cc = 0; cc < VEC; ++cc) c += popc64(ballot(a[u * VEC + cc]));
     if (lane == 0) sm.tile_cnt[par][u][w] = c;
   }
   __syncthreads();
@@ -364,45 +441,103 @@ __device__ __forceinline__ uint32_t tile_exchange(Smem<KMAX>& sm, uint32_t f, in
   return total;
 }
 
-template <int KMAX, int VEC>
-__device__ void stream_chunk(Smem<KMAX>& sm, const float* __restrict__ rowp, uint32_t c0, uint32_t c1,
-                             uint32_t keep, uint32_t& cnt, uint32_t& L) {
-  constexpr int NL = kElems / VEC;
-  const uint32_t t = threadIdx.x;
-  int par = 0;
-  float xa[kElems], xb[kElems];
-  load_tile<VEC>(rowp, c1, c0, xa);
-  for (uint32_t p0 = c0; p0 < c1; p0 += kTile) {
-    const bool more = p0 + kTile < c1;
-    if (more) load_tile<VEC>(rowp, c1, p0 + kTile, xb);
-    uint32_t off[NL];
-    uint32_t f = tile_flags<VEC>(xa, p0, c1, L);
-    uint32_t total = tile_exchange<KMAX, VEC>(sm, f, par, off);
-    if (cnt + total > (uint32_t)Shape<KMAX>::kCap) {
-      compact<KMAX>(sm, cnt, keep, L);
-      f = tile_flags<VEC>(xa, p0, c1, L);
-      total = tile_exchange<KMAX, VEC>(sm, f, par, off);
+template <int VEC, bool FULL>
+__device__ __forceinline__ void tile_accept(const float (&x)[kElems], uint32_t pbase, uint32_t c1, float bf,
+                                            bool (&a)[kElems]) {
+#pragma unroll
+  for (int u = 0; u < kElems / VEC; ++u) {
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) {
+      const int e = u * VEC + c;
+      const bool in = FULL || pbase + (uint32_t)u * (kBlock * VEC) + c < c1;
+      a[e] = in && x[e] >= bf;
     }
+  }
+}
+
+// Filters one tile into the candidate buffer, compacting first if the
+// tile's accepted elements would not fit.
+template <int KMAX, int VEC, bool FULL>
+__device__ __forceinline__ void process_tile(Smem<KMAX>& sm, const float (&x)[kElems], uint32_t p0, uint32_t c1,
+                                             uint32_t keep, uint32_t& cnt, uint32_t& L, int& par) {
+  constexpr int NL = kElems / VEC;
+  const uint32_t pbase = p0 + threadIdx.x * VEC;
+  bool a[kElems];
+  uint32_t off[NL];
+  tile_accept<VEC, FULL>(x, pbase, c1, accept_floor(L), a);
+  uint32_t total = tile_exchange<KMAX, VEC>(sm, a, par, off);
+  if (cnt + total > (uint32_t)Shape<KMAX>::kCap) {
+    L = compact<KMAX>(sm, cnt, keep, L);
+    cnt = keep;
+    tile_accept<VEC, FULL>(x, pbase, c1, accept_floor(L), a);
+    total = tile_exchange<KMAX, VEC>(sm, a, par, off);
+  }
+  if (total != 0) {
 #pragma unroll
     for (int u = 0; u < NL; ++u) {
       uint32_t r = cnt + off[u];
 #pragma unroll
-      for (int c = 0; c < VEC; ++c) r += lanes_below(ballot((f >> (u * VEC + c)) & 1u));
+      for (int c = 0; c < VEC; ++c) r += lanes_below(ballot(a[u * VEC + c]));
 #pragma unroll
       for (int c = 0; c < VEC; ++c) {
         const int e = u * VEC + c;
-        if ((f >> e) & 1u) {
-          sm.key[r] = ord_key(__float_as_uint(xa[e]));
-          sm.idx[r] = p0 + (uint32_t)u * (kBlock * VEC) + t * VEC + c;
-          ++r;
+        if (a[e]) {
+          const uint32_t key = ord_key(__float_as_uint(x[e]));
+          sm.key[r] = key;
+          sm.idx[r] = pbase + (uint32_t)u * (kBlock * VEC) + c;
+          atomicAdd(&sm.hist1[key >> 21], 1u);
         }
+        r += a[e] ? 1u : 0u;
       }
     }
-    cnt += total;
-    if (more) {
+  }
+  cnt += total;
+}
+
+// Streams [c0, c1) through the filter.  Full tiles come through a ring of
+// kPrefetch register buffers: the load for tile j + kPrefetch - 1 is issued
+// before tile j is processed, so about (kPrefetch - 1) tiles per workgroup
+// are in flight.  Prefetch addresses past the last full tile are clamped to
+// it (a cache hit), which keeps the load pattern identical every iteration.
+// The partial last tile is loaded with per-element bounds checks.
+template <int KMAX, int VEC>
+__device__ void stream_chunk(Smem<KMAX>& sm, const float* __restrict__ rowp, uint32_t c0, uint32_t c1,
+                             uint32_t keep, uint32_t& cnt, uint32_t& L) {
+  constexpr int PF = kPrefetch;
+  const uint32_t F = (c1 - c0) / kTile;  // full tiles
+  int par = 0;
+  if (F > 0) {
+    float buf[PF][kElems];
 #pragma unroll
-      for (int e = 0; e < kElems; ++e) xa[e] = xb[e];
+    for (int s = 0; s < PF - 1; ++s) {
+      load_full<VEC>(rowp, c0 + ((uint32_t)s < F ? (uint32_t)s : F - 1) * kTile, buf[s]);
+      __builtin_amdgcn_sched_barrier(0);  // keep tiles in issue order: waits then retire oldest first
     }
+    // Whole rounds of PF tiles: one uniform back edge, so the compiler's
+    // load-counter waits stay exact (retire only the tile about to be used).
+    const uint32_t Fr = F - F % PF;
+    for (uint32_t j0 = 0; j0 < Fr; j0 += PF) {
+#pragma unroll
+      for (int slot = 0; slot < PF; ++slot) {
+        const uint32_t j = j0 + slot;
+        const uint32_t jn = j + PF - 1 < F ? j + PF - 1 : F - 1;
+        load_full<VEC>(rowp, c0 + jn * kTile, buf[(slot + PF - 1) % PF]);
+        __builtin_amdgcn_sched_barrier(0);
+        process_tile<KMAX, VEC, true>(sm, buf[slot], c0 + j * kTile, c1, keep, cnt, L, par);
+      }
+    }
+    // The last F % PF full tiles are already in buf[0..]: no more loads.
+#pragma unroll
+    for (int slot = 0; slot < PF - 1; ++slot) {
+      const uint32_t j = Fr + slot;
+      if (j < F) process_tile<KMAX, VEC, true>(sm, buf[slot], c0 + j * kTile, c1, keep, cnt, L, par);
+    }
+  }
+  const uint32_t pt = c0 + F * kTile;
+  if (pt < c1) {
+    float x[kElems];
+    load_tail<VEC>(rowp, c1, pt, x);
+    process_tile<KMAX, VEC, false>(sm, x, pt, c1, keep, cnt, L, par);
   }
   __syncthreads();
 }
@@ -418,15 +553,21 @@ __device__ __forceinline__ void write_all_then_pad(int32_t* out, int64_t n, int 
   for (int i = threadIdx.x; i < K; i += kBlock) out[i] = i < n ? i : -1;
 }
 
+template <int KMAX>
+__device__ __forceinline__ void zero_histograms(Smem<KMAX>& sm) {
+  for (int i = threadIdx.x; i < kBins; i += kBlock) {
+    sm.hist1[i] = 0u;
+    sm.hist2[i] = 0u;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // One workgroup per row, persistent over rows.
 // ---------------------------------------------------------------------------
 template <int KMAX, int VEC>
 __global__ void __launch_bounds__(kBlock) topk_single_kernel(KernelParams p) {
   __shared__ Smem<KMAX> sm;
-  constexpr int S = Shape<KMAX>::kSlots;
-  const int t = threadIdx.x;
-  for (int i = t; i < kBins; i += kBlock) sm.hist[i] = 0u;
+  zero_histograms(sm);
   __syncthreads();
   const uint32_t K = (uint32_t)p.K;
   for (int row = blockIdx.x; row < p.num_rows; row += gridDim.x) {
@@ -439,11 +580,7 @@ __global__ void __launch_bounds__(kBlock) topk_single_kernel(KernelParams p) {
     const float* rowp = p.scores + (int64_t)row * p.row_stride;
     uint32_t cnt = 0, L = 0;
     stream_chunk<KMAX, VEC>(sm, rowp, 0u, (uint32_t)n, K, cnt, L);
-    uint32_t k[S], ix[S];
-    load_buffer<KMAX>(sm, cnt, k, ix);
-    const Sel s = radix_select<KMAX>(sm, k, cnt, K);
-    ordered_emit<KMAX>(sm, k, ix, cnt, s, 0u, 0u, s.krem, out, K);
-    __syncthreads();
+    final_select<KMAX>(sm, cnt, K, out);
   }
 }
 
@@ -473,7 +610,7 @@ __device__ void group_barrier(uint32_t* ctr, uint32_t target, uint32_t spin_limi
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
-// Adds the LDS histogram into a workspace histogram (non-zero bins only) and
+// Adds an LDS histogram into a workspace histogram (non-zero bins only) and
 // zeroes the LDS copy.
 __device__ __forceinline__ void merge_hist(uint32_t* lds_hist, uint32_t* gh) {
   for (int i = threadIdx.x; i < kBins; i += kBlock) {
@@ -499,7 +636,7 @@ __global__ void __launch_bounds__(kBlock) topk_multi_kernel(KernelParams p) {
   __shared__ Smem<KMAX> sm;
   constexpr int S = Shape<KMAX>::kSlots;
   constexpr int CAP = Shape<KMAX>::kCap;
-  const int t = threadIdx.x, lane = t & 63;
+  const int t = threadIdx.x;
   const int G = p.wg_per_row;
   const int row = blockIdx.x / G;
   const int g = blockIdx.x - row * G;
@@ -524,7 +661,7 @@ __global__ void __launch_bounds__(kBlock) topk_multi_kernel(KernelParams p) {
   uint32_t* h2 = reinterpret_cast<uint32_t*>(blk + lay.h2);
   uint32_t* lists = reinterpret_cast<uint32_t*>(blk + lay.lists);
 
-  for (int i = t; i < kBins; i += kBlock) sm.hist[i] = 0u;
+  zero_histograms(sm);
   if (t < 8) sm.acc[t] = 0u;
   __syncthreads();
 
@@ -535,18 +672,16 @@ __global__ void __launch_bounds__(kBlock) topk_multi_kernel(KernelParams p) {
   stream_chunk<KMAX, VEC>(sm, rowp, (uint32_t)c0, (uint32_t)c1, K, cnt, L);
 
   uint32_t k[S], ix[S];
-  load_buffer<KMAX>(sm, cnt, k, ix);
+  load_owned<KMAX>(sm, k, ix);
+  const uint32_t base = (uint32_t)t * S;
 
-  // Round 1: top 11 bits.
-#pragma unroll
-  for (int j = 0; j < S; ++j)
-    if ((uint32_t)(t + j * kBlock) < cnt) atomicAdd(&sm.hist[k[j] >> 21], 1u);
-  __syncthreads();
-  merge_hist(sm.hist, h1);
+  // Round 1: the chunk's top-digit histogram (already in hist1) into the
+  // row's, then the row-wide threshold digit.
+  merge_hist(sm.hist1, h1);
   group_barrier(ctr, 1u * grow, p.spin_limit, err);
-  load_hist(sm.hist, h1);
+  load_hist(sm.hist2, h1);
   __syncthreads();
-  if (t < 64) wave_search<2048>(sm.hist, K, sm.res);
+  search<2048, true>(sm.hist2, K, sm.res);
   __syncthreads();
   uint32_t ok = sm.res[3];
   uint32_t krem = K - sm.res[1];
@@ -555,22 +690,22 @@ __global__ void __launch_bounds__(kBlock) topk_multi_kernel(KernelParams p) {
 
   // Round 2: next 11 bits of the entries in the threshold bin; publish how
   // many of this chunk's entries lie above it.
-  uint32_t n_above1 = 0;
+  uint32_t n_above = 0;
 #pragma unroll
   for (int j = 0; j < S; ++j) {
-    const bool valid = (uint32_t)(t + j * kBlock) < cnt;
+    const bool valid = base + j < cnt;
     const uint32_t km = k[j] & pmask;
-    if (valid && km == prefix) atomicAdd(&sm.hist[(k[j] >> 10) & 2047u], 1u);
-    n_above1 += popc64(ballot(valid && km > prefix));
+    if (valid && km == prefix) atomicAdd(&sm.hist2[(k[j] >> 10) & 2047u], 1u);
+    n_above += popc64(ballot(valid && km > prefix));
   }
-  wave_add(&sm.acc[0], n_above1);
+  wave_add(&sm.acc[0], n_above);
   __syncthreads();
-  merge_hist(sm.hist, h2);
+  merge_hist(sm.hist2, h2);
   if (t == 0) slots[4 * g + 0] = sm.acc[0];
   group_barrier(ctr, 2u * grow, p.spin_limit, err);
-  load_hist(sm.hist, h2);
+  load_hist(sm.hist2, h2);
   __syncthreads();
-  if (t < 64) wave_search<2048>(sm.hist, krem, sm.res);
+  search<2048, true>(sm.hist2, krem, sm.res);
   __syncthreads();
   ok &= sm.res[3];
   krem -= sm.res[1];
@@ -580,34 +715,27 @@ __global__ void __launch_bounds__(kBlock) topk_multi_kernel(KernelParams p) {
   // Round 3: publish the keys still undecided after 22 bits, in index order,
   // and the count above them.
   {
-    uint32_t n_above2 = 0;
-    uint32_t pm[S];
-    bool m[S];
+    uint32_t mine = 0;
+    n_above = 0;
 #pragma unroll
     for (int j = 0; j < S; ++j) {
-      const bool valid = (uint32_t)(t + j * kBlock) < cnt;
+      const bool valid = base + j < cnt;
       const uint32_t km = k[j] & pmask;
-      n_above2 += popc64(ballot(valid && km > prefix));
-      m[j] = valid && km == prefix;
-      const uint64_t mm = ballot(m[j]);
-      pm[j] = lanes_below(mm);
-      if (lane == 0) sm.rank_cnt[j][t >> 6] = popc64(mm);
+      mine += (valid && km == prefix) ? 1u : 0u;
+      n_above += popc64(ballot(valid && km > prefix));
     }
-    wave_add(&sm.acc[1], n_above2);
-    __syncthreads();
-    const int w = t >> 6;
-    uint32_t run = 0;
+    wave_add(&sm.acc[1], n_above);
+    uint32_t len;
+    uint32_t at = block_excl_scan(sm, mine, &len);
     uint32_t* my_list = lists + (uint64_t)g * CAP;
 #pragma unroll
     for (int j = 0; j < S; ++j) {
-      const uint4 v = *reinterpret_cast<const uint4*>(sm.rank_cnt[j]);
-      const uint32_t before = (w > 0 ? v.x : 0u) + (w > 1 ? v.y : 0u) + (w > 2 ? v.z : 0u);
-      if (m[j]) my_list[run + before + pm[j]] = k[j];
-      run += v.x + v.y + v.z + v.w;
+      const bool valid = base + j < cnt;
+      if (valid && (k[j] & pmask) == prefix) my_list[at++] = k[j];
     }
     if (t == 0) {
       slots[4 * g + 1] = sm.acc[1] - sm.acc[0];
-      slots[4 * g + 2] = run;
+      slots[4 * g + 2] = len;
     }
   }
   group_barrier(ctr, 3u * grow, p.spin_limit, err);
@@ -617,10 +745,10 @@ __global__ void __launch_bounds__(kBlock) topk_multi_kernel(KernelParams p) {
     uint32_t len = slots[4 * gg + 2];
     len = len < (uint32_t)CAP ? len : (uint32_t)CAP;
     const uint32_t* lst = lists + (uint64_t)gg * CAP;
-    for (uint32_t i = t; i < len; i += kBlock) atomicAdd(&sm.hist[lst[i] & 1023u], 1u);
+    for (uint32_t i = t; i < len; i += kBlock) atomicAdd(&sm.hist2[lst[i] & 1023u], 1u);
   }
   __syncthreads();
-  if (t < 64) wave_search<1024>(sm.hist, krem, sm.res);
+  search<1024, true>(sm.hist2, krem, sm.res);
   __syncthreads();
   ok &= sm.res[3];
   const uint32_t T = prefix | sm.res[0];
@@ -639,8 +767,8 @@ __global__ void __launch_bounds__(kBlock) topk_multi_kernel(KernelParams p) {
       }
       if (t == 0) gt_b += slots[4 * gg + 0] + slots[4 * gg + 1];
     }
-    // gt_b from lists is wave-uniform; slot counts were added on thread 0 only.
-    if (lane == 0) {
+    // List counts are wave-uniform; the slot counts were added on thread 0 only.
+    if ((t & 63) == 0) {
       if (gt_b) atomicAdd(&sm.acc[2], gt_b);
       if (eq_b) atomicAdd(&sm.acc[3], eq_b);
     }
@@ -661,14 +789,21 @@ __global__ void __launch_bounds__(kBlock) topk_multi_kernel(KernelParams p) {
       h1[i] = 0u;
       h2[i] = 0u;
     }
+    for (int gg = 0; gg < grow; ++gg) {
+      uint32_t len = slots[4 * gg + 2];
+      len = len < (uint32_t)CAP ? len : (uint32_t)CAP;
+      uint32_t* lst = lists + (uint64_t)gg * CAP;
+      for (uint32_t i = t; i < len; i += kBlock) lst[i] = 0u;
+    }
+    __syncthreads();  // every list length has been read before the slots are cleared
+    if (t < 4 * grow) slots[t] = 0u;
     if (t == 0) {
       __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(exit_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 
-  const Sel s{T, 0xffffffffu, take_eq, ok};
-  ordered_emit<KMAX>(sm, k, ix, cnt, s, gt_base, eq_base, take_eq, out, K);
+  emit_chosen<KMAX>(sm, k, ix, cnt, T, 0xffffffffu, gt_base, eq_base, take_eq, out, K);
 }
 
 // ---------------------------------------------------------------------------
