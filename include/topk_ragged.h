@@ -107,12 +107,16 @@ const char* topk_ragged_last_error(void);
 
 /* Device facts the planner uses.  occupancy_* are workgroups per CU of the
  * exact kernel instance that would run (PR #41189 page, implementation
- * notes: query the instance actually launched, not a sibling). */
+ * notes: query the instance actually launched, not a sibling).  The "16"
+ * instances keep 16-bit candidate indices (rows or chunks of at most 65536
+ * elements) and a larger candidate buffer. */
 typedef struct {
   int32_t num_cus;
-  int32_t occupancy_single;  /* one workgroup per row kernel */
-  int32_t occupancy_multi;   /* several workgroups per row kernel */
+  int32_t occupancy_single;    /* one workgroup per row kernel, 32-bit indices */
+  int32_t occupancy_multi;     /* several workgroups per row kernel, 32-bit indices */
   int32_t max_lds_per_block;
+  int32_t occupancy_single16;  /* one workgroup per row kernel, 16-bit indices */
+  int32_t occupancy_multi16;   /* several workgroups per row kernel, 16-bit indices */
 } topk_device_props;
 
 typedef enum {
@@ -123,7 +127,7 @@ typedef enum {
 
 typedef struct {
   int32_t path;           /* topk_path */
-  int32_t kmax;           /* kernel instance: K rounded up to 256/512/1024/2048 */
+  int32_t kmax;           /* largest K the kernel instance handles (TOPK_RAGGED_MAX_K) */
   int32_t vec;            /* fp32 elements per load: 4, 2 or 1 */
   int32_t block;          /* threads per workgroup */
   int32_t grid;           /* workgroups launched */
@@ -133,7 +137,7 @@ typedef struct {
   int32_t headroom;       /* slots left free when workgroups wait on each other */
   int32_t lds_bytes;      /* static LDS per workgroup */
   int32_t fell_back;      /* 1 if a requested multi plan could not be made co-resident */
-  int32_t reserved;
+  int32_t idx16;          /* 1 if the instance keeps 16-bit candidate indices */
   uint64_t workspace_bytes;
 } topk_plan;
 

@@ -31,7 +31,8 @@ EXPORTED = (
 
 class DeviceProps(ctypes.Structure):
     _fields_ = [("num_cus", ctypes.c_int32), ("occupancy_single", ctypes.c_int32),
-                ("occupancy_multi", ctypes.c_int32), ("max_lds_per_block", ctypes.c_int32)]
+                ("occupancy_multi", ctypes.c_int32), ("max_lds_per_block", ctypes.c_int32),
+                ("occupancy_single16", ctypes.c_int32), ("occupancy_multi16", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -39,11 +40,11 @@ class Plan(ctypes.Structure):
                 ("block", ctypes.c_int32), ("grid", ctypes.c_int32), ("wg_per_row", ctypes.c_int32),
                 ("chunk", ctypes.c_int64), ("resident_cap", ctypes.c_int32),
                 ("headroom", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
-                ("fell_back", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("fell_back", ctypes.c_int32), ("idx16", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_uint64)]
 
     def as_dict(self) -> dict:
-        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+        return {name: getattr(self, name) for name, _ in self._fields_}
 
 
 class Overrides(ctypes.Structure):
@@ -128,8 +129,11 @@ def _ov_ptr(ov: Overrides | None):
 
 def plan_for_props(num_cus: int, occupancy_single: int, occupancy_multi: int, num_rows: int,
                    row_stride: int, K: int, vec_allowed: int = 4, max_lds_per_block: int = 163840,
+                   occupancy_single16: int | None = None, occupancy_multi16: int | None = None,
                    **overrides) -> dict:
-    props = DeviceProps(num_cus, occupancy_single, occupancy_multi, max_lds_per_block)
+    props = DeviceProps(num_cus, occupancy_single, occupancy_multi, max_lds_per_block,
+                        occupancy_single if occupancy_single16 is None else occupancy_single16,
+                        occupancy_multi if occupancy_multi16 is None else occupancy_multi16)
     plan = Plan()
     ov = Overrides.make(**overrides)
     rc = load().topk_ragged_plan(ctypes.byref(props), num_rows, row_stride, K, vec_allowed,

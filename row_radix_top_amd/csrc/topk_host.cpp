@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -26,13 +27,6 @@ int fail(int code, const std::string& msg) {
 
 constexpr int64_t kDefaultMinChunk = 8192;
 
-int kmax_for(int K) {
-  if (K <= 256) return 256;
-  if (K <= 512) return 512;
-  if (K <= 1024) return 1024;
-  return 2048;
-}
-
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool verbose() {
@@ -46,9 +40,9 @@ bool verbose() {
 std::string describe(const topk_plan& p) {
   char buf[512];
   std::snprintf(buf, sizeof(buf),
-                "path=%d kmax=%d vec=%d block=%d grid=%d wg_per_row=%d chunk=%lld "
+                "path=%d idx16=%d vec=%d block=%d grid=%d wg_per_row=%d chunk=%lld "
                 "resident_cap=%d headroom=%d lds=%d fell_back=%d workspace=%llu",
-                p.path, p.kmax, p.vec, p.block, p.grid, p.wg_per_row, (long long)p.chunk,
+                p.path, p.idx16, p.vec, p.block, p.grid, p.wg_per_row, (long long)p.chunk,
                 p.resident_cap, p.headroom, p.lds_bytes, p.fell_back,
                 (unsigned long long)p.workspace_bytes);
   return buf;
@@ -61,7 +55,7 @@ std::string describe(const topk_plan& p) {
 struct DevInfo {
   int num_cus = 0;
   int max_lds_block = 0;
-  std::map<std::tuple<int, int, int>, int> occ;  // (path, kmax, vec) -> WGs per CU
+  std::map<std::tuple<int, int, int>, int> occ;  // (path, vec, idx16) -> WGs per CU
 };
 
 std::mutex g_mu;
@@ -91,9 +85,9 @@ int device_info(int dev, DevInfo** out) {
 }
 
 // Occupancy of the exact instance that will be launched.
-int occupancy(int dev, DevInfo* d, int path, int kmax, int vec, int* occ) {
+int occupancy(int dev, DevInfo* d, int path, int vec, bool idx16, int* occ) {
   std::lock_guard<std::mutex> lk(g_mu);
-  const auto key = std::make_tuple(path, kmax, vec);
+  const auto key = std::make_tuple(path, vec, idx16 ? 1 : 0);
   auto it = d->occ.find(key);
   if (it != d->occ.end()) {
     *occ = it->second;
@@ -104,12 +98,12 @@ int occupancy(int dev, DevInfo* d, int path, int kmax, int vec, int* occ) {
   if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
   int o = 0;
   if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, rrt::kernel_ptr(path, kmax, vec), rrt::kBlock, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, rrt::kernel_ptr(path, vec, idx16), rrt::kBlock, 0);
   if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
   if (e != hipSuccess) {
     char buf[256];
-    std::snprintf(buf, sizeof(buf), "occupancy query failed (path=%d kmax=%d vec=%d): %s", path, kmax,
-                  vec, hipGetErrorString(e));
+    std::snprintf(buf, sizeof(buf), "occupancy query failed (path=%d vec=%d idx16=%d): %s", path, vec,
+                  idx16 ? 1 : 0, hipGetErrorString(e));
     return fail(TOPK_EDEVICE, buf);
   }
   d->occ[key] = o;
@@ -137,16 +131,18 @@ int chosen_vec(int vec_allowed, const topk_overrides* ov, int* vec) {
   return TOPK_OK;
 }
 
-// Fills props for the instances (kmax, vec) of both paths on device dev.
-int real_props(int dev, int kmax, int vec, topk_device_props* props) {
+// Fills props for the load width vec of every kernel instance on device dev.
+int real_props(int dev, int vec, topk_device_props* props) {
   DevInfo* d = nullptr;
   int rc = device_info(dev, &d);
   if (rc != TOPK_OK) return rc;
   std::memset(props, 0, sizeof(*props));
   props->num_cus = d->num_cus;
   props->max_lds_per_block = d->max_lds_block;
-  rc = occupancy(dev, d, 1, kmax, vec, &props->occupancy_single);
-  if (rc == TOPK_OK) rc = occupancy(dev, d, 2, kmax, vec, &props->occupancy_multi);
+  rc = occupancy(dev, d, 1, vec, false, &props->occupancy_single);
+  if (rc == TOPK_OK) rc = occupancy(dev, d, 2, vec, false, &props->occupancy_multi);
+  if (rc == TOPK_OK) rc = occupancy(dev, d, 1, vec, true, &props->occupancy_single16);
+  if (rc == TOPK_OK) rc = occupancy(dev, d, 2, vec, true, &props->occupancy_multi16);
   return rc;
 }
 
@@ -174,7 +170,7 @@ int plan_for_call(const float* scores, int32_t num_rows, int64_t row_stride, int
   rc = stream_device(stream, &dev);
   if (rc != TOPK_OK) return rc;
   topk_device_props props;
-  rc = real_props(dev, kmax_for(K), vec, &props);
+  rc = real_props(dev, vec, &props);
   if (rc != TOPK_OK) return rc;
   if (dev_out) *dev_out = dev;
   return topk_ragged_plan(&props, num_rows, row_stride, K, va, ov, plan);
@@ -197,7 +193,7 @@ int topk_ragged_plan(const topk_device_props* props, int32_t num_rows, int64_t r
   rc = chosen_vec(vec_allowed, ov, &vec);
   if (rc != TOPK_OK) return rc;
 
-  plan->kmax = kmax_for(K);
+  plan->kmax = TOPK_RAGGED_MAX_K;
   plan->vec = vec;
   plan->block = rrt::kBlock;
   plan->wg_per_row = 1;
@@ -215,7 +211,9 @@ int topk_ragged_plan(const topk_device_props* props, int32_t num_rows, int64_t r
   // the device.
   const bool long_rows = row_stride > TOPK_RAGGED_RADIX_THRESHOLD;
   if (want == TOPK_PATH_MULTI || (want == 0 && long_rows)) {
-    const int occ = props->occupancy_multi;
+    // Size with the less resident of the two instances; the chunk length then
+    // picks the instance (16-bit indices when a chunk fits them).
+    const int occ = std::min(props->occupancy_multi, props->occupancy_multi16);
     if (occ < 1) {
       if (want == TOPK_PATH_MULTI) return fail(TOPK_EDEVICE, "multi-workgroup kernel cannot be resident");
     } else {
@@ -261,14 +259,16 @@ int topk_ragged_plan(const topk_device_props* props, int32_t num_rows, int64_t r
       if (usable) {
         const int64_t grid = (int64_t)num_rows * G;
         if (grid <= avail) {
-          const rrt::GroupLayout lay = rrt::group_layout((int)G, rrt::cap_of(plan->kmax));
+          const bool i16 = chunk <= rrt::kIdx16Limit;
+          const rrt::GroupLayout lay = rrt::group_layout((int)G, rrt::cap_of(i16));
           plan->path = TOPK_PATH_MULTI;
+          plan->idx16 = i16 ? 1 : 0;
           plan->wg_per_row = (int)G;
           plan->chunk = chunk;
           plan->grid = (int)grid;
           plan->resident_cap = (int)cap;
           plan->headroom = (int)headroom;
-          plan->lds_bytes = rrt::lds_bytes_of(2, plan->kmax);
+          plan->lds_bytes = rrt::lds_bytes_of(i16);
           plan->workspace_bytes = rrt::kWsHeader + (uint64_t)num_rows * lay.bytes;
           return TOPK_OK;
         }
@@ -281,7 +281,8 @@ int topk_ragged_plan(const topk_device_props* props, int32_t num_rows, int64_t r
     }
   }
 
-  const int occ = props->occupancy_single;
+  const bool i16 = row_stride <= rrt::kIdx16Limit;
+  const int occ = i16 ? props->occupancy_single16 : props->occupancy_single;
   if (occ < 1) return fail(TOPK_EDEVICE, "single-workgroup kernel cannot be resident");
   const int64_t cap = (int64_t)props->num_cus * occ;
   int64_t grid = num_rows < cap ? num_rows : cap;
@@ -292,7 +293,8 @@ int topk_ragged_plan(const topk_device_props* props, int32_t num_rows, int64_t r
   plan->grid = (int)grid;
   plan->resident_cap = (int)cap;
   plan->headroom = 0;
-  plan->lds_bytes = rrt::lds_bytes_of(1, plan->kmax);
+  plan->idx16 = i16 ? 1 : 0;
+  plan->lds_bytes = rrt::lds_bytes_of(i16);
   plan->workspace_bytes = 0;
   return TOPK_OK;
 }
@@ -368,7 +370,7 @@ int topk_ragged_ex(const float* scores, int64_t row_stride, const int32_t* lengt
   kp.row_stride = row_stride;
   kp.chunk = plan.chunk;
   kp.group_bytes = plan.path == TOPK_PATH_MULTI
-                       ? rrt::group_layout(plan.wg_per_row, rrt::cap_of(plan.kmax)).bytes
+                       ? rrt::group_layout(plan.wg_per_row, rrt::cap_of(plan.idx16 != 0)).bytes
                        : 0;
   kp.num_rows = num_rows;
   kp.K = K;
@@ -378,7 +380,7 @@ int topk_ragged_ex(const float* scores, int64_t row_stride, const int32_t* lengt
   if (verbose()) std::fprintf(stderr, "[topk_ragged] rows=%d stride=%lld K=%d %s\n", num_rows,
                               (long long)row_stride, K, describe(plan).c_str());
   void* args[] = {&kp};
-  const void* fn = rrt::kernel_ptr(plan.path, plan.kmax, plan.vec);
+  const void* fn = rrt::kernel_ptr(plan.path, plan.vec, plan.idx16 != 0);
   hipError_t e = hipLaunchKernel(fn, dim3(plan.grid), dim3(plan.block), args, 0, stream);
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) {

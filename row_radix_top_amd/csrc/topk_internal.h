@@ -14,12 +14,17 @@ constexpr int kTile = kBlock * kElems;      // 2048 elements streamed per tile
 constexpr int kBins = 2048;                 // 11-bit radix digit
 constexpr int kPrefetch = 4;                // register ring of tiles per thread
 constexpr int kMaxGroup = 64;               // most workgroups that may share a row
+constexpr int kMaxK = 2048;
 constexpr uint32_t kDefaultSpin = 1u << 24; // polls before a cooperative wait gives up
 
-// Candidate buffer capacity of a kernel instance: room for the KMAX kept
-// entries plus one full tile, so a tile always fits after a compaction;
-// rounded up to 1024 so every thread owns a whole number of uint4s.
-constexpr int cap_of(int kmax) { return (kmax + kTile + 1023) / 1024 * 1024; }
+// Candidate buffer capacity.  It must hold K = 2048 kept entries plus one full
+// tile, so a tile always fits after a compaction.  With 16-bit indices (rows
+// or chunks of at most 65536 elements) an entry takes 6 bytes and the buffer
+// holds 5120 entries in less LDS than 4096 entries with 32-bit indices; the
+// slack lets most compactions stop at the top digit.  The 16-bit layout fits
+// four workgroups in a CU's 160 KB of LDS, the 32-bit one three.
+constexpr int kIdx16Limit = 65536;
+constexpr int cap_of(bool idx16) { return idx16 ? 5120 : 4096; }
 
 // Workspace: a 256-byte header (word 0: error bits) followed by one block per
 // row of the multi-workgroup path.
@@ -65,9 +70,9 @@ struct KernelParams {
 };
 
 // Kernel lookup for the host side.  path: 1 single, 2 multi.
-const void* kernel_ptr(int path, int kmax, int vec);
+const void* kernel_ptr(int path, int vec, bool idx16);
 const void* zero_kernel_ptr();
 const void* keys_kernel_ptr();
-int lds_bytes_of(int path, int kmax);
+int lds_bytes_of(bool idx16);
 
 }  // namespace rrt

@@ -25,9 +25,10 @@
 //   of entries kept from it).
 //
 // * Radix select.  Later digits (11 then 10 bits) are histogrammed with LDS
-//   atomics over the register-held buffer; one wavefront scans a histogram
-//   from the top with DPP prefix sums to find the threshold digit.  Ties at
-//   the final 32-bit key go to the lower buffer position, the lower index.
+//   atomics over the register-held buffer.  Every wavefront scans a histogram
+//   from the top with DPP prefix sums and finds the threshold digit itself,
+//   so a search costs no barrier.  Ties at the final 32-bit key go to the
+//   lower buffer position, the lower index.
 //
 // * Ordered emit.  Each thread owns a contiguous slice of the buffer; one
 //   workgroup prefix sum of the per-thread (greater, equal) counts gives every
@@ -36,7 +37,8 @@
 //
 // * Multi-workgroup rows.  G workgroups each filter a contiguous chunk, then
 //   merge digit histograms in the workspace with agent-scope atomics across
-//   three cooperative rounds (an arrival-counter barrier each), publish the
+//   three cooperative rounds (an arrival-counter barrier each; all workspace
+//   traffic is atomic, so no cache-wide fences are needed), publish the
 //   few keys left undecided after 22 bits, and derive their output offsets
 //   from per-workgroup counts.  The last workgroup to leave zeroes everything
 //   the row touched, so the workspace is all-zero when the kernel ends (the
@@ -51,6 +53,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "topk_internal.h"
 
@@ -81,10 +85,7 @@ __device__ __forceinline__ float accept_floor(uint32_t L) {
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-// Pointers into LDS (address space 3), so out-of-line helpers address it with
-// ds_* instructions directly.
-typedef __attribute__((address_space(3))) uint32_t lds_u32;
-typedef __attribute__((address_space(3))) u32x4 lds_u4;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
@@ -116,40 +117,47 @@ __device__ __forceinline__ uint32_t lane_value(uint32_t v, int lane) {
 // Shared memory of one workgroup
 // ---------------------------------------------------------------------------
 
-template <int KMAX>
+template <bool I16>
 struct Shape {
-  static constexpr int kCap = cap_of(KMAX);
+  static constexpr int kCap = cap_of(I16);
   static constexpr int kSlots = kCap / kBlock;  // buffer entries owned per thread
-  static_assert(kCap % kBlock == 0 && kSlots % 4 == 0, "capacity must tile the workgroup in uint4s");
+  using Idx = typename std::conditional<I16, uint16_t, uint32_t>::type;
+  static_assert(kCap % kBlock == 0 && kSlots % 4 == 0, "capacity must tile the workgroup in aligned runs");
   static_assert(kCap < 65536, "packed 16-bit counts");
+  static_assert(kCap >= kMaxK + kTile, "a tile must fit after a compaction");
 };
 
-template <int KMAX>
+template <bool I16>
 struct __align__(16) Smem {
-  uint32_t key[Shape<KMAX>::kCap];  // candidate keys, index order
-  uint32_t idx[Shape<KMAX>::kCap];  // their column indices
-  uint32_t hist1[kBins];            // top-digit histogram of the buffer, kept current
-  uint32_t hist2[kBins];            // scratch histogram for later digits (zero between uses)
+  uint32_t key[Shape<I16>::kCap];                 // candidate keys, index order
+  typename Shape<I16>::Idx idx[Shape<I16>::kCap];  // their indices, relative to the chunk start
+  uint32_t hist1[kBins];                          // top-digit histogram of the buffer, kept current
   uint32_t tile_cnt[2][kElems][kWaves];
   uint32_t wsum[kWaves];
-  uint32_t res[4];
-  uint32_t acc[8];
+  uint32_t acc[16];
 };
 
 // ---------------------------------------------------------------------------
-// Threshold search: wavefront 0 finds the bin holding the krem-th largest
-// entry, counting down from the top bin; with ZERO it leaves the histogram
-// zeroed.  res = {bin, entries in bins above it, entries in the bin, ok}.
-// Kept out of line: inlined, its per-lane LDS addresses are hoisted out of
-// the row loop and pinned in registers for the whole kernel.
+// Threshold search.  Every wavefront of the workgroup runs it on the same
+// histogram and gets the same wave-uniform answer: the bin holding the
+// krem-th largest entry, counting down from the top bin, the number of
+// entries in bins above it and in the bin.  No barrier is needed to share the
+// result.  The lane id goes through an empty asm statement so the compiler
+// cannot hoist the per-lane LDS addresses out of the row loop and pin them in
+// registers for the whole kernel.
 // ---------------------------------------------------------------------------
-template <int NB, bool ZERO>
-__device__ __noinline__ void wave_search(lds_u32* hist, uint32_t krem, lds_u32* res) {
+struct Found {
+  uint32_t bin, above, in_bin, ok;
+};
+
+template <int NB>
+__device__ __forceinline__ Found wave_find(const uint32_t* hist, uint32_t krem) {
   constexpr int kPer = NB / 64;  // bins per lane-group: 32 or 16
   constexpr int kVec = kPer / 4;
-  const int lane = threadIdx.x & 63;
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
   // Lane l owns group 63 - l, so lane order is descending bin order.
-  lds_u4* grp = (lds_u4*)(hist + (63 - lane) * kPer);
+  const u32x4* grp = reinterpret_cast<const u32x4*>(hist + (63 - lane) * kPer);
   uint32_t s = 0;
 #pragma unroll
   for (int c = 0; c < kVec; ++c) {
@@ -158,45 +166,34 @@ __device__ __noinline__ void wave_search(lds_u32* hist, uint32_t krem, lds_u32* 
   }
   const uint32_t incl = wave_incl_scan(s);
   const uint64_t reach = ballot(incl >= krem);
+  Found f;
   if (reach == 0) {  // fewer than krem entries: inconsistent histogram
-    if (lane == 0) {
-      res[0] = 0u;
-      res[1] = 0u;
-      res[2] = lane_value(incl, 63);
-      res[3] = 0u;
-    }
-  } else {
-    // The first lane whose running count reaches krem owns the threshold
-    // group; its bins are scanned by as many lanes, top bin first.
-    const int lc = __builtin_ctzll(reach);
-    const uint32_t before = lane_value(incl, lc) - lane_value(s, lc);
-    const int qc = 63 - lc;
-    const uint32_t v = lane < kPer ? hist[qc * kPer + (kPer - 1 - lane)] : 0u;
-    const uint32_t in2 = wave_incl_scan(v) + before;
-    const uint64_t reach2 = ballot(lane < kPer && in2 >= krem);
-    const int l2 = __builtin_ctzll(reach2);
-    if (lane == l2) {
-      res[0] = (uint32_t)(qc * kPer + (kPer - 1 - l2));
-      res[1] = in2 - v;
-      res[2] = v;
-      res[3] = 1u;
-    }
+    f.bin = 0u;
+    f.above = 0u;
+    f.in_bin = lane_value(incl, 63);
+    f.ok = 0u;
+    return f;
   }
-  if (ZERO) {
-#pragma unroll
-    for (int c = 0; c < kVec; ++c) grp[(c + lane) & (kVec - 1)] = u32x4{0u, 0u, 0u, 0u};
-  }
-}
-
-template <int NB, bool ZERO>
-__device__ __forceinline__ void search(uint32_t* hist, uint32_t krem, uint32_t* res) {
-  if (threadIdx.x < 64) wave_search<NB, ZERO>((lds_u32*)hist, krem, (lds_u32*)res);
+  // The first lane whose running count reaches krem owns the threshold group;
+  // its bins are scanned by as many lanes, top bin first.
+  const int lc = __builtin_ctzll(reach);
+  const uint32_t before = lane_value(incl, lc) - lane_value(s, lc);
+  const int qc = 63 - lc;
+  const uint32_t v = lane < kPer ? hist[qc * kPer + (kPer - 1 - lane)] : 0u;
+  const uint32_t in2 = wave_incl_scan(v) + before;
+  const uint64_t reach2 = ballot(lane < kPer && in2 >= krem);
+  const int l2 = __builtin_ctzll(reach2);
+  f.bin = (uint32_t)(qc * kPer + (kPer - 1 - l2));
+  f.in_bin = lane_value(v, l2);
+  f.above = lane_value(in2, l2) - f.in_bin;
+  f.ok = 1u;
+  return f;
 }
 
 // Exclusive prefix sum of v over the workgroup in thread order; *total gets
 // the sum.  Contains one barrier.
-template <int KMAX>
-__device__ __forceinline__ uint32_t block_excl_scan(Smem<KMAX>& sm, uint32_t v, uint32_t* total) {
+template <bool I16>
+__device__ __forceinline__ uint32_t block_excl_scan(Smem<I16>& sm, uint32_t v, uint32_t* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const uint32_t incl = wave_incl_scan(v);
   if (lane == 63) sm.wsum[w] = incl;
@@ -218,93 +215,139 @@ struct Sel {
   uint32_t ok;
   uint32_t b1;      // threshold top digit
   uint32_t krem1;   // entries taken from bin b1
+  uint32_t used2;   // hist1 was reused for a later digit
 };
 
-// Thread t owns buffer positions [t*S, t*S + S); loads keys and indices.
-template <int KMAX>
-__device__ __forceinline__ void load_owned(const Smem<KMAX>& sm, uint32_t (&k)[Shape<KMAX>::kSlots],
-                                           uint32_t (&ix)[Shape<KMAX>::kSlots]) {
-  constexpr int S = Shape<KMAX>::kSlots;
+// Thread t owns buffer positions [t*S, t*S + S).
+template <bool I16>
+__device__ __forceinline__ void load_keys(const Smem<I16>& sm, uint32_t (&k)[Shape<I16>::kSlots]) {
+  constexpr int S = Shape<I16>::kSlots;
   const uint32_t base = threadIdx.x * S;
 #pragma unroll
   for (int q = 0; q < S / 4; ++q) {
     const u32x4 a = *reinterpret_cast<const u32x4*>(&sm.key[base + 4 * q]);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(&sm.idx[base + 4 * q]);
     k[4 * q + 0] = a.x;
     k[4 * q + 1] = a.y;
     k[4 * q + 2] = a.z;
     k[4 * q + 3] = a.w;
-    ix[4 * q + 0] = b.x;
-    ix[4 * q + 1] = b.y;
-    ix[4 * q + 2] = b.z;
-    ix[4 * q + 3] = b.w;
   }
 }
 
-// The keep best of the cnt buffer entries (keys in registers, contiguous
-// ownership): those with (key & pmask) > prefix plus the first krem with
-// (key & pmask) == prefix.  hist1 must be the top-digit histogram of the
-// buffer; it is read, not changed.  hist2 is left zeroed.  keep <= cnt.
-template <int KMAX>
-__device__ Sel select_keep(Smem<KMAX>& sm, const uint32_t (&k)[Shape<KMAX>::kSlots], uint32_t cnt,
-                           uint32_t keep) {
-  constexpr int S = Shape<KMAX>::kSlots;
+template <bool I16>
+__device__ __forceinline__ void load_idx(const Smem<I16>& sm, uint32_t (&ix)[Shape<I16>::kSlots]) {
+  constexpr int S = Shape<I16>::kSlots;
   const uint32_t base = threadIdx.x * S;
+  if constexpr (I16) {
+#pragma unroll
+    for (int q = 0; q < S / 4; ++q) {
+      const u32x2 a = *reinterpret_cast<const u32x2*>(&sm.idx[base + 4 * q]);
+      ix[4 * q + 0] = a.x & 0xffffu;
+      ix[4 * q + 1] = a.x >> 16;
+      ix[4 * q + 2] = a.y & 0xffffu;
+      ix[4 * q + 3] = a.y >> 16;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < S / 4; ++q) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(&sm.idx[base + 4 * q]);
+      ix[4 * q + 0] = a.x;
+      ix[4 * q + 1] = a.y;
+      ix[4 * q + 2] = a.z;
+      ix[4 * q + 3] = a.w;
+    }
+  }
+}
+
+// Histogram (into hist1, which must be zero) of one more digit over the
+// entries matching the decided prefix.
+template <bool I16, int SHIFT, uint32_t DMASK>
+__device__ __forceinline__ void digit_hist(Smem<I16>& sm, const uint32_t (&k)[Shape<I16>::kSlots], uint32_t cnt,
+                                           uint32_t prefix, uint32_t pmask) {
+  constexpr int S = Shape<I16>::kSlots;
+  const uint32_t base = threadIdx.x * S;
+#pragma unroll
+  for (int j = 0; j < S; ++j)
+    if (base + j < cnt && (k[j] & pmask) == prefix) atomicAdd(&sm.hist1[(k[j] >> SHIFT) & DMASK], 1u);
+}
+
+template <bool I16>
+__device__ __forceinline__ void clear_hist(Smem<I16>& sm) {
+  for (int i = threadIdx.x; i < kBins; i += kBlock) sm.hist1[i] = 0u;
+}
+
+// The keep best of the cnt buffer entries (keys in registers): those with
+// (key & pmask) > prefix plus the first krem with (key & pmask) == prefix.
+// hist1 must be the top-digit histogram of the buffer.  Later digits reuse
+// hist1 as scratch (used2 = 1): it then no longer describes the buffer.
+// keep <= cnt.
+template <bool I16>
+__device__ Sel select_keep(Smem<I16>& sm, const uint32_t (&k)[Shape<I16>::kSlots], uint32_t cnt,
+                           uint32_t keep) {
   Sel r;
-  search<2048, false>(sm.hist1, keep, sm.res);
-  __syncthreads();
-  r.b1 = sm.res[0];
-  r.ok = sm.res[3];
-  r.krem = keep - sm.res[1];
+  const Found f1 = wave_find<2048>(sm.hist1, keep);
+  r.b1 = f1.bin;
+  r.ok = f1.ok;
+  r.krem = keep - f1.above;
   r.krem1 = r.krem;
-  r.prefix = r.b1 << 21;
+  r.prefix = f1.bin << 21;
   r.pmask = 0xffe00000u;
-  uint32_t in_bin = sm.res[2];
-#pragma unroll
-  for (int pass = 1; pass < 3; ++pass) {
-    if (in_bin == r.krem) break;  // every entry of the bin is taken
-    const int shift = pass == 1 ? 10 : 0;
-    const uint32_t dmask = pass == 1 ? 2047u : 1023u;
-#pragma unroll
-    for (int j = 0; j < S; ++j)
-      if (base + j < cnt && (k[j] & r.pmask) == r.prefix) atomicAdd(&sm.hist2[(k[j] >> shift) & dmask], 1u);
+  r.used2 = 0u;
+  if (f1.in_bin != r.krem) {
+    __syncthreads();  // every wave has read hist1
+    clear_hist(sm);
     __syncthreads();
-    if (pass == 1)
-      search<2048, true>(sm.hist2, r.krem, sm.res);
-    else
-      search<1024, true>(sm.hist2, r.krem, sm.res);
+    digit_hist<I16, 10, 2047u>(sm, k, cnt, r.prefix, r.pmask);
     __syncthreads();
-    r.ok &= sm.res[3];
-    r.krem -= sm.res[1];
-    r.prefix |= sm.res[0] << shift;
-    r.pmask |= dmask << shift;
-    in_bin = sm.res[2];
+    const Found f2 = wave_find<2048>(sm.hist1, r.krem);
+    r.used2 = 1u;
+    r.ok &= f2.ok;
+    r.krem -= f2.above;
+    r.prefix |= f2.bin << 10;
+    r.pmask = 0xfffffc00u;
+    if (f2.in_bin != r.krem) {
+      __syncthreads();
+      clear_hist(sm);
+      __syncthreads();
+      digit_hist<I16, 0, 1023u>(sm, k, cnt, r.prefix, r.pmask);
+      __syncthreads();
+      const Found f3 = wave_find<1024>(sm.hist1, r.krem);
+      r.ok &= f3.ok;
+      r.krem -= f3.above;
+      r.prefix |= f3.bin;
+      r.pmask = 0xffffffffu;
+    }
   }
   return r;
 }
+
+// After-emit bookkeeping of hist1, done between the emit barrier and the
+// next use: kPostCoarse / kPostCompact leave it describing the kept entries,
+// kPostFinal clears it for the next row.
+enum PostEmit { kPostNone = 0, kPostCompact = 1, kPostFinal = 2, kPostCoarse = 3 };
 
 // Writes the chosen entries in buffer order.  An entry is chosen if
 // (key & pmask) > prefix, or if it equals prefix and fewer than take_eq
 // equal entries precede it (gt_base / eq_base count greater / equal entries
 // of earlier chunks of the row).  Its rank = earlier greater entries +
 // min(earlier equal entries, take_eq).  Ranks >= limit are dropped (only
-// reachable with an inconsistent workspace).  To LDS (key, idx) when out is
-// null, else idx to out[rank].  Contains one barrier.
-template <int KMAX>
-__device__ __forceinline__ void emit_chosen(Smem<KMAX>& sm, const uint32_t (&k)[Shape<KMAX>::kSlots],
-                                            const uint32_t (&ix)[Shape<KMAX>::kSlots], uint32_t cnt,
-                                            uint32_t prefix, uint32_t pmask, uint32_t gt_base,
-                                            uint32_t eq_base, uint32_t take_eq, int32_t* out,
-                                            uint32_t limit) {
-  constexpr int S = Shape<KMAX>::kSlots;
+// reachable with an inconsistent workspace).  To LDS when out is null, else
+// ibase + idx to out[rank].  Contains one barrier; every thread has read its
+// buffer slice before any thread writes.  POST then fixes hist1.
+template <bool I16, int POST>
+__device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[Shape<I16>::kSlots], uint32_t cnt,
+                                            const Sel& s, uint32_t gt_base, uint32_t eq_base,
+                                            uint32_t take_eq, int32_t* out, uint32_t limit, uint32_t ibase) {
+  constexpr int S = Shape<I16>::kSlots;
   const uint32_t base = threadIdx.x * S;
+  uint32_t ix[S];
+  load_idx<I16>(sm, ix);
   uint32_t packed = 0;
 #pragma unroll
   for (int j = 0; j < S; ++j) {
     const bool valid = base + j < cnt;
-    const uint32_t km = k[j] & pmask;
-    packed += (valid && km > prefix) ? 1u : 0u;
-    packed += (valid && km == prefix) ? 0x10000u : 0u;
+    const uint32_t km = k[j] & s.pmask;
+    packed += (valid && km > s.prefix) ? 1u : 0u;
+    packed += (valid && km == s.prefix) ? 0x10000u : 0u;
   }
   uint32_t total;
   const uint32_t excl = block_excl_scan(sm, packed, &total);
@@ -313,65 +356,101 @@ __device__ __forceinline__ void emit_chosen(Smem<KMAX>& sm, const uint32_t (&k)[
 #pragma unroll
   for (int j = 0; j < S; ++j) {
     const bool valid = base + j < cnt;
-    const uint32_t km = k[j] & pmask;
-    const bool gt = valid && km > prefix;
-    const bool eq = valid && km == prefix;
+    const uint32_t km = k[j] & s.pmask;
+    const bool gt = valid && km > s.prefix;
+    const bool eq = valid && km == s.prefix;
     const bool take = gt || (eq && e < take_eq);
     const uint32_t pos = g + (e < take_eq ? e : take_eq);
     if (take && pos < limit) {
       if (out != nullptr) {
-        out[pos] = (int32_t)ix[j];
+        out[pos] = (int32_t)(ibase + ix[j]);
       } else {
         sm.key[pos] = k[j];
-        sm.idx[pos] = ix[j];
+        sm.idx[pos] = (typename Shape<I16>::Idx)ix[j];
       }
     }
     g += gt ? 1u : 0u;
     e += eq ? 1u : 0u;
   }
-}
-
-// Compacts the buffer (cnt > keep entries) to its keep best, index order
-// kept, corrects the running histogram and returns the raised acceptance
-// bound.  Arguments and result go by value: as an out-of-line call, a
-// by-reference counter would live in scratch, and every scratch reload waits
-// on all outstanding prefetches.
-template <int KMAX>
-__device__ __noinline__ uint32_t compact(Smem<KMAX>& sm, uint32_t cnt, uint32_t keep, uint32_t L) {
-  constexpr int S = Shape<KMAX>::kSlots;
-  uint32_t k[S], ix[S];
-  load_owned<KMAX>(sm, k, ix);
-  const Sel s = select_keep<KMAX>(sm, k, cnt, keep);
-  emit_chosen<KMAX>(sm, k, ix, cnt, s.prefix, s.pmask, 0u, 0u, s.krem, nullptr,
-                    (uint32_t)Shape<KMAX>::kCap);
-  // Kept entries: bins above b1 unchanged, krem1 from bin b1, none below.
-  for (uint32_t i = threadIdx.x; i < (uint32_t)kBins; i += kBlock) {
-    if (i < s.b1) sm.hist1[i] = 0u;
-    if (i == s.b1) sm.hist1[i] = s.krem1;
+  if (POST == kPostFinal || (POST == kPostCompact && s.used2)) clear_hist(sm);
+  if (POST == kPostCoarse || (POST == kPostCompact && !s.used2)) {
+    // The top-digit counts of kept entries are unchanged, except that only
+    // krem1 entries of bin b1 survive an exact selection.
+    for (uint32_t i = threadIdx.x; i < (uint32_t)kBins; i += kBlock) {
+      if (i < s.b1) sm.hist1[i] = 0u;
+      if (POST == kPostCompact && i == s.b1) sm.hist1[i] = s.krem1;
+    }
   }
-  __syncthreads();
-  // Every element still to come has a higher index than all kept entries, so
-  // it must beat the K-th best key strictly to matter.  When the K-th best key
-  // is known only to its top bits, accept anything from that prefix up.
-  uint32_t Ln;
-  if (s.pmask == 0xffffffffu)
-    Ln = s.prefix == 0xffffffffu ? 0xffffffffu : s.prefix + 1u;
-  else
-    Ln = s.prefix;
-  return Ln > L ? Ln : L;
+  if (POST == kPostCompact && s.used2) {
+    // hist1 served as scratch: rebuild it from the kept entries.
+    __syncthreads();
+    uint32_t e2 = eq_base + (excl >> 16);
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      const bool valid = base + j < cnt;
+      const uint32_t km = k[j] & s.pmask;
+      const bool gt = valid && km > s.prefix;
+      const bool eq = valid && km == s.prefix;
+      if (gt || (eq && e2 < take_eq)) atomicAdd(&sm.hist1[k[j] >> 21], 1u);
+      e2 += eq ? 1u : 0u;
+    }
+  }
 }
 
-// The K best of the buffer, written to out in index order; the running
-// histogram is cleared for the next row.
-template <int KMAX>
-__device__ __noinline__ void final_select(Smem<KMAX>& sm, uint32_t cnt, uint32_t K, int32_t* out) {
-  constexpr int S = Shape<KMAX>::kSlots;
-  uint32_t k[S], ix[S];
-  load_owned<KMAX>(sm, k, ix);
-  const Sel s = select_keep<KMAX>(sm, k, cnt, K);
-  emit_chosen<KMAX>(sm, k, ix, cnt, s.prefix, s.pmask, 0u, 0u, s.krem, out, K);
-  for (uint32_t i = threadIdx.x; i < (uint32_t)kBins; i += kBlock) sm.hist1[i] = 0u;
-  __syncthreads();
+// Frees buffer space when a tile would not fit (cnt > keep entries), keeping
+// index order and the running histogram; returns (new count << 32) | new
+// bound.  Coarse first: drop every entry below the top-digit bin holding the
+// keep-th best entry, if what remains leaves room for a tile.  Otherwise
+// (mostly ties crowding one bin) exact: keep exactly the keep best.  Every
+// element still to come has a higher index than all kept entries, so after
+// an exact selection it must beat the keep-th best key strictly to matter;
+// after a coarse one anything from the bin's lower edge up is accepted.
+// Out of line: inlined into each slot of the unrolled streaming loop it
+// would multiply the register demand.  Arguments and result go by value: a
+// by-reference counter would live in scratch, and every scratch reload waits
+// on all outstanding prefetches.  The caller's next barrier orders the
+// rewritten buffer and histogram before their next use.
+template <bool I16>
+__device__ __noinline__ uint64_t compact(Smem<I16>& sm, uint32_t cnt, uint32_t keep, uint32_t L) {
+  constexpr int S = Shape<I16>::kSlots;
+  uint32_t k[S];
+  load_keys<I16>(sm, k);
+  const Found f = wave_find<2048>(sm.hist1, keep);
+  uint32_t Ln, cn;
+  if (f.ok && f.above + f.in_bin + kTile <= (uint32_t)Shape<I16>::kCap) {
+    Sel s;
+    s.prefix = f.bin << 21;
+    s.pmask = 0xffe00000u;
+    s.krem = 0xffffffffu;
+    s.ok = 1u;
+    s.b1 = f.bin;
+    s.krem1 = f.in_bin;
+    s.used2 = 0u;
+    emit_chosen<I16, kPostCoarse>(sm, k, cnt, s, 0u, 0u, 0xffffffffu, nullptr, (uint32_t)Shape<I16>::kCap, 0u);
+    Ln = s.prefix;
+    cn = f.above + f.in_bin;
+  } else {
+    const Sel s = select_keep<I16>(sm, k, cnt, keep);
+    emit_chosen<I16, kPostCompact>(sm, k, cnt, s, 0u, 0u, s.krem, nullptr, (uint32_t)Shape<I16>::kCap, 0u);
+    if (s.pmask == 0xffffffffu)
+      Ln = s.prefix == 0xffffffffu ? 0xffffffffu : s.prefix + 1u;
+    else
+      Ln = s.prefix;
+    cn = keep;
+  }
+  Ln = Ln > L ? Ln : L;
+  return ((uint64_t)cn << 32) | Ln;
+}
+
+// The K best of the buffer, written to out in index order; hist1 is left
+// cleared for the next row.
+template <bool I16>
+__device__ __noinline__ void final_select(Smem<I16>& sm, uint32_t cnt, uint32_t K, int32_t* out) {
+  constexpr int S = Shape<I16>::kSlots;
+  uint32_t k[S];
+  load_keys<I16>(sm, k);
+  const Sel s = select_keep<I16>(sm, k, cnt, K);
+  emit_chosen<I16, kPostFinal>(sm, k, cnt, s, 0u, 0u, s.krem, out, K, 0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -416,8 +495,8 @@ __device__ __forceinline__ void load_tail(const float* __restrict__ rowp, uint32
 // Per-wave counts of accepted elements for each load slot go through LDS
 // (double-buffered by par); returns the tile total and this wave's offset
 // for each slot.
-template <int KMAX, int VEC>
-__device__ __forceinline__ uint32_t tile_exchange(Smem<KMAX>& sm, const bool (&a)[kElems], int& par,
+template <bool I16, int VEC>
+__device__ __forceinline__ uint32_t tile_exchange(Smem<I16>& sm, const bool (&a)[kElems], int& par,
                                                   uint32_t (&off)[kElems / VEC]) {
   constexpr int NL = kElems / VEC;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -455,41 +534,52 @@ __device__ __forceinline__ void tile_accept(const float (&x)[kElems], uint32_t p
   }
 }
 
+// Appends the accepted elements of one tile at cnt + (their rank in the tile).
+template <bool I16, int VEC>
+__device__ __forceinline__ void tile_append(Smem<I16>& sm, const float (&x)[kElems], const bool (&a)[kElems],
+                                            const uint32_t (&off)[kElems / VEC], uint32_t cnt, uint32_t rel) {
+  constexpr int NL = kElems / VEC;
+#pragma unroll
+  for (int u = 0; u < NL; ++u) {
+    uint32_t r = cnt + off[u];
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) r += lanes_below(ballot(a[u * VEC + c]));
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) {
+      const int e = u * VEC + c;
+      if (a[e]) {
+        const uint32_t key = ord_key(__float_as_uint(x[e]));
+        sm.key[r] = key;
+        sm.idx[r] = (typename Shape<I16>::Idx)(rel + (uint32_t)u * (kBlock * VEC) + c);
+        atomicAdd(&sm.hist1[key >> 21], 1u);
+      }
+      r += a[e] ? 1u : 0u;
+    }
+  }
+}
+
 // Filters one tile into the candidate buffer, compacting first if the
-// tile's accepted elements would not fit.
-template <int KMAX, int VEC, bool FULL>
-__device__ __forceinline__ void process_tile(Smem<KMAX>& sm, const float (&x)[kElems], uint32_t p0, uint32_t c1,
-                                             uint32_t keep, uint32_t& cnt, uint32_t& L, int& par) {
+// tile's accepted elements would not fit.  p0 and c1 are absolute row
+// positions; indices are stored relative to ibase.
+template <bool I16, int VEC, bool FULL>
+__device__ __forceinline__ void process_tile(Smem<I16>& sm, const float (&x)[kElems], uint32_t p0, uint32_t c1,
+                                             uint32_t ibase, uint32_t keep, uint32_t& cnt, uint32_t& L,
+                                             int& par) {
   constexpr int NL = kElems / VEC;
   const uint32_t pbase = p0 + threadIdx.x * VEC;
   bool a[kElems];
   uint32_t off[NL];
   tile_accept<VEC, FULL>(x, pbase, c1, accept_floor(L), a);
-  uint32_t total = tile_exchange<KMAX, VEC>(sm, a, par, off);
-  if (cnt + total > (uint32_t)Shape<KMAX>::kCap) {
-    L = compact<KMAX>(sm, cnt, keep, L);
-    cnt = keep;
+  uint32_t total = tile_exchange<I16, VEC>(sm, a, par, off);
+  if (cnt + total > (uint32_t)Shape<I16>::kCap) {
+    const uint64_t r = compact<I16>(sm, cnt, keep, L);
+    L = (uint32_t)r;
+    cnt = (uint32_t)(r >> 32);
     tile_accept<VEC, FULL>(x, pbase, c1, accept_floor(L), a);
-    total = tile_exchange<KMAX, VEC>(sm, a, par, off);
-  }
-  if (total != 0) {
-#pragma unroll
-    for (int u = 0; u < NL; ++u) {
-      uint32_t r = cnt + off[u];
-#pragma unroll
-      for (int c = 0; c < VEC; ++c) r += lanes_below(ballot(a[u * VEC + c]));
-#pragma unroll
-      for (int c = 0; c < VEC; ++c) {
-        const int e = u * VEC + c;
-        if (a[e]) {
-          const uint32_t key = ord_key(__float_as_uint(x[e]));
-          sm.key[r] = key;
-          sm.idx[r] = pbase + (uint32_t)u * (kBlock * VEC) + c;
-          atomicAdd(&sm.hist1[key >> 21], 1u);
-        }
-        r += a[e] ? 1u : 0u;
-      }
-    }
+    total = tile_exchange<I16, VEC>(sm, a, par, off);
+    if (total != 0) tile_append<I16, VEC>(sm, x, a, off, cnt, pbase - ibase);
+  } else if (total != 0) {
+    tile_append<I16, VEC>(sm, x, a, off, cnt, pbase - ibase);
   }
   cnt += total;
 }
@@ -500,8 +590,8 @@ __device__ __forceinline__ void process_tile(Smem<KMAX>& sm, const float (&x)[kE
 // are in flight.  Prefetch addresses past the last full tile are clamped to
 // it (a cache hit), which keeps the load pattern identical every iteration.
 // The partial last tile is loaded with per-element bounds checks.
-template <int KMAX, int VEC>
-__device__ void stream_chunk(Smem<KMAX>& sm, const float* __restrict__ rowp, uint32_t c0, uint32_t c1,
+template <bool I16, int VEC>
+__device__ void stream_chunk(Smem<I16>& sm, const float* __restrict__ rowp, uint32_t c0, uint32_t c1,
                              uint32_t keep, uint32_t& cnt, uint32_t& L) {
   constexpr int PF = kPrefetch;
   const uint32_t F = (c1 - c0) / kTile;  // full tiles
@@ -523,21 +613,21 @@ __device__ void stream_chunk(Smem<KMAX>& sm, const float* __restrict__ rowp, uin
         const uint32_t jn = j + PF - 1 < F ? j + PF - 1 : F - 1;
         load_full<VEC>(rowp, c0 + jn * kTile, buf[(slot + PF - 1) % PF]);
         __builtin_amdgcn_sched_barrier(0);
-        process_tile<KMAX, VEC, true>(sm, buf[slot], c0 + j * kTile, c1, keep, cnt, L, par);
+        process_tile<I16, VEC, true>(sm, buf[slot], c0 + j * kTile, c1, c0, keep, cnt, L, par);
       }
     }
     // The last F % PF full tiles are already in buf[0..]: no more loads.
 #pragma unroll
     for (int slot = 0; slot < PF - 1; ++slot) {
       const uint32_t j = Fr + slot;
-      if (j < F) process_tile<KMAX, VEC, true>(sm, buf[slot], c0 + j * kTile, c1, keep, cnt, L, par);
+      if (j < F) process_tile<I16, VEC, true>(sm, buf[slot], c0 + j * kTile, c1, c0, keep, cnt, L, par);
     }
   }
   const uint32_t pt = c0 + F * kTile;
   if (pt < c1) {
     float x[kElems];
     load_tail<VEC>(rowp, c1, pt, x);
-    process_tile<KMAX, VEC, false>(sm, x, pt, c1, keep, cnt, L, par);
+    process_tile<I16, VEC, false>(sm, x, pt, c1, c0, keep, cnt, L, par);
   }
   __syncthreads();
 }
@@ -553,20 +643,17 @@ __device__ __forceinline__ void write_all_then_pad(int32_t* out, int64_t n, int 
   for (int i = threadIdx.x; i < K; i += kBlock) out[i] = i < n ? i : -1;
 }
 
-template <int KMAX>
-__device__ __forceinline__ void zero_histograms(Smem<KMAX>& sm) {
-  for (int i = threadIdx.x; i < kBins; i += kBlock) {
-    sm.hist1[i] = 0u;
-    sm.hist2[i] = 0u;
-  }
+template <bool I16>
+__device__ __forceinline__ void zero_histograms(Smem<I16>& sm) {
+  clear_hist(sm);
 }
 
 // ---------------------------------------------------------------------------
 // One workgroup per row, persistent over rows.
 // ---------------------------------------------------------------------------
-template <int KMAX, int VEC>
+template <int VEC, bool I16>
 __global__ void __launch_bounds__(kBlock) topk_single_kernel(KernelParams p) {
-  __shared__ Smem<KMAX> sm;
+  __shared__ Smem<I16> sm;
   zero_histograms(sm);
   __syncthreads();
   const uint32_t K = (uint32_t)p.K;
@@ -579,8 +666,8 @@ __global__ void __launch_bounds__(kBlock) topk_single_kernel(KernelParams p) {
     }
     const float* rowp = p.scores + (int64_t)row * p.row_stride;
     uint32_t cnt = 0, L = 0;
-    stream_chunk<KMAX, VEC>(sm, rowp, 0u, (uint32_t)n, K, cnt, L);
-    final_select<KMAX>(sm, cnt, K, out);
+    stream_chunk<I16, VEC>(sm, rowp, 0u, (uint32_t)n, K, cnt, L);
+    final_select<I16>(sm, cnt, K, out);
   }
 }
 
@@ -588,18 +675,34 @@ __global__ void __launch_bounds__(kBlock) topk_single_kernel(KernelParams p) {
 // Several workgroups per row, cooperating through the workspace.
 // ---------------------------------------------------------------------------
 
-// Arrival barrier of the workgroups sharing a row.  Every thread publishes
-// its global writes at agent scope, one thread arrives and polls, everyone
-// acquires.  A wait that exceeds spin_limit polls sets an error bit and
-// returns, so no wave can wait forever.
+// Workspace traffic between the workgroups of a row goes only through
+// agent-scope atomic operations (loads, stores, adds), which are coherent at
+// device scope on their own; no cache-wide write-back or invalidate is
+// needed.  Ordering: a writer wave waits until all its atomics have completed
+// before the workgroup arrives at the barrier, and readers issue their loads
+// only after seeing the arrival count.
+__device__ __forceinline__ uint32_t ws_load(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ws_store(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ws_add(uint32_t* p, uint32_t v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Arrival barrier of the workgroups sharing a row: every wave drains its
+// outstanding memory operations, one thread arrives and polls.  A wait that
+// exceeds spin_limit polls sets an error bit and returns, so no wave can
+// wait forever.
 __device__ void group_barrier(uint32_t* ctr, uint32_t target, uint32_t spin_limit, uint32_t* err) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    ws_add(ctr, 1u);
     uint32_t polls = 0;
-    while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(2);
+    while (ws_load(ctr) < target) {
+      __builtin_amdgcn_s_sleep(1);
       if (++polls > spin_limit) {
         __hip_atomic_fetch_or(err, kErrSpin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
@@ -607,7 +710,6 @@ __device__ void group_barrier(uint32_t* ctr, uint32_t target, uint32_t spin_limi
     }
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
 // Adds an LDS histogram into a workspace histogram (non-zero bins only) and
@@ -616,14 +718,14 @@ __device__ __forceinline__ void merge_hist(uint32_t* lds_hist, uint32_t* gh) {
   for (int i = threadIdx.x; i < kBins; i += kBlock) {
     const uint32_t v = lds_hist[i];
     if (v) {
-      __hip_atomic_fetch_add(gh + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ws_add(gh + i, v);
       lds_hist[i] = 0u;
     }
   }
 }
 
 __device__ __forceinline__ void load_hist(uint32_t* lds_hist, const uint32_t* gh) {
-  for (int i = threadIdx.x; i < kBins; i += kBlock) lds_hist[i] = gh[i];
+  for (int i = threadIdx.x; i < kBins; i += kBlock) lds_hist[i] = ws_load(gh + i);
 }
 
 // Adds a wave-uniform count into an LDS accumulator (one lane per wave).
@@ -631,15 +733,36 @@ __device__ __forceinline__ void wave_add(uint32_t* acc, uint32_t v) {
   if ((threadIdx.x & 63) == 0 && v) atomicAdd(acc, v);
 }
 
-template <int KMAX, int VEC>
+// Index of the list holding flattened position i: the last gg with
+// off[gg] <= i (off ascending, off[0] = 0, n lists).
+__device__ __forceinline__ int list_of(const uint32_t* off, int n, uint32_t i) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= i)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+template <int VEC, bool I16>
 __global__ void __launch_bounds__(kBlock) topk_multi_kernel(KernelParams p) {
-  __shared__ Smem<KMAX> sm;
-  constexpr int S = Shape<KMAX>::kSlots;
-  constexpr int CAP = Shape<KMAX>::kCap;
+  __shared__ Smem<I16> sm;
+  __shared__ uint32_t s_off[kMaxGroup + 1];
+  __shared__ uint32_t s_above[kMaxGroup];
+  constexpr int S = Shape<I16>::kSlots;
+  constexpr int CAP = Shape<I16>::kCap;
   const int t = threadIdx.x;
   const int G = p.wg_per_row;
-  const int row = blockIdx.x / G;
-  const int g = blockIdx.x - row * G;
+  // Workgroups are dispatched round-robin over the 8 XCDs.  Renumber them so
+  // that consecutive logical ids -- the G workgroups of one row -- share an
+  // XCD and its L2 (performance only; any mapping is correct).
+  const int W = (int)gridDim.x;
+  const int l = (W & 7) == 0 ? (int)(blockIdx.x & 7) * (W >> 3) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
+  const int row = l / G;
+  const int g = l - row * G;
   if (row >= p.num_rows) return;
   const uint32_t K = (uint32_t)p.K;
   const int64_t n = clamp_len(p, row);
@@ -662,54 +785,55 @@ __global__ void __launch_bounds__(kBlock) topk_multi_kernel(KernelParams p) {
   uint32_t* lists = reinterpret_cast<uint32_t*>(blk + lay.lists);
 
   zero_histograms(sm);
-  if (t < 8) sm.acc[t] = 0u;
+  if (t < 16) sm.acc[t] = 0u;
   __syncthreads();
 
   const int64_t c0 = (int64_t)g * p.chunk;
   const int64_t c1 = c0 + p.chunk < n ? c0 + p.chunk : n;
   const float* rowp = p.scores + (int64_t)row * p.row_stride;
   uint32_t cnt = 0, L = 0;
-  stream_chunk<KMAX, VEC>(sm, rowp, (uint32_t)c0, (uint32_t)c1, K, cnt, L);
+  stream_chunk<I16, VEC>(sm, rowp, (uint32_t)c0, (uint32_t)c1, K, cnt, L);
 
-  uint32_t k[S], ix[S];
-  load_owned<KMAX>(sm, k, ix);
+  uint32_t k[S];
+  load_keys<I16>(sm, k);
   const uint32_t base = (uint32_t)t * S;
 
   // Round 1: the chunk's top-digit histogram (already in hist1) into the
-  // row's, then the row-wide threshold digit.
+  // row's, then the row-wide threshold digit from a copy of the row's.
   merge_hist(sm.hist1, h1);
   group_barrier(ctr, 1u * grow, p.spin_limit, err);
-  load_hist(sm.hist2, h1);
+  load_hist(sm.hist1, h1);
   __syncthreads();
-  search<2048, true>(sm.hist2, K, sm.res);
-  __syncthreads();
-  uint32_t ok = sm.res[3];
-  uint32_t krem = K - sm.res[1];
-  uint32_t prefix = sm.res[0] << 21;
+  const Found f1 = wave_find<2048>(sm.hist1, K);
+  uint32_t ok = f1.ok;
+  uint32_t krem = K - f1.above;
+  uint32_t prefix = f1.bin << 21;
   uint32_t pmask = 0xffe00000u;
 
   // Round 2: next 11 bits of the entries in the threshold bin; publish how
   // many of this chunk's entries lie above it.
+  __syncthreads();  // every wave has read the row's copy
+  clear_hist(sm);
+  __syncthreads();
   uint32_t n_above = 0;
 #pragma unroll
   for (int j = 0; j < S; ++j) {
     const bool valid = base + j < cnt;
     const uint32_t km = k[j] & pmask;
-    if (valid && km == prefix) atomicAdd(&sm.hist2[(k[j] >> 10) & 2047u], 1u);
+    if (valid && km == prefix) atomicAdd(&sm.hist1[(k[j] >> 10) & 2047u], 1u);
     n_above += popc64(ballot(valid && km > prefix));
   }
   wave_add(&sm.acc[0], n_above);
   __syncthreads();
-  merge_hist(sm.hist2, h2);
-  if (t == 0) slots[4 * g + 0] = sm.acc[0];
+  merge_hist(sm.hist1, h2);
+  if (t == 0) ws_store(&slots[4 * g + 0], sm.acc[0]);
   group_barrier(ctr, 2u * grow, p.spin_limit, err);
-  load_hist(sm.hist2, h2);
+  load_hist(sm.hist1, h2);
   __syncthreads();
-  search<2048, true>(sm.hist2, krem, sm.res);
-  __syncthreads();
-  ok &= sm.res[3];
-  krem -= sm.res[1];
-  prefix |= sm.res[0] << 10;
+  const Found f2 = wave_find<2048>(sm.hist1, krem);
+  ok &= f2.ok;
+  krem -= f2.above;
+  prefix |= f2.bin << 10;
   pmask = 0xfffffc00u;
 
   // Round 3: publish the keys still undecided after 22 bits, in index order,
@@ -731,46 +855,65 @@ __global__ void __launch_bounds__(kBlock) topk_multi_kernel(KernelParams p) {
 #pragma unroll
     for (int j = 0; j < S; ++j) {
       const bool valid = base + j < cnt;
-      if (valid && (k[j] & pmask) == prefix) my_list[at++] = k[j];
+      if (valid && (k[j] & pmask) == prefix) ws_store(&my_list[at++], k[j]);
     }
     if (t == 0) {
-      slots[4 * g + 1] = sm.acc[1] - sm.acc[0];
-      slots[4 * g + 2] = len;
+      ws_store(&slots[4 * g + 1], sm.acc[1] - sm.acc[0]);
+      ws_store(&slots[4 * g + 2], len);
     }
   }
   group_barrier(ctr, 3u * grow, p.spin_limit, err);
+  clear_hist(sm);  // every wave read round 2's copy before the barrier
 
-  // Last 10 bits over every chunk's list; then this chunk's offsets.
-  for (int gg = 0; gg < grow; ++gg) {
-    uint32_t len = slots[4 * gg + 2];
-    len = len < (uint32_t)CAP ? len : (uint32_t)CAP;
-    const uint32_t* lst = lists + (uint64_t)gg * CAP;
-    for (uint32_t i = t; i < len; i += kBlock) atomicAdd(&sm.hist2[lst[i] & 1023u], 1u);
+  // Every chunk's list, flattened: offsets by a prefix sum over the lengths.
+  if (t < 64) {
+    uint32_t len = 0, above = 0;
+    if (t < grow) {
+      len = ws_load(&slots[4 * t + 2]);
+      len = len < (uint32_t)CAP ? len : (uint32_t)CAP;
+      above = ws_load(&slots[4 * t + 0]) + ws_load(&slots[4 * t + 1]);
+    }
+    const uint32_t incl = wave_incl_scan(len);
+    if (t < grow) {
+      s_off[t + 1] = incl;
+      s_above[t] = above;
+    }
+    if (t == 0) s_off[0] = 0u;
   }
   __syncthreads();
-  search<1024, true>(sm.hist2, krem, sm.res);
+  const uint32_t total = s_off[grow];
+  // Last 10 bits over all lists.
+  for (uint32_t i = t; i < total; i += kBlock) {
+    const int gg = list_of(s_off, grow, i);
+    const uint32_t v = ws_load(&lists[(uint64_t)gg * CAP + (i - s_off[gg])]);
+    atomicAdd(&sm.hist1[v & 1023u], 1u);
+  }
   __syncthreads();
-  ok &= sm.res[3];
-  const uint32_t T = prefix | sm.res[0];
-  const uint32_t take_eq = krem - sm.res[1];
+  const Found f3 = wave_find<1024>(sm.hist1, krem);
+  ok &= f3.ok;
+  const uint32_t T = prefix | f3.bin;
+  const uint32_t take_eq = krem - f3.above;
+  // Entries of earlier chunks: above the 22-bit prefix (slots), and in the
+  // lists above / equal to T.
   {
     uint32_t gt_b = 0, eq_b = 0;
-    for (int gg = 0; gg < g; ++gg) {
-      uint32_t len = slots[4 * gg + 2];
-      len = len < (uint32_t)CAP ? len : (uint32_t)CAP;
-      const uint32_t* lst = lists + (uint64_t)gg * CAP;
-      for (uint32_t i0 = 0; i0 < len; i0 += kBlock) {
-        const uint32_t i = i0 + t;
-        const uint32_t v = i < len ? lst[i] : 0u;
-        gt_b += popc64(ballot(i < len && v > T));
-        eq_b += popc64(ballot(i < len && v == T));
+    const uint32_t lim = s_off[g];
+    for (uint32_t i0 = 0; i0 < lim; i0 += kBlock) {
+      const uint32_t i = i0 + t;
+      uint32_t v = 0;
+      if (i < lim) {
+        const int gg = list_of(s_off, grow, i);
+        v = ws_load(&lists[(uint64_t)gg * CAP + (i - s_off[gg])]);
       }
-      if (t == 0) gt_b += slots[4 * gg + 0] + slots[4 * gg + 1];
+      gt_b += popc64(ballot(i < lim && v > T));
+      eq_b += popc64(ballot(i < lim && v == T));
     }
-    // List counts are wave-uniform; the slot counts were added on thread 0 only.
-    if ((t & 63) == 0) {
-      if (gt_b) atomicAdd(&sm.acc[2], gt_b);
-      if (eq_b) atomicAdd(&sm.acc[3], eq_b);
+    wave_add(&sm.acc[2], gt_b);
+    wave_add(&sm.acc[3], eq_b);
+    if (t == 0) {
+      uint32_t a = 0;
+      for (int gg = 0; gg < g; ++gg) a += s_above[gg];
+      if (a) atomicAdd(&sm.acc[2], a);
     }
   }
   __syncthreads();
@@ -779,31 +922,36 @@ __global__ void __launch_bounds__(kBlock) topk_multi_kernel(KernelParams p) {
 
   // Leave: the last workgroup out zeroes what this row used in the workspace.
   if (t == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(exit_ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    sm.res[0] = (old == (uint32_t)grow - 1u) ? 1u : 0u;
+    const uint32_t old = __hip_atomic_fetch_add(exit_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.acc[4] = (old == (uint32_t)grow - 1u) ? 1u : 0u;
     if (!ok) __hip_atomic_fetch_or(err, kErrSearch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  if (sm.res[0]) {
+  if (sm.acc[4]) {
     for (int i = t; i < kBins; i += kBlock) {
-      h1[i] = 0u;
-      h2[i] = 0u;
+      ws_store(&h1[i], 0u);
+      ws_store(&h2[i], 0u);
     }
-    for (int gg = 0; gg < grow; ++gg) {
-      uint32_t len = slots[4 * gg + 2];
-      len = len < (uint32_t)CAP ? len : (uint32_t)CAP;
-      uint32_t* lst = lists + (uint64_t)gg * CAP;
-      for (uint32_t i = t; i < len; i += kBlock) lst[i] = 0u;
+    for (uint32_t i = t; i < total; i += kBlock) {
+      const int gg = list_of(s_off, grow, i);
+      ws_store(&lists[(uint64_t)gg * CAP + (i - s_off[gg])], 0u);
     }
-    __syncthreads();  // every list length has been read before the slots are cleared
-    if (t < 4 * grow) slots[t] = 0u;
+    if (t < 4 * grow) ws_store(&slots[t], 0u);
     if (t == 0) {
-      __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(exit_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ws_store(ctr, 0u);
+      ws_store(exit_ctr, 0u);
     }
   }
 
-  emit_chosen<KMAX>(sm, k, ix, cnt, T, 0xffffffffu, gt_base, eq_base, take_eq, out, K);
+  Sel s;
+  s.prefix = T;
+  s.pmask = 0xffffffffu;
+  s.krem = take_eq;
+  s.ok = ok;
+  s.b1 = 0u;
+  s.krem1 = 0u;
+  s.used2 = 0u;
+  emit_chosen<I16, kPostNone>(sm, k, cnt, s, gt_base, eq_base, take_eq, out, K, (uint32_t)c0);
 }
 
 // ---------------------------------------------------------------------------
@@ -824,38 +972,21 @@ __global__ void keys_kernel(const uint32_t* bits, uint32_t* keys, int64_t n) {
 // Instance table
 // ---------------------------------------------------------------------------
 
-template <int KMAX>
+template <bool I16>
 static const void* pick(int path, int vec) {
   if (path == 1) {
-    if (vec == 4) return reinterpret_cast<const void*>(&topk_single_kernel<KMAX, 4>);
-    if (vec == 2) return reinterpret_cast<const void*>(&topk_single_kernel<KMAX, 2>);
-    return reinterpret_cast<const void*>(&topk_single_kernel<KMAX, 1>);
+    if (vec == 4) return reinterpret_cast<const void*>(&topk_single_kernel<4, I16>);
+    if (vec == 2) return reinterpret_cast<const void*>(&topk_single_kernel<2, I16>);
+    return reinterpret_cast<const void*>(&topk_single_kernel<1, I16>);
   }
-  if (vec == 4) return reinterpret_cast<const void*>(&topk_multi_kernel<KMAX, 4>);
-  if (vec == 2) return reinterpret_cast<const void*>(&topk_multi_kernel<KMAX, 2>);
-  return reinterpret_cast<const void*>(&topk_multi_kernel<KMAX, 1>);
+  if (vec == 4) return reinterpret_cast<const void*>(&topk_multi_kernel<4, I16>);
+  if (vec == 2) return reinterpret_cast<const void*>(&topk_multi_kernel<2, I16>);
+  return reinterpret_cast<const void*>(&topk_multi_kernel<1, I16>);
 }
 
-const void* kernel_ptr(int path, int kmax, int vec) {
-  switch (kmax) {
-    case 256: return pick<256>(path, vec);
-    case 512: return pick<512>(path, vec);
-    case 1024: return pick<1024>(path, vec);
-    case 2048: return pick<2048>(path, vec);
-    default: return nullptr;
-  }
-}
+const void* kernel_ptr(int path, int vec, bool idx16) { return idx16 ? pick<true>(path, vec) : pick<false>(path, vec); }
 
-int lds_bytes_of(int path, int kmax) {
-  (void)path;
-  switch (kmax) {
-    case 256: return (int)sizeof(Smem<256>);
-    case 512: return (int)sizeof(Smem<512>);
-    case 1024: return (int)sizeof(Smem<1024>);
-    case 2048: return (int)sizeof(Smem<2048>);
-    default: return 0;
-  }
-}
+int lds_bytes_of(bool idx16) { return idx16 ? (int)sizeof(Smem<true>) : (int)sizeof(Smem<false>); }
 
 const void* zero_kernel_ptr() { return reinterpret_cast<const void*>(&zero_kernel); }
 const void* keys_kernel_ptr() { return reinterpret_cast<const void*>(&keys_kernel); }
