@@ -184,6 +184,16 @@ int topk_ragged_workspace_status(const void* workspace, hipStream_t stream, uint
  * device memory; asynchronous on stream. */
 int topk_ragged_debug_keys(const uint32_t* bits, uint32_t* keys, int64_t n, hipStream_t stream);
 
+/* Streaming-read reference (measurement only): row_max_keys[r] = the
+ * order-preserving uint32 key of the largest of the first lengths[r] scores of
+ * row r (0 for an empty row).  It reads exactly the bytes topk_ragged reads,
+ * with the same tiles, load width and prefetch depth, and does no selection,
+ * so its rate bounds what the selection can reach on the same input.
+ * Arguments as for topk_ragged; row_max_keys is a device array of num_rows
+ * entries.  Asynchronous on stream. */
+int topk_ragged_read_reference(const float* scores, int64_t row_stride, const int32_t* lengths,
+                               int32_t num_rows, uint32_t* row_max_keys, hipStream_t stream);
+
 /* Library version: major * 10000 + minor * 100 + patch. */
 int topk_ragged_version(void);
 

@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     new_workspace,
     plan_for_props,
     query_plan,
+    read_reference,
     topk_ragged,
     workspace_init,
     workspace_size,

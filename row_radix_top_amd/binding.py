@@ -25,7 +25,7 @@ EXPORTED = (
     "topk_ragged", "topk_ragged_workspace_size", "topk_ragged_workspace_init",
     "topk_ragged_last_error", "topk_ragged_plan", "topk_ragged_query_plan",
     "topk_ragged_workspace_size_ex", "topk_ragged_ex", "topk_ragged_workspace_status",
-    "topk_ragged_debug_keys", "topk_ragged_version",
+    "topk_ragged_debug_keys", "topk_ragged_version", "topk_ragged_read_reference",
 )
 
 
@@ -104,6 +104,7 @@ def load() -> ctypes.CDLL:
         lib.topk_ragged_workspace_status.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
         lib.topk_ragged_debug_keys.argtypes = [vp, vp, i64, vp]
         lib.topk_ragged_version.argtypes = []
+        lib.topk_ragged_read_reference.argtypes = [vp, i64, vp, i32, vp, vp]
         for name in EXPORTED:
             getattr(lib, name).restype = ctypes.c_int if name != "topk_ragged_last_error" else ctypes.c_char_p
         _lib = lib
@@ -262,6 +263,20 @@ def debug_keys(bits):
                                        _stream_ptr(None, bits.device))
     _check(rc, "topk_ragged_debug_keys")
     return keys
+
+
+def read_reference(scores, lengths, *, out=None, stream=None):
+    """Streaming-read reference: the device key of each row's largest valid
+    score, read exactly as topk_ragged reads the row (measurement only)."""
+    import torch
+    _validate(scores, lengths, None, 1)
+    num_rows = scores.shape[0]
+    if out is None:
+        out = torch.empty(num_rows, dtype=torch.int32, device=scores.device)
+    rc = load().topk_ragged_read_reference(scores.data_ptr(), scores.stride(0), lengths.data_ptr(), num_rows,
+                                           out.data_ptr(), _stream_ptr(stream, scores.device))
+    _check(rc, "topk_ragged_read_reference")
+    return out
 
 
 def version() -> int:

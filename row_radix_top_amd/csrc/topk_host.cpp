@@ -422,6 +422,43 @@ int topk_ragged_debug_keys(const uint32_t* bits, uint32_t* keys, int64_t n, hipS
   return TOPK_OK;
 }
 
+int topk_ragged_read_reference(const float* scores, int64_t row_stride, const int32_t* lengths,
+                               int32_t num_rows, uint32_t* row_max_keys, hipStream_t stream) {
+  if (num_rows < 0) return fail(TOPK_EINVAL, "num_rows must be >= 0");
+  if (row_stride < 1 || row_stride > INT32_MAX) return fail(TOPK_EINVAL, "row_stride must be in [1, 2^31 - 1]");
+  if (num_rows == 0) return TOPK_OK;
+  if (scores == nullptr || lengths == nullptr || row_max_keys == nullptr)
+    return fail(TOPK_EINVAL, "null scores, lengths or row_max_keys");
+  if (reinterpret_cast<uintptr_t>(scores) % 4 != 0 || reinterpret_cast<uintptr_t>(lengths) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(row_max_keys) % 4 != 0)
+    return fail(TOPK_EINVAL, "scores, lengths and row_max_keys must be 4-byte aligned");
+  int dev = 0;
+  int rc = stream_device(stream, &dev);
+  if (rc != TOPK_OK) return rc;
+  DevInfo* d = nullptr;
+  rc = device_info(dev, &d);
+  if (rc != TOPK_OK) return rc;
+  const int vec = vec_allowed_for(scores, row_stride);
+  int occ = 0;
+  rc = occupancy(dev, d, 3, vec, false, &occ);
+  if (rc != TOPK_OK) return rc;
+  if (occ < 1) return fail(TOPK_EDEVICE, "read reference kernel cannot be resident");
+  const int64_t cap = (int64_t)d->num_cus * occ;
+  const int64_t grid = num_rows < cap ? num_rows : cap;
+  rrt::KernelParams kp{};
+  kp.scores = scores;
+  kp.lengths = lengths;
+  kp.out = reinterpret_cast<int32_t*>(row_max_keys);
+  kp.row_stride = row_stride;
+  kp.num_rows = num_rows;
+  void* args[] = {&kp};
+  hipError_t e = hipLaunchKernel(rrt::kernel_ptr(3, vec, false), dim3((unsigned)grid), dim3(rrt::kBlock), args,
+                                 0, stream);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return fail(TOPK_ELAUNCH, std::string("read reference: ") + hipGetErrorString(e));
+  return TOPK_OK;
+}
+
 int topk_ragged_version(void) { return 100; }
 
 }  // extern "C"

@@ -17,6 +17,18 @@ constexpr int kMaxGroup = 64;               // most workgroups that may share a 
 constexpr int kMaxK = 2048;
 constexpr uint32_t kDefaultSpin = 1u << 24; // polls before a cooperative wait gives up
 
+// Speculative bound (one-workgroup rows): at the first compaction the bound
+// is raised to the key of the r-th best element seen so far, with
+// r = max(kSpecMinRank, ceil(kSpecNum / kSpecDen * K * seen / n)), when that
+// r is below K.  kSpecNum / kSpecDen is the safety factor over the expected
+// rank of the K-th best of the row; kSpecMinRank keeps the sample quantile
+// from resting on too few elements.
+// Rows shorter than kSpecMinLen do not speculate: too few tiles remain after
+// the first compaction to repay an exact selection.
+constexpr uint32_t kSpecNum = 3, kSpecDen = 2;
+constexpr uint32_t kSpecMinRank = 128;
+constexpr uint32_t kSpecMinLen = 16384;
+
 // Candidate buffer capacity.  It must hold K = 2048 kept entries plus one full
 // tile, so a tile always fits after a compaction.  With 16-bit indices (rows
 // or chunks of at most 65536 elements) an entry takes 6 bytes and the buffer
@@ -69,7 +81,8 @@ struct KernelParams {
   uint32_t spin_limit;
 };
 
-// Kernel lookup for the host side.  path: 1 single, 2 multi.
+// Kernel lookup for the host side.  path: 1 single, 2 multi, 3 the
+// streaming-read reference (idx16 ignored).
 const void* kernel_ptr(int path, int vec, bool idx16);
 const void* zero_kernel_ptr();
 const void* keys_kernel_ptr();

@@ -216,6 +216,7 @@ struct Sel {
   uint32_t b1;      // threshold top digit
   uint32_t krem1;   // entries taken from bin b1
   uint32_t used2;   // hist1 was reused for a later digit
+  uint32_t eqn;     // entries with (key & pmask) == prefix
 };
 
 // Thread t owns buffer positions [t*S, t*S + S).
@@ -292,6 +293,7 @@ __device__ Sel select_keep(Smem<I16>& sm, const uint32_t (&k)[Shape<I16>::kSlots
   r.prefix = f1.bin << 21;
   r.pmask = 0xffe00000u;
   r.used2 = 0u;
+  r.eqn = f1.in_bin;
   if (f1.in_bin != r.krem) {
     __syncthreads();  // every wave has read hist1
     clear_hist(sm);
@@ -304,6 +306,7 @@ __device__ Sel select_keep(Smem<I16>& sm, const uint32_t (&k)[Shape<I16>::kSlots
     r.krem -= f2.above;
     r.prefix |= f2.bin << 10;
     r.pmask = 0xfffffc00u;
+    r.eqn = f2.in_bin;
     if (f2.in_bin != r.krem) {
       __syncthreads();
       clear_hist(sm);
@@ -315,14 +318,15 @@ __device__ Sel select_keep(Smem<I16>& sm, const uint32_t (&k)[Shape<I16>::kSlots
       r.krem -= f3.above;
       r.prefix |= f3.bin;
       r.pmask = 0xffffffffu;
+      r.eqn = f3.in_bin;
     }
   }
   return r;
 }
 
 // After-emit bookkeeping of hist1, done between the emit barrier and the
-// next use: kPostCoarse / kPostCompact leave it describing the kept entries,
-// kPostFinal clears it for the next row.
+// next use: kPostCoarse and kPostCompact leave it describing the kept
+// entries, kPostFinal clears it for the next row.
 enum PostEmit { kPostNone = 0, kPostCompact = 1, kPostFinal = 2, kPostCoarse = 3 };
 
 // Writes the chosen entries in buffer order.  An entry is chosen if
@@ -374,12 +378,10 @@ __device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[S
   }
   if (POST == kPostFinal || (POST == kPostCompact && s.used2)) clear_hist(sm);
   if (POST == kPostCoarse || (POST == kPostCompact && !s.used2)) {
-    // The top-digit counts of kept entries are unchanged, except that only
-    // krem1 entries of bin b1 survive an exact selection.
-    for (uint32_t i = threadIdx.x; i < (uint32_t)kBins; i += kBlock) {
+    // Bins below b1 lose all their entries; every other bin keeps all of its
+    // entries (a selection that stops at the top digit takes bin b1 whole).
+    for (uint32_t i = threadIdx.x; i < (uint32_t)kBins; i += kBlock)
       if (i < s.b1) sm.hist1[i] = 0u;
-      if (POST == kPostCompact && i == s.b1) sm.hist1[i] = s.krem1;
-    }
   }
   if (POST == kPostCompact && s.used2) {
     // hist1 served as scratch: rebuild it from the kept entries.
@@ -399,39 +401,79 @@ __device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[S
 
 // Frees buffer space when a tile would not fit (cnt > keep entries), keeping
 // index order and the running histogram; returns (new count << 32) | new
-// bound.  Coarse first: drop every entry below the top-digit bin holding the
-// keep-th best entry, if what remains leaves room for a tile.  Otherwise
-// (mostly ties crowding one bin) exact: keep exactly the keep best.  Every
-// element still to come has a higher index than all kept entries, so after
-// an exact selection it must beat the keep-th best key strictly to matter;
-// after a coarse one anything from the bin's lower edge up is accepted.
+// bound.
+//
+// Speculative (spec_n = row length, first compaction of a row only; every
+// element seen so far is then in the buffer): keep every entry whose key is
+// at least that of the r-th best entry (r as set by kSpecNum, kSpecDen and
+// kSpecMinRank) and make that key the bound.  This assumes the K-th best of
+// the whole row is at least as large; the caller checks that at the end of
+// the row (at least K entries reached the buffer) and streams the row again
+// without speculation if not.  Entries below the bound can then only be
+// beaten by at least K others, so dropping them is safe whenever the check
+// passes.
+//
+// Otherwise coarse first: drop every entry below the top-digit bin holding
+// the keep-th best entry, if what remains leaves room for a tile.  Failing
+// that (mostly ties crowding one bin) exact: keep exactly the keep best.
+// Every element still to come has a higher index than all kept entries, so
+// after an exact selection it must beat the keep-th best key strictly to
+// matter; after a coarse one anything from the bin's lower edge up is
+// accepted.
+//
 // Out of line: inlined into each slot of the unrolled streaming loop it
 // would multiply the register demand.  Arguments and result go by value: a
 // by-reference counter would live in scratch, and every scratch reload waits
 // on all outstanding prefetches.  The caller's next barrier orders the
 // rewritten buffer and histogram before their next use.
 template <bool I16>
-__device__ __noinline__ uint64_t compact(Smem<I16>& sm, uint32_t cnt, uint32_t keep, uint32_t L) {
+__device__ __noinline__ uint64_t compact(Smem<I16>& sm, uint32_t cnt, uint32_t keep, uint32_t L, uint32_t spec_n) {
   constexpr int S = Shape<I16>::kSlots;
+  constexpr uint32_t CAP = (uint32_t)Shape<I16>::kCap;
   uint32_t k[S];
   load_keys<I16>(sm, k);
-  const Found f = wave_find<2048>(sm.hist1, keep);
+  bool spec = false;
+  if (spec_n != 0u) {
+    const uint64_t want = ((uint64_t)kSpecNum * keep * cnt + (uint64_t)kSpecDen * spec_n - 1) /
+                          ((uint64_t)kSpecDen * spec_n);
+    const uint32_t r = want > kSpecMinRank ? (uint32_t)want : kSpecMinRank;
+    if (r < keep) {
+      // Entries at or above the r-th best all lie in bins from its top digit
+      // up; speculate only if those certainly leave room for a tile.
+      const Found f = wave_find<2048>(sm.hist1, r);
+      if (f.ok && f.above + f.in_bin + kTile <= CAP) {
+        spec = true;
+        keep = r;
+      }
+    }
+  }
+  if (!spec) {
+    const Found f = wave_find<2048>(sm.hist1, keep);
+    if (f.ok && f.above + f.in_bin + kTile <= CAP) {
+      Sel s;
+      s.prefix = f.bin << 21;
+      s.pmask = 0xffe00000u;
+      s.krem = 0xffffffffu;
+      s.ok = 1u;
+      s.b1 = f.bin;
+      s.krem1 = f.in_bin;
+      s.used2 = 0u;
+      s.eqn = f.in_bin;
+      emit_chosen<I16, kPostCoarse>(sm, k, cnt, s, 0u, 0u, 0xffffffffu, nullptr, CAP, 0u);
+      const uint32_t Ln = s.prefix > L ? s.prefix : L;
+      return ((uint64_t)(f.above + f.in_bin) << 32) | Ln;
+    }
+  }
+  // Exact selection of the keep best; a speculative one then keeps every
+  // entry equal to the r-th best key too.
+  const Sel s = select_keep<I16>(sm, k, cnt, keep);
+  const uint32_t take_eq = spec ? 0xffffffffu : s.krem;
+  emit_chosen<I16, kPostCompact>(sm, k, cnt, s, 0u, 0u, take_eq, nullptr, CAP, 0u);
   uint32_t Ln, cn;
-  if (f.ok && f.above + f.in_bin + kTile <= (uint32_t)Shape<I16>::kCap) {
-    Sel s;
-    s.prefix = f.bin << 21;
-    s.pmask = 0xffe00000u;
-    s.krem = 0xffffffffu;
-    s.ok = 1u;
-    s.b1 = f.bin;
-    s.krem1 = f.in_bin;
-    s.used2 = 0u;
-    emit_chosen<I16, kPostCoarse>(sm, k, cnt, s, 0u, 0u, 0xffffffffu, nullptr, (uint32_t)Shape<I16>::kCap, 0u);
+  if (spec) {
     Ln = s.prefix;
-    cn = f.above + f.in_bin;
+    cn = keep - s.krem + s.eqn;
   } else {
-    const Sel s = select_keep<I16>(sm, k, cnt, keep);
-    emit_chosen<I16, kPostCompact>(sm, k, cnt, s, 0u, 0u, s.krem, nullptr, (uint32_t)Shape<I16>::kCap, 0u);
     if (s.pmask == 0xffffffffu)
       Ln = s.prefix == 0xffffffffu ? 0xffffffffu : s.prefix + 1u;
     else
@@ -564,7 +606,7 @@ __device__ __forceinline__ void tile_append(Smem<I16>& sm, const float (&x)[kEle
 template <bool I16, int VEC, bool FULL>
 __device__ __forceinline__ void process_tile(Smem<I16>& sm, const float (&x)[kElems], uint32_t p0, uint32_t c1,
                                              uint32_t ibase, uint32_t keep, uint32_t& cnt, uint32_t& L,
-                                             int& par) {
+                                             uint32_t& spec, int& par) {
   constexpr int NL = kElems / VEC;
   const uint32_t pbase = p0 + threadIdx.x * VEC;
   bool a[kElems];
@@ -572,7 +614,8 @@ __device__ __forceinline__ void process_tile(Smem<I16>& sm, const float (&x)[kEl
   tile_accept<VEC, FULL>(x, pbase, c1, accept_floor(L), a);
   uint32_t total = tile_exchange<I16, VEC>(sm, a, par, off);
   if (cnt + total > (uint32_t)Shape<I16>::kCap) {
-    const uint64_t r = compact<I16>(sm, cnt, keep, L);
+    const uint64_t r = compact<I16>(sm, cnt, keep, L, spec);
+    spec = 0u;
     L = (uint32_t)r;
     cnt = (uint32_t)(r >> 32);
     tile_accept<VEC, FULL>(x, pbase, c1, accept_floor(L), a);
@@ -589,10 +632,11 @@ __device__ __forceinline__ void process_tile(Smem<I16>& sm, const float (&x)[kEl
 // before tile j is processed, so about (kPrefetch - 1) tiles per workgroup
 // are in flight.  Prefetch addresses past the last full tile are clamped to
 // it (a cache hit), which keeps the load pattern identical every iteration.
-// The partial last tile is loaded with per-element bounds checks.
+// The partial last tile is loaded with per-element bounds checks.  spec:
+// the row length if the first compaction may speculate, else 0.
 template <bool I16, int VEC>
 __device__ void stream_chunk(Smem<I16>& sm, const float* __restrict__ rowp, uint32_t c0, uint32_t c1,
-                             uint32_t keep, uint32_t& cnt, uint32_t& L) {
+                             uint32_t keep, uint32_t& cnt, uint32_t& L, uint32_t spec) {
   constexpr int PF = kPrefetch;
   const uint32_t F = (c1 - c0) / kTile;  // full tiles
   int par = 0;
@@ -613,21 +657,21 @@ __device__ void stream_chunk(Smem<I16>& sm, const float* __restrict__ rowp, uint
         const uint32_t jn = j + PF - 1 < F ? j + PF - 1 : F - 1;
         load_full<VEC>(rowp, c0 + jn * kTile, buf[(slot + PF - 1) % PF]);
         __builtin_amdgcn_sched_barrier(0);
-        process_tile<I16, VEC, true>(sm, buf[slot], c0 + j * kTile, c1, c0, keep, cnt, L, par);
+        process_tile<I16, VEC, true>(sm, buf[slot], c0 + j * kTile, c1, c0, keep, cnt, L, spec, par);
       }
     }
     // The last F % PF full tiles are already in buf[0..]: no more loads.
 #pragma unroll
     for (int slot = 0; slot < PF - 1; ++slot) {
       const uint32_t j = Fr + slot;
-      if (j < F) process_tile<I16, VEC, true>(sm, buf[slot], c0 + j * kTile, c1, c0, keep, cnt, L, par);
+      if (j < F) process_tile<I16, VEC, true>(sm, buf[slot], c0 + j * kTile, c1, c0, keep, cnt, L, spec, par);
     }
   }
   const uint32_t pt = c0 + F * kTile;
   if (pt < c1) {
     float x[kElems];
     load_tail<VEC>(rowp, c1, pt, x);
-    process_tile<I16, VEC, false>(sm, x, pt, c1, c0, keep, cnt, L, par);
+    process_tile<I16, VEC, false>(sm, x, pt, c1, c0, keep, cnt, L, spec, par);
   }
   __syncthreads();
 }
@@ -657,17 +701,30 @@ __global__ void __launch_bounds__(kBlock) topk_single_kernel(KernelParams p) {
   zero_histograms(sm);
   __syncthreads();
   const uint32_t K = (uint32_t)p.K;
-  for (int row = blockIdx.x; row < p.num_rows; row += gridDim.x) {
+  uint32_t redo = 0u;  // 1 while a row is streamed again after a failed speculation
+  for (int row = blockIdx.x; row < p.num_rows;) {
     const int64_t n = clamp_len(p, row);
     int32_t* out = p.out + (int64_t)row * p.K;
     if (n <= (int64_t)K) {
       write_all_then_pad(out, n, p.K);
+      row += gridDim.x;
       continue;
     }
     const float* rowp = p.scores + (int64_t)row * p.row_stride;
     uint32_t cnt = 0, L = 0;
-    stream_chunk<I16, VEC>(sm, rowp, 0u, (uint32_t)n, K, cnt, L);
+    const uint32_t spec = (redo || n < (int64_t)kSpecMinLen) ? 0u : (uint32_t)n;
+    stream_chunk<I16, VEC>(sm, rowp, 0u, (uint32_t)n, K, cnt, L, spec);
+    if (cnt < K && !redo) {
+      // Fewer than K elements reached the speculative bound: it was above
+      // the K-th best.  Stream the same row again without speculating.
+      redo = 1u;
+      clear_hist(sm);
+      __syncthreads();
+      continue;
+    }
+    redo = 0u;
     final_select<I16>(sm, cnt, K, out);
+    row += gridDim.x;
   }
 }
 
@@ -792,7 +849,7 @@ __global__ void __launch_bounds__(kBlock) topk_multi_kernel(KernelParams p) {
   const int64_t c1 = c0 + p.chunk < n ? c0 + p.chunk : n;
   const float* rowp = p.scores + (int64_t)row * p.row_stride;
   uint32_t cnt = 0, L = 0;
-  stream_chunk<I16, VEC>(sm, rowp, (uint32_t)c0, (uint32_t)c1, K, cnt, L);
+  stream_chunk<I16, VEC>(sm, rowp, (uint32_t)c0, (uint32_t)c1, K, cnt, L, 0u);
 
   uint32_t k[S];
   load_keys<I16>(sm, k);
@@ -951,7 +1008,85 @@ __global__ void __launch_bounds__(kBlock) topk_multi_kernel(KernelParams p) {
   s.b1 = 0u;
   s.krem1 = 0u;
   s.used2 = 0u;
+  s.eqn = 0u;
   emit_chosen<I16, kPostNone>(sm, k, cnt, s, gt_base, eq_base, take_eq, out, K, (uint32_t)c0);
+}
+
+// ---------------------------------------------------------------------------
+// Streaming-read reference (measurement only): the largest key of each row's
+// valid prefix, read with the same tiles, load width and prefetch ring as the
+// selection kernels, and no filtering.  Its rate is the ceiling the streaming
+// filter can approach on the same bytes.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t tile_max(const float (&x)[kElems], uint32_t m) {
+#pragma unroll
+  for (int e = 0; e < kElems; ++e) {
+    const uint32_t k = ord_key(__float_as_uint(x[e]));
+    m = k > m ? k : m;
+  }
+  return m;
+}
+
+template <int VEC>
+__global__ void __launch_bounds__(kBlock) read_ref_kernel(KernelParams p) {
+  __shared__ uint32_t wmax[kWaves];
+  constexpr int PF = kPrefetch;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int row = blockIdx.x; row < p.num_rows; row += gridDim.x) {
+    const uint32_t n = (uint32_t)clamp_len(p, row);
+    const float* rowp = p.scores + (int64_t)row * p.row_stride;
+    const uint32_t F = n / kTile;
+    uint32_t m = 0;
+    if (F > 0) {
+      float buf[PF][kElems];
+#pragma unroll
+      for (int s = 0; s < PF - 1; ++s) {
+        load_full<VEC>(rowp, ((uint32_t)s < F ? (uint32_t)s : F - 1) * kTile, buf[s]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const uint32_t Fr = F - F % PF;
+      for (uint32_t j0 = 0; j0 < Fr; j0 += PF) {
+#pragma unroll
+        for (int slot = 0; slot < PF; ++slot) {
+          const uint32_t j = j0 + slot;
+          const uint32_t jn = j + PF - 1 < F ? j + PF - 1 : F - 1;
+          load_full<VEC>(rowp, jn * kTile, buf[(slot + PF - 1) % PF]);
+          __builtin_amdgcn_sched_barrier(0);
+          m = tile_max(buf[slot], m);
+        }
+      }
+#pragma unroll
+      for (int slot = 0; slot < PF - 1; ++slot)
+        if (Fr + slot < F) m = tile_max(buf[slot], m);
+    }
+    const uint32_t pt = F * kTile;
+    if (pt < n) {
+      float x[kElems];
+      load_tail<VEC>(rowp, n, pt, x);
+#pragma unroll
+      for (int u = 0; u < kElems / VEC; ++u)
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) {
+          const uint32_t pos = pt + (uint32_t)u * (kBlock * VEC) + threadIdx.x * VEC + c;
+          const uint32_t k = ord_key(__float_as_uint(x[u * VEC + c]));
+          if (pos < n && k > m) m = k;
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const uint32_t o = (uint32_t)__shfl_xor((int)m, off);
+      m = o > m ? o : m;
+    }
+    if (lane == 0) wmax[w] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t r = wmax[0];
+#pragma unroll
+      for (int i = 1; i < kWaves; ++i) r = wmax[i] > r ? wmax[i] : r;
+      reinterpret_cast<uint32_t*>(p.out)[row] = r;
+    }
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -974,6 +1109,11 @@ __global__ void keys_kernel(const uint32_t* bits, uint32_t* keys, int64_t n) {
 
 template <bool I16>
 static const void* pick(int path, int vec) {
+  if (path == 3) {
+    if (vec == 4) return reinterpret_cast<const void*>(&read_ref_kernel<4>);
+    if (vec == 2) return reinterpret_cast<const void*>(&read_ref_kernel<2>);
+    return reinterpret_cast<const void*>(&read_ref_kernel<1>);
+  }
   if (path == 1) {
     if (vec == 4) return reinterpret_cast<const void*>(&topk_single_kernel<4, I16>);
     if (vec == 2) return reinterpret_cast<const void*>(&topk_single_kernel<2, I16>);

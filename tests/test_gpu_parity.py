@@ -192,6 +192,32 @@ def test_increasing_rows_refill_every_tile():
         assert_same(got, exp, f"inc path={path}")
 
 
+def test_speculative_bound_fallback():
+    """Rows whose first tiles hold their largest values: a bound taken from
+    the first elements is above the K-th best of the row, so the row must be
+    streamed again.  One workgroup walks all rows (grid capped at 1), so
+    rows that need the second pass alternate with rows that do not."""
+    rng = np.random.default_rng(41)
+    stride = 65536
+    rows = []
+    for r in range(6):
+        x = rng.standard_normal(stride, dtype=np.float32)
+        if r % 2 == 0:
+            x[4096 * (1 + r // 2):] -= np.float32(10.0)   # a cliff after the first tiles
+        rows.append(x)
+    rows.append(-np.arange(stride, dtype=np.float32))     # strictly decreasing
+    rows.append(np.arange(stride, dtype=np.float32))      # strictly increasing
+    s = np.ascontiguousarray(np.stack(rows))
+    lens = np.array([stride, stride - 7, 40000, 33333, 20000, stride, stride, 9000], dtype=np.int32)
+    for K in (129, 1000, 2048):
+        exp = topk_ragged_oracle(s, lens, K)
+        for grid in (1, 0):
+            got, plan = run_gpu(s, lens, K, tag=f"spec-fallback K={K} grid={grid}", force_path=1,
+                                max_grid=grid)
+            assert plan["path"] == rrt.PATH_SINGLE
+            assert_same(got, exp, f"spec fallback K={K} grid={grid}")
+
+
 def test_many_rows_random_lengths():
     rng = np.random.default_rng(31)
     lens = rng.integers(0, 20000, size=700)
@@ -200,6 +226,39 @@ def test_many_rows_random_lengths():
         exp = topk_ragged_oracle(s, L, K)
         got, _ = run_gpu(s, L, K, tag=f"700 rows K={K}")
         assert_same(got, exp, f"700 rows K={K}")
+
+
+# ---------------------------------------------------------------------------
+# Streaming-read reference (measurement kernel)
+# ---------------------------------------------------------------------------
+
+def _max_key_of_prefix(row: np.ndarray, n: int) -> int:
+    if n <= 0:
+        return 0
+    u = row[:n].view(np.uint32).astype(np.uint64)
+    u = np.where(u == 0x80000000, 0, u)
+    k = np.where(u & 0x80000000, (~u) & 0xFFFFFFFF, u | 0x80000000)
+    return int(k.max())
+
+
+@pytest.mark.parametrize("offset", [0, 1, 2])
+def test_read_reference_reads_exactly_the_valid_prefix(offset):
+    import torch
+    # Tails hold random bit patterns (NaNs, infinities): reading past a
+    # length would change the answer.
+    w = workloads.make_workload("decode")
+    lens = w.flat_lengths.copy()
+    lens[:6] = [0, 1, 2047, 2048, 2049, 32768]
+    dev = torch.device("cuda:0")
+    flat = np.ascontiguousarray(w.scores.reshape(-1))
+    buf = torch.empty(flat.size + offset + 4, dtype=torch.float32, device=dev)
+    buf[offset:offset + flat.size].copy_(torch.from_numpy(flat))
+    s = buf[offset:offset + flat.size].view(w.scores.shape)
+    L = torch.from_numpy(lens).to(dev)
+    got = rrt.read_reference(s, L).cpu().numpy().view(np.uint32)
+    exp = [_max_key_of_prefix(w.scores[r], int(min(max(lens[r], 0), w.row_stride)))
+           for r in range(w.num_rows)]
+    assert got.tolist() == exp
 
 
 # ---------------------------------------------------------------------------
