@@ -88,8 +88,10 @@ int topk_ragged(const float* scores, int64_t row_stride, const int32_t* lengths,
                 void* workspace, hipStream_t stream);
 
 /* Bytes of workspace topk_ragged needs for this shape on the stream's device.
- * *bytes = 0 means no workspace is used (rows at or under the radix
- * threshold, or enough rows to give every workgroup a row of its own). */
+ * *bytes = 0 means no workspace is used: one workgroup per row and no more
+ * rows than resident workgroups.  With more rows than that, a 256-byte
+ * workspace holds the counter that hands rows to workgroups as they finish;
+ * rows split over several workgroups need a block per row on top. */
 int topk_ragged_workspace_size(int32_t num_rows, int64_t row_stride, int32_t K,
                                hipStream_t stream, size_t* bytes);
 

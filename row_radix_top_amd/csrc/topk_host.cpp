@@ -295,7 +295,9 @@ int topk_ragged_plan(const topk_device_props* props, int32_t num_rows, int64_t r
   plan->headroom = 0;
   plan->idx16 = i16 ? 1 : 0;
   plan->lds_bytes = rrt::lds_bytes_of(i16);
-  plan->workspace_bytes = 0;
+  // More rows than workgroups: later rows are handed out by a ticket counter
+  // in the workspace header.
+  plan->workspace_bytes = num_rows > grid ? rrt::kWsHeader : 0;
   return TOPK_OK;
 }
 
@@ -366,7 +368,7 @@ int topk_ragged_ex(const float* scores, int64_t row_stride, const int32_t* lengt
   kp.scores = scores;
   kp.lengths = lengths;
   kp.out = out_idx;
-  kp.ws = static_cast<uint8_t*>(workspace);
+  kp.ws = plan.workspace_bytes > 0 ? static_cast<uint8_t*>(workspace) : nullptr;
   kp.row_stride = row_stride;
   kp.chunk = plan.chunk;
   kp.group_bytes = plan.path == TOPK_PATH_MULTI

@@ -38,9 +38,12 @@ constexpr uint32_t kSpecMinLen = 16384;
 constexpr int kIdx16Limit = 65536;
 constexpr int cap_of(bool idx16) { return idx16 ? 5120 : 4096; }
 
-// Workspace: a 256-byte header (word 0: error bits) followed by one block per
-// row of the multi-workgroup path.
+// Workspace: a 256-byte header followed by one block per row of the
+// multi-workgroup path.  Header word 0: error bits; the word at byte
+// kTicketOff: the next-row ticket of the one-workgroup-per-row path when
+// rows outnumber its grid (zero between launches).
 constexpr uint64_t kWsHeader = 256;
+constexpr uint64_t kTicketOff = 128;
 constexpr uint32_t kErrSpin = 1u;
 constexpr uint32_t kErrSearch = 2u;
 

@@ -694,6 +694,16 @@ __device__ __forceinline__ void zero_histograms(Smem<I16>& sm) {
 
 // ---------------------------------------------------------------------------
 // One workgroup per row, persistent over rows.
+//
+// Workgroup b takes row b first.  With a workspace (rows outnumber the
+// grid) every later row comes from a ticket counter, so workgroups that run
+// faster -- the hardware favours the oldest waves -- take more rows.  Each
+// workgroup draws its next ticket when it starts a row, hiding the atomic's
+// latency behind the row, and stops at the first ticket past the last row.
+// There are exactly num_rows draws per launch (one per row after the first
+// gridDim.x, plus one failing draw per workgroup), so the draw that returns
+// num_rows - 1 is the last touch of the counter and resets it to zero.
+// Without a workspace row b + k * gridDim.x is taken in turn.
 // ---------------------------------------------------------------------------
 template <int VEC, bool I16>
 __global__ void __launch_bounds__(kBlock) topk_single_kernel(KernelParams p) {
@@ -701,30 +711,44 @@ __global__ void __launch_bounds__(kBlock) topk_single_kernel(KernelParams p) {
   zero_histograms(sm);
   __syncthreads();
   const uint32_t K = (uint32_t)p.K;
+  uint32_t* ticket = p.ws != nullptr ? reinterpret_cast<uint32_t*>(p.ws + kTicketOff) : nullptr;
   uint32_t redo = 0u;  // 1 while a row is streamed again after a failed speculation
-  for (int row = blockIdx.x; row < p.num_rows;) {
+  uint32_t next = 0u;  // thread 0: the row after this one
+  int row = blockIdx.x;
+  while (row < p.num_rows) {
+    if (threadIdx.x == 0 && !redo) {
+      if (ticket != nullptr) {
+        const uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (t == (uint32_t)p.num_rows - 1u) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        next = gridDim.x + t;
+      } else {
+        next = (uint32_t)row + gridDim.x;
+      }
+    }
     const int64_t n = clamp_len(p, row);
     int32_t* out = p.out + (int64_t)row * p.K;
     if (n <= (int64_t)K) {
       write_all_then_pad(out, n, p.K);
-      row += gridDim.x;
-      continue;
+    } else {
+      const float* rowp = p.scores + (int64_t)row * p.row_stride;
+      uint32_t cnt = 0, L = 0;
+      const uint32_t spec = (redo || n < (int64_t)kSpecMinLen) ? 0u : (uint32_t)n;
+      stream_chunk<I16, VEC>(sm, rowp, 0u, (uint32_t)n, K, cnt, L, spec);
+      if (cnt < K && !redo) {
+        // Fewer than K elements reached the speculative bound: it was above
+        // the K-th best.  Stream the same row again without speculating.
+        redo = 1u;
+        clear_hist(sm);
+        __syncthreads();
+        continue;
+      }
+      redo = 0u;
+      final_select<I16>(sm, cnt, K, out);
     }
-    const float* rowp = p.scores + (int64_t)row * p.row_stride;
-    uint32_t cnt = 0, L = 0;
-    const uint32_t spec = (redo || n < (int64_t)kSpecMinLen) ? 0u : (uint32_t)n;
-    stream_chunk<I16, VEC>(sm, rowp, 0u, (uint32_t)n, K, cnt, L, spec);
-    if (cnt < K && !redo) {
-      // Fewer than K elements reached the speculative bound: it was above
-      // the K-th best.  Stream the same row again without speculating.
-      redo = 1u;
-      clear_hist(sm);
-      __syncthreads();
-      continue;
-    }
-    redo = 0u;
-    final_select<I16>(sm, cnt, K, out);
-    row += gridDim.x;
+    if (threadIdx.x == 0) sm.acc[8] = next;
+    __syncthreads();
+    row = (int)min(sm.acc[8], (uint32_t)p.num_rows);
+    __syncthreads();  // every thread has read the next row before it is overwritten
   }
 }
 

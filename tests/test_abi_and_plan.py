@@ -61,6 +61,9 @@ def test_plan_many_long_rows_use_persistent_single_path():
     assert p["grid"] == 768 == p["resident_cap"]
     p = rrt.plan_for_props(256, 3, 3, 4096, 65536, 2048, max_grid=100)
     assert p["grid"] == 100
+    assert p["workspace_bytes"] == 256
+    p = rrt.plan_for_props(256, 3, 3, 768, 65536, 2048)
+    assert p["grid"] == 768 and p["workspace_bytes"] == 0
 
 
 @pytest.mark.parametrize("cus,occ", [(256, 1), (256, 2), (256, 3), (256, 4), (80, 2), (4, 1), (1, 1)])
@@ -79,14 +82,16 @@ def test_plan_multi_is_always_coresident(cus, occ, rows, stride):
         assert p["workspace_bytes"] > 0
     else:
         assert p["path"] == rrt.PATH_SINGLE
-        assert p["workspace_bytes"] == 0
+        # A ticket counter in the workspace header hands out rows past the grid.
+        assert p["workspace_bytes"] == (256 if rows > p["grid"] else 0)
         assert p["grid"] <= cap
 
 
 def test_plan_forced_multi_that_cannot_be_resident_falls_back():
     # 64 rows x 16 workgroups cannot be resident on 8 CUs with occupancy 1.
     p = rrt.plan_for_props(8, 1, 1, 64, 65536, 2048, force_path=2, force_wg_per_row=16)
-    assert p["path"] == rrt.PATH_SINGLE and p["fell_back"] == 1 and p["workspace_bytes"] == 0
+    assert p["path"] == rrt.PATH_SINGLE and p["fell_back"] == 1 and p["grid"] == 8
+    assert p["workspace_bytes"] == 256  # 64 rows on 8 workgroups: ticket counter
     p = rrt.plan_for_props(256, 2, 2, 4, 65536, 2048, force_path=2, force_wg_per_row=4)
     assert p["path"] == rrt.PATH_MULTI and p["wg_per_row"] == 4
 

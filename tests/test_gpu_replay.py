@@ -38,8 +38,10 @@ def _length_patterns(rng, npat, rows, stride):
     return pats
 
 
-@pytest.mark.parametrize("path,G", [(2, 0), (2, 7), (1, 0)])
-def test_graph_replay_changing_lengths(path, G):
+@pytest.mark.parametrize("path,G,grid", [(2, 0, 0), (2, 7, 0), (1, 0, 0), (1, 0, 5)])
+def test_graph_replay_changing_lengths(path, G, grid):
+    # grid=5 < 12 rows: the one-workgroup path hands rows out by a ticket
+    # counter in the workspace, which must be back at zero after each replay.
     import torch
     dev = torch.device("cuda:0")
     rows, stride, K = 12, 65536, 2048
@@ -53,6 +55,8 @@ def test_graph_replay_changing_lengths(path, G):
     L = pats_d[0].clone()
     out = torch.empty((rows, K), dtype=torch.int32, device=dev)
     ov = dict(force_path=path, force_wg_per_row=G) if G else dict(force_path=path)
+    if grid:
+        ov["max_grid"] = grid
     plan = rrt.query_plan(scores, K, **ov)
     note(f"replay plan={plan}")
     assert plan["path"] == path
