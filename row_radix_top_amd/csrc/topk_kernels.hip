@@ -9,26 +9,18 @@
 //
 // * Streaming filter.  A workgroup walks its row (or its chunk of a row) once,
 //   in 2048-element tiles of coalesced vector loads kept in flight by a
-//   register ring.  It keeps an index-ordered candidate buffer in LDS and a
-//   lower bound L on the key of the K-th best element seen so far; an element
-//   is appended only if its key is >= L, which costs one IEEE compare per
-//   element.  When a tile would overflow the buffer, the buffer is compacted
-//   to exactly its K best entries and L rises to just above the K-th best key.
-//   Later elements equal to that key can never win (every kept entry has a
-//   lower index), so the buffer never fills with ties.  Each score is read
-//   from HBM exactly once.
+//   register ring.  It keeps an index-ordered candidate buffer in LDS (fp32
+//   bits and indices) and a lower bound L on the key of the K-th best
+//   element seen so far; an element is appended only if its key is >= L,
+//   which costs one IEEE compare per element, and appending is two LDS
+//   stores.  When a tile would overflow the buffer, the buffer is compacted
+//   and L rises (see compact()).  Each score is read from HBM exactly once.
 //
-// * Running histogram.  Every appended key also bumps an 11-bit (top digit)
-//   LDS histogram of the buffer, so the first radix pass of every selection
-//   is already done; after a compaction the histogram is corrected bin-wise
-//   (bins below the threshold digit empty, the threshold bin holds the number
-//   of entries kept from it).
-//
-// * Radix select.  Later digits (11 then 10 bits) are histogrammed with LDS
-//   atomics over the register-held buffer.  Every wavefront scans a histogram
-//   from the top with DPP prefix sums and finds the threshold digit itself,
-//   so a search costs no barrier.  Ties at the final 32-bit key go to the
-//   lower buffer position, the lower index.
+// * Radix select.  Over the register-held buffer: an 11-bit top-digit
+//   histogram, then 11- and 10-bit digits, each with LDS atomics.  Every
+//   wavefront scans a histogram from the top with DPP prefix sums and finds
+//   the threshold digit itself, so a search costs no barrier.  Ties at the
+//   final 32-bit key go to the lower buffer position, the lower index.
 //
 // * Ordered emit.  Each thread owns a contiguous slice of the buffer; one
 //   workgroup prefix sum of the per-thread (greater, equal) counts gives every
@@ -69,6 +61,11 @@ namespace rrt {
 __device__ __forceinline__ uint32_t ord_key(uint32_t u) {
   u = (u == 0x80000000u) ? 0u : u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inverse of ord_key (up to the sign of zero): the fp32 bits of a key.
+__device__ __forceinline__ uint32_t key_bits(uint32_t k) {
+  return (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
 }
 
 // The float whose key is L: {x : x >= key_floor(L)} == {x : key(x) >= L} for
@@ -129,9 +126,9 @@ struct Shape {
 
 template <bool I16>
 struct __align__(16) Smem {
-  uint32_t key[Shape<I16>::kCap];                 // candidate keys, index order
+  uint32_t val[Shape<I16>::kCap];                 // candidate fp32 bits, index order
   typename Shape<I16>::Idx idx[Shape<I16>::kCap];  // their indices, relative to the chunk start
-  uint32_t hist1[kBins];                          // top-digit histogram of the buffer, kept current
+  uint32_t hist1[kBins];                          // digit histogram; all-zero outside a selection
   uint32_t tile_cnt[2][kElems][kWaves];
   uint32_t wsum[kWaves];
   uint32_t acc[16];
@@ -219,18 +216,18 @@ struct Sel {
   uint32_t eqn;     // entries with (key & pmask) == prefix
 };
 
-// Thread t owns buffer positions [t*S, t*S + S).
+// Thread t owns buffer positions [t*S, t*S + S); their keys go to registers.
 template <bool I16>
 __device__ __forceinline__ void load_keys(const Smem<I16>& sm, uint32_t (&k)[Shape<I16>::kSlots]) {
   constexpr int S = Shape<I16>::kSlots;
   const uint32_t base = threadIdx.x * S;
 #pragma unroll
   for (int q = 0; q < S / 4; ++q) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(&sm.key[base + 4 * q]);
-    k[4 * q + 0] = a.x;
-    k[4 * q + 1] = a.y;
-    k[4 * q + 2] = a.z;
-    k[4 * q + 3] = a.w;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(&sm.val[base + 4 * q]);
+    k[4 * q + 0] = ord_key(a.x);
+    k[4 * q + 1] = ord_key(a.y);
+    k[4 * q + 2] = ord_key(a.z);
+    k[4 * q + 3] = ord_key(a.w);
   }
 }
 
@@ -276,10 +273,22 @@ __device__ __forceinline__ void clear_hist(Smem<I16>& sm) {
   for (int i = threadIdx.x; i < kBins; i += kBlock) sm.hist1[i] = 0u;
 }
 
+// Top-digit histogram (into hist1, which must be zero) of the cnt buffer
+// entries whose keys are in registers, followed by a barrier.
+template <bool I16>
+__device__ __forceinline__ void top_hist(Smem<I16>& sm, const uint32_t (&k)[Shape<I16>::kSlots], uint32_t cnt) {
+  constexpr int S = Shape<I16>::kSlots;
+  const uint32_t base = threadIdx.x * S;
+#pragma unroll
+  for (int j = 0; j < S; ++j)
+    if (base + j < cnt) atomicAdd(&sm.hist1[k[j] >> 21], 1u);
+  __syncthreads();
+}
+
 // The keep best of the cnt buffer entries (keys in registers): those with
 // (key & pmask) > prefix plus the first krem with (key & pmask) == prefix.
 // hist1 must be the top-digit histogram of the buffer.  Later digits reuse
-// hist1 as scratch (used2 = 1): it then no longer describes the buffer.
+// it for their own histograms (used2 = 1).
 // keep <= cnt.
 template <bool I16>
 __device__ Sel select_keep(Smem<I16>& sm, const uint32_t (&k)[Shape<I16>::kSlots], uint32_t cnt,
@@ -324,19 +333,22 @@ __device__ Sel select_keep(Smem<I16>& sm, const uint32_t (&k)[Shape<I16>::kSlots
   return r;
 }
 
-// After-emit bookkeeping of hist1, done between the emit barrier and the
-// next use: kPostCoarse and kPostCompact leave it describing the kept
-// entries, kPostFinal clears it for the next row.
-enum PostEmit { kPostNone = 0, kPostCompact = 1, kPostFinal = 2, kPostCoarse = 3 };
+// After the emit: kPostClear leaves hist1 all-zero (a selection over the
+// buffer), kPostNone leaves it alone.
+enum PostEmit { kPostNone = 0, kPostClear = 1 };
 
 // Writes the chosen entries in buffer order.  An entry is chosen if
 // (key & pmask) > prefix, or if it equals prefix and fewer than take_eq
 // equal entries precede it (gt_base / eq_base count greater / equal entries
 // of earlier chunks of the row).  Its rank = earlier greater entries +
 // min(earlier equal entries, take_eq).  Ranks >= limit are dropped (only
-// reachable with an inconsistent workspace).  To LDS when out is null, else
-// ibase + idx to out[rank].  Contains one barrier; every thread has read its
-// buffer slice before any thread writes.  POST then fixes hist1.
+// reachable with an inconsistent workspace).  To the buffer (as fp32 bits)
+// when out is null.  Otherwise ibase + idx goes to out[rank]: the chosen
+// ranks of this buffer are one contiguous range (the buffer is one
+// contiguous stretch of the row), so they are staged in hist1 and copied
+// out with coalesced stores, which also leaves hist1 all-zero.  Every
+// thread has read its buffer slice, and every wave has finished reading
+// hist1, before any thread writes (the scan's barrier).
 template <bool I16, int POST>
 __device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[Shape<I16>::kSlots], uint32_t cnt,
                                             const Sel& s, uint32_t gt_base, uint32_t eq_base,
@@ -357,6 +369,7 @@ __device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[S
   const uint32_t excl = block_excl_scan(sm, packed, &total);
   uint32_t g = gt_base + (excl & 0xffffu);
   uint32_t e = eq_base + (excl >> 16);
+  const uint32_t first = gt_base + (eq_base < take_eq ? eq_base : take_eq);  // rank of the first chosen
 #pragma unroll
   for (int j = 0; j < S; ++j) {
     const bool valid = base + j < cnt;
@@ -367,35 +380,28 @@ __device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[S
     const uint32_t pos = g + (e < take_eq ? e : take_eq);
     if (take && pos < limit) {
       if (out != nullptr) {
-        out[pos] = (int32_t)(ibase + ix[j]);
+        sm.hist1[pos - first] = ibase + ix[j];
       } else {
-        sm.key[pos] = k[j];
+        sm.val[pos] = key_bits(k[j]);
         sm.idx[pos] = (typename Shape<I16>::Idx)ix[j];
       }
     }
     g += gt ? 1u : 0u;
     e += eq ? 1u : 0u;
   }
-  if (POST == kPostFinal || (POST == kPostCompact && s.used2)) clear_hist(sm);
-  if (POST == kPostCoarse || (POST == kPostCompact && !s.used2)) {
-    // Bins below b1 lose all their entries; every other bin keeps all of its
-    // entries (a selection that stops at the top digit takes bin b1 whole).
-    for (uint32_t i = threadIdx.x; i < (uint32_t)kBins; i += kBlock)
-      if (i < s.b1) sm.hist1[i] = 0u;
-  }
-  if (POST == kPostCompact && s.used2) {
-    // hist1 served as scratch: rebuild it from the kept entries.
+  if (out != nullptr) {
+    const uint32_t eq_end = eq_base + (total >> 16);
+    uint32_t last = gt_base + (total & 0xffffu) + (eq_end < take_eq ? eq_end : take_eq);
+    last = last < limit ? last : limit;
+    const uint32_t m = last > first ? last - first : 0u;
     __syncthreads();
-    uint32_t e2 = eq_base + (excl >> 16);
-#pragma unroll
-    for (int j = 0; j < S; ++j) {
-      const bool valid = base + j < cnt;
-      const uint32_t km = k[j] & s.pmask;
-      const bool gt = valid && km > s.prefix;
-      const bool eq = valid && km == s.prefix;
-      if (gt || (eq && e2 < take_eq)) atomicAdd(&sm.hist1[k[j] >> 21], 1u);
-      e2 += eq ? 1u : 0u;
+    for (uint32_t i = threadIdx.x; i < (uint32_t)kBins; i += kBlock) {
+      const uint32_t v = sm.hist1[i];
+      sm.hist1[i] = 0u;
+      if (i < m) out[first + i] = (int32_t)v;
     }
+  } else if (POST == kPostClear) {
+    clear_hist(sm);
   }
 }
 
@@ -432,6 +438,7 @@ __device__ __noinline__ uint64_t compact(Smem<I16>& sm, uint32_t cnt, uint32_t k
   constexpr uint32_t CAP = (uint32_t)Shape<I16>::kCap;
   uint32_t k[S];
   load_keys<I16>(sm, k);
+  top_hist<I16>(sm, k, cnt);
   bool spec = false;
   if (spec_n != 0u) {
     const uint64_t want = ((uint64_t)kSpecNum * keep * cnt + (uint64_t)kSpecDen * spec_n - 1) /
@@ -459,7 +466,7 @@ __device__ __noinline__ uint64_t compact(Smem<I16>& sm, uint32_t cnt, uint32_t k
       s.krem1 = f.in_bin;
       s.used2 = 0u;
       s.eqn = f.in_bin;
-      emit_chosen<I16, kPostCoarse>(sm, k, cnt, s, 0u, 0u, 0xffffffffu, nullptr, CAP, 0u);
+      emit_chosen<I16, kPostClear>(sm, k, cnt, s, 0u, 0u, 0xffffffffu, nullptr, CAP, 0u);
       const uint32_t Ln = s.prefix > L ? s.prefix : L;
       return ((uint64_t)(f.above + f.in_bin) << 32) | Ln;
     }
@@ -468,7 +475,7 @@ __device__ __noinline__ uint64_t compact(Smem<I16>& sm, uint32_t cnt, uint32_t k
   // entry equal to the r-th best key too.
   const Sel s = select_keep<I16>(sm, k, cnt, keep);
   const uint32_t take_eq = spec ? 0xffffffffu : s.krem;
-  emit_chosen<I16, kPostCompact>(sm, k, cnt, s, 0u, 0u, take_eq, nullptr, CAP, 0u);
+  emit_chosen<I16, kPostClear>(sm, k, cnt, s, 0u, 0u, take_eq, nullptr, CAP, 0u);
   uint32_t Ln, cn;
   if (spec) {
     Ln = s.prefix;
@@ -484,44 +491,52 @@ __device__ __noinline__ uint64_t compact(Smem<I16>& sm, uint32_t cnt, uint32_t k
   return ((uint64_t)cn << 32) | Ln;
 }
 
-// The K best of the buffer, written to out in index order; hist1 is left
-// cleared for the next row.
+// The K best of the buffer, written to out in index order.
 template <bool I16>
 __device__ __noinline__ void final_select(Smem<I16>& sm, uint32_t cnt, uint32_t K, int32_t* out) {
   constexpr int S = Shape<I16>::kSlots;
   uint32_t k[S];
   load_keys<I16>(sm, k);
+  top_hist<I16>(sm, k, cnt);
   const Sel s = select_keep<I16>(sm, k, cnt, K);
-  emit_chosen<I16, kPostFinal>(sm, k, cnt, s, 0u, 0u, s.krem, out, K, 0u);
+  emit_chosen<I16, kPostClear>(sm, k, cnt, s, 0u, 0u, s.krem, out, K, 0u);
 }
 
 // ---------------------------------------------------------------------------
 // Streaming filter over [c0, c1) of one row
 // ---------------------------------------------------------------------------
 
+// Wave-uniform copy of a value that is the same in every lane, so that the
+// compiler keeps it (and what is computed from it) in scalar registers.
+__device__ __forceinline__ uint32_t uni(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+
+// One full tile starting at `tile` (a wave-uniform pointer): thread t loads
+// elements u * 256 * VEC + t * VEC .. + VEC - 1, so each load instruction of a
+// wave covers one contiguous 64 * VEC * 4-byte run.
 template <int VEC>
-__device__ __forceinline__ void load_full(const float* __restrict__ rowp, uint32_t p0, float (&x)[kElems]) {
+__device__ __forceinline__ void load_full(const float* __restrict__ tile, float (&x)[kElems]) {
   const uint32_t t = threadIdx.x;
 #pragma unroll
   for (int u = 0; u < kElems / VEC; ++u) {
-    const uint32_t pos = p0 + (uint32_t)u * (kBlock * VEC) + t * VEC;
+    const uint32_t pos = (uint32_t)u * (kBlock * VEC) + t * VEC;
     if constexpr (VEC == 4) {
-      const float4 v = *reinterpret_cast<const float4*>(rowp + pos);
+      const float4 v = *reinterpret_cast<const float4*>(tile + pos);
       x[u * 4 + 0] = v.x;
       x[u * 4 + 1] = v.y;
       x[u * 4 + 2] = v.z;
       x[u * 4 + 3] = v.w;
     } else if constexpr (VEC == 2) {
-      const float2 v = *reinterpret_cast<const float2*>(rowp + pos);
+      const float2 v = *reinterpret_cast<const float2*>(tile + pos);
       x[u * 2 + 0] = v.x;
       x[u * 2 + 1] = v.y;
     } else {
-      x[u] = rowp[pos];
+      x[u] = tile[pos];
     }
   }
 }
 
-// The partial last tile: per-element bounds checks, nothing read at or past c1.
+// The partial last tile [p0, c1): per-element bounds checks, nothing read at
+// or past c1.
 template <int VEC>
 __device__ __forceinline__ void load_tail(const float* __restrict__ rowp, uint32_t c1, uint32_t p0,
                                           float (&x)[kElems]) {
@@ -534,97 +549,112 @@ __device__ __forceinline__ void load_tail(const float* __restrict__ rowp, uint32
   }
 }
 
+// Whether element e of this thread's share of a tile is accepted: inside
+// the chunk and at least the bound's float bf.  Evaluated where it is used
+// (a compare is one instruction; a stored per-lane flag would cost more to
+// keep and unpack).
+template <int VEC, bool FULL>
+__device__ __forceinline__ bool accepted(const float (&x)[kElems], int e, uint32_t pbase, uint32_t c1, float bf) {
+  const int u = e / VEC, c = e % VEC;
+  const bool in = FULL || pbase + (uint32_t)u * (kBlock * VEC) + c < c1;
+  return in && x[e] >= bf;
+}
+
+// The wave's ballot of each element's acceptance.
+template <int VEC, bool FULL>
+__device__ __forceinline__ void tile_accept(const float (&x)[kElems], uint32_t pbase, uint32_t c1, float bf,
+                                            uint64_t (&bal)[kElems]) {
+#pragma unroll
+  for (int e = 0; e < kElems; ++e) bal[e] = ballot(accepted<VEC, FULL>(x, e, pbase, c1, bf));
+}
+
 // Per-wave counts of accepted elements for each load slot go through LDS
 // (double-buffered by par); returns the tile total and this wave's offset
-// for each slot.
+// for each slot, all wave-uniform.
 template <bool I16, int VEC>
-__device__ __forceinline__ uint32_t tile_exchange(Smem<I16>& sm, const bool (&a)[kElems], int& par,
+__device__ __forceinline__ uint32_t tile_exchange(Smem<I16>& sm, const uint64_t (&bal)[kElems], int& par,
                                                   uint32_t (&off)[kElems / VEC]) {
   constexpr int NL = kElems / VEC;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t w = uni(threadIdx.x >> 6);
 #pragma unroll
   for (int u = 0; u < NL; ++u) {
     uint32_t c = 0;
 #pragma unroll
-    for (int cc = 0; cc < VEC; ++cc) c += popc64(ballot(a[u * VEC + cc]));
+    for (int cc = 0; cc < VEC; ++cc) c += popc64(bal[u * VEC + cc]);
     if (lane == 0) sm.tile_cnt[par][u][w] = c;
   }
   __syncthreads();
   uint32_t total = 0;
 #pragma unroll
   for (int u = 0; u < NL; ++u) {
-    const uint4 v = *reinterpret_cast<const uint4*>(sm.tile_cnt[par][u]);
-    const uint32_t before = (w > 0 ? v.x : 0u) + (w > 1 ? v.y : 0u) + (w > 2 ? v.z : 0u);
-    off[u] = total + before;
-    total += v.x + v.y + v.z + v.w;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(sm.tile_cnt[par][u]);
+    const uint32_t v0 = uni(v.x), v1 = uni(v.y), v2 = uni(v.z), v3 = uni(v.w);
+    off[u] = total + (w > 0 ? v0 : 0u) + (w > 1 ? v1 : 0u) + (w > 2 ? v2 : 0u);
+    total += v0 + v1 + v2 + v3;
   }
   par ^= 1;
   return total;
 }
 
-template <int VEC, bool FULL>
-__device__ __forceinline__ void tile_accept(const float (&x)[kElems], uint32_t pbase, uint32_t c1, float bf,
-                                            bool (&a)[kElems]) {
-#pragma unroll
-  for (int u = 0; u < kElems / VEC; ++u) {
-#pragma unroll
-    for (int c = 0; c < VEC; ++c) {
-      const int e = u * VEC + c;
-      const bool in = FULL || pbase + (uint32_t)u * (kBlock * VEC) + c < c1;
-      a[e] = in && x[e] >= bf;
-    }
-  }
-}
-
-// Appends the accepted elements of one tile at cnt + (their rank in the tile).
-template <bool I16, int VEC>
-__device__ __forceinline__ void tile_append(Smem<I16>& sm, const float (&x)[kElems], const bool (&a)[kElems],
-                                            const uint32_t (&off)[kElems / VEC], uint32_t cnt, uint32_t rel) {
+// Appends the accepted elements of one tile, in index order, at cnt + their
+// rank in the tile: fp32 bits and the index relative to the chunk start.
+template <bool I16, int VEC, bool FULL>
+__device__ __forceinline__ void tile_append(Smem<I16>& sm, const float (&x)[kElems], const uint64_t (&bal)[kElems],
+                                            const uint32_t (&off)[kElems / VEC], uint32_t cnt, uint32_t pbase,
+                                            uint32_t c1, float bf, uint32_t rel) {
   constexpr int NL = kElems / VEC;
 #pragma unroll
   for (int u = 0; u < NL; ++u) {
     uint32_t r = cnt + off[u];
 #pragma unroll
-    for (int c = 0; c < VEC; ++c) r += lanes_below(ballot(a[u * VEC + c]));
+    for (int c = 0; c < VEC; ++c) r = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[u * VEC + c] >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)bal[u * VEC + c], r));
 #pragma unroll
     for (int c = 0; c < VEC; ++c) {
       const int e = u * VEC + c;
-      if (a[e]) {
-        const uint32_t key = ord_key(__float_as_uint(x[e]));
-        sm.key[r] = key;
+      const bool take = accepted<VEC, FULL>(x, e, pbase, c1, bf);
+      if (take) {
+        sm.val[r] = __float_as_uint(x[e]);
         sm.idx[r] = (typename Shape<I16>::Idx)(rel + (uint32_t)u * (kBlock * VEC) + c);
-        atomicAdd(&sm.hist1[key >> 21], 1u);
       }
-      r += a[e] ? 1u : 0u;
+      r += take ? 1u : 0u;
     }
   }
 }
+
+// Stream state of one workgroup, all wave-uniform: buffer count, bound (as a
+// key and as the float every accepted element must reach), the pending
+// speculation (row length, or 0), and the tile-count parity.
+struct Stream {
+  uint32_t cnt, L, spec;
+  float bf;
+  int par;
+};
 
 // Filters one tile into the candidate buffer, compacting first if the
 // tile's accepted elements would not fit.  p0 and c1 are absolute row
 // positions; indices are stored relative to ibase.
 template <bool I16, int VEC, bool FULL>
 __device__ __forceinline__ void process_tile(Smem<I16>& sm, const float (&x)[kElems], uint32_t p0, uint32_t c1,
-                                             uint32_t ibase, uint32_t keep, uint32_t& cnt, uint32_t& L,
-                                             uint32_t& spec, int& par) {
+                                             uint32_t ibase, uint32_t keep, Stream& st) {
   constexpr int NL = kElems / VEC;
   const uint32_t pbase = p0 + threadIdx.x * VEC;
-  bool a[kElems];
+  uint64_t bal[kElems];
   uint32_t off[NL];
-  tile_accept<VEC, FULL>(x, pbase, c1, accept_floor(L), a);
-  uint32_t total = tile_exchange<I16, VEC>(sm, a, par, off);
-  if (cnt + total > (uint32_t)Shape<I16>::kCap) {
-    const uint64_t r = compact<I16>(sm, cnt, keep, L, spec);
-    spec = 0u;
-    L = (uint32_t)r;
-    cnt = (uint32_t)(r >> 32);
-    tile_accept<VEC, FULL>(x, pbase, c1, accept_floor(L), a);
-    total = tile_exchange<I16, VEC>(sm, a, par, off);
-    if (total != 0) tile_append<I16, VEC>(sm, x, a, off, cnt, pbase - ibase);
-  } else if (total != 0) {
-    tile_append<I16, VEC>(sm, x, a, off, cnt, pbase - ibase);
+  tile_accept<VEC, FULL>(x, pbase, c1, st.bf, bal);
+  uint32_t total = tile_exchange<I16, VEC>(sm, bal, st.par, off);
+  if (st.cnt + total > (uint32_t)Shape<I16>::kCap) {
+    const uint64_t r = compact<I16>(sm, st.cnt, keep, st.L, st.spec);
+    st.spec = 0u;
+    st.L = uni((uint32_t)r);
+    st.cnt = uni((uint32_t)(r >> 32));
+    st.bf = accept_floor(st.L);
+    tile_accept<VEC, FULL>(x, pbase, c1, st.bf, bal);
+    total = tile_exchange<I16, VEC>(sm, bal, st.par, off);
   }
-  cnt += total;
+  if (total != 0) tile_append<I16, VEC, FULL>(sm, x, bal, off, st.cnt, pbase, c1, st.bf, pbase - ibase);
+  st.cnt += total;
 }
 
 // Streams [c0, c1) through the filter.  Full tiles come through a ring of
@@ -638,13 +668,21 @@ template <bool I16, int VEC>
 __device__ void stream_chunk(Smem<I16>& sm, const float* __restrict__ rowp, uint32_t c0, uint32_t c1,
                              uint32_t keep, uint32_t& cnt, uint32_t& L, uint32_t spec) {
   constexpr int PF = kPrefetch;
+  c0 = uni(c0);
+  c1 = uni(c1);
+  Stream st;
+  st.cnt = uni(cnt);
+  st.L = uni(L);
+  st.spec = uni(spec);
+  st.bf = accept_floor(st.L);
+  st.par = 0;
   const uint32_t F = (c1 - c0) / kTile;  // full tiles
-  int par = 0;
+  const float* base = rowp + c0;
   if (F > 0) {
     float buf[PF][kElems];
 #pragma unroll
     for (int s = 0; s < PF - 1; ++s) {
-      load_full<VEC>(rowp, c0 + ((uint32_t)s < F ? (uint32_t)s : F - 1) * kTile, buf[s]);
+      load_full<VEC>(base + ((uint32_t)s < F ? (uint32_t)s : F - 1) * kTile, buf[s]);
       __builtin_amdgcn_sched_barrier(0);  // keep tiles in issue order: waits then retire oldest first
     }
     // Whole rounds of PF tiles: one uniform back edge, so the compiler's
@@ -655,25 +693,27 @@ __device__ void stream_chunk(Smem<I16>& sm, const float* __restrict__ rowp, uint
       for (int slot = 0; slot < PF; ++slot) {
         const uint32_t j = j0 + slot;
         const uint32_t jn = j + PF - 1 < F ? j + PF - 1 : F - 1;
-        load_full<VEC>(rowp, c0 + jn * kTile, buf[(slot + PF - 1) % PF]);
+        load_full<VEC>(base + jn * kTile, buf[(slot + PF - 1) % PF]);
         __builtin_amdgcn_sched_barrier(0);
-        process_tile<I16, VEC, true>(sm, buf[slot], c0 + j * kTile, c1, c0, keep, cnt, L, spec, par);
+        process_tile<I16, VEC, true>(sm, buf[slot], c0 + j * kTile, c1, c0, keep, st);
       }
     }
     // The last F % PF full tiles are already in buf[0..]: no more loads.
 #pragma unroll
     for (int slot = 0; slot < PF - 1; ++slot) {
       const uint32_t j = Fr + slot;
-      if (j < F) process_tile<I16, VEC, true>(sm, buf[slot], c0 + j * kTile, c1, c0, keep, cnt, L, spec, par);
+      if (j < F) process_tile<I16, VEC, true>(sm, buf[slot], c0 + j * kTile, c1, c0, keep, st);
     }
   }
   const uint32_t pt = c0 + F * kTile;
   if (pt < c1) {
     float x[kElems];
     load_tail<VEC>(rowp, c1, pt, x);
-    process_tile<I16, VEC, false>(sm, x, pt, c1, c0, keep, cnt, L, spec, par);
+    process_tile<I16, VEC, false>(sm, x, pt, c1, c0, keep, st);
   }
   __syncthreads();
+  cnt = st.cnt;
+  L = st.L;
 }
 
 __device__ __forceinline__ int64_t clamp_len(const KernelParams& p, int row) {
@@ -714,9 +754,13 @@ __global__ void __launch_bounds__(kBlock) topk_single_kernel(KernelParams p) {
   uint32_t* ticket = p.ws != nullptr ? reinterpret_cast<uint32_t*>(p.ws + kTicketOff) : nullptr;
   uint32_t redo = 0u;  // 1 while a row is streamed again after a failed speculation
   uint32_t next = 0u;  // thread 0: the row after this one
+  bool drawn = false;  // thread 0: next is set for the current row
   int row = blockIdx.x;
-  while (row < p.num_rows) {
-    if (threadIdx.x == 0 && !redo) {
+  // The first row's draw waits until its scores are streamed: at launch every
+  // workgroup would hit the counter at once, and the wait for the first tile
+  // would include that queue.
+  auto draw = [&]() {
+    if (threadIdx.x == 0 && !drawn) {
       if (ticket != nullptr) {
         const uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (t == (uint32_t)p.num_rows - 1u) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -724,7 +768,12 @@ __global__ void __launch_bounds__(kBlock) topk_single_kernel(KernelParams p) {
       } else {
         next = (uint32_t)row + gridDim.x;
       }
+      drawn = true;
     }
+  };
+  bool first_row = true;
+  while (row < p.num_rows) {
+    if (!first_row) draw();
     const int64_t n = clamp_len(p, row);
     int32_t* out = p.out + (int64_t)row * p.K;
     if (n <= (int64_t)K) {
@@ -743,11 +792,15 @@ __global__ void __launch_bounds__(kBlock) topk_single_kernel(KernelParams p) {
         continue;
       }
       redo = 0u;
+      draw();
       final_select<I16>(sm, cnt, K, out);
     }
+    draw();
+    first_row = false;
+    drawn = false;
     if (threadIdx.x == 0) sm.acc[8] = next;
     __syncthreads();
-    row = (int)min(sm.acc[8], (uint32_t)p.num_rows);
+    row = (int)uni(min(sm.acc[8], (uint32_t)p.num_rows));
     __syncthreads();  // every thread has read the next row before it is overwritten
   }
 }
@@ -879,8 +932,9 @@ __global__ void __launch_bounds__(kBlock) topk_multi_kernel(KernelParams p) {
   load_keys<I16>(sm, k);
   const uint32_t base = (uint32_t)t * S;
 
-  // Round 1: the chunk's top-digit histogram (already in hist1) into the
-  // row's, then the row-wide threshold digit from a copy of the row's.
+  // Round 1: the chunk's top-digit histogram into the row's, then the
+  // row-wide threshold digit from a copy of the row's.
+  top_hist<I16>(sm, k, cnt);
   merge_hist(sm.hist1, h1);
   group_barrier(ctr, 1u * grow, p.spin_limit, err);
   load_hist(sm.hist1, h1);
@@ -1065,7 +1119,7 @@ __global__ void __launch_bounds__(kBlock) read_ref_kernel(KernelParams p) {
       float buf[PF][kElems];
 #pragma unroll
       for (int s = 0; s < PF - 1; ++s) {
-        load_full<VEC>(rowp, ((uint32_t)s < F ? (uint32_t)s : F - 1) * kTile, buf[s]);
+        load_full<VEC>(rowp + ((uint32_t)s < F ? (uint32_t)s : F - 1) * kTile, buf[s]);
         __builtin_amdgcn_sched_barrier(0);
       }
       const uint32_t Fr = F - F % PF;
@@ -1074,7 +1128,7 @@ __global__ void __launch_bounds__(kBlock) read_ref_kernel(KernelParams p) {
         for (int slot = 0; slot < PF; ++slot) {
           const uint32_t j = j0 + slot;
           const uint32_t jn = j + PF - 1 < F ? j + PF - 1 : F - 1;
-          load_full<VEC>(rowp, jn * kTile, buf[(slot + PF - 1) % PF]);
+          load_full<VEC>(rowp + jn * kTile, buf[(slot + PF - 1) % PF]);
           __builtin_amdgcn_sched_barrier(0);
           m = tile_max(buf[slot], m);
         }
