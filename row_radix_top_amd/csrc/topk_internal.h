@@ -11,7 +11,8 @@ constexpr int kBlock = 256;                 // threads per workgroup (4 wave64)
 constexpr int kWaves = kBlock / 64;
 constexpr int kElems = 8;                   // fp32 elements per thread per tile
 constexpr int kTile = kBlock * kElems;      // 2048 elements streamed per tile
-constexpr int kBins = 2048;                 // 11-bit radix digit
+constexpr int kBins = 2048;                 // bins of a first-pass histogram
+constexpr int kSmallBins = 256;             // bins of a second-pass histogram (= kBlock)
 constexpr int kPrefetch = 4;                // register ring of tiles per thread
 constexpr int kMaxGroup = 64;               // most workgroups that may share a row
 constexpr int kMaxK = 2048;

@@ -110,6 +110,10 @@ __device__ __forceinline__ uint32_t lane_value(uint32_t v, int lane) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
 }
 
+// Wave-uniform copy of a value that is the same in every lane, so that the
+// compiler keeps it (and what is computed from it) in scalar registers.
+__device__ __forceinline__ uint32_t uni(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+
 // ---------------------------------------------------------------------------
 // Shared memory of one workgroup
 // ---------------------------------------------------------------------------
@@ -129,6 +133,8 @@ struct __align__(16) Smem {
   uint32_t val[Shape<I16>::kCap];                 // candidate fp32 bits, index order
   typename Shape<I16>::Idx idx[Shape<I16>::kCap];  // their indices, relative to the chunk start
   uint32_t hist1[kBins];                          // digit histogram; all-zero outside a selection
+  uint32_t hs[kSmallBins];                        // second digit histogram; all-zero outside a selection
+  uint32_t red[2 * kWaves];                       // per-wave partial results
   uint32_t tile_cnt[2][kElems][kWaves];
   uint32_t wsum[kWaves];
   uint32_t acc[16];
@@ -203,312 +209,411 @@ __device__ __forceinline__ uint32_t block_excl_scan(Smem<I16>& sm, uint32_t v, u
 
 // ---------------------------------------------------------------------------
 // Selection over the candidate buffer
+//
+// The cnt entries are split into 256 contiguous slices of sp entries (sp
+// even, just enough to cover cnt), thread t owning positions [t*sp, t*sp +
+// sp); their keys sit in registers k[0..sp).  Work per selection therefore
+// scales with cnt, not with the buffer's capacity.
+//
+// A selection narrows a key interval [lo, hi] known to hold the wanted
+// entry.  Each pass histograms the keys inside it by (key - lo) >> s, with s
+// chosen so the interval fills at most 2048 (even passes) or 256 (odd
+// passes) bins, finds the bin holding the krem-th largest, and continues in
+// that bin.  Starting from the exact range of the keys, the first pass
+// usually leaves a handful of entries, whatever the data's scale; 32 bits
+// take at most four passes.  Passes alternate between two histograms, so
+// the second pass needs no clearing barrier.
 // ---------------------------------------------------------------------------
 
+// Chosen set of a selection: every key > hi, plus the first `take` entries
+// (in buffer order, i.e. lowest index first) with lo <= key <= hi.
 struct Sel {
-  uint32_t prefix;  // decided key bits
-  uint32_t pmask;   // which bits are decided
-  uint32_t krem;    // entries equal to prefix (under pmask) to take, lowest position first
-  uint32_t ok;
-  uint32_t b1;      // threshold top digit
-  uint32_t krem1;   // entries taken from bin b1
-  uint32_t used2;   // hist1 was reused for a later digit
-  uint32_t eqn;     // entries with (key & pmask) == prefix
+  uint32_t lo, hi, take;
+  uint32_t above;   // entries with key > hi
+  uint32_t in_bin;  // entries with lo <= key <= hi
+  uint32_t ok;      // 0 if a histogram was inconsistent
+  bool all_in;      // take covers every entry inside [lo, hi]: the set is key >= lo
 };
 
-// Thread t owns buffer positions [t*S, t*S + S); their keys go to registers.
 template <bool I16>
-__device__ __forceinline__ void load_keys(const Smem<I16>& sm, uint32_t (&k)[Shape<I16>::kSlots]) {
-  constexpr int S = Shape<I16>::kSlots;
-  const uint32_t base = threadIdx.x * S;
-#pragma unroll
-  for (int q = 0; q < S / 4; ++q) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(&sm.val[base + 4 * q]);
-    k[4 * q + 0] = ord_key(a.x);
-    k[4 * q + 1] = ord_key(a.y);
-    k[4 * q + 2] = ord_key(a.z);
-    k[4 * q + 3] = ord_key(a.w);
-  }
+__device__ __forceinline__ uint32_t slice_of(uint32_t cnt) {
+  constexpr uint32_t S = (uint32_t)Shape<I16>::kSlots;
+  uint32_t sp = (uni(cnt) + kBlock - 1) / kBlock;
+  sp = (sp + 1u) & ~1u;
+  return sp < S ? sp : S;
 }
 
+// Entries of this thread's slice that hold data (of cnt): slice positions
+// j < valid_in_slice(...) are valid.
+__device__ __forceinline__ uint32_t valid_in_slice(uint32_t sp, uint32_t cnt) {
+  const uint32_t base = threadIdx.x * sp;
+  const uint32_t v = cnt > base ? cnt - base : 0u;
+  return v < sp ? v : sp;
+}
+
+// Keys of this thread's slice (positions t*sp + j, j < sp).
 template <bool I16>
-__device__ __forceinline__ void load_idx(const Smem<I16>& sm, uint32_t (&ix)[Shape<I16>::kSlots]) {
+__device__ __forceinline__ void load_keys(const Smem<I16>& sm, uint32_t (&k)[Shape<I16>::kSlots], uint32_t sp) {
   constexpr int S = Shape<I16>::kSlots;
-  const uint32_t base = threadIdx.x * S;
-  if constexpr (I16) {
+  const uint32_t base = threadIdx.x * sp;
 #pragma unroll
-    for (int q = 0; q < S / 4; ++q) {
-      const u32x2 a = *reinterpret_cast<const u32x2*>(&sm.idx[base + 4 * q]);
-      ix[4 * q + 0] = a.x & 0xffffu;
-      ix[4 * q + 1] = a.x >> 16;
-      ix[4 * q + 2] = a.y & 0xffffu;
-      ix[4 * q + 3] = a.y >> 16;
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < S / 4; ++q) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(&sm.idx[base + 4 * q]);
-      ix[4 * q + 0] = a.x;
-      ix[4 * q + 1] = a.y;
-      ix[4 * q + 2] = a.z;
-      ix[4 * q + 3] = a.w;
+  for (int q = 0; q < S / 2; ++q) {
+    if ((uint32_t)(2 * q) < sp) {
+      const u32x2 a = *reinterpret_cast<const u32x2*>(&sm.val[base + 2 * q]);
+      k[2 * q + 0] = ord_key(a.x);
+      k[2 * q + 1] = ord_key(a.y);
     }
   }
 }
 
-// Histogram (into hist1, which must be zero) of one more digit over the
-// entries matching the decided prefix.
-template <bool I16, int SHIFT, uint32_t DMASK>
-__device__ __forceinline__ void digit_hist(Smem<I16>& sm, const uint32_t (&k)[Shape<I16>::kSlots], uint32_t cnt,
-                                           uint32_t prefix, uint32_t pmask) {
+template <bool I16>
+__device__ __forceinline__ void load_idx(const Smem<I16>& sm, uint32_t (&ix)[Shape<I16>::kSlots], uint32_t sp) {
   constexpr int S = Shape<I16>::kSlots;
-  const uint32_t base = threadIdx.x * S;
+  const uint32_t base = threadIdx.x * sp;
 #pragma unroll
-  for (int j = 0; j < S; ++j)
-    if (base + j < cnt && (k[j] & pmask) == prefix) atomicAdd(&sm.hist1[(k[j] >> SHIFT) & DMASK], 1u);
+  for (int q = 0; q < S / 2; ++q) {
+    if ((uint32_t)(2 * q) < sp) {
+      if constexpr (I16) {
+        const uint32_t a = *reinterpret_cast<const uint32_t*>(&sm.idx[base + 2 * q]);
+        ix[2 * q + 0] = a & 0xffffu;
+        ix[2 * q + 1] = a >> 16;
+      } else {
+        const u32x2 a = *reinterpret_cast<const u32x2*>(&sm.idx[base + 2 * q]);
+        ix[2 * q + 0] = a.x;
+        ix[2 * q + 1] = a.y;
+      }
+    }
+  }
 }
 
+static_assert(kSmallBins == kBlock, "one second-pass bin per thread");
+
 template <bool I16>
-__device__ __forceinline__ void clear_hist(Smem<I16>& sm) {
+__device__ __forceinline__ void clear_hists(Smem<I16>& sm) {
   for (int i = threadIdx.x; i < kBins; i += kBlock) sm.hist1[i] = 0u;
+  sm.hs[threadIdx.x] = 0u;
 }
 
-// Top-digit histogram (into hist1, which must be zero) of the cnt buffer
-// entries whose keys are in registers, followed by a barrier.
+// Maximum over the wavefront by DPP row shifts and row broadcasts; every
+// lane gets the result.
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  uint32_t x = v;
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true));   // row_shr:1
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true));   // row_shr:2
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true));   // row_shr:4
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true));   // row_shr:8
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return lane_value(x, 63);
+}
+
+// Minimum over the wavefront (lanes without a DPP source keep the identity).
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+  const int id = -1;
+  uint32_t x = v;
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x111, 0xf, 0xf, false));  // row_shr:1
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x112, 0xf, 0xf, false));  // row_shr:2
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x114, 0xf, 0xf, false));  // row_shr:4
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x118, 0xf, 0xf, false));  // row_shr:8
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return lane_value(x, 63);
+}
+
+// [lo, hi]: the smallest and largest key of the cnt entries (both wave-
+// uniform).  Contains one barrier.
 template <bool I16>
-__device__ __forceinline__ void top_hist(Smem<I16>& sm, const uint32_t (&k)[Shape<I16>::kSlots], uint32_t cnt) {
+__device__ __forceinline__ void key_range(Smem<I16>& sm, const uint32_t (&k)[Shape<I16>::kSlots], uint32_t sp,
+                                          uint32_t cnt, uint32_t& lo, uint32_t& hi) {
   constexpr int S = Shape<I16>::kSlots;
-  const uint32_t base = threadIdx.x * S;
+  const uint32_t nv = valid_in_slice(sp, cnt);
+  uint32_t mn = 0xffffffffu, mx = 0;
 #pragma unroll
-  for (int j = 0; j < S; ++j)
-    if (base + j < cnt) atomicAdd(&sm.hist1[k[j] >> 21], 1u);
-  __syncthreads();
-}
-
-// The keep best of the cnt buffer entries (keys in registers): those with
-// (key & pmask) > prefix plus the first krem with (key & pmask) == prefix.
-// hist1 must be the top-digit histogram of the buffer.  Later digits reuse
-// it for their own histograms (used2 = 1).
-// keep <= cnt.
-template <bool I16>
-__device__ Sel select_keep(Smem<I16>& sm, const uint32_t (&k)[Shape<I16>::kSlots], uint32_t cnt,
-                           uint32_t keep) {
-  Sel r;
-  const Found f1 = wave_find<2048>(sm.hist1, keep);
-  r.b1 = f1.bin;
-  r.ok = f1.ok;
-  r.krem = keep - f1.above;
-  r.krem1 = r.krem;
-  r.prefix = f1.bin << 21;
-  r.pmask = 0xffe00000u;
-  r.used2 = 0u;
-  r.eqn = f1.in_bin;
-  if (f1.in_bin != r.krem) {
-    __syncthreads();  // every wave has read hist1
-    clear_hist(sm);
-    __syncthreads();
-    digit_hist<I16, 10, 2047u>(sm, k, cnt, r.prefix, r.pmask);
-    __syncthreads();
-    const Found f2 = wave_find<2048>(sm.hist1, r.krem);
-    r.used2 = 1u;
-    r.ok &= f2.ok;
-    r.krem -= f2.above;
-    r.prefix |= f2.bin << 10;
-    r.pmask = 0xfffffc00u;
-    r.eqn = f2.in_bin;
-    if (f2.in_bin != r.krem) {
-      __syncthreads();
-      clear_hist(sm);
-      __syncthreads();
-      digit_hist<I16, 0, 1023u>(sm, k, cnt, r.prefix, r.pmask);
-      __syncthreads();
-      const Found f3 = wave_find<1024>(sm.hist1, r.krem);
-      r.ok &= f3.ok;
-      r.krem -= f3.above;
-      r.prefix |= f3.bin;
-      r.pmask = 0xffffffffu;
-      r.eqn = f3.in_bin;
+  for (int j = 0; j < S; ++j) {
+    if ((uint32_t)(j) < sp) {
+      if ((uint32_t)j < nv) {
+        mn = min(mn, k[j]);
+        mx = max(mx, k[j]);
+      }
     }
   }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sm.red[w] = mn;
+    sm.red[kWaves + w] = mx;
+  }
+  __syncthreads();
+  const u32x4 a = *reinterpret_cast<const u32x4*>(&sm.red[0]);
+  const u32x4 b = *reinterpret_cast<const u32x4*>(&sm.red[kWaves]);
+  lo = uni(min(min(a.x, a.y), min(a.z, a.w)));
+  hi = uni(max(max(b.x, b.y), max(b.z, b.w)));
+}
+
+// Narrows [lo, hi] (which holds every entry) to the bin holding the keep-th
+// largest entry.  Stops when that bin is taken whole (its entries are
+// exactly the ones still needed, or entries above plus the bin number at
+// most stop_total) or holds a single key; the result's take is then the
+// whole bin or the entries still needed.  stop_total = 0 asks for an exact
+// selection of keep entries.  Both histograms are zero on entry and hold
+// garbage on return.
+template <bool I16>
+__device__ Sel range_select(Smem<I16>& sm, const uint32_t (&k)[Shape<I16>::kSlots], uint32_t sp, uint32_t cnt,
+                            uint32_t lo, uint32_t hi, uint32_t keep, uint32_t stop_total) {
+  constexpr int S = Shape<I16>::kSlots;
+  const uint32_t nv = valid_in_slice(sp, cnt);
+  Sel r;
+  r.ok = 1u;
+  r.above = 0u;
+  r.in_bin = 0u;
+  uint32_t krem = keep;
+  bool whole = false;
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const bool big = (pass & 1) == 0;
+    uint32_t* h = big ? sm.hist1 : sm.hs;
+    const uint32_t bits = big ? 11u : 8u;
+    if (pass >= 2) {  // this histogram was used two passes ago
+      __syncthreads();
+      if (big) {
+        for (int i = threadIdx.x; i < kBins; i += kBlock) h[i] = 0u;
+      } else {
+        h[threadIdx.x] = 0u;
+      }
+      __syncthreads();
+    }
+    const uint32_t range = hi - lo;
+    const uint32_t nb = range != 0u ? 32u - (uint32_t)__builtin_clz(range) : 0u;
+    const uint32_t sh = nb > bits ? nb - bits : 0u;
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      if ((uint32_t)(j) < sp) {
+        if ((uint32_t)j < nv && k[j] - lo <= range) atomicAdd(&h[(k[j] - lo) >> sh], 1u);
+      }
+    }
+    __syncthreads();
+    const Found f = big ? wave_find<kBins>(h, krem) : wave_find<kSmallBins>(h, krem);
+    r.ok &= f.ok;
+    krem -= f.above;
+    r.above += f.above;
+    r.in_bin = f.in_bin;
+    lo += f.bin << sh;
+    const uint32_t width = (1u << sh) - 1u;
+    hi = hi - lo > width ? lo + width : hi;
+    whole = f.in_bin == krem || r.above + f.in_bin <= stop_total;
+    if (whole || sh == 0u || !f.ok) break;
+  }
+  r.lo = lo;
+  r.hi = hi;
+  r.take = whole ? r.in_bin : krem;
+  r.all_in = whole;
   return r;
 }
 
-// After the emit: kPostClear leaves hist1 all-zero (a selection over the
-// buffer), kPostNone leaves it alone.
-enum PostEmit { kPostNone = 0, kPostClear = 1 };
+// Where the emit goes: kToBuffer (a compaction) or kToOut (the output).
+// Either way both histograms are all-zero afterwards.
+enum EmitMode { kToBuffer = 0, kToOut = 1 };
 
-// Writes the chosen entries in buffer order.  An entry is chosen if
-// (key & pmask) > prefix, or if it equals prefix and fewer than take_eq
-// equal entries precede it (gt_base / eq_base count greater / equal entries
-// of earlier chunks of the row).  Its rank = earlier greater entries +
-// min(earlier equal entries, take_eq).  Ranks >= limit are dropped (only
-// reachable with an inconsistent workspace).  To the buffer (as fp32 bits)
-// when out is null.  Otherwise ibase + idx goes to out[rank]: the chosen
-// ranks of this buffer are one contiguous range (the buffer is one
-// contiguous stretch of the row), so they are staged in hist1 and copied
-// out with coalesced stores, which also leaves hist1 all-zero.  Every
-// thread has read its buffer slice, and every wave has finished reading
-// hist1, before any thread writes (the scan's barrier).
-template <bool I16, int POST>
-__device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[Shape<I16>::kSlots], uint32_t cnt,
-                                            const Sel& s, uint32_t gt_base, uint32_t eq_base,
-                                            uint32_t take_eq, int32_t* out, uint32_t limit, uint32_t ibase) {
+// Writes the chosen entries (of Sel s, see above) in buffer order.  gt_base
+// / eq_base count the entries above / inside [lo, hi] of earlier chunks of
+// the row; an entry's rank = earlier entries above + min(earlier entries
+// inside, take).  Ranks >= limit are dropped (only reachable with an
+// inconsistent workspace).  To the buffer (as fp32 bits) for kToBuffer.
+// Otherwise ibase + idx goes to out[rank]: the chosen ranks of this buffer
+// are one contiguous range (the buffer is one contiguous stretch of the
+// row), so they are staged in hist1 and copied out with coalesced stores.
+// Every thread has read its buffer slice, and every wave has finished
+// reading the histograms, before any thread writes (the scan's barrier).
+template <bool I16, int MODE>
+__device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[Shape<I16>::kSlots], uint32_t sp,
+                                            uint32_t cnt, const Sel& s, uint32_t gt_base, uint32_t eq_base,
+                                            int32_t* out, uint32_t limit, uint32_t ibase) {
   constexpr int S = Shape<I16>::kSlots;
-  const uint32_t base = threadIdx.x * S;
-  uint32_t ix[S];
-  load_idx<I16>(sm, ix);
-  uint32_t packed = 0;
+  static_assert(S <= 32, "slice flags fit one word");
+  const uint32_t nv = valid_in_slice(sp, cnt);
+  const uint32_t width = s.hi - s.lo;
+  const uint32_t take = s.take;
+  // Whole interval taken and no earlier chunks: the chosen set is simply
+  // every key >= lo.  Otherwise flags for above / inside the interval.
+  const bool whole = s.all_in && gt_base == 0u && eq_base == 0u;
+  uint32_t gtm = 0, eqm = 0;
+  if (whole) {
 #pragma unroll
-  for (int j = 0; j < S; ++j) {
-    const bool valid = base + j < cnt;
-    const uint32_t km = k[j] & s.pmask;
-    packed += (valid && km > s.prefix) ? 1u : 0u;
-    packed += (valid && km == s.prefix) ? 0x10000u : 0u;
-  }
-  uint32_t total;
-  const uint32_t excl = block_excl_scan(sm, packed, &total);
-  uint32_t g = gt_base + (excl & 0xffffu);
-  uint32_t e = eq_base + (excl >> 16);
-  const uint32_t first = gt_base + (eq_base < take_eq ? eq_base : take_eq);  // rank of the first chosen
+    for (int j = 0; j < S; ++j)
+      if ((uint32_t)(j) < sp) gtm |= ((uint32_t)j < nv && k[j] >= s.lo) ? (1u << j) : 0u;
+  } else {
 #pragma unroll
-  for (int j = 0; j < S; ++j) {
-    const bool valid = base + j < cnt;
-    const uint32_t km = k[j] & s.pmask;
-    const bool gt = valid && km > s.prefix;
-    const bool eq = valid && km == s.prefix;
-    const bool take = gt || (eq && e < take_eq);
-    const uint32_t pos = g + (e < take_eq ? e : take_eq);
-    if (take && pos < limit) {
-      if (out != nullptr) {
-        sm.hist1[pos - first] = ibase + ix[j];
-      } else {
-        sm.val[pos] = key_bits(k[j]);
-        sm.idx[pos] = (typename Shape<I16>::Idx)ix[j];
+    for (int j = 0; j < S; ++j) {
+      if ((uint32_t)(j) < sp) {
+        const bool valid = (uint32_t)j < nv;
+        gtm |= (valid && k[j] > s.hi) ? (1u << j) : 0u;
+        eqm |= (valid && k[j] - s.lo <= width) ? (1u << j) : 0u;
       }
     }
-    g += gt ? 1u : 0u;
-    e += eq ? 1u : 0u;
   }
-  if (out != nullptr) {
-    const uint32_t eq_end = eq_base + (total >> 16);
-    uint32_t last = gt_base + (total & 0xffffu) + (eq_end < take_eq ? eq_end : take_eq);
-    last = last < limit ? last : limit;
-    const uint32_t m = last > first ? last - first : 0u;
-    __syncthreads();
-    for (uint32_t i = threadIdx.x; i < (uint32_t)kBins; i += kBlock) {
-      const uint32_t v = sm.hist1[i];
-      sm.hist1[i] = 0u;
-      if (i < m) out[first + i] = (int32_t)v;
+  // Indices are read before the scan's barrier: a compaction then moves
+  // entries down into other threads' slices.
+  uint32_t ix[S];
+  load_idx<I16>(sm, ix, sp);
+  uint32_t total;
+  const uint32_t excl = block_excl_scan(sm, (uint32_t)__popc(gtm) | ((uint32_t)__popc(eqm) << 16), &total);
+  uint32_t first, m;
+  if (whole) {
+    // Rank of slice position j = this thread's first rank + picks before j.
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      if ((uint32_t)(j) < sp) {
+        const uint32_t pos = (uint32_t)__popc(gtm & ((1u << j) - 1u)) + excl;
+        if (((gtm >> j) & 1u) && pos < limit) {
+          if constexpr (MODE != kToBuffer) {
+            sm.hist1[pos] = ibase + ix[j];
+          } else {
+            sm.val[pos] = key_bits(k[j]);
+            sm.idx[pos] = (typename Shape<I16>::Idx)ix[j];
+          }
+        }
+      }
     }
-  } else if (POST == kPostClear) {
-    clear_hist(sm);
+    first = 0u;
+    m = total < limit ? total : limit;
+  } else {
+    uint32_t g = gt_base + (excl & 0xffffu);
+    uint32_t e = eq_base + (excl >> 16);
+    first = gt_base + (eq_base < take ? eq_base : take);  // rank of the first chosen
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      if ((uint32_t)(j) < sp) {
+        const bool gt = (gtm >> j) & 1u;
+        const bool eq = (eqm >> j) & 1u;
+        const bool pick = gt || (eq && e < take);
+        const uint32_t pos = g + (e < take ? e : take);
+        if (pick && pos < limit) {
+          if constexpr (MODE != kToBuffer) {
+            sm.hist1[pos - first] = ibase + ix[j];
+          } else {
+            sm.val[pos] = key_bits(k[j]);
+            sm.idx[pos] = (typename Shape<I16>::Idx)ix[j];
+          }
+        }
+        g += gt ? 1u : 0u;
+        e += eq ? 1u : 0u;
+      }
+    }
+    const uint32_t eq_end = eq_base + (total >> 16);
+    uint32_t last = gt_base + (total & 0xffffu) + (eq_end < take ? eq_end : take);
+    last = last < limit ? last : limit;
+    m = last > first ? last - first : 0u;
+  }
+  if constexpr (MODE != kToBuffer) {
+    // Copy the staged ranks [0, m) to out[first + ...], clearing as we go.
+    __syncthreads();
+    int32_t* dst = out + first;
+    if ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0u && (m & 3u) == 0u) {
+      for (uint32_t i = threadIdx.x * 4u; i < (uint32_t)kBins; i += kBlock * 4u) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&sm.hist1[i]);
+        *reinterpret_cast<u32x4*>(&sm.hist1[i]) = u32x4{0u, 0u, 0u, 0u};
+        if (i < m) *reinterpret_cast<u32x4*>(dst + i) = v;
+      }
+    } else {
+      for (uint32_t i = threadIdx.x; i < (uint32_t)kBins; i += kBlock) {
+        const uint32_t v = sm.hist1[i];
+        sm.hist1[i] = 0u;
+        if (i < m) dst[i] = (int32_t)v;
+      }
+    }
+    sm.hs[threadIdx.x] = 0u;
+  } else {
+    clear_hists(sm);
   }
 }
 
 // Frees buffer space when a tile would not fit (cnt > keep entries), keeping
-// index order and the running histogram; returns (new count << 32) | new
-// bound.
+// index order; returns (new count << 32) | new bound.
 //
 // Speculative (spec_n = row length, first compaction of a row only; every
-// element seen so far is then in the buffer): keep every entry whose key is
-// at least that of the r-th best entry (r as set by kSpecNum, kSpecDen and
-// kSpecMinRank) and make that key the bound.  This assumes the K-th best of
-// the whole row is at least as large; the caller checks that at the end of
-// the row (at least K entries reached the buffer) and streams the row again
-// without speculation if not.  Entries below the bound can then only be
-// beaten by at least K others, so dropping them is safe whenever the check
-// passes.
+// element seen so far is then in the buffer): keep every entry at or above
+// a key near the r-th best (r as set by kSpecNum, kSpecDen and
+// kSpecMinRank; the bin of the r-th best is kept whole when it is small) and
+// make that key the bound.  This assumes the K-th best of the whole row is
+// at least as large; the caller checks that at the end of the row (at least
+// K entries reached the buffer) and streams the row again without
+// speculating if not.  Entries below the bound can then only be beaten by
+// at least K others, so dropping them is safe whenever the check passes.
 //
-// Otherwise coarse first: drop every entry below the top-digit bin holding
-// the keep-th best entry, if what remains leaves room for a tile.  Failing
-// that (mostly ties crowding one bin) exact: keep exactly the keep best.
-// Every element still to come has a higher index than all kept entries, so
-// after an exact selection it must beat the keep-th best key strictly to
-// matter; after a coarse one anything from the bin's lower edge up is
-// accepted.
+// Otherwise keep the bin holding the keep-th best whole, with everything
+// above it, as soon as that leaves room for a tile; the bound becomes the
+// bin's lowest key.  Failing that (ties crowding one key) keep exactly the
+// keep best: every element still to come has a higher index than all kept
+// entries, so it must beat the keep-th best key strictly to matter.
 //
 // Out of line: inlined into each slot of the unrolled streaming loop it
 // would multiply the register demand.  Arguments and result go by value: a
 // by-reference counter would live in scratch, and every scratch reload waits
 // on all outstanding prefetches.  The caller's next barrier orders the
-// rewritten buffer and histogram before their next use.
+// rewritten buffer before its next use.
 template <bool I16>
 __device__ __noinline__ uint64_t compact(Smem<I16>& sm, uint32_t cnt, uint32_t keep, uint32_t L, uint32_t spec_n) {
   constexpr int S = Shape<I16>::kSlots;
   constexpr uint32_t CAP = (uint32_t)Shape<I16>::kCap;
+  cnt = uni(cnt);
+  keep = uni(keep);
+  L = uni(L);
+  spec_n = uni(spec_n);
+  const uint32_t sp = slice_of<I16>(cnt);
   uint32_t k[S];
-  load_keys<I16>(sm, k);
-  top_hist<I16>(sm, k, cnt);
-  bool spec = false;
+  load_keys<I16>(sm, k, sp);
+  uint32_t lo, hi;
+  key_range<I16>(sm, k, sp, cnt, lo, hi);
   if (spec_n != 0u) {
     const uint64_t want = ((uint64_t)kSpecNum * keep * cnt + (uint64_t)kSpecDen * spec_n - 1) /
                           ((uint64_t)kSpecDen * spec_n);
     const uint32_t r = want > kSpecMinRank ? (uint32_t)want : kSpecMinRank;
     if (r < keep) {
-      // Entries at or above the r-th best all lie in bins from its top digit
-      // up; speculate only if those certainly leave room for a tile.
-      const Found f = wave_find<2048>(sm.hist1, r);
-      if (f.ok && f.above + f.in_bin + kTile <= CAP) {
-        spec = true;
-        keep = r;
+      Sel s = range_select<I16>(sm, k, sp, cnt, lo, hi, r, r + r / 8u + 8u);
+      const uint32_t kept = s.above + s.in_bin;
+      if (s.ok && kept + kTile <= CAP) {
+        s.take = s.in_bin;  // every entry at or above the bin's lowest key
+        s.all_in = true;
+        emit_chosen<I16, kToBuffer>(sm, k, sp, cnt, s, 0u, 0u, nullptr, CAP, 0u);
+        const uint32_t Ln = s.lo > L ? s.lo : L;
+        return ((uint64_t)kept << 32) | Ln;
       }
+      __syncthreads();
+      clear_hists(sm);
+      __syncthreads();
     }
   }
-  if (!spec) {
-    const Found f = wave_find<2048>(sm.hist1, keep);
-    if (f.ok && f.above + f.in_bin + kTile <= CAP) {
-      Sel s;
-      s.prefix = f.bin << 21;
-      s.pmask = 0xffe00000u;
-      s.krem = 0xffffffffu;
-      s.ok = 1u;
-      s.b1 = f.bin;
-      s.krem1 = f.in_bin;
-      s.used2 = 0u;
-      s.eqn = f.in_bin;
-      emit_chosen<I16, kPostClear>(sm, k, cnt, s, 0u, 0u, 0xffffffffu, nullptr, CAP, 0u);
-      const uint32_t Ln = s.prefix > L ? s.prefix : L;
-      return ((uint64_t)(f.above + f.in_bin) << 32) | Ln;
-    }
-  }
-  // Exact selection of the keep best; a speculative one then keeps every
-  // entry equal to the r-th best key too.
-  const Sel s = select_keep<I16>(sm, k, cnt, keep);
-  const uint32_t take_eq = spec ? 0xffffffffu : s.krem;
-  emit_chosen<I16, kPostClear>(sm, k, cnt, s, 0u, 0u, take_eq, nullptr, CAP, 0u);
-  uint32_t Ln, cn;
-  if (spec) {
-    Ln = s.prefix;
-    cn = keep - s.krem + s.eqn;
+  const Sel s = range_select<I16>(sm, k, sp, cnt, lo, hi, keep, CAP - kTile);
+  emit_chosen<I16, kToBuffer>(sm, k, sp, cnt, s, 0u, 0u, nullptr, CAP, 0u);
+  uint32_t Ln;
+  if (s.all_in) {
+    Ln = s.lo;  // the bin was kept whole
   } else {
-    if (s.pmask == 0xffffffffu)
-      Ln = s.prefix == 0xffffffffu ? 0xffffffffu : s.prefix + 1u;
-    else
-      Ln = s.prefix;
-    cn = keep;
+    Ln = s.lo == 0xffffffffu ? 0xffffffffu : s.lo + 1u;  // exact split at the single key lo
   }
   Ln = Ln > L ? Ln : L;
-  return ((uint64_t)cn << 32) | Ln;
+  return ((uint64_t)(s.above + s.take) << 32) | Ln;
 }
 
 // The K best of the buffer, written to out in index order.
 template <bool I16>
 __device__ __noinline__ void final_select(Smem<I16>& sm, uint32_t cnt, uint32_t K, int32_t* out) {
   constexpr int S = Shape<I16>::kSlots;
+  cnt = uni(cnt);
+  K = uni(K);
+  const uint32_t sp = slice_of<I16>(cnt);
   uint32_t k[S];
-  load_keys<I16>(sm, k);
-  top_hist<I16>(sm, k, cnt);
-  const Sel s = select_keep<I16>(sm, k, cnt, K);
-  emit_chosen<I16, kPostClear>(sm, k, cnt, s, 0u, 0u, s.krem, out, K, 0u);
+  load_keys<I16>(sm, k, sp);
+  uint32_t lo, hi;
+  key_range<I16>(sm, k, sp, cnt, lo, hi);
+  const Sel s = range_select<I16>(sm, k, sp, cnt, lo, hi, K, 0u);
+  emit_chosen<I16, kToOut>(sm, k, sp, cnt, s, 0u, 0u, out, K, 0u);
 }
 
 // ---------------------------------------------------------------------------
 // Streaming filter over [c0, c1) of one row
 // ---------------------------------------------------------------------------
-
-// Wave-uniform copy of a value that is the same in every lane, so that the
-// compiler keeps it (and what is computed from it) in scalar registers.
-__device__ __forceinline__ uint32_t uni(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
 
 // One full tile starting at `tile` (a wave-uniform pointer): thread t loads
 // elements u * 256 * VEC + t * VEC .. + VEC - 1, so each load instruction of a
@@ -729,7 +834,7 @@ __device__ __forceinline__ void write_all_then_pad(int32_t* out, int64_t n, int 
 
 template <bool I16>
 __device__ __forceinline__ void zero_histograms(Smem<I16>& sm) {
-  clear_hist(sm);
+  clear_hists(sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -787,7 +892,6 @@ __global__ void __launch_bounds__(kBlock) topk_single_kernel(KernelParams p) {
         // Fewer than K elements reached the speculative bound: it was above
         // the K-th best.  Stream the same row again without speculating.
         redo = 1u;
-        clear_hist(sm);
         __syncthreads();
         continue;
       }
@@ -928,13 +1032,20 @@ __global__ void __launch_bounds__(kBlock) topk_multi_kernel(KernelParams p) {
   uint32_t cnt = 0, L = 0;
   stream_chunk<I16, VEC>(sm, rowp, (uint32_t)c0, (uint32_t)c1, K, cnt, L, 0u);
 
+  const uint32_t sp = slice_of<I16>(cnt);
   uint32_t k[S];
-  load_keys<I16>(sm, k);
-  const uint32_t base = (uint32_t)t * S;
+  load_keys<I16>(sm, k, sp);
+  const uint32_t base = (uint32_t)t * sp;
 
-  // Round 1: the chunk's top-digit histogram into the row's, then the
-  // row-wide threshold digit from a copy of the row's.
-  top_hist<I16>(sm, k, cnt);
+  // Round 1: the chunk's top-digit (11-bit) histogram into the row's, then
+  // the row-wide threshold digit from a copy of the row's.
+#pragma unroll
+  for (int j = 0; j < S; ++j) {
+    if ((uint32_t)(j) < sp) {
+      if (base + j < cnt) atomicAdd(&sm.hist1[k[j] >> 21], 1u);
+    }
+  }
+  __syncthreads();
   merge_hist(sm.hist1, h1);
   group_barrier(ctr, 1u * grow, p.spin_limit, err);
   load_hist(sm.hist1, h1);
@@ -948,15 +1059,17 @@ __global__ void __launch_bounds__(kBlock) topk_multi_kernel(KernelParams p) {
   // Round 2: next 11 bits of the entries in the threshold bin; publish how
   // many of this chunk's entries lie above it.
   __syncthreads();  // every wave has read the row's copy
-  clear_hist(sm);
+  for (int i = t; i < kBins; i += kBlock) sm.hist1[i] = 0u;
   __syncthreads();
   uint32_t n_above = 0;
 #pragma unroll
   for (int j = 0; j < S; ++j) {
-    const bool valid = base + j < cnt;
-    const uint32_t km = k[j] & pmask;
-    if (valid && km == prefix) atomicAdd(&sm.hist1[(k[j] >> 10) & 2047u], 1u);
-    n_above += popc64(ballot(valid && km > prefix));
+    if ((uint32_t)(j) < sp) {
+      const bool valid = base + j < cnt;
+      const uint32_t km = k[j] & pmask;
+      if (valid && km == prefix) atomicAdd(&sm.hist1[(k[j] >> 10) & 2047u], 1u);
+      n_above += popc64(ballot(valid && km > prefix));
+    }
   }
   wave_add(&sm.acc[0], n_above);
   __syncthreads();
@@ -978,10 +1091,12 @@ __global__ void __launch_bounds__(kBlock) topk_multi_kernel(KernelParams p) {
     n_above = 0;
 #pragma unroll
     for (int j = 0; j < S; ++j) {
-      const bool valid = base + j < cnt;
-      const uint32_t km = k[j] & pmask;
-      mine += (valid && km == prefix) ? 1u : 0u;
-      n_above += popc64(ballot(valid && km > prefix));
+      if ((uint32_t)(j) < sp) {
+        const bool valid = base + j < cnt;
+        const uint32_t km = k[j] & pmask;
+        mine += (valid && km == prefix) ? 1u : 0u;
+        n_above += popc64(ballot(valid && km > prefix));
+      }
     }
     wave_add(&sm.acc[1], n_above);
     uint32_t len;
@@ -989,8 +1104,10 @@ __global__ void __launch_bounds__(kBlock) topk_multi_kernel(KernelParams p) {
     uint32_t* my_list = lists + (uint64_t)g * CAP;
 #pragma unroll
     for (int j = 0; j < S; ++j) {
-      const bool valid = base + j < cnt;
-      if (valid && (k[j] & pmask) == prefix) ws_store(&my_list[at++], k[j]);
+      if ((uint32_t)(j) < sp) {
+        const bool valid = base + j < cnt;
+        if (valid && (k[j] & pmask) == prefix) ws_store(&my_list[at++], k[j]);
+      }
     }
     if (t == 0) {
       ws_store(&slots[4 * g + 1], sm.acc[1] - sm.acc[0]);
@@ -998,7 +1115,7 @@ __global__ void __launch_bounds__(kBlock) topk_multi_kernel(KernelParams p) {
     }
   }
   group_barrier(ctr, 3u * grow, p.spin_limit, err);
-  clear_hist(sm);  // every wave read round 2's copy before the barrier
+  for (int i = t; i < kBins; i += kBlock) sm.hist1[i] = 0u;  // every wave read round 2's copy before the barrier
 
   // Every chunk's list, flattened: offsets by a prefix sum over the lengths.
   if (t < 64) {
@@ -1079,15 +1196,14 @@ __global__ void __launch_bounds__(kBlock) topk_multi_kernel(KernelParams p) {
   }
 
   Sel s;
-  s.prefix = T;
-  s.pmask = 0xffffffffu;
-  s.krem = take_eq;
+  s.lo = T;
+  s.hi = T;
+  s.take = take_eq;
+  s.above = 0u;
+  s.in_bin = 0u;
   s.ok = ok;
-  s.b1 = 0u;
-  s.krem1 = 0u;
-  s.used2 = 0u;
-  s.eqn = 0u;
-  emit_chosen<I16, kPostNone>(sm, k, cnt, s, gt_base, eq_base, take_eq, out, K, (uint32_t)c0);
+  s.all_in = false;
+  emit_chosen<I16, kToOut>(sm, k, sp, cnt, s, gt_base, eq_base, out, K, (uint32_t)c0);
 }
 
 // ---------------------------------------------------------------------------
