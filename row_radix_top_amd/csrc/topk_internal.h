@@ -18,14 +18,14 @@ constexpr int kMaxGroup = 64;               // most workgroups that may share a 
 constexpr int kMaxK = 2048;
 constexpr uint32_t kDefaultSpin = 1u << 24; // polls before a cooperative wait gives up
 
-// Speculative bound (one-workgroup rows): at the first compaction the bound
-// is raised to the key of the r-th best element seen so far, with
-// r = max(kSpecMinRank, ceil(kSpecNum / kSpecDen * K * seen / n)), when that
+// Speculative bound (one-workgroup rows of at least kSpecMinLen elements):
+// before the first two tiles are filtered, the bound is raised to (about) the
+// key of the r-th best of their 4096 elements, with
+// r = max(kSpecMinRank, ceil(kSpecNum / kSpecDen * K * 4096 / n)), when that
 // r is below K.  kSpecNum / kSpecDen is the safety factor over the expected
 // rank of the K-th best of the row; kSpecMinRank keeps the sample quantile
-// from resting on too few elements.
-// Rows shorter than kSpecMinLen do not speculate: too few tiles remain after
-// the first compaction to repay an exact selection.
+// from resting on too few elements.  Shorter rows have too few tiles left to
+// repay the selection.
 constexpr uint32_t kSpecNum = 3, kSpecDen = 2;
 constexpr uint32_t kSpecMinRank = 128;
 constexpr uint32_t kSpecMinLen = 16384;

@@ -126,6 +126,9 @@ struct Shape {
   static_assert(kCap % kBlock == 0 && kSlots % 4 == 0, "capacity must tile the workgroup in aligned runs");
   static_assert(kCap < 65536, "packed 16-bit counts");
   static_assert(kCap >= kMaxK + kTile, "a tile must fit after a compaction");
+  // Workgroups per CU the LDS footprint allows (160 KB per CU); the register
+  // budget is held to match.
+  static constexpr int kResident = I16 ? 4 : 3;
 };
 
 template <bool I16>
@@ -322,10 +325,9 @@ __device__ __forceinline__ uint32_t wave_min(uint32_t v) {
 
 // [lo, hi]: the smallest and largest key of the cnt entries (both wave-
 // uniform).  Contains one barrier.
-template <bool I16>
-__device__ __forceinline__ void key_range(Smem<I16>& sm, const uint32_t (&k)[Shape<I16>::kSlots], uint32_t sp,
-                                          uint32_t cnt, uint32_t& lo, uint32_t& hi) {
-  constexpr int S = Shape<I16>::kSlots;
+template <bool I16, int S>
+__device__ __forceinline__ void key_range(Smem<I16>& sm, const uint32_t (&k)[S], uint32_t sp, uint32_t cnt,
+                                          uint32_t& lo, uint32_t& hi) {
   const uint32_t nv = valid_in_slice(sp, cnt);
   uint32_t mn = 0xffffffffu, mx = 0;
 #pragma unroll
@@ -358,10 +360,9 @@ __device__ __forceinline__ void key_range(Smem<I16>& sm, const uint32_t (&k)[Sha
 // whole bin or the entries still needed.  stop_total = 0 asks for an exact
 // selection of keep entries.  Both histograms are zero on entry and hold
 // garbage on return.
-template <bool I16>
-__device__ Sel range_select(Smem<I16>& sm, const uint32_t (&k)[Shape<I16>::kSlots], uint32_t sp, uint32_t cnt,
-                            uint32_t lo, uint32_t hi, uint32_t keep, uint32_t stop_total) {
-  constexpr int S = Shape<I16>::kSlots;
+template <bool I16, int S>
+__device__ Sel range_select(Smem<I16>& sm, const uint32_t (&k)[S], uint32_t sp, uint32_t cnt, uint32_t lo,
+                            uint32_t hi, uint32_t keep, uint32_t stop_total) {
   const uint32_t nv = valid_in_slice(sp, cnt);
   Sel r;
   r.ok = 1u;
@@ -529,23 +530,12 @@ __device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[S
 }
 
 // Frees buffer space when a tile would not fit (cnt > keep entries), keeping
-// index order; returns (new count << 32) | new bound.
-//
-// Speculative (spec_n = row length, first compaction of a row only; every
-// element seen so far is then in the buffer): keep every entry at or above
-// a key near the r-th best (r as set by kSpecNum, kSpecDen and
-// kSpecMinRank; the bin of the r-th best is kept whole when it is small) and
-// make that key the bound.  This assumes the K-th best of the whole row is
-// at least as large; the caller checks that at the end of the row (at least
-// K entries reached the buffer) and streams the row again without
-// speculating if not.  Entries below the bound can then only be beaten by
-// at least K others, so dropping them is safe whenever the check passes.
-//
-// Otherwise keep the bin holding the keep-th best whole, with everything
-// above it, as soon as that leaves room for a tile; the bound becomes the
-// bin's lowest key.  Failing that (ties crowding one key) keep exactly the
-// keep best: every element still to come has a higher index than all kept
-// entries, so it must beat the keep-th best key strictly to matter.
+// index order; returns (new count << 32) | new bound.  Keeps the bin holding
+// the keep-th best whole, with everything above it, as soon as that leaves
+// room for a tile; the bound becomes the bin's lowest key.  Failing that
+// (ties crowding one key) keeps exactly the keep best: every element still
+// to come has a higher index than all kept entries, so it must beat the
+// keep-th best key strictly to matter.
 //
 // Out of line: inlined into each slot of the unrolled streaming loop it
 // would multiply the register demand.  Arguments and result go by value: a
@@ -553,38 +543,18 @@ __device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[S
 // on all outstanding prefetches.  The caller's next barrier orders the
 // rewritten buffer before its next use.
 template <bool I16>
-__device__ __noinline__ uint64_t compact(Smem<I16>& sm, uint32_t cnt, uint32_t keep, uint32_t L, uint32_t spec_n) {
+__device__ __noinline__ uint64_t compact(Smem<I16>& sm, uint32_t cnt, uint32_t keep, uint32_t L) {
   constexpr int S = Shape<I16>::kSlots;
   constexpr uint32_t CAP = (uint32_t)Shape<I16>::kCap;
   cnt = uni(cnt);
   keep = uni(keep);
   L = uni(L);
-  spec_n = uni(spec_n);
   const uint32_t sp = slice_of<I16>(cnt);
   uint32_t k[S];
   load_keys<I16>(sm, k, sp);
   uint32_t lo, hi;
-  key_range<I16>(sm, k, sp, cnt, lo, hi);
-  if (spec_n != 0u) {
-    const uint64_t want = ((uint64_t)kSpecNum * keep * cnt + (uint64_t)kSpecDen * spec_n - 1) /
-                          ((uint64_t)kSpecDen * spec_n);
-    const uint32_t r = want > kSpecMinRank ? (uint32_t)want : kSpecMinRank;
-    if (r < keep) {
-      Sel s = range_select<I16>(sm, k, sp, cnt, lo, hi, r, r + r / 8u + 8u);
-      const uint32_t kept = s.above + s.in_bin;
-      if (s.ok && kept + kTile <= CAP) {
-        s.take = s.in_bin;  // every entry at or above the bin's lowest key
-        s.all_in = true;
-        emit_chosen<I16, kToBuffer>(sm, k, sp, cnt, s, 0u, 0u, nullptr, CAP, 0u);
-        const uint32_t Ln = s.lo > L ? s.lo : L;
-        return ((uint64_t)kept << 32) | Ln;
-      }
-      __syncthreads();
-      clear_hists(sm);
-      __syncthreads();
-    }
-  }
-  const Sel s = range_select<I16>(sm, k, sp, cnt, lo, hi, keep, CAP - kTile);
+  key_range<I16, S>(sm, k, sp, cnt, lo, hi);
+  const Sel s = range_select<I16, S>(sm, k, sp, cnt, lo, hi, keep, CAP - kTile);
   emit_chosen<I16, kToBuffer>(sm, k, sp, cnt, s, 0u, 0u, nullptr, CAP, 0u);
   uint32_t Ln;
   if (s.all_in) {
@@ -606,8 +576,8 @@ __device__ __noinline__ void final_select(Smem<I16>& sm, uint32_t cnt, uint32_t 
   uint32_t k[S];
   load_keys<I16>(sm, k, sp);
   uint32_t lo, hi;
-  key_range<I16>(sm, k, sp, cnt, lo, hi);
-  const Sel s = range_select<I16>(sm, k, sp, cnt, lo, hi, K, 0u);
+  key_range<I16, S>(sm, k, sp, cnt, lo, hi);
+  const Sel s = range_select<I16, S>(sm, k, sp, cnt, lo, hi, K, 0u);
   emit_chosen<I16, kToOut>(sm, k, sp, cnt, s, 0u, 0u, out, K, 0u);
 }
 
@@ -732,7 +702,7 @@ __device__ __forceinline__ void tile_append(Smem<I16>& sm, const float (&x)[kEle
 // key and as the float every accepted element must reach), the pending
 // speculation (row length, or 0), and the tile-count parity.
 struct Stream {
-  uint32_t cnt, L, spec;
+  uint32_t cnt, L;
   float bf;
   int par;
 };
@@ -750,8 +720,7 @@ __device__ __forceinline__ void process_tile(Smem<I16>& sm, const float (&x)[kEl
   tile_accept<VEC, FULL>(x, pbase, c1, st.bf, bal);
   uint32_t total = tile_exchange<I16, VEC>(sm, bal, st.par, off);
   if (st.cnt + total > (uint32_t)Shape<I16>::kCap) {
-    const uint64_t r = compact<I16>(sm, st.cnt, keep, st.L, st.spec);
-    st.spec = 0u;
+    const uint64_t r = compact<I16>(sm, st.cnt, keep, st.L);
     st.L = uni((uint32_t)r);
     st.cnt = uni((uint32_t)(r >> 32));
     st.bf = accept_floor(st.L);
@@ -762,13 +731,55 @@ __device__ __forceinline__ void process_tile(Smem<I16>& sm, const float (&x)[kEl
   st.cnt += total;
 }
 
+// The speculative bound for a row of n elements whose first two tiles are
+// in x0 and x1 (n >= kSpecMinLen): the key of (about) the r-th best of those
+// 4096 elements, r = max(kSpecMinRank, ceil(kSpecNum / kSpecDen * K * 4096 / n)),
+// or 0 (no bound) when r >= K.  The bin holding the r-th best is taken whole
+// when it is small, which only lowers the bound.  The caller checks at the
+// end of the row that at least K elements reached the bound and streams the
+// row again without it if not; when the check passes, every element below
+// the bound is beaten by at least K others.  Runs on register-held keys
+// while the next tiles' loads are in flight.  Leaves the histograms zero.
+template <bool I16>
+__device__ __forceinline__ uint32_t spec_bound(Smem<I16>& sm, float (&x0)[kElems], float (&x1)[kElems], uint32_t n,
+                                               uint32_t K) {
+  constexpr uint32_t M = 2u * kTile;
+  const uint64_t want = ((uint64_t)kSpecNum * K * M + (uint64_t)kSpecDen * n - 1) / ((uint64_t)kSpecDen * n);
+  const uint32_t r = want > kSpecMinRank ? (uint32_t)want : kSpecMinRank;
+  if (r >= K) return 0u;
+  // The keys replace the values in place (registers are scarce here) and
+  // are turned back afterwards; only the sign of a zero can change, which no
+  // comparison sees.
+  uint32_t k[2 * kElems];
+#pragma unroll
+  for (int e = 0; e < kElems; ++e) {
+    k[e] = ord_key(__float_as_uint(x0[e]));
+    k[kElems + e] = ord_key(__float_as_uint(x1[e]));
+  }
+  uint32_t lo, hi;
+  key_range<I16, 2 * kElems>(sm, k, 2 * kElems, M, lo, hi);
+  const Sel s = range_select<I16, 2 * kElems>(sm, k, 2 * kElems, M, lo, hi, r, r + r / 8u + 8u);
+#pragma unroll
+  for (int e = 0; e < kElems; ++e) {
+    x0[e] = __uint_as_float(key_bits(k[e]));
+    x1[e] = __uint_as_float(key_bits(k[kElems + e]));
+  }
+  __syncthreads();  // every wave is done with the histograms
+  clear_hists(sm);
+  return s.ok ? s.lo : 0u;
+}
+
 // Streams [c0, c1) through the filter.  Full tiles come through a ring of
 // kPrefetch register buffers: the load for tile j + kPrefetch - 1 is issued
 // before tile j is processed, so about (kPrefetch - 1) tiles per workgroup
 // are in flight.  Prefetch addresses past the last full tile are clamped to
 // it (a cache hit), which keeps the load pattern identical every iteration.
-// The partial last tile is loaded with per-element bounds checks.  spec:
-// the row length if the first compaction may speculate, else 0.
+// The partial last tile is loaded with per-element bounds checks.
+//
+// spec = the row length (>= kSpecMinLen) to start from a speculative bound
+// taken from the first two tiles (see spec_bound), else 0.  Those two tiles
+// are then loaded ahead of the ring, which starts at tile 2 with its loads
+// issued before the bound is computed.
 template <bool I16, int VEC>
 __device__ void stream_chunk(Smem<I16>& sm, const float* __restrict__ rowp, uint32_t c0, uint32_t c1,
                              uint32_t keep, uint32_t& cnt, uint32_t& L, uint32_t spec) {
@@ -778,22 +789,35 @@ __device__ void stream_chunk(Smem<I16>& sm, const float* __restrict__ rowp, uint
   Stream st;
   st.cnt = uni(cnt);
   st.L = uni(L);
-  st.spec = uni(spec);
   st.bf = accept_floor(st.L);
   st.par = 0;
   const uint32_t F = (c1 - c0) / kTile;  // full tiles
   const float* base = rowp + c0;
-  if (F > 0) {
+  const bool pre = uni(spec) != 0u && F >= 2u;
+  const uint32_t j1 = pre ? 2u : 0u;  // first tile of the ring
+  float x0[kElems], x1[kElems];
+  if (pre) {
+    load_full<VEC>(base, x0);
+    load_full<VEC>(base + kTile, x1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (F > j1) {
     float buf[PF][kElems];
 #pragma unroll
     for (int s = 0; s < PF - 1; ++s) {
-      load_full<VEC>(base + ((uint32_t)s < F ? (uint32_t)s : F - 1) * kTile, buf[s]);
+      load_full<VEC>(base + (j1 + (uint32_t)s < F ? j1 + (uint32_t)s : F - 1) * kTile, buf[s]);
       __builtin_amdgcn_sched_barrier(0);  // keep tiles in issue order: waits then retire oldest first
+    }
+    if (pre) {
+      st.L = uni(spec_bound<I16>(sm, x0, x1, uni(spec), keep));
+      st.bf = accept_floor(st.L);
+      process_tile<I16, VEC, true>(sm, x0, c0, c1, c0, keep, st);
+      process_tile<I16, VEC, true>(sm, x1, c0 + kTile, c1, c0, keep, st);
     }
     // Whole rounds of PF tiles: one uniform back edge, so the compiler's
     // load-counter waits stay exact (retire only the tile about to be used).
-    const uint32_t Fr = F - F % PF;
-    for (uint32_t j0 = 0; j0 < Fr; j0 += PF) {
+    const uint32_t Fr = j1 + (F - j1) - (F - j1) % PF;
+    for (uint32_t j0 = j1; j0 < Fr; j0 += PF) {
 #pragma unroll
       for (int slot = 0; slot < PF; ++slot) {
         const uint32_t j = j0 + slot;
@@ -803,12 +827,16 @@ __device__ void stream_chunk(Smem<I16>& sm, const float* __restrict__ rowp, uint
         process_tile<I16, VEC, true>(sm, buf[slot], c0 + j * kTile, c1, c0, keep, st);
       }
     }
-    // The last F % PF full tiles are already in buf[0..]: no more loads.
+    // The last (F - j1) % PF full tiles are already in buf[0..]: no more loads.
 #pragma unroll
     for (int slot = 0; slot < PF - 1; ++slot) {
       const uint32_t j = Fr + slot;
       if (j < F) process_tile<I16, VEC, true>(sm, buf[slot], c0 + j * kTile, c1, c0, keep, st);
     }
+  } else if (pre) {
+    // Exactly two full tiles: no ring, no bound worth taking.
+    process_tile<I16, VEC, true>(sm, x0, c0, c1, c0, keep, st);
+    process_tile<I16, VEC, true>(sm, x1, c0 + kTile, c1, c0, keep, st);
   }
   const uint32_t pt = c0 + F * kTile;
   if (pt < c1) {
@@ -851,7 +879,7 @@ __device__ __forceinline__ void zero_histograms(Smem<I16>& sm) {
 // Without a workspace row b + k * gridDim.x is taken in turn.
 // ---------------------------------------------------------------------------
 template <int VEC, bool I16>
-__global__ void __launch_bounds__(kBlock) topk_single_kernel(KernelParams p) {
+__global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_kernel(KernelParams p) {
   __shared__ Smem<I16> sm;
   zero_histograms(sm);
   __syncthreads();
@@ -986,7 +1014,7 @@ __device__ __forceinline__ int list_of(const uint32_t* off, int n, uint32_t i) {
 }
 
 template <int VEC, bool I16>
-__global__ void __launch_bounds__(kBlock) topk_multi_kernel(KernelParams p) {
+__global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_multi_kernel(KernelParams p) {
   __shared__ Smem<I16> sm;
   __shared__ uint32_t s_off[kMaxGroup + 1];
   __shared__ uint32_t s_above[kMaxGroup];
