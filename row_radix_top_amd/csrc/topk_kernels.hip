@@ -110,6 +110,16 @@ __device__ __forceinline__ uint32_t lane_value(uint32_t v, int lane) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
 }
 
+// threadIdx.x laundered through an empty asm statement: values computed
+// from it cannot be hoisted out of the row loop and kept live (in registers
+// or spilled) across the whole kernel.  Used on the selection paths, which
+// run once per row.
+__device__ __forceinline__ uint32_t tid() {
+  uint32_t t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // Wave-uniform copy of a value that is the same in every lane, so that the
 // compiler keeps it (and what is computed from it) in scalar registers.
 __device__ __forceinline__ uint32_t uni(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
@@ -200,7 +210,8 @@ __device__ __forceinline__ Found wave_find(const uint32_t* hist, uint32_t krem) 
 // the sum.  Contains one barrier.
 template <bool I16>
 __device__ __forceinline__ uint32_t block_excl_scan(Smem<I16>& sm, uint32_t v, uint32_t* total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t t = tid();
+  const int lane = t & 63, w = t >> 6;
   const uint32_t incl = wave_incl_scan(v);
   if (lane == 63) sm.wsum[w] = incl;
   __syncthreads();
@@ -249,30 +260,61 @@ __device__ __forceinline__ uint32_t slice_of(uint32_t cnt) {
 // Entries of this thread's slice that hold data (of cnt): slice positions
 // j < valid_in_slice(...) are valid.
 __device__ __forceinline__ uint32_t valid_in_slice(uint32_t sp, uint32_t cnt) {
-  const uint32_t base = threadIdx.x * sp;
+  const uint32_t base = tid() * sp;
   const uint32_t v = cnt > base ? cnt - base : 0u;
   return v < sp ? v : sp;
 }
 
+// Where the buffer's positions live in LDS.  Normally position p is slot p.
+// After a row streamed wave by wave (stream_row_waves), wave w's entries --
+// positions [pre[w], pre[w + 1]) in index order -- sit from slot w * SUB on,
+// so position p is slot p + d[w] for the segment w that holds it.
+struct Segs {
+  uint32_t pre1, pre2, pre3;  // first position of segments 1, 2, 3
+  uint32_t d1, d2, d3;        // slot - position within segments 1, 2, 3
+};
+
+__device__ __forceinline__ uint32_t seg_slot(const Segs& g, uint32_t p) {
+  uint32_t d = 0u;
+  d = p >= g.pre1 ? g.d1 : d;
+  d = p >= g.pre2 ? g.d2 : d;
+  d = p >= g.pre3 ? g.d3 : d;
+  return p + d;
+}
+
 // Keys of this thread's slice (positions t*sp + j, j < sp).
-template <bool I16>
-__device__ __forceinline__ void load_keys(const Smem<I16>& sm, uint32_t (&k)[Shape<I16>::kSlots], uint32_t sp) {
+template <bool I16, bool SEG = false>
+__device__ __forceinline__ void load_keys(const Smem<I16>& sm, uint32_t (&k)[Shape<I16>::kSlots], uint32_t sp,
+                                          const Segs& g = Segs{}) {
   constexpr int S = Shape<I16>::kSlots;
-  const uint32_t base = threadIdx.x * sp;
+  const uint32_t base = tid() * sp;
+  if constexpr (SEG) {
 #pragma unroll
-  for (int q = 0; q < S / 2; ++q) {
-    if ((uint32_t)(2 * q) < sp) {
-      const u32x2 a = *reinterpret_cast<const u32x2*>(&sm.val[base + 2 * q]);
-      k[2 * q + 0] = ord_key(a.x);
-      k[2 * q + 1] = ord_key(a.y);
+    for (int j = 0; j < S; ++j)
+      if ((uint32_t)j < sp) k[j] = ord_key(sm.val[seg_slot(g, base + j)]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < S / 2; ++q) {
+      if ((uint32_t)(2 * q) < sp) {
+        const u32x2 a = *reinterpret_cast<const u32x2*>(&sm.val[base + 2 * q]);
+        k[2 * q + 0] = ord_key(a.x);
+        k[2 * q + 1] = ord_key(a.y);
+      }
     }
   }
 }
 
-template <bool I16>
-__device__ __forceinline__ void load_idx(const Smem<I16>& sm, uint32_t (&ix)[Shape<I16>::kSlots], uint32_t sp) {
+template <bool I16, bool SEG = false>
+__device__ __forceinline__ void load_idx(const Smem<I16>& sm, uint32_t (&ix)[Shape<I16>::kSlots], uint32_t sp,
+                                         const Segs& g = Segs{}) {
   constexpr int S = Shape<I16>::kSlots;
-  const uint32_t base = threadIdx.x * sp;
+  const uint32_t base = tid() * sp;
+  if constexpr (SEG) {
+#pragma unroll
+    for (int j = 0; j < S; ++j)
+      if ((uint32_t)j < sp) ix[j] = sm.idx[seg_slot(g, base + j)];
+    return;
+  }
 #pragma unroll
   for (int q = 0; q < S / 2; ++q) {
     if ((uint32_t)(2 * q) < sp) {
@@ -293,8 +335,8 @@ static_assert(kSmallBins == kBlock, "one second-pass bin per thread");
 
 template <bool I16>
 __device__ __forceinline__ void clear_hists(Smem<I16>& sm) {
-  for (int i = threadIdx.x; i < kBins; i += kBlock) sm.hist1[i] = 0u;
-  sm.hs[threadIdx.x] = 0u;
+  for (int i = tid(); i < kBins; i += kBlock) sm.hist1[i] = 0u;
+  sm.hs[tid()] = 0u;
 }
 
 // Maximum over the wavefront by DPP row shifts and row broadcasts; every
@@ -341,8 +383,8 @@ __device__ __forceinline__ void key_range(Smem<I16>& sm, const uint32_t (&k)[S],
   }
   mn = wave_min(mn);
   mx = wave_max(mx);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
+  const int w = tid() >> 6;
+  if ((tid() & 63) == 0) {
     sm.red[w] = mn;
     sm.red[kWaves + w] = mx;
   }
@@ -378,9 +420,9 @@ __device__ Sel range_select(Smem<I16>& sm, const uint32_t (&k)[S], uint32_t sp, 
     if (pass >= 2) {  // this histogram was used two passes ago
       __syncthreads();
       if (big) {
-        for (int i = threadIdx.x; i < kBins; i += kBlock) h[i] = 0u;
+        for (int i = tid(); i < kBins; i += kBlock) h[i] = 0u;
       } else {
-        h[threadIdx.x] = 0u;
+        h[tid()] = 0u;
       }
       __syncthreads();
     }
@@ -426,10 +468,11 @@ enum EmitMode { kToBuffer = 0, kToOut = 1 };
 // row), so they are staged in hist1 and copied out with coalesced stores.
 // Every thread has read its buffer slice, and every wave has finished
 // reading the histograms, before any thread writes (the scan's barrier).
-template <bool I16, int MODE>
+template <bool I16, int MODE, bool SEG = false>
 __device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[Shape<I16>::kSlots], uint32_t sp,
                                             uint32_t cnt, const Sel& s, uint32_t gt_base, uint32_t eq_base,
-                                            int32_t* out, uint32_t limit, uint32_t ibase) {
+                                            int32_t* out, uint32_t limit, uint32_t ibase, const Segs& g = Segs{}) {
+  static_assert(!SEG || MODE == kToOut, "a segmented buffer is only ever emitted to the output");
   constexpr int S = Shape<I16>::kSlots;
   static_assert(S <= 32, "slice flags fit one word");
   const uint32_t nv = valid_in_slice(sp, cnt);
@@ -456,7 +499,7 @@ __device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[S
   // Indices are read before the scan's barrier: a compaction then moves
   // entries down into other threads' slices.
   uint32_t ix[S];
-  load_idx<I16>(sm, ix, sp);
+  load_idx<I16, SEG>(sm, ix, sp, g);
   uint32_t total;
   const uint32_t excl = block_excl_scan(sm, (uint32_t)__popc(gtm) | ((uint32_t)__popc(eqm) << 16), &total);
   uint32_t first, m;
@@ -511,19 +554,19 @@ __device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[S
     __syncthreads();
     int32_t* dst = out + first;
     if ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0u && (m & 3u) == 0u) {
-      for (uint32_t i = threadIdx.x * 4u; i < (uint32_t)kBins; i += kBlock * 4u) {
+      for (uint32_t i = tid() * 4u; i < (uint32_t)kBins; i += kBlock * 4u) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(&sm.hist1[i]);
         *reinterpret_cast<u32x4*>(&sm.hist1[i]) = u32x4{0u, 0u, 0u, 0u};
         if (i < m) *reinterpret_cast<u32x4*>(dst + i) = v;
       }
     } else {
-      for (uint32_t i = threadIdx.x; i < (uint32_t)kBins; i += kBlock) {
+      for (uint32_t i = tid(); i < (uint32_t)kBins; i += kBlock) {
         const uint32_t v = sm.hist1[i];
         sm.hist1[i] = 0u;
         if (i < m) dst[i] = (int32_t)v;
       }
     }
-    sm.hs[threadIdx.x] = 0u;
+    sm.hs[tid()] = 0u;
   } else {
     clear_hists(sm);
   }
@@ -566,19 +609,21 @@ __device__ __noinline__ uint64_t compact(Smem<I16>& sm, uint32_t cnt, uint32_t k
   return ((uint64_t)(s.above + s.take) << 32) | Ln;
 }
 
-// The K best of the buffer, written to out in index order.
-template <bool I16>
-__device__ __noinline__ void final_select(Smem<I16>& sm, uint32_t cnt, uint32_t K, int32_t* out) {
+// The K best of the buffer, written to out in index order.  Inline, so that
+// loads issued before it (the next row's first tiles) stay in flight.
+template <bool I16, bool SEG = false>
+__device__ __forceinline__ void final_select(Smem<I16>& sm, uint32_t cnt, uint32_t K, int32_t* out,
+                                             const Segs& g = Segs{}) {
   constexpr int S = Shape<I16>::kSlots;
   cnt = uni(cnt);
   K = uni(K);
   const uint32_t sp = slice_of<I16>(cnt);
   uint32_t k[S];
-  load_keys<I16>(sm, k, sp);
+  load_keys<I16, SEG>(sm, k, sp, g);
   uint32_t lo, hi;
   key_range<I16, S>(sm, k, sp, cnt, lo, hi);
   const Sel s = range_select<I16, S>(sm, k, sp, cnt, lo, hi, K, 0u);
-  emit_chosen<I16, kToOut>(sm, k, sp, cnt, s, 0u, 0u, out, K, 0u);
+  emit_chosen<I16, kToOut, SEG>(sm, k, sp, cnt, s, 0u, 0u, out, K, 0u, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -778,11 +823,14 @@ __device__ __forceinline__ uint32_t spec_bound(Smem<I16>& sm, float (&x0)[kElems
 //
 // spec = the row length (>= kSpecMinLen) to start from a speculative bound
 // taken from the first two tiles (see spec_bound), else 0.  Those two tiles
-// are then loaded ahead of the ring, which starts at tile 2 with its loads
-// issued before the bound is computed.
+// go through x0 and x1 ahead of the ring, which starts at tile 2 with its
+// loads issued before the bound is computed; with preloaded they were
+// already loaded by the caller.
 template <bool I16, int VEC>
-__device__ void stream_chunk(Smem<I16>& sm, const float* __restrict__ rowp, uint32_t c0, uint32_t c1,
-                             uint32_t keep, uint32_t& cnt, uint32_t& L, uint32_t spec) {
+__device__ __forceinline__ void stream_chunk(Smem<I16>& sm, const float* __restrict__ rowp, uint32_t c0,
+                                             uint32_t c1, uint32_t keep, uint32_t& cnt, uint32_t& L,
+                                             uint32_t spec, float (&x0)[kElems], float (&x1)[kElems],
+                                             bool preloaded) {
   constexpr int PF = kPrefetch;
   c0 = uni(c0);
   c1 = uni(c1);
@@ -795,8 +843,7 @@ __device__ void stream_chunk(Smem<I16>& sm, const float* __restrict__ rowp, uint
   const float* base = rowp + c0;
   const bool pre = uni(spec) != 0u && F >= 2u;
   const uint32_t j1 = pre ? 2u : 0u;  // first tile of the ring
-  float x0[kElems], x1[kElems];
-  if (pre) {
+  if (pre && !preloaded) {
     load_full<VEC>(base, x0);
     load_full<VEC>(base + kTile, x1);
     __builtin_amdgcn_sched_barrier(0);
@@ -847,6 +894,201 @@ __device__ void stream_chunk(Smem<I16>& sm, const float* __restrict__ rowp, uint
   __syncthreads();
   cnt = st.cnt;
   L = st.L;
+}
+
+// ---------------------------------------------------------------------------
+// Wave-by-wave streaming of a row with a speculative bound
+//
+// Rows long enough to speculate (see spec_bound) usually end with a few
+// thousand candidates.  Each wavefront then streams its own contiguous
+// quarter of the row into its own quarter of the buffer, with positions from
+// its own ballots: no per-tile exchange between wavefronts and no per-tile
+// barrier.  The quarters are contiguous in index order, so the buffer read
+// segment by segment is in index order too.  If a wavefront's quarter of the
+// buffer would overflow (or the bound turns out too high) the row is
+// streamed again on the general path.
+// ---------------------------------------------------------------------------
+
+constexpr uint32_t kWaveTile = 64u * kElems;  // elements one wavefront loads per step
+
+// Elements per wavefront quarter of a row of n: whole wave tiles.
+__device__ __forceinline__ uint32_t quarter_of(uint32_t n) {
+  const uint32_t q = (n + kWaves - 1) / kWaves;
+  return (q + kWaveTile - 1) / kWaveTile * kWaveTile;
+}
+
+// Whether a row of n elements (n > K) goes wave by wave: long enough to
+// speculate, with a speculative rank below K.
+__device__ __forceinline__ bool wave_mode(uint32_t n, uint32_t K) {
+  if (n < kSpecMinLen) return false;
+  const uint64_t want = ((uint64_t)kSpecNum * K * (2u * kTile) + (uint64_t)kSpecDen * n - 1) / ((uint64_t)kSpecDen * n);
+  const uint32_t r = want > kSpecMinRank ? (uint32_t)want : kSpecMinRank;
+  return r < K;
+}
+
+// One full wave tile at `tile` (wave-uniform): lane l loads elements
+// u * 64 * VEC + l * VEC .. + VEC - 1.
+template <int VEC>
+__device__ __forceinline__ void load_wave_full(const float* __restrict__ tile, float (&x)[kElems]) {
+  const uint32_t l = threadIdx.x & 63;
+#pragma unroll
+  for (int u = 0; u < kElems / VEC; ++u) {
+    const uint32_t pos = (uint32_t)u * (64u * VEC) + l * VEC;
+    if constexpr (VEC == 4) {
+      const float4 v = *reinterpret_cast<const float4*>(tile + pos);
+      x[u * 4 + 0] = v.x;
+      x[u * 4 + 1] = v.y;
+      x[u * 4 + 2] = v.z;
+      x[u * 4 + 3] = v.w;
+    } else if constexpr (VEC == 2) {
+      const float2 v = *reinterpret_cast<const float2*>(tile + pos);
+      x[u * 2 + 0] = v.x;
+      x[u * 2 + 1] = v.y;
+    } else {
+      x[u] = tile[pos];
+    }
+  }
+}
+
+// The partial last wave tile [p0, end): nothing read at or past end.
+template <int VEC>
+__device__ __forceinline__ void load_wave_tail(const float* __restrict__ rowp, uint32_t end, uint32_t p0,
+                                               float (&x)[kElems]) {
+  const uint32_t l = threadIdx.x & 63;
+#pragma unroll
+  for (int u = 0; u < kElems / VEC; ++u) {
+    const uint32_t pos = p0 + (uint32_t)u * (64u * VEC) + l * VEC;
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) x[u * VEC + c] = (pos + c < end) ? rowp[pos + c] : 0.0f;
+  }
+}
+
+// Filters one wave tile (row positions p0 + ...) into this wavefront's part
+// of the buffer, slots sub0 + [0, SUB), after its cnt entries.  If the tile's
+// accepted elements would not fit, sets ovf and appends nothing from then on.
+template <bool I16, int VEC, bool FULL>
+__device__ __forceinline__ void wave_tile(Smem<I16>& sm, const float (&x)[kElems], uint32_t p0, uint32_t end, float bf,
+                                          uint32_t sub0, uint32_t& cnt, bool& ovf) {
+  constexpr uint32_t SUB = (uint32_t)Shape<I16>::kCap / kWaves;
+  constexpr int NL = kElems / VEC;
+  const uint32_t pbase = p0 + (threadIdx.x & 63) * VEC;
+  uint64_t bal[kElems];
+  uint32_t total = 0;
+#pragma unroll
+  for (int e = 0; e < kElems; ++e) {
+    const int u = e / VEC, c = e % VEC;
+    const bool in = FULL || pbase + (uint32_t)u * (64u * VEC) + c < end;
+    bal[e] = ballot(in && x[e] >= bf);
+    total += popc64(bal[e]);
+  }
+  if (ovf || cnt + total > SUB) {
+    ovf = true;
+    return;
+  }
+  uint32_t r0 = sub0 + cnt;
+#pragma unroll
+  for (int u = 0; u < NL; ++u) {
+    uint32_t r = r0;
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) r = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[u * VEC + c] >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)bal[u * VEC + c], r));
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) {
+      const int e = u * VEC + c;
+      const uint32_t pos = pbase + (uint32_t)u * (64u * VEC) + c;
+      const bool take = (FULL || pos < end) && x[e] >= bf;
+      if (take) {
+        sm.val[r] = __float_as_uint(x[e]);
+        sm.idx[r] = (typename Shape<I16>::Idx)pos;
+      }
+      r += take ? 1u : 0u;
+    }
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) r0 += popc64(bal[u * VEC + c]);
+  }
+  cnt += total;
+}
+
+// Streams row [0, n) wave by wave (wave_mode(n, K) holds; indices fit the
+// buffer's index type).  x0 / x1 carry each wavefront's first two wave tiles
+// (already loaded when preloaded); together they sample 4096 elements from
+// the four quarters for the speculative bound.  Returns false if the row must
+// be streamed again on the general path; otherwise total is the number of
+// candidates and g maps their positions to slots.
+template <bool I16, int VEC>
+__device__ __forceinline__ bool stream_row_waves(Smem<I16>& sm, const float* __restrict__ rowp, uint32_t n,
+                                                 uint32_t K, float (&x0)[kElems], float (&x1)[kElems],
+                                                 bool preloaded, uint32_t& total, Segs& g) {
+  constexpr int PF = kPrefetch;
+  constexpr uint32_t WT = kWaveTile;
+  constexpr uint32_t SUB = (uint32_t)Shape<I16>::kCap / kWaves;
+  n = uni(n);
+  K = uni(K);
+  const uint32_t w = uni(threadIdx.x >> 6);
+  const uint32_t Q = quarter_of(n);
+  const uint32_t qs = w * Q;
+  const uint32_t qe = qs + Q < n ? qs + Q : n;
+  const float* qp = rowp + qs;
+  if (!preloaded) {
+    load_wave_full<VEC>(qp, x0);
+    load_wave_full<VEC>(qp + WT, x1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Every quarter holds at least 2560 elements (n >= kSpecMinLen): F >= 5.
+  const uint32_t F = (qe - qs) / WT;
+  float buf[PF][kElems];
+#pragma unroll
+  for (int s = 0; s < PF - 1; ++s) {
+    load_wave_full<VEC>(qp + (2u + (uint32_t)s < F ? 2u + (uint32_t)s : F - 1) * WT, buf[s]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const uint32_t L = uni(spec_bound<I16>(sm, x0, x1, n, K));
+  const float bf = accept_floor(L);
+  const uint32_t sub0 = w * SUB;
+  uint32_t cnt = 0;
+  bool ovf = L == 0u;  // no bound: the quarters of the buffer could not hold the row
+  wave_tile<I16, VEC, true>(sm, x0, qs, qe, bf, sub0, cnt, ovf);
+  wave_tile<I16, VEC, true>(sm, x1, qs + WT, qe, bf, sub0, cnt, ovf);
+  const uint32_t Fr = F - (F - 2u) % PF;
+  for (uint32_t j0 = 2; j0 < Fr; j0 += PF) {
+#pragma unroll
+    for (int slot = 0; slot < PF; ++slot) {
+      const uint32_t j = j0 + slot;
+      const uint32_t jn = j + PF - 1 < F ? j + PF - 1 : F - 1;
+      load_wave_full<VEC>(qp + jn * WT, buf[(slot + PF - 1) % PF]);
+      __builtin_amdgcn_sched_barrier(0);
+      wave_tile<I16, VEC, true>(sm, buf[slot], qs + j * WT, qe, bf, sub0, cnt, ovf);
+    }
+  }
+#pragma unroll
+  for (int slot = 0; slot < PF - 1; ++slot) {
+    const uint32_t j = Fr + slot;
+    if (j < F) wave_tile<I16, VEC, true>(sm, buf[slot], qs + j * WT, qe, bf, sub0, cnt, ovf);
+  }
+  const uint32_t pt = qs + F * WT;
+  if (pt < qe) {
+    float x[kElems];
+    load_wave_tail<VEC>(rowp, qe, pt, x);
+    wave_tile<I16, VEC, false>(sm, x, pt, qe, bf, sub0, cnt, ovf);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    sm.red[w] = cnt;
+    sm.red[kWaves + w] = ovf ? 1u : 0u;
+  }
+  __syncthreads();
+  const u32x4 c = *reinterpret_cast<const u32x4*>(&sm.red[0]);
+  const u32x4 o = *reinterpret_cast<const u32x4*>(&sm.red[kWaves]);
+  const uint32_t c0 = uni(c.x), c1 = uni(c.y), c2 = uni(c.z), c3 = uni(c.w);
+  const bool bad = uni(o.x | o.y | o.z | o.w) != 0u;
+  total = c0 + c1 + c2 + c3;
+  g.pre1 = c0;
+  g.pre2 = c0 + c1;
+  g.pre3 = c0 + c1 + c2;
+  g.d1 = SUB - g.pre1;
+  g.d2 = 2u * SUB - g.pre2;
+  g.d3 = 3u * SUB - g.pre3;
+  __syncthreads();  // every wave has read the counts before sm.red is reused
+  return !bad && total >= K;
 }
 
 __device__ __forceinline__ int64_t clamp_len(const KernelParams& p, int row) {
@@ -905,34 +1147,79 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_ker
     }
   };
   bool first_row = true;
+  // The next row's first two tiles are loaded before this row's final
+  // selection, so that their latency hides behind it.
+  bool have_pre = false;
+  float x0[kElems], x1[kElems];
+  int64_t n = row < p.num_rows ? clamp_len(p, row) : 0;
+  bool waved = false;  // the current row's candidates sit wave by wave (Segs g)
+  Segs g{};
   while (row < p.num_rows) {
     if (!first_row) draw();
-    const int64_t n = clamp_len(p, row);
     int32_t* out = p.out + (int64_t)row * p.K;
+    uint32_t cnt = 0;
+    waved = false;
     if (n <= (int64_t)K) {
       write_all_then_pad(out, n, p.K);
     } else {
       const float* rowp = p.scores + (int64_t)row * p.row_stride;
-      uint32_t cnt = 0, L = 0;
-      const uint32_t spec = (redo || n < (int64_t)kSpecMinLen) ? 0u : (uint32_t)n;
-      stream_chunk<I16, VEC>(sm, rowp, 0u, (uint32_t)n, K, cnt, L, spec);
-      if (cnt < K && !redo) {
-        // Fewer than K elements reached the speculative bound: it was above
-        // the K-th best.  Stream the same row again without speculating.
-        redo = 1u;
-        __syncthreads();
-        continue;
+      if (I16 && !redo && wave_mode((uint32_t)n, K)) {
+        waved = stream_row_waves<I16, VEC>(sm, rowp, (uint32_t)n, K, x0, x1, have_pre, cnt, g);
+        have_pre = false;
+        if (!waved) {
+          // A quarter of the buffer overflowed, or fewer than K elements
+          // reached the speculative bound: stream the row again on the
+          // general path, without speculating.
+          redo = 1u;
+          continue;
+        }
+      } else {
+        uint32_t L = 0;
+        const uint32_t spec = (redo || n < (int64_t)kSpecMinLen) ? 0u : (uint32_t)n;
+        stream_chunk<I16, VEC>(sm, rowp, 0u, (uint32_t)n, K, cnt, L, spec, x0, x1, have_pre);
+        have_pre = false;
+        if (cnt < K && !redo) {
+          // Fewer than K elements reached the speculative bound: it was above
+          // the K-th best.  Stream the same row again without speculating.
+          redo = 1u;
+          __syncthreads();
+          continue;
+        }
       }
       redo = 0u;
-      draw();
-      final_select<I16>(sm, cnt, K, out);
     }
     draw();
+    if (threadIdx.x == 0) {
+      sm.acc[8] = next;
+      sm.acc[9] = next < (uint32_t)p.num_rows ? (uint32_t)clamp_len(p, (int)next) : 0u;
+    }
+    __syncthreads();
+    const int nrow = (int)uni(min(sm.acc[8], (uint32_t)p.num_rows));
+    const int64_t nn = (int64_t)uni(sm.acc[9]);
+    if (nrow < p.num_rows && nn >= (int64_t)kSpecMinLen && nn > (int64_t)K) {
+      // The next row's first two tiles: per wavefront quarter when it will
+      // go wave by wave, else the row's first two tiles.
+      const float* nrowp = p.scores + (int64_t)nrow * p.row_stride;
+      if (I16 && wave_mode((uint32_t)nn, K)) {
+        const float* qp = nrowp + uni(threadIdx.x >> 6) * quarter_of((uint32_t)nn);
+        load_wave_full<VEC>(qp, x0);
+        load_wave_full<VEC>(qp + kWaveTile, x1);
+      } else {
+        load_full<VEC>(nrowp, x0);
+        load_full<VEC>(nrowp + kTile, x1);
+      }
+      have_pre = true;
+    }
+    if (n > (int64_t)K) {
+      if (waved)
+        final_select<I16, true>(sm, cnt, K, out, g);
+      else
+        final_select<I16>(sm, cnt, K, out);
+    }
     first_row = false;
     drawn = false;
-    if (threadIdx.x == 0) sm.acc[8] = next;
-    __syncthreads();
-    row = (int)uni(min(sm.acc[8], (uint32_t)p.num_rows));
+    row = nrow;
+    n = nn;
     __syncthreads();  // every thread has read the next row before it is overwritten
   }
 }
@@ -1058,7 +1345,8 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_multi_kern
   const int64_t c1 = c0 + p.chunk < n ? c0 + p.chunk : n;
   const float* rowp = p.scores + (int64_t)row * p.row_stride;
   uint32_t cnt = 0, L = 0;
-  stream_chunk<I16, VEC>(sm, rowp, (uint32_t)c0, (uint32_t)c1, K, cnt, L, 0u);
+  float x0[kElems], x1[kElems];
+  stream_chunk<I16, VEC>(sm, rowp, (uint32_t)c0, (uint32_t)c1, K, cnt, L, 0u, x0, x1, false);
 
   const uint32_t sp = slice_of<I16>(cnt);
   uint32_t k[S];

@@ -218,6 +218,43 @@ def test_speculative_bound_fallback():
             assert_same(got, exp, f"spec fallback K={K} grid={grid}")
 
 
+@pytest.mark.parametrize("offset", [0, 1, 2])
+def test_wave_by_wave_rows(offset):
+    """Rows long enough for each wavefront to stream its own quarter: quarter
+    edges (n at and just past the speculation threshold, lengths that leave
+    a short last quarter), a quarter holding all the large values (its part
+    of the buffer overflows and the row is streamed again), ties, monotone
+    rows, and load widths of 4, 2 and 1 elements."""
+    rng = np.random.default_rng(61 + offset)
+    stride = {0: 65536, 1: 65529, 2: 65530}[offset]   # load widths 4, 1, 2
+    lens = [16384, 16385, 16383, 20479, 40000, stride - 1, 49153, 30001]
+    rows = []
+    for i, n in enumerate(lens):
+        kind = i % 4
+        if kind == 0:
+            x = rng.standard_normal(stride, dtype=np.float32)
+        elif kind == 1:
+            x = rng.standard_normal(stride, dtype=np.float32)
+            x[3 * n // 4:] += np.float32(5.0)           # the last quarter holds the largest values
+        elif kind == 2:
+            x = rng.integers(0, 3, size=stride).astype(np.float32)   # heavy ties
+        else:
+            x = (np.arange(stride, dtype=np.float32) * np.float32(0.25))
+            if i % 8 == 7:
+                x = -x
+        rows.append(x)
+    s = np.ascontiguousarray(np.stack(rows))
+    workloads.fill_tails(rng, s, np.array(lens))
+    L = np.array(lens, dtype=np.int32)
+    for K in (129, 700, 2048):
+        exp = topk_ragged_oracle(s, L, K)
+        for grid in (0, 1):
+            got, plan = run_gpu(s, L, K, offset=offset, tag=f"waves off={offset} K={K} grid={grid}",
+                                force_path=1, max_grid=grid)
+            assert plan["path"] == rrt.PATH_SINGLE and plan["idx16"] == 1
+            assert_same(got, exp, f"waves offset={offset} K={K} grid={grid}")
+
+
 def test_many_rows_random_lengths():
     rng = np.random.default_rng(31)
     lens = rng.integers(0, 20000, size=700)
