@@ -249,81 +249,76 @@ struct Sel {
   bool all_in;      // take covers every entry inside [lo, hi]: the set is key >= lo
 };
 
-template <bool I16>
-__device__ __forceinline__ uint32_t slice_of(uint32_t cnt) {
-  constexpr uint32_t S = (uint32_t)Shape<I16>::kSlots;
-  uint32_t sp = (uni(cnt) + kBlock - 1) / kBlock;
-  sp = (sp + 1u) & ~1u;
-  return sp < S ? sp : S;
-}
-
-// Entries of this thread's slice that hold data (of cnt): slice positions
-// j < valid_in_slice(...) are valid.
-__device__ __forceinline__ uint32_t valid_in_slice(uint32_t sp, uint32_t cnt) {
-  const uint32_t base = tid() * sp;
-  const uint32_t v = cnt > base ? cnt - base : 0u;
-  return v < sp ? v : sp;
-}
-
-// Where the buffer's positions live in LDS.  Normally position p is slot p.
-// After a row streamed wave by wave (stream_row_waves), wave w's entries --
-// positions [pre[w], pre[w + 1]) in index order -- sit from slot w * SUB on,
-// so position p is slot p + d[w] for the segment w that holds it.
-struct Segs {
-  uint32_t pre1, pre2, pre3;  // first position of segments 1, 2, 3
-  uint32_t d1, d2, d3;        // slot - position within segments 1, 2, 3
+// A thread's share of the buffer during a selection: slots base .. base +
+// sp - 1 (sp even and wave-uniform), of which the first nv hold entries.
+// Slices in thread order cover the entries in index order.
+struct Slice {
+  uint32_t base, sp, nv;
 };
 
-__device__ __forceinline__ uint32_t seg_slot(const Segs& g, uint32_t p) {
-  uint32_t d = 0u;
-  d = p >= g.pre1 ? g.d1 : d;
-  d = p >= g.pre2 ? g.d2 : d;
-  d = p >= g.pre3 ? g.d3 : d;
-  return p + d;
+// The buffer as filled by the general path: cnt entries in slots [0, cnt),
+// cut into 256 equal slices just large enough to cover them.
+template <bool I16>
+__device__ __forceinline__ Slice plain_slice(uint32_t cnt) {
+  constexpr uint32_t S = (uint32_t)Shape<I16>::kSlots;
+  cnt = uni(cnt);
+  uint32_t sp = (cnt + kBlock - 1) / kBlock;
+  sp = (sp + 1u) & ~1u;
+  sp = sp < S ? sp : S;
+  Slice sl;
+  sl.sp = sp;
+  sl.base = tid() * sp;
+  const uint32_t v = cnt > sl.base ? cnt - sl.base : 0u;
+  sl.nv = v < sp ? v : sp;
+  return sl;
 }
 
-// Keys of this thread's slice (positions t*sp + j, j < sp).
-template <bool I16, bool SEG = false>
-__device__ __forceinline__ void load_keys(const Smem<I16>& sm, uint32_t (&k)[Shape<I16>::kSlots], uint32_t sp,
-                                          const Segs& g = Segs{}) {
+// The buffer as filled wave by wave: this wavefront's cw entries in slots
+// [w * SUB, w * SUB + cw), cut into 64 slices, one per lane.
+template <bool I16>
+__device__ __forceinline__ Slice wave_slice(uint32_t cw) {
+  constexpr uint32_t S = (uint32_t)Shape<I16>::kSlots;
+  constexpr uint32_t SUB = (uint32_t)Shape<I16>::kCap / kWaves;
+  cw = uni(cw);
+  uint32_t sp = (cw + 63u) / 64u;
+  sp = (sp + 1u) & ~1u;
+  sp = sp < S ? sp : S;
+  const uint32_t t = tid();
+  const uint32_t lane = t & 63u;
+  Slice sl;
+  sl.sp = sp;
+  sl.base = (t >> 6) * SUB + lane * sp;
+  const uint32_t v = cw > lane * sp ? cw - lane * sp : 0u;
+  sl.nv = v < sp ? v : sp;
+  return sl;
+}
+
+// Keys of this thread's slice.
+template <bool I16>
+__device__ __forceinline__ void load_keys(const Smem<I16>& sm, uint32_t (&k)[Shape<I16>::kSlots], const Slice& sl) {
   constexpr int S = Shape<I16>::kSlots;
-  const uint32_t base = tid() * sp;
-  if constexpr (SEG) {
 #pragma unroll
-    for (int j = 0; j < S; ++j)
-      if ((uint32_t)j < sp) k[j] = ord_key(sm.val[seg_slot(g, base + j)]);
-  } else {
-#pragma unroll
-    for (int q = 0; q < S / 2; ++q) {
-      if ((uint32_t)(2 * q) < sp) {
-        const u32x2 a = *reinterpret_cast<const u32x2*>(&sm.val[base + 2 * q]);
-        k[2 * q + 0] = ord_key(a.x);
-        k[2 * q + 1] = ord_key(a.y);
-      }
+  for (int q = 0; q < S / 2; ++q) {
+    if ((uint32_t)(2 * q) < sl.sp) {
+      const u32x2 a = *reinterpret_cast<const u32x2*>(&sm.val[sl.base + 2 * q]);
+      k[2 * q + 0] = ord_key(a.x);
+      k[2 * q + 1] = ord_key(a.y);
     }
   }
 }
 
-template <bool I16, bool SEG = false>
-__device__ __forceinline__ void load_idx(const Smem<I16>& sm, uint32_t (&ix)[Shape<I16>::kSlots], uint32_t sp,
-                                         const Segs& g = Segs{}) {
+template <bool I16>
+__device__ __forceinline__ void load_idx(const Smem<I16>& sm, uint32_t (&ix)[Shape<I16>::kSlots], const Slice& sl) {
   constexpr int S = Shape<I16>::kSlots;
-  const uint32_t base = tid() * sp;
-  if constexpr (SEG) {
-#pragma unroll
-    for (int j = 0; j < S; ++j)
-      if ((uint32_t)j < sp) ix[j] = sm.idx[seg_slot(g, base + j)];
-    return;
-  }
 #pragma unroll
   for (int q = 0; q < S / 2; ++q) {
-    if ((uint32_t)(2 * q) < sp) {
+    if ((uint32_t)(2 * q) < sl.sp) {
       if constexpr (I16) {
-        const uint32_t a = *reinterpret_cast<const uint32_t*>(&sm.idx[base + 2 * q]);
+        const uint32_t a = *reinterpret_cast<const uint32_t*>(&sm.idx[sl.base + 2 * q]);
         ix[2 * q + 0] = a & 0xffffu;
         ix[2 * q + 1] = a >> 16;
       } else {
-        const u32x2 a = *reinterpret_cast<const u32x2*>(&sm.idx[base + 2 * q]);
+        const u32x2 a = *reinterpret_cast<const u32x2*>(&sm.idx[sl.base + 2 * q]);
         ix[2 * q + 0] = a.x;
         ix[2 * q + 1] = a.y;
       }
@@ -365,17 +360,16 @@ __device__ __forceinline__ uint32_t wave_min(uint32_t v) {
   return lane_value(x, 63);
 }
 
-// [lo, hi]: the smallest and largest key of the cnt entries (both wave-
-// uniform).  Contains one barrier.
+// [lo, hi]: the smallest and largest key of the entries (both uniform).
+// Contains one barrier.
 template <bool I16, int S>
-__device__ __forceinline__ void key_range(Smem<I16>& sm, const uint32_t (&k)[S], uint32_t sp, uint32_t cnt,
-                                          uint32_t& lo, uint32_t& hi) {
-  const uint32_t nv = valid_in_slice(sp, cnt);
+__device__ __forceinline__ void key_range(Smem<I16>& sm, const uint32_t (&k)[S], const Slice& sl, uint32_t& lo,
+                                          uint32_t& hi) {
   uint32_t mn = 0xffffffffu, mx = 0;
 #pragma unroll
   for (int j = 0; j < S; ++j) {
-    if ((uint32_t)(j) < sp) {
-      if ((uint32_t)j < nv) {
+    if ((uint32_t)(j) < sl.sp) {
+      if ((uint32_t)j < sl.nv) {
         mn = min(mn, k[j]);
         mx = max(mx, k[j]);
       }
@@ -403,9 +397,8 @@ __device__ __forceinline__ void key_range(Smem<I16>& sm, const uint32_t (&k)[S],
 // selection of keep entries.  Both histograms are zero on entry and hold
 // garbage on return.
 template <bool I16, int S>
-__device__ Sel range_select(Smem<I16>& sm, const uint32_t (&k)[S], uint32_t sp, uint32_t cnt, uint32_t lo,
-                            uint32_t hi, uint32_t keep, uint32_t stop_total) {
-  const uint32_t nv = valid_in_slice(sp, cnt);
+__device__ Sel range_select(Smem<I16>& sm, const uint32_t (&k)[S], const Slice& sl, uint32_t lo, uint32_t hi,
+                            uint32_t keep, uint32_t stop_total) {
   Sel r;
   r.ok = 1u;
   r.above = 0u;
@@ -431,8 +424,8 @@ __device__ Sel range_select(Smem<I16>& sm, const uint32_t (&k)[S], uint32_t sp, 
     const uint32_t sh = nb > bits ? nb - bits : 0u;
 #pragma unroll
     for (int j = 0; j < S; ++j) {
-      if ((uint32_t)(j) < sp) {
-        if ((uint32_t)j < nv && k[j] - lo <= range) atomicAdd(&h[(k[j] - lo) >> sh], 1u);
+      if ((uint32_t)(j) < sl.sp) {
+        if ((uint32_t)j < sl.nv && k[j] - lo <= range) atomicAdd(&h[(k[j] - lo) >> sh], 1u);
       }
     }
     __syncthreads();
@@ -468,14 +461,13 @@ enum EmitMode { kToBuffer = 0, kToOut = 1 };
 // row), so they are staged in hist1 and copied out with coalesced stores.
 // Every thread has read its buffer slice, and every wave has finished
 // reading the histograms, before any thread writes (the scan's barrier).
-template <bool I16, int MODE, bool SEG = false>
-__device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[Shape<I16>::kSlots], uint32_t sp,
-                                            uint32_t cnt, const Sel& s, uint32_t gt_base, uint32_t eq_base,
-                                            int32_t* out, uint32_t limit, uint32_t ibase, const Segs& g = Segs{}) {
-  static_assert(!SEG || MODE == kToOut, "a segmented buffer is only ever emitted to the output");
+template <bool I16, int MODE>
+__device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[Shape<I16>::kSlots], const Slice& sl,
+                                            const Sel& s, uint32_t gt_base, uint32_t eq_base, int32_t* out,
+                                            uint32_t limit, uint32_t ibase) {
   constexpr int S = Shape<I16>::kSlots;
   static_assert(S <= 32, "slice flags fit one word");
-  const uint32_t nv = valid_in_slice(sp, cnt);
+  const uint32_t sp = sl.sp, nv = sl.nv;
   const uint32_t width = s.hi - s.lo;
   const uint32_t take = s.take;
   // Whole interval taken and no earlier chunks: the chosen set is simply
@@ -499,7 +491,7 @@ __device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[S
   // Indices are read before the scan's barrier: a compaction then moves
   // entries down into other threads' slices.
   uint32_t ix[S];
-  load_idx<I16, SEG>(sm, ix, sp, g);
+  load_idx<I16>(sm, ix, sl);
   uint32_t total;
   const uint32_t excl = block_excl_scan(sm, (uint32_t)__popc(gtm) | ((uint32_t)__popc(eqm) << 16), &total);
   uint32_t first, m;
@@ -589,16 +581,15 @@ template <bool I16>
 __device__ __noinline__ uint64_t compact(Smem<I16>& sm, uint32_t cnt, uint32_t keep, uint32_t L) {
   constexpr int S = Shape<I16>::kSlots;
   constexpr uint32_t CAP = (uint32_t)Shape<I16>::kCap;
-  cnt = uni(cnt);
   keep = uni(keep);
   L = uni(L);
-  const uint32_t sp = slice_of<I16>(cnt);
+  const Slice sl = plain_slice<I16>(cnt);
   uint32_t k[S];
-  load_keys<I16>(sm, k, sp);
+  load_keys<I16>(sm, k, sl);
   uint32_t lo, hi;
-  key_range<I16, S>(sm, k, sp, cnt, lo, hi);
-  const Sel s = range_select<I16, S>(sm, k, sp, cnt, lo, hi, keep, CAP - kTile);
-  emit_chosen<I16, kToBuffer>(sm, k, sp, cnt, s, 0u, 0u, nullptr, CAP, 0u);
+  key_range<I16, S>(sm, k, sl, lo, hi);
+  const Sel s = range_select<I16, S>(sm, k, sl, lo, hi, keep, CAP - kTile);
+  emit_chosen<I16, kToBuffer>(sm, k, sl, s, 0u, 0u, nullptr, CAP, 0u);
   uint32_t Ln;
   if (s.all_in) {
     Ln = s.lo;  // the bin was kept whole
@@ -611,19 +602,16 @@ __device__ __noinline__ uint64_t compact(Smem<I16>& sm, uint32_t cnt, uint32_t k
 
 // The K best of the buffer, written to out in index order.  Inline, so that
 // loads issued before it (the next row's first tiles) stay in flight.
-template <bool I16, bool SEG = false>
-__device__ __forceinline__ void final_select(Smem<I16>& sm, uint32_t cnt, uint32_t K, int32_t* out,
-                                             const Segs& g = Segs{}) {
+template <bool I16>
+__device__ __forceinline__ void final_select(Smem<I16>& sm, const Slice& sl, uint32_t K, int32_t* out) {
   constexpr int S = Shape<I16>::kSlots;
-  cnt = uni(cnt);
   K = uni(K);
-  const uint32_t sp = slice_of<I16>(cnt);
   uint32_t k[S];
-  load_keys<I16, SEG>(sm, k, sp, g);
+  load_keys<I16>(sm, k, sl);
   uint32_t lo, hi;
-  key_range<I16, S>(sm, k, sp, cnt, lo, hi);
-  const Sel s = range_select<I16, S>(sm, k, sp, cnt, lo, hi, K, 0u);
-  emit_chosen<I16, kToOut, SEG>(sm, k, sp, cnt, s, 0u, 0u, out, K, 0u, g);
+  key_range<I16, S>(sm, k, sl, lo, hi);
+  const Sel s = range_select<I16, S>(sm, k, sl, lo, hi, K, 0u);
+  emit_chosen<I16, kToOut>(sm, k, sl, s, 0u, 0u, out, K, 0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -801,9 +789,13 @@ __device__ __forceinline__ uint32_t spec_bound(Smem<I16>& sm, float (&x0)[kElems
     k[e] = ord_key(__float_as_uint(x0[e]));
     k[kElems + e] = ord_key(__float_as_uint(x1[e]));
   }
+  Slice sl;
+  sl.base = 0u;
+  sl.sp = 2u * kElems;
+  sl.nv = 2u * kElems;
   uint32_t lo, hi;
-  key_range<I16, 2 * kElems>(sm, k, 2 * kElems, M, lo, hi);
-  const Sel s = range_select<I16, 2 * kElems>(sm, k, 2 * kElems, M, lo, hi, r, r + r / 8u + 8u);
+  key_range<I16, 2 * kElems>(sm, k, sl, lo, hi);
+  const Sel s = range_select<I16, 2 * kElems>(sm, k, sl, lo, hi, r, r + r / 8u + 8u);
 #pragma unroll
   for (int e = 0; e < kElems; ++e) {
     x0[e] = __uint_as_float(key_bits(k[e]));
@@ -1013,12 +1005,12 @@ __device__ __forceinline__ void wave_tile(Smem<I16>& sm, const float (&x)[kElems
 // buffer's index type).  x0 / x1 carry each wavefront's first two wave tiles
 // (already loaded when preloaded); together they sample 4096 elements from
 // the four quarters for the speculative bound.  Returns false if the row must
-// be streamed again on the general path; otherwise total is the number of
-// candidates and g maps their positions to slots.
+// be streamed again on the general path; otherwise mine is this
+// wavefront's number of candidates (in slots [w * SUB, w * SUB + mine)).
 template <bool I16, int VEC>
 __device__ __forceinline__ bool stream_row_waves(Smem<I16>& sm, const float* __restrict__ rowp, uint32_t n,
                                                  uint32_t K, float (&x0)[kElems], float (&x1)[kElems],
-                                                 bool preloaded, uint32_t& total, Segs& g) {
+                                                 bool preloaded, uint32_t& mine) {
   constexpr int PF = kPrefetch;
   constexpr uint32_t WT = kWaveTile;
   constexpr uint32_t SUB = (uint32_t)Shape<I16>::kCap / kWaves;
@@ -1080,15 +1072,9 @@ __device__ __forceinline__ bool stream_row_waves(Smem<I16>& sm, const float* __r
   const u32x4 o = *reinterpret_cast<const u32x4*>(&sm.red[kWaves]);
   const uint32_t c0 = uni(c.x), c1 = uni(c.y), c2 = uni(c.z), c3 = uni(c.w);
   const bool bad = uni(o.x | o.y | o.z | o.w) != 0u;
-  total = c0 + c1 + c2 + c3;
-  g.pre1 = c0;
-  g.pre2 = c0 + c1;
-  g.pre3 = c0 + c1 + c2;
-  g.d1 = SUB - g.pre1;
-  g.d2 = 2u * SUB - g.pre2;
-  g.d3 = 3u * SUB - g.pre3;
+  mine = cnt;
   __syncthreads();  // every wave has read the counts before sm.red is reused
-  return !bad && total >= K;
+  return !bad && c0 + c1 + c2 + c3 >= K;
 }
 
 __device__ __forceinline__ int64_t clamp_len(const KernelParams& p, int row) {
@@ -1152,8 +1138,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_ker
   bool have_pre = false;
   float x0[kElems], x1[kElems];
   int64_t n = row < p.num_rows ? clamp_len(p, row) : 0;
-  bool waved = false;  // the current row's candidates sit wave by wave (Segs g)
-  Segs g{};
+  bool waved = false;  // the current row's candidates sit wave by wave
   while (row < p.num_rows) {
     if (!first_row) draw();
     int32_t* out = p.out + (int64_t)row * p.K;
@@ -1164,7 +1149,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_ker
     } else {
       const float* rowp = p.scores + (int64_t)row * p.row_stride;
       if (I16 && !redo && wave_mode((uint32_t)n, K)) {
-        waved = stream_row_waves<I16, VEC>(sm, rowp, (uint32_t)n, K, x0, x1, have_pre, cnt, g);
+        waved = stream_row_waves<I16, VEC>(sm, rowp, (uint32_t)n, K, x0, x1, have_pre, cnt);
         have_pre = false;
         if (!waved) {
           // A quarter of the buffer overflowed, or fewer than K elements
@@ -1211,10 +1196,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_ker
       have_pre = true;
     }
     if (n > (int64_t)K) {
-      if (waved)
-        final_select<I16, true>(sm, cnt, K, out, g);
-      else
-        final_select<I16>(sm, cnt, K, out);
+      final_select<I16>(sm, waved ? wave_slice<I16>(cnt) : plain_slice<I16>(cnt), K, out);
     }
     first_row = false;
     drawn = false;
@@ -1348,17 +1330,17 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_multi_kern
   float x0[kElems], x1[kElems];
   stream_chunk<I16, VEC>(sm, rowp, (uint32_t)c0, (uint32_t)c1, K, cnt, L, 0u, x0, x1, false);
 
-  const uint32_t sp = slice_of<I16>(cnt);
+  const Slice sl = plain_slice<I16>(cnt);
+  const uint32_t sp = sl.sp, nv = sl.nv;
   uint32_t k[S];
-  load_keys<I16>(sm, k, sp);
-  const uint32_t base = (uint32_t)t * sp;
+  load_keys<I16>(sm, k, sl);
 
   // Round 1: the chunk's top-digit (11-bit) histogram into the row's, then
   // the row-wide threshold digit from a copy of the row's.
 #pragma unroll
   for (int j = 0; j < S; ++j) {
     if ((uint32_t)(j) < sp) {
-      if (base + j < cnt) atomicAdd(&sm.hist1[k[j] >> 21], 1u);
+      if ((uint32_t)j < nv) atomicAdd(&sm.hist1[k[j] >> 21], 1u);
     }
   }
   __syncthreads();
@@ -1381,7 +1363,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_multi_kern
 #pragma unroll
   for (int j = 0; j < S; ++j) {
     if ((uint32_t)(j) < sp) {
-      const bool valid = base + j < cnt;
+      const bool valid = (uint32_t)j < nv;
       const uint32_t km = k[j] & pmask;
       if (valid && km == prefix) atomicAdd(&sm.hist1[(k[j] >> 10) & 2047u], 1u);
       n_above += popc64(ballot(valid && km > prefix));
@@ -1408,7 +1390,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_multi_kern
 #pragma unroll
     for (int j = 0; j < S; ++j) {
       if ((uint32_t)(j) < sp) {
-        const bool valid = base + j < cnt;
+        const bool valid = (uint32_t)j < nv;
         const uint32_t km = k[j] & pmask;
         mine += (valid && km == prefix) ? 1u : 0u;
         n_above += popc64(ballot(valid && km > prefix));
@@ -1421,7 +1403,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_multi_kern
 #pragma unroll
     for (int j = 0; j < S; ++j) {
       if ((uint32_t)(j) < sp) {
-        const bool valid = base + j < cnt;
+        const bool valid = (uint32_t)j < nv;
         if (valid && (k[j] & pmask) == prefix) ws_store(&my_list[at++], k[j]);
       }
     }
@@ -1519,7 +1501,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_multi_kern
   s.in_bin = 0u;
   s.ok = ok;
   s.all_in = false;
-  emit_chosen<I16, kToOut>(sm, k, sp, cnt, s, gt_base, eq_base, out, K, (uint32_t)c0);
+  emit_chosen<I16, kToOut>(sm, k, sl, s, gt_base, eq_base, out, K, (uint32_t)c0);
 }
 
 // ---------------------------------------------------------------------------
