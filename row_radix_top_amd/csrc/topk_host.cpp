@@ -205,11 +205,13 @@ int topk_ragged_plan(const topk_device_props* props, int32_t num_rows, int64_t r
   if (want != 0 && want != TOPK_PATH_SINGLE && want != TOPK_PATH_MULTI)
     return fail(TOPK_EINVAL, "force_path must be 0, 1 or 2");
 
-  // Several workgroups per row only pay off when rows are long (the pages'
-  // 32K radix threshold, strict) and too few to occupy the GPU one per
-  // workgroup.  row_stride stands in for the longest length, which lives on
-  // the device.
-  const bool long_rows = row_stride > TOPK_RAGGED_RADIX_THRESHOLD;
+  // Several workgroups per row only pay off when rows are long and too few
+  // to occupy the GPU one per workgroup.  The pages split rows above their
+  // 32K radix threshold; here the one-workgroup path streams rows of up to
+  // 64K elements wave by wave faster than any split, so rows are split
+  // automatically only above that, and only into at least kMinSplit parts.
+  // row_stride stands in for the longest length, which lives on the device.
+  const bool long_rows = row_stride > TOPK_RAGGED_RADIX_THRESHOLD && row_stride > rrt::kSplitMinStride;
   if (want == TOPK_PATH_MULTI || (want == 0 && long_rows)) {
     // Size with the less resident of the two instances; the chunk length then
     // picks the instance (16-bit indices when a chunk fits them).
@@ -255,7 +257,7 @@ int topk_ragged_plan(const topk_device_props* props, int32_t num_rows, int64_t r
         std::snprintf(buf, sizeof(buf), "wg_per_row=%lld exceeds %d", (long long)G, rrt::kMaxGroup);
         return fail(TOPK_EINVAL, buf);
       }
-      const bool usable = want == TOPK_PATH_MULTI ? G >= 1 : G >= 2;
+      const bool usable = want == TOPK_PATH_MULTI ? G >= 1 : G >= rrt::kMinSplit;
       if (usable) {
         const int64_t grid = (int64_t)num_rows * G;
         if (grid <= avail) {

@@ -30,14 +30,21 @@ constexpr uint32_t kSpecNum = 3, kSpecDen = 2;
 constexpr uint32_t kSpecMinRank = 128;
 constexpr uint32_t kSpecMinLen = 16384;
 
-// Candidate buffer capacity.  It must hold K = 2048 kept entries plus one full
-// tile, so a tile always fits after a compaction.  With 16-bit indices (rows
-// or chunks of at most 65536 elements) an entry takes 6 bytes and the buffer
-// holds 5120 entries in less LDS than 4096 entries with 32-bit indices; the
-// slack lets most compactions stop at the top digit.  The 16-bit layout fits
-// four workgroups in a CU's 160 KB of LDS, the 32-bit one three.
+// Candidate buffer capacity: 5120 entries.  It must hold K = 2048 kept
+// entries plus one full tile, so a tile always fits after a compaction; the
+// slack lets most compactions keep a whole bin, and gives each of the four
+// wavefronts 1280 slots when a row streams wave by wave.  With 16-bit
+// indices (rows or chunks of at most 65536 elements) an entry takes 6 bytes
+// and four workgroups fit in a CU's 160 KB of LDS; with 32-bit indices,
+// three.
 constexpr int kIdx16Limit = 65536;
-constexpr int cap_of(bool idx16) { return idx16 ? 5120 : 4096; }
+constexpr int cap_of(bool) { return 5120; }
+
+// Rows are split over several workgroups only when longer than this (the
+// one-workgroup path streams shorter rows wave by wave faster than any
+// split) and only with at least kMinSplit workgroups per row.
+constexpr int64_t kSplitMinStride = 65536;
+constexpr int64_t kMinSplit = 4;
 
 // Workspace: a 256-byte header followed by one block per row of the
 // multi-workgroup path.  Header word 0: error bits; the word at byte

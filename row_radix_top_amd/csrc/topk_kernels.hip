@@ -134,6 +134,7 @@ struct Shape {
   static constexpr int kSlots = kCap / kBlock;  // buffer entries owned per thread
   using Idx = typename std::conditional<I16, uint16_t, uint32_t>::type;
   static_assert(kCap % kBlock == 0 && kSlots % 4 == 0, "capacity must tile the workgroup in aligned runs");
+  static_assert(kCap % (kWaves * 64) == 0 && kCap / kWaves <= 64 * kSlots, "a wavefront's quarter fits its slices");
   static_assert(kCap < 65536, "packed 16-bit counts");
   static_assert(kCap >= kMaxK + kTile, "a tile must fit after a compaction");
   // Workgroups per CU the LDS footprint allows (160 KB per CU); the register
@@ -1148,7 +1149,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_ker
       write_all_then_pad(out, n, p.K);
     } else {
       const float* rowp = p.scores + (int64_t)row * p.row_stride;
-      if (I16 && !redo && wave_mode((uint32_t)n, K)) {
+      if (!redo && wave_mode((uint32_t)n, K)) {
         waved = stream_row_waves<I16, VEC>(sm, rowp, (uint32_t)n, K, x0, x1, have_pre, cnt);
         have_pre = false;
         if (!waved) {
@@ -1185,7 +1186,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_ker
       // The next row's first two tiles: per wavefront quarter when it will
       // go wave by wave, else the row's first two tiles.
       const float* nrowp = p.scores + (int64_t)nrow * p.row_stride;
-      if (I16 && wave_mode((uint32_t)nn, K)) {
+      if (wave_mode((uint32_t)nn, K)) {
         const float* qp = nrowp + uni(threadIdx.x >> 6) * quarter_of((uint32_t)nn);
         load_wave_full<VEC>(qp, x0);
         load_wave_full<VEC>(qp + kWaveTile, x1);

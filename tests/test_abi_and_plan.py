@@ -51,8 +51,18 @@ def test_plan_single_path_for_short_rows():
     # At the threshold exactly: still one workgroup per row (strict ">").
     p = rrt.plan_for_props(256, 3, 3, 2, 32768, 1024)
     assert p["path"] == rrt.PATH_SINGLE
-    p = rrt.plan_for_props(256, 3, 3, 2, 32769, 1024)
-    assert p["path"] == rrt.PATH_MULTI
+    # Rows up to 65536 elements stay on one workgroup each, whatever their count.
+    for stride in (32769, 40000, 65536):
+        p = rrt.plan_for_props(256, 3, 3, 2, stride, 1024)
+        assert p["path"] == rrt.PATH_SINGLE, (stride, p)
+    p = rrt.plan_for_props(256, 3, 3, 2, 65537, 1024)
+    assert p["path"] == rrt.PATH_MULTI and p["wg_per_row"] >= 4
+    # A split into fewer than four parts is not worth it: one workgroup per row.
+    p = rrt.plan_for_props(256, 3, 3, 200, 131072, 1024)
+    assert p["path"] == rrt.PATH_SINGLE and p["fell_back"] == 0
+    # Unless the caller asks for it.
+    p = rrt.plan_for_props(256, 3, 3, 2, 40000, 1024, force_path=2)
+    assert p["path"] == rrt.PATH_MULTI and p["wg_per_row"] >= 2
 
 
 def test_plan_many_long_rows_use_persistent_single_path():
@@ -76,7 +86,7 @@ def test_plan_multi_is_always_coresident(cus, occ, rows, stride):
         assert p["headroom"] == headroom
         assert p["grid"] == rows * p["wg_per_row"]
         assert p["grid"] <= cap - headroom, p
-        assert p["wg_per_row"] >= 2
+        assert stride > 65536 and p["wg_per_row"] >= 4
         assert p["chunk"] % 2048 == 0
         assert (p["wg_per_row"] - 1) * p["chunk"] < stride <= p["wg_per_row"] * p["chunk"]
         assert p["workspace_bytes"] > 0
@@ -99,10 +109,13 @@ def test_plan_forced_multi_that_cannot_be_resident_falls_back():
 def test_plan_headroom_only_when_there_is_room():
     # One CU, occupancy 1: no room for headroom plus a group -> no headroom,
     # and a group of 2 cannot be resident -> single path.
-    p = rrt.plan_for_props(1, 1, 1, 1, 65536, 2048)
+    p = rrt.plan_for_props(1, 1, 1, 1, 131072, 2048)
     assert p["path"] == rrt.PATH_SINGLE
-    p = rrt.plan_for_props(4, 1, 1, 1, 65536, 2048)
-    assert p["path"] == rrt.PATH_MULTI and p["headroom"] == 1 and p["grid"] <= 3
+    # Four slots less one of headroom leave a group of 3: below the minimum split.
+    p = rrt.plan_for_props(4, 1, 1, 1, 131072, 2048)
+    assert p["path"] == rrt.PATH_SINGLE
+    p = rrt.plan_for_props(8, 1, 1, 1, 131072, 2048)
+    assert p["path"] == rrt.PATH_MULTI and p["headroom"] == 1 and 4 <= p["grid"] <= 7
 
 
 def test_plan_single_when_multi_kernel_cannot_run():

@@ -67,20 +67,35 @@ def test_workload_parity(name):
     exp = topk_ragged_oracle(w.scores, w.lengths, w.K)
     got, plan = run_gpu(w.scores, w.lengths, w.K, tag=name)
     assert_same(got, exp, name)
-    if name in ("mtp", "long_k1024", "long_k2048"):
-        assert plan["path"] == rrt.PATH_MULTI, plan
+    if name in ("long_k1024", "long_k2048"):
+        assert plan["path"] == rrt.PATH_MULTI and plan["wg_per_row"] >= 4, plan
+    if name == "mtp":
+        # Rows of at most 65536 elements stay on one workgroup each.
+        assert plan["path"] == rrt.PATH_SINGLE and plan["idx16"] == 1, plan
     if name == "prefill":
         assert plan["path"] == rrt.PATH_SINGLE and plan["grid"] < w.num_rows, plan
 
 
-@pytest.mark.parametrize("name", ["mtp", "long_k1024", "long_k2048"])
+@pytest.mark.parametrize("name", ["long_k1024", "long_k2048"])
 def test_long_rows_one_workgroup_per_row(name):
-    # The same long rows with the cooperative path switched off.
+    # The same long rows with the cooperative path switched off: 32-bit
+    # candidate indices, streamed wave by wave.
     w = workloads.make_workload(name)
     exp = topk_ragged_oracle(w.scores, w.lengths, w.K)
     got, plan = run_gpu(w.scores, w.lengths, w.K, tag=name + "/single", force_path=1)
-    assert plan["path"] == rrt.PATH_SINGLE
+    assert plan["path"] == rrt.PATH_SINGLE and plan["idx16"] == 0
     assert_same(got, exp, name + " single path")
+
+
+@pytest.mark.parametrize("G", [0, 2, 4])
+def test_mtp_rows_split_across_workgroups(G):
+    # The multi-token rows with the cooperative path forced on.
+    w = workloads.make_workload("mtp")
+    exp = topk_ragged_oracle(w.scores, w.lengths, w.K)
+    ov = dict(force_path=2, force_wg_per_row=G) if G else dict(force_path=2)
+    got, plan = run_gpu(w.scores, w.lengths, w.K, tag=f"mtp/multi G={G}", **ov)
+    assert plan["path"] == rrt.PATH_MULTI
+    assert_same(got, exp, f"mtp multi G={G}")
 
 
 @pytest.mark.parametrize("G", [1, 2, 3, 5, 16, 31, 64])
