@@ -137,6 +137,46 @@ def cpu_baseline(w, budget_s: float):
     }
 
 
+def host_call_us(fn, n: int) -> float:
+    """Host time per call (Python binding + C ABI + kernel enqueue), timed
+    on the CPU over n calls without waiting for the GPU in between."""
+    import time
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        fn(i)
+    t1 = time.perf_counter()
+    torch.cuda.synchronize()
+    return (t1 - t0) / n * 1e6
+
+
+def graph_replay_ms(fn, n: int, replays: int = 5) -> float:
+    """Average ms per launch when n launches are captured in one HIP graph
+    and the graph is replayed: the device-side cost without host overhead."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(n):
+                fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / (replays * n)
+    del g
+    return ms
+
+
 def bench_other(name: str, copies_bytes: int = 1 << 30, launches: int = 200):
     """Per-launch time of another workload over rotating input copies."""
     import torch
@@ -159,9 +199,13 @@ def bench_other(name: str, copies_bytes: int = 1 << 30, launches: int = 200):
     for i in range(min(20, ncopy)):
         launch(i)
     ms = time_launches(launch, launches)
+    host_us = host_call_us(launch, launches)
+    graph_ms = graph_replay_ms(launch, min(launches, 100))
     valid, _ = algorithmic_bytes(w.flat_lengths, w.row_stride, w.K)
     res = {
         "us_per_launch": round(ms * 1e3, 3),
+        "graph_us_per_launch": round(graph_ms * 1e3, 3),
+        "host_us_per_call": round(host_us, 3),
         "rows_per_s": w.num_rows / (ms * 1e-3),
         "effective_GBps": round(valid / (ms * 1e-3) / 1e9, 1),
         "frac_of_hbm_peak": round(valid / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),

@@ -141,6 +141,9 @@ typedef struct {
   int32_t fell_back;      /* 1 if a requested multi plan could not be made co-resident */
   int32_t idx16;          /* 1 if the instance keeps 16-bit candidate indices */
   uint64_t workspace_bytes;
+  int32_t split_rows;     /* single path: the last split_rows rows are split into chunks */
+  int32_t split_g;        /* chunks per split row */
+  int64_t split_chunk;    /* elements per chunk (a multiple of 2048) */
 } topk_plan;
 
 typedef struct {
@@ -151,6 +154,9 @@ typedef struct {
   int64_t force_chunk;       /* 0 auto, else elements per workgroup (multiple of 4) */
   uint32_t spin_limit;       /* 0 default; bound on a cooperative wait (polls) */
   int32_t min_chunk;         /* 0 default; smallest per-workgroup chunk the planner picks */
+  int32_t split_rows;        /* single path: 0 auto, -1 none, else split the last split_rows rows */
+  int32_t split_g;           /* 0 auto, else chunks per split row (1 .. 16) */
+  int64_t split_chunk;       /* 0 auto, else elements per chunk (a multiple of 2048) */
 } topk_overrides;
 
 /* Pure planning function (host only, no GPU needed).  vec_allowed is the

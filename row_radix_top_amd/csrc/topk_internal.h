@@ -78,6 +78,18 @@ inline constexpr GroupLayout group_layout(int wg_per_row, int cap) {
   return L;
 }
 
+// Split rows (one-workgroup kernel): the last rows of a launch may each be
+// cut into split_g chunks of split_chunk elements that any workgroup takes
+// as separate work units.  A chunk publishes its candidates to the row's
+// block; the last chunk to arrive selects over all of them.  Block layout
+// (bytes): 0 arrival counter (u32), 64 per-chunk candidate counts (u32),
+// kSplitHead chunk lists, each cap fp32 bit patterns then cap indices.
+constexpr int kMaxSplit = 16;
+constexpr uint64_t kSplitHead = 256;
+inline constexpr uint64_t split_block_bytes(int split_g, int cap) {
+  return round_up(kSplitHead + 8ull * (uint64_t)cap * (uint64_t)split_g, 256);
+}
+
 struct KernelParams {
   const float* scores;
   const int32_t* lengths;
@@ -90,10 +102,17 @@ struct KernelParams {
   int32_t K;
   int32_t wg_per_row;    // multi path: G
   uint32_t spin_limit;
+  // One-workgroup path: rows [split_from, num_rows) are split (see above);
+  // units = split_from + (num_rows - split_from) * split_g work units.
+  int32_t split_from;
+  int32_t split_g;
+  int64_t split_chunk;
+  uint64_t split_bytes;  // bytes per split row block, after the header
+  uint32_t num_units;
 };
 
 // Kernel lookup for the host side.  path: 1 single, 2 multi, 3 the
-// streaming-read reference (idx16 ignored).
+// streaming-read reference (idx16 ignored), 4 single with split rows.
 const void* kernel_ptr(int path, int vec, bool idx16);
 const void* zero_kernel_ptr();
 const void* keys_kernel_ptr();

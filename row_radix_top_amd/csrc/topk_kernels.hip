@@ -152,7 +152,13 @@ struct __align__(16) Smem {
   uint32_t tile_cnt[2][kElems][kWaves];
   uint32_t wsum[kWaves];
   uint32_t acc[16];
+  // Split-row merge (between streaming and selection, when tile_cnt is
+  // idle): each chunk's first slot in the buffer, and its list's offset in
+  // the row block less that slot.
+  __device__ uint32_t* part() { return &tile_cnt[0][0][0]; }
+  __device__ uint32_t* delta() { return &tile_cnt[0][0][0] + (kMaxSplit + 1); }
 };
+static_assert(2 * kMaxSplit + 1 <= 2 * kElems * kWaves, "merge offsets fit the tile-count area");
 
 // ---------------------------------------------------------------------------
 // Threshold search.  Every wavefront of the workgroup runs it on the same
@@ -1078,6 +1084,232 @@ __device__ __forceinline__ bool stream_row_waves(Smem<I16>& sm, const float* __r
   return !bad && c0 + c1 + c2 + c3 >= K;
 }
 
+// Workspace traffic between the workgroups of a row goes only through
+// agent-scope atomic operations (loads, stores, adds), which are coherent at
+// device scope on their own; no cache-wide write-back or invalidate is
+// needed.  Ordering: a writer wave waits until all its atomics have completed
+// before the workgroup arrives at the barrier, and readers issue their loads
+// only after seeing the arrival count.
+__device__ __forceinline__ uint32_t ws_load(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ws_store(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ws_add(uint32_t* p, uint32_t v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// Split rows: a chunk of a row as a unit of its own
+//
+// Every chunk of a row takes the same speculative bound: from the same 4096
+// elements (the first two wave tiles of each quarter of the row, the sample
+// a whole row streamed wave by wave uses) through the same integer
+// selection.  A chunk keeps every element of its range at or above the
+// bound, wave by wave; if a wavefront's part of the buffer overflows, the
+// chunk is streamed again on the general path from the same bound, whose
+// compactions keep a superset of the chunk's own K best.  Either way, every
+// element of the chunk that is among the row's K best is published once at
+// least K elements of the row reached the bound: such an element is at least
+// the K-th best key of the row, which is at least the bound, or it is among
+// its chunk's K best.  The last chunk to arrive checks that count and
+// selects over the union; failing it, it streams the whole row itself.
+// No workgroup ever waits for another, so nothing needs to be co-resident.
+// ---------------------------------------------------------------------------
+
+// Whether a split row of n elements is processed chunk by chunk (else its
+// chunk 0 takes it whole and the other chunks have nothing to do).
+__device__ __forceinline__ bool splits(uint32_t n, uint32_t K, uint32_t chunk) {
+  return n > chunk && wave_mode(n, K);
+}
+
+// Streams [c0, c1) of a row of n elements wave by wave, each wavefront its
+// own quarter of the range, from the row's speculative bound (returned in
+// L; 0 if none could be taken).  x0 / x1 hold the row's sample (loaded here
+// unless preloaded).  Returns false if a wavefront's part of the buffer
+// overflowed; otherwise mine / off are this wavefront's candidate count and
+// its offset among the chunk's total (in slots [w * SUB, w * SUB + mine)).
+template <bool I16, int VEC>
+__device__ __forceinline__ bool stream_piece_waves(Smem<I16>& sm, const float* __restrict__ rowp, uint32_t n,
+                                                   uint32_t K, uint32_t c0, uint32_t c1, float (&x0)[kElems],
+                                                   float (&x1)[kElems], bool preloaded, uint32_t& mine,
+                                                   uint32_t& off, uint32_t& total, uint32_t& L) {
+  constexpr int PF = kPrefetch;
+  constexpr uint32_t WT = kWaveTile;
+  constexpr uint32_t SUB = (uint32_t)Shape<I16>::kCap / kWaves;
+  n = uni(n);
+  K = uni(K);
+  c0 = uni(c0);
+  c1 = uni(c1);
+  const uint32_t w = uni(threadIdx.x >> 6);
+  if (!preloaded) {
+    const float* sp = rowp + w * quarter_of(n);
+    load_wave_full<VEC>(sp, x0);
+    load_wave_full<VEC>(sp + WT, x1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const uint32_t q = quarter_of(c1 - c0);
+  const uint32_t qs = c0 + w * q;  // at or past c1 when the range has fewer quarters
+  const uint32_t qe = qs + q < c1 ? qs + q : c1;
+  const uint32_t F = qe > qs ? (qe - qs) / WT : 0u;
+  const float* qp = rowp + qs;
+  float buf[PF][kElems];
+  if (F > 0u) {
+#pragma unroll
+    for (int s = 0; s < PF - 1; ++s) {
+      load_wave_full<VEC>(qp + ((uint32_t)s < F ? (uint32_t)s : F - 1) * WT, buf[s]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  L = uni(spec_bound<I16>(sm, x0, x1, n, K));
+  const float bf = accept_floor(L);
+  const uint32_t sub0 = w * SUB;
+  uint32_t cnt = 0;
+  bool ovf = L == 0u;
+  const uint32_t Fr = F - F % PF;
+  for (uint32_t j0 = 0; j0 < Fr; j0 += PF) {
+#pragma unroll
+    for (int slot = 0; slot < PF; ++slot) {
+      const uint32_t j = j0 + slot;
+      const uint32_t jn = j + PF - 1 < F ? j + PF - 1 : F - 1;
+      load_wave_full<VEC>(qp + jn * WT, buf[(slot + PF - 1) % PF]);
+      __builtin_amdgcn_sched_barrier(0);
+      wave_tile<I16, VEC, true>(sm, buf[slot], qs + j * WT, qe, bf, sub0, cnt, ovf);
+    }
+  }
+#pragma unroll
+  for (int slot = 0; slot < PF - 1; ++slot) {
+    const uint32_t j = Fr + slot;
+    if (j < F) wave_tile<I16, VEC, true>(sm, buf[slot], qs + j * WT, qe, bf, sub0, cnt, ovf);
+  }
+  const uint32_t pt = qs + F * WT;
+  if (pt < qe) {
+    float x[kElems];
+    load_wave_tail<VEC>(rowp, qe, pt, x);
+    wave_tile<I16, VEC, false>(sm, x, pt, qe, bf, sub0, cnt, ovf);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    sm.red[w] = cnt;
+    sm.red[kWaves + w] = ovf ? 1u : 0u;
+  }
+  __syncthreads();
+  const u32x4 c = *reinterpret_cast<const u32x4*>(&sm.red[0]);
+  const u32x4 o = *reinterpret_cast<const u32x4*>(&sm.red[kWaves]);
+  const uint32_t v0 = uni(c.x), v1 = uni(c.y), v2 = uni(c.z), v3 = uni(c.w);
+  const bool bad = uni(o.x | o.y | o.z | o.w) != 0u;
+  mine = cnt;
+  off = (w > 0 ? v0 : 0u) + (w > 1 ? v1 : 0u) + (w > 2 ? v2 : 0u);
+  total = v0 + v1 + v2 + v3;
+  __syncthreads();  // every wave has read the counts before sm.red is reused
+  return !bad;
+}
+
+// The block of split row `row` in the workspace (as 32-bit words).
+__device__ __forceinline__ uint32_t* split_block(const KernelParams& p, int row) {
+  return reinterpret_cast<uint32_t*>(p.ws + kWsHeader + (uint64_t)(row - p.split_from) * p.split_bytes);
+}
+
+// Writes this chunk's candidates to its list in the row block (fp32 bits,
+// row indices) and its count, then arrives.  Candidates sit wave by wave
+// (waved: this wavefront's mine at slots [w * SUB, ...), going to offset
+// off) or in slots [0, total) with indices relative to ibase.  Every store
+// is an agent-scope atomic and completes before the arrival, so the last
+// arriver, on any XCD, reads them after its own arrival without cache
+// maintenance.  Returns how many chunks arrived before this one.
+template <bool I16>
+__device__ __forceinline__ uint32_t publish_piece(Smem<I16>& sm, uint32_t* blk, int c, bool waved, uint32_t mine,
+                                                  uint32_t off, uint32_t total, uint32_t ibase) {
+  constexpr uint32_t CAP = (uint32_t)Shape<I16>::kCap;
+  constexpr uint32_t SUB = CAP / kWaves;
+  uint32_t* bits = blk + kSplitHead / 4 + (uint32_t)c * 2u * CAP;
+  uint32_t* idxs = bits + CAP;
+  const uint32_t t = tid();
+  if (waved) {
+    const uint32_t lane = t & 63u, s0 = (t >> 6) * SUB;
+    for (uint32_t i = lane; i < mine; i += 64u) {
+      ws_store(bits + off + i, sm.val[s0 + i]);
+      ws_store(idxs + off + i, (uint32_t)sm.idx[s0 + i]);
+    }
+  } else {
+    for (uint32_t i = t; i < total; i += kBlock) {
+      ws_store(bits + i, sm.val[i]);
+      ws_store(idxs + i, (uint32_t)sm.idx[i] + ibase);
+    }
+  }
+  if (t == 0) ws_store(blk + 16 + c, total);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (t == 0) sm.acc[10] = __hip_atomic_fetch_add(blk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  return uni(sm.acc[10]);
+}
+
+// The last arriver of a split row with geff chunks: resets the arrival
+// counter and gathers every chunk's list, in chunk order (so in index
+// order), into the buffer's slots [0, total).  Returns total; the buffer is
+// filled only when K <= total <= the capacity.  All loads are issued before
+// any is used (addresses clamped into the block), so the gather costs about
+// one round trip.  Then the lists and counts it read are zeroed, so the
+// block is all-zero again when the launch ends.
+template <bool I16>
+__device__ __forceinline__ uint32_t merge_pieces(Smem<I16>& sm, uint32_t* blk, uint32_t geff, uint32_t K) {
+  constexpr int S = Shape<I16>::kSlots;
+  constexpr uint32_t CAP = (uint32_t)Shape<I16>::kCap;
+  const uint32_t t = tid();
+  if (t < 64u) {
+    const uint32_t v = t < geff ? ws_load(blk + 16 + t) : 0u;
+    const uint32_t incl = wave_incl_scan(v);
+    if (t < geff) {
+      sm.part()[t + 1] = incl;
+      sm.delta()[t] = t * 2u * CAP - (incl - v);
+    }
+    if (t == 0) {
+      sm.part()[0] = 0u;
+      ws_store(blk, 0u);  // no other chunk of this row touches the counter again
+    }
+  }
+  __syncthreads();
+  const uint32_t total = uni(sm.part()[geff]);
+  uint32_t* lists = blk + kSplitHead / 4;
+  if (total >= K && total <= CAP) {
+    // Chunk boundaries as wave-uniform values (past geff: never reached).
+    uint32_t P[kMaxSplit];
+#pragma unroll
+    for (int g = 1; g < kMaxSplit; ++g) P[g] = (uint32_t)g < geff ? uni(sm.part()[g]) : 0xffffffffu;
+    uint32_t vb[S], vi[S];
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      const uint32_t i = t + (uint32_t)j * kBlock;
+      uint32_t ch = 0;
+#pragma unroll
+      for (int g = 1; g < kMaxSplit; ++g) ch += i >= P[g] ? 1u : 0u;
+      const uint32_t a = i < total ? i + sm.delta()[ch] : 0u;
+      vb[j] = ws_load(lists + a);
+      vi[j] = ws_load(lists + a + CAP);
+    }
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      const uint32_t i = t + (uint32_t)j * kBlock;
+      if (i < total) {
+        sm.val[i] = vb[j];
+        sm.idx[i] = (typename Shape<I16>::Idx)vi[j];
+      }
+    }
+    __syncthreads();  // every gather load has completed before its word is cleared
+  }
+  for (uint32_t g = 0; g < geff; ++g) {
+    const uint32_t m = uni(sm.part()[g + 1]) - uni(sm.part()[g]);
+    uint32_t* bits = lists + g * 2u * CAP;
+    for (uint32_t i = t; i < m; i += kBlock) {
+      ws_store(bits + i, 0u);
+      ws_store(bits + CAP + i, 0u);
+    }
+  }
+  if (t < geff) ws_store(blk + 16 + t, 0u);
+  return total;
+}
+
 __device__ __forceinline__ int64_t clamp_len(const KernelParams& p, int row) {
   int64_t n = p.lengths[row];
   n = n < 0 ? 0 : n;
@@ -1095,61 +1327,114 @@ __device__ __forceinline__ void zero_histograms(Smem<I16>& sm) {
 }
 
 // ---------------------------------------------------------------------------
-// One workgroup per row, persistent over rows.
+// One workgroup per row, persistent over work units.
 //
-// Workgroup b takes row b first.  With a workspace (rows outnumber the
-// grid) every later row comes from a ticket counter, so workgroups that run
-// faster -- the hardware favours the oldest waves -- take more rows.  Each
-// workgroup draws its next ticket when it starts a row, hiding the atomic's
-// latency behind the row, and stops at the first ticket past the last row.
-// There are exactly num_rows draws per launch (one per row after the first
-// gridDim.x, plus one failing draw per workgroup), so the draw that returns
-// num_rows - 1 is the last touch of the counter and resets it to zero.
-// Without a workspace row b + k * gridDim.x is taken in turn.
+// A unit is a whole row, or one chunk of a split row (the last rows of the
+// launch, when the plan splits them).  Workgroup b takes unit b first.
+// With a workspace every later unit comes from a ticket counter, so
+// workgroups that run faster -- the hardware favours the oldest waves --
+// take more units, and the small chunk units come last, evening out the
+// end of the launch.  Each workgroup draws its next ticket when it starts a
+// unit, hiding the atomic's latency behind the unit, and stops at the first
+// ticket past the last unit.  There are exactly num_units draws per launch
+// (one per unit after the first gridDim.x, plus one failing draw per
+// workgroup), so the draw that returns num_units - 1 is the last touch of
+// the counter and resets it to zero.  Without a workspace unit b + k *
+// gridDim.x is taken in turn.
 // ---------------------------------------------------------------------------
-template <int VEC, bool I16>
+
+// Row and chunk of unit u (chunk -1: a whole row).
+__device__ __forceinline__ void unit_of(const KernelParams& p, uint32_t u, int& row, int& c) {
+  if (u < (uint32_t)p.split_from) {
+    row = (int)u;
+    c = -1;
+  } else {
+    const uint32_t v = u - (uint32_t)p.split_from;
+    row = p.split_from + (int)(v / (uint32_t)p.split_g);
+    c = (int)(v % (uint32_t)p.split_g);
+  }
+}
+
+// SPLIT: the launch has split rows.  Without, every unit is a whole row and
+// the split-row code is compiled out (it costs registers the row loop needs).
+template <int VEC, bool I16, bool SPLIT>
 __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_kernel(KernelParams p) {
   __shared__ Smem<I16> sm;
   zero_histograms(sm);
   __syncthreads();
   const uint32_t K = (uint32_t)p.K;
+  const uint32_t U = p.num_units;
+  const uint32_t CH = (uint32_t)p.split_chunk;
   uint32_t* ticket = p.ws != nullptr ? reinterpret_cast<uint32_t*>(p.ws + kTicketOff) : nullptr;
   uint32_t redo = 0u;  // 1 while a row is streamed again after a failed speculation
-  uint32_t next = 0u;  // thread 0: the row after this one
-  bool drawn = false;  // thread 0: next is set for the current row
-  int row = blockIdx.x;
-  // The first row's draw waits until its scores are streamed: at launch every
+  uint32_t next = 0u;  // thread 0: the unit after this one
+  bool drawn = false;  // thread 0: next is set for the current unit
+  uint32_t unit = blockIdx.x;
+  // The first unit's draw waits until its scores are streamed: at launch every
   // workgroup would hit the counter at once, and the wait for the first tile
   // would include that queue.
   auto draw = [&]() {
     if (threadIdx.x == 0 && !drawn) {
       if (ticket != nullptr) {
         const uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (t == (uint32_t)p.num_rows - 1u) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (t == U - 1u) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         next = gridDim.x + t;
       } else {
-        next = (uint32_t)row + gridDim.x;
+        next = unit + gridDim.x;
       }
       drawn = true;
     }
   };
-  bool first_row = true;
-  // The next row's first two tiles are loaded before this row's final
-  // selection, so that their latency hides behind it.
+  bool first_unit = true;
+  // The next unit's first tiles (or its row's sample) are loaded before this
+  // unit's final selection, so that their latency hides behind it.
   bool have_pre = false;
   float x0[kElems], x1[kElems];
-  int64_t n = row < p.num_rows ? clamp_len(p, row) : 0;
-  bool waved = false;  // the current row's candidates sit wave by wave
-  while (row < p.num_rows) {
-    if (!first_row) draw();
+  int row = (int)unit, c = -1;
+  if constexpr (SPLIT) {
+    if (unit < U) unit_of(p, unit, row, c);
+  }
+  int64_t n = unit < U ? clamp_len(p, row) : 0;
+  while (unit < U) {
+    if (!first_unit) draw();
     int32_t* out = p.out + (int64_t)row * p.K;
     uint32_t cnt = 0;
-    waved = false;
-    if (n <= (int64_t)K) {
+    bool waved = false;  // the candidates sit wave by wave
+    bool select = false;
+    const bool piece = SPLIT && c >= 0 && splits((uint32_t)n, K, CH);
+    if (SPLIT && c > 0 && !piece) {
+      // Chunk of a row taken whole by its chunk 0: nothing to do.
+    } else if (n <= (int64_t)K) {
       write_all_then_pad(out, n, p.K);
     } else {
       const float* rowp = p.scores + (int64_t)row * p.row_stride;
-      if (!redo && wave_mode((uint32_t)n, K)) {
+      uint32_t g0 = 0, g1 = (uint32_t)n, gL = 0;  // general path: range, starting bound
+      bool general = true;
+      uint32_t mine = 0, off = 0;
+      if (SPLIT && (piece || (!redo && wave_mode((uint32_t)n, K)))) {
+        // One wave-by-wave streamer for chunks and whole rows alike (a second
+        // inlined copy would cost the loop registers).
+        if (piece) {
+          g0 = (uint32_t)c * CH;
+          g1 = g0 + CH < (uint32_t)n ? g0 + CH : (uint32_t)n;
+        }
+        if (g0 < g1) {
+          waved = stream_piece_waves<I16, VEC>(sm, rowp, (uint32_t)n, K, g0, g1, x0, x1, have_pre, mine, off, cnt,
+                                               gL);
+          general = !waved;
+        } else {
+          general = false;  // past the row's end: nothing to publish or wait for
+        }
+        have_pre = false;
+        if (!piece) {
+          if (!waved || cnt < K) {
+            // As below: stream the row again on the general path.
+            redo = 1u;
+            continue;
+          }
+          cnt = mine;
+        }
+      } else if (!redo && wave_mode((uint32_t)n, K)) {
         waved = stream_row_waves<I16, VEC>(sm, rowp, (uint32_t)n, K, x0, x1, have_pre, cnt);
         have_pre = false;
         if (!waved) {
@@ -1159,12 +1444,14 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_ker
           redo = 1u;
           continue;
         }
-      } else {
-        uint32_t L = 0;
-        const uint32_t spec = (redo || n < (int64_t)kSpecMinLen) ? 0u : (uint32_t)n;
-        stream_chunk<I16, VEC>(sm, rowp, 0u, (uint32_t)n, K, cnt, L, spec, x0, x1, have_pre);
+        general = false;
+      }
+      if (general) {
+        cnt = 0u;  // a failed wave-by-wave attempt leaves its count behind
+        const uint32_t spec = (piece || redo || n < (int64_t)kSpecMinLen) ? 0u : (uint32_t)n;
+        stream_chunk<I16, VEC>(sm, rowp, g0, g1, K, cnt, gL, spec, x0, x1, have_pre);
         have_pre = false;
-        if (cnt < K && !redo) {
+        if (!piece && cnt < K && !redo) {
           // Fewer than K elements reached the speculative bound: it was above
           // the K-th best.  Stream the same row again without speculating.
           redo = 1u;
@@ -1172,19 +1459,62 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_ker
           continue;
         }
       }
+      if (SPLIT && piece) {
+        const uint32_t geff = ((uint32_t)n + CH - 1u) / CH;
+        if (g0 < g1) {
+          uint32_t* blk = split_block(p, row);
+          const uint32_t before = publish_piece<I16>(sm, blk, c, waved, mine, off, cnt, g0);
+          if (before == geff - 1u) {
+            cnt = merge_pieces<I16>(sm, blk, geff, K);
+            if (cnt < K || cnt > (uint32_t)Shape<I16>::kCap) {
+              // Too few elements reached the bound, or too many to gather:
+              // this workgroup streams the whole row on the general path.
+              c = -1;
+              redo = 1u;
+              continue;
+            }
+            waved = false;
+            select = true;
+          }
+        }
+      } else {
+        select = true;
+      }
       redo = 0u;
     }
     draw();
     if (threadIdx.x == 0) {
-      sm.acc[8] = next;
-      sm.acc[9] = next < (uint32_t)p.num_rows ? (uint32_t)clamp_len(p, (int)next) : 0u;
+      uint32_t nrow = next, nc = 0u, nn = 0u;
+      if (next < U) {
+        if constexpr (SPLIT) {
+          int r, cc;
+          unit_of(p, next, r, cc);
+          nrow = (uint32_t)r;
+          nc = (uint32_t)(cc + 1);
+        }
+        nn = (uint32_t)clamp_len(p, (int)nrow);
+      }
+      sm.acc[8] = next < U ? next : U;
+      sm.acc[9] = nn;
+      if constexpr (SPLIT) {
+        sm.acc[11] = nrow;
+        sm.acc[12] = nc;
+      }
     }
     __syncthreads();
-    const int nrow = (int)uni(min(sm.acc[8], (uint32_t)p.num_rows));
+    const uint32_t nunit = uni(sm.acc[8]);
     const int64_t nn = (int64_t)uni(sm.acc[9]);
-    if (nrow < p.num_rows && nn >= (int64_t)kSpecMinLen && nn > (int64_t)K) {
-      // The next row's first two tiles: per wavefront quarter when it will
-      // go wave by wave, else the row's first two tiles.
+    int nrow = (int)nunit, nc = -1;
+    if constexpr (SPLIT) {
+      nrow = (int)uni(sm.acc[11]);
+      nc = (int)uni(sm.acc[12]) - 1;
+    }
+    // Prefetch for the next unit unless it is a chunk with nothing to do.
+    const bool npiece = SPLIT && nc >= 0 && splits((uint32_t)nn, K, CH);
+    if (nunit < U && nn >= (int64_t)kSpecMinLen && nn > (int64_t)K && (nc <= 0 || npiece)) {
+      // The next unit's first two tiles: per wavefront quarter (the row's
+      // sample) when it will go wave by wave or is a chunk, else the row's
+      // first two tiles.
       const float* nrowp = p.scores + (int64_t)nrow * p.row_stride;
       if (wave_mode((uint32_t)nn, K)) {
         const float* qp = nrowp + uni(threadIdx.x >> 6) * quarter_of((uint32_t)nn);
@@ -1196,36 +1526,22 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_ker
       }
       have_pre = true;
     }
-    if (n > (int64_t)K) {
+    if (select) {
       final_select<I16>(sm, waved ? wave_slice<I16>(cnt) : plain_slice<I16>(cnt), K, out);
     }
-    first_row = false;
+    first_unit = false;
     drawn = false;
+    unit = nunit;
     row = nrow;
+    c = nc;
     n = nn;
-    __syncthreads();  // every thread has read the next row before it is overwritten
+    __syncthreads();  // every thread has read the next unit before it is overwritten
   }
 }
 
 // ---------------------------------------------------------------------------
 // Several workgroups per row, cooperating through the workspace.
 // ---------------------------------------------------------------------------
-
-// Workspace traffic between the workgroups of a row goes only through
-// agent-scope atomic operations (loads, stores, adds), which are coherent at
-// device scope on their own; no cache-wide write-back or invalidate is
-// needed.  Ordering: a writer wave waits until all its atomics have completed
-// before the workgroup arrives at the barrier, and readers issue their loads
-// only after seeing the arrival count.
-__device__ __forceinline__ uint32_t ws_load(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void ws_store(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void ws_add(uint32_t* p, uint32_t v) {
-  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Arrival barrier of the workgroups sharing a row: every wave drains its
 // outstanding memory operations, one thread arrives and polls.  A wait that
@@ -1608,9 +1924,14 @@ static const void* pick(int path, int vec) {
     return reinterpret_cast<const void*>(&read_ref_kernel<1>);
   }
   if (path == 1) {
-    if (vec == 4) return reinterpret_cast<const void*>(&topk_single_kernel<4, I16>);
-    if (vec == 2) return reinterpret_cast<const void*>(&topk_single_kernel<2, I16>);
-    return reinterpret_cast<const void*>(&topk_single_kernel<1, I16>);
+    if (vec == 4) return reinterpret_cast<const void*>(&topk_single_kernel<4, I16, false>);
+    if (vec == 2) return reinterpret_cast<const void*>(&topk_single_kernel<2, I16, false>);
+    return reinterpret_cast<const void*>(&topk_single_kernel<1, I16, false>);
+  }
+  if (path == 4) {
+    if (vec == 4) return reinterpret_cast<const void*>(&topk_single_kernel<4, I16, true>);
+    if (vec == 2) return reinterpret_cast<const void*>(&topk_single_kernel<2, I16, true>);
+    return reinterpret_cast<const void*>(&topk_single_kernel<1, I16, true>);
   }
   if (vec == 4) return reinterpret_cast<const void*>(&topk_multi_kernel<4, I16>);
   if (vec == 2) return reinterpret_cast<const void*>(&topk_multi_kernel<2, I16>);

@@ -181,3 +181,28 @@ def test_plan_forced_group_sizes_are_kept():
     # 16 x 64 = 1024 workgroups exceed 768 slots less 256 of headroom.
     p = rrt.plan_for_props(256, 3, 3, 16, 131072, 2048, force_path=2, force_wg_per_row=64)
     assert p["path"] == rrt.PATH_SINGLE and p["fell_back"] == 1
+
+
+def test_plan_split_rows():
+    # Forced split of the last rows: units, grid and workspace follow.
+    p = rrt.plan_for_props(256, 4, 4, 64, 32768, 2048, split_rows=64, split_g=4)
+    assert p["path"] == rrt.PATH_SINGLE and p["split_rows"] == 64 and p["split_g"] == 4
+    assert p["split_chunk"] == 8192 and p["grid"] == 256
+    block = (256 + 8 * 5120 * 4 + 255) // 256 * 256
+    assert p["workspace_bytes"] == 256 + 64 * block
+    p = rrt.plan_for_props(256, 4, 4, 4096, 65536, 2048, split_rows=512, split_g=4)
+    assert p["split_rows"] == 512 and p["split_chunk"] == 16384 and p["grid"] == 1024
+    assert p["workspace_bytes"] == 256 + 512 * ((256 + 8 * 5120 * 4 + 255) // 256 * 256)
+    # More split rows than rows: all of them.
+    p = rrt.plan_for_props(256, 4, 4, 10, 65536, 2048, split_rows=99, split_g=2)
+    assert p["split_rows"] == 10 and p["grid"] == 20 and p["split_chunk"] == 32768
+    # Chunk given: a multiple of 2048 that covers the row with split_g chunks.
+    p = rrt.plan_for_props(256, 4, 4, 8, 65536, 2048, split_rows=8, split_g=4, split_chunk=16384)
+    assert p["split_chunk"] == 16384
+    for bad in (dict(split_g=17), dict(split_g=-1), dict(split_g=4, split_chunk=1000),
+                dict(split_g=2, split_chunk=8192)):
+        with pytest.raises(rrt.TopKError):
+            rrt.plan_for_props(256, 4, 4, 8, 65536, 2048, split_rows=8, **bad)
+    # -1: never split.
+    p = rrt.plan_for_props(256, 4, 4, 64, 32768, 2048, split_rows=-1)
+    assert p["split_rows"] == 0 and p["workspace_bytes"] == 0
