@@ -217,6 +217,66 @@ def bench_other(name: str, copies_bytes: int = 1 << 30, launches: int = 200):
     return res
 
 
+def decode_latency(launches: int = 400):
+    """Per-launch host and device overhead on the decode shape (64 rows,
+    row_stride 32768, K=2048, no workspace): what a decode step pays.
+
+    host: the Python binding's call, and the bare C-ABI call through ctypes
+    with ready pointers (enqueue only, no waiting on the GPU).  device:
+    eager back-to-back launches and hipGraph replay (HIP events), next to two
+    floors on the same input: a launch whose rows are all empty (it reads no
+    scores and only writes the -1 padding) and the streaming-read reference
+    (reads every valid score, selects nothing)."""
+    import ctypes
+    import time
+    import torch
+    import row_radix_top_amd as rrt
+    from row_radix_top_amd import binding, workloads
+    w = workloads.make_workload("decode")
+    dev = torch.device("cuda:0")
+    one = torch.from_numpy(w.scores).to(dev)
+    ncopy = max(1, min(1024, (1 << 30) // (one.numel() * 4)))
+    pool = torch.empty((ncopy,) + tuple(one.shape), dtype=torch.float32, device=dev)
+    pool.copy_(one.unsqueeze(0).expand_as(pool))
+    L = torch.from_numpy(w.flat_lengths).to(dev)
+    Z = torch.zeros_like(L)
+    out = torch.empty((w.num_rows, w.K), dtype=torch.int32, device=dev)
+    keys = torch.empty(w.num_rows, dtype=torch.int32, device=dev)
+    nbytes = rrt.workspace_size(w.num_rows, w.row_stride, w.K, device=dev)
+    assert nbytes == 0, "the decode shape needs no workspace"
+    lib = binding.load()
+    sp = int(torch.cuda.current_stream(dev).cuda_stream)
+    ptrs = [pool[i].data_ptr() for i in range(ncopy)]
+    lp, op = L.data_ptr(), out.data_ptr()
+    fn = lib.topk_ragged
+
+    def abi(i):
+        rc = fn(ptrs[i % ncopy], w.row_stride, lp, w.num_rows, 1, w.K, op, None, sp)
+        if rc != 0:
+            raise rrt.TopKError(rc, "topk_ragged", lib.topk_ragged_last_error().decode())
+
+    def py(i):
+        rrt.topk_ragged(pool[i % ncopy], L, w.K, out=out)
+
+    for i in range(20):
+        abi(i)
+    torch.cuda.synchronize()
+    res = {
+        "config": "decode: 64 rows, row_stride 32768, lengths U{1..32768}, K=2048, no workspace",
+        "eager_us_per_launch": round(time_launches(abi, launches) * 1e3, 3),
+        "graph_us_per_launch": round(graph_replay_ms(py, 100) * 1e3, 3),
+        "host_us_per_call_binding": round(host_call_us(py, launches), 3),
+        "host_us_per_call_c_abi": round(host_call_us(abi, launches), 3),
+        "empty_rows_us_per_launch": round(time_launches(
+            lambda i: rrt.topk_ragged(pool[i % ncopy], Z, w.K, out=out), launches) * 1e3, 3),
+        "read_reference_us_per_launch": round(time_launches(
+            lambda i: rrt.read_reference(pool[i % ncopy], L, out=keys), launches) * 1e3, 3),
+    }
+    del pool
+    torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -325,6 +385,8 @@ def main() -> int:
             log(f"timing {name}")
             others[name] = bench_other(name)
         result["workloads"] = others
+        log("decode launch latency")
+        result["decode_latency"] = decode_latency()
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
