@@ -157,6 +157,8 @@ typedef struct {
   int32_t split_rows;        /* single path: 0 auto, -1 none, else split the last split_rows rows */
   int32_t split_g;           /* 0 auto, else chunks per split row (1 .. 16) */
   int64_t split_chunk;       /* 0 auto, else elements per chunk (a multiple of 2048) */
+  int32_t max_occupancy;     /* 0 the device's, else plan as if no instance could keep more
+                                workgroups per CU resident (emulates a smaller device) */
 } topk_overrides;
 
 /* Pure planning function (host only, no GPU needed).  vec_allowed is the

@@ -53,7 +53,7 @@ class Overrides(ctypes.Structure):
                 ("max_grid", ctypes.c_int32), ("force_vec", ctypes.c_int32),
                 ("force_chunk", ctypes.c_int64), ("spin_limit", ctypes.c_uint32),
                 ("min_chunk", ctypes.c_int32), ("split_rows", ctypes.c_int32),
-                ("split_g", ctypes.c_int32), ("split_chunk", ctypes.c_int64)]
+                ("split_g", ctypes.c_int32), ("split_chunk", ctypes.c_int64), ("max_occupancy", ctypes.c_int32)]
 
     @classmethod
     def make(cls, **kw) -> "Overrides | None":

@@ -183,9 +183,19 @@ int plan_for_call(const float* scores, int32_t num_rows, int64_t row_stride, int
 
 extern "C" {
 
-int topk_ragged_plan(const topk_device_props* props, int32_t num_rows, int64_t row_stride, int32_t K,
+int topk_ragged_plan(const topk_device_props* props_in, int32_t num_rows, int64_t row_stride, int32_t K,
                      int32_t vec_allowed, const topk_overrides* ov, topk_plan* plan) {
-  if (props == nullptr || plan == nullptr) return fail(TOPK_EINVAL, "null props or plan");
+  if (props_in == nullptr || plan == nullptr) return fail(TOPK_EINVAL, "null props or plan");
+  // A smaller device, for testing the residency rules on this one: every
+  // instance keeps at most max_occupancy workgroups per CU.
+  topk_device_props capped = *props_in;
+  if (ov != nullptr && ov->max_occupancy != 0) {
+    if (ov->max_occupancy < 0) return fail(TOPK_EINVAL, "max_occupancy must be >= 0");
+    for (int32_t* o : {&capped.occupancy_single, &capped.occupancy_multi, &capped.occupancy_single16,
+                       &capped.occupancy_multi16})
+      *o = std::min(*o, ov->max_occupancy);
+  }
+  const topk_device_props* props = &capped;
   std::memset(plan, 0, sizeof(*plan));
   int rc = check_common(num_rows, row_stride, K);
   if (rc != TOPK_OK) return rc;

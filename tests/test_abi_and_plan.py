@@ -206,3 +206,30 @@ def test_plan_split_rows():
     # -1: never split.
     p = rrt.plan_for_props(256, 4, 4, 64, 32768, 2048, split_rows=-1)
     assert p["split_rows"] == 0 and p["workspace_bytes"] == 0
+
+
+def test_plan_occupancy_cap():
+    # A device that keeps one workgroup per CU: one slot of headroom, and
+    # every row group must fit the remaining 255 slots.
+    p = rrt.plan_for_props(256, 3, 3, 16, 131072, 2048, max_occupancy=1)
+    assert p["path"] == rrt.PATH_MULTI and p["resident_cap"] == 256 and p["headroom"] == 1
+    assert p["grid"] <= 255 and p["wg_per_row"] >= 4
+    assert p["grid"] == 16 * p["wg_per_row"]
+    # The one-workgroup path's persistent grid shrinks with it.
+    p = rrt.plan_for_props(256, 4, 4, 4096, 65536, 2048, max_occupancy=1)
+    assert p["path"] == rrt.PATH_SINGLE and p["grid"] == 256 and p["resident_cap"] == 256
+    # A forced group that no longer fits falls back to one workgroup per row.
+    p = rrt.plan_for_props(256, 3, 3, 16, 131072, 2048, max_occupancy=1, force_path=2, force_wg_per_row=16)
+    assert p["path"] == rrt.PATH_SINGLE and p["fell_back"] == 1
+    # Too many rows for four workgroups each: one per row.
+    p = rrt.plan_for_props(256, 3, 3, 100, 131072, 2048, max_occupancy=1)
+    assert p["path"] == rrt.PATH_SINGLE and p["fell_back"] == 0
+    # Occupancy 2: a CU's worth of headroom.
+    p = rrt.plan_for_props(256, 3, 3, 16, 131072, 2048, max_occupancy=2)
+    assert p["path"] == rrt.PATH_MULTI and p["resident_cap"] == 512 and p["headroom"] == 256
+    assert p["grid"] <= 256
+    # A cap above the device's changes nothing.
+    assert rrt.plan_for_props(256, 3, 3, 16, 131072, 2048, max_occupancy=8) == \
+        rrt.plan_for_props(256, 3, 3, 16, 131072, 2048)
+    with pytest.raises(rrt.TopKError):
+        rrt.plan_for_props(256, 3, 3, 16, 131072, 2048, max_occupancy=-1)
