@@ -87,6 +87,26 @@ int topk_ragged(const float* scores, int64_t row_stride, const int32_t* lengths,
                 int32_t num_rows, int32_t next_n, int32_t K, int32_t* out_idx,
                 void* workspace, hipStream_t stream);
 
+/*
+ * topk_ragged_offsets -- the same selection, with each row's chosen indices
+ * shifted into a flat ragged layout.  The PR #41189 page calls a
+ * "RaggedTransform" variant of the ragged top-K without defining it; this
+ * library reads it as: a row r whose scores start at row_offsets[r] in a
+ * flat (concatenated) layout reports positions in that layout.
+ *
+ *   row_offsets  int32 device array, num_rows entries, 4-byte aligned.
+ *   out_idx[r, i] = row_offsets[r] + (the i-th chosen index) for
+ *                   i < min(K, n_r), and -1 after that (unchanged).
+ *
+ * The sum is formed in 32-bit two's complement; the caller keeps
+ * row_offsets[r] + n_r - 1 within int32 (not checked on the device).  Every
+ * other argument, the workspace and the errors are as for topk_ragged; a
+ * null row_offsets with num_rows > 0 is TOPK_EINVAL.
+ */
+int topk_ragged_offsets(const float* scores, int64_t row_stride, const int32_t* lengths,
+                        const int32_t* row_offsets, int32_t num_rows, int32_t next_n, int32_t K,
+                        int32_t* out_idx, void* workspace, hipStream_t stream);
+
 /* Bytes of workspace topk_ragged needs for this shape on the stream's device.
  * *bytes = 0 means no workspace is used: one workgroup per row and no more
  * rows than resident workgroups.  With more rows than that, a 256-byte
@@ -179,10 +199,15 @@ int topk_ragged_workspace_size_ex(const float* scores, int32_t num_rows, int64_t
                                   int32_t K, const topk_overrides* ov, hipStream_t stream,
                                   size_t* bytes);
 
-/* topk_ragged with planner overrides (testing and benchmarking). */
+/* topk_ragged / topk_ragged_offsets with planner overrides (testing and
+ * benchmarking). */
 int topk_ragged_ex(const float* scores, int64_t row_stride, const int32_t* lengths,
                    int32_t num_rows, int32_t next_n, int32_t K, int32_t* out_idx,
                    void* workspace, hipStream_t stream, const topk_overrides* ov);
+int topk_ragged_offsets_ex(const float* scores, int64_t row_stride, const int32_t* lengths,
+                           const int32_t* row_offsets, int32_t num_rows, int32_t next_n, int32_t K,
+                           int32_t* out_idx, void* workspace, hipStream_t stream,
+                           const topk_overrides* ov);
 
 /* Error bits a kernel left in the workspace header (synchronises stream):
  * bit 0: a cooperative wait hit its spin limit; bit 1: a threshold search

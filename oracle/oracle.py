@@ -67,3 +67,24 @@ def topk_ragged_oracle(scores: np.ndarray, lengths: np.ndarray, K: int,
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (rc={rc})")
     return out
+
+
+def topk_ragged_offsets_oracle(scores: np.ndarray, lengths: np.ndarray, K: int, row_offsets,
+                               next_n: int | None = None, threads: int = 0) -> np.ndarray:
+    """The same selection with every chosen index of row r reported as
+    row_offsets[r] + index; the -1 padding is unchanged.
+
+    Reading of the PR #41189 page, whose fallback calls a "RaggedTransform"
+    variant of the ragged top-K without defining it: a row whose scores start
+    at row_offsets[r] in a flat layout (the rows' valid prefixes laid end to
+    end) reports positions in that layout.  Raises if a shifted index falls
+    outside [0, 2^31 - 1] (out of contract).
+    """
+    out = topk_ragged_oracle(scores, lengths, K, next_n=next_n, threads=threads).astype(np.int64)
+    off = np.asarray(row_offsets, dtype=np.int64).reshape(-1)
+    assert off.shape[0] == out.shape[0], "one offset per row"
+    shifted = np.where(out >= 0, out + off[:, None], -1)
+    chosen = out >= 0
+    if chosen.any() and (shifted[chosen].min() < 0 or shifted[chosen].max() > 2**31 - 1):
+        raise ValueError("row_offsets[r] + index leaves [0, 2^31 - 1]: outside the op's contract")
+    return shifted.astype(np.int32)

@@ -26,6 +26,7 @@ EXPORTED = (
     "topk_ragged_last_error", "topk_ragged_plan", "topk_ragged_query_plan",
     "topk_ragged_workspace_size_ex", "topk_ragged_ex", "topk_ragged_workspace_status",
     "topk_ragged_debug_keys", "topk_ragged_version", "topk_ragged_read_reference",
+    "topk_ragged_offsets", "topk_ragged_offsets_ex",
 )
 
 
@@ -107,6 +108,9 @@ def load() -> ctypes.CDLL:
         lib.topk_ragged_debug_keys.argtypes = [vp, vp, i64, vp]
         lib.topk_ragged_version.argtypes = []
         lib.topk_ragged_read_reference.argtypes = [vp, i64, vp, i32, vp, vp]
+        lib.topk_ragged_offsets.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp, vp]
+        lib.topk_ragged_offsets_ex.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp, vp,
+                                               ctypes.POINTER(Overrides)]
         for name in EXPORTED:
             getattr(lib, name).restype = ctypes.c_int if name != "topk_ragged_last_error" else ctypes.c_char_p
         _lib = lib
@@ -226,14 +230,16 @@ def _validate(scores, lengths, out, K):
 
 
 def topk_ragged(scores, lengths, K: int, *, out=None, workspace=None, next_n: int | None = None,
-                stream=None, **overrides):
+                stream=None, row_offsets=None, **overrides):
     """Indices of the K largest of the first lengths[r] scores of each row.
 
     scores: float32 CUDA [num_rows, row_stride-or-wider view] with unit column
     stride; lengths: int32 CUDA [num_rows] or [batch, next_n] (next_n is then
     taken from its second dimension); returns int32 [num_rows, K], ascending
     per row, -1 padded.  workspace: a tensor from new_workspace() sized by
-    workspace_size(), needed only when that size is nonzero.
+    workspace_size(), needed only when that size is nonzero.  row_offsets:
+    int32 CUDA [num_rows]; if given, row r's chosen indices are reported as
+    row_offsets[r] + index (topk_ragged_offsets).
     """
     import torch
     if next_n is None:
@@ -246,6 +252,18 @@ def topk_ragged(scores, lengths, K: int, *, out=None, workspace=None, next_n: in
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     lib = load()
     sp = _stream_ptr(stream, scores.device)
+    if row_offsets is not None:
+        if (row_offsets.dtype != torch.int32 or not row_offsets.is_cuda or row_offsets.numel() != num_rows
+                or not row_offsets.is_contiguous()):
+            raise ValueError("row_offsets must be a contiguous int32 CUDA tensor with one entry per row")
+        args = (scores.data_ptr(), scores.stride(0), lengths.data_ptr(), row_offsets.data_ptr(), num_rows,
+                next_n, K, out.data_ptr(), ws_ptr, sp)
+        if ov is None:
+            rc = lib.topk_ragged_offsets(*args)
+        else:
+            rc = lib.topk_ragged_offsets_ex(*args, ctypes.byref(ov))
+        _check(rc, "topk_ragged_offsets")
+        return out
     if ov is None:
         rc = lib.topk_ragged(scores.data_ptr(), scores.stride(0), lengths.data_ptr(), num_rows, next_n,
                              K, out.data_ptr(), ws_ptr, sp)

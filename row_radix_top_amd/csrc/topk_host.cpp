@@ -395,9 +395,13 @@ int topk_ragged_workspace_init(void* workspace, size_t bytes, hipStream_t stream
   return TOPK_OK;
 }
 
-int topk_ragged_ex(const float* scores, int64_t row_stride, const int32_t* lengths, int32_t num_rows,
-                   int32_t next_n, int32_t K, int32_t* out_idx, void* workspace, hipStream_t stream,
-                   const topk_overrides* ov) {
+}  // extern "C"
+
+namespace {
+
+int launch(const float* scores, int64_t row_stride, const int32_t* lengths, const int32_t* row_offsets,
+           int32_t num_rows, int32_t next_n, int32_t K, int32_t* out_idx, void* workspace, hipStream_t stream,
+           const topk_overrides* ov) {
   if (num_rows < 0) return fail(TOPK_EINVAL, "num_rows must be >= 0");
   if (next_n < 1) return fail(TOPK_EINVAL, "next_n must be >= 1");
   if (num_rows % next_n != 0) return fail(TOPK_EINVAL, "num_rows must be a multiple of next_n");
@@ -407,8 +411,8 @@ int topk_ragged_ex(const float* scores, int64_t row_stride, const int32_t* lengt
   if (scores == nullptr || lengths == nullptr || out_idx == nullptr)
     return fail(TOPK_EINVAL, "null scores, lengths or out_idx");
   if (reinterpret_cast<uintptr_t>(out_idx) % 4 != 0 || reinterpret_cast<uintptr_t>(lengths) % 4 != 0 ||
-      reinterpret_cast<uintptr_t>(scores) % 4 != 0)
-    return fail(TOPK_EINVAL, "scores, lengths and out_idx must be 4-byte aligned");
+      reinterpret_cast<uintptr_t>(scores) % 4 != 0 || reinterpret_cast<uintptr_t>(row_offsets) % 4 != 0)
+    return fail(TOPK_EINVAL, "scores, lengths, row_offsets and out_idx must be 4-byte aligned");
   topk_plan plan;
   rc = plan_for_call(scores, num_rows, row_stride, K, ov, stream, nullptr, &plan);
   if (rc != TOPK_OK) return rc;
@@ -421,6 +425,7 @@ int topk_ragged_ex(const float* scores, int64_t row_stride, const int32_t* lengt
   rrt::KernelParams kp{};
   kp.scores = scores;
   kp.lengths = lengths;
+  kp.row_offsets = row_offsets;
   kp.out = out_idx;
   kp.ws = plan.workspace_bytes > 0 ? static_cast<uint8_t*>(workspace) : nullptr;
   kp.row_stride = row_stride;
@@ -456,9 +461,34 @@ int topk_ragged_ex(const float* scores, int64_t row_stride, const int32_t* lengt
   return TOPK_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int topk_ragged_ex(const float* scores, int64_t row_stride, const int32_t* lengths, int32_t num_rows,
+                   int32_t next_n, int32_t K, int32_t* out_idx, void* workspace, hipStream_t stream,
+                   const topk_overrides* ov) {
+  return launch(scores, row_stride, lengths, nullptr, num_rows, next_n, K, out_idx, workspace, stream, ov);
+}
+
 int topk_ragged(const float* scores, int64_t row_stride, const int32_t* lengths, int32_t num_rows,
                 int32_t next_n, int32_t K, int32_t* out_idx, void* workspace, hipStream_t stream) {
-  return topk_ragged_ex(scores, row_stride, lengths, num_rows, next_n, K, out_idx, workspace, stream, nullptr);
+  return launch(scores, row_stride, lengths, nullptr, num_rows, next_n, K, out_idx, workspace, stream, nullptr);
+}
+
+int topk_ragged_offsets(const float* scores, int64_t row_stride, const int32_t* lengths,
+                        const int32_t* row_offsets, int32_t num_rows, int32_t next_n, int32_t K,
+                        int32_t* out_idx, void* workspace, hipStream_t stream) {
+  if (num_rows > 0 && row_offsets == nullptr) return fail(TOPK_EINVAL, "null row_offsets");
+  return launch(scores, row_stride, lengths, row_offsets, num_rows, next_n, K, out_idx, workspace, stream,
+                nullptr);
+}
+
+int topk_ragged_offsets_ex(const float* scores, int64_t row_stride, const int32_t* lengths,
+                           const int32_t* row_offsets, int32_t num_rows, int32_t next_n, int32_t K,
+                           int32_t* out_idx, void* workspace, hipStream_t stream, const topk_overrides* ov) {
+  if (num_rows > 0 && row_offsets == nullptr) return fail(TOPK_EINVAL, "null row_offsets");
+  return launch(scores, row_stride, lengths, row_offsets, num_rows, next_n, K, out_idx, workspace, stream, ov);
 }
 
 const char* topk_ragged_last_error(void) { return g_last_error.c_str(); }

@@ -93,6 +93,7 @@ inline constexpr uint64_t split_block_bytes(int split_g, int cap) {
 struct KernelParams {
   const float* scores;
   const int32_t* lengths;
+  const int32_t* row_offsets;  // nullable: added to each row's chosen indices
   int32_t* out;
   uint8_t* ws;
   int64_t row_stride;

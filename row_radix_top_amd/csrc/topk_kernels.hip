@@ -607,10 +607,12 @@ __device__ __noinline__ uint64_t compact(Smem<I16>& sm, uint32_t cnt, uint32_t k
   return ((uint64_t)(s.above + s.take) << 32) | Ln;
 }
 
-// The K best of the buffer, written to out in index order.  Inline, so that
-// loads issued before it (the next row's first tiles) stay in flight.
+// The K best of the buffer, written to out in index order as ibase + index.
+// Inline, so that loads issued before it (the next row's first tiles) stay
+// in flight.
 template <bool I16>
-__device__ __forceinline__ void final_select(Smem<I16>& sm, const Slice& sl, uint32_t K, int32_t* out) {
+__device__ __forceinline__ void final_select(Smem<I16>& sm, const Slice& sl, uint32_t K, int32_t* out,
+                                             uint32_t ibase) {
   constexpr int S = Shape<I16>::kSlots;
   K = uni(K);
   uint32_t k[S];
@@ -618,7 +620,7 @@ __device__ __forceinline__ void final_select(Smem<I16>& sm, const Slice& sl, uin
   uint32_t lo, hi;
   key_range<I16, S>(sm, k, sl, lo, hi);
   const Sel s = range_select<I16, S>(sm, k, sl, lo, hi, K, 0u);
-  emit_chosen<I16, kToOut>(sm, k, sl, s, 0u, 0u, out, K, 0u);
+  emit_chosen<I16, kToOut>(sm, k, sl, s, 0u, 0u, out, K, ibase);
 }
 
 // ---------------------------------------------------------------------------
@@ -1316,9 +1318,15 @@ __device__ __forceinline__ int64_t clamp_len(const KernelParams& p, int row) {
   return n > p.row_stride ? p.row_stride : n;
 }
 
-// n <= K: every valid index, then -1.  Reads no scores.
-__device__ __forceinline__ void write_all_then_pad(int32_t* out, int64_t n, int K) {
-  for (int i = threadIdx.x; i < K; i += kBlock) out[i] = i < n ? i : -1;
+// n <= K: every valid index (plus the row's offset), then -1.  Reads no scores.
+__device__ __forceinline__ void write_all_then_pad(int32_t* out, int64_t n, int K, uint32_t off) {
+  for (int i = threadIdx.x; i < K; i += kBlock) out[i] = i < n ? (int32_t)(off + (uint32_t)i) : -1;
+}
+
+// What a row's chosen indices are shifted by in the output: its offset in a
+// flat ragged layout when the caller gives row offsets, else 0.
+__device__ __forceinline__ uint32_t offset_of(const KernelParams& p, int row) {
+  return p.row_offsets != nullptr ? (uint32_t)p.row_offsets[row] : 0u;
 }
 
 template <bool I16>
@@ -1395,6 +1403,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_ker
     if (unit < U) unit_of(p, unit, row, c);
   }
   int64_t n = unit < U ? clamp_len(p, row) : 0;
+  uint32_t off = unit < U ? uni(offset_of(p, row)) : 0u;
   while (unit < U) {
     if (!first_unit) draw();
     int32_t* out = p.out + (int64_t)row * p.K;
@@ -1405,7 +1414,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_ker
     if (SPLIT && c > 0 && !piece) {
       // Chunk of a row taken whole by its chunk 0: nothing to do.
     } else if (n <= (int64_t)K) {
-      write_all_then_pad(out, n, p.K);
+      write_all_then_pad(out, n, p.K, off);
     } else {
       const float* rowp = p.scores + (int64_t)row * p.row_stride;
       uint32_t g0 = 0, g1 = (uint32_t)n, gL = 0;  // general path: range, starting bound
@@ -1493,6 +1502,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_ker
           nc = (uint32_t)(cc + 1);
         }
         nn = (uint32_t)clamp_len(p, (int)nrow);
+        sm.acc[13] = offset_of(p, (int)nrow);
       }
       sm.acc[8] = next < U ? next : U;
       sm.acc[9] = nn;
@@ -1504,6 +1514,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_ker
     __syncthreads();
     const uint32_t nunit = uni(sm.acc[8]);
     const int64_t nn = (int64_t)uni(sm.acc[9]);
+    const uint32_t noff = uni(sm.acc[13]);
     int nrow = (int)nunit, nc = -1;
     if constexpr (SPLIT) {
       nrow = (int)uni(sm.acc[11]);
@@ -1527,7 +1538,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_ker
       have_pre = true;
     }
     if (select) {
-      final_select<I16>(sm, waved ? wave_slice<I16>(cnt) : plain_slice<I16>(cnt), K, out);
+      final_select<I16>(sm, waved ? wave_slice<I16>(cnt) : plain_slice<I16>(cnt), K, out, off);
     }
     first_unit = false;
     drawn = false;
@@ -1535,6 +1546,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_ker
     row = nrow;
     c = nc;
     n = nn;
+    off = noff;
     __syncthreads();  // every thread has read the next unit before it is overwritten
   }
 }
@@ -1620,7 +1632,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_multi_kern
   const int64_t n = clamp_len(p, row);
   int32_t* out = p.out + (int64_t)row * p.K;
   if (n <= (int64_t)K) {
-    if (g == 0) write_all_then_pad(out, n, p.K);
+    if (g == 0) write_all_then_pad(out, n, p.K, offset_of(p, row));
     return;
   }
   const int grow = (int)((n + p.chunk - 1) / p.chunk);  // workgroups with data in this row
@@ -1818,7 +1830,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_multi_kern
   s.in_bin = 0u;
   s.ok = ok;
   s.all_in = false;
-  emit_chosen<I16, kToOut>(sm, k, sl, s, gt_base, eq_base, out, K, (uint32_t)c0);
+  emit_chosen<I16, kToOut>(sm, k, sl, s, gt_base, eq_base, out, K, (uint32_t)c0 + offset_of(p, row));
 }
 
 // ---------------------------------------------------------------------------

@@ -24,7 +24,7 @@ def note(msg: str) -> None:
 
 
 def run_gpu(scores: np.ndarray, lengths: np.ndarray, K: int, *, next_n=None, offset: int = 0,
-            check_workspace: bool = True, tag: str = "", **overrides):
+            check_workspace: bool = True, tag: str = "", row_offsets=None, **overrides):
     """Copies inputs to the GPU, runs topk_ragged, returns (out, plan).
 
     offset > 0 places row 0 at element `offset` of the device buffer, so the
@@ -41,7 +41,10 @@ def run_gpu(scores: np.ndarray, lengths: np.ndarray, K: int, *, next_n=None, off
     note(f"{tag} rows={num_rows} stride={stride} K={K} offset={offset} plan={plan}")
     nbytes = rrt.workspace_size(num_rows, stride, K, scores=s, **overrides)
     ws = rrt.new_workspace(nbytes, dev)
-    out = rrt.topk_ragged(s, L, K, workspace=ws, next_n=next_n, **overrides)
+    ro = None
+    if row_offsets is not None:
+        ro = torch.from_numpy(np.ascontiguousarray(row_offsets, dtype=np.int32)).to(dev)
+    out = rrt.topk_ragged(s, L, K, workspace=ws, next_n=next_n, row_offsets=ro, **overrides)
     torch.cuda.synchronize()
     if check_workspace and ws is not None:
         assert int(ws.count_nonzero().item()) == 0, "workspace must be all-zero after a launch"

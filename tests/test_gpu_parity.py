@@ -332,3 +332,36 @@ def test_missing_workspace_is_an_error():
     torch.cuda.synchronize()
     assert out[0].tolist() == list(range(512))
     note("errors ok")
+
+
+# ---------------------------------------------------------------------------
+# Row offsets (topk_ragged_offsets): indices into a flat ragged layout
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["decode", "mtp", "long_k2048", "prefill"])
+def test_row_offsets_flat_layout(name):
+    from oracle import topk_ragged_offsets_oracle
+    w = workloads.make_workload(name)
+    n = np.clip(w.flat_lengths.astype(np.int64), 0, w.row_stride)
+    starts = np.concatenate([[0], np.cumsum(n)[:-1]])
+    assert starts[-1] + n[-1] <= 2**31 - 1
+    exp = topk_ragged_offsets_oracle(w.scores, w.lengths, w.K, starts)
+    paths = [{}, dict(force_path=1)]
+    if name != "prefill":
+        paths += [dict(force_path=2), dict(force_path=1, split_rows=w.num_rows, split_g=4)]
+    for ov in paths:
+        got, _ = run_gpu(w.scores, w.lengths, w.K, tag=f"{name} offsets {ov}", row_offsets=starts, **ov)
+        assert_same(got, exp, f"{name} offsets {ov}")
+
+
+def test_row_offsets_near_int32_limit():
+    from oracle import topk_ragged_offsets_oracle
+    rng = np.random.default_rng(77)
+    lens = [0, 1, 100, 2048, 2049, 40000, 65536, 20000]
+    s, L = workloads.random_rows(77, len(lens), 65536, lens, dist="levels", levels=300)
+    offs = (2**31 - 1 - np.asarray(lens, dtype=np.int64)).clip(0, None) - rng.integers(0, 1000, len(lens))
+    for K in (64, 2048):
+        exp = topk_ragged_offsets_oracle(s, L, K, offs)
+        for ov in ({}, dict(force_path=2), dict(force_path=1, max_grid=3)):
+            got, _ = run_gpu(s, L, K, tag=f"offsets near 2^31 K={K} {ov}", row_offsets=offs, **ov)
+            assert_same(got, exp, f"offsets near 2^31 K={K} {ov}")

@@ -192,3 +192,48 @@ def test_thread_count_does_not_change_result():
     a = topk_ragged_oracle(w.scores, w.lengths, w.K, threads=1)
     b = topk_ragged_oracle(w.scores, w.lengths, w.K, threads=7)
     assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# Row offsets (the reading of the pages' "RaggedTransform")
+# ---------------------------------------------------------------------------
+
+def test_offsets_index_a_flat_ragged_layout():
+    """Lay the rows' valid prefixes end to end and give each row its start:
+    the shifted indices must address that flat array, fall inside the row's
+    own stretch in ascending order, and gather exactly the row's best values
+    (checked against numpy's stable argsort of the row, not the oracle)."""
+    from oracle import topk_ragged_offsets_oracle
+    rng = np.random.default_rng(7)
+    rows, stride = 40, 3000
+    lens = rng.integers(0, stride + 1, size=rows).astype(np.int32)
+    lens[:3] = [0, 1, 5]
+    s = rng.integers(-20, 20, size=(rows, stride)).astype(np.float32)  # plenty of ties
+    flat = np.concatenate([s[r, :lens[r]] for r in range(rows)])
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int32)
+    for K in (1, 7, 64, 3000):
+        out = topk_ragged_offsets_oracle(s, lens, K, starts)
+        for r in range(rows):
+            n = int(lens[r])
+            m = min(K, n)
+            assert np.all(out[r, m:] == -1)
+            pos = out[r, :m]
+            assert np.all(pos >= starts[r]) and np.all(pos < starts[r] + n)
+            assert np.all(np.diff(pos) > 0)
+            exp = argsort_row(s[r], n, K)[:m] + starts[r]
+            assert np.array_equal(pos, exp), (K, r)
+            assert np.array_equal(np.sort(flat[pos]), np.sort(s[r, exp - starts[r]]))
+
+
+def test_offsets_zero_and_range():
+    from oracle import topk_ragged_offsets_oracle
+    s, L = workloads.random_rows(8, 6, 500, [0, 1, 499, 500, 250, 17], dist="normal")
+    base = topk_ragged_oracle(s, L, 32)
+    assert np.array_equal(topk_ragged_offsets_oracle(s, L, 32, np.zeros(6, np.int32)), base)
+    big = np.full(6, 2**31 - 500, dtype=np.int64)
+    out = topk_ragged_offsets_oracle(s, L, 32, big)
+    assert np.array_equal(out, np.where(base >= 0, base + big[:, None], -1))
+    with pytest.raises(ValueError):
+        topk_ragged_offsets_oracle(s, L, 32, np.full(6, 2**31 - 10, dtype=np.int64))
+    with pytest.raises(ValueError):
+        topk_ragged_offsets_oracle(s, L, 32, np.full(6, -1, dtype=np.int64))
