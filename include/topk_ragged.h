@@ -107,6 +107,24 @@ int topk_ragged_offsets(const float* scores, int64_t row_stride, const int32_t* 
                         const int32_t* row_offsets, int32_t num_rows, int32_t next_n, int32_t K,
                         int32_t* out_idx, void* workspace, hipStream_t stream);
 
+/*
+ * topk_ragged_values -- the selection (with or without row offsets) plus the
+ * chosen scores.  Not on the pages, which return indices only.
+ *
+ *   row_offsets  NULL, or as for topk_ragged_offsets.
+ *   out_val      float device array [num_rows, K], 4-byte aligned:
+ *                out_val[r, i] = the fp32 score at out_idx[r, i] (its exact
+ *                bits, -0.0 included) for i < min(K, n_r), -inf after that.
+ *
+ * The values are gathered by a second kernel on the same stream, after the
+ * selection; both launches can be captured in one graph.  Other arguments and
+ * errors as for topk_ragged; a null out_val with num_rows > 0 is
+ * TOPK_EINVAL.
+ */
+int topk_ragged_values(const float* scores, int64_t row_stride, const int32_t* lengths,
+                       const int32_t* row_offsets, int32_t num_rows, int32_t next_n, int32_t K,
+                       int32_t* out_idx, float* out_val, void* workspace, hipStream_t stream);
+
 /* Bytes of workspace topk_ragged needs for this shape on the stream's device.
  * *bytes = 0 means no workspace is used: one workgroup per row and no more
  * rows than resident workgroups.  With more rows than that, a 256-byte
@@ -208,6 +226,10 @@ int topk_ragged_offsets_ex(const float* scores, int64_t row_stride, const int32_
                            const int32_t* row_offsets, int32_t num_rows, int32_t next_n, int32_t K,
                            int32_t* out_idx, void* workspace, hipStream_t stream,
                            const topk_overrides* ov);
+int topk_ragged_values_ex(const float* scores, int64_t row_stride, const int32_t* lengths,
+                          const int32_t* row_offsets, int32_t num_rows, int32_t next_n, int32_t K,
+                          int32_t* out_idx, float* out_val, void* workspace, hipStream_t stream,
+                          const topk_overrides* ov);
 
 /* Error bits a kernel left in the workspace header (synchronises stream):
  * bit 0: a cooperative wait hit its spin limit; bit 1: a threshold search

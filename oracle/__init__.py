@@ -12,4 +12,9 @@ order or the padding; the readings used are stated in ``oracle_topk.cpp`` and
 ``topk_ragged_oracle`` below.
 """
 
-from .oracle import load_library, topk_ragged_offsets_oracle, topk_ragged_oracle  # noqa: F401
+from .oracle import (  # noqa: F401
+    load_library,
+    topk_ragged_offsets_oracle,
+    topk_ragged_oracle,
+    topk_ragged_values_oracle,
+)

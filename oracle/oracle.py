@@ -88,3 +88,21 @@ def topk_ragged_offsets_oracle(scores: np.ndarray, lengths: np.ndarray, K: int, 
     if chosen.any() and (shifted[chosen].min() < 0 or shifted[chosen].max() > 2**31 - 1):
         raise ValueError("row_offsets[r] + index leaves [0, 2^31 - 1]: outside the op's contract")
     return shifted.astype(np.int32)
+
+
+def topk_ragged_values_oracle(scores: np.ndarray, lengths: np.ndarray, K: int, row_offsets=None,
+                              next_n: int | None = None, threads: int = 0):
+    """(indices, values): the selection (shifted by row_offsets when given)
+    and, at each chosen position, the score itself (its exact fp32 bits);
+    -inf where the index is -1.  Not on the pages: a convenience output."""
+    scores = np.ascontiguousarray(scores, dtype=np.float32)
+    if row_offsets is None:
+        idx = topk_ragged_oracle(scores, lengths, K, next_n=next_n, threads=threads)
+        off = np.zeros(scores.shape[0], dtype=np.int64)
+    else:
+        idx = topk_ragged_offsets_oracle(scores, lengths, K, row_offsets, next_n=next_n, threads=threads)
+        off = np.asarray(row_offsets, dtype=np.int64).reshape(-1)
+    vals = np.full(idx.shape, -np.inf, dtype=np.float32)
+    rows, cols = np.nonzero(idx >= 0)
+    vals[rows, cols] = scores[rows, idx[rows, cols].astype(np.int64) - off[rows]]
+    return idx, vals

@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     query_plan,
     read_reference,
     topk_ragged,
+    topk_ragged_values,
     workspace_init,
     workspace_size,
     workspace_status,

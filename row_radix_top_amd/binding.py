@@ -26,7 +26,7 @@ EXPORTED = (
     "topk_ragged_last_error", "topk_ragged_plan", "topk_ragged_query_plan",
     "topk_ragged_workspace_size_ex", "topk_ragged_ex", "topk_ragged_workspace_status",
     "topk_ragged_debug_keys", "topk_ragged_version", "topk_ragged_read_reference",
-    "topk_ragged_offsets", "topk_ragged_offsets_ex",
+    "topk_ragged_offsets", "topk_ragged_offsets_ex", "topk_ragged_values", "topk_ragged_values_ex",
 )
 
 
@@ -111,6 +111,9 @@ def load() -> ctypes.CDLL:
         lib.topk_ragged_offsets.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp, vp]
         lib.topk_ragged_offsets_ex.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp, vp,
                                                ctypes.POINTER(Overrides)]
+        lib.topk_ragged_values.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp, vp, vp]
+        lib.topk_ragged_values_ex.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp, vp, vp,
+                                              ctypes.POINTER(Overrides)]
         for name in EXPORTED:
             getattr(lib, name).restype = ctypes.c_int if name != "topk_ragged_last_error" else ctypes.c_char_p
         _lib = lib
@@ -227,6 +230,41 @@ def _validate(scores, lengths, out, K):
         if (not out.is_cuda or out.dtype != torch.int32 or not out.is_contiguous()
                 or tuple(out.shape) != (scores.shape[0], K)):
             raise ValueError("out must be a contiguous int32 CUDA tensor of shape [num_rows, K]")
+
+
+def topk_ragged_values(scores, lengths, K: int, *, out=None, out_values=None, workspace=None,
+                       next_n: int | None = None, stream=None, row_offsets=None, **overrides):
+    """topk_ragged plus the chosen scores: returns (indices, values), values
+    float32 [num_rows, K] with the exact score bits and -inf in the padding."""
+    import torch
+    if next_n is None:
+        next_n = int(lengths.shape[1]) if lengths.dim() == 2 else 1
+    _validate(scores, lengths, out, K)
+    num_rows = scores.shape[0]
+    if out is None:
+        out = torch.empty((num_rows, K), dtype=torch.int32, device=scores.device)
+    if out_values is None:
+        out_values = torch.empty((num_rows, K), dtype=torch.float32, device=scores.device)
+    if (out_values.dtype != torch.float32 or not out_values.is_cuda or not out_values.is_contiguous()
+            or tuple(out_values.shape) != (num_rows, K)):
+        raise ValueError("out_values must be a contiguous float32 CUDA tensor of shape [num_rows, K]")
+    ro = None
+    if row_offsets is not None:
+        if (row_offsets.dtype != torch.int32 or not row_offsets.is_cuda or row_offsets.numel() != num_rows
+                or not row_offsets.is_contiguous()):
+            raise ValueError("row_offsets must be a contiguous int32 CUDA tensor with one entry per row")
+        ro = row_offsets.data_ptr()
+    ov = Overrides.make(**overrides)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    lib = load()
+    args = (scores.data_ptr(), scores.stride(0), lengths.data_ptr(), ro, num_rows, next_n, K, out.data_ptr(),
+            out_values.data_ptr(), ws_ptr, _stream_ptr(stream, scores.device))
+    if ov is None:
+        rc = lib.topk_ragged_values(*args)
+    else:
+        rc = lib.topk_ragged_values_ex(*args, ctypes.byref(ov))
+    _check(rc, "topk_ragged_values")
+    return out, out_values
 
 
 def topk_ragged(scores, lengths, K: int, *, out=None, workspace=None, next_n: int | None = None,

@@ -484,6 +484,31 @@ int topk_ragged_offsets(const float* scores, int64_t row_stride, const int32_t* 
                 nullptr);
 }
 
+int topk_ragged_values_ex(const float* scores, int64_t row_stride, const int32_t* lengths,
+                          const int32_t* row_offsets, int32_t num_rows, int32_t next_n, int32_t K,
+                          int32_t* out_idx, float* out_val, void* workspace, hipStream_t stream,
+                          const topk_overrides* ov) {
+  if (num_rows > 0 && out_val == nullptr) return fail(TOPK_EINVAL, "null out_val");
+  if (reinterpret_cast<uintptr_t>(out_val) % 4 != 0) return fail(TOPK_EINVAL, "out_val must be 4-byte aligned");
+  int rc = launch(scores, row_stride, lengths, row_offsets, num_rows, next_n, K, out_idx, workspace, stream, ov);
+  if (rc != TOPK_OK || num_rows == 0) return rc;
+  // The values, from the indices just written (same stream, so in order).
+  const int64_t total = (int64_t)num_rows * K;
+  const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 4096);
+  void* args[] = {&scores, &row_stride, &out_idx, &row_offsets, &num_rows, &K, &out_val};
+  hipError_t e = hipLaunchKernel(rrt::values_kernel_ptr(), dim3(blocks), dim3(256), args, 0, stream);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return fail(TOPK_ELAUNCH, std::string("values kernel: ") + hipGetErrorString(e));
+  return TOPK_OK;
+}
+
+int topk_ragged_values(const float* scores, int64_t row_stride, const int32_t* lengths, const int32_t* row_offsets,
+                       int32_t num_rows, int32_t next_n, int32_t K, int32_t* out_idx, float* out_val,
+                       void* workspace, hipStream_t stream) {
+  return topk_ragged_values_ex(scores, row_stride, lengths, row_offsets, num_rows, next_n, K, out_idx, out_val,
+                               workspace, stream, nullptr);
+}
+
 int topk_ragged_offsets_ex(const float* scores, int64_t row_stride, const int32_t* lengths,
                            const int32_t* row_offsets, int32_t num_rows, int32_t next_n, int32_t K,
                            int32_t* out_idx, void* workspace, hipStream_t stream, const topk_overrides* ov) {

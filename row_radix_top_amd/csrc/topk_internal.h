@@ -117,6 +117,7 @@ struct KernelParams {
 const void* kernel_ptr(int path, int vec, bool idx16);
 const void* zero_kernel_ptr();
 const void* keys_kernel_ptr();
+const void* values_kernel_ptr();
 int lds_bytes_of(bool idx16);
 
 }  // namespace rrt

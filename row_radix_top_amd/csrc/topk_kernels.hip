@@ -1919,6 +1919,27 @@ __global__ void zero_kernel(uint32_t* p, uint64_t words) {
   for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += stride) p[i] = 0u;
 }
 
+// Values of the chosen entries: vals[r, i] = the score bits at out[r, i] (less
+// the row's offset), -inf where out[r, i] = -1.  Runs after the selection on
+// the same stream.  A column outside [0, row_stride) -- impossible for an
+// output of the selection -- yields NaN instead of a read.
+__global__ void values_kernel(const float* __restrict__ scores, int64_t row_stride, const int32_t* __restrict__ out,
+                              const int32_t* __restrict__ row_offsets, int32_t num_rows, int32_t K,
+                              float* __restrict__ vals) {
+  const int64_t total = (int64_t)num_rows * K;
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += step) {
+    const int64_t r = e / K;
+    const int32_t ix = out[e];
+    float v = -__builtin_huge_valf();
+    if (ix >= 0) {
+      const int64_t col = (int64_t)(uint32_t)ix - (row_offsets != nullptr ? (int64_t)(uint32_t)row_offsets[r] : 0);
+      v = (col >= 0 && col < row_stride) ? scores[r * row_stride + col] : __builtin_nanf("");
+    }
+    vals[e] = v;
+  }
+}
+
 __global__ void keys_kernel(const uint32_t* bits, uint32_t* keys, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) keys[i] = ord_key(bits[i]);
@@ -1956,5 +1977,6 @@ int lds_bytes_of(bool idx16) { return idx16 ? (int)sizeof(Smem<true>) : (int)siz
 
 const void* zero_kernel_ptr() { return reinterpret_cast<const void*>(&zero_kernel); }
 const void* keys_kernel_ptr() { return reinterpret_cast<const void*>(&keys_kernel); }
+const void* values_kernel_ptr() { return reinterpret_cast<const void*>(&values_kernel); }
 
 }  // namespace rrt

@@ -365,3 +365,30 @@ def test_row_offsets_near_int32_limit():
         for ov in ({}, dict(force_path=2), dict(force_path=1, max_grid=3)):
             got, _ = run_gpu(s, L, K, tag=f"offsets near 2^31 K={K} {ov}", row_offsets=offs, **ov)
             assert_same(got, exp, f"offsets near 2^31 K={K} {ov}")
+
+
+# ---------------------------------------------------------------------------
+# Values output (topk_ragged_values): exact score bits beside the indices
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["decode", "long_k1024", "prefill"])
+def test_values_output(name):
+    import torch
+    from oracle import topk_ragged_values_oracle
+    dev = torch.device("cuda:0")
+    w = workloads.make_workload(name)
+    if name == "decode":
+        w.scores[1, :40] = np.float32(-0.0)   # chosen signed zeros keep their sign
+        w.scores[1, 40:] = np.float32(-1.0)
+    s = torch.from_numpy(w.scores).to(dev)
+    L = torch.from_numpy(w.flat_lengths).to(dev)
+    n = np.clip(w.flat_lengths.astype(np.int64), 0, w.row_stride)
+    starts = np.concatenate([[0], np.cumsum(n)[:-1]])
+    for offs in (None, starts):
+        exp_i, exp_v = topk_ragged_values_oracle(w.scores, w.lengths, w.K, offs)
+        ro = None if offs is None else torch.from_numpy(offs.astype(np.int32)).to(dev)
+        ws = rrt.new_workspace(rrt.workspace_size(w.num_rows, w.row_stride, w.K, scores=s), dev)
+        gi, gv = rrt.topk_ragged_values(s, L, w.K, workspace=ws, row_offsets=ro)
+        torch.cuda.synchronize()
+        assert_same(gi.cpu().numpy(), exp_i, f"{name} values idx offs={offs is not None}")
+        assert np.array_equal(gv.cpu().numpy().view(np.uint32), exp_v.view(np.uint32)), name

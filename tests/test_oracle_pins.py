@@ -237,3 +237,30 @@ def test_offsets_zero_and_range():
         topk_ragged_offsets_oracle(s, L, 32, np.full(6, 2**31 - 10, dtype=np.int64))
     with pytest.raises(ValueError):
         topk_ragged_offsets_oracle(s, L, 32, np.full(6, -1, dtype=np.int64))
+
+
+def test_values_are_the_best_scores_bit_for_bit():
+    """The values output: each row's chosen scores, in index order, are its
+    min(K, n) largest (numpy's sort of the prefix, not the oracle), the bits
+    are the input's (a chosen -0.0 stays -0.0), the padding is -inf."""
+    from oracle import topk_ragged_values_oracle
+    rng = np.random.default_rng(11)
+    rows, stride = 30, 700
+    lens = rng.integers(0, stride + 1, size=rows).astype(np.int32)
+    s = rng.standard_normal((rows, stride)).astype(np.float32)
+    s[0, :5] = [-0.0, 0.0, -0.0, -1.0, -2.0]
+    lens[0] = 5
+    for K in (1, 3, 50, 700):
+        idx, vals = topk_ragged_values_oracle(s, lens, K)
+        for r in range(rows):
+            n = int(lens[r])
+            m = min(K, n)
+            assert np.all(np.isneginf(vals[r, m:]))
+            assert np.array_equal(vals[r, :m].view(np.uint32), s[r, idx[r, :m]].view(np.uint32))
+            assert np.array_equal(np.sort(vals[r, :m]), np.sort(np.sort(s[r, :n])[::-1][:m]))
+    idx, vals = topk_ragged_values_oracle(s, lens, 3)
+    assert list(idx[0]) == [0, 1, 2]
+    assert list(vals[0].view(np.uint32)) == [0x80000000, 0, 0x80000000]
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    idx2, vals2 = topk_ragged_values_oracle(s, lens, 50, starts)
+    assert np.array_equal(vals2.view(np.uint32), topk_ragged_values_oracle(s, lens, 50)[1].view(np.uint32))
