@@ -125,6 +125,35 @@ int topk_ragged_values(const float* scores, int64_t row_stride, const int32_t* l
                        const int32_t* row_offsets, int32_t num_rows, int32_t next_n, int32_t K,
                        int32_t* out_idx, float* out_val, void* workspace, hipStream_t stream);
 
+/*
+ * topk_ragged_strided -- rows with any column stride (the pages' op takes
+ * both logits strides: PR #54110 page, the top_k_per_row_decode call).
+ *
+ *   scores       element (r, c) at scores + r * row_stride + c * col_stride;
+ *                row_stride >= 0, col_stride >= 1 (elements).
+ *   num_cols     columns of the matrix (>= 1): lengths are clamped to
+ *                [0, num_cols], since row_stride no longer bounds a row.
+ *   row_offsets  NULL or as for topk_ragged_offsets; out_val NULL or as for
+ *                topk_ragged_values.
+ *   workspace    at least topk_ragged_strided_workspace_size() bytes,
+ *                256-byte aligned, zeroed once by topk_ragged_workspace_init.
+ *                Its first part is the ordinary workspace of
+ *                (num_rows, num_cols, K), returned to zero by every launch;
+ *                after it, each row's valid prefix is packed contiguously
+ *                (contents undefined between launches).
+ *
+ * Each row's valid prefix is first copied into the workspace (nothing past a
+ * length is read), then selected as contiguous rows of stride num_cols.  A
+ * slow path for unusual layouts: it reads the valid scores once strided and
+ * once packed.  Asynchronous, graph-capturable; errors as for topk_ragged.
+ */
+int topk_ragged_strided_workspace_size(int32_t num_rows, int64_t num_cols, int32_t K,
+                                       hipStream_t stream, size_t* bytes);
+int topk_ragged_strided(const float* scores, int64_t row_stride, int64_t col_stride, int64_t num_cols,
+                        const int32_t* lengths, const int32_t* row_offsets, int32_t num_rows,
+                        int32_t next_n, int32_t K, int32_t* out_idx, float* out_val,
+                        void* workspace, hipStream_t stream);
+
 /* Bytes of workspace topk_ragged needs for this shape on the stream's device.
  * *bytes = 0 means no workspace is used: one workgroup per row and no more
  * rows than resident workgroups.  With more rows than that, a 256-byte

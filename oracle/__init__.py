@@ -16,5 +16,6 @@ from .oracle import (  # noqa: F401
     load_library,
     topk_ragged_offsets_oracle,
     topk_ragged_oracle,
+    topk_ragged_strided_oracle,
     topk_ragged_values_oracle,
 )

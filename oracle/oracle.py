@@ -106,3 +106,21 @@ def topk_ragged_values_oracle(scores: np.ndarray, lengths: np.ndarray, K: int, r
     rows, cols = np.nonzero(idx >= 0)
     vals[rows, cols] = scores[rows, idx[rows, cols].astype(np.int64) - off[rows]]
     return idx, vals
+
+
+def topk_ragged_strided_oracle(flat: np.ndarray, row_stride: int, col_stride: int, num_cols: int,
+                               num_rows: int, lengths: np.ndarray, K: int, next_n: int | None = None,
+                               threads: int = 0) -> np.ndarray:
+    """The selection over rows with a column stride (the PR #54110 page
+    passes both logits strides to the per-row top-K): entry (r, c) is
+    flat[r * row_stride + c * col_stride], lengths are clamped to
+    [0, num_cols].  Only valid entries are read; the rest of each dense row
+    is NaN, which the selection never reads."""
+    flat = np.asarray(flat, dtype=np.float32).reshape(-1)
+    L = np.asarray(lengths).reshape(-1).astype(np.int64)
+    dense = np.full((num_rows, num_cols), np.nan, dtype=np.float32)
+    for r in range(num_rows):
+        n = int(min(max(L[r], 0), num_cols))
+        if n:
+            dense[r, :n] = flat[r * row_stride + np.arange(n, dtype=np.int64) * col_stride]
+    return topk_ragged_oracle(dense, np.asarray(lengths), K, next_n=next_n, threads=threads)

@@ -19,7 +19,9 @@ from .binding import (  # noqa: F401
     plan_for_props,
     query_plan,
     read_reference,
+    strided_workspace_size,
     topk_ragged,
+    topk_ragged_strided,
     topk_ragged_values,
     workspace_init,
     workspace_size,

@@ -27,6 +27,7 @@ EXPORTED = (
     "topk_ragged_workspace_size_ex", "topk_ragged_ex", "topk_ragged_workspace_status",
     "topk_ragged_debug_keys", "topk_ragged_version", "topk_ragged_read_reference",
     "topk_ragged_offsets", "topk_ragged_offsets_ex", "topk_ragged_values", "topk_ragged_values_ex",
+    "topk_ragged_strided", "topk_ragged_strided_workspace_size",
 )
 
 
@@ -112,6 +113,8 @@ def load() -> ctypes.CDLL:
         lib.topk_ragged_offsets_ex.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp, vp,
                                                ctypes.POINTER(Overrides)]
         lib.topk_ragged_values.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp, vp, vp]
+        lib.topk_ragged_strided.argtypes = [vp, i64, i64, i64, vp, vp, i32, i32, i32, vp, vp, vp, vp]
+        lib.topk_ragged_strided_workspace_size.argtypes = [i32, i64, i32, vp, ctypes.POINTER(sz)]
         lib.topk_ragged_values_ex.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp, vp, vp,
                                               ctypes.POINTER(Overrides)]
         for name in EXPORTED:
@@ -230,6 +233,43 @@ def _validate(scores, lengths, out, K):
         if (not out.is_cuda or out.dtype != torch.int32 or not out.is_contiguous()
                 or tuple(out.shape) != (scores.shape[0], K)):
             raise ValueError("out must be a contiguous int32 CUDA tensor of shape [num_rows, K]")
+
+
+def strided_workspace_size(num_rows: int, num_cols: int, K: int, device=None) -> int:
+    """Workspace bytes for topk_ragged_strided on (num_rows, num_cols, K)."""
+    n = ctypes.c_size_t(0)
+    rc = load().topk_ragged_strided_workspace_size(num_rows, num_cols, K, _stream_ptr(None, device),
+                                                   ctypes.byref(n))
+    _check(rc, "topk_ragged_strided_workspace_size")
+    return int(n.value)
+
+
+def topk_ragged_strided(scores, lengths, K: int, *, workspace, out=None, out_values=None, row_offsets=None,
+                        next_n: int | None = None, stream=None):
+    """topk_ragged for a float32 CUDA view with any strides ([num_rows,
+    num_cols], e.g. a transpose): each row's valid prefix is packed into the
+    workspace first.  Returns the indices, or (indices, values) when
+    out_values is given (a float32 [num_rows, K] tensor)."""
+    import torch
+    if scores.dtype != torch.float32 or not scores.is_cuda or scores.dim() != 2:
+        raise ValueError("scores must be a 2-D float32 CUDA tensor")
+    if lengths.dtype != torch.int32 or not lengths.is_cuda or not lengths.is_contiguous():
+        raise ValueError("lengths must be a contiguous int32 CUDA tensor")
+    if next_n is None:
+        next_n = int(lengths.shape[1]) if lengths.dim() == 2 else 1
+    num_rows, num_cols = scores.shape
+    if lengths.numel() != num_rows:
+        raise ValueError("one length per row")
+    if out is None:
+        out = torch.empty((num_rows, K), dtype=torch.int32, device=scores.device)
+    ro = None if row_offsets is None else row_offsets.data_ptr()
+    vp_ = None if out_values is None else out_values.data_ptr()
+    rc = load().topk_ragged_strided(scores.data_ptr(), scores.stride(0), scores.stride(1), num_cols,
+                                    lengths.data_ptr(), ro, num_rows, next_n, K, out.data_ptr(), vp_,
+                                    workspace.data_ptr() if workspace is not None else None,
+                                    _stream_ptr(stream, scores.device))
+    _check(rc, "topk_ragged_strided")
+    return out if out_values is None else (out, out_values)
 
 
 def topk_ragged_values(scores, lengths, K: int, *, out=None, out_values=None, workspace=None,

@@ -484,6 +484,51 @@ int topk_ragged_offsets(const float* scores, int64_t row_stride, const int32_t* 
                 nullptr);
 }
 
+int topk_ragged_strided_workspace_size(int32_t num_rows, int64_t num_cols, int32_t K, hipStream_t stream,
+                                       size_t* bytes) {
+  if (bytes == nullptr) return fail(TOPK_EINVAL, "null bytes");
+  if (num_cols < 1 || num_cols > INT32_MAX) return fail(TOPK_EINVAL, "num_cols must be in [1, 2^31 - 1]");
+  size_t plan_bytes = 0;
+  const int rc = topk_ragged_workspace_size(num_rows, num_cols, K, stream, &plan_bytes);
+  if (rc != TOPK_OK) return rc;
+  *bytes = num_rows == 0 ? 0 : rrt::round_up(plan_bytes, 256) + 4ull * (uint64_t)num_rows * (uint64_t)num_cols;
+  return TOPK_OK;
+}
+
+int topk_ragged_strided(const float* scores, int64_t row_stride, int64_t col_stride, int64_t num_cols,
+                        const int32_t* lengths, const int32_t* row_offsets, int32_t num_rows, int32_t next_n,
+                        int32_t K, int32_t* out_idx, float* out_val, void* workspace, hipStream_t stream) {
+  if (num_rows < 0) return fail(TOPK_EINVAL, "num_rows must be >= 0");
+  if (col_stride < 1) return fail(TOPK_EINVAL, "col_stride must be >= 1");
+  if (row_stride < 0) return fail(TOPK_EINVAL, "row_stride must be >= 0");
+  size_t need = 0;
+  int rc = topk_ragged_strided_workspace_size(num_rows, num_cols, K, stream, &need);
+  if (rc != TOPK_OK) return rc;
+  if (num_rows == 0) return TOPK_OK;
+  if (scores == nullptr || lengths == nullptr) return fail(TOPK_EINVAL, "null scores or lengths");
+  if (workspace == nullptr) return fail(TOPK_EWORKSPACE, "strided rows need a workspace of " + std::to_string(need) +
+                                                             " bytes (topk_ragged_strided_workspace_size)");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(TOPK_EINVAL, "workspace must be 256-byte aligned");
+  if (reinterpret_cast<uintptr_t>(scores) % 4 != 0 || reinterpret_cast<uintptr_t>(lengths) % 4 != 0)
+    return fail(TOPK_EINVAL, "scores and lengths must be 4-byte aligned");
+  size_t plan_bytes = 0;
+  rc = topk_ragged_workspace_size(num_rows, num_cols, K, stream, &plan_bytes);
+  if (rc != TOPK_OK) return rc;
+  float* packed = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + rrt::round_up(plan_bytes, 256));
+  {
+    const unsigned blocks = (unsigned)std::min<int64_t>(num_rows, 4096);
+    void* args[] = {&scores, &row_stride, &col_stride, &num_cols, &lengths, &num_rows, &packed};
+    hipError_t e = hipLaunchKernel(rrt::pack_kernel_ptr(), dim3(blocks), dim3(256), args, 0, stream);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) return fail(TOPK_ELAUNCH, std::string("pack kernel: ") + hipGetErrorString(e));
+  }
+  void* plan_ws = plan_bytes > 0 ? workspace : nullptr;
+  if (out_val != nullptr)
+    return topk_ragged_values_ex(packed, num_cols, lengths, row_offsets, num_rows, next_n, K, out_idx, out_val,
+                                 plan_ws, stream, nullptr);
+  return launch(packed, num_cols, lengths, row_offsets, num_rows, next_n, K, out_idx, plan_ws, stream, nullptr);
+}
+
 int topk_ragged_values_ex(const float* scores, int64_t row_stride, const int32_t* lengths,
                           const int32_t* row_offsets, int32_t num_rows, int32_t next_n, int32_t K,
                           int32_t* out_idx, float* out_val, void* workspace, hipStream_t stream,

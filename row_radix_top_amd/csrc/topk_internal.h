@@ -118,6 +118,7 @@ const void* kernel_ptr(int path, int vec, bool idx16);
 const void* zero_kernel_ptr();
 const void* keys_kernel_ptr();
 const void* values_kernel_ptr();
+const void* pack_kernel_ptr();
 int lds_bytes_of(bool idx16);
 
 }  // namespace rrt

@@ -1940,6 +1940,22 @@ __global__ void values_kernel(const float* __restrict__ scores, int64_t row_stri
   }
 }
 
+// Packs rows with a column stride into contiguous rows of num_cols:
+// packed[r * num_cols + c] = scores[r * row_stride + c * col_stride] for
+// c < clamp(lengths[r], 0, num_cols).  Nothing at or past a length is read
+// or written.
+__global__ void pack_kernel(const float* __restrict__ scores, int64_t row_stride, int64_t col_stride,
+                            int64_t num_cols, const int32_t* __restrict__ lengths, int32_t num_rows,
+                            float* __restrict__ packed) {
+  for (int64_t r = blockIdx.x; r < num_rows; r += gridDim.x) {
+    int64_t n = lengths[r];
+    n = n < 0 ? 0 : (n > num_cols ? num_cols : n);
+    const float* src = scores + r * row_stride;
+    float* dst = packed + r * num_cols;
+    for (int64_t c = threadIdx.x; c < n; c += blockDim.x) dst[c] = src[c * col_stride];
+  }
+}
+
 __global__ void keys_kernel(const uint32_t* bits, uint32_t* keys, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) keys[i] = ord_key(bits[i]);
@@ -1978,5 +1994,6 @@ int lds_bytes_of(bool idx16) { return idx16 ? (int)sizeof(Smem<true>) : (int)siz
 const void* zero_kernel_ptr() { return reinterpret_cast<const void*>(&zero_kernel); }
 const void* keys_kernel_ptr() { return reinterpret_cast<const void*>(&keys_kernel); }
 const void* values_kernel_ptr() { return reinterpret_cast<const void*>(&values_kernel); }
+const void* pack_kernel_ptr() { return reinterpret_cast<const void*>(&pack_kernel); }
 
 }  // namespace rrt

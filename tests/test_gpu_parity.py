@@ -392,3 +392,49 @@ def test_values_output(name):
         torch.cuda.synchronize()
         assert_same(gi.cpu().numpy(), exp_i, f"{name} values idx offs={offs is not None}")
         assert np.array_equal(gv.cpu().numpy().view(np.uint32), exp_v.view(np.uint32)), name
+
+
+# ---------------------------------------------------------------------------
+# Column strides (topk_ragged_strided): rows packed into the workspace first
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("layout", ["transposed", "every_other", "stride3"])
+def test_strided_rows(layout):
+    import torch
+    from oracle import topk_ragged_strided_oracle, topk_ragged_values_oracle
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng({"transposed": 1, "every_other": 2, "stride3": 3}[layout])
+    R, N = 48, 40000
+    if layout == "transposed":
+        flat = rng.standard_normal(N * R).astype(np.float32)
+        rs, cs = 1, R
+    elif layout == "every_other":
+        rs, cs = 2 * N + 5, 2
+        flat = rng.standard_normal(R * rs).astype(np.float32)
+    else:
+        rs, cs = 3 * N + 7, 3
+        flat = rng.standard_normal(R * rs).astype(np.float32)
+    lens = rng.integers(0, N + 1, size=R).astype(np.int32)
+    lens[:6] = [0, 1, 2047, 2048, 2049, N]
+    base = torch.from_numpy(flat).to(dev)
+    view = torch.as_strided(base, (R, N), (rs, cs))
+    L = torch.from_numpy(lens).to(dev)
+    for K in (100, 2048):
+        exp = topk_ragged_strided_oracle(flat, rs, cs, N, R, lens, K)
+        nbytes = rrt.strided_workspace_size(R, N, K, device=dev)
+        ws = rrt.new_workspace(nbytes, dev)
+        got = rrt.topk_ragged_strided(view, L, K, workspace=ws)
+        torch.cuda.synchronize()
+        assert_same(got.cpu().numpy(), exp, f"{layout} K={K}")
+        plan_bytes = rrt.workspace_size(R, N, K, device=dev)
+        assert int(ws[:plan_bytes // ws.element_size()].count_nonzero().item()) == 0
+        # With row offsets and values.
+        dense = np.ascontiguousarray(view.cpu().numpy())
+        starts = np.concatenate([[0], np.cumsum(lens.astype(np.int64))[:-1]])
+        ei, ev = topk_ragged_values_oracle(dense, lens, K, starts)
+        vals = torch.empty((R, K), dtype=torch.float32, device=dev)
+        gi, gv = rrt.topk_ragged_strided(view, L, K, workspace=ws, out_values=vals,
+                                         row_offsets=torch.from_numpy(starts.astype(np.int32)).to(dev))
+        torch.cuda.synchronize()
+        assert_same(gi.cpu().numpy(), ei, f"{layout} K={K} offsets")
+        assert np.array_equal(gv.cpu().numpy().view(np.uint32), ev.view(np.uint32))

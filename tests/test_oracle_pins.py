@@ -264,3 +264,25 @@ def test_values_are_the_best_scores_bit_for_bit():
     starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
     idx2, vals2 = topk_ragged_values_oracle(s, lens, 50, starts)
     assert np.array_equal(vals2.view(np.uint32), topk_ragged_values_oracle(s, lens, 50)[1].view(np.uint32))
+
+
+def test_strided_rows_match_dense_copies():
+    """Rows with a column stride: the transposed layout must select exactly
+    what the oracle selects on numpy's transposed copy, every other column of
+    a wider matrix what it selects on the sliced copy, and a unit column
+    stride what it selects on the plain rows."""
+    from oracle import topk_ragged_strided_oracle
+    rng = np.random.default_rng(21)
+    N, R = 900, 12
+    base = rng.integers(-30, 30, size=(N, R)).astype(np.float32)   # columns become rows
+    lens = rng.integers(0, N + 1, size=R).astype(np.int32)
+    for K in (1, 40, 900):
+        got = topk_ragged_strided_oracle(base, 1, R, N, R, lens, K)
+        assert np.array_equal(got, topk_ragged_oracle(np.ascontiguousarray(base.T), lens, K))
+        for r in range(R):
+            check_invariants(np.ascontiguousarray(base.T)[r], lens[r], K, got[r])
+    wide = rng.standard_normal((R, 2 * N + 3)).astype(np.float32)
+    got = topk_ragged_strided_oracle(wide, 2 * N + 3, 2, N, R, lens, 64)
+    assert np.array_equal(got, topk_ragged_oracle(np.ascontiguousarray(wide[:, :2 * N:2]), lens, 64))
+    got = topk_ragged_strided_oracle(wide, 2 * N + 3, 1, 2 * N + 3, R, lens, 64)
+    assert np.array_equal(got, topk_ragged_oracle(wide, lens, 64))
