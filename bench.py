@@ -277,6 +277,39 @@ def decode_latency(launches: int = 400):
     return res
 
 
+def extensions(w, scores, L, launches: int = 20):
+    """Per-launch time of the extended entry points on the prefill-shaped
+    batch, beside the plain launch: row offsets (a flat ragged layout),
+    values (a gather kernel after the selection), and a transposed view
+    (each row packed from a column stride of num_rows, then selected)."""
+    import torch
+    import row_radix_top_amd as rrt
+    dev = scores.device
+    out = torch.empty((w.num_rows, w.K), dtype=torch.int32, device=dev)
+    vals = torch.empty((w.num_rows, w.K), dtype=torch.float32, device=dev)
+    ws = rrt.new_workspace(rrt.workspace_size(w.num_rows, w.row_stride, w.K, device=dev), dev)
+    n = np.clip(w.flat_lengths.astype(np.int64), 0, w.row_stride)
+    starts = torch.from_numpy(np.concatenate([[0], np.cumsum(n)[:-1]]).astype(np.int32)).to(dev)
+    res = {"workload": "prefill-shaped batch (the bench line's)"}
+    res["plain_us"] = round(time_launches(lambda i: rrt.topk_ragged(scores, L, w.K, out=out, workspace=ws),
+                                          launches) * 1e3, 2)
+    res["row_offsets_us"] = round(time_launches(
+        lambda i: rrt.topk_ragged(scores, L, w.K, out=out, workspace=ws, row_offsets=starts), launches) * 1e3, 2)
+    res["values_us"] = round(time_launches(
+        lambda i: rrt.topk_ragged_values(scores, L, w.K, out=out, out_values=vals, workspace=ws), launches) * 1e3, 2)
+    del ws
+    # The same scores as a transposed view: column stride num_rows.
+    st = torch.empty((w.row_stride, w.num_rows), dtype=torch.float32, device=dev)
+    st.copy_(scores.t())
+    view = st.t()
+    sws = rrt.new_workspace(rrt.strided_workspace_size(w.num_rows, w.row_stride, w.K, device=dev), dev)
+    res["transposed_view_us"] = round(time_launches(
+        lambda i: rrt.topk_ragged_strided(view, L, w.K, workspace=sws, out=out), launches) * 1e3, 2)
+    del st, view, sws, out, vals
+    torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -387,6 +420,9 @@ def main() -> int:
         result["workloads"] = others
         log("decode launch latency")
         result["decode_latency"] = decode_latency()
+        if w.name == "prefill":
+            log("extended entry points")
+            result["extensions"] = extensions(w, scores, lengths)
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")

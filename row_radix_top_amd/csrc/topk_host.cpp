@@ -401,7 +401,7 @@ namespace {
 
 int launch(const float* scores, int64_t row_stride, const int32_t* lengths, const int32_t* row_offsets,
            int32_t num_rows, int32_t next_n, int32_t K, int32_t* out_idx, void* workspace, hipStream_t stream,
-           const topk_overrides* ov) {
+           const topk_overrides* ov, float* out_val = nullptr) {
   if (num_rows < 0) return fail(TOPK_EINVAL, "num_rows must be >= 0");
   if (next_n < 1) return fail(TOPK_EINVAL, "next_n must be >= 1");
   if (num_rows % next_n != 0) return fail(TOPK_EINVAL, "num_rows must be a multiple of next_n");
@@ -426,6 +426,7 @@ int launch(const float* scores, int64_t row_stride, const int32_t* lengths, cons
   kp.scores = scores;
   kp.lengths = lengths;
   kp.row_offsets = row_offsets;
+  kp.out_val = out_val;
   kp.out = out_idx;
   kp.ws = plan.workspace_bytes > 0 ? static_cast<uint8_t*>(workspace) : nullptr;
   kp.row_stride = row_stride;
@@ -449,7 +450,7 @@ int launch(const float* scores, int64_t row_stride, const int32_t* lengths, cons
   // Split rows run on the one-workgroup kernel's split instance (same
   // occupancy: both are held to the same register and LDS budget).
   const int kpath = (plan.path == TOPK_PATH_SINGLE && plan.split_rows > 0) ? 4 : plan.path;
-  const void* fn = rrt::kernel_ptr(kpath, plan.vec, plan.idx16 != 0);
+  const void* fn = rrt::kernel_ptr(kpath, plan.vec, plan.idx16 != 0, out_val != nullptr);
   hipError_t e = hipLaunchKernel(fn, dim3(plan.grid), dim3(plan.block), args, 0, stream);
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) {
@@ -535,16 +536,8 @@ int topk_ragged_values_ex(const float* scores, int64_t row_stride, const int32_t
                           const topk_overrides* ov) {
   if (num_rows > 0 && out_val == nullptr) return fail(TOPK_EINVAL, "null out_val");
   if (reinterpret_cast<uintptr_t>(out_val) % 4 != 0) return fail(TOPK_EINVAL, "out_val must be 4-byte aligned");
-  int rc = launch(scores, row_stride, lengths, row_offsets, num_rows, next_n, K, out_idx, workspace, stream, ov);
-  if (rc != TOPK_OK || num_rows == 0) return rc;
-  // The values, from the indices just written (same stream, so in order).
-  const int64_t total = (int64_t)num_rows * K;
-  const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 4096);
-  void* args[] = {&scores, &row_stride, &out_idx, &row_offsets, &num_rows, &K, &out_val};
-  hipError_t e = hipLaunchKernel(rrt::values_kernel_ptr(), dim3(blocks), dim3(256), args, 0, stream);
-  if (e == hipSuccess) e = hipGetLastError();
-  if (e != hipSuccess) return fail(TOPK_ELAUNCH, std::string("values kernel: ") + hipGetErrorString(e));
-  return TOPK_OK;
+  return launch(scores, row_stride, lengths, row_offsets, num_rows, next_n, K, out_idx, workspace, stream, ov,
+                out_val);
 }
 
 int topk_ragged_values(const float* scores, int64_t row_stride, const int32_t* lengths, const int32_t* row_offsets,

@@ -94,6 +94,7 @@ struct KernelParams {
   const float* scores;
   const int32_t* lengths;
   const int32_t* row_offsets;  // nullable: added to each row's chosen indices
+  float* out_val;              // nullable: the chosen scores, [num_rows, K]
   int32_t* out;
   uint8_t* ws;
   int64_t row_stride;
@@ -114,10 +115,11 @@ struct KernelParams {
 
 // Kernel lookup for the host side.  path: 1 single, 2 multi, 3 the
 // streaming-read reference (idx16 ignored), 4 single with split rows.
-const void* kernel_ptr(int path, int vec, bool idx16);
+// vals: the one-workgroup instance that also writes the chosen scores (the
+// multi-workgroup kernel always can).
+const void* kernel_ptr(int path, int vec, bool idx16, bool vals = false);
 const void* zero_kernel_ptr();
 const void* keys_kernel_ptr();
-const void* values_kernel_ptr();
 const void* pack_kernel_ptr();
 int lds_bytes_of(bool idx16);
 

@@ -63,7 +63,13 @@ __device__ __forceinline__ uint32_t ord_key(uint32_t u) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Inverse of ord_key (up to the sign of zero): the fp32 bits of a key.
+// The same order without folding -0.0 into +0.0 (-0.0 sorts just below it),
+// exactly reversible by key_bits; for transforms that must give the bits back.
+__device__ __forceinline__ uint32_t raw_key(uint32_t u) {
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inverse of ord_key (up to the sign of zero) and of raw_key: fp32 bits.
 __device__ __forceinline__ uint32_t key_bits(uint32_t k) {
   return (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
 }
@@ -314,6 +320,20 @@ __device__ __forceinline__ void load_keys(const Smem<I16>& sm, uint32_t (&k)[Sha
   }
 }
 
+// The fp32 bits of this thread's slice, as stored.
+template <bool I16>
+__device__ __forceinline__ void load_bits(const Smem<I16>& sm, uint32_t (&v)[Shape<I16>::kSlots], const Slice& sl) {
+  constexpr int S = Shape<I16>::kSlots;
+#pragma unroll
+  for (int q = 0; q < S / 2; ++q) {
+    if ((uint32_t)(2 * q) < sl.sp) {
+      const u32x2 a = *reinterpret_cast<const u32x2*>(&sm.val[sl.base + 2 * q]);
+      v[2 * q + 0] = a.x;
+      v[2 * q + 1] = a.y;
+    }
+  }
+}
+
 template <bool I16>
 __device__ __forceinline__ void load_idx(const Smem<I16>& sm, uint32_t (&ix)[Shape<I16>::kSlots], const Slice& sl) {
   constexpr int S = Shape<I16>::kSlots;
@@ -468,10 +488,17 @@ enum EmitMode { kToBuffer = 0, kToOut = 1 };
 // row), so they are staged in hist1 and copied out with coalesced stores.
 // Every thread has read its buffer slice, and every wave has finished
 // reading the histograms, before any thread writes (the scan's barrier).
+//
+// vout (kToOut only, may be null): the chosen scores' exact bits go to
+// vout[rank] beside the indices.  They are read from the buffer's fp32 bits
+// (which nothing overwrites in this mode) and staged over the index array,
+// which nobody reads after the scan's barrier.
 template <bool I16, int MODE>
 __device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[Shape<I16>::kSlots], const Slice& sl,
                                             const Sel& s, uint32_t gt_base, uint32_t eq_base, int32_t* out,
-                                            uint32_t limit, uint32_t ibase) {
+                                            uint32_t limit, uint32_t ibase, float* vout = nullptr) {
+  static_assert(sizeof(sm.idx) >= 4 * kMaxK, "values staged over the index array");
+  uint32_t* vstage = reinterpret_cast<uint32_t*>(&sm.idx[0]);
   constexpr int S = Shape<I16>::kSlots;
   static_assert(S <= 32, "slice flags fit one word");
   const uint32_t sp = sl.sp, nv = sl.nv;
@@ -495,10 +522,14 @@ __device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[S
       }
     }
   }
-  // Indices are read before the scan's barrier: a compaction then moves
-  // entries down into other threads' slices.
+  // Indices (and, for a compaction, the fp32 bits) are read before the
+  // scan's barrier: a compaction then moves entries down into other threads'
+  // slices.  The bits are kept rather than rebuilt from the keys, which fold
+  // -0.0 into +0.0.
   uint32_t ix[S];
   load_idx<I16>(sm, ix, sl);
+  uint32_t rv[MODE == kToBuffer ? S : 1];
+  if constexpr (MODE == kToBuffer) load_bits<I16>(sm, rv, sl);
   uint32_t total;
   const uint32_t excl = block_excl_scan(sm, (uint32_t)__popc(gtm) | ((uint32_t)__popc(eqm) << 16), &total);
   uint32_t first, m;
@@ -511,8 +542,9 @@ __device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[S
         if (((gtm >> j) & 1u) && pos < limit) {
           if constexpr (MODE != kToBuffer) {
             sm.hist1[pos] = ibase + ix[j];
+            if (vout != nullptr) vstage[pos] = sm.val[sl.base + j];
           } else {
-            sm.val[pos] = key_bits(k[j]);
+            sm.val[pos] = rv[MODE == kToBuffer ? j : 0];
             sm.idx[pos] = (typename Shape<I16>::Idx)ix[j];
           }
         }
@@ -534,8 +566,9 @@ __device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[S
         if (pick && pos < limit) {
           if constexpr (MODE != kToBuffer) {
             sm.hist1[pos - first] = ibase + ix[j];
+            if (vout != nullptr) vstage[pos - first] = sm.val[sl.base + j];
           } else {
-            sm.val[pos] = key_bits(k[j]);
+            sm.val[pos] = rv[MODE == kToBuffer ? j : 0];
             sm.idx[pos] = (typename Shape<I16>::Idx)ix[j];
           }
         }
@@ -566,6 +599,10 @@ __device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[S
       }
     }
     sm.hs[tid()] = 0u;
+    if (vout != nullptr) {
+      float* vdst = vout + first;
+      for (uint32_t i = tid(); i < m; i += kBlock) vdst[i] = __uint_as_float(vstage[i]);
+    }
   } else {
     clear_hists(sm);
   }
@@ -612,7 +649,7 @@ __device__ __noinline__ uint64_t compact(Smem<I16>& sm, uint32_t cnt, uint32_t k
 // in flight.
 template <bool I16>
 __device__ __forceinline__ void final_select(Smem<I16>& sm, const Slice& sl, uint32_t K, int32_t* out,
-                                             uint32_t ibase) {
+                                             uint32_t ibase, float* vout = nullptr) {
   constexpr int S = Shape<I16>::kSlots;
   K = uni(K);
   uint32_t k[S];
@@ -620,7 +657,7 @@ __device__ __forceinline__ void final_select(Smem<I16>& sm, const Slice& sl, uin
   uint32_t lo, hi;
   key_range<I16, S>(sm, k, sl, lo, hi);
   const Sel s = range_select<I16, S>(sm, k, sl, lo, hi, K, 0u);
-  emit_chosen<I16, kToOut>(sm, k, sl, s, 0u, 0u, out, K, ibase);
+  emit_chosen<I16, kToOut>(sm, k, sl, s, 0u, 0u, out, K, ibase, vout);
 }
 
 // ---------------------------------------------------------------------------
@@ -790,13 +827,14 @@ __device__ __forceinline__ uint32_t spec_bound(Smem<I16>& sm, float (&x0)[kElems
   const uint32_t r = want > kSpecMinRank ? (uint32_t)want : kSpecMinRank;
   if (r >= K) return 0u;
   // The keys replace the values in place (registers are scarce here) and
-  // are turned back afterwards; only the sign of a zero can change, which no
-  // comparison sees.
+  // are turned back afterwards, bit for bit: raw_key keeps -0.0 apart from
+  // +0.0 (just below it), which only a bound of exactly zero can see, and
+  // both floats of that bound accept both zeros.
   uint32_t k[2 * kElems];
 #pragma unroll
   for (int e = 0; e < kElems; ++e) {
-    k[e] = ord_key(__float_as_uint(x0[e]));
-    k[kElems + e] = ord_key(__float_as_uint(x1[e]));
+    k[e] = raw_key(__float_as_uint(x0[e]));
+    k[kElems + e] = raw_key(__float_as_uint(x1[e]));
   }
   Slice sl;
   sl.base = 0u;
@@ -1319,8 +1357,13 @@ __device__ __forceinline__ int64_t clamp_len(const KernelParams& p, int row) {
 }
 
 // n <= K: every valid index (plus the row's offset), then -1.  Reads no scores.
-__device__ __forceinline__ void write_all_then_pad(int32_t* out, int64_t n, int K, uint32_t off) {
-  for (int i = threadIdx.x; i < K; i += kBlock) out[i] = i < n ? (int32_t)(off + (uint32_t)i) : -1;
+// With vout, the n scores themselves (read from rowp) and -inf after them.
+__device__ __forceinline__ void write_all_then_pad(int32_t* out, int64_t n, int K, uint32_t off,
+                                                   float* vout = nullptr, const float* rowp = nullptr) {
+  for (int i = threadIdx.x; i < K; i += kBlock) {
+    out[i] = i < n ? (int32_t)(off + (uint32_t)i) : -1;
+    if (vout != nullptr) vout[i] = i < n ? rowp[i] : -__builtin_huge_valf();
+  }
 }
 
 // What a row's chosen indices are shifted by in the output: its offset in a
@@ -1365,7 +1408,9 @@ __device__ __forceinline__ void unit_of(const KernelParams& p, uint32_t u, int& 
 
 // SPLIT: the launch has split rows.  Without, every unit is a whole row and
 // the split-row code is compiled out (it costs registers the row loop needs).
-template <int VEC, bool I16, bool SPLIT>
+// VALS: the launch also writes the chosen scores (compiled out otherwise, for
+// the same reason).
+template <int VEC, bool I16, bool SPLIT, bool VALS>
 __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_kernel(KernelParams p) {
   __shared__ Smem<I16> sm;
   zero_histograms(sm);
@@ -1414,7 +1459,10 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_ker
     if (SPLIT && c > 0 && !piece) {
       // Chunk of a row taken whole by its chunk 0: nothing to do.
     } else if (n <= (int64_t)K) {
-      write_all_then_pad(out, n, p.K, off);
+      if constexpr (VALS)
+        write_all_then_pad(out, n, p.K, off, p.out_val + (int64_t)row * p.K, p.scores + (int64_t)row * p.row_stride);
+      else
+        write_all_then_pad(out, n, p.K, off);
     } else {
       const float* rowp = p.scores + (int64_t)row * p.row_stride;
       uint32_t g0 = 0, g1 = (uint32_t)n, gL = 0;  // general path: range, starting bound
@@ -1538,7 +1586,8 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_ker
       have_pre = true;
     }
     if (select) {
-      final_select<I16>(sm, waved ? wave_slice<I16>(cnt) : plain_slice<I16>(cnt), K, out, off);
+      final_select<I16>(sm, waved ? wave_slice<I16>(cnt) : plain_slice<I16>(cnt), K, out, off,
+                        VALS ? p.out_val + (int64_t)row * p.K : nullptr);
     }
     first_unit = false;
     drawn = false;
@@ -1632,7 +1681,9 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_multi_kern
   const int64_t n = clamp_len(p, row);
   int32_t* out = p.out + (int64_t)row * p.K;
   if (n <= (int64_t)K) {
-    if (g == 0) write_all_then_pad(out, n, p.K, offset_of(p, row));
+    if (g == 0)
+      write_all_then_pad(out, n, p.K, offset_of(p, row), p.out_val != nullptr ? p.out_val + (int64_t)row * p.K : nullptr,
+                         p.scores + (int64_t)row * p.row_stride);
     return;
   }
   const int grow = (int)((n + p.chunk - 1) / p.chunk);  // workgroups with data in this row
@@ -1663,6 +1714,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_multi_kern
   const uint32_t sp = sl.sp, nv = sl.nv;
   uint32_t k[S];
   load_keys<I16>(sm, k, sl);
+  float* vout = p.out_val != nullptr ? p.out_val + (int64_t)row * p.K : nullptr;
 
   // Round 1: the chunk's top-digit (11-bit) histogram into the row's, then
   // the row-wide threshold digit from a copy of the row's.
@@ -1830,7 +1882,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_multi_kern
   s.in_bin = 0u;
   s.ok = ok;
   s.all_in = false;
-  emit_chosen<I16, kToOut>(sm, k, sl, s, gt_base, eq_base, out, K, (uint32_t)c0 + offset_of(p, row));
+  emit_chosen<I16, kToOut>(sm, k, sl, s, gt_base, eq_base, out, K, (uint32_t)c0 + offset_of(p, row), vout);
 }
 
 // ---------------------------------------------------------------------------
@@ -1919,27 +1971,6 @@ __global__ void zero_kernel(uint32_t* p, uint64_t words) {
   for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += stride) p[i] = 0u;
 }
 
-// Values of the chosen entries: vals[r, i] = the score bits at out[r, i] (less
-// the row's offset), -inf where out[r, i] = -1.  Runs after the selection on
-// the same stream.  A column outside [0, row_stride) -- impossible for an
-// output of the selection -- yields NaN instead of a read.
-__global__ void values_kernel(const float* __restrict__ scores, int64_t row_stride, const int32_t* __restrict__ out,
-                              const int32_t* __restrict__ row_offsets, int32_t num_rows, int32_t K,
-                              float* __restrict__ vals) {
-  const int64_t total = (int64_t)num_rows * K;
-  const int64_t step = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += step) {
-    const int64_t r = e / K;
-    const int32_t ix = out[e];
-    float v = -__builtin_huge_valf();
-    if (ix >= 0) {
-      const int64_t col = (int64_t)(uint32_t)ix - (row_offsets != nullptr ? (int64_t)(uint32_t)row_offsets[r] : 0);
-      v = (col >= 0 && col < row_stride) ? scores[r * row_stride + col] : __builtin_nanf("");
-    }
-    vals[e] = v;
-  }
-}
-
 // Packs rows with a column stride into contiguous rows of num_cols:
 // packed[r * num_cols + c] = scores[r * row_stride + c * col_stride] for
 // c < clamp(lengths[r], 0, num_cols).  Nothing at or past a length is read
@@ -1966,34 +1997,46 @@ __global__ void keys_kernel(const uint32_t* bits, uint32_t* keys, int64_t n) {
 // ---------------------------------------------------------------------------
 
 template <bool I16>
-static const void* pick(int path, int vec) {
+static const void* pick(int path, int vec, bool vals) {
   if (path == 3) {
     if (vec == 4) return reinterpret_cast<const void*>(&read_ref_kernel<4>);
     if (vec == 2) return reinterpret_cast<const void*>(&read_ref_kernel<2>);
     return reinterpret_cast<const void*>(&read_ref_kernel<1>);
   }
-  if (path == 1) {
-    if (vec == 4) return reinterpret_cast<const void*>(&topk_single_kernel<4, I16, false>);
-    if (vec == 2) return reinterpret_cast<const void*>(&topk_single_kernel<2, I16, false>);
-    return reinterpret_cast<const void*>(&topk_single_kernel<1, I16, false>);
-  }
-  if (path == 4) {
-    if (vec == 4) return reinterpret_cast<const void*>(&topk_single_kernel<4, I16, true>);
-    if (vec == 2) return reinterpret_cast<const void*>(&topk_single_kernel<2, I16, true>);
-    return reinterpret_cast<const void*>(&topk_single_kernel<1, I16, true>);
+  if (path == 1 || path == 4) {
+    const bool sp = path == 4;
+    if (sp && vals) {
+      if (vec == 4) return reinterpret_cast<const void*>(&topk_single_kernel<4, I16, true, true>);
+      if (vec == 2) return reinterpret_cast<const void*>(&topk_single_kernel<2, I16, true, true>);
+      return reinterpret_cast<const void*>(&topk_single_kernel<1, I16, true, true>);
+    }
+    if (sp) {
+      if (vec == 4) return reinterpret_cast<const void*>(&topk_single_kernel<4, I16, true, false>);
+      if (vec == 2) return reinterpret_cast<const void*>(&topk_single_kernel<2, I16, true, false>);
+      return reinterpret_cast<const void*>(&topk_single_kernel<1, I16, true, false>);
+    }
+    if (vals) {
+      if (vec == 4) return reinterpret_cast<const void*>(&topk_single_kernel<4, I16, false, true>);
+      if (vec == 2) return reinterpret_cast<const void*>(&topk_single_kernel<2, I16, false, true>);
+      return reinterpret_cast<const void*>(&topk_single_kernel<1, I16, false, true>);
+    }
+    if (vec == 4) return reinterpret_cast<const void*>(&topk_single_kernel<4, I16, false, false>);
+    if (vec == 2) return reinterpret_cast<const void*>(&topk_single_kernel<2, I16, false, false>);
+    return reinterpret_cast<const void*>(&topk_single_kernel<1, I16, false, false>);
   }
   if (vec == 4) return reinterpret_cast<const void*>(&topk_multi_kernel<4, I16>);
   if (vec == 2) return reinterpret_cast<const void*>(&topk_multi_kernel<2, I16>);
   return reinterpret_cast<const void*>(&topk_multi_kernel<1, I16>);
 }
 
-const void* kernel_ptr(int path, int vec, bool idx16) { return idx16 ? pick<true>(path, vec) : pick<false>(path, vec); }
+const void* kernel_ptr(int path, int vec, bool idx16, bool vals) {
+  return idx16 ? pick<true>(path, vec, vals) : pick<false>(path, vec, vals);
+}
 
 int lds_bytes_of(bool idx16) { return idx16 ? (int)sizeof(Smem<true>) : (int)sizeof(Smem<false>); }
 
 const void* zero_kernel_ptr() { return reinterpret_cast<const void*>(&zero_kernel); }
 const void* keys_kernel_ptr() { return reinterpret_cast<const void*>(&keys_kernel); }
-const void* values_kernel_ptr() { return reinterpret_cast<const void*>(&values_kernel); }
 const void* pack_kernel_ptr() { return reinterpret_cast<const void*>(&pack_kernel); }
 
 }  // namespace rrt
