@@ -517,7 +517,8 @@ int topk_ragged_strided(const float* scores, int64_t row_stride, int64_t col_str
   if (rc != TOPK_OK) return rc;
   float* packed = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + rrt::round_up(plan_bytes, 256));
   {
-    const unsigned blocks = (unsigned)std::min<int64_t>(num_rows, 4096);
+    const int64_t tiles = ((num_rows + 63) / 64) * ((num_cols + 63) / 64);
+    const unsigned blocks = (unsigned)std::min<int64_t>(tiles, 4096);
     void* args[] = {&scores, &row_stride, &col_stride, &num_cols, &lengths, &num_rows, &packed};
     hipError_t e = hipLaunchKernel(rrt::pack_kernel_ptr(), dim3(blocks), dim3(256), args, 0, stream);
     if (e == hipSuccess) e = hipGetLastError();

@@ -1974,16 +1974,42 @@ __global__ void zero_kernel(uint32_t* p, uint64_t words) {
 // Packs rows with a column stride into contiguous rows of num_cols:
 // packed[r * num_cols + c] = scores[r * row_stride + c * col_stride] for
 // c < clamp(lengths[r], 0, num_cols).  Nothing at or past a length is read
-// or written.
-__global__ void pack_kernel(const float* __restrict__ scores, int64_t row_stride, int64_t col_stride,
-                            int64_t num_cols, const int32_t* __restrict__ lengths, int32_t num_rows,
-                            float* __restrict__ packed) {
-  for (int64_t r = blockIdx.x; r < num_rows; r += gridDim.x) {
-    int64_t n = lengths[r];
-    n = n < 0 ? 0 : (n > num_cols ? num_cols : n);
-    const float* src = scores + r * row_stride;
-    float* dst = packed + r * num_cols;
-    for (int64_t c = threadIdx.x; c < n; c += blockDim.x) dst[c] = src[c * col_stride];
+// or written.  Tiles of 64 rows x 64 columns go through LDS: loaded with the
+// lanes along whichever of rows and columns is closer in memory (a
+// transposed view reads consecutive addresses), written with the lanes
+// along the packed rows.
+constexpr int kPackTile = 64;
+
+__global__ void __launch_bounds__(256) pack_kernel(const float* __restrict__ scores, int64_t row_stride,
+                                                   int64_t col_stride, int64_t num_cols,
+                                                   const int32_t* __restrict__ lengths, int32_t num_rows,
+                                                   float* __restrict__ packed) {
+  __shared__ float tile[kPackTile][kPackTile + 1];  // [column][row]
+  __shared__ int32_t len[kPackTile];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t tiles_r = (num_rows + kPackTile - 1) / kPackTile;
+  const int64_t tiles_c = (num_cols + kPackTile - 1) / kPackTile;
+  const bool rows_close = row_stride < col_stride;
+  for (int64_t tt = blockIdx.x; tt < tiles_r * tiles_c; tt += gridDim.x) {
+    const int64_t r0 = (tt % tiles_r) * kPackTile, c0 = (tt / tiles_r) * kPackTile;
+    if (threadIdx.x < kPackTile) {
+      const int64_t r = r0 + threadIdx.x;
+      int64_t n = r < num_rows ? lengths[r] : 0;
+      n = n < 0 ? 0 : (n > num_cols ? num_cols : n);
+      len[threadIdx.x] = (int32_t)(n > c0 ? (n - c0 < kPackTile ? n - c0 : kPackTile) : 0);
+    }
+    __syncthreads();
+    if (rows_close) {
+      for (int cc = w; cc < kPackTile; cc += 4)
+        if (cc < len[lane]) tile[cc][lane] = scores[(r0 + lane) * row_stride + (c0 + cc) * col_stride];
+    } else {
+      for (int rr = w; rr < kPackTile; rr += 4)
+        if (lane < len[rr]) tile[lane][rr] = scores[(r0 + rr) * row_stride + (c0 + lane) * col_stride];
+    }
+    __syncthreads();
+    for (int rr = w; rr < kPackTile; rr += 4)
+      if (lane < len[rr]) packed[(r0 + rr) * num_cols + c0 + lane] = tile[lane][rr];
+    __syncthreads();  // the tile and lengths are reused
   }
 }
 
