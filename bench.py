@@ -280,7 +280,7 @@ def decode_latency(launches: int = 400):
 def extensions(w, scores, L, launches: int = 20):
     """Per-launch time of the extended entry points on the prefill-shaped
     batch, beside the plain launch: row offsets (a flat ragged layout),
-    values (a gather kernel after the selection), and a transposed view
+    values, bf16 scores (the same batch rounded), and a transposed view
     (each row packed from a column stride of num_rows, then selected)."""
     import torch
     import row_radix_top_amd as rrt
@@ -297,7 +297,14 @@ def extensions(w, scores, L, launches: int = 20):
         lambda i: rrt.topk_ragged(scores, L, w.K, out=out, workspace=ws, row_offsets=starts), launches) * 1e3, 2)
     res["values_us"] = round(time_launches(
         lambda i: rrt.topk_ragged_values(scores, L, w.K, out=out, out_values=vals, workspace=ws), launches) * 1e3, 2)
-    del ws
+    # The same scores rounded to bf16 (half the bytes).
+    sb = scores.to(torch.bfloat16)
+    bf_us = time_launches(lambda i: rrt.topk_ragged_bf16(sb, L, w.K, out=out, workspace=ws), launches) * 1e3
+    valid = 2 * int(n.sum())
+    res["bf16_us"] = round(bf_us, 2)
+    res["bf16_rows_per_s"] = w.num_rows / (bf_us * 1e-6)
+    res["bf16_effective_GBps"] = round(valid / (bf_us * 1e-6) / 1e9, 1)
+    del ws, sb
     # The same scores as a transposed view: column stride num_rows.
     st = torch.empty((w.row_stride, w.num_rows), dtype=torch.float32, device=dev)
     st.copy_(scores.t())

@@ -154,6 +154,26 @@ int topk_ragged_strided(const float* scores, int64_t row_stride, int64_t col_str
                         int32_t next_n, int32_t K, int32_t* out_idx, float* out_val,
                         void* workspace, hipStream_t stream);
 
+/*
+ * topk_ragged_bf16 -- the same selection over bf16 scores (not on the pages,
+ * whose logits are fp32).
+ *
+ *   scores       bf16 values as their 16 bits, row r at scores + r * row_stride
+ *                (elements), 2-byte aligned; rows with a 16-byte-aligned start
+ *                and row_stride % 8 == 0 load 8 elements at a time.
+ *   row_offsets  NULL or as for topk_ragged_offsets.
+ *   out_val      NULL or as for topk_ragged_values: the chosen scores widened
+ *                to fp32 (exact).
+ *
+ * Each score is widened to fp32 by shifting its bits up, which is exact, so
+ * the order, the ties and the chosen indices are those of the fp32 values.
+ * Workspace and errors as for topk_ragged (topk_ragged_workspace_size gives
+ * the size for the same shape).
+ */
+int topk_ragged_bf16(const uint16_t* scores, int64_t row_stride, const int32_t* lengths,
+                     const int32_t* row_offsets, int32_t num_rows, int32_t next_n, int32_t K,
+                     int32_t* out_idx, float* out_val, void* workspace, hipStream_t stream);
+
 /* Bytes of workspace topk_ragged needs for this shape on the stream's device.
  * *bytes = 0 means no workspace is used: one workgroup per row and no more
  * rows than resident workgroups.  With more rows than that, a 256-byte
@@ -197,7 +217,7 @@ typedef enum {
 typedef struct {
   int32_t path;           /* topk_path */
   int32_t kmax;           /* largest K the kernel instance handles (TOPK_RAGGED_MAX_K) */
-  int32_t vec;            /* fp32 elements per load: 4, 2 or 1 */
+  int32_t vec;            /* elements per load: 4, 2 or 1 (fp32), 8 or 1 (bf16) */
   int32_t block;          /* threads per workgroup */
   int32_t grid;           /* workgroups launched */
   int32_t wg_per_row;     /* G (1 on the single path) */
@@ -217,7 +237,7 @@ typedef struct {
   int32_t force_path;        /* 0 auto, TOPK_PATH_SINGLE or TOPK_PATH_MULTI */
   int32_t force_wg_per_row;  /* 0 auto, else G for the multi path */
   int32_t max_grid;          /* 0 auto, else cap on the single path's persistent grid */
-  int32_t force_vec;         /* 0 auto, else 1, 2 or 4 (must suit the alignment) */
+  int32_t force_vec;         /* 0 auto, else 1, 2 or 4 for fp32, 1 or 8 for bf16 (must suit the alignment) */
   int64_t force_chunk;       /* 0 auto, else elements per workgroup (multiple of 4) */
   uint32_t spin_limit;       /* 0 default; bound on a cooperative wait (polls) */
   int32_t min_chunk;         /* 0 default; smallest per-workgroup chunk the planner picks */
@@ -229,8 +249,8 @@ typedef struct {
 } topk_overrides;
 
 /* Pure planning function (host only, no GPU needed).  vec_allowed is the
- * widest load the pointer/stride alignment permits (4, 2 or 1).  ov may be
- * NULL. */
+ * widest load, in elements, the pointer/stride alignment permits (1, 2, 4
+ * or 8).  ov may be NULL. */
 int topk_ragged_plan(const topk_device_props* props, int32_t num_rows, int64_t row_stride,
                      int32_t K, int32_t vec_allowed, const topk_overrides* ov,
                      topk_plan* plan);
@@ -259,6 +279,10 @@ int topk_ragged_values_ex(const float* scores, int64_t row_stride, const int32_t
                           const int32_t* row_offsets, int32_t num_rows, int32_t next_n, int32_t K,
                           int32_t* out_idx, float* out_val, void* workspace, hipStream_t stream,
                           const topk_overrides* ov);
+int topk_ragged_bf16_ex(const uint16_t* scores, int64_t row_stride, const int32_t* lengths,
+                        const int32_t* row_offsets, int32_t num_rows, int32_t next_n, int32_t K,
+                        int32_t* out_idx, float* out_val, void* workspace, hipStream_t stream,
+                        const topk_overrides* ov);
 
 /* Error bits a kernel left in the workspace header (synchronises stream):
  * bit 0: a cooperative wait hit its spin limit; bit 1: a threshold search

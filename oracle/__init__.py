@@ -14,6 +14,8 @@ order or the padding; the readings used are stated in ``oracle_topk.cpp`` and
 
 from .oracle import (  # noqa: F401
     load_library,
+    topk_ragged_bf16_oracle,
+    widen_bf16,
     topk_ragged_offsets_oracle,
     topk_ragged_oracle,
     topk_ragged_strided_oracle,

@@ -124,3 +124,16 @@ def topk_ragged_strided_oracle(flat: np.ndarray, row_stride: int, col_stride: in
         if n:
             dense[r, :n] = flat[r * row_stride + np.arange(n, dtype=np.int64) * col_stride]
     return topk_ragged_oracle(dense, np.asarray(lengths), K, next_n=next_n, threads=threads)
+
+
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 values (their 16 bits as uint16) as fp32: the 16 bits become the
+    high half of the fp32 word, which is exact."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def topk_ragged_bf16_oracle(bits: np.ndarray, lengths: np.ndarray, K: int, next_n: int | None = None,
+                            threads: int = 0) -> np.ndarray:
+    """The selection over bf16 scores (given as uint16 bits [num_rows,
+    row_stride]): the same rule on their exact fp32 widening."""
+    return topk_ragged_oracle(widen_bf16(bits), lengths, K, next_n=next_n, threads=threads)

@@ -21,6 +21,7 @@ from .binding import (  # noqa: F401
     read_reference,
     strided_workspace_size,
     topk_ragged,
+    topk_ragged_bf16,
     topk_ragged_strided,
     topk_ragged_values,
     workspace_init,

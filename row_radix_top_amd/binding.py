@@ -27,7 +27,7 @@ EXPORTED = (
     "topk_ragged_workspace_size_ex", "topk_ragged_ex", "topk_ragged_workspace_status",
     "topk_ragged_debug_keys", "topk_ragged_version", "topk_ragged_read_reference",
     "topk_ragged_offsets", "topk_ragged_offsets_ex", "topk_ragged_values", "topk_ragged_values_ex",
-    "topk_ragged_strided", "topk_ragged_strided_workspace_size",
+    "topk_ragged_strided", "topk_ragged_strided_workspace_size", "topk_ragged_bf16", "topk_ragged_bf16_ex",
 )
 
 
@@ -114,6 +114,9 @@ def load() -> ctypes.CDLL:
                                                ctypes.POINTER(Overrides)]
         lib.topk_ragged_values.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp, vp, vp]
         lib.topk_ragged_strided.argtypes = [vp, i64, i64, i64, vp, vp, i32, i32, i32, vp, vp, vp, vp]
+        lib.topk_ragged_bf16.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp, vp, vp]
+        lib.topk_ragged_bf16_ex.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp, vp, vp,
+                                            ctypes.POINTER(Overrides)]
         lib.topk_ragged_strided_workspace_size.argtypes = [i32, i64, i32, vp, ctypes.POINTER(sz)]
         lib.topk_ragged_values_ex.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp, vp, vp,
                                               ctypes.POINTER(Overrides)]
@@ -269,6 +272,32 @@ def topk_ragged_strided(scores, lengths, K: int, *, workspace, out=None, out_val
                                     workspace.data_ptr() if workspace is not None else None,
                                     _stream_ptr(stream, scores.device))
     _check(rc, "topk_ragged_strided")
+    return out if out_values is None else (out, out_values)
+
+
+def topk_ragged_bf16(scores, lengths, K: int, *, out=None, out_values=None, workspace=None,
+                     next_n: int | None = None, stream=None, row_offsets=None, **overrides):
+    """topk_ragged over bf16 scores (a torch.bfloat16 CUDA tensor with unit
+    column stride).  Returns the indices, or (indices, values) when
+    out_values (float32 [num_rows, K]) is given."""
+    import torch
+    if scores.dtype != torch.bfloat16 or not scores.is_cuda or scores.dim() != 2 or scores.stride(1) != 1:
+        raise ValueError("scores must be a 2-D bfloat16 CUDA tensor with unit column stride")
+    if lengths.dtype != torch.int32 or not lengths.is_cuda or not lengths.is_contiguous():
+        raise ValueError("lengths must be a contiguous int32 CUDA tensor")
+    if next_n is None:
+        next_n = int(lengths.shape[1]) if lengths.dim() == 2 else 1
+    num_rows = scores.shape[0]
+    if out is None:
+        out = torch.empty((num_rows, K), dtype=torch.int32, device=scores.device)
+    ro = None if row_offsets is None else row_offsets.data_ptr()
+    vp_ = None if out_values is None else out_values.data_ptr()
+    ov = Overrides.make(**overrides)
+    args = (scores.data_ptr(), scores.stride(0), lengths.data_ptr(), ro, num_rows, next_n, K, out.data_ptr(), vp_,
+            workspace.data_ptr() if workspace is not None else None, _stream_ptr(stream, scores.device))
+    lib = load()
+    rc = lib.topk_ragged_bf16(*args) if ov is None else lib.topk_ragged_bf16_ex(*args, ctypes.byref(ov))
+    _check(rc, "topk_ragged_bf16")
     return out if out_values is None else (out, out_values)
 
 

@@ -58,7 +58,7 @@ std::string describe(const topk_plan& p) {
 struct DevInfo {
   int num_cus = 0;
   int max_lds_block = 0;
-  std::map<std::tuple<int, int, int>, int> occ;  // (path, vec, idx16) -> WGs per CU
+  std::map<std::tuple<int, int, int, int>, int> occ;  // (path, vec, idx16, bf16) -> WGs per CU
 };
 
 std::mutex g_mu;
@@ -88,9 +88,9 @@ int device_info(int dev, DevInfo** out) {
 }
 
 // Occupancy of the exact instance that will be launched.
-int occupancy(int dev, DevInfo* d, int path, int vec, bool idx16, int* occ) {
+int occupancy(int dev, DevInfo* d, int path, int vec, bool idx16, int* occ, bool bf16 = false) {
   std::lock_guard<std::mutex> lk(g_mu);
-  const auto key = std::make_tuple(path, vec, idx16 ? 1 : 0);
+  const auto key = std::make_tuple(path, vec, idx16 ? 1 : 0, bf16 ? 1 : 0);
   auto it = d->occ.find(key);
   if (it != d->occ.end()) {
     *occ = it->second;
@@ -101,7 +101,7 @@ int occupancy(int dev, DevInfo* d, int path, int vec, bool idx16, int* occ) {
   if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
   int o = 0;
   if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, rrt::kernel_ptr(path, vec, idx16), rrt::kBlock, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, rrt::kernel_ptr(path, vec, idx16, false, bf16), rrt::kBlock, 0);
   if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
   if (e != hipSuccess) {
     char buf[256];
@@ -114,8 +114,11 @@ int occupancy(int dev, DevInfo* d, int path, int vec, bool idx16, int* occ) {
   return TOPK_OK;
 }
 
-int vec_allowed_for(const float* scores, int64_t row_stride) {
+// Widest load, in elements, that the pointer and stride alignment allow:
+// fp32 rows take 16-, 8- or 4-byte loads, bf16 rows 16- or 2-byte loads.
+int vec_allowed_for(const void* scores, int64_t row_stride, bool bf16 = false) {
   const uintptr_t a = reinterpret_cast<uintptr_t>(scores);
+  if (bf16) return (a % 16 == 0 && row_stride % 8 == 0) ? 8 : 1;
   if (a % 16 == 0 && row_stride % 4 == 0) return 4;
   if (a % 8 == 0 && row_stride % 2 == 0) return 2;
   return 1;
@@ -124,8 +127,8 @@ int vec_allowed_for(const float* scores, int64_t row_stride) {
 int chosen_vec(int vec_allowed, const topk_overrides* ov, int* vec) {
   int v = vec_allowed;
   if (ov != nullptr && ov->force_vec != 0) {
-    if (ov->force_vec != 1 && ov->force_vec != 2 && ov->force_vec != 4)
-      return fail(TOPK_EINVAL, "force_vec must be 1, 2 or 4");
+    if (ov->force_vec != 1 && ov->force_vec != 2 && ov->force_vec != 4 && ov->force_vec != 8)
+      return fail(TOPK_EINVAL, "force_vec must be 1, 2, 4 or 8");
     if (ov->force_vec > vec_allowed)
       return fail(TOPK_EINVAL, "force_vec is wider than the scores pointer/stride alignment allows");
     v = ov->force_vec;
@@ -135,17 +138,17 @@ int chosen_vec(int vec_allowed, const topk_overrides* ov, int* vec) {
 }
 
 // Fills props for the load width vec of every kernel instance on device dev.
-int real_props(int dev, int vec, topk_device_props* props) {
+int real_props(int dev, int vec, topk_device_props* props, bool bf16 = false) {
   DevInfo* d = nullptr;
   int rc = device_info(dev, &d);
   if (rc != TOPK_OK) return rc;
   std::memset(props, 0, sizeof(*props));
   props->num_cus = d->num_cus;
   props->max_lds_per_block = d->max_lds_block;
-  rc = occupancy(dev, d, 1, vec, false, &props->occupancy_single);
-  if (rc == TOPK_OK) rc = occupancy(dev, d, 2, vec, false, &props->occupancy_multi);
-  if (rc == TOPK_OK) rc = occupancy(dev, d, 1, vec, true, &props->occupancy_single16);
-  if (rc == TOPK_OK) rc = occupancy(dev, d, 2, vec, true, &props->occupancy_multi16);
+  rc = occupancy(dev, d, 1, vec, false, &props->occupancy_single, bf16);
+  if (rc == TOPK_OK) rc = occupancy(dev, d, 2, vec, false, &props->occupancy_multi, bf16);
+  if (rc == TOPK_OK) rc = occupancy(dev, d, 1, vec, true, &props->occupancy_single16, bf16);
+  if (rc == TOPK_OK) rc = occupancy(dev, d, 2, vec, true, &props->occupancy_multi16, bf16);
   return rc;
 }
 
@@ -161,19 +164,20 @@ int check_common(int32_t num_rows, int64_t row_stride, int32_t K) {
   return TOPK_OK;
 }
 
-int plan_for_call(const float* scores, int32_t num_rows, int64_t row_stride, int32_t K,
-                  const topk_overrides* ov, hipStream_t stream, int* dev_out, topk_plan* plan) {
+int plan_for_call(const void* scores, int32_t num_rows, int64_t row_stride, int32_t K,
+                  const topk_overrides* ov, hipStream_t stream, int* dev_out, topk_plan* plan, bool bf16 = false) {
   int rc = check_common(num_rows, row_stride, K);
   if (rc != TOPK_OK) return rc;
-  const int va = vec_allowed_for(scores, row_stride);
+  const int va = vec_allowed_for(scores, row_stride, bf16);
   int vec = 4;
   rc = chosen_vec(va, ov, &vec);
   if (rc != TOPK_OK) return rc;
+  if (bf16 && vec != 8 && vec != 1) return fail(TOPK_EINVAL, "bf16 rows load 8 elements or 1 (force_vec 8 or 1)");
   int dev = 0;
   rc = stream_device(stream, &dev);
   if (rc != TOPK_OK) return rc;
   topk_device_props props;
-  rc = real_props(dev, vec, &props);
+  rc = real_props(dev, vec, &props, bf16);
   if (rc != TOPK_OK) return rc;
   if (dev_out) *dev_out = dev;
   return topk_ragged_plan(&props, num_rows, row_stride, K, va, ov, plan);
@@ -199,8 +203,8 @@ int topk_ragged_plan(const topk_device_props* props_in, int32_t num_rows, int64_
   std::memset(plan, 0, sizeof(*plan));
   int rc = check_common(num_rows, row_stride, K);
   if (rc != TOPK_OK) return rc;
-  if (vec_allowed != 1 && vec_allowed != 2 && vec_allowed != 4)
-    return fail(TOPK_EINVAL, "vec_allowed must be 1, 2 or 4");
+  if (vec_allowed != 1 && vec_allowed != 2 && vec_allowed != 4 && vec_allowed != 8)
+    return fail(TOPK_EINVAL, "vec_allowed must be 1, 2, 4 or 8");
   if (props->num_cus < 1) return fail(TOPK_EDEVICE, "device reports no compute units");
   int vec = 4;
   rc = chosen_vec(vec_allowed, ov, &vec);
@@ -399,9 +403,9 @@ int topk_ragged_workspace_init(void* workspace, size_t bytes, hipStream_t stream
 
 namespace {
 
-int launch(const float* scores, int64_t row_stride, const int32_t* lengths, const int32_t* row_offsets,
+int launch(const void* scores, int64_t row_stride, const int32_t* lengths, const int32_t* row_offsets,
            int32_t num_rows, int32_t next_n, int32_t K, int32_t* out_idx, void* workspace, hipStream_t stream,
-           const topk_overrides* ov, float* out_val = nullptr) {
+           const topk_overrides* ov, float* out_val = nullptr, bool bf16 = false) {
   if (num_rows < 0) return fail(TOPK_EINVAL, "num_rows must be >= 0");
   if (next_n < 1) return fail(TOPK_EINVAL, "next_n must be >= 1");
   if (num_rows % next_n != 0) return fail(TOPK_EINVAL, "num_rows must be a multiple of next_n");
@@ -411,10 +415,10 @@ int launch(const float* scores, int64_t row_stride, const int32_t* lengths, cons
   if (scores == nullptr || lengths == nullptr || out_idx == nullptr)
     return fail(TOPK_EINVAL, "null scores, lengths or out_idx");
   if (reinterpret_cast<uintptr_t>(out_idx) % 4 != 0 || reinterpret_cast<uintptr_t>(lengths) % 4 != 0 ||
-      reinterpret_cast<uintptr_t>(scores) % 4 != 0 || reinterpret_cast<uintptr_t>(row_offsets) % 4 != 0)
-    return fail(TOPK_EINVAL, "scores, lengths, row_offsets and out_idx must be 4-byte aligned");
+      reinterpret_cast<uintptr_t>(scores) % (bf16 ? 2 : 4) != 0 || reinterpret_cast<uintptr_t>(row_offsets) % 4 != 0)
+    return fail(TOPK_EINVAL, "scores must be aligned to their element; lengths, row_offsets and out_idx to 4 bytes");
   topk_plan plan;
-  rc = plan_for_call(scores, num_rows, row_stride, K, ov, stream, nullptr, &plan);
+  rc = plan_for_call(scores, num_rows, row_stride, K, ov, stream, nullptr, &plan, bf16);
   if (rc != TOPK_OK) return rc;
   if (plan.workspace_bytes > 0 && workspace == nullptr)
     return fail(TOPK_EWORKSPACE, "this launch needs a workspace of " + std::to_string(plan.workspace_bytes) +
@@ -450,7 +454,7 @@ int launch(const float* scores, int64_t row_stride, const int32_t* lengths, cons
   // Split rows run on the one-workgroup kernel's split instance (same
   // occupancy: both are held to the same register and LDS budget).
   const int kpath = (plan.path == TOPK_PATH_SINGLE && plan.split_rows > 0) ? 4 : plan.path;
-  const void* fn = rrt::kernel_ptr(kpath, plan.vec, plan.idx16 != 0, out_val != nullptr);
+  const void* fn = rrt::kernel_ptr(kpath, plan.vec, plan.idx16 != 0, out_val != nullptr, bf16);
   hipError_t e = hipLaunchKernel(fn, dim3(plan.grid), dim3(plan.block), args, 0, stream);
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) {
@@ -546,6 +550,22 @@ int topk_ragged_values(const float* scores, int64_t row_stride, const int32_t* l
                        void* workspace, hipStream_t stream) {
   return topk_ragged_values_ex(scores, row_stride, lengths, row_offsets, num_rows, next_n, K, out_idx, out_val,
                                workspace, stream, nullptr);
+}
+
+int topk_ragged_bf16_ex(const uint16_t* scores, int64_t row_stride, const int32_t* lengths,
+                        const int32_t* row_offsets, int32_t num_rows, int32_t next_n, int32_t K, int32_t* out_idx,
+                        float* out_val, void* workspace, hipStream_t stream, const topk_overrides* ov) {
+  if (reinterpret_cast<uintptr_t>(scores) % 2 != 0) return fail(TOPK_EINVAL, "bf16 scores must be 2-byte aligned");
+  if (reinterpret_cast<uintptr_t>(out_val) % 4 != 0) return fail(TOPK_EINVAL, "out_val must be 4-byte aligned");
+  return launch(scores, row_stride, lengths, row_offsets, num_rows, next_n, K, out_idx, workspace, stream, ov,
+                out_val, true);
+}
+
+int topk_ragged_bf16(const uint16_t* scores, int64_t row_stride, const int32_t* lengths, const int32_t* row_offsets,
+                     int32_t num_rows, int32_t next_n, int32_t K, int32_t* out_idx, float* out_val,
+                     void* workspace, hipStream_t stream) {
+  return topk_ragged_bf16_ex(scores, row_stride, lengths, row_offsets, num_rows, next_n, K, out_idx, out_val,
+                             workspace, stream, nullptr);
 }
 
 int topk_ragged_offsets_ex(const float* scores, int64_t row_stride, const int32_t* lengths,

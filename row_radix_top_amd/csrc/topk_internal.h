@@ -91,7 +91,7 @@ inline constexpr uint64_t split_block_bytes(int split_g, int cap) {
 }
 
 struct KernelParams {
-  const float* scores;
+  const void* scores;          // fp32, or bf16 as uint16_t bits (the kernel instance says which)
   const int32_t* lengths;
   const int32_t* row_offsets;  // nullable: added to each row's chosen indices
   float* out_val;              // nullable: the chosen scores, [num_rows, K]
@@ -117,7 +117,8 @@ struct KernelParams {
 // streaming-read reference (idx16 ignored), 4 single with split rows.
 // vals: the one-workgroup instance that also writes the chosen scores (the
 // multi-workgroup kernel always can).
-const void* kernel_ptr(int path, int vec, bool idx16, bool vals = false);
+// bf16: the instance that reads bf16 scores (vec 8 or 1).
+const void* kernel_ptr(int path, int vec, bool idx16, bool vals = false, bool bf16 = false);
 const void* zero_kernel_ptr();
 const void* keys_kernel_ptr();
 const void* pack_kernel_ptr();

@@ -664,42 +664,68 @@ __device__ __forceinline__ void final_select(Smem<I16>& sm, const Slice& sl, uin
 // Streaming filter over [c0, c1) of one row
 // ---------------------------------------------------------------------------
 
-// One full tile starting at `tile` (a wave-uniform pointer): thread t loads
-// elements u * 256 * VEC + t * VEC .. + VEC - 1, so each load instruction of a
-// wave covers one contiguous 64 * VEC * 4-byte run.
-template <int VEC>
-__device__ __forceinline__ void load_full(const float* __restrict__ tile, float (&x)[kElems]) {
-  const uint32_t t = threadIdx.x;
-#pragma unroll
-  for (int u = 0; u < kElems / VEC; ++u) {
-    const uint32_t pos = (uint32_t)u * (kBlock * VEC) + t * VEC;
+// Scores are fp32 or bf16 (kept as its 16 bits).  Either way they enter the
+// registers as fp32: widening bf16 shifts its bits up, which is exact, so
+// every later step sees the same values and keys.
+__device__ __forceinline__ float widen(float v) { return v; }
+__device__ __forceinline__ float widen(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// VEC consecutive elements at p (aligned to VEC elements) into x[o .. o + VEC).
+template <int VEC, typename T>
+__device__ __forceinline__ void load_run(const T* __restrict__ p, float (&x)[kElems], int o) {
+  if constexpr (std::is_same<T, float>::value) {
+    static_assert(VEC == 4 || VEC == 2 || VEC == 1, "fp32 loads of 16, 8 or 4 bytes");
     if constexpr (VEC == 4) {
-      const float4 v = *reinterpret_cast<const float4*>(tile + pos);
-      x[u * 4 + 0] = v.x;
-      x[u * 4 + 1] = v.y;
-      x[u * 4 + 2] = v.z;
-      x[u * 4 + 3] = v.w;
+      const float4 v = *reinterpret_cast<const float4*>(p);
+      x[o + 0] = v.x;
+      x[o + 1] = v.y;
+      x[o + 2] = v.z;
+      x[o + 3] = v.w;
     } else if constexpr (VEC == 2) {
-      const float2 v = *reinterpret_cast<const float2*>(tile + pos);
-      x[u * 2 + 0] = v.x;
-      x[u * 2 + 1] = v.y;
+      const float2 v = *reinterpret_cast<const float2*>(p);
+      x[o + 0] = v.x;
+      x[o + 1] = v.y;
     } else {
-      x[u] = tile[pos];
+      x[o] = *p;
+    }
+  } else {
+    static_assert(std::is_same<T, uint16_t>::value && (VEC == 8 || VEC == 1), "bf16 loads of 16 or 2 bytes");
+    if constexpr (VEC == 8) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+      x[o + 0] = __uint_as_float(v.x << 16);
+      x[o + 1] = __uint_as_float(v.x & 0xffff0000u);
+      x[o + 2] = __uint_as_float(v.y << 16);
+      x[o + 3] = __uint_as_float(v.y & 0xffff0000u);
+      x[o + 4] = __uint_as_float(v.z << 16);
+      x[o + 5] = __uint_as_float(v.z & 0xffff0000u);
+      x[o + 6] = __uint_as_float(v.w << 16);
+      x[o + 7] = __uint_as_float(v.w & 0xffff0000u);
+    } else {
+      x[o] = widen(*p);
     }
   }
 }
 
+// One full tile starting at `tile` (a wave-uniform pointer): thread t loads
+// elements u * 256 * VEC + t * VEC .. + VEC - 1, so each load instruction of a
+// wave covers one contiguous run of 64 * VEC elements.
+template <int VEC, typename T>
+__device__ __forceinline__ void load_full(const T* __restrict__ tile, float (&x)[kElems]) {
+  const uint32_t t = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < kElems / VEC; ++u) load_run<VEC>(tile + (uint32_t)u * (kBlock * VEC) + t * VEC, x, u * VEC);
+}
+
 // The partial last tile [p0, c1): per-element bounds checks, nothing read at
 // or past c1.
-template <int VEC>
-__device__ __forceinline__ void load_tail(const float* __restrict__ rowp, uint32_t c1, uint32_t p0,
-                                          float (&x)[kElems]) {
+template <int VEC, typename T>
+__device__ __forceinline__ void load_tail(const T* __restrict__ rowp, uint32_t c1, uint32_t p0, float (&x)[kElems]) {
   const uint32_t t = threadIdx.x;
 #pragma unroll
   for (int u = 0; u < kElems / VEC; ++u) {
     const uint32_t pos = p0 + (uint32_t)u * (kBlock * VEC) + t * VEC;
 #pragma unroll
-    for (int c = 0; c < VEC; ++c) x[u * VEC + c] = (pos + c < c1) ? rowp[pos + c] : 0.0f;
+    for (int c = 0; c < VEC; ++c) x[u * VEC + c] = (pos + c < c1) ? widen(rowp[pos + c]) : 0.0f;
   }
 }
 
@@ -865,8 +891,8 @@ __device__ __forceinline__ uint32_t spec_bound(Smem<I16>& sm, float (&x0)[kElems
 // go through x0 and x1 ahead of the ring, which starts at tile 2 with its
 // loads issued before the bound is computed; with preloaded they were
 // already loaded by the caller.
-template <bool I16, int VEC>
-__device__ __forceinline__ void stream_chunk(Smem<I16>& sm, const float* __restrict__ rowp, uint32_t c0,
+template <bool I16, int VEC, typename T>
+__device__ __forceinline__ void stream_chunk(Smem<I16>& sm, const T* __restrict__ rowp, uint32_t c0,
                                              uint32_t c1, uint32_t keep, uint32_t& cnt, uint32_t& L,
                                              uint32_t spec, float (&x0)[kElems], float (&x1)[kElems],
                                              bool preloaded) {
@@ -879,7 +905,7 @@ __device__ __forceinline__ void stream_chunk(Smem<I16>& sm, const float* __restr
   st.bf = accept_floor(st.L);
   st.par = 0;
   const uint32_t F = (c1 - c0) / kTile;  // full tiles
-  const float* base = rowp + c0;
+  const T* base = rowp + c0;
   const bool pre = uni(spec) != 0u && F >= 2u;
   const uint32_t j1 = pre ? 2u : 0u;  // first tile of the ring
   if (pre && !preloaded) {
@@ -967,38 +993,23 @@ __device__ __forceinline__ bool wave_mode(uint32_t n, uint32_t K) {
 
 // One full wave tile at `tile` (wave-uniform): lane l loads elements
 // u * 64 * VEC + l * VEC .. + VEC - 1.
-template <int VEC>
-__device__ __forceinline__ void load_wave_full(const float* __restrict__ tile, float (&x)[kElems]) {
+template <int VEC, typename T>
+__device__ __forceinline__ void load_wave_full(const T* __restrict__ tile, float (&x)[kElems]) {
   const uint32_t l = threadIdx.x & 63;
 #pragma unroll
-  for (int u = 0; u < kElems / VEC; ++u) {
-    const uint32_t pos = (uint32_t)u * (64u * VEC) + l * VEC;
-    if constexpr (VEC == 4) {
-      const float4 v = *reinterpret_cast<const float4*>(tile + pos);
-      x[u * 4 + 0] = v.x;
-      x[u * 4 + 1] = v.y;
-      x[u * 4 + 2] = v.z;
-      x[u * 4 + 3] = v.w;
-    } else if constexpr (VEC == 2) {
-      const float2 v = *reinterpret_cast<const float2*>(tile + pos);
-      x[u * 2 + 0] = v.x;
-      x[u * 2 + 1] = v.y;
-    } else {
-      x[u] = tile[pos];
-    }
-  }
+  for (int u = 0; u < kElems / VEC; ++u) load_run<VEC>(tile + (uint32_t)u * (64u * VEC) + l * VEC, x, u * VEC);
 }
 
 // The partial last wave tile [p0, end): nothing read at or past end.
-template <int VEC>
-__device__ __forceinline__ void load_wave_tail(const float* __restrict__ rowp, uint32_t end, uint32_t p0,
+template <int VEC, typename T>
+__device__ __forceinline__ void load_wave_tail(const T* __restrict__ rowp, uint32_t end, uint32_t p0,
                                                float (&x)[kElems]) {
   const uint32_t l = threadIdx.x & 63;
 #pragma unroll
   for (int u = 0; u < kElems / VEC; ++u) {
     const uint32_t pos = p0 + (uint32_t)u * (64u * VEC) + l * VEC;
 #pragma unroll
-    for (int c = 0; c < VEC; ++c) x[u * VEC + c] = (pos + c < end) ? rowp[pos + c] : 0.0f;
+    for (int c = 0; c < VEC; ++c) x[u * VEC + c] = (pos + c < end) ? widen(rowp[pos + c]) : 0.0f;
   }
 }
 
@@ -1054,8 +1065,8 @@ __device__ __forceinline__ void wave_tile(Smem<I16>& sm, const float (&x)[kElems
 // the four quarters for the speculative bound.  Returns false if the row must
 // be streamed again on the general path; otherwise mine is this
 // wavefront's number of candidates (in slots [w * SUB, w * SUB + mine)).
-template <bool I16, int VEC>
-__device__ __forceinline__ bool stream_row_waves(Smem<I16>& sm, const float* __restrict__ rowp, uint32_t n,
+template <bool I16, int VEC, typename T>
+__device__ __forceinline__ bool stream_row_waves(Smem<I16>& sm, const T* __restrict__ rowp, uint32_t n,
                                                  uint32_t K, float (&x0)[kElems], float (&x1)[kElems],
                                                  bool preloaded, uint32_t& mine) {
   constexpr int PF = kPrefetch;
@@ -1067,7 +1078,7 @@ __device__ __forceinline__ bool stream_row_waves(Smem<I16>& sm, const float* __r
   const uint32_t Q = quarter_of(n);
   const uint32_t qs = w * Q;
   const uint32_t qe = qs + Q < n ? qs + Q : n;
-  const float* qp = rowp + qs;
+  const T* qp = rowp + qs;
   if (!preloaded) {
     load_wave_full<VEC>(qp, x0);
     load_wave_full<VEC>(qp + WT, x1);
@@ -1170,8 +1181,8 @@ __device__ __forceinline__ bool splits(uint32_t n, uint32_t K, uint32_t chunk) {
 // unless preloaded).  Returns false if a wavefront's part of the buffer
 // overflowed; otherwise mine / off are this wavefront's candidate count and
 // its offset among the chunk's total (in slots [w * SUB, w * SUB + mine)).
-template <bool I16, int VEC>
-__device__ __forceinline__ bool stream_piece_waves(Smem<I16>& sm, const float* __restrict__ rowp, uint32_t n,
+template <bool I16, int VEC, typename T>
+__device__ __forceinline__ bool stream_piece_waves(Smem<I16>& sm, const T* __restrict__ rowp, uint32_t n,
                                                    uint32_t K, uint32_t c0, uint32_t c1, float (&x0)[kElems],
                                                    float (&x1)[kElems], bool preloaded, uint32_t& mine,
                                                    uint32_t& off, uint32_t& total, uint32_t& L) {
@@ -1184,7 +1195,7 @@ __device__ __forceinline__ bool stream_piece_waves(Smem<I16>& sm, const float* _
   c1 = uni(c1);
   const uint32_t w = uni(threadIdx.x >> 6);
   if (!preloaded) {
-    const float* sp = rowp + w * quarter_of(n);
+    const T* sp = rowp + w * quarter_of(n);
     load_wave_full<VEC>(sp, x0);
     load_wave_full<VEC>(sp + WT, x1);
     __builtin_amdgcn_sched_barrier(0);
@@ -1193,7 +1204,7 @@ __device__ __forceinline__ bool stream_piece_waves(Smem<I16>& sm, const float* _
   const uint32_t qs = c0 + w * q;  // at or past c1 when the range has fewer quarters
   const uint32_t qe = qs + q < c1 ? qs + q : c1;
   const uint32_t F = qe > qs ? (qe - qs) / WT : 0u;
-  const float* qp = rowp + qs;
+  const T* qp = rowp + qs;
   float buf[PF][kElems];
   if (F > 0u) {
 #pragma unroll
@@ -1350,6 +1361,12 @@ __device__ __forceinline__ uint32_t merge_pieces(Smem<I16>& sm, uint32_t* blk, u
   return total;
 }
 
+// Row r of the scores, as elements of type T.
+template <typename T>
+__device__ __forceinline__ const T* row_of(const KernelParams& p, int64_t r) {
+  return static_cast<const T*>(p.scores) + r * p.row_stride;
+}
+
 __device__ __forceinline__ int64_t clamp_len(const KernelParams& p, int row) {
   int64_t n = p.lengths[row];
   n = n < 0 ? 0 : n;
@@ -1357,12 +1374,13 @@ __device__ __forceinline__ int64_t clamp_len(const KernelParams& p, int row) {
 }
 
 // n <= K: every valid index (plus the row's offset), then -1.  Reads no scores.
-// With vout, the n scores themselves (read from rowp) and -inf after them.
+// With vout, the n scores themselves (read from rowp, as fp32) and -inf after them.
+template <typename T = float>
 __device__ __forceinline__ void write_all_then_pad(int32_t* out, int64_t n, int K, uint32_t off,
-                                                   float* vout = nullptr, const float* rowp = nullptr) {
+                                                   float* vout = nullptr, const T* rowp = nullptr) {
   for (int i = threadIdx.x; i < K; i += kBlock) {
     out[i] = i < n ? (int32_t)(off + (uint32_t)i) : -1;
-    if (vout != nullptr) vout[i] = i < n ? rowp[i] : -__builtin_huge_valf();
+    if (vout != nullptr) vout[i] = i < n ? widen(rowp[i]) : -__builtin_huge_valf();
   }
 }
 
@@ -1410,7 +1428,8 @@ __device__ __forceinline__ void unit_of(const KernelParams& p, uint32_t u, int& 
 // the split-row code is compiled out (it costs registers the row loop needs).
 // VALS: the launch also writes the chosen scores (compiled out otherwise, for
 // the same reason).
-template <int VEC, bool I16, bool SPLIT, bool VALS>
+// T: the score type (float, or uint16_t holding bf16).
+template <int VEC, bool I16, bool SPLIT, bool VALS, typename T>
 __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_kernel(KernelParams p) {
   __shared__ Smem<I16> sm;
   zero_histograms(sm);
@@ -1460,11 +1479,11 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_ker
       // Chunk of a row taken whole by its chunk 0: nothing to do.
     } else if (n <= (int64_t)K) {
       if constexpr (VALS)
-        write_all_then_pad(out, n, p.K, off, p.out_val + (int64_t)row * p.K, p.scores + (int64_t)row * p.row_stride);
+        write_all_then_pad<T>(out, n, p.K, off, p.out_val + (int64_t)row * p.K, row_of<T>(p, row));
       else
         write_all_then_pad(out, n, p.K, off);
     } else {
-      const float* rowp = p.scores + (int64_t)row * p.row_stride;
+      const T* rowp = row_of<T>(p, row);
       uint32_t g0 = 0, g1 = (uint32_t)n, gL = 0;  // general path: range, starting bound
       bool general = true;
       uint32_t mine = 0, off = 0;
@@ -1574,9 +1593,9 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_ker
       // The next unit's first two tiles: per wavefront quarter (the row's
       // sample) when it will go wave by wave or is a chunk, else the row's
       // first two tiles.
-      const float* nrowp = p.scores + (int64_t)nrow * p.row_stride;
+      const T* nrowp = row_of<T>(p, nrow);
       if (wave_mode((uint32_t)nn, K)) {
-        const float* qp = nrowp + uni(threadIdx.x >> 6) * quarter_of((uint32_t)nn);
+        const T* qp = nrowp + uni(threadIdx.x >> 6) * quarter_of((uint32_t)nn);
         load_wave_full<VEC>(qp, x0);
         load_wave_full<VEC>(qp + kWaveTile, x1);
       } else {
@@ -1660,7 +1679,7 @@ __device__ __forceinline__ int list_of(const uint32_t* off, int n, uint32_t i) {
   return lo;
 }
 
-template <int VEC, bool I16>
+template <int VEC, bool I16, typename E>
 __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_multi_kernel(KernelParams p) {
   __shared__ Smem<I16> sm;
   __shared__ uint32_t s_off[kMaxGroup + 1];
@@ -1682,8 +1701,8 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_multi_kern
   int32_t* out = p.out + (int64_t)row * p.K;
   if (n <= (int64_t)K) {
     if (g == 0)
-      write_all_then_pad(out, n, p.K, offset_of(p, row), p.out_val != nullptr ? p.out_val + (int64_t)row * p.K : nullptr,
-                         p.scores + (int64_t)row * p.row_stride);
+      write_all_then_pad<E>(out, n, p.K, offset_of(p, row),
+                            p.out_val != nullptr ? p.out_val + (int64_t)row * p.K : nullptr, row_of<E>(p, row));
     return;
   }
   const int grow = (int)((n + p.chunk - 1) / p.chunk);  // workgroups with data in this row
@@ -1705,7 +1724,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_multi_kern
 
   const int64_t c0 = (int64_t)g * p.chunk;
   const int64_t c1 = c0 + p.chunk < n ? c0 + p.chunk : n;
-  const float* rowp = p.scores + (int64_t)row * p.row_stride;
+  const E* rowp = row_of<E>(p, row);
   uint32_t cnt = 0, L = 0;
   float x0[kElems], x1[kElems];
   stream_chunk<I16, VEC>(sm, rowp, (uint32_t)c0, (uint32_t)c1, K, cnt, L, 0u, x0, x1, false);
@@ -1900,14 +1919,14 @@ __device__ __forceinline__ uint32_t tile_max(const float (&x)[kElems], uint32_t 
   return m;
 }
 
-template <int VEC>
+template <int VEC, typename T>
 __global__ void __launch_bounds__(kBlock) read_ref_kernel(KernelParams p) {
   __shared__ uint32_t wmax[kWaves];
   constexpr int PF = kPrefetch;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (int row = blockIdx.x; row < p.num_rows; row += gridDim.x) {
     const uint32_t n = (uint32_t)clamp_len(p, row);
-    const float* rowp = p.scores + (int64_t)row * p.row_stride;
+    const T* rowp = row_of<T>(p, row);
     const uint32_t F = n / kTile;
     uint32_t m = 0;
     if (F > 0) {
@@ -2022,41 +2041,27 @@ __global__ void keys_kernel(const uint32_t* bits, uint32_t* keys, int64_t n) {
 // Instance table
 // ---------------------------------------------------------------------------
 
-template <bool I16>
-static const void* pick(int path, int vec, bool vals) {
-  if (path == 3) {
-    if (vec == 4) return reinterpret_cast<const void*>(&read_ref_kernel<4>);
-    if (vec == 2) return reinterpret_cast<const void*>(&read_ref_kernel<2>);
-    return reinterpret_cast<const void*>(&read_ref_kernel<1>);
-  }
-  if (path == 1 || path == 4) {
-    const bool sp = path == 4;
-    if (sp && vals) {
-      if (vec == 4) return reinterpret_cast<const void*>(&topk_single_kernel<4, I16, true, true>);
-      if (vec == 2) return reinterpret_cast<const void*>(&topk_single_kernel<2, I16, true, true>);
-      return reinterpret_cast<const void*>(&topk_single_kernel<1, I16, true, true>);
-    }
-    if (sp) {
-      if (vec == 4) return reinterpret_cast<const void*>(&topk_single_kernel<4, I16, true, false>);
-      if (vec == 2) return reinterpret_cast<const void*>(&topk_single_kernel<2, I16, true, false>);
-      return reinterpret_cast<const void*>(&topk_single_kernel<1, I16, true, false>);
-    }
-    if (vals) {
-      if (vec == 4) return reinterpret_cast<const void*>(&topk_single_kernel<4, I16, false, true>);
-      if (vec == 2) return reinterpret_cast<const void*>(&topk_single_kernel<2, I16, false, true>);
-      return reinterpret_cast<const void*>(&topk_single_kernel<1, I16, false, true>);
-    }
-    if (vec == 4) return reinterpret_cast<const void*>(&topk_single_kernel<4, I16, false, false>);
-    if (vec == 2) return reinterpret_cast<const void*>(&topk_single_kernel<2, I16, false, false>);
-    return reinterpret_cast<const void*>(&topk_single_kernel<1, I16, false, false>);
-  }
-  if (vec == 4) return reinterpret_cast<const void*>(&topk_multi_kernel<4, I16>);
-  if (vec == 2) return reinterpret_cast<const void*>(&topk_multi_kernel<2, I16>);
-  return reinterpret_cast<const void*>(&topk_multi_kernel<1, I16>);
+template <int VEC, bool I16, typename T>
+static const void* pick_vec(int path, bool vals) {
+  if (path == 3) return reinterpret_cast<const void*>(&read_ref_kernel<VEC, T>);
+  if (path == 2) return reinterpret_cast<const void*>(&topk_multi_kernel<VEC, I16, T>);
+  const bool sp = path == 4;
+  if (sp && vals) return reinterpret_cast<const void*>(&topk_single_kernel<VEC, I16, true, true, T>);
+  if (sp) return reinterpret_cast<const void*>(&topk_single_kernel<VEC, I16, true, false, T>);
+  if (vals) return reinterpret_cast<const void*>(&topk_single_kernel<VEC, I16, false, true, T>);
+  return reinterpret_cast<const void*>(&topk_single_kernel<VEC, I16, false, false, T>);
 }
 
-const void* kernel_ptr(int path, int vec, bool idx16, bool vals) {
-  return idx16 ? pick<true>(path, vec, vals) : pick<false>(path, vec, vals);
+template <bool I16>
+static const void* pick(int path, int vec, bool vals, bool bf16) {
+  if (bf16) return vec == 8 ? pick_vec<8, I16, uint16_t>(path, vals) : pick_vec<1, I16, uint16_t>(path, vals);
+  if (vec == 4) return pick_vec<4, I16, float>(path, vals);
+  if (vec == 2) return pick_vec<2, I16, float>(path, vals);
+  return pick_vec<1, I16, float>(path, vals);
+}
+
+const void* kernel_ptr(int path, int vec, bool idx16, bool vals, bool bf16) {
+  return idx16 ? pick<true>(path, vec, vals, bf16) : pick<false>(path, vec, vals, bf16);
 }
 
 int lds_bytes_of(bool idx16) { return idx16 ? (int)sizeof(Smem<true>) : (int)sizeof(Smem<false>); }

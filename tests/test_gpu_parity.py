@@ -438,3 +438,75 @@ def test_strided_rows(layout):
         torch.cuda.synchronize()
         assert_same(gi.cpu().numpy(), ei, f"{layout} K={K} offsets")
         assert np.array_equal(gv.cpu().numpy().view(np.uint32), ev.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# bf16 scores (topk_ragged_bf16): the same selection on the exact widening
+# ---------------------------------------------------------------------------
+
+def _to_bf16(scores: np.ndarray):
+    import torch
+    t = torch.from_numpy(scores).to(torch.bfloat16)   # round to nearest even
+    return t, t.view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("name", ["small", "decode", "mtp", "long_k1024", "long_k2048", "prefill"])
+def test_bf16_workloads(name):
+    import torch
+    from oracle import topk_ragged_bf16_oracle
+    dev = torch.device("cuda:0")
+    w = workloads.make_workload(name)
+    tb, bits = _to_bf16(w.scores)
+    # bf16 tails of random bits, as for fp32 (never read)
+    rng = np.random.default_rng(9)
+    for r, n in enumerate(np.clip(w.flat_lengths, 0, w.row_stride)):
+        bits[r, n:] = rng.integers(0, 65536, size=w.row_stride - n, dtype=np.uint32).astype(np.uint16)
+    exp = topk_ragged_bf16_oracle(bits, w.lengths, w.K)
+    s = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    L = torch.from_numpy(w.flat_lengths).to(dev)
+    paths = [{}, dict(force_path=1)]
+    if name in ("mtp", "long_k2048"):
+        paths.append(dict(force_path=2))
+    for ov in paths:
+        ws = rrt.new_workspace(rrt.workspace_size(w.num_rows, w.row_stride, w.K, device=dev, **ov), dev)
+        got = rrt.topk_ragged_bf16(s, L, w.K, workspace=ws, next_n=w.next_n, **ov)
+        torch.cuda.synchronize()
+        assert_same(got.cpu().numpy(), exp, f"bf16 {name} {ov}")
+        assert ws is None or int(ws.count_nonzero().item()) == 0
+
+
+@pytest.mark.parametrize("offset", [0, 1])
+def test_bf16_edges_values_offsets(offset):
+    """Ties (bf16 keeps 8 bits of mantissa), signed zeros, lengths around K
+    and the tiles, 16- and 2-byte loads (offset 1 misaligns every row),
+    values and row offsets."""
+    import torch
+    from oracle import topk_ragged_bf16_oracle, topk_ragged_values_oracle, widen_bf16
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(13 + offset)
+    stride = 40000 if offset == 0 else 40001
+    lens = np.array([0, 1, 700, 2047, 2048, 2049, 16384, 16385, 30000, stride], dtype=np.int32)
+    x = rng.standard_normal((len(lens), stride)).astype(np.float32)
+    x[3] = np.where(rng.random(stride) < 0.5, -0.0, 0.0).astype(np.float32)
+    x[8] = rng.integers(-3, 3, size=stride).astype(np.float32)
+    _, bits = _to_bf16(x)
+    flat = np.zeros(bits.size + offset, dtype=np.uint16)
+    flat[offset:] = bits.reshape(-1)
+    buf = torch.from_numpy(flat.view(np.int16)).to(dev).view(torch.bfloat16)
+    s = buf[offset:].view(len(lens), stride)
+    L = torch.from_numpy(lens).to(dev)
+    n = np.clip(lens.astype(np.int64), 0, stride)
+    starts = np.concatenate([[0], np.cumsum(n)[:-1]])
+    ro = torch.from_numpy(starts.astype(np.int32)).to(dev)
+    for K in (1, 129, 2048):
+        exp = topk_ragged_bf16_oracle(bits, lens, K)
+        ws = rrt.new_workspace(rrt.workspace_size(len(lens), stride, K, device=dev), dev)
+        got = rrt.topk_ragged_bf16(s, L, K, workspace=ws)
+        torch.cuda.synchronize()
+        assert_same(got.cpu().numpy(), exp, f"bf16 edges offset={offset} K={K}")
+        ei, ev = topk_ragged_values_oracle(widen_bf16(bits), lens, K, starts)
+        vals = torch.empty((len(lens), K), dtype=torch.float32, device=dev)
+        gi, gv = rrt.topk_ragged_bf16(s, L, K, workspace=ws, out_values=vals, row_offsets=ro)
+        torch.cuda.synchronize()
+        assert_same(gi.cpu().numpy(), ei, f"bf16 values offset={offset} K={K}")
+        assert np.array_equal(gv.cpu().numpy().view(np.uint32), ev.view(np.uint32))

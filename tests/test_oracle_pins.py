@@ -286,3 +286,24 @@ def test_strided_rows_match_dense_copies():
     assert np.array_equal(got, topk_ragged_oracle(np.ascontiguousarray(wide[:, :2 * N:2]), lens, 64))
     got = topk_ragged_strided_oracle(wide, 2 * N + 3, 1, 2 * N + 3, R, lens, 64)
     assert np.array_equal(got, topk_ragged_oracle(wide, lens, 64))
+
+
+def test_bf16_widening_matches_torch():
+    """The oracle widens bf16 by shifting its bits; torch's own bf16 -> fp32
+    conversion must agree on every one of the 65536 bit patterns (NaNs
+    compared by NaN-ness), and the selection on a bf16 tensor converted by
+    torch must equal the oracle's."""
+    import torch
+    from oracle import topk_ragged_bf16_oracle, widen_bf16
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    mine = widen_bf16(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    rng = np.random.default_rng(5)
+    x = torch.from_numpy(rng.standard_normal((20, 3000)).astype(np.float32)).to(torch.bfloat16)
+    b = x.view(torch.int16).numpy().view(np.uint16)
+    lens = rng.integers(0, 3001, size=20).astype(np.int32)
+    for K in (1, 100, 3000):
+        assert np.array_equal(topk_ragged_bf16_oracle(b, lens, K), topk_ragged_oracle(x.float().numpy(), lens, K))
