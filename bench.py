@@ -280,7 +280,7 @@ def decode_latency(launches: int = 400):
 def extensions(w, scores, L, launches: int = 20):
     """Per-launch time of the extended entry points on the prefill-shaped
     batch, beside the plain launch: row offsets (a flat ragged layout),
-    values, bf16 scores (the same batch rounded), and a transposed view
+    values, K = 4096, bf16 scores (the same batch rounded), and a transposed view
     (each row packed from a column stride of num_rows, then selected)."""
     import torch
     import row_radix_top_amd as rrt
@@ -297,6 +297,12 @@ def extensions(w, scores, L, launches: int = 20):
         lambda i: rrt.topk_ragged(scores, L, w.K, out=out, workspace=ws, row_offsets=starts), launches) * 1e3, 2)
     res["values_us"] = round(time_launches(
         lambda i: rrt.topk_ragged_values(scores, L, w.K, out=out, out_values=vals, workspace=ws), launches) * 1e3, 2)
+    # K = 4096 (the large layout).
+    out4 = torch.empty((w.num_rows, 4096), dtype=torch.int32, device=dev)
+    ws4 = rrt.new_workspace(rrt.workspace_size(w.num_rows, w.row_stride, 4096, device=dev), dev)
+    res["k4096_us"] = round(time_launches(lambda i: rrt.topk_ragged(scores, L, 4096, out=out4, workspace=ws4),
+                                          launches) * 1e3, 2)
+    del out4, ws4
     # The same scores rounded to bf16 (half the bytes).
     sb = scores.to(torch.bfloat16)
     bf_us = time_launches(lambda i: rrt.topk_ragged_bf16(sb, L, w.K, out=out, workspace=ws), launches) * 1e3

@@ -49,7 +49,7 @@ typedef enum {
   TOPK_ELAUNCH = -5          /* the kernel launch reported an error */
 } topk_status;
 
-#define TOPK_RAGGED_MAX_K 2048
+#define TOPK_RAGGED_MAX_K 4096
 /* Rows whose stride exceeds this may be split over several workgroups that
  * cooperate through the workspace (the pages' RADIX_THRESHOLD of 32K with a
  * strict comparison: PR #41189 page, csrc/topk.cu excerpt and review notes). */
@@ -216,7 +216,8 @@ typedef enum {
 
 typedef struct {
   int32_t path;           /* topk_path */
-  int32_t kmax;           /* largest K the kernel instance handles (TOPK_RAGGED_MAX_K) */
+  int32_t kmax;           /* largest K the kernel instance handles: 2048, or 4096 for the
+                             large layout that K above 2048 takes */
   int32_t vec;            /* elements per load: 4, 2 or 1 (fp32), 8 or 1 (bf16) */
   int32_t block;          /* threads per workgroup */
   int32_t grid;           /* workgroups launched */
@@ -246,6 +247,8 @@ typedef struct {
   int64_t split_chunk;       /* 0 auto, else elements per chunk (a multiple of 2048) */
   int32_t max_occupancy;     /* 0 the device's, else plan as if no instance could keep more
                                 workgroups per CU resident (emulates a smaller device) */
+  int32_t force_idx32;       /* 1: never keep 16-bit candidate indices (testing; also what
+                                values with K above 2048 need) */
 } topk_overrides;
 
 /* Pure planning function (host only, no GPU needed).  vec_allowed is the

@@ -17,7 +17,7 @@ TOPK_OK = 0
 STATUS_NAMES = {0: "TOPK_OK", -1: "TOPK_EINVAL", -2: "TOPK_EUNSUPPORTED_K", -3: "TOPK_EWORKSPACE",
                 -4: "TOPK_EDEVICE", -5: "TOPK_ELAUNCH"}
 PATH_NONE, PATH_SINGLE, PATH_MULTI = 0, 1, 2
-MAX_K = 2048
+MAX_K = 4096
 RADIX_THRESHOLD = 32768
 
 # Every symbol include/topk_ragged.h declares.
@@ -55,7 +55,8 @@ class Overrides(ctypes.Structure):
                 ("max_grid", ctypes.c_int32), ("force_vec", ctypes.c_int32),
                 ("force_chunk", ctypes.c_int64), ("spin_limit", ctypes.c_uint32),
                 ("min_chunk", ctypes.c_int32), ("split_rows", ctypes.c_int32),
-                ("split_g", ctypes.c_int32), ("split_chunk", ctypes.c_int64), ("max_occupancy", ctypes.c_int32)]
+                ("split_g", ctypes.c_int32), ("split_chunk", ctypes.c_int64), ("max_occupancy", ctypes.c_int32),
+                ("force_idx32", ctypes.c_int32)]
 
     @classmethod
     def make(cls, **kw) -> "Overrides | None":

@@ -58,7 +58,7 @@ std::string describe(const topk_plan& p) {
 struct DevInfo {
   int num_cus = 0;
   int max_lds_block = 0;
-  std::map<std::tuple<int, int, int, int>, int> occ;  // (path, vec, idx16, bf16) -> WGs per CU
+  std::map<std::tuple<int, int, int, int, int>, int> occ;  // (path, vec, idx16, bf16, big K) -> WGs per CU
 };
 
 std::mutex g_mu;
@@ -88,9 +88,9 @@ int device_info(int dev, DevInfo** out) {
 }
 
 // Occupancy of the exact instance that will be launched.
-int occupancy(int dev, DevInfo* d, int path, int vec, bool idx16, int* occ, bool bf16 = false) {
+int occupancy(int dev, DevInfo* d, int path, int vec, bool idx16, int* occ, bool bf16 = false, bool big_k = false) {
   std::lock_guard<std::mutex> lk(g_mu);
-  const auto key = std::make_tuple(path, vec, idx16 ? 1 : 0, bf16 ? 1 : 0);
+  const auto key = std::make_tuple(path, vec, idx16 ? 1 : 0, bf16 ? 1 : 0, big_k ? 1 : 0);
   auto it = d->occ.find(key);
   if (it != d->occ.end()) {
     *occ = it->second;
@@ -101,7 +101,8 @@ int occupancy(int dev, DevInfo* d, int path, int vec, bool idx16, int* occ, bool
   if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
   int o = 0;
   if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, rrt::kernel_ptr(path, vec, idx16, false, bf16), rrt::kBlock, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, rrt::kernel_ptr(path, vec, idx16, false, bf16, big_k),
+                                                     rrt::kBlock, 0);
   if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
   if (e != hipSuccess) {
     char buf[256];
@@ -138,17 +139,18 @@ int chosen_vec(int vec_allowed, const topk_overrides* ov, int* vec) {
 }
 
 // Fills props for the load width vec of every kernel instance on device dev.
-int real_props(int dev, int vec, topk_device_props* props, bool bf16 = false) {
+// big_k: the instances of the large layout (K above 2048).
+int real_props(int dev, int vec, topk_device_props* props, bool bf16 = false, bool big_k = false) {
   DevInfo* d = nullptr;
   int rc = device_info(dev, &d);
   if (rc != TOPK_OK) return rc;
   std::memset(props, 0, sizeof(*props));
   props->num_cus = d->num_cus;
   props->max_lds_per_block = d->max_lds_block;
-  rc = occupancy(dev, d, 1, vec, false, &props->occupancy_single, bf16);
-  if (rc == TOPK_OK) rc = occupancy(dev, d, 2, vec, false, &props->occupancy_multi, bf16);
-  if (rc == TOPK_OK) rc = occupancy(dev, d, 1, vec, true, &props->occupancy_single16, bf16);
-  if (rc == TOPK_OK) rc = occupancy(dev, d, 2, vec, true, &props->occupancy_multi16, bf16);
+  rc = occupancy(dev, d, 1, vec, false, &props->occupancy_single, bf16, big_k);
+  if (rc == TOPK_OK) rc = occupancy(dev, d, 2, vec, false, &props->occupancy_multi, bf16, big_k);
+  if (rc == TOPK_OK) rc = occupancy(dev, d, 1, vec, true, &props->occupancy_single16, bf16, big_k);
+  if (rc == TOPK_OK) rc = occupancy(dev, d, 2, vec, true, &props->occupancy_multi16, bf16, big_k);
   return rc;
 }
 
@@ -177,7 +179,7 @@ int plan_for_call(const void* scores, int32_t num_rows, int64_t row_stride, int3
   rc = stream_device(stream, &dev);
   if (rc != TOPK_OK) return rc;
   topk_device_props props;
-  rc = real_props(dev, vec, &props, bf16);
+  rc = real_props(dev, vec, &props, bf16, K > rrt::kMaxK);
   if (rc != TOPK_OK) return rc;
   if (dev_out) *dev_out = dev;
   return topk_ragged_plan(&props, num_rows, row_stride, K, va, ov, plan);
@@ -210,7 +212,11 @@ int topk_ragged_plan(const topk_device_props* props_in, int32_t num_rows, int64_
   rc = chosen_vec(vec_allowed, ov, &vec);
   if (rc != TOPK_OK) return rc;
 
-  plan->kmax = TOPK_RAGGED_MAX_K;
+  // K above 2048 takes the large layout (more candidates, fewer workgroups
+  // per CU); props must then describe those instances.
+  const bool big = K > rrt::kMaxK;
+  const bool idx32_only = ov != nullptr && ov->force_idx32 != 0;
+  plan->kmax = rrt::kmax_of(rrt::layout_of(false, big));
   plan->vec = vec;
   plan->block = rrt::kBlock;
   plan->wg_per_row = 1;
@@ -278,8 +284,8 @@ int topk_ragged_plan(const topk_device_props* props_in, int32_t num_rows, int64_
       if (usable) {
         const int64_t grid = (int64_t)num_rows * G;
         if (grid <= avail) {
-          const bool i16 = chunk <= rrt::kIdx16Limit;
-          const rrt::GroupLayout lay = rrt::group_layout((int)G, rrt::cap_of(i16));
+          const bool i16 = chunk <= rrt::kIdx16Limit && !idx32_only;
+          const rrt::GroupLayout lay = rrt::group_layout((int)G, rrt::cap_of(rrt::layout_of(i16, big)));
           plan->path = TOPK_PATH_MULTI;
           plan->idx16 = i16 ? 1 : 0;
           plan->wg_per_row = (int)G;
@@ -287,7 +293,7 @@ int topk_ragged_plan(const topk_device_props* props_in, int32_t num_rows, int64_
           plan->grid = (int)grid;
           plan->resident_cap = (int)cap;
           plan->headroom = (int)headroom;
-          plan->lds_bytes = rrt::lds_bytes_of(i16);
+          plan->lds_bytes = rrt::lds_bytes_of(i16, big);
           plan->workspace_bytes = rrt::kWsHeader + (uint64_t)num_rows * lay.bytes;
           return TOPK_OK;
         }
@@ -300,7 +306,7 @@ int topk_ragged_plan(const topk_device_props* props_in, int32_t num_rows, int64_
     }
   }
 
-  const bool i16 = row_stride <= rrt::kIdx16Limit;
+  const bool i16 = row_stride <= rrt::kIdx16Limit && !idx32_only;
   const int occ = i16 ? props->occupancy_single16 : props->occupancy_single;
   if (occ < 1) return fail(TOPK_EDEVICE, "single-workgroup kernel cannot be resident");
   const int64_t cap = (int64_t)props->num_cus * occ;
@@ -350,12 +356,13 @@ int topk_ragged_plan(const topk_device_props* props_in, int32_t num_rows, int64_
   plan->resident_cap = (int)cap;
   plan->headroom = 0;
   plan->idx16 = i16 ? 1 : 0;
-  plan->lds_bytes = rrt::lds_bytes_of(i16);
+  plan->lds_bytes = rrt::lds_bytes_of(i16, big);
   // More units than workgroups: later units are handed out by a ticket
   // counter in the workspace header.  Split rows add a block each.
   plan->workspace_bytes = (units > grid || split_rows > 0) ? rrt::kWsHeader : 0;
   if (split_rows > 0)
-    plan->workspace_bytes += (uint64_t)split_rows * rrt::split_block_bytes((int)split_g, rrt::cap_of(i16));
+    plan->workspace_bytes +=
+        (uint64_t)split_rows * rrt::split_block_bytes((int)split_g, rrt::cap_of(rrt::layout_of(i16, big)));
   return TOPK_OK;
 }
 
@@ -417,6 +424,15 @@ int launch(const void* scores, int64_t row_stride, const int32_t* lengths, const
   if (reinterpret_cast<uintptr_t>(out_idx) % 4 != 0 || reinterpret_cast<uintptr_t>(lengths) % 4 != 0 ||
       reinterpret_cast<uintptr_t>(scores) % (bf16 ? 2 : 4) != 0 || reinterpret_cast<uintptr_t>(row_offsets) % 4 != 0)
     return fail(TOPK_EINVAL, "scores must be aligned to their element; lengths, row_offsets and out_idx to 4 bytes");
+  // Values with K above 2048: the large layout stages them over 32-bit
+  // indices only (the 16-bit index array is too small).
+  const bool big = K > rrt::kMaxK;
+  topk_overrides ov_idx32{};
+  if (out_val != nullptr && big) {
+    if (ov != nullptr) ov_idx32 = *ov;
+    ov_idx32.force_idx32 = 1;
+    ov = &ov_idx32;
+  }
   topk_plan plan;
   rc = plan_for_call(scores, num_rows, row_stride, K, ov, stream, nullptr, &plan, bf16);
   if (rc != TOPK_OK) return rc;
@@ -436,7 +452,7 @@ int launch(const void* scores, int64_t row_stride, const int32_t* lengths, const
   kp.row_stride = row_stride;
   kp.chunk = plan.chunk;
   kp.group_bytes = plan.path == TOPK_PATH_MULTI
-                       ? rrt::group_layout(plan.wg_per_row, rrt::cap_of(plan.idx16 != 0)).bytes
+                       ? rrt::group_layout(plan.wg_per_row, rrt::cap_of(rrt::layout_of(plan.idx16 != 0, big))).bytes
                        : 0;
   kp.num_rows = num_rows;
   kp.K = K;
@@ -445,7 +461,8 @@ int launch(const void* scores, int64_t row_stride, const int32_t* lengths, const
   kp.split_from = num_rows - plan.split_rows;
   kp.split_g = plan.split_rows > 0 ? plan.split_g : 1;
   kp.split_chunk = plan.split_rows > 0 ? plan.split_chunk : row_stride;
-  kp.split_bytes = plan.split_rows > 0 ? rrt::split_block_bytes(plan.split_g, rrt::cap_of(plan.idx16 != 0)) : 0;
+  kp.split_bytes =
+      plan.split_rows > 0 ? rrt::split_block_bytes(plan.split_g, rrt::cap_of(rrt::layout_of(plan.idx16 != 0, big))) : 0;
   kp.num_units = (uint32_t)(kp.split_from + (int64_t)plan.split_rows * kp.split_g);
 
   if (verbose()) std::fprintf(stderr, "[topk_ragged] rows=%d stride=%lld K=%d %s\n", num_rows,
@@ -454,7 +471,8 @@ int launch(const void* scores, int64_t row_stride, const int32_t* lengths, const
   // Split rows run on the one-workgroup kernel's split instance (same
   // occupancy: both are held to the same register and LDS budget).
   const int kpath = (plan.path == TOPK_PATH_SINGLE && plan.split_rows > 0) ? 4 : plan.path;
-  const void* fn = rrt::kernel_ptr(kpath, plan.vec, plan.idx16 != 0, out_val != nullptr, bf16);
+  const void* fn = rrt::kernel_ptr(kpath, plan.vec, plan.idx16 != 0, out_val != nullptr, bf16, big);
+  if (fn == nullptr) return fail(TOPK_EINVAL, "no kernel instance for this plan (" + describe(plan) + ")");
   hipError_t e = hipLaunchKernel(fn, dim3(plan.grid), dim3(plan.block), args, 0, stream);
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) {

@@ -38,7 +38,17 @@ constexpr uint32_t kSpecMinLen = 16384;
 // and four workgroups fit in a CU's 160 KB of LDS; with 32-bit indices,
 // three.
 constexpr int kIdx16Limit = 65536;
-constexpr int cap_of(bool) { return 5120; }
+
+// Buffer layout of a kernel instance (a bit set): 16-bit candidate indices,
+// and room for K up to kMaxKBig.  The large layout holds 7168 candidates:
+// K plus a tile, and 1792 per wavefront for the ~1.5 K that survive a
+// speculative bound; its LDS footprint leaves two workgroups per CU.
+constexpr int kLayIdx16 = 1;
+constexpr int kLayBigK = 2;
+constexpr int kMaxKBig = 4096;
+constexpr int layout_of(bool idx16, bool big_k) { return (idx16 ? kLayIdx16 : 0) | (big_k ? kLayBigK : 0); }
+constexpr int cap_of(int lay) { return (lay & kLayBigK) ? 7168 : 5120; }
+constexpr int kmax_of(int lay) { return (lay & kLayBigK) ? kMaxKBig : kMaxK; }
 
 // Rows are split over several workgroups only when longer than this (the
 // one-workgroup path streams shorter rows wave by wave faster than any
@@ -117,11 +127,12 @@ struct KernelParams {
 // streaming-read reference (idx16 ignored), 4 single with split rows.
 // vals: the one-workgroup instance that also writes the chosen scores (the
 // multi-workgroup kernel always can).
-// bf16: the instance that reads bf16 scores (vec 8 or 1).
-const void* kernel_ptr(int path, int vec, bool idx16, bool vals = false, bool bf16 = false);
+// bf16: the instance that reads bf16 scores (vec 8 or 1); big_k: the large
+// layout (K up to kMaxKBig).
+const void* kernel_ptr(int path, int vec, bool idx16, bool vals = false, bool bf16 = false, bool big_k = false);
 const void* zero_kernel_ptr();
 const void* keys_kernel_ptr();
 const void* pack_kernel_ptr();
-int lds_bytes_of(bool idx16);
+int lds_bytes_of(bool idx16, bool big_k = false);
 
 }  // namespace rrt

@@ -134,25 +134,32 @@ __device__ __forceinline__ uint32_t uni(uint32_t v) { return (uint32_t)__builtin
 // Shared memory of one workgroup
 // ---------------------------------------------------------------------------
 
-template <bool I16>
+template <int LAY>
 struct Shape {
-  static constexpr int kCap = cap_of(I16);
+  static constexpr bool kIdx16 = (LAY & kLayIdx16) != 0;
+  static constexpr int kMaxK = kmax_of(LAY);
+  static constexpr int kCap = cap_of(LAY);
   static constexpr int kSlots = kCap / kBlock;  // buffer entries owned per thread
-  using Idx = typename std::conditional<I16, uint16_t, uint32_t>::type;
+  // Entries of the first histogram, which also stages the output ranks.
+  static constexpr int kStage = kMaxK > kBins ? kMaxK : kBins;
+  using Idx = typename std::conditional<kIdx16, uint16_t, uint32_t>::type;
   static_assert(kCap % kBlock == 0 && kSlots % 4 == 0, "capacity must tile the workgroup in aligned runs");
   static_assert(kCap % (kWaves * 64) == 0 && kCap / kWaves <= 64 * kSlots, "a wavefront's quarter fits its slices");
   static_assert(kCap < 65536, "packed 16-bit counts");
   static_assert(kCap >= kMaxK + kTile, "a tile must fit after a compaction");
+  // Chosen scores are staged over the index array (see emit_chosen): the
+  // large layout with 16-bit indices has no room for them.
+  static constexpr bool kValues = (size_t)kCap * sizeof(Idx) >= 4u * (size_t)kMaxK;
   // Workgroups per CU the LDS footprint allows (160 KB per CU); the register
   // budget is held to match.
-  static constexpr int kResident = I16 ? 4 : 3;
+  static constexpr int kResident = (LAY & kLayBigK) ? 2 : (kIdx16 ? 4 : 3);
 };
 
-template <bool I16>
+template <int LAY>
 struct __align__(16) Smem {
-  uint32_t val[Shape<I16>::kCap];                 // candidate fp32 bits, index order
-  typename Shape<I16>::Idx idx[Shape<I16>::kCap];  // their indices, relative to the chunk start
-  uint32_t hist1[kBins];                          // digit histogram; all-zero outside a selection
+  uint32_t val[Shape<LAY>::kCap];                 // candidate fp32 bits, index order
+  typename Shape<LAY>::Idx idx[Shape<LAY>::kCap];  // their indices, relative to the chunk start
+  uint32_t hist1[Shape<LAY>::kStage];             // digit histogram; all-zero outside a selection
   uint32_t hs[kSmallBins];                        // second digit histogram; all-zero outside a selection
   uint32_t red[2 * kWaves];                       // per-wave partial results
   uint32_t tile_cnt[2][kElems][kWaves];
@@ -221,8 +228,8 @@ __device__ __forceinline__ Found wave_find(const uint32_t* hist, uint32_t krem) 
 
 // Exclusive prefix sum of v over the workgroup in thread order; *total gets
 // the sum.  Contains one barrier.
-template <bool I16>
-__device__ __forceinline__ uint32_t block_excl_scan(Smem<I16>& sm, uint32_t v, uint32_t* total) {
+template <int LAY>
+__device__ __forceinline__ uint32_t block_excl_scan(Smem<LAY>& sm, uint32_t v, uint32_t* total) {
   const uint32_t t = tid();
   const int lane = t & 63, w = t >> 6;
   const uint32_t incl = wave_incl_scan(v);
@@ -271,9 +278,9 @@ struct Slice {
 
 // The buffer as filled by the general path: cnt entries in slots [0, cnt),
 // cut into 256 equal slices just large enough to cover them.
-template <bool I16>
+template <int LAY>
 __device__ __forceinline__ Slice plain_slice(uint32_t cnt) {
-  constexpr uint32_t S = (uint32_t)Shape<I16>::kSlots;
+  constexpr uint32_t S = (uint32_t)Shape<LAY>::kSlots;
   cnt = uni(cnt);
   uint32_t sp = (cnt + kBlock - 1) / kBlock;
   sp = (sp + 1u) & ~1u;
@@ -288,10 +295,10 @@ __device__ __forceinline__ Slice plain_slice(uint32_t cnt) {
 
 // The buffer as filled wave by wave: this wavefront's cw entries in slots
 // [w * SUB, w * SUB + cw), cut into 64 slices, one per lane.
-template <bool I16>
+template <int LAY>
 __device__ __forceinline__ Slice wave_slice(uint32_t cw) {
-  constexpr uint32_t S = (uint32_t)Shape<I16>::kSlots;
-  constexpr uint32_t SUB = (uint32_t)Shape<I16>::kCap / kWaves;
+  constexpr uint32_t S = (uint32_t)Shape<LAY>::kSlots;
+  constexpr uint32_t SUB = (uint32_t)Shape<LAY>::kCap / kWaves;
   cw = uni(cw);
   uint32_t sp = (cw + 63u) / 64u;
   sp = (sp + 1u) & ~1u;
@@ -307,9 +314,9 @@ __device__ __forceinline__ Slice wave_slice(uint32_t cw) {
 }
 
 // Keys of this thread's slice.
-template <bool I16>
-__device__ __forceinline__ void load_keys(const Smem<I16>& sm, uint32_t (&k)[Shape<I16>::kSlots], const Slice& sl) {
-  constexpr int S = Shape<I16>::kSlots;
+template <int LAY>
+__device__ __forceinline__ void load_keys(const Smem<LAY>& sm, uint32_t (&k)[Shape<LAY>::kSlots], const Slice& sl) {
+  constexpr int S = Shape<LAY>::kSlots;
 #pragma unroll
   for (int q = 0; q < S / 2; ++q) {
     if ((uint32_t)(2 * q) < sl.sp) {
@@ -321,9 +328,9 @@ __device__ __forceinline__ void load_keys(const Smem<I16>& sm, uint32_t (&k)[Sha
 }
 
 // The fp32 bits of this thread's slice, as stored.
-template <bool I16>
-__device__ __forceinline__ void load_bits(const Smem<I16>& sm, uint32_t (&v)[Shape<I16>::kSlots], const Slice& sl) {
-  constexpr int S = Shape<I16>::kSlots;
+template <int LAY>
+__device__ __forceinline__ void load_bits(const Smem<LAY>& sm, uint32_t (&v)[Shape<LAY>::kSlots], const Slice& sl) {
+  constexpr int S = Shape<LAY>::kSlots;
 #pragma unroll
   for (int q = 0; q < S / 2; ++q) {
     if ((uint32_t)(2 * q) < sl.sp) {
@@ -334,13 +341,13 @@ __device__ __forceinline__ void load_bits(const Smem<I16>& sm, uint32_t (&v)[Sha
   }
 }
 
-template <bool I16>
-__device__ __forceinline__ void load_idx(const Smem<I16>& sm, uint32_t (&ix)[Shape<I16>::kSlots], const Slice& sl) {
-  constexpr int S = Shape<I16>::kSlots;
+template <int LAY>
+__device__ __forceinline__ void load_idx(const Smem<LAY>& sm, uint32_t (&ix)[Shape<LAY>::kSlots], const Slice& sl) {
+  constexpr int S = Shape<LAY>::kSlots;
 #pragma unroll
   for (int q = 0; q < S / 2; ++q) {
     if ((uint32_t)(2 * q) < sl.sp) {
-      if constexpr (I16) {
+      if constexpr (Shape<LAY>::kIdx16) {
         const uint32_t a = *reinterpret_cast<const uint32_t*>(&sm.idx[sl.base + 2 * q]);
         ix[2 * q + 0] = a & 0xffffu;
         ix[2 * q + 1] = a >> 16;
@@ -355,8 +362,8 @@ __device__ __forceinline__ void load_idx(const Smem<I16>& sm, uint32_t (&ix)[Sha
 
 static_assert(kSmallBins == kBlock, "one second-pass bin per thread");
 
-template <bool I16>
-__device__ __forceinline__ void clear_hists(Smem<I16>& sm) {
+template <int LAY>
+__device__ __forceinline__ void clear_hists(Smem<LAY>& sm) {
   for (int i = tid(); i < kBins; i += kBlock) sm.hist1[i] = 0u;
   sm.hs[tid()] = 0u;
 }
@@ -389,8 +396,8 @@ __device__ __forceinline__ uint32_t wave_min(uint32_t v) {
 
 // [lo, hi]: the smallest and largest key of the entries (both uniform).
 // Contains one barrier.
-template <bool I16, int S>
-__device__ __forceinline__ void key_range(Smem<I16>& sm, const uint32_t (&k)[S], const Slice& sl, uint32_t& lo,
+template <int LAY, int S>
+__device__ __forceinline__ void key_range(Smem<LAY>& sm, const uint32_t (&k)[S], const Slice& sl, uint32_t& lo,
                                           uint32_t& hi) {
   uint32_t mn = 0xffffffffu, mx = 0;
 #pragma unroll
@@ -423,8 +430,8 @@ __device__ __forceinline__ void key_range(Smem<I16>& sm, const uint32_t (&k)[S],
 // whole bin or the entries still needed.  stop_total = 0 asks for an exact
 // selection of keep entries.  Both histograms are zero on entry and hold
 // garbage on return.
-template <bool I16, int S>
-__device__ Sel range_select(Smem<I16>& sm, const uint32_t (&k)[S], const Slice& sl, uint32_t lo, uint32_t hi,
+template <int LAY, int S>
+__device__ Sel range_select(Smem<LAY>& sm, const uint32_t (&k)[S], const Slice& sl, uint32_t lo, uint32_t hi,
                             uint32_t keep, uint32_t stop_total) {
   Sel r;
   r.ok = 1u;
@@ -493,13 +500,13 @@ enum EmitMode { kToBuffer = 0, kToOut = 1 };
 // vout[rank] beside the indices.  They are read from the buffer's fp32 bits
 // (which nothing overwrites in this mode) and staged over the index array,
 // which nobody reads after the scan's barrier.
-template <bool I16, int MODE>
-__device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[Shape<I16>::kSlots], const Slice& sl,
+template <int LAY, int MODE>
+__device__ __forceinline__ void emit_chosen(Smem<LAY>& sm, const uint32_t (&k)[Shape<LAY>::kSlots], const Slice& sl,
                                             const Sel& s, uint32_t gt_base, uint32_t eq_base, int32_t* out,
                                             uint32_t limit, uint32_t ibase, float* vout = nullptr) {
-  static_assert(sizeof(sm.idx) >= 4 * kMaxK, "values staged over the index array");
+  static_assert(!Shape<LAY>::kValues || sizeof(sm.idx) >= 4 * Shape<LAY>::kMaxK, "values staged over the index array");
   uint32_t* vstage = reinterpret_cast<uint32_t*>(&sm.idx[0]);
-  constexpr int S = Shape<I16>::kSlots;
+  constexpr int S = Shape<LAY>::kSlots;
   static_assert(S <= 32, "slice flags fit one word");
   const uint32_t sp = sl.sp, nv = sl.nv;
   const uint32_t width = s.hi - s.lo;
@@ -527,9 +534,9 @@ __device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[S
   // slices.  The bits are kept rather than rebuilt from the keys, which fold
   // -0.0 into +0.0.
   uint32_t ix[S];
-  load_idx<I16>(sm, ix, sl);
+  load_idx<LAY>(sm, ix, sl);
   uint32_t rv[MODE == kToBuffer ? S : 1];
-  if constexpr (MODE == kToBuffer) load_bits<I16>(sm, rv, sl);
+  if constexpr (MODE == kToBuffer) load_bits<LAY>(sm, rv, sl);
   uint32_t total;
   const uint32_t excl = block_excl_scan(sm, (uint32_t)__popc(gtm) | ((uint32_t)__popc(eqm) << 16), &total);
   uint32_t first, m;
@@ -545,7 +552,7 @@ __device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[S
             if (vout != nullptr) vstage[pos] = sm.val[sl.base + j];
           } else {
             sm.val[pos] = rv[MODE == kToBuffer ? j : 0];
-            sm.idx[pos] = (typename Shape<I16>::Idx)ix[j];
+            sm.idx[pos] = (typename Shape<LAY>::Idx)ix[j];
           }
         }
       }
@@ -569,7 +576,7 @@ __device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[S
             if (vout != nullptr) vstage[pos - first] = sm.val[sl.base + j];
           } else {
             sm.val[pos] = rv[MODE == kToBuffer ? j : 0];
-            sm.idx[pos] = (typename Shape<I16>::Idx)ix[j];
+            sm.idx[pos] = (typename Shape<LAY>::Idx)ix[j];
           }
         }
         g += gt ? 1u : 0u;
@@ -586,13 +593,13 @@ __device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[S
     __syncthreads();
     int32_t* dst = out + first;
     if ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0u && (m & 3u) == 0u) {
-      for (uint32_t i = tid() * 4u; i < (uint32_t)kBins; i += kBlock * 4u) {
+      for (uint32_t i = tid() * 4u; i < (uint32_t)Shape<LAY>::kStage; i += kBlock * 4u) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(&sm.hist1[i]);
         *reinterpret_cast<u32x4*>(&sm.hist1[i]) = u32x4{0u, 0u, 0u, 0u};
         if (i < m) *reinterpret_cast<u32x4*>(dst + i) = v;
       }
     } else {
-      for (uint32_t i = tid(); i < (uint32_t)kBins; i += kBlock) {
+      for (uint32_t i = tid(); i < (uint32_t)Shape<LAY>::kStage; i += kBlock) {
         const uint32_t v = sm.hist1[i];
         sm.hist1[i] = 0u;
         if (i < m) dst[i] = (int32_t)v;
@@ -621,19 +628,19 @@ __device__ __forceinline__ void emit_chosen(Smem<I16>& sm, const uint32_t (&k)[S
 // by-reference counter would live in scratch, and every scratch reload waits
 // on all outstanding prefetches.  The caller's next barrier orders the
 // rewritten buffer before its next use.
-template <bool I16>
-__device__ __noinline__ uint64_t compact(Smem<I16>& sm, uint32_t cnt, uint32_t keep, uint32_t L) {
-  constexpr int S = Shape<I16>::kSlots;
-  constexpr uint32_t CAP = (uint32_t)Shape<I16>::kCap;
+template <int LAY>
+__device__ __noinline__ uint64_t compact(Smem<LAY>& sm, uint32_t cnt, uint32_t keep, uint32_t L) {
+  constexpr int S = Shape<LAY>::kSlots;
+  constexpr uint32_t CAP = (uint32_t)Shape<LAY>::kCap;
   keep = uni(keep);
   L = uni(L);
-  const Slice sl = plain_slice<I16>(cnt);
+  const Slice sl = plain_slice<LAY>(cnt);
   uint32_t k[S];
-  load_keys<I16>(sm, k, sl);
+  load_keys<LAY>(sm, k, sl);
   uint32_t lo, hi;
-  key_range<I16, S>(sm, k, sl, lo, hi);
-  const Sel s = range_select<I16, S>(sm, k, sl, lo, hi, keep, CAP - kTile);
-  emit_chosen<I16, kToBuffer>(sm, k, sl, s, 0u, 0u, nullptr, CAP, 0u);
+  key_range<LAY, S>(sm, k, sl, lo, hi);
+  const Sel s = range_select<LAY, S>(sm, k, sl, lo, hi, keep, CAP - kTile);
+  emit_chosen<LAY, kToBuffer>(sm, k, sl, s, 0u, 0u, nullptr, CAP, 0u);
   uint32_t Ln;
   if (s.all_in) {
     Ln = s.lo;  // the bin was kept whole
@@ -647,17 +654,17 @@ __device__ __noinline__ uint64_t compact(Smem<I16>& sm, uint32_t cnt, uint32_t k
 // The K best of the buffer, written to out in index order as ibase + index.
 // Inline, so that loads issued before it (the next row's first tiles) stay
 // in flight.
-template <bool I16>
-__device__ __forceinline__ void final_select(Smem<I16>& sm, const Slice& sl, uint32_t K, int32_t* out,
+template <int LAY>
+__device__ __forceinline__ void final_select(Smem<LAY>& sm, const Slice& sl, uint32_t K, int32_t* out,
                                              uint32_t ibase, float* vout = nullptr) {
-  constexpr int S = Shape<I16>::kSlots;
+  constexpr int S = Shape<LAY>::kSlots;
   K = uni(K);
   uint32_t k[S];
-  load_keys<I16>(sm, k, sl);
+  load_keys<LAY>(sm, k, sl);
   uint32_t lo, hi;
-  key_range<I16, S>(sm, k, sl, lo, hi);
-  const Sel s = range_select<I16, S>(sm, k, sl, lo, hi, K, 0u);
-  emit_chosen<I16, kToOut>(sm, k, sl, s, 0u, 0u, out, K, ibase, vout);
+  key_range<LAY, S>(sm, k, sl, lo, hi);
+  const Sel s = range_select<LAY, S>(sm, k, sl, lo, hi, K, 0u);
+  emit_chosen<LAY, kToOut>(sm, k, sl, s, 0u, 0u, out, K, ibase, vout);
 }
 
 // ---------------------------------------------------------------------------
@@ -751,8 +758,8 @@ __device__ __forceinline__ void tile_accept(const float (&x)[kElems], uint32_t p
 // Per-wave counts of accepted elements for each load slot go through LDS
 // (double-buffered by par); returns the tile total and this wave's offset
 // for each slot, all wave-uniform.
-template <bool I16, int VEC>
-__device__ __forceinline__ uint32_t tile_exchange(Smem<I16>& sm, const uint64_t (&bal)[kElems], int& par,
+template <int LAY, int VEC>
+__device__ __forceinline__ uint32_t tile_exchange(Smem<LAY>& sm, const uint64_t (&bal)[kElems], int& par,
                                                   uint32_t (&off)[kElems / VEC]) {
   constexpr int NL = kElems / VEC;
   const uint32_t lane = threadIdx.x & 63;
@@ -779,8 +786,8 @@ __device__ __forceinline__ uint32_t tile_exchange(Smem<I16>& sm, const uint64_t 
 
 // Appends the accepted elements of one tile, in index order, at cnt + their
 // rank in the tile: fp32 bits and the index relative to the chunk start.
-template <bool I16, int VEC, bool FULL>
-__device__ __forceinline__ void tile_append(Smem<I16>& sm, const float (&x)[kElems], const uint64_t (&bal)[kElems],
+template <int LAY, int VEC, bool FULL>
+__device__ __forceinline__ void tile_append(Smem<LAY>& sm, const float (&x)[kElems], const uint64_t (&bal)[kElems],
                                             const uint32_t (&off)[kElems / VEC], uint32_t cnt, uint32_t pbase,
                                             uint32_t c1, float bf, uint32_t rel) {
   constexpr int NL = kElems / VEC;
@@ -796,7 +803,7 @@ __device__ __forceinline__ void tile_append(Smem<I16>& sm, const float (&x)[kEle
       const bool take = accepted<VEC, FULL>(x, e, pbase, c1, bf);
       if (take) {
         sm.val[r] = __float_as_uint(x[e]);
-        sm.idx[r] = (typename Shape<I16>::Idx)(rel + (uint32_t)u * (kBlock * VEC) + c);
+        sm.idx[r] = (typename Shape<LAY>::Idx)(rel + (uint32_t)u * (kBlock * VEC) + c);
       }
       r += take ? 1u : 0u;
     }
@@ -815,24 +822,24 @@ struct Stream {
 // Filters one tile into the candidate buffer, compacting first if the
 // tile's accepted elements would not fit.  p0 and c1 are absolute row
 // positions; indices are stored relative to ibase.
-template <bool I16, int VEC, bool FULL>
-__device__ __forceinline__ void process_tile(Smem<I16>& sm, const float (&x)[kElems], uint32_t p0, uint32_t c1,
+template <int LAY, int VEC, bool FULL>
+__device__ __forceinline__ void process_tile(Smem<LAY>& sm, const float (&x)[kElems], uint32_t p0, uint32_t c1,
                                              uint32_t ibase, uint32_t keep, Stream& st) {
   constexpr int NL = kElems / VEC;
   const uint32_t pbase = p0 + threadIdx.x * VEC;
   uint64_t bal[kElems];
   uint32_t off[NL];
   tile_accept<VEC, FULL>(x, pbase, c1, st.bf, bal);
-  uint32_t total = tile_exchange<I16, VEC>(sm, bal, st.par, off);
-  if (st.cnt + total > (uint32_t)Shape<I16>::kCap) {
-    const uint64_t r = compact<I16>(sm, st.cnt, keep, st.L);
+  uint32_t total = tile_exchange<LAY, VEC>(sm, bal, st.par, off);
+  if (st.cnt + total > (uint32_t)Shape<LAY>::kCap) {
+    const uint64_t r = compact<LAY>(sm, st.cnt, keep, st.L);
     st.L = uni((uint32_t)r);
     st.cnt = uni((uint32_t)(r >> 32));
     st.bf = accept_floor(st.L);
     tile_accept<VEC, FULL>(x, pbase, c1, st.bf, bal);
-    total = tile_exchange<I16, VEC>(sm, bal, st.par, off);
+    total = tile_exchange<LAY, VEC>(sm, bal, st.par, off);
   }
-  if (total != 0) tile_append<I16, VEC, FULL>(sm, x, bal, off, st.cnt, pbase, c1, st.bf, pbase - ibase);
+  if (total != 0) tile_append<LAY, VEC, FULL>(sm, x, bal, off, st.cnt, pbase, c1, st.bf, pbase - ibase);
   st.cnt += total;
 }
 
@@ -845,8 +852,8 @@ __device__ __forceinline__ void process_tile(Smem<I16>& sm, const float (&x)[kEl
 // row again without it if not; when the check passes, every element below
 // the bound is beaten by at least K others.  Runs on register-held keys
 // while the next tiles' loads are in flight.  Leaves the histograms zero.
-template <bool I16>
-__device__ __forceinline__ uint32_t spec_bound(Smem<I16>& sm, float (&x0)[kElems], float (&x1)[kElems], uint32_t n,
+template <int LAY>
+__device__ __forceinline__ uint32_t spec_bound(Smem<LAY>& sm, float (&x0)[kElems], float (&x1)[kElems], uint32_t n,
                                                uint32_t K) {
   constexpr uint32_t M = 2u * kTile;
   const uint64_t want = ((uint64_t)kSpecNum * K * M + (uint64_t)kSpecDen * n - 1) / ((uint64_t)kSpecDen * n);
@@ -867,8 +874,8 @@ __device__ __forceinline__ uint32_t spec_bound(Smem<I16>& sm, float (&x0)[kElems
   sl.sp = 2u * kElems;
   sl.nv = 2u * kElems;
   uint32_t lo, hi;
-  key_range<I16, 2 * kElems>(sm, k, sl, lo, hi);
-  const Sel s = range_select<I16, 2 * kElems>(sm, k, sl, lo, hi, r, r + r / 8u + 8u);
+  key_range<LAY, 2 * kElems>(sm, k, sl, lo, hi);
+  const Sel s = range_select<LAY, 2 * kElems>(sm, k, sl, lo, hi, r, r + r / 8u + 8u);
 #pragma unroll
   for (int e = 0; e < kElems; ++e) {
     x0[e] = __uint_as_float(key_bits(k[e]));
@@ -891,8 +898,8 @@ __device__ __forceinline__ uint32_t spec_bound(Smem<I16>& sm, float (&x0)[kElems
 // go through x0 and x1 ahead of the ring, which starts at tile 2 with its
 // loads issued before the bound is computed; with preloaded they were
 // already loaded by the caller.
-template <bool I16, int VEC, typename T>
-__device__ __forceinline__ void stream_chunk(Smem<I16>& sm, const T* __restrict__ rowp, uint32_t c0,
+template <int LAY, int VEC, typename T>
+__device__ __forceinline__ void stream_chunk(Smem<LAY>& sm, const T* __restrict__ rowp, uint32_t c0,
                                              uint32_t c1, uint32_t keep, uint32_t& cnt, uint32_t& L,
                                              uint32_t spec, float (&x0)[kElems], float (&x1)[kElems],
                                              bool preloaded) {
@@ -921,10 +928,10 @@ __device__ __forceinline__ void stream_chunk(Smem<I16>& sm, const T* __restrict_
       __builtin_amdgcn_sched_barrier(0);  // keep tiles in issue order: waits then retire oldest first
     }
     if (pre) {
-      st.L = uni(spec_bound<I16>(sm, x0, x1, uni(spec), keep));
+      st.L = uni(spec_bound<LAY>(sm, x0, x1, uni(spec), keep));
       st.bf = accept_floor(st.L);
-      process_tile<I16, VEC, true>(sm, x0, c0, c1, c0, keep, st);
-      process_tile<I16, VEC, true>(sm, x1, c0 + kTile, c1, c0, keep, st);
+      process_tile<LAY, VEC, true>(sm, x0, c0, c1, c0, keep, st);
+      process_tile<LAY, VEC, true>(sm, x1, c0 + kTile, c1, c0, keep, st);
     }
     // Whole rounds of PF tiles: one uniform back edge, so the compiler's
     // load-counter waits stay exact (retire only the tile about to be used).
@@ -936,25 +943,25 @@ __device__ __forceinline__ void stream_chunk(Smem<I16>& sm, const T* __restrict_
         const uint32_t jn = j + PF - 1 < F ? j + PF - 1 : F - 1;
         load_full<VEC>(base + jn * kTile, buf[(slot + PF - 1) % PF]);
         __builtin_amdgcn_sched_barrier(0);
-        process_tile<I16, VEC, true>(sm, buf[slot], c0 + j * kTile, c1, c0, keep, st);
+        process_tile<LAY, VEC, true>(sm, buf[slot], c0 + j * kTile, c1, c0, keep, st);
       }
     }
     // The last (F - j1) % PF full tiles are already in buf[0..]: no more loads.
 #pragma unroll
     for (int slot = 0; slot < PF - 1; ++slot) {
       const uint32_t j = Fr + slot;
-      if (j < F) process_tile<I16, VEC, true>(sm, buf[slot], c0 + j * kTile, c1, c0, keep, st);
+      if (j < F) process_tile<LAY, VEC, true>(sm, buf[slot], c0 + j * kTile, c1, c0, keep, st);
     }
   } else if (pre) {
     // Exactly two full tiles: no ring, no bound worth taking.
-    process_tile<I16, VEC, true>(sm, x0, c0, c1, c0, keep, st);
-    process_tile<I16, VEC, true>(sm, x1, c0 + kTile, c1, c0, keep, st);
+    process_tile<LAY, VEC, true>(sm, x0, c0, c1, c0, keep, st);
+    process_tile<LAY, VEC, true>(sm, x1, c0 + kTile, c1, c0, keep, st);
   }
   const uint32_t pt = c0 + F * kTile;
   if (pt < c1) {
     float x[kElems];
     load_tail<VEC>(rowp, c1, pt, x);
-    process_tile<I16, VEC, false>(sm, x, pt, c1, c0, keep, st);
+    process_tile<LAY, VEC, false>(sm, x, pt, c1, c0, keep, st);
   }
   __syncthreads();
   cnt = st.cnt;
@@ -1016,10 +1023,10 @@ __device__ __forceinline__ void load_wave_tail(const T* __restrict__ rowp, uint3
 // Filters one wave tile (row positions p0 + ...) into this wavefront's part
 // of the buffer, slots sub0 + [0, SUB), after its cnt entries.  If the tile's
 // accepted elements would not fit, sets ovf and appends nothing from then on.
-template <bool I16, int VEC, bool FULL>
-__device__ __forceinline__ void wave_tile(Smem<I16>& sm, const float (&x)[kElems], uint32_t p0, uint32_t end, float bf,
+template <int LAY, int VEC, bool FULL>
+__device__ __forceinline__ void wave_tile(Smem<LAY>& sm, const float (&x)[kElems], uint32_t p0, uint32_t end, float bf,
                                           uint32_t sub0, uint32_t& cnt, bool& ovf) {
-  constexpr uint32_t SUB = (uint32_t)Shape<I16>::kCap / kWaves;
+  constexpr uint32_t SUB = (uint32_t)Shape<LAY>::kCap / kWaves;
   constexpr int NL = kElems / VEC;
   const uint32_t pbase = p0 + (threadIdx.x & 63) * VEC;
   uint64_t bal[kElems];
@@ -1049,7 +1056,7 @@ __device__ __forceinline__ void wave_tile(Smem<I16>& sm, const float (&x)[kElems
       const bool take = (FULL || pos < end) && x[e] >= bf;
       if (take) {
         sm.val[r] = __float_as_uint(x[e]);
-        sm.idx[r] = (typename Shape<I16>::Idx)pos;
+        sm.idx[r] = (typename Shape<LAY>::Idx)pos;
       }
       r += take ? 1u : 0u;
     }
@@ -1065,13 +1072,13 @@ __device__ __forceinline__ void wave_tile(Smem<I16>& sm, const float (&x)[kElems
 // the four quarters for the speculative bound.  Returns false if the row must
 // be streamed again on the general path; otherwise mine is this
 // wavefront's number of candidates (in slots [w * SUB, w * SUB + mine)).
-template <bool I16, int VEC, typename T>
-__device__ __forceinline__ bool stream_row_waves(Smem<I16>& sm, const T* __restrict__ rowp, uint32_t n,
+template <int LAY, int VEC, typename T>
+__device__ __forceinline__ bool stream_row_waves(Smem<LAY>& sm, const T* __restrict__ rowp, uint32_t n,
                                                  uint32_t K, float (&x0)[kElems], float (&x1)[kElems],
                                                  bool preloaded, uint32_t& mine) {
   constexpr int PF = kPrefetch;
   constexpr uint32_t WT = kWaveTile;
-  constexpr uint32_t SUB = (uint32_t)Shape<I16>::kCap / kWaves;
+  constexpr uint32_t SUB = (uint32_t)Shape<LAY>::kCap / kWaves;
   n = uni(n);
   K = uni(K);
   const uint32_t w = uni(threadIdx.x >> 6);
@@ -1092,13 +1099,13 @@ __device__ __forceinline__ bool stream_row_waves(Smem<I16>& sm, const T* __restr
     load_wave_full<VEC>(qp + (2u + (uint32_t)s < F ? 2u + (uint32_t)s : F - 1) * WT, buf[s]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  const uint32_t L = uni(spec_bound<I16>(sm, x0, x1, n, K));
+  const uint32_t L = uni(spec_bound<LAY>(sm, x0, x1, n, K));
   const float bf = accept_floor(L);
   const uint32_t sub0 = w * SUB;
   uint32_t cnt = 0;
   bool ovf = L == 0u;  // no bound: the quarters of the buffer could not hold the row
-  wave_tile<I16, VEC, true>(sm, x0, qs, qe, bf, sub0, cnt, ovf);
-  wave_tile<I16, VEC, true>(sm, x1, qs + WT, qe, bf, sub0, cnt, ovf);
+  wave_tile<LAY, VEC, true>(sm, x0, qs, qe, bf, sub0, cnt, ovf);
+  wave_tile<LAY, VEC, true>(sm, x1, qs + WT, qe, bf, sub0, cnt, ovf);
   const uint32_t Fr = F - (F - 2u) % PF;
   for (uint32_t j0 = 2; j0 < Fr; j0 += PF) {
 #pragma unroll
@@ -1107,19 +1114,19 @@ __device__ __forceinline__ bool stream_row_waves(Smem<I16>& sm, const T* __restr
       const uint32_t jn = j + PF - 1 < F ? j + PF - 1 : F - 1;
       load_wave_full<VEC>(qp + jn * WT, buf[(slot + PF - 1) % PF]);
       __builtin_amdgcn_sched_barrier(0);
-      wave_tile<I16, VEC, true>(sm, buf[slot], qs + j * WT, qe, bf, sub0, cnt, ovf);
+      wave_tile<LAY, VEC, true>(sm, buf[slot], qs + j * WT, qe, bf, sub0, cnt, ovf);
     }
   }
 #pragma unroll
   for (int slot = 0; slot < PF - 1; ++slot) {
     const uint32_t j = Fr + slot;
-    if (j < F) wave_tile<I16, VEC, true>(sm, buf[slot], qs + j * WT, qe, bf, sub0, cnt, ovf);
+    if (j < F) wave_tile<LAY, VEC, true>(sm, buf[slot], qs + j * WT, qe, bf, sub0, cnt, ovf);
   }
   const uint32_t pt = qs + F * WT;
   if (pt < qe) {
     float x[kElems];
     load_wave_tail<VEC>(rowp, qe, pt, x);
-    wave_tile<I16, VEC, false>(sm, x, pt, qe, bf, sub0, cnt, ovf);
+    wave_tile<LAY, VEC, false>(sm, x, pt, qe, bf, sub0, cnt, ovf);
   }
   if ((threadIdx.x & 63) == 0) {
     sm.red[w] = cnt;
@@ -1181,14 +1188,14 @@ __device__ __forceinline__ bool splits(uint32_t n, uint32_t K, uint32_t chunk) {
 // unless preloaded).  Returns false if a wavefront's part of the buffer
 // overflowed; otherwise mine / off are this wavefront's candidate count and
 // its offset among the chunk's total (in slots [w * SUB, w * SUB + mine)).
-template <bool I16, int VEC, typename T>
-__device__ __forceinline__ bool stream_piece_waves(Smem<I16>& sm, const T* __restrict__ rowp, uint32_t n,
+template <int LAY, int VEC, typename T>
+__device__ __forceinline__ bool stream_piece_waves(Smem<LAY>& sm, const T* __restrict__ rowp, uint32_t n,
                                                    uint32_t K, uint32_t c0, uint32_t c1, float (&x0)[kElems],
                                                    float (&x1)[kElems], bool preloaded, uint32_t& mine,
                                                    uint32_t& off, uint32_t& total, uint32_t& L) {
   constexpr int PF = kPrefetch;
   constexpr uint32_t WT = kWaveTile;
-  constexpr uint32_t SUB = (uint32_t)Shape<I16>::kCap / kWaves;
+  constexpr uint32_t SUB = (uint32_t)Shape<LAY>::kCap / kWaves;
   n = uni(n);
   K = uni(K);
   c0 = uni(c0);
@@ -1213,7 +1220,7 @@ __device__ __forceinline__ bool stream_piece_waves(Smem<I16>& sm, const T* __res
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  L = uni(spec_bound<I16>(sm, x0, x1, n, K));
+  L = uni(spec_bound<LAY>(sm, x0, x1, n, K));
   const float bf = accept_floor(L);
   const uint32_t sub0 = w * SUB;
   uint32_t cnt = 0;
@@ -1226,19 +1233,19 @@ __device__ __forceinline__ bool stream_piece_waves(Smem<I16>& sm, const T* __res
       const uint32_t jn = j + PF - 1 < F ? j + PF - 1 : F - 1;
       load_wave_full<VEC>(qp + jn * WT, buf[(slot + PF - 1) % PF]);
       __builtin_amdgcn_sched_barrier(0);
-      wave_tile<I16, VEC, true>(sm, buf[slot], qs + j * WT, qe, bf, sub0, cnt, ovf);
+      wave_tile<LAY, VEC, true>(sm, buf[slot], qs + j * WT, qe, bf, sub0, cnt, ovf);
     }
   }
 #pragma unroll
   for (int slot = 0; slot < PF - 1; ++slot) {
     const uint32_t j = Fr + slot;
-    if (j < F) wave_tile<I16, VEC, true>(sm, buf[slot], qs + j * WT, qe, bf, sub0, cnt, ovf);
+    if (j < F) wave_tile<LAY, VEC, true>(sm, buf[slot], qs + j * WT, qe, bf, sub0, cnt, ovf);
   }
   const uint32_t pt = qs + F * WT;
   if (pt < qe) {
     float x[kElems];
     load_wave_tail<VEC>(rowp, qe, pt, x);
-    wave_tile<I16, VEC, false>(sm, x, pt, qe, bf, sub0, cnt, ovf);
+    wave_tile<LAY, VEC, false>(sm, x, pt, qe, bf, sub0, cnt, ovf);
   }
   if ((threadIdx.x & 63) == 0) {
     sm.red[w] = cnt;
@@ -1268,10 +1275,10 @@ __device__ __forceinline__ uint32_t* split_block(const KernelParams& p, int row)
 // is an agent-scope atomic and completes before the arrival, so the last
 // arriver, on any XCD, reads them after its own arrival without cache
 // maintenance.  Returns how many chunks arrived before this one.
-template <bool I16>
-__device__ __forceinline__ uint32_t publish_piece(Smem<I16>& sm, uint32_t* blk, int c, bool waved, uint32_t mine,
+template <int LAY>
+__device__ __forceinline__ uint32_t publish_piece(Smem<LAY>& sm, uint32_t* blk, int c, bool waved, uint32_t mine,
                                                   uint32_t off, uint32_t total, uint32_t ibase) {
-  constexpr uint32_t CAP = (uint32_t)Shape<I16>::kCap;
+  constexpr uint32_t CAP = (uint32_t)Shape<LAY>::kCap;
   constexpr uint32_t SUB = CAP / kWaves;
   uint32_t* bits = blk + kSplitHead / 4 + (uint32_t)c * 2u * CAP;
   uint32_t* idxs = bits + CAP;
@@ -1303,10 +1310,10 @@ __device__ __forceinline__ uint32_t publish_piece(Smem<I16>& sm, uint32_t* blk, 
 // any is used (addresses clamped into the block), so the gather costs about
 // one round trip.  Then the lists and counts it read are zeroed, so the
 // block is all-zero again when the launch ends.
-template <bool I16>
-__device__ __forceinline__ uint32_t merge_pieces(Smem<I16>& sm, uint32_t* blk, uint32_t geff, uint32_t K) {
-  constexpr int S = Shape<I16>::kSlots;
-  constexpr uint32_t CAP = (uint32_t)Shape<I16>::kCap;
+template <int LAY>
+__device__ __forceinline__ uint32_t merge_pieces(Smem<LAY>& sm, uint32_t* blk, uint32_t geff, uint32_t K) {
+  constexpr int S = Shape<LAY>::kSlots;
+  constexpr uint32_t CAP = (uint32_t)Shape<LAY>::kCap;
   const uint32_t t = tid();
   if (t < 64u) {
     const uint32_t v = t < geff ? ws_load(blk + 16 + t) : 0u;
@@ -1344,7 +1351,7 @@ __device__ __forceinline__ uint32_t merge_pieces(Smem<I16>& sm, uint32_t* blk, u
       const uint32_t i = t + (uint32_t)j * kBlock;
       if (i < total) {
         sm.val[i] = vb[j];
-        sm.idx[i] = (typename Shape<I16>::Idx)vi[j];
+        sm.idx[i] = (typename Shape<LAY>::Idx)vi[j];
       }
     }
     __syncthreads();  // every gather load has completed before its word is cleared
@@ -1390,8 +1397,8 @@ __device__ __forceinline__ uint32_t offset_of(const KernelParams& p, int row) {
   return p.row_offsets != nullptr ? (uint32_t)p.row_offsets[row] : 0u;
 }
 
-template <bool I16>
-__device__ __forceinline__ void zero_histograms(Smem<I16>& sm) {
+template <int LAY>
+__device__ __forceinline__ void zero_histograms(Smem<LAY>& sm) {
   clear_hists(sm);
 }
 
@@ -1429,9 +1436,9 @@ __device__ __forceinline__ void unit_of(const KernelParams& p, uint32_t u, int& 
 // VALS: the launch also writes the chosen scores (compiled out otherwise, for
 // the same reason).
 // T: the score type (float, or uint16_t holding bf16).
-template <int VEC, bool I16, bool SPLIT, bool VALS, typename T>
-__global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_kernel(KernelParams p) {
-  __shared__ Smem<I16> sm;
+template <int VEC, int LAY, bool SPLIT, bool VALS, typename T>
+__global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_single_kernel(KernelParams p) {
+  __shared__ Smem<LAY> sm;
   zero_histograms(sm);
   __syncthreads();
   const uint32_t K = (uint32_t)p.K;
@@ -1495,7 +1502,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_ker
           g1 = g0 + CH < (uint32_t)n ? g0 + CH : (uint32_t)n;
         }
         if (g0 < g1) {
-          waved = stream_piece_waves<I16, VEC>(sm, rowp, (uint32_t)n, K, g0, g1, x0, x1, have_pre, mine, off, cnt,
+          waved = stream_piece_waves<LAY, VEC>(sm, rowp, (uint32_t)n, K, g0, g1, x0, x1, have_pre, mine, off, cnt,
                                                gL);
           general = !waved;
         } else {
@@ -1511,7 +1518,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_ker
           cnt = mine;
         }
       } else if (!redo && wave_mode((uint32_t)n, K)) {
-        waved = stream_row_waves<I16, VEC>(sm, rowp, (uint32_t)n, K, x0, x1, have_pre, cnt);
+        waved = stream_row_waves<LAY, VEC>(sm, rowp, (uint32_t)n, K, x0, x1, have_pre, cnt);
         have_pre = false;
         if (!waved) {
           // A quarter of the buffer overflowed, or fewer than K elements
@@ -1525,7 +1532,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_ker
       if (general) {
         cnt = 0u;  // a failed wave-by-wave attempt leaves its count behind
         const uint32_t spec = (piece || redo || n < (int64_t)kSpecMinLen) ? 0u : (uint32_t)n;
-        stream_chunk<I16, VEC>(sm, rowp, g0, g1, K, cnt, gL, spec, x0, x1, have_pre);
+        stream_chunk<LAY, VEC>(sm, rowp, g0, g1, K, cnt, gL, spec, x0, x1, have_pre);
         have_pre = false;
         if (!piece && cnt < K && !redo) {
           // Fewer than K elements reached the speculative bound: it was above
@@ -1539,10 +1546,10 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_ker
         const uint32_t geff = ((uint32_t)n + CH - 1u) / CH;
         if (g0 < g1) {
           uint32_t* blk = split_block(p, row);
-          const uint32_t before = publish_piece<I16>(sm, blk, c, waved, mine, off, cnt, g0);
+          const uint32_t before = publish_piece<LAY>(sm, blk, c, waved, mine, off, cnt, g0);
           if (before == geff - 1u) {
-            cnt = merge_pieces<I16>(sm, blk, geff, K);
-            if (cnt < K || cnt > (uint32_t)Shape<I16>::kCap) {
+            cnt = merge_pieces<LAY>(sm, blk, geff, K);
+            if (cnt < K || cnt > (uint32_t)Shape<LAY>::kCap) {
               // Too few elements reached the bound, or too many to gather:
               // this workgroup streams the whole row on the general path.
               c = -1;
@@ -1605,7 +1612,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_single_ker
       have_pre = true;
     }
     if (select) {
-      final_select<I16>(sm, waved ? wave_slice<I16>(cnt) : plain_slice<I16>(cnt), K, out, off,
+      final_select<LAY>(sm, waved ? wave_slice<LAY>(cnt) : plain_slice<LAY>(cnt), K, out, off,
                         VALS ? p.out_val + (int64_t)row * p.K : nullptr);
     }
     first_unit = false;
@@ -1679,13 +1686,13 @@ __device__ __forceinline__ int list_of(const uint32_t* off, int n, uint32_t i) {
   return lo;
 }
 
-template <int VEC, bool I16, typename E>
-__global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_multi_kernel(KernelParams p) {
-  __shared__ Smem<I16> sm;
+template <int VEC, int LAY, typename E>
+__global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kernel(KernelParams p) {
+  __shared__ Smem<LAY> sm;
   __shared__ uint32_t s_off[kMaxGroup + 1];
   __shared__ uint32_t s_above[kMaxGroup];
-  constexpr int S = Shape<I16>::kSlots;
-  constexpr int CAP = Shape<I16>::kCap;
+  constexpr int S = Shape<LAY>::kSlots;
+  constexpr int CAP = Shape<LAY>::kCap;
   const int t = threadIdx.x;
   const int G = p.wg_per_row;
   // Workgroups are dispatched round-robin over the 8 XCDs.  Renumber them so
@@ -1727,12 +1734,12 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_multi_kern
   const E* rowp = row_of<E>(p, row);
   uint32_t cnt = 0, L = 0;
   float x0[kElems], x1[kElems];
-  stream_chunk<I16, VEC>(sm, rowp, (uint32_t)c0, (uint32_t)c1, K, cnt, L, 0u, x0, x1, false);
+  stream_chunk<LAY, VEC>(sm, rowp, (uint32_t)c0, (uint32_t)c1, K, cnt, L, 0u, x0, x1, false);
 
-  const Slice sl = plain_slice<I16>(cnt);
+  const Slice sl = plain_slice<LAY>(cnt);
   const uint32_t sp = sl.sp, nv = sl.nv;
   uint32_t k[S];
-  load_keys<I16>(sm, k, sl);
+  load_keys<LAY>(sm, k, sl);
   float* vout = p.out_val != nullptr ? p.out_val + (int64_t)row * p.K : nullptr;
 
   // Round 1: the chunk's top-digit (11-bit) histogram into the row's, then
@@ -1901,7 +1908,7 @@ __global__ void __launch_bounds__(kBlock, Shape<I16>::kResident) topk_multi_kern
   s.in_bin = 0u;
   s.ok = ok;
   s.all_in = false;
-  emit_chosen<I16, kToOut>(sm, k, sl, s, gt_base, eq_base, out, K, (uint32_t)c0 + offset_of(p, row), vout);
+  emit_chosen<LAY, kToOut>(sm, k, sl, s, gt_base, eq_base, out, K, (uint32_t)c0 + offset_of(p, row), vout);
 }
 
 // ---------------------------------------------------------------------------
@@ -2041,30 +2048,46 @@ __global__ void keys_kernel(const uint32_t* bits, uint32_t* keys, int64_t n) {
 // Instance table
 // ---------------------------------------------------------------------------
 
-template <int VEC, bool I16, typename T>
+template <int VEC, int LAY, typename T>
 static const void* pick_vec(int path, bool vals) {
   if (path == 3) return reinterpret_cast<const void*>(&read_ref_kernel<VEC, T>);
-  if (path == 2) return reinterpret_cast<const void*>(&topk_multi_kernel<VEC, I16, T>);
+  if (path == 2) return reinterpret_cast<const void*>(&topk_multi_kernel<VEC, LAY, T>);
   const bool sp = path == 4;
-  if (sp && vals) return reinterpret_cast<const void*>(&topk_single_kernel<VEC, I16, true, true, T>);
-  if (sp) return reinterpret_cast<const void*>(&topk_single_kernel<VEC, I16, true, false, T>);
-  if (vals) return reinterpret_cast<const void*>(&topk_single_kernel<VEC, I16, false, true, T>);
-  return reinterpret_cast<const void*>(&topk_single_kernel<VEC, I16, false, false, T>);
+  if constexpr (Shape<LAY>::kValues) {
+    if (sp && vals) return reinterpret_cast<const void*>(&topk_single_kernel<VEC, LAY, true, true, T>);
+    if (vals) return reinterpret_cast<const void*>(&topk_single_kernel<VEC, LAY, false, true, T>);
+  } else {
+    if (vals) return nullptr;  // no room to stage the values: the host plans another layout
+  }
+  if (sp) return reinterpret_cast<const void*>(&topk_single_kernel<VEC, LAY, true, false, T>);
+  return reinterpret_cast<const void*>(&topk_single_kernel<VEC, LAY, false, false, T>);
 }
 
-template <bool I16>
+template <int LAY>
 static const void* pick(int path, int vec, bool vals, bool bf16) {
-  if (bf16) return vec == 8 ? pick_vec<8, I16, uint16_t>(path, vals) : pick_vec<1, I16, uint16_t>(path, vals);
-  if (vec == 4) return pick_vec<4, I16, float>(path, vals);
-  if (vec == 2) return pick_vec<2, I16, float>(path, vals);
-  return pick_vec<1, I16, float>(path, vals);
+  if (bf16) return vec == 8 ? pick_vec<8, LAY, uint16_t>(path, vals) : pick_vec<1, LAY, uint16_t>(path, vals);
+  if (vec == 4) return pick_vec<4, LAY, float>(path, vals);
+  if (vec == 2) return pick_vec<2, LAY, float>(path, vals);
+  return pick_vec<1, LAY, float>(path, vals);
 }
 
-const void* kernel_ptr(int path, int vec, bool idx16, bool vals, bool bf16) {
-  return idx16 ? pick<true>(path, vec, vals, bf16) : pick<false>(path, vec, vals, bf16);
+const void* kernel_ptr(int path, int vec, bool idx16, bool vals, bool bf16, bool big_k) {
+  switch (layout_of(idx16, big_k)) {
+    case kLayIdx16: return pick<kLayIdx16>(path, vec, vals, bf16);
+    case kLayBigK: return pick<kLayBigK>(path, vec, vals, bf16);
+    case kLayIdx16 | kLayBigK: return pick<kLayIdx16 | kLayBigK>(path, vec, vals, bf16);
+    default: return pick<0>(path, vec, vals, bf16);
+  }
 }
 
-int lds_bytes_of(bool idx16) { return idx16 ? (int)sizeof(Smem<true>) : (int)sizeof(Smem<false>); }
+int lds_bytes_of(bool idx16, bool big_k) {
+  switch (layout_of(idx16, big_k)) {
+    case kLayIdx16: return (int)sizeof(Smem<kLayIdx16>);
+    case kLayBigK: return (int)sizeof(Smem<kLayBigK>);
+    case kLayIdx16 | kLayBigK: return (int)sizeof(Smem<kLayIdx16 | kLayBigK>);
+    default: return (int)sizeof(Smem<0>);
+  }
+}
 
 const void* zero_kernel_ptr() { return reinterpret_cast<const void*>(&zero_kernel); }
 const void* keys_kernel_ptr() { return reinterpret_cast<const void*>(&keys_kernel); }

@@ -145,8 +145,8 @@ def test_plan_rejects_bad_arguments():
         rrt.plan_for_props(256, 2, 2, 4, 8192, 0)
     assert e.value.code == -2
     with pytest.raises(rrt.TopKError) as e:
-        rrt.plan_for_props(256, 2, 2, 4, 8192, 2049)
-    assert e.value.code == -2 and "2049" in str(e.value)
+        rrt.plan_for_props(256, 2, 2, 4, 8192, 4097)
+    assert e.value.code == -2 and "4097" in str(e.value)
     with pytest.raises(rrt.TopKError) as e:
         rrt.plan_for_props(256, 2, 2, -1, 8192, 10)
     assert e.value.code == -1
@@ -233,3 +233,19 @@ def test_plan_occupancy_cap():
         rrt.plan_for_props(256, 3, 3, 16, 131072, 2048)
     with pytest.raises(rrt.TopKError):
         rrt.plan_for_props(256, 3, 3, 16, 131072, 2048, max_occupancy=-1)
+
+
+def test_plan_large_k_layout():
+    # K above 2048 takes the large layout: kmax 4096, more LDS per workgroup.
+    small = rrt.plan_for_props(256, 4, 4, 64, 32768, 2048)
+    big = rrt.plan_for_props(256, 2, 2, 64, 32768, 2049)
+    assert small["kmax"] == 2048 and big["kmax"] == 4096
+    assert big["lds_bytes"] > small["lds_bytes"]
+    assert rrt.plan_for_props(256, 2, 2, 64, 32768, 4096)["kmax"] == 4096
+    # Forcing 32-bit indices changes the index width only.
+    p = rrt.plan_for_props(256, 2, 2, 64, 32768, 3000, force_idx32=1)
+    assert p["idx16"] == 0 and p["kmax"] == 4096
+    assert rrt.plan_for_props(256, 2, 2, 64, 32768, 3000)["idx16"] == 1
+    # Split-row blocks and cooperative lists size with the layout's capacity.
+    p = rrt.plan_for_props(256, 2, 2, 8, 65536, 4096, split_rows=8, split_g=4)
+    assert p["workspace_bytes"] == 256 + 8 * ((256 + 8 * 7168 * 4 + 255) // 256 * 256)
