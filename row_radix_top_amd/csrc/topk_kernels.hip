@@ -16,11 +16,18 @@
 //   stores.  When a tile would overflow the buffer, the buffer is compacted
 //   and L rises (see compact()).  Each score is read from HBM exactly once.
 //
-// * Radix select.  Over the register-held buffer: an 11-bit top-digit
-//   histogram, then 11- and 10-bit digits, each with LDS atomics.  Every
-//   wavefront scans a histogram from the top with DPP prefix sums and finds
-//   the threshold digit itself, so a search costs no barrier.  Ties at the
-//   final 32-bit key go to the lower buffer position, the lower index.
+// * Speculative bound.  On long rows the bound starts at (about) the key of
+//   the 1.5 K * 4096 / n-th best of a 4096-element sample, so only ~1.5 K
+//   elements reach the buffer; each wavefront then streams its own quarter
+//   of the row without per-tile barriers.  A row whose bound proves too high
+//   (fewer than K reached it) is streamed again without one.
+//
+// * Range select.  Over the register-held buffer: passes histogram the keys
+//   of the current interval [lo, hi] (starting from their exact range) into
+//   2048 or 256 bins with LDS atomics.  Every wavefront scans a histogram
+//   from the top with DPP prefix sums and finds the threshold bin itself, so
+//   a search costs no barrier.  Ties at the final 32-bit key go to the lower
+//   buffer position, the lower index.
 //
 // * Ordered emit.  Each thread owns a contiguous slice of the buffer; one
 //   workgroup prefix sum of the per-thread (greater, equal) counts gives every
@@ -36,6 +43,16 @@
 //   the row touched, so the workspace is all-zero when the kernel ends (the
 //   in-kernel cleanup of the PR #41748 page, without the race its review
 //   describes: nothing is reset while another workgroup can still read it).
+//
+// * Split rows (opt-in).  Chunks of a row as separate work units that publish
+//   their candidates; the last to arrive selects over all of them, and no
+//   workgroup ever waits for another.
+//
+// Instances differ in the buffer layout (16-bit or 32-bit candidate indices;
+// room for K up to 2048 or 4096), the load width, the score type (fp32, or
+// bf16 widened exactly at the load), and whether the launch has split rows
+// or writes the chosen scores (compiled out otherwise, to keep the row
+// loop's registers).
 //
 // The key function maps fp32 bits to uint32 so that unsigned order equals
 // IEEE order for non-NaN values, with -0.0 and +0.0 mapped to the same key.
