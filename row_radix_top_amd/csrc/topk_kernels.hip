@@ -182,6 +182,9 @@ struct __align__(16) Smem {
   uint32_t tile_cnt[2][kElems][kWaves];
   uint32_t wsum[kWaves];
   uint32_t acc[16];
+  // Target of histogram adds that count nothing: one word per lane, so the
+  // lanes of one add never collide on it (never read).
+  uint32_t sink[64];
   // Split-row merge (between streaming and selection, when tile_cnt is
   // idle): each chunk's first slot in the buffer, and its list's offset in
   // the row block less that slot.
@@ -211,11 +214,18 @@ __device__ __forceinline__ Found wave_find(const uint32_t* hist, uint32_t krem) 
   asm volatile("" : "+v"(lane));
   // Lane l owns group 63 - l, so lane order is descending bin order.
   const u32x4* grp = reinterpret_cast<const u32x4*>(hist + (63 - lane) * kPer);
+  // Loads go out four at a time (rotated start: spreads the banks), so their
+  // latencies overlap without holding the whole group in registers.
+  constexpr int kB = kVec < 4 ? kVec : 4;
+  static_assert(kVec % kB == 0, "whole batches");
   uint32_t s = 0;
 #pragma unroll
-  for (int c = 0; c < kVec; ++c) {
-    const u32x4 v = grp[(c + lane) & (kVec - 1)];  // rotated start: spreads the banks
-    s += v.x + v.y + v.z + v.w;
+  for (int c0 = 0; c0 < kVec; c0 += kB) {
+    u32x4 g[kB];
+#pragma unroll
+    for (int c = 0; c < kB; ++c) g[c] = grp[(c0 + c + lane) & (kVec - 1)];
+#pragma unroll
+    for (int c = 0; c < kB; ++c) s += (g[c].x + g[c].y) + (g[c].z + g[c].w);
   }
   const uint32_t incl = wave_incl_scan(s);
   const uint64_t reach = ballot(incl >= krem);
@@ -287,7 +297,10 @@ struct Sel {
 };
 
 // A thread's share of the buffer during a selection: slots base .. base +
-// sp - 1 (sp even and wave-uniform), of which the first nv hold entries.
+// sp - 1 (sp a multiple of 4 and wave-uniform), of which the first nv hold
+// entries.  Loops over a slice test sp once per group of 4 slots: a test per
+// slot would split the unrolled loop into one basic block per slot, and a
+// lone wavefront then waits out each block's dependent chain in turn.
 // Slices in thread order cover the entries in index order.
 struct Slice {
   uint32_t base, sp, nv;
@@ -300,7 +313,7 @@ __device__ __forceinline__ Slice plain_slice(uint32_t cnt) {
   constexpr uint32_t S = (uint32_t)Shape<LAY>::kSlots;
   cnt = uni(cnt);
   uint32_t sp = (cnt + kBlock - 1) / kBlock;
-  sp = (sp + 1u) & ~1u;
+  sp = (sp + 3u) & ~3u;
   sp = sp < S ? sp : S;
   Slice sl;
   sl.sp = sp;
@@ -318,7 +331,7 @@ __device__ __forceinline__ Slice wave_slice(uint32_t cw) {
   constexpr uint32_t SUB = (uint32_t)Shape<LAY>::kCap / kWaves;
   cw = uni(cw);
   uint32_t sp = (cw + 63u) / 64u;
-  sp = (sp + 1u) & ~1u;
+  sp = (sp + 3u) & ~3u;
   sp = sp < S ? sp : S;
   const uint32_t t = tid();
   const uint32_t lane = t & 63u;
@@ -330,16 +343,18 @@ __device__ __forceinline__ Slice wave_slice(uint32_t cw) {
   return sl;
 }
 
-// Keys of this thread's slice.
+// Keys of this thread's slice.  (base is a multiple of 4: 16-byte reads.)
 template <int LAY>
 __device__ __forceinline__ void load_keys(const Smem<LAY>& sm, uint32_t (&k)[Shape<LAY>::kSlots], const Slice& sl) {
   constexpr int S = Shape<LAY>::kSlots;
 #pragma unroll
-  for (int q = 0; q < S / 2; ++q) {
-    if ((uint32_t)(2 * q) < sl.sp) {
-      const u32x2 a = *reinterpret_cast<const u32x2*>(&sm.val[sl.base + 2 * q]);
-      k[2 * q + 0] = ord_key(a.x);
-      k[2 * q + 1] = ord_key(a.y);
+  for (int q = 0; q < S / 4; ++q) {
+    if ((uint32_t)(4 * q) < sl.sp) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(&sm.val[sl.base + 4 * q]);
+      k[4 * q + 0] = ord_key(a.x);
+      k[4 * q + 1] = ord_key(a.y);
+      k[4 * q + 2] = ord_key(a.z);
+      k[4 * q + 3] = ord_key(a.w);
     }
   }
 }
@@ -349,11 +364,13 @@ template <int LAY>
 __device__ __forceinline__ void load_bits(const Smem<LAY>& sm, uint32_t (&v)[Shape<LAY>::kSlots], const Slice& sl) {
   constexpr int S = Shape<LAY>::kSlots;
 #pragma unroll
-  for (int q = 0; q < S / 2; ++q) {
-    if ((uint32_t)(2 * q) < sl.sp) {
-      const u32x2 a = *reinterpret_cast<const u32x2*>(&sm.val[sl.base + 2 * q]);
-      v[2 * q + 0] = a.x;
-      v[2 * q + 1] = a.y;
+  for (int q = 0; q < S / 4; ++q) {
+    if ((uint32_t)(4 * q) < sl.sp) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(&sm.val[sl.base + 4 * q]);
+      v[4 * q + 0] = a.x;
+      v[4 * q + 1] = a.y;
+      v[4 * q + 2] = a.z;
+      v[4 * q + 3] = a.w;
     }
   }
 }
@@ -362,16 +379,20 @@ template <int LAY>
 __device__ __forceinline__ void load_idx(const Smem<LAY>& sm, uint32_t (&ix)[Shape<LAY>::kSlots], const Slice& sl) {
   constexpr int S = Shape<LAY>::kSlots;
 #pragma unroll
-  for (int q = 0; q < S / 2; ++q) {
-    if ((uint32_t)(2 * q) < sl.sp) {
+  for (int q = 0; q < S / 4; ++q) {
+    if ((uint32_t)(4 * q) < sl.sp) {
       if constexpr (Shape<LAY>::kIdx16) {
-        const uint32_t a = *reinterpret_cast<const uint32_t*>(&sm.idx[sl.base + 2 * q]);
-        ix[2 * q + 0] = a & 0xffffu;
-        ix[2 * q + 1] = a >> 16;
+        const u32x2 a = *reinterpret_cast<const u32x2*>(&sm.idx[sl.base + 4 * q]);
+        ix[4 * q + 0] = a.x & 0xffffu;
+        ix[4 * q + 1] = a.x >> 16;
+        ix[4 * q + 2] = a.y & 0xffffu;
+        ix[4 * q + 3] = a.y >> 16;
       } else {
-        const u32x2 a = *reinterpret_cast<const u32x2*>(&sm.idx[sl.base + 2 * q]);
-        ix[2 * q + 0] = a.x;
-        ix[2 * q + 1] = a.y;
+        const u32x4 a = *reinterpret_cast<const u32x4*>(&sm.idx[sl.base + 4 * q]);
+        ix[4 * q + 0] = a.x;
+        ix[4 * q + 1] = a.y;
+        ix[4 * q + 2] = a.z;
+        ix[4 * q + 3] = a.w;
       }
     }
   }
@@ -416,18 +437,29 @@ __device__ __forceinline__ uint32_t wave_min(uint32_t v) {
 template <int LAY, int S>
 __device__ __forceinline__ void key_range(Smem<LAY>& sm, const uint32_t (&k)[S], const Slice& sl, uint32_t& lo,
                                           uint32_t& hi) {
-  uint32_t mn = 0xffffffffu, mx = 0;
+  // Two independent chains (even and odd slots) halve the dependent latency.
+  uint32_t mn0 = 0xffffffffu, mx0 = 0, mn1 = 0xffffffffu, mx1 = 0;
 #pragma unroll
-  for (int j = 0; j < S; ++j) {
-    if ((uint32_t)(j) < sl.sp) {
-      if ((uint32_t)j < sl.nv) {
-        mn = min(mn, k[j]);
-        mx = max(mx, k[j]);
+  for (int q = 0; q < S / 4; ++q) {
+    if ((uint32_t)(4 * q) < sl.sp) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int j = 4 * q + c;
+        const bool v = (uint32_t)j < sl.nv;
+        const uint32_t a = v ? k[j] : 0xffffffffu;
+        const uint32_t b = v ? k[j] : 0u;
+        if (c & 1) {
+          mn1 = min(mn1, a);
+          mx1 = max(mx1, b);
+        } else {
+          mn0 = min(mn0, a);
+          mx0 = max(mx0, b);
+        }
       }
     }
   }
-  mn = wave_min(mn);
-  mx = wave_max(mx);
+  const uint32_t mn = wave_min(min(mn0, mn1));
+  const uint32_t mx = wave_max(max(mx0, mx1));
   const int w = tid() >> 6;
   if ((tid() & 63) == 0) {
     sm.red[w] = mn;
@@ -473,10 +505,21 @@ __device__ Sel range_select(Smem<LAY>& sm, const uint32_t (&k)[S], const Slice& 
     const uint32_t range = hi - lo;
     const uint32_t nb = range != 0u ? 32u - (uint32_t)__builtin_clz(range) : 0u;
     const uint32_t sh = nb > bits ? nb - bits : 0u;
+    // One LDS add per slot and no per-slot branch: entries outside the
+    // interval (and empty slots) add to the lane's own sink word instead of a
+    // bin.  (Adding 0 to some bin would let every such lane of a wave hit the
+    // same bin when the keys share their low bits, as bf16 scores do.)
+    uint32_t* const sink = &sm.sink[tid() & 63];
 #pragma unroll
-    for (int j = 0; j < S; ++j) {
-      if ((uint32_t)(j) < sl.sp) {
-        if ((uint32_t)j < sl.nv && k[j] - lo <= range) atomicAdd(&h[(k[j] - lo) >> sh], 1u);
+    for (int q = 0; q < S / 4; ++q) {
+      if ((uint32_t)(4 * q) < sl.sp) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int j = 4 * q + c;
+          const uint32_t d = k[j] - lo;
+          const bool in = (uint32_t)j < sl.nv && d <= range;
+          atomicAdd(in ? &h[d >> sh] : sink, 1u);
+        }
       }
     }
     __syncthreads();
@@ -534,15 +577,26 @@ __device__ __forceinline__ void emit_chosen(Smem<LAY>& sm, const uint32_t (&k)[S
   uint32_t gtm = 0, eqm = 0;
   if (whole) {
 #pragma unroll
-    for (int j = 0; j < S; ++j)
-      if ((uint32_t)(j) < sp) gtm |= ((uint32_t)j < nv && k[j] >= s.lo) ? (1u << j) : 0u;
+    for (int q = 0; q < S / 4; ++q) {
+      if ((uint32_t)(4 * q) < sp) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int j = 4 * q + c;
+          gtm |= ((uint32_t)j < nv && k[j] >= s.lo) ? (1u << j) : 0u;
+        }
+      }
+    }
   } else {
 #pragma unroll
-    for (int j = 0; j < S; ++j) {
-      if ((uint32_t)(j) < sp) {
-        const bool valid = (uint32_t)j < nv;
-        gtm |= (valid && k[j] > s.hi) ? (1u << j) : 0u;
-        eqm |= (valid && k[j] - s.lo <= width) ? (1u << j) : 0u;
+    for (int q = 0; q < S / 4; ++q) {
+      if ((uint32_t)(4 * q) < sp) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int j = 4 * q + c;
+          const bool valid = (uint32_t)j < nv;
+          gtm |= (valid && k[j] > s.hi) ? (1u << j) : 0u;
+          eqm |= (valid && k[j] - s.lo <= width) ? (1u << j) : 0u;
+        }
       }
     }
   }
@@ -559,18 +613,23 @@ __device__ __forceinline__ void emit_chosen(Smem<LAY>& sm, const uint32_t (&k)[S
   uint32_t first, m;
   if (whole) {
     // Rank of slice position j = this thread's first rank + picks before j.
+    uint32_t pos = excl;
 #pragma unroll
-    for (int j = 0; j < S; ++j) {
-      if ((uint32_t)(j) < sp) {
-        const uint32_t pos = (uint32_t)__popc(gtm & ((1u << j) - 1u)) + excl;
-        if (((gtm >> j) & 1u) && pos < limit) {
-          if constexpr (MODE != kToBuffer) {
-            sm.hist1[pos] = ibase + ix[j];
-            if (vout != nullptr) vstage[pos] = sm.val[sl.base + j];
-          } else {
-            sm.val[pos] = rv[MODE == kToBuffer ? j : 0];
-            sm.idx[pos] = (typename Shape<LAY>::Idx)ix[j];
+    for (int q = 0; q < S / 4; ++q) {
+      if ((uint32_t)(4 * q) < sp) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int j = 4 * q + c;
+          if (((gtm >> j) & 1u) && pos < limit) {
+            if constexpr (MODE != kToBuffer) {
+              sm.hist1[pos] = ibase + ix[j];
+              if (vout != nullptr) vstage[pos] = sm.val[sl.base + j];
+            } else {
+              sm.val[pos] = rv[MODE == kToBuffer ? j : 0];
+              sm.idx[pos] = (typename Shape<LAY>::Idx)ix[j];
+            }
           }
+          pos += (gtm >> j) & 1u;
         }
       }
     }
@@ -581,23 +640,27 @@ __device__ __forceinline__ void emit_chosen(Smem<LAY>& sm, const uint32_t (&k)[S
     uint32_t e = eq_base + (excl >> 16);
     first = gt_base + (eq_base < take ? eq_base : take);  // rank of the first chosen
 #pragma unroll
-    for (int j = 0; j < S; ++j) {
-      if ((uint32_t)(j) < sp) {
-        const bool gt = (gtm >> j) & 1u;
-        const bool eq = (eqm >> j) & 1u;
-        const bool pick = gt || (eq && e < take);
-        const uint32_t pos = g + (e < take ? e : take);
-        if (pick && pos < limit) {
-          if constexpr (MODE != kToBuffer) {
-            sm.hist1[pos - first] = ibase + ix[j];
-            if (vout != nullptr) vstage[pos - first] = sm.val[sl.base + j];
-          } else {
-            sm.val[pos] = rv[MODE == kToBuffer ? j : 0];
-            sm.idx[pos] = (typename Shape<LAY>::Idx)ix[j];
+    for (int q = 0; q < S / 4; ++q) {
+      if ((uint32_t)(4 * q) < sp) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int j = 4 * q + c;
+          const bool gt = (gtm >> j) & 1u;
+          const bool eq = (eqm >> j) & 1u;
+          const bool pick = gt || (eq && e < take);
+          const uint32_t pos = g + (e < take ? e : take);
+          if (pick && pos < limit) {
+            if constexpr (MODE != kToBuffer) {
+              sm.hist1[pos - first] = ibase + ix[j];
+              if (vout != nullptr) vstage[pos - first] = sm.val[sl.base + j];
+            } else {
+              sm.val[pos] = rv[MODE == kToBuffer ? j : 0];
+              sm.idx[pos] = (typename Shape<LAY>::Idx)ix[j];
+            }
           }
+          g += gt ? 1u : 0u;
+          e += eq ? 1u : 0u;
         }
-        g += gt ? 1u : 0u;
-        e += eq ? 1u : 0u;
       }
     }
     const uint32_t eq_end = eq_base + (total >> 16);
