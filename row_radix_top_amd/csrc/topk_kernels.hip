@@ -1529,22 +1529,26 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_single_ker
   uint32_t next = 0u;  // thread 0: the unit after this one
   bool drawn = false;  // thread 0: next is set for the current unit
   uint32_t unit = blockIdx.x;
-  // The first unit's draw waits until its scores are streamed: at launch every
-  // workgroup would hit the counter at once, and the wait for the first tile
-  // would include that queue.
+  bool first_unit = true;
+  // Every unit draws its successor when it starts, so the atomic's latency
+  // hides behind the unit.  The first unit's successor is fixed (unit +
+  // grid): at launch every workgroup would hit the counter at once, and at
+  // the end of the first units, which end close together, nearly as many.
+  // Tickets therefore start at two grids; U - grid draws are made in all
+  // (each workgroup with a second unit draws until it gets no unit), and the
+  // last one resets the counter.
   auto draw = [&]() {
     if (threadIdx.x == 0 && !drawn) {
-      if (ticket != nullptr) {
+      if (ticket != nullptr && !first_unit) {
         const uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (t == U - 1u) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        next = gridDim.x + t;
+        if (t == U - gridDim.x - 1u) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        next = 2u * gridDim.x + t;
       } else {
         next = unit + gridDim.x;
       }
       drawn = true;
     }
   };
-  bool first_unit = true;
   // The next unit's first tiles (or its row's sample) are loaded before this
   // unit's final selection, so that their latency hides behind it.
   bool have_pre = false;
@@ -1556,7 +1560,7 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_single_ker
   int64_t n = unit < U ? clamp_len(p, row) : 0;
   uint32_t off = unit < U ? uni(offset_of(p, row)) : 0u;
   while (unit < U) {
-    if (!first_unit) draw();
+    draw();
     int32_t* out = p.out + (int64_t)row * p.K;
     uint32_t cnt = 0;
     bool waved = false;  // the candidates sit wave by wave
