@@ -224,9 +224,11 @@ def decode_latency(launches: int = 400):
     host: the Python binding's call, and the bare C-ABI call through ctypes
     with ready pointers (enqueue only, no waiting on the GPU).  device:
     eager back-to-back launches and hipGraph replay (HIP events), next to two
-    floors on the same input: a launch whose rows are all empty (it reads no
-    scores and only writes the -1 padding) and the streaming-read reference
-    (reads every valid score, selects nothing)."""
+    floors on the same input, both replayed from a hipGraph so that the host
+    cost of a call (about as long as these kernels) does not set the pace: a
+    launch whose rows are all empty (it reads no scores and only writes the
+    -1 padding) and the streaming-read reference (reads every valid score,
+    selects nothing)."""
     import ctypes
     import time
     import torch
@@ -267,10 +269,10 @@ def decode_latency(launches: int = 400):
         "graph_us_per_launch": round(graph_replay_ms(py, 100) * 1e3, 3),
         "host_us_per_call_binding": round(host_call_us(py, launches), 3),
         "host_us_per_call_c_abi": round(host_call_us(abi, launches), 3),
-        "empty_rows_us_per_launch": round(time_launches(
-            lambda i: rrt.topk_ragged(pool[i % ncopy], Z, w.K, out=out), launches) * 1e3, 3),
-        "read_reference_us_per_launch": round(time_launches(
-            lambda i: rrt.read_reference(pool[i % ncopy], L, out=keys), launches) * 1e3, 3),
+        "empty_rows_us_per_launch": round(graph_replay_ms(
+            lambda i: rrt.topk_ragged(pool[i % ncopy], Z, w.K, out=out), 100) * 1e3, 3),
+        "read_reference_us_per_launch": round(graph_replay_ms(
+            lambda i: rrt.read_reference(pool[i % ncopy], L, out=keys), 100) * 1e3, 3),
     }
     del pool
     torch.cuda.empty_cache()
