@@ -1827,11 +1827,18 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kern
   float* vout = p.out_val != nullptr ? p.out_val + (int64_t)row * p.K : nullptr;
 
   // Round 1: the chunk's top-digit (11-bit) histogram into the row's, then
-  // the row-wide threshold digit from a copy of the row's.
+  // the row-wide threshold digit from a copy of the row's.  (Loops over the
+  // slice test it once per group of 4 slots, and adds that count nothing go
+  // to the lane's sink word, as in range_select.)
+  uint32_t* const sink = &sm.sink[t & 63];
 #pragma unroll
-  for (int j = 0; j < S; ++j) {
-    if ((uint32_t)(j) < sp) {
-      if ((uint32_t)j < nv) atomicAdd(&sm.hist1[k[j] >> 21], 1u);
+  for (int q = 0; q < S / 4; ++q) {
+    if ((uint32_t)(4 * q) < sp) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int j = 4 * q + c;
+        atomicAdd((uint32_t)j < nv ? &sm.hist1[k[j] >> 21] : sink, 1u);
+      }
     }
   }
   __syncthreads();
@@ -1852,12 +1859,16 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kern
   __syncthreads();
   uint32_t n_above = 0;
 #pragma unroll
-  for (int j = 0; j < S; ++j) {
-    if ((uint32_t)(j) < sp) {
-      const bool valid = (uint32_t)j < nv;
-      const uint32_t km = k[j] & pmask;
-      if (valid && km == prefix) atomicAdd(&sm.hist1[(k[j] >> 10) & 2047u], 1u);
-      n_above += popc64(ballot(valid && km > prefix));
+  for (int q = 0; q < S / 4; ++q) {
+    if ((uint32_t)(4 * q) < sp) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int j = 4 * q + c;
+        const bool valid = (uint32_t)j < nv;
+        const uint32_t km = k[j] & pmask;
+        atomicAdd(valid && km == prefix ? &sm.hist1[(k[j] >> 10) & 2047u] : sink, 1u);
+        n_above += popc64(ballot(valid && km > prefix));
+      }
     }
   }
   wave_add(&sm.acc[0], n_above);
@@ -1879,12 +1890,16 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kern
     uint32_t mine = 0;
     n_above = 0;
 #pragma unroll
-    for (int j = 0; j < S; ++j) {
-      if ((uint32_t)(j) < sp) {
-        const bool valid = (uint32_t)j < nv;
-        const uint32_t km = k[j] & pmask;
-        mine += (valid && km == prefix) ? 1u : 0u;
-        n_above += popc64(ballot(valid && km > prefix));
+    for (int q = 0; q < S / 4; ++q) {
+      if ((uint32_t)(4 * q) < sp) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int j = 4 * q + c;
+          const bool valid = (uint32_t)j < nv;
+          const uint32_t km = k[j] & pmask;
+          mine += (valid && km == prefix) ? 1u : 0u;
+          n_above += popc64(ballot(valid && km > prefix));
+        }
       }
     }
     wave_add(&sm.acc[1], n_above);
@@ -1892,10 +1907,14 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kern
     uint32_t at = block_excl_scan(sm, mine, &len);
     uint32_t* my_list = lists + (uint64_t)g * CAP;
 #pragma unroll
-    for (int j = 0; j < S; ++j) {
-      if ((uint32_t)(j) < sp) {
-        const bool valid = (uint32_t)j < nv;
-        if (valid && (k[j] & pmask) == prefix) ws_store(&my_list[at++], k[j]);
+    for (int q = 0; q < S / 4; ++q) {
+      if ((uint32_t)(4 * q) < sp) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int j = 4 * q + c;
+          const bool valid = (uint32_t)j < nv;
+          if (valid && (k[j] & pmask) == prefix) ws_store(&my_list[at++], k[j]);
+        }
       }
     }
     if (t == 0) {
