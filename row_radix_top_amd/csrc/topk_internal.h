@@ -71,9 +71,10 @@ constexpr uint32_t kErrSearch = 2u;
 //   256  per-workgroup slots, 4 x u32 each: [above digit 1, above digit 2, list length, -]
 //   ...  digit-1 histogram, 2048 x u32
 //   ...  digit-2 histogram, 2048 x u32
+//   ...  their sums over groups of 32 bins, 64 x u32 each (digit 1, digit 2)
 //   ...  per-workgroup lists, cap x u32 each
 struct GroupLayout {
-  uint64_t slots, h1, h2, lists, bytes;
+  uint64_t slots, h1, h2, c1, c2, lists, bytes;
 };
 
 inline constexpr uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
@@ -83,7 +84,9 @@ inline constexpr GroupLayout group_layout(int wg_per_row, int cap) {
   L.slots = 256;
   L.h1 = L.slots + round_up(16ull * (uint64_t)wg_per_row, 256);
   L.h2 = L.h1 + 4ull * kBins;
-  L.lists = L.h2 + 4ull * kBins;
+  L.c1 = L.h2 + 4ull * kBins;
+  L.c2 = L.c1 + 256;
+  L.lists = L.c2 + 256;
   L.bytes = round_up(L.lists + 4ull * (uint64_t)cap * (uint64_t)wg_per_row, 256);
   return L;
 }

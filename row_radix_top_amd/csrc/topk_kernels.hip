@@ -1735,20 +1735,64 @@ __device__ void group_barrier(uint32_t* ctr, uint32_t target, uint32_t spin_limi
   __syncthreads();
 }
 
-// Adds an LDS histogram into a workspace histogram (non-zero bins only) and
-// zeroes the LDS copy.
-__device__ __forceinline__ void merge_hist(uint32_t* lds_hist, uint32_t* gh) {
-  for (int i = threadIdx.x; i < kBins; i += kBlock) {
-    const uint32_t v = lds_hist[i];
-    if (v) {
-      ws_add(gh + i, v);
-      lds_hist[i] = 0u;
+// Adds a complete LDS histogram into a workspace histogram (non-zero bins
+// only) and its sums over groups of 32 bins into the workspace's group sums
+// gc.  The LDS copy is left as it is.
+__device__ __forceinline__ void merge_hist(const uint32_t* lds_hist, uint32_t* gh, uint32_t* gc) {
+  const int t = threadIdx.x;
+  if (t < kBins / 32) {
+    const u32x4* grp = reinterpret_cast<const u32x4*>(lds_hist + t * 32);
+    uint32_t s = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const u32x4 v = grp[(c + t) & 7];  // rotated start: spreads the banks
+      s += (v.x + v.y) + (v.z + v.w);
     }
+    if (s) ws_add(gc + t, s);
+  }
+  for (int i = t; i < kBins; i += kBlock) {
+    const uint32_t v = lds_hist[i];
+    if (v) ws_add(gh + i, v);
   }
 }
 
-__device__ __forceinline__ void load_hist(uint32_t* lds_hist, const uint32_t* gh) {
-  for (int i = threadIdx.x; i < kBins; i += kBlock) lds_hist[i] = ws_load(gh + i);
+// The threshold search of wave_find<2048> run straight on a merged workspace
+// histogram: the 64 group sums first, then the 32 bins of the group holding
+// the krem-th largest entry (96 loads per wavefront instead of copying 2048
+// bins to LDS).  Wave-uniform result; every wavefront runs it itself.
+__device__ Found ws_find(const uint32_t* gh, const uint32_t* gc, uint32_t krem) {
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  const uint32_t s = ws_load(gc + (63 - lane));  // lane order is descending group order
+  const uint32_t incl = wave_incl_scan(s);
+  const uint64_t reach = ballot(incl >= krem);
+  Found f;
+  if (reach == 0) {  // fewer than krem entries: inconsistent histogram
+    f.bin = 0u;
+    f.above = 0u;
+    f.in_bin = lane_value(incl, 63);
+    f.ok = 0u;
+    return f;
+  }
+  const int lc = __builtin_ctzll(reach);
+  const uint32_t before = lane_value(incl, lc) - lane_value(s, lc);
+  const int qc = 63 - lc;
+  const uint32_t v = lane < 32 ? ws_load(gh + qc * 32 + (31 - lane)) : 0u;
+  const uint32_t in2 = wave_incl_scan(v) + before;
+  const uint64_t reach2 = ballot(lane < 32 && in2 >= krem);
+  if (reach2 == 0) {  // the group's bins disagree with its sum: inconsistent
+    f.bin = (uint32_t)qc * 32u;
+    f.above = before;
+    f.in_bin = 0u;
+    f.ok = 0u;
+    return f;
+  }
+  const int l2 = __builtin_ctzll(reach2);
+  f.bin = (uint32_t)(qc * 32 + (31 - l2));
+  f.in_bin = lane_value(v, l2);
+  f.above = lane_value(in2, l2) - f.in_bin;
+  f.ok = 1u;
+  return f;
 }
 
 // Adds a wave-uniform count into an LDS accumulator (one lane per wave).
@@ -1807,6 +1851,8 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kern
   uint32_t* slots = reinterpret_cast<uint32_t*>(blk + lay.slots);
   uint32_t* h1 = reinterpret_cast<uint32_t*>(blk + lay.h1);
   uint32_t* h2 = reinterpret_cast<uint32_t*>(blk + lay.h2);
+  uint32_t* gs1 = reinterpret_cast<uint32_t*>(blk + lay.c1);
+  uint32_t* gs2 = reinterpret_cast<uint32_t*>(blk + lay.c2);
   uint32_t* lists = reinterpret_cast<uint32_t*>(blk + lay.lists);
 
   zero_histograms(sm);
@@ -1842,11 +1888,9 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kern
     }
   }
   __syncthreads();
-  merge_hist(sm.hist1, h1);
+  merge_hist(sm.hist1, h1, gs1);
   group_barrier(ctr, 1u * grow, p.spin_limit, err);
-  load_hist(sm.hist1, h1);
-  __syncthreads();
-  const Found f1 = wave_find<2048>(sm.hist1, K);
+  const Found f1 = ws_find(h1, gs1, K);
   uint32_t ok = f1.ok;
   uint32_t krem = K - f1.above;
   uint32_t prefix = f1.bin << 21;
@@ -1873,12 +1917,10 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kern
   }
   wave_add(&sm.acc[0], n_above);
   __syncthreads();
-  merge_hist(sm.hist1, h2);
+  merge_hist(sm.hist1, h2, gs2);
   if (t == 0) ws_store(&slots[4 * g + 0], sm.acc[0]);
   group_barrier(ctr, 2u * grow, p.spin_limit, err);
-  load_hist(sm.hist1, h2);
-  __syncthreads();
-  const Found f2 = wave_find<2048>(sm.hist1, krem);
+  const Found f2 = ws_find(h2, gs2, krem);
   ok &= f2.ok;
   krem -= f2.above;
   prefix |= f2.bin << 10;
@@ -1923,7 +1965,7 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kern
     }
   }
   group_barrier(ctr, 3u * grow, p.spin_limit, err);
-  for (int i = t; i < kBins; i += kBlock) sm.hist1[i] = 0u;  // every wave read round 2's copy before the barrier
+  for (int i = t; i < kBins; i += kBlock) sm.hist1[i] = 0u;  // round 2's local histogram was merged before the barrier
 
   // Every chunk's list, flattened: offsets by a prefix sum over the lengths.
   if (t < 64) {
@@ -1991,6 +2033,10 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kern
     for (int i = t; i < kBins; i += kBlock) {
       ws_store(&h1[i], 0u);
       ws_store(&h2[i], 0u);
+    }
+    if (t < kBins / 32) {
+      ws_store(&gs1[t], 0u);
+      ws_store(&gs2[t], 0u);
     }
     for (uint32_t i = t; i < total; i += kBlock) {
       const int gg = list_of(s_off, grow, i);
