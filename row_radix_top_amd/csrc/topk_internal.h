@@ -24,11 +24,13 @@ constexpr uint32_t kDefaultSpin = 1u << 24; // polls before a cooperative wait g
 // r = max(kSpecMinRank, ceil(kSpecNum / kSpecDen * K * 4096 / n)), when that
 // r is below K.  kSpecNum / kSpecDen is the safety factor over the expected
 // rank of the K-th best of the row; kSpecMinRank keeps the sample quantile
-// from resting on too few elements.  Shorter rows have too few tiles left to
-// repay the selection.
+// from resting on too few elements.  From 8192 elements on, speculating
+// beats the general path's compactions (alone on a CU, rows of 12288 and
+// 16383 elements took 20.6 and 24.2 us on the general path, 16384 took 13.4
+// wave by wave); below it the sample would be more than half the row.
 constexpr uint32_t kSpecNum = 3, kSpecDen = 2;
 constexpr uint32_t kSpecMinRank = 128;
-constexpr uint32_t kSpecMinLen = 16384;
+constexpr uint32_t kSpecMinLen = 8192;
 
 // Candidate buffer capacity: 5120 entries.  It must hold K = 2048 kept
 // entries plus one full tile, so a tile always fits after a compaction; the

@@ -1070,9 +1070,12 @@ __device__ __forceinline__ uint32_t quarter_of(uint32_t n) {
 }
 
 // Whether a row of n elements (n > K) goes wave by wave: long enough to
-// speculate, with a speculative rank below K.
+// speculate, every quarter holding the two full wave tiles of the sample
+// (true for every n >= 8704; below that only for n = 8192), and a
+// speculative rank below K.
 __device__ __forceinline__ bool wave_mode(uint32_t n, uint32_t K) {
   if (n < kSpecMinLen) return false;
+  if (n < 3u * quarter_of(n) + 2u * kWaveTile) return false;  // short last quarter
   const uint64_t want = ((uint64_t)kSpecNum * K * (2u * kTile) + (uint64_t)kSpecDen * n - 1) / ((uint64_t)kSpecDen * n);
   const uint32_t r = want > kSpecMinRank ? (uint32_t)want : kSpecMinRank;
   return r < K;
@@ -1171,7 +1174,7 @@ __device__ __forceinline__ bool stream_row_waves(Smem<LAY>& sm, const T* __restr
     load_wave_full<VEC>(qp + WT, x1);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // Every quarter holds at least 2560 elements (n >= kSpecMinLen): F >= 5.
+  // wave_mode(n, K): every quarter holds at least two full wave tiles, F >= 2.
   const uint32_t F = (qe - qs) / WT;
   float buf[PF][kElems];
 #pragma unroll

@@ -242,7 +242,11 @@ def test_wave_by_wave_rows(offset):
     rows, and load widths of 4, 2 and 1 elements."""
     rng = np.random.default_rng(61 + offset)
     stride = {0: 65536, 1: 65529, 2: 65530}[offset]   # load widths 4, 1, 2
-    lens = [16384, 16385, 16383, 20479, 40000, stride - 1, 49153, 30001]
+    # Wave-by-wave rows start at 8192 elements (below 8704 only n = 8192,
+    # where every quarter first holds the sample's two wave tiles); 8193 and
+    # 8703 take the general path with a speculative bound.
+    lens = [16384, 16385, 16383, 20479, 40000, stride - 1, 49153, 30001,
+            8192, 8193, 8703, 8704, 8705, 10239, 12288, 9000]
     rows = []
     for i, n in enumerate(lens):
         kind = i % 4

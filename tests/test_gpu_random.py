@@ -37,7 +37,8 @@ def _case(seed: int):
     elif kind == 1:
         lens = np.full(rows, stride)
     elif kind == 2:
-        lens = rng.choice([0, 1, K - 1, K, K + 1, 2047, 2048, 2049, 16383, 16384, 16385, stride, stride + 5, -3],
+        lens = rng.choice([0, 1, K - 1, K, K + 1, 2047, 2048, 2049, 8191, 8192, 8193, 8703, 8704, 16383, 16384,
+                           16385, stride, stride + 5, -3],
                           size=rows)
     else:
         lens = stride - rng.integers(0, 64, size=rows)
