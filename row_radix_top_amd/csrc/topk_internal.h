@@ -31,11 +31,6 @@ constexpr uint32_t kDefaultSpin = 1u << 24; // polls before a cooperative wait g
 constexpr uint32_t kSpecNum = 3, kSpecDen = 2;
 constexpr uint32_t kSpecMinRank = 128;
 constexpr uint32_t kSpecMinLen = 8192;
-// Rows streamed on the general path speculate from their first two tiles
-// from this length on (the bound is skipped when r >= K, as it is for every
-// K below 6145 elements): from 6145 to 8191 elements it saves the general
-// path's compaction.
-constexpr uint32_t kGeneralSpecMinLen = 2u * kTile;
 
 // Candidate buffer capacity: 5120 entries.  It must hold K = 2048 kept
 // entries plus one full tile, so a tile always fits after a compaction; the

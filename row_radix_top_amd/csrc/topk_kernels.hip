@@ -924,7 +924,7 @@ __device__ __forceinline__ void process_tile(Smem<LAY>& sm, const float (&x)[kEl
 }
 
 // The speculative bound for a row of n elements whose first two tiles are
-// in x0 and x1 (n >= kGeneralSpecMinLen): the key of (about) the r-th best of those
+// in x0 and x1 (n >= kSpecMinLen): the key of (about) the r-th best of those
 // 4096 elements, r = max(kSpecMinRank, ceil(kSpecNum / kSpecDen * K * 4096 / n)),
 // or 0 (no bound) when r >= K.  The bin holding the r-th best is taken whole
 // when it is small, which only lowers the bound.  The caller checks at the
@@ -973,7 +973,7 @@ __device__ __forceinline__ uint32_t spec_bound(Smem<LAY>& sm, float (&x0)[kElems
 // it (a cache hit), which keeps the load pattern identical every iteration.
 // The partial last tile is loaded with per-element bounds checks.
 //
-// spec = the row length (>= kGeneralSpecMinLen) to start from a speculative bound
+// spec = the row length (>= kSpecMinLen) to start from a speculative bound
 // taken from the first two tiles (see spec_bound), else 0.  Those two tiles
 // go through x0 and x1 ahead of the ring, which starts at tile 2 with its
 // loads issued before the bound is computed; with preloaded they were
@@ -1618,7 +1618,7 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_single_ker
       }
       if (general) {
         cnt = 0u;  // a failed wave-by-wave attempt leaves its count behind
-        const uint32_t spec = (piece || redo || n < (int64_t)kGeneralSpecMinLen) ? 0u : (uint32_t)n;
+        const uint32_t spec = (piece || redo || n < (int64_t)kSpecMinLen) ? 0u : (uint32_t)n;
         stream_chunk<LAY, VEC>(sm, rowp, g0, g1, K, cnt, gL, spec, x0, x1, have_pre);
         have_pre = false;
         if (!piece && cnt < K && !redo) {
@@ -1683,7 +1683,7 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_single_ker
     }
     // Prefetch for the next unit unless it is a chunk with nothing to do.
     const bool npiece = SPLIT && nc >= 0 && splits((uint32_t)nn, K, CH);
-    if (nunit < U && nn >= (int64_t)kGeneralSpecMinLen && nn > (int64_t)K && (nc <= 0 || npiece)) {
+    if (nunit < U && nn >= (int64_t)kSpecMinLen && nn > (int64_t)K && (nc <= 0 || npiece)) {
       // The next unit's first two tiles: per wavefront quarter (the row's
       // sample) when it will go wave by wave or is a chunk, else the row's
       // first two tiles.
