@@ -1867,7 +1867,19 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kern
   const E* rowp = row_of<E>(p, row);
   uint32_t cnt = 0, L = 0;
   float x0[kElems], x1[kElems];
-  stream_chunk<LAY, VEC>(sm, rowp, (uint32_t)c0, (uint32_t)c1, K, cnt, L, 0u, x0, x1, false);
+  // The chunk speculates from its first two tiles, as a general-path row
+  // does: the bound keeps its candidates below the buffer's capacity, so no
+  // compaction runs.  Every chunk element below the bound is beaten by the
+  // cnt >= K kept ones; if fewer than K reached it, the chunk is streamed
+  // again without one.
+  const uint32_t clen = (uint32_t)(c1 - c0);
+  stream_chunk<LAY, VEC>(sm, rowp, (uint32_t)c0, (uint32_t)c1, K, cnt, L, clen >= 2u * kTile ? clen : 0u, x0, x1,
+                         false);
+  if (cnt < K && clen > K) {
+    cnt = 0u;
+    L = 0u;
+    stream_chunk<LAY, VEC>(sm, rowp, (uint32_t)c0, (uint32_t)c1, K, cnt, L, 0u, x0, x1, false);
+  }
 
   const Slice sl = plain_slice<LAY>(cnt);
   const uint32_t sp = sl.sp, nv = sl.nv;
