@@ -27,6 +27,12 @@
  * Return values are topk_status codes.  On failure a description is
  * available from topk_ragged_last_error() (thread-local).  A kernel that
  * faults reports at the caller's next synchronisation, like any HIP op.
+ *
+ * Scores are ordinary IEEE fp32 values (or bf16, widened exactly).  A NaN in
+ * a row's valid prefix is outside the contract: NaNs are never selected, so
+ * a row with fewer than K non-NaN values among its first lengths[r] entries
+ * gets undefined output.  Entries at or past lengths[r] are never read and
+ * may hold anything, NaN included.
  */
 #ifndef TOPK_RAGGED_H
 #define TOPK_RAGGED_H
@@ -116,10 +122,10 @@ int topk_ragged_offsets(const float* scores, int64_t row_stride, const int32_t* 
  *                out_val[r, i] = the fp32 score at out_idx[r, i] (its exact
  *                bits, -0.0 included) for i < min(K, n_r), -inf after that.
  *
- * The values are gathered by a second kernel on the same stream, after the
- * selection; both launches can be captured in one graph.  Other arguments and
- * errors as for topk_ragged; a null out_val with num_rows > 0 is
- * TOPK_EINVAL.
+ * The selection writes the values itself, in the same single launch: each
+ * chosen entry's stored fp32 bits go out beside its index, so no score is
+ * read twice and -0.0 stays -0.0.  Other arguments and errors as for
+ * topk_ragged; a null out_val with num_rows > 0 is TOPK_EINVAL.
  */
 int topk_ragged_values(const float* scores, int64_t row_stride, const int32_t* lengths,
                        const int32_t* row_offsets, int32_t num_rows, int32_t next_n, int32_t K,
@@ -175,18 +181,46 @@ int topk_ragged_bf16(const uint16_t* scores, int64_t row_stride, const int32_t* 
                      int32_t* out_idx, float* out_val, void* workspace, hipStream_t stream);
 
 /* Bytes of workspace topk_ragged needs for this shape on the stream's device.
+ * The PR #41444 page (risk section) relies on the workspace being large
+ * enough and on a check that it is; here the size is a function of the
+ * launch plan, and a launch that needs one and is given NULL fails with
+ * TOPK_EWORKSPACE.
+ *
+ *   num_rows, row_stride, K  as for topk_ragged (same ranges and errors).
+ *   stream                   selects the device whose properties the plan uses.
+ *   bytes                    host pointer, receives the size; must not be NULL
+ *                            (TOPK_EINVAL).
+ *
  * *bytes = 0 means no workspace is used: one workgroup per row and no more
- * rows than resident workgroups.  With more rows than that, a 256-byte
- * workspace holds the counter that hands rows to workgroups as they finish;
- * rows split over several workgroups need a block per row on top. */
+ * rows than resident workgroups (the PR #41748 page, Motivation: rows up to
+ * the radix threshold need no workspace).  With more rows than that, a
+ * 256-byte workspace holds the counter that hands rows to workgroups as they
+ * finish; rows split over several workgroups need a block per row on top. */
 int topk_ragged_workspace_size(int32_t num_rows, int64_t row_stride, int32_t K,
                                hipStream_t stream, size_t* bytes);
 
-/* One-time zeroing of a freshly allocated workspace, asynchronous on stream
- * (a small fill kernel, not a memset node).  Not needed between launches. */
+/* One-time zeroing of a freshly allocated workspace.  The PR #41748 page
+ * (Motivation) replaces a per-call memset of the workspace with cleanup at
+ * the end of the kernel; this call is the zeroing that remains, once per
+ * allocation.  Every launch leaves the workspace all-zero again, so it is
+ * not needed between launches, only after a failed launch.
+ *
+ *   workspace  device pointer, 4-byte aligned; may be NULL when bytes == 0.
+ *   bytes      a multiple of 4.
+ *   stream     the fill runs asynchronously on it, as a small kernel (not a
+ *              memset node, so it can be captured in a graph).
+ *
+ * Errors: TOPK_EINVAL for a NULL or misaligned workspace with bytes > 0;
+ * TOPK_ELAUNCH if the fill kernel cannot be launched.  The caller owns the
+ * memory. */
 int topk_ragged_workspace_init(void* workspace, size_t bytes, hipStream_t stream);
 
-/* Diagnostic text for the last failing call on this host thread ("" if none). */
+/* Diagnostic text for the last failing call on this host thread ("" if none):
+ * the counterpart of the checks with messages that the PR #41189 page's
+ * topk.cu excerpt raises (for example when the occupancy query fails, with
+ * the HIP error string, or when a launch would oversubscribe, with the plan's
+ * numbers).  The pointer stays valid until the next failing call on the same
+ * thread; the library owns it. */
 const char* topk_ragged_last_error(void);
 
 /* ---------------------------------------------------------------------------
