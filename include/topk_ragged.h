@@ -341,6 +341,32 @@ int topk_ragged_debug_keys(const uint32_t* bits, uint32_t* keys, int64_t n, hipS
 int topk_ragged_read_reference(const float* scores, int64_t row_stride, const int32_t* lengths,
                                int32_t num_rows, uint32_t* row_max_keys, hipStream_t stream);
 
+/*
+ * topk_ragged_noalloc -- topk_ragged without a workspace argument, for
+ * callers that cannot allocate device memory: code under hipGraph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Arguments, results and errors are those of topk_ragged.  Where a launch
+ * needs a workspace it uses a library-owned static device array of
+ * TOPK_RAGGED_NOALLOC_SCRATCH_BYTES (8 MiB) instead: one per GPU, held
+ * from the first call on that GPU until the process ends.  The call never
+ * allocates or frees device memory.
+ *   - A launch whose plan needs more than that fails with TOPK_EWORKSPACE
+ *     and launches nothing (topk_ragged_workspace_size gives the need: the
+ *     prefill-shaped batches need 256 bytes, the long-row batches about
+ *     0.35 MB per row).
+ *   - The first call on a GPU also queues a fill kernel on `stream` that
+ *     zeroes the array, ahead of its own launch; every launch leaves the
+ *     array all-zero again (in-kernel cleanup).
+ *   - Every call on a GPU shares that GPU's array: calls that may overlap
+ *     on one GPU (different streams, or different host threads without
+ *     ordering) race and give undefined results.  Serialise them.
+ */
+#define TOPK_RAGGED_NOALLOC_SCRATCH_BYTES (8u << 20)
+int topk_ragged_noalloc(const float* scores, int64_t row_stride, const int32_t* lengths,
+                        int32_t num_rows, int32_t next_n, int32_t K, int32_t* out_idx,
+                        hipStream_t stream);
+
 /* Library version: major * 10000 + minor * 100 + patch. */
 int topk_ragged_version(void);
 

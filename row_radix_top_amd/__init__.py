@@ -8,6 +8,7 @@ HIP library ``lib/libtopk_ragged.so``; this package only marshals arguments.
 
 from .binding import (  # noqa: F401
     MAX_K,
+    NOALLOC_SCRATCH_BYTES,
     RADIX_THRESHOLD,
     PATH_MULTI,
     PATH_NONE,
@@ -22,6 +23,7 @@ from .binding import (  # noqa: F401
     strided_workspace_size,
     topk_ragged,
     topk_ragged_bf16,
+    topk_ragged_noalloc,
     topk_ragged_strided,
     topk_ragged_values,
     workspace_init,

@@ -28,7 +28,9 @@ EXPORTED = (
     "topk_ragged_debug_keys", "topk_ragged_version", "topk_ragged_read_reference",
     "topk_ragged_offsets", "topk_ragged_offsets_ex", "topk_ragged_values", "topk_ragged_values_ex",
     "topk_ragged_strided", "topk_ragged_strided_workspace_size", "topk_ragged_bf16", "topk_ragged_bf16_ex",
+    "topk_ragged_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class DeviceProps(ctypes.Structure):
@@ -96,6 +98,7 @@ def load() -> ctypes.CDLL:
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         lib.topk_ragged.argtypes = [vp, i64, vp, i32, i32, i32, vp, vp, vp]
         lib.topk_ragged_ex.argtypes = [vp, i64, vp, i32, i32, i32, vp, vp, vp, ctypes.POINTER(Overrides)]
+        lib.topk_ragged_noalloc.argtypes = [vp, i64, vp, i32, i32, i32, vp, vp]
         lib.topk_ragged_workspace_size.argtypes = [i32, i64, i32, vp, ctypes.POINTER(sz)]
         lib.topk_ragged_workspace_size_ex.argtypes = [vp, i32, i64, i32, ctypes.POINTER(Overrides), vp,
                                                       ctypes.POINTER(sz)]
@@ -379,6 +382,24 @@ def topk_ragged(scores, lengths, K: int, *, out=None, workspace=None, next_n: in
         rc = lib.topk_ragged_ex(scores.data_ptr(), scores.stride(0), lengths.data_ptr(), num_rows,
                                 next_n, K, out.data_ptr(), ws_ptr, sp, ctypes.byref(ov))
     _check(rc, "topk_ragged")
+    return out
+
+
+def topk_ragged_noalloc(scores, lengths, K: int, *, out=None, next_n: int | None = None, stream=None):
+    """topk_ragged without a workspace argument: a launch that needs one
+    uses the library's static per-device scratch array (at most
+    NOALLOC_SCRATCH_BYTES).  Calls on one GPU share that array, so calls
+    that may overlap must be serialised by the caller."""
+    import torch
+    if next_n is None:
+        next_n = int(lengths.shape[1]) if lengths.dim() == 2 else 1
+    _validate(scores, lengths, out, K)
+    num_rows = scores.shape[0]
+    if out is None:
+        out = torch.empty((num_rows, K), dtype=torch.int32, device=scores.device)
+    rc = load().topk_ragged_noalloc(scores.data_ptr(), scores.stride(0), lengths.data_ptr(), num_rows, next_n, K,
+                                    out.data_ptr(), _stream_ptr(stream, scores.device))
+    _check(rc, "topk_ragged_noalloc")
     return out
 
 

@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libtopk_ragged.so")
-SOURCES = [os.path.join(CSRC, "topk_kernels.hip"), os.path.join(CSRC, "topk_host.cpp")]
+SOURCES = [os.path.join(CSRC, "topk_kernels.hip"), os.path.join(CSRC, "topk_host.cpp"),
+           os.path.join(CSRC, "topk_noalloc.hip")]
 
 HIP_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared",

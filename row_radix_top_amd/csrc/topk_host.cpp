@@ -412,7 +412,7 @@ namespace {
 
 int launch(const void* scores, int64_t row_stride, const int32_t* lengths, const int32_t* row_offsets,
            int32_t num_rows, int32_t next_n, int32_t K, int32_t* out_idx, void* workspace, hipStream_t stream,
-           const topk_overrides* ov, float* out_val = nullptr, bool bf16 = false) {
+           const topk_overrides* ov, float* out_val = nullptr, bool bf16 = false, bool noalloc = false) {
   if (num_rows < 0) return fail(TOPK_EINVAL, "num_rows must be >= 0");
   if (next_n < 1) return fail(TOPK_EINVAL, "next_n must be >= 1");
   if (num_rows % next_n != 0) return fail(TOPK_EINVAL, "num_rows must be a multiple of next_n");
@@ -434,8 +434,20 @@ int launch(const void* scores, int64_t row_stride, const int32_t* lengths, const
     ov = &ov_idx32;
   }
   topk_plan plan;
-  rc = plan_for_call(scores, num_rows, row_stride, K, ov, stream, nullptr, &plan, bf16);
+  int dev = 0;
+  rc = plan_for_call(scores, num_rows, row_stride, K, ov, stream, &dev, &plan, bf16);
   if (rc != TOPK_OK) return rc;
+  if (noalloc && plan.workspace_bytes > 0) {
+    // The library's static scratch array stands in for the workspace.
+    if (plan.workspace_bytes > rrt::kNoallocScratchBytes)
+      return fail(TOPK_EWORKSPACE, "this launch needs " + std::to_string(plan.workspace_bytes) +
+                                       " bytes of workspace; the allocation-free entry point's scratch holds " +
+                                       std::to_string(rrt::kNoallocScratchBytes) + " (" + describe(plan) + ")");
+    const char* what = "";
+    const int e = rrt::noalloc_scratch(dev, stream, &workspace, &what);
+    if (e != 0)
+      return fail(TOPK_EDEVICE, std::string(what) + ": " + hipGetErrorString(static_cast<hipError_t>(e)));
+  }
   if (plan.workspace_bytes > 0 && workspace == nullptr)
     return fail(TOPK_EWORKSPACE, "this launch needs a workspace of " + std::to_string(plan.workspace_bytes) +
                                      " bytes (" + describe(plan) + ")");
@@ -497,6 +509,12 @@ int topk_ragged_ex(const float* scores, int64_t row_stride, const int32_t* lengt
 int topk_ragged(const float* scores, int64_t row_stride, const int32_t* lengths, int32_t num_rows,
                 int32_t next_n, int32_t K, int32_t* out_idx, void* workspace, hipStream_t stream) {
   return launch(scores, row_stride, lengths, nullptr, num_rows, next_n, K, out_idx, workspace, stream, nullptr);
+}
+
+int topk_ragged_noalloc(const float* scores, int64_t row_stride, const int32_t* lengths, int32_t num_rows,
+                        int32_t next_n, int32_t K, int32_t* out_idx, hipStream_t stream) {
+  return launch(scores, row_stride, lengths, nullptr, num_rows, next_n, K, out_idx, nullptr, stream, nullptr,
+                nullptr, false, true);
 }
 
 int topk_ragged_offsets(const float* scores, int64_t row_stride, const int32_t* lengths,

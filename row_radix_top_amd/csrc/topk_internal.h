@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <hip/hip_runtime_api.h>
+
 namespace rrt {
 
 constexpr int kBlock = 256;                 // threads per workgroup (4 wave64)
@@ -136,6 +138,13 @@ struct KernelParams {
 // layout (K up to kMaxKBig).
 const void* kernel_ptr(int path, int vec, bool idx16, bool vals = false, bool bf16 = false, bool big_k = false);
 const void* zero_kernel_ptr();
+
+// Allocation-free launches (topk_ragged_noalloc) take their workspace from a
+// static device array of this many bytes per device (topk_noalloc.hip).
+constexpr uint64_t kNoallocScratchBytes = 8ull << 20;
+// Device address of dev's scratch array (set up on first use, zeroed by a
+// fill kernel on stream); 0 or a HIP error code, *msg naming the step.
+int noalloc_scratch(int dev, hipStream_t stream, void** out, const char** msg);
 const void* keys_kernel_ptr();
 const void* pack_kernel_ptr();
 int lds_bytes_of(bool idx16, bool big_k = false);
