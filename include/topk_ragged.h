@@ -240,6 +240,12 @@ typedef struct {
   int32_t max_lds_per_block;
   int32_t occupancy_single16;  /* one workgroup per row kernel, 16-bit indices */
   int32_t occupancy_multi16;   /* several workgroups per row kernel, 16-bit indices */
+  /* The same four occupancies (single, multi, single16, multi16) of the
+   * 512- and 1024-thread instances; 0 where the library has no such
+   * instance or it cannot be resident.  The fields above describe the
+   * 256-thread instances. */
+  int32_t occupancy_w512[4];
+  int32_t occupancy_w1024[4];
 } topk_device_props;
 
 typedef enum {
@@ -253,7 +259,7 @@ typedef struct {
   int32_t kmax;           /* largest K the kernel instance handles: 2048, or 4096 for the
                              large layout that K above 2048 takes */
   int32_t vec;            /* elements per load: 4, 2 or 1 (fp32), 8 or 1 (bf16) */
-  int32_t block;          /* threads per workgroup */
+  int32_t block;          /* threads per workgroup: 256, or 512 / 1024 (8 or 16 wavefronts per row) */
   int32_t grid;           /* workgroups launched */
   int32_t wg_per_row;     /* G (1 on the single path) */
   int64_t chunk;          /* elements of a row per workgroup (multi path) */
@@ -281,8 +287,8 @@ typedef struct {
   int64_t split_chunk;       /* 0 auto, else elements per chunk (a multiple of 2048) */
   int32_t max_occupancy;     /* 0 the device's, else plan as if no instance could keep more
                                 workgroups per CU resident (emulates a smaller device) */
-  int32_t force_idx32;       /* 1: never keep 16-bit candidate indices (testing; also what
-                                values with K above 2048 need) */
+  int32_t force_idx32;       /* 1: never keep 16-bit candidate indices (testing) */
+  int32_t force_block;       /* 0 auto, else threads per workgroup: 256, 512 or 1024 */
 } topk_overrides;
 
 /* Pure planning function (host only, no GPU needed).  vec_allowed is the

@@ -36,7 +36,8 @@ NOALLOC_SCRATCH_BYTES = 8 << 20
 class DeviceProps(ctypes.Structure):
     _fields_ = [("num_cus", ctypes.c_int32), ("occupancy_single", ctypes.c_int32),
                 ("occupancy_multi", ctypes.c_int32), ("max_lds_per_block", ctypes.c_int32),
-                ("occupancy_single16", ctypes.c_int32), ("occupancy_multi16", ctypes.c_int32)]
+                ("occupancy_single16", ctypes.c_int32), ("occupancy_multi16", ctypes.c_int32),
+                ("occupancy_w512", ctypes.c_int32 * 4), ("occupancy_w1024", ctypes.c_int32 * 4)]
 
 
 class Plan(ctypes.Structure):
@@ -58,7 +59,7 @@ class Overrides(ctypes.Structure):
                 ("force_chunk", ctypes.c_int64), ("spin_limit", ctypes.c_uint32),
                 ("min_chunk", ctypes.c_int32), ("split_rows", ctypes.c_int32),
                 ("split_g", ctypes.c_int32), ("split_chunk", ctypes.c_int64), ("max_occupancy", ctypes.c_int32),
-                ("force_idx32", ctypes.c_int32)]
+                ("force_idx32", ctypes.c_int32), ("force_block", ctypes.c_int32)]
 
     @classmethod
     def make(cls, **kw) -> "Overrides | None":
@@ -150,10 +151,14 @@ def _ov_ptr(ov: Overrides | None):
 def plan_for_props(num_cus: int, occupancy_single: int, occupancy_multi: int, num_rows: int,
                    row_stride: int, K: int, vec_allowed: int = 4, max_lds_per_block: int = 163840,
                    occupancy_single16: int | None = None, occupancy_multi16: int | None = None,
-                   **overrides) -> dict:
+                   occupancy_w512=(0, 0, 0, 0), occupancy_w1024=(0, 0, 0, 0), **overrides) -> dict:
+    """The pure planner on made-up device facts.  occupancy_w512 and
+    occupancy_w1024 are (single, multi, single16, multi16) of the wider
+    instances; zeros mean there are none."""
     props = DeviceProps(num_cus, occupancy_single, occupancy_multi, max_lds_per_block,
                         occupancy_single if occupancy_single16 is None else occupancy_single16,
-                        occupancy_multi if occupancy_multi16 is None else occupancy_multi16)
+                        occupancy_multi if occupancy_multi16 is None else occupancy_multi16,
+                        (ctypes.c_int32 * 4)(*occupancy_w512), (ctypes.c_int32 * 4)(*occupancy_w1024))
     plan = Plan()
     ov = Overrides.make(**overrides)
     rc = load().topk_ragged_plan(ctypes.byref(props), num_rows, row_stride, K, vec_allowed,

@@ -8,10 +8,8 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
-#include <map>
-#include <mutex>
+#include <atomic>
 #include <string>
-#include <tuple>
 
 #include "topk_internal.h"
 #include "topk_ragged.h"
@@ -27,7 +25,6 @@ int fail(int code, const std::string& msg) {
 
 constexpr int64_t kDefaultMinChunk = 8192;
 constexpr int64_t kSplitMinChunk = 8192;
-constexpr bool kAutoSplit = false;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -53,64 +50,85 @@ std::string describe(const topk_plan& p) {
 
 // ---------------------------------------------------------------------------
 // Device facts, cached per device (the stream's device, looked up per call,
-// so a cached value can never belong to another device).
+// so a cached value can never belong to another device).  After the first
+// call on a device every lookup is a plain array read: the entries are
+// atomics filled once (a query is deterministic, so two threads filling the
+// same entry store the same value) and no lock is taken.
 // ---------------------------------------------------------------------------
-struct DevInfo {
-  int num_cus = 0;
-  int max_lds_block = 0;
-  std::map<std::tuple<int, int, int, int, int>, int> occ;  // (path, vec, idx16, bf16, big K) -> WGs per CU
+constexpr int kMaxDevices = 64;
+
+// Occupancy entries: (path single / multi / read reference) x (vec 1, 2, 4,
+// 8) x idx16 x bf16 x big K x (block 256, 512, 1024).
+constexpr int kOccEntries = 3 * 4 * 2 * 2 * 2 * 3;
+
+struct DevCache {
+  std::atomic<int> num_cus{0};  // 0 until the attributes were read
+  std::atomic<int> max_lds_block{0};
+  std::atomic<int> occ[kOccEntries];  // -1 unknown, else workgroups per CU (0: no such instance)
+  DevCache() {
+    for (auto& o : occ) o.store(-1, std::memory_order_relaxed);
+  }
 };
 
-std::mutex g_mu;
-std::map<int, DevInfo> g_dev;
+DevCache g_dev[kMaxDevices];
 
 int stream_device(hipStream_t stream, int* dev) {
   hipError_t e = stream == nullptr ? hipGetDevice(dev) : hipStreamGetDevice(stream, dev);
   if (e != hipSuccess)
     return fail(TOPK_EDEVICE, std::string("cannot find the stream's device: ") + hipGetErrorString(e));
+  if (*dev < 0 || *dev >= kMaxDevices) return fail(TOPK_EDEVICE, "device ordinal beyond the library's table");
   return TOPK_OK;
 }
 
-int device_info(int dev, DevInfo** out) {
-  std::lock_guard<std::mutex> lk(g_mu);
-  auto it = g_dev.find(dev);
-  if (it == g_dev.end()) {
-    DevInfo d;
-    hipError_t e = hipDeviceGetAttribute(&d.num_cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess)
-      e = hipDeviceGetAttribute(&d.max_lds_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+int device_info(int dev, DevCache** out) {
+  DevCache& d = g_dev[dev];
+  if (d.num_cus.load(std::memory_order_acquire) == 0) {
+    int cus = 0, lds = 0;
+    hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
     if (e != hipSuccess)
       return fail(TOPK_EDEVICE, std::string("device attribute query failed: ") + hipGetErrorString(e));
-    it = g_dev.emplace(dev, d).first;
+    if (cus < 1) return fail(TOPK_EDEVICE, "device reports no compute units");
+    d.max_lds_block.store(lds, std::memory_order_relaxed);
+    d.num_cus.store(cus, std::memory_order_release);
   }
-  *out = &it->second;
+  *out = &d;
   return TOPK_OK;
 }
 
-// Occupancy of the exact instance that will be launched.
-int occupancy(int dev, DevInfo* d, int path, int vec, bool idx16, int* occ, bool bf16 = false, bool big_k = false) {
-  std::lock_guard<std::mutex> lk(g_mu);
-  const auto key = std::make_tuple(path, vec, idx16 ? 1 : 0, bf16 ? 1 : 0, big_k ? 1 : 0);
-  auto it = d->occ.find(key);
-  if (it != d->occ.end()) {
-    *occ = it->second;
+int occ_slot(int path, int vec, bool idx16, bool bf16, bool big_k, int block) {
+  const int v = vec == 8 ? 3 : vec == 4 ? 2 : vec == 2 ? 1 : 0;
+  const int b = block == 1024 ? 2 : block == 512 ? 1 : 0;
+  const int pi = path == 2 ? 1 : path == 3 ? 2 : 0;
+  return (((((pi * 4 + v) * 2 + (idx16 ? 1 : 0)) * 2 + (bf16 ? 1 : 0)) * 2 + (big_k ? 1 : 0)) * 3) + b;
+}
+
+// Occupancy of the exact instance that will be launched (0 when the library
+// has no such instance).
+int occupancy(int dev, DevCache* d, int path, int vec, bool idx16, int* occ, bool bf16 = false, bool big_k = false,
+              int block = rrt::kBlock) {
+  std::atomic<int>& slot = d->occ[occ_slot(path, vec, idx16, bf16, big_k, block)];
+  const int cached = slot.load(std::memory_order_acquire);
+  if (cached >= 0) {
+    *occ = cached;
     return TOPK_OK;
   }
-  int cur = -1;
-  hipError_t e = hipGetDevice(&cur);
-  if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+  const void* fn = rrt::kernel_ptr(path, vec, idx16, false, bf16, big_k, block);
   int o = 0;
-  if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, rrt::kernel_ptr(path, vec, idx16, false, bf16, big_k),
-                                                     rrt::kBlock, 0);
-  if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
-  if (e != hipSuccess) {
-    char buf[256];
-    std::snprintf(buf, sizeof(buf), "occupancy query failed (path=%d vec=%d idx16=%d): %s", path, vec,
-                  idx16 ? 1 : 0, hipGetErrorString(e));
-    return fail(TOPK_EDEVICE, buf);
+  if (fn != nullptr) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, fn, block, 0);
+    if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess) {
+      char buf[256];
+      std::snprintf(buf, sizeof(buf), "occupancy query failed (path=%d vec=%d idx16=%d block=%d): %s", path, vec,
+                    idx16 ? 1 : 0, block, hipGetErrorString(e));
+      return fail(TOPK_EDEVICE, buf);
+    }
   }
-  d->occ[key] = o;
+  slot.store(o, std::memory_order_release);
   *occ = o;
   return TOPK_OK;
 }
@@ -138,19 +156,24 @@ int chosen_vec(int vec_allowed, const topk_overrides* ov, int* vec) {
   return TOPK_OK;
 }
 
-// Fills props for the load width vec of every kernel instance on device dev.
+// Fills props for the load width vec of every kernel instance on device dev:
+// the 256-thread instances and the wider ones (0 where none exists).
 // big_k: the instances of the large layout (K above 2048).
 int real_props(int dev, int vec, topk_device_props* props, bool bf16 = false, bool big_k = false) {
-  DevInfo* d = nullptr;
+  DevCache* d = nullptr;
   int rc = device_info(dev, &d);
   if (rc != TOPK_OK) return rc;
   std::memset(props, 0, sizeof(*props));
-  props->num_cus = d->num_cus;
-  props->max_lds_per_block = d->max_lds_block;
-  rc = occupancy(dev, d, 1, vec, false, &props->occupancy_single, bf16, big_k);
-  if (rc == TOPK_OK) rc = occupancy(dev, d, 2, vec, false, &props->occupancy_multi, bf16, big_k);
-  if (rc == TOPK_OK) rc = occupancy(dev, d, 1, vec, true, &props->occupancy_single16, bf16, big_k);
-  if (rc == TOPK_OK) rc = occupancy(dev, d, 2, vec, true, &props->occupancy_multi16, bf16, big_k);
+  props->num_cus = d->num_cus.load(std::memory_order_relaxed);
+  props->max_lds_per_block = d->max_lds_block.load(std::memory_order_relaxed);
+  int32_t* base[4] = {&props->occupancy_single, &props->occupancy_multi, &props->occupancy_single16,
+                      &props->occupancy_multi16};
+  for (int i = 0; i < 4 && rc == TOPK_OK; ++i)
+    rc = occupancy(dev, d, (i & 1) ? 2 : 1, vec, i >= 2, base[i], bf16, big_k, rrt::kBlock);
+  for (int i = 0; i < 4 && rc == TOPK_OK; ++i)
+    rc = occupancy(dev, d, (i & 1) ? 2 : 1, vec, i >= 2, &props->occupancy_w512[i], bf16, big_k, 512);
+  for (int i = 0; i < 4 && rc == TOPK_OK; ++i)
+    rc = occupancy(dev, d, (i & 1) ? 2 : 1, vec, i >= 2, &props->occupancy_w1024[i], bf16, big_k, 1024);
   return rc;
 }
 
@@ -164,6 +187,38 @@ int check_common(int32_t num_rows, int64_t row_stride, int32_t K) {
     return fail(TOPK_EUNSUPPORTED_K, buf);
   }
   return TOPK_OK;
+}
+
+// The four occupancies of the instances of one workgroup width.
+struct OccSet {
+  int single, multi, single16, multi16;
+};
+
+OccSet occ_for(const topk_device_props* p, int block) {
+  if (block == 512) return {p->occupancy_w512[0], p->occupancy_w512[1], p->occupancy_w512[2], p->occupancy_w512[3]};
+  if (block == 1024)
+    return {p->occupancy_w1024[0], p->occupancy_w1024[1], p->occupancy_w1024[2], p->occupancy_w1024[3]};
+  return {p->occupancy_single, p->occupancy_multi, p->occupancy_single16, p->occupancy_multi16};
+}
+
+// Workgroup width of the one-workgroup path when the caller does not force
+// one.
+int auto_block_single(const topk_device_props* p, int32_t num_rows, int64_t row_stride, int32_t K) {
+  (void)p;
+  (void)num_rows;
+  (void)row_stride;
+  (void)K;
+  return rrt::kBlock;
+}
+
+// Workgroup width of the multi-workgroup path when the caller does not
+// force one.
+int auto_block_multi(const topk_device_props* p, int32_t num_rows, int64_t row_stride, int32_t K) {
+  (void)p;
+  (void)num_rows;
+  (void)row_stride;
+  (void)K;
+  return rrt::kBlock;
 }
 
 int plan_for_call(const void* scores, int32_t num_rows, int64_t row_stride, int32_t K,
@@ -200,6 +255,10 @@ int topk_ragged_plan(const topk_device_props* props_in, int32_t num_rows, int64_
     for (int32_t* o : {&capped.occupancy_single, &capped.occupancy_multi, &capped.occupancy_single16,
                        &capped.occupancy_multi16})
       *o = std::min(*o, ov->max_occupancy);
+    for (int i = 0; i < 4; ++i) {
+      capped.occupancy_w512[i] = std::min(capped.occupancy_w512[i], ov->max_occupancy);
+      capped.occupancy_w1024[i] = std::min(capped.occupancy_w1024[i], ov->max_occupancy);
+    }
   }
   const topk_device_props* props = &capped;
   std::memset(plan, 0, sizeof(*plan));
@@ -211,6 +270,9 @@ int topk_ragged_plan(const topk_device_props* props_in, int32_t num_rows, int64_
   int vec = 4;
   rc = chosen_vec(vec_allowed, ov, &vec);
   if (rc != TOPK_OK) return rc;
+  const int want_block = ov != nullptr ? ov->force_block : 0;
+  if (want_block != 0 && want_block != 256 && want_block != 512 && want_block != 1024)
+    return fail(TOPK_EINVAL, "force_block must be 0, 256, 512 or 1024");
 
   // K above 2048 takes the large layout (more candidates, fewer workgroups
   // per CU); props must then describe those instances.
@@ -236,9 +298,15 @@ int topk_ragged_plan(const topk_device_props* props_in, int32_t num_rows, int64_
   // row_stride stands in for the longest length, which lives on the device.
   const bool long_rows = row_stride > TOPK_RAGGED_RADIX_THRESHOLD && row_stride > rrt::kSplitMinStride;
   if (want == TOPK_PATH_MULTI || (want == 0 && long_rows)) {
+    int block = want_block != 0 ? want_block : auto_block_multi(props, num_rows, row_stride, K);
+    OccSet os = occ_for(props, block);
+    if (want_block == 0 && std::min(os.multi, os.multi16) < 1) {
+      block = rrt::kBlock;  // no wider instance resident: the base one
+      os = occ_for(props, block);
+    }
     // Size with the less resident of the two instances; the chunk length then
     // picks the instance (16-bit indices when a chunk fits them).
-    const int occ = std::min(props->occupancy_multi, props->occupancy_multi16);
+    const int occ = std::min(os.multi, os.multi16);
     if (occ < 1) {
       if (want == TOPK_PATH_MULTI) return fail(TOPK_EDEVICE, "multi-workgroup kernel cannot be resident");
     } else {
@@ -252,7 +320,9 @@ int topk_ragged_plan(const topk_device_props* props_in, int32_t num_rows, int64_
         avail -= headroom;
       else
         headroom = 0;
-      const int64_t min_chunk = (ov != nullptr && ov->min_chunk > 0) ? ov->min_chunk : kDefaultMinChunk;
+      const int64_t tile = rrt::tile_of(rrt::layout_of(false, false, block));
+      const int64_t min_chunk =
+          (ov != nullptr && ov->min_chunk > 0) ? ov->min_chunk : std::max<int64_t>(kDefaultMinChunk, 2 * tile);
       int64_t G = 0, chunk = 0;
       if (ov != nullptr && ov->force_chunk > 0) {
         if (ov->force_chunk % 4 != 0) return fail(TOPK_EINVAL, "force_chunk must be a multiple of 4");
@@ -270,7 +340,7 @@ int topk_ragged_plan(const topk_device_props* props_in, int32_t num_rows, int64_
         if (G >= 1) {
           // Automatic chunks are whole tiles; a requested G keeps its count
           // (chunks only need 4-element alignment).
-          const uint64_t align = (ov != nullptr && ov->force_wg_per_row > 0) ? 4 : rrt::kTile;
+          const uint64_t align = (ov != nullptr && ov->force_wg_per_row > 0) ? 4 : (uint64_t)tile;
           chunk = (int64_t)rrt::round_up((uint64_t)ceil_div(row_stride, G), align);
           G = ceil_div(row_stride, chunk);
         }
@@ -285,15 +355,16 @@ int topk_ragged_plan(const topk_device_props* props_in, int32_t num_rows, int64_
         const int64_t grid = (int64_t)num_rows * G;
         if (grid <= avail) {
           const bool i16 = chunk <= rrt::kIdx16Limit && !idx32_only;
-          const rrt::GroupLayout lay = rrt::group_layout((int)G, rrt::cap_of(rrt::layout_of(i16, big)));
+          const rrt::GroupLayout lay = rrt::group_layout((int)G, rrt::cap_of(rrt::layout_of(i16, big, block)));
           plan->path = TOPK_PATH_MULTI;
+          plan->block = block;
           plan->idx16 = i16 ? 1 : 0;
           plan->wg_per_row = (int)G;
           plan->chunk = chunk;
           plan->grid = (int)grid;
           plan->resident_cap = (int)cap;
           plan->headroom = (int)headroom;
-          plan->lds_bytes = rrt::lds_bytes_of(i16, big);
+          plan->lds_bytes = rrt::lds_bytes_of(i16, big, block);
           plan->workspace_bytes = rrt::kWsHeader + (uint64_t)num_rows * lay.bytes;
           return TOPK_OK;
         }
@@ -307,24 +378,24 @@ int topk_ragged_plan(const topk_device_props* props_in, int32_t num_rows, int64_
   }
 
   const bool i16 = row_stride <= rrt::kIdx16Limit && !idx32_only;
-  const int occ = i16 ? props->occupancy_single16 : props->occupancy_single;
+  const int32_t want_split = ov != nullptr ? ov->split_rows : 0;
+  int block = want_block != 0 ? want_block : (want_split > 0 ? rrt::kBlock : auto_block_single(props, num_rows, row_stride, K));
+  if (want_split > 0 && block != rrt::kBlock)
+    return fail(TOPK_EINVAL, "split rows run on 256-thread workgroups only");
+  int occ = i16 ? occ_for(props, block).single16 : occ_for(props, block).single;
+  if (occ < 1 && want_block == 0 && block != rrt::kBlock) {
+    block = rrt::kBlock;  // no wider instance resident: the base one
+    occ = i16 ? props->occupancy_single16 : props->occupancy_single;
+  }
   if (occ < 1) return fail(TOPK_EDEVICE, "single-workgroup kernel cannot be resident");
   const int64_t cap = (int64_t)props->num_cus * occ;
 
   // Split rows: the last split_rows rows are cut into split_g chunks that
   // any workgroup takes as units of their own (no workgroup waits for
-  // another, so residency does not matter).  Automatic only when the rows
-  // are too few to give every resident workgroup one: then all rows are
-  // split, into as many chunks of at least kSplitMinChunk elements as the
-  // free slots allow.
+  // another, so residency does not matter).  Only when asked for: it
+  // measured slower than whole rows on every workload.
   int64_t split_rows = 0, split_g = 0, split_chunk = 0;
-  const int32_t want_split = ov != nullptr ? ov->split_rows : 0;
-  if (want_split > 0) {
-    split_rows = std::min<int64_t>(want_split, num_rows);
-  } else if (want_split == 0 && kAutoSplit && 2 * (int64_t)num_rows <= cap && row_stride >= (int64_t)rrt::kSpecMinLen &&
-             row_stride > kSplitMinChunk) {
-    split_rows = num_rows;
-  }
+  if (want_split > 0) split_rows = std::min<int64_t>(want_split, num_rows);
   if (split_rows > 0) {
     if (ov != nullptr && ov->split_g != 0) {
       if (ov->split_g < 1 || ov->split_g > rrt::kMaxSplit) return fail(TOPK_EINVAL, "split_g must be in [1, 16]");
@@ -350,13 +421,14 @@ int topk_ragged_plan(const topk_device_props* props_in, int32_t num_rows, int64_
   plan->split_g = (int32_t)split_g;
   plan->split_chunk = split_chunk;
   plan->path = TOPK_PATH_SINGLE;
+  plan->block = block;
   plan->wg_per_row = 1;
   plan->chunk = row_stride;
   plan->grid = (int)grid;
   plan->resident_cap = (int)cap;
   plan->headroom = 0;
   plan->idx16 = i16 ? 1 : 0;
-  plan->lds_bytes = rrt::lds_bytes_of(i16, big);
+  plan->lds_bytes = rrt::lds_bytes_of(i16, big, block);
   // More units than workgroups: later units are handed out by a ticket
   // counter in the workspace header.  Split rows add a block each.
   plan->workspace_bytes = (units > grid || split_rows > 0) ? rrt::kWsHeader : 0;
@@ -424,15 +496,7 @@ int launch(const void* scores, int64_t row_stride, const int32_t* lengths, const
   if (reinterpret_cast<uintptr_t>(out_idx) % 4 != 0 || reinterpret_cast<uintptr_t>(lengths) % 4 != 0 ||
       reinterpret_cast<uintptr_t>(scores) % (bf16 ? 2 : 4) != 0 || reinterpret_cast<uintptr_t>(row_offsets) % 4 != 0)
     return fail(TOPK_EINVAL, "scores must be aligned to their element; lengths, row_offsets and out_idx to 4 bytes");
-  // Values with K above 2048: the large layout stages them over 32-bit
-  // indices only (the 16-bit index array is too small).
   const bool big = K > rrt::kMaxK;
-  topk_overrides ov_idx32{};
-  if (out_val != nullptr && big) {
-    if (ov != nullptr) ov_idx32 = *ov;
-    ov_idx32.force_idx32 = 1;
-    ov = &ov_idx32;
-  }
   topk_plan plan;
   int dev = 0;
   rc = plan_for_call(scores, num_rows, row_stride, K, ov, stream, &dev, &plan, bf16);
@@ -464,7 +528,8 @@ int launch(const void* scores, int64_t row_stride, const int32_t* lengths, const
   kp.row_stride = row_stride;
   kp.chunk = plan.chunk;
   kp.group_bytes = plan.path == TOPK_PATH_MULTI
-                       ? rrt::group_layout(plan.wg_per_row, rrt::cap_of(rrt::layout_of(plan.idx16 != 0, big))).bytes
+                       ? rrt::group_layout(plan.wg_per_row, rrt::cap_of(rrt::layout_of(plan.idx16 != 0, big, plan.block)))
+                             .bytes
                        : 0;
   kp.num_rows = num_rows;
   kp.K = K;
@@ -483,7 +548,7 @@ int launch(const void* scores, int64_t row_stride, const int32_t* lengths, const
   // Split rows run on the one-workgroup kernel's split instance (same
   // occupancy: both are held to the same register and LDS budget).
   const int kpath = (plan.path == TOPK_PATH_SINGLE && plan.split_rows > 0) ? 4 : plan.path;
-  const void* fn = rrt::kernel_ptr(kpath, plan.vec, plan.idx16 != 0, out_val != nullptr, bf16, big);
+  const void* fn = rrt::kernel_ptr(kpath, plan.vec, plan.idx16 != 0, out_val != nullptr, bf16, big, plan.block);
   if (fn == nullptr) return fail(TOPK_EINVAL, "no kernel instance for this plan (" + describe(plan) + ")");
   hipError_t e = hipLaunchKernel(fn, dim3(plan.grid), dim3(plan.block), args, 0, stream);
   if (e == hipSuccess) e = hipGetLastError();
@@ -649,7 +714,7 @@ int topk_ragged_read_reference(const float* scores, int64_t row_stride, const in
   int dev = 0;
   int rc = stream_device(stream, &dev);
   if (rc != TOPK_OK) return rc;
-  DevInfo* d = nullptr;
+  DevCache* d = nullptr;
   rc = device_info(dev, &d);
   if (rc != TOPK_OK) return rc;
   const int vec = vec_allowed_for(scores, row_stride);
@@ -657,7 +722,7 @@ int topk_ragged_read_reference(const float* scores, int64_t row_stride, const in
   rc = occupancy(dev, d, 3, vec, false, &occ);
   if (rc != TOPK_OK) return rc;
   if (occ < 1) return fail(TOPK_EDEVICE, "read reference kernel cannot be resident");
-  const int64_t cap = (int64_t)d->num_cus * occ;
+  const int64_t cap = (int64_t)d->num_cus.load(std::memory_order_relaxed) * occ;
   const int64_t grid = num_rows < cap ? num_rows : cap;
   rrt::KernelParams kp{};
   kp.scores = scores;

@@ -1,0 +1,12 @@
+// Kernel instances of the 256-thread layout (kLayBigK): every load width, fp32
+// and bf16 scores, with and without split rows and values.
+#include "topk_instances.hpp"
+
+namespace rrt {
+
+const void* kernels_w256_l2(int lay, int path, int vec, bool vals, bool bf16) {
+  constexpr int L = kLayBigK;
+  return lay == L ? pick<L, true>(path, vec, vals, bf16) : nullptr;
+}
+
+}  // namespace rrt

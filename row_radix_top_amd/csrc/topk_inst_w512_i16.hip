@@ -1,0 +1,14 @@
+// Kernel instances of the 512-thread layouts with 16-bit candidate indices
+// (K up to 2048 and up to 4096): every load width, fp32 and bf16 scores.
+#include "topk_instances.hpp"
+
+namespace rrt {
+
+const void* kernels_w512_i16(int lay, int path, int vec, bool vals, bool bf16) {
+  constexpr int A = kLayW512 | kLayIdx16, B = kLayW512 | kLayIdx16 | kLayBigK;
+  if (lay == A) return pick<A, true>(path, vec, vals, bf16);
+  if (lay == B) return pick<B, true>(path, vec, vals, bf16);
+  return nullptr;
+}
+
+}  // namespace rrt

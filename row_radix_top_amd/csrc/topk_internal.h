@@ -9,12 +9,11 @@
 
 namespace rrt {
 
-constexpr int kBlock = 256;                 // threads per workgroup (4 wave64)
-constexpr int kWaves = kBlock / 64;
+constexpr int kBlock = 256;                 // threads per workgroup of the base instances (4 wave64)
 constexpr int kElems = 8;                   // fp32 elements per thread per tile
-constexpr int kTile = kBlock * kElems;      // 2048 elements streamed per tile
+constexpr int kTile = kBlock * kElems;      // 2048 elements per tile of the base instances
 constexpr int kBins = 2048;                 // bins of a first-pass histogram
-constexpr int kSmallBins = 256;             // bins of a second-pass histogram (= kBlock)
+constexpr int kSmallBins = 256;             // bins of a second-pass histogram
 constexpr int kPrefetch = 4;                // register ring of tiles per thread
 constexpr int kMaxGroup = 64;               // most workgroups that may share a row
 constexpr int kMaxK = 2048;
@@ -44,15 +43,41 @@ constexpr uint32_t kSpecMinLen = 8192;
 constexpr int kIdx16Limit = 65536;
 
 // Buffer layout of a kernel instance (a bit set): 16-bit candidate indices,
-// and room for K up to kMaxKBig.  The large layout holds 7168 candidates:
-// K plus a tile, and 1792 per wavefront for the ~1.5 K that survive a
-// speculative bound; its LDS footprint leaves two workgroups per CU.
+// room for K up to kMaxKBig, and the workgroup width (256 threads, or 512 /
+// 1024: 8 or 16 wavefronts on one row).  The capacity holds K plus one tile
+// (kElems per thread) for the general path, and about twice the ~1.5 K that
+// pass a speculative bound, split between the wavefronts.  256 threads:
+// 5120 (7168 for the large K), four workgroups per CU with 16-bit indices,
+// three with 32-bit ones, two for the large K.  512 threads: 6144 (8192),
+// two per CU (one for the large K with 32-bit indices).  1024 threads: 12288,
+// one per CU.  At most 16 wavefronts per CU in every case, so each keeps
+// 128 VGPRs (256 where fewer fit).
 constexpr int kLayIdx16 = 1;
 constexpr int kLayBigK = 2;
+constexpr int kLayW512 = 4;
+constexpr int kLayW1024 = 8;
 constexpr int kMaxKBig = 4096;
-constexpr int layout_of(bool idx16, bool big_k) { return (idx16 ? kLayIdx16 : 0) | (big_k ? kLayBigK : 0); }
-constexpr int cap_of(int lay) { return (lay & kLayBigK) ? 7168 : 5120; }
+constexpr int layout_of(bool idx16, bool big_k, int block = kBlock) {
+  return (idx16 ? kLayIdx16 : 0) | (big_k ? kLayBigK : 0) | (block == 1024 ? kLayW1024 : block == 512 ? kLayW512 : 0);
+}
+constexpr int block_of(int lay) { return (lay & kLayW1024) ? 1024 : (lay & kLayW512) ? 512 : kBlock; }
+constexpr int tile_of(int lay) { return block_of(lay) * kElems; }
+constexpr int cap_of(int lay) {
+  return block_of(lay) == 1024 ? 12288 : block_of(lay) == 512 ? ((lay & kLayBigK) ? 8192 : 6144)
+                                                              : ((lay & kLayBigK) ? 7168 : 5120);
+}
 constexpr int kmax_of(int lay) { return (lay & kLayBigK) ? kMaxKBig : kMaxK; }
+constexpr int resident_of(int lay) {
+  return block_of(lay) == 1024 ? 1
+       : block_of(lay) == 512 ? (((lay & kLayBigK) && !(lay & kLayIdx16)) ? 1 : 2)
+                              : ((lay & kLayBigK) ? 2 : ((lay & kLayIdx16) ? 4 : 3));
+}
+// Workgroup widths with instances: 256 for every load width and score type;
+// 512 for every load width of fp32 and bf16 scores, without split rows;
+// 1024 for fp32 scores only, without split rows.
+constexpr bool has_block(int block, bool bf16, bool split) {
+  return block == kBlock || (!split && (block == 512 || (block == 1024 && !bf16)));
+}
 
 // Rows are split over several workgroups only when longer than this (the
 // one-workgroup path streams shorter rows wave by wave faster than any
@@ -131,12 +156,26 @@ struct KernelParams {
 };
 
 // Kernel lookup for the host side.  path: 1 single, 2 multi, 3 the
-// streaming-read reference (idx16 ignored), 4 single with split rows.
-// vals: the one-workgroup instance that also writes the chosen scores (the
-// multi-workgroup kernel always can).
-// bf16: the instance that reads bf16 scores (vec 8 or 1); big_k: the large
-// layout (K up to kMaxKBig).
-const void* kernel_ptr(int path, int vec, bool idx16, bool vals = false, bool bf16 = false, bool big_k = false);
+// streaming-read reference (idx16, big_k and block ignored), 4 single with
+// split rows.  vals: the one-workgroup instance that also writes the chosen
+// scores (the multi-workgroup kernel always can).  bf16: the instance that
+// reads bf16 scores (vec 8 or 1); big_k: the large layout (K up to
+// kMaxKBig); block: threads per workgroup.  nullptr if no such instance.
+const void* kernel_ptr(int path, int vec, bool idx16, bool vals = false, bool bf16 = false, bool big_k = false,
+                       int block = kBlock);
+// Per instance file: the kernels of the layouts it compiles (nullptr for
+// others), and static LDS bytes per workgroup of a layout.
+const void* kernels_w256_l0(int lay, int path, int vec, bool vals, bool bf16);
+const void* kernels_w256_l1(int lay, int path, int vec, bool vals, bool bf16);
+const void* kernels_w256_l2(int lay, int path, int vec, bool vals, bool bf16);
+const void* kernels_w256_l3(int lay, int path, int vec, bool vals, bool bf16);
+const void* kernels_w512_i16(int lay, int path, int vec, bool vals, bool bf16);
+const void* kernels_w512_i32(int lay, int path, int vec, bool vals, bool bf16);
+const void* kernels_w1024_l0(int lay, int path, int vec, bool vals, bool bf16);
+const void* kernels_w1024_l1(int lay, int path, int vec, bool vals, bool bf16);
+const void* kernels_w1024_l2(int lay, int path, int vec, bool vals, bool bf16);
+const void* kernels_w1024_l3(int lay, int path, int vec, bool vals, bool bf16);
+const void* read_ref_kernel_ptr(int vec);
 const void* zero_kernel_ptr();
 
 // Allocation-free launches (topk_ragged_noalloc) take their workspace from a
@@ -147,6 +186,6 @@ constexpr uint64_t kNoallocScratchBytes = 8ull << 20;
 int noalloc_scratch(int dev, hipStream_t stream, void** out, const char** msg);
 const void* keys_kernel_ptr();
 const void* pack_kernel_ptr();
-int lds_bytes_of(bool idx16, bool big_k = false);
+int lds_bytes_of(bool idx16, bool big_k = false, int block = kBlock);
 
 }  // namespace rrt

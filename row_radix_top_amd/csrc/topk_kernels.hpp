@@ -48,17 +48,21 @@
 //   their candidates; the last to arrive selects over all of them, and no
 //   workgroup ever waits for another.
 //
-// Instances differ in the buffer layout (16-bit or 32-bit candidate indices;
-// room for K up to 2048 or 4096), the load width, the score type (fp32, or
-// bf16 widened exactly at the load), and whether the launch has split rows
-// or writes the chosen scores (compiled out otherwise, to keep the row
-// loop's registers).
+// Instances differ in the workgroup width (256, 512 or 1024 threads: 4, 8 or
+// 16 wavefronts share a row), the buffer layout (16-bit or 32-bit candidate
+// indices; room for K up to 2048 or 4096), the load width, the score type
+// (fp32, or bf16 widened exactly at the load), and whether the launch has
+// split rows or writes the chosen scores (compiled out otherwise, to keep the
+// row loop's registers).  This header holds the templates; the instance
+// files compile groups of them in parallel.
 //
 // The key function maps fp32 bits to uint32 so that unsigned order equals
 // IEEE order for non-NaN values, with -0.0 and +0.0 mapped to the same key.
 // Everything on the selection path is integer or bit manipulation except the
 // streaming compare x >= f(L), an exact IEEE comparison (denormals are kept:
 // the library is built without flush-to-zero).
+
+#pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -153,34 +157,36 @@ __device__ __forceinline__ uint32_t uni(uint32_t v) { return (uint32_t)__builtin
 
 template <int LAY>
 struct Shape {
+  static constexpr int kBlock = block_of(LAY);   // threads per workgroup
+  static constexpr int kWaves = kBlock / 64;
+  static constexpr int kTile = kBlock * kElems;  // elements one general-path tile covers
   static constexpr bool kIdx16 = (LAY & kLayIdx16) != 0;
   static constexpr int kMaxK = kmax_of(LAY);
   static constexpr int kCap = cap_of(LAY);
   static constexpr int kSlots = kCap / kBlock;  // buffer entries owned per thread
-  // Entries of the first histogram, which also stages the output ranks.
-  static constexpr int kStage = kMaxK > kBins ? kMaxK : kBins;
   using Idx = typename std::conditional<kIdx16, uint16_t, uint32_t>::type;
   static_assert(kCap % kBlock == 0 && kSlots % 4 == 0, "capacity must tile the workgroup in aligned runs");
-  static_assert(kCap % (kWaves * 64) == 0 && kCap / kWaves <= 64 * kSlots, "a wavefront's quarter fits its slices");
+  static_assert(kCap % (kWaves * 64) == 0 && kCap / kWaves <= 64 * kSlots, "a wavefront's part fits its slices");
+  static_assert(kWaves % 4 == 0 && kWaves <= 16, "per-wave partials are read four at a time");
   static_assert(kCap < 65536, "packed 16-bit counts");
   static_assert(kCap >= kMaxK + kTile, "a tile must fit after a compaction");
-  // Chosen scores are staged over the index array (see emit_chosen): the
-  // large layout with 16-bit indices has no room for them.
-  static constexpr bool kValues = (size_t)kCap * sizeof(Idx) >= 4u * (size_t)kMaxK;
   // Workgroups per CU the LDS footprint allows (160 KB per CU); the register
-  // budget is held to match.
-  static constexpr int kResident = (LAY & kLayBigK) ? 2 : (kIdx16 ? 4 : 3);
+  // budget is held to match (at most 16 wavefronts per CU: 128 VGPRs).
+  static constexpr int kResident = resident_of(LAY);
+  // HIP's second launch bound is waves per SIMD (four SIMDs per CU): the
+  // register budget that lets kResident workgroups share a CU.
+  static constexpr int kWavesPerSimd = kResident * kWaves / 4;
 };
 
 template <int LAY>
 struct __align__(16) Smem {
   uint32_t val[Shape<LAY>::kCap];                 // candidate fp32 bits, index order
   typename Shape<LAY>::Idx idx[Shape<LAY>::kCap];  // their indices, relative to the chunk start
-  uint32_t hist1[Shape<LAY>::kStage];             // digit histogram; all-zero outside a selection
+  uint32_t hist1[kBins];                          // digit histogram; all-zero outside a selection
   uint32_t hs[kSmallBins];                        // second digit histogram; all-zero outside a selection
-  uint32_t red[2 * kWaves];                       // per-wave partial results
-  uint32_t tile_cnt[2][kElems][kWaves];
-  uint32_t wsum[kWaves];
+  uint32_t red[2 * Shape<LAY>::kWaves];           // per-wave partial results
+  uint32_t tile_cnt[2][kElems][Shape<LAY>::kWaves];
+  uint32_t wsum[Shape<LAY>::kWaves];
   uint32_t acc[16];
   // Target of histogram adds that count nothing: one word per lane, so the
   // lanes of one add never collide on it (never read).
@@ -190,8 +196,8 @@ struct __align__(16) Smem {
   // the row block less that slot.
   __device__ uint32_t* part() { return &tile_cnt[0][0][0]; }
   __device__ uint32_t* delta() { return &tile_cnt[0][0][0] + (kMaxSplit + 1); }
+  static_assert(2 * kMaxSplit + 1 <= 2 * kElems * Shape<LAY>::kWaves, "merge offsets fit the tile-count area");
 };
-static_assert(2 * kMaxSplit + 1 <= 2 * kElems * kWaves, "merge offsets fit the tile-count area");
 
 // ---------------------------------------------------------------------------
 // Threshold search.  Every wavefront of the workgroup runs it on the same
@@ -253,28 +259,46 @@ __device__ __forceinline__ Found wave_find(const uint32_t* hist, uint32_t krem) 
   return f;
 }
 
-// Exclusive prefix sum of v over the workgroup in thread order; *total gets
-// the sum.  Contains one barrier.
+// Sum of v over the wavefront (every lane gets it), by DPP row shifts and
+// broadcasts.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) { return lane_value(wave_incl_scan(v), 63); }
+
+// Exclusive prefix over the wavefronts of the workgroup of a wave-uniform
+// value v (this wavefront's share): the sum of v over the lower wavefronts,
+// with the sum over all of them in *total.  One barrier; sm.wsum is free
+// again after the next barrier.
 template <int LAY>
-__device__ __forceinline__ uint32_t block_excl_scan(Smem<LAY>& sm, uint32_t v, uint32_t* total) {
+__device__ __forceinline__ uint32_t wave_exclusive(Smem<LAY>& sm, uint32_t v, uint32_t* total) {
+  constexpr int W = Shape<LAY>::kWaves;
   const uint32_t t = tid();
-  const int lane = t & 63, w = t >> 6;
-  const uint32_t incl = wave_incl_scan(v);
-  if (lane == 63) sm.wsum[w] = incl;
+  const uint32_t w = t >> 6;
+  if ((t & 63) == 0) sm.wsum[w] = v;
   __syncthreads();
-  const uint4 ws = *reinterpret_cast<const uint4*>(sm.wsum);
-  *total = ws.x + ws.y + ws.z + ws.w;
-  const uint32_t before = (w > 0 ? ws.x : 0u) + (w > 1 ? ws.y : 0u) + (w > 2 ? ws.z : 0u);
-  return before + incl - v;
+  uint32_t tot = 0, before = 0;
+#pragma unroll
+  for (int q = 0; q < W / 4; ++q) {
+    const uint4 ws = *reinterpret_cast<const uint4*>(&sm.wsum[4 * q]);
+    const uint32_t a[4] = {ws.x, ws.y, ws.z, ws.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      before += ((uint32_t)(4 * q + c) < w) ? a[c] : 0u;
+      tot += a[c];
+    }
+  }
+  *total = uni(tot);
+  return uni(before);
 }
 
 // ---------------------------------------------------------------------------
 // Selection over the candidate buffer
 //
-// The cnt entries are split into 256 contiguous slices of sp entries (sp
-// even, just enough to cover cnt), thread t owning positions [t*sp, t*sp +
-// sp); their keys sit in registers k[0..sp).  Work per selection therefore
-// scales with cnt, not with the buffer's capacity.
+// Each wavefront owns a contiguous range of the buffer, in index order, and
+// its lanes hold that range interleaved: slot j of lane l is position
+// ws + 64 j + l.  The keys of a lane's slots sit in registers k[0..sp).  A
+// wavefront's slot j thus covers 64 consecutive positions, so ranks come from
+// one ballot per slot and every lane of a slot reads and writes neighbouring
+// words (no LDS bank conflicts, coalesced output stores).  Work per selection
+// scales with the entries present, not with the buffer's capacity.
 //
 // A selection narrows a key interval [lo, hi] known to hold the wanted
 // entry.  Each pass histograms the keys inside it by (key - lo) >> s, with s
@@ -296,81 +320,80 @@ struct Sel {
   bool all_in;      // take covers every entry inside [lo, hi]: the set is key >= lo
 };
 
-// A thread's share of the buffer during a selection: slots base .. base +
-// sp - 1 (sp a multiple of 4 and wave-uniform), of which the first nv hold
-// entries.  Loops over a slice test sp once per group of 4 slots: a test per
-// slot would split the unrolled loop into one basic block per slot, and a
-// lone wavefront then waits out each block's dependent chain in turn.
-// Slices in thread order cover the entries in index order.
+// A wavefront's share of the buffer during a selection: positions [ws, ws +
+// wn) in index order, lane l holding slots j at ws + 64 j + l; sp slots are
+// visited (a multiple of 4, wave-uniform), of which this lane's first nv hold
+// entries.  Loops over the slots test sp once per group of 4: a test per slot
+// would split the unrolled loop into one basic block per slot, and a lone
+// wavefront then waits out each block's dependent chain in turn.
 struct Slice {
-  uint32_t base, sp, nv;
+  uint32_t ws, sp, nv;
 };
 
-// The buffer as filled by the general path: cnt entries in slots [0, cnt),
-// cut into 256 equal slices just large enough to cover them.
+template <int LAY>
+__device__ __forceinline__ Slice make_slice(uint32_t ws, uint32_t wn) {
+  constexpr uint32_t S = (uint32_t)Shape<LAY>::kSlots;
+  ws = uni(ws);
+  wn = uni(wn);
+  uint32_t sp = (wn + 63u) / 64u;
+  sp = (sp + 3u) & ~3u;
+  sp = sp < S ? sp : S;
+  const uint32_t lane = tid() & 63u;
+  Slice sl;
+  sl.ws = ws;
+  sl.sp = sp;
+  sl.nv = wn > lane ? (wn - lane + 63u) / 64u : 0u;
+  return sl;
+}
+
+// The buffer as filled by the general path: cnt entries in positions [0,
+// cnt), cut into one contiguous range per wavefront (whole groups of 64).
 template <int LAY>
 __device__ __forceinline__ Slice plain_slice(uint32_t cnt) {
-  constexpr uint32_t S = (uint32_t)Shape<LAY>::kSlots;
+  constexpr uint32_t W = (uint32_t)Shape<LAY>::kWaves;
   cnt = uni(cnt);
-  uint32_t sp = (cnt + kBlock - 1) / kBlock;
-  sp = (sp + 3u) & ~3u;
-  sp = sp < S ? sp : S;
-  Slice sl;
-  sl.sp = sp;
-  sl.base = tid() * sp;
-  const uint32_t v = cnt > sl.base ? cnt - sl.base : 0u;
-  sl.nv = v < sp ? v : sp;
-  return sl;
+  const uint32_t seg = ((cnt + W - 1u) / W + 63u) / 64u * 64u;
+  const uint32_t ws = uni(tid() >> 6) * seg;
+  const uint32_t rest = cnt > ws ? cnt - ws : 0u;
+  return make_slice<LAY>(ws, rest < seg ? rest : seg);
 }
 
-// The buffer as filled wave by wave: this wavefront's cw entries in slots
-// [w * SUB, w * SUB + cw), cut into 64 slices, one per lane.
+// The buffer as filled wave by wave: this wavefront's cw entries in
+// positions [w * SUB, w * SUB + cw).
 template <int LAY>
 __device__ __forceinline__ Slice wave_slice(uint32_t cw) {
-  constexpr uint32_t S = (uint32_t)Shape<LAY>::kSlots;
-  constexpr uint32_t SUB = (uint32_t)Shape<LAY>::kCap / kWaves;
-  cw = uni(cw);
-  uint32_t sp = (cw + 63u) / 64u;
-  sp = (sp + 3u) & ~3u;
-  sp = sp < S ? sp : S;
-  const uint32_t t = tid();
-  const uint32_t lane = t & 63u;
-  Slice sl;
-  sl.sp = sp;
-  sl.base = (t >> 6) * SUB + lane * sp;
-  const uint32_t v = cw > lane * sp ? cw - lane * sp : 0u;
-  sl.nv = v < sp ? v : sp;
-  return sl;
+  constexpr uint32_t SUB = (uint32_t)Shape<LAY>::kCap / Shape<LAY>::kWaves;
+  return make_slice<LAY>(uni(tid() >> 6) * SUB, cw);
 }
 
-// Keys of this thread's slice.  (base is a multiple of 4: 16-byte reads.)
+// Position of this lane's slot j.
+__device__ __forceinline__ uint32_t slot_pos(const Slice& sl, int j) { return sl.ws + 64u * (uint32_t)j + (tid() & 63u); }
+
+// Keys of this lane's slots (every visited slot is read: positions past the
+// entries stay inside the buffer and their keys are never counted).
 template <int LAY>
 __device__ __forceinline__ void load_keys(const Smem<LAY>& sm, uint32_t (&k)[Shape<LAY>::kSlots], const Slice& sl) {
   constexpr int S = Shape<LAY>::kSlots;
+  const uint32_t p0 = slot_pos(sl, 0);
 #pragma unroll
   for (int q = 0; q < S / 4; ++q) {
     if ((uint32_t)(4 * q) < sl.sp) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(&sm.val[sl.base + 4 * q]);
-      k[4 * q + 0] = ord_key(a.x);
-      k[4 * q + 1] = ord_key(a.y);
-      k[4 * q + 2] = ord_key(a.z);
-      k[4 * q + 3] = ord_key(a.w);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) k[4 * q + c] = ord_key(sm.val[p0 + 64u * (uint32_t)(4 * q + c)]);
     }
   }
 }
 
-// The fp32 bits of this thread's slice, as stored.
+// The fp32 bits of this lane's slots, as stored.
 template <int LAY>
 __device__ __forceinline__ void load_bits(const Smem<LAY>& sm, uint32_t (&v)[Shape<LAY>::kSlots], const Slice& sl) {
   constexpr int S = Shape<LAY>::kSlots;
+  const uint32_t p0 = slot_pos(sl, 0);
 #pragma unroll
   for (int q = 0; q < S / 4; ++q) {
     if ((uint32_t)(4 * q) < sl.sp) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(&sm.val[sl.base + 4 * q]);
-      v[4 * q + 0] = a.x;
-      v[4 * q + 1] = a.y;
-      v[4 * q + 2] = a.z;
-      v[4 * q + 3] = a.w;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[4 * q + c] = sm.val[p0 + 64u * (uint32_t)(4 * q + c)];
     }
   }
 }
@@ -378,32 +401,28 @@ __device__ __forceinline__ void load_bits(const Smem<LAY>& sm, uint32_t (&v)[Sha
 template <int LAY>
 __device__ __forceinline__ void load_idx(const Smem<LAY>& sm, uint32_t (&ix)[Shape<LAY>::kSlots], const Slice& sl) {
   constexpr int S = Shape<LAY>::kSlots;
+  const uint32_t p0 = slot_pos(sl, 0);
 #pragma unroll
   for (int q = 0; q < S / 4; ++q) {
     if ((uint32_t)(4 * q) < sl.sp) {
-      if constexpr (Shape<LAY>::kIdx16) {
-        const u32x2 a = *reinterpret_cast<const u32x2*>(&sm.idx[sl.base + 4 * q]);
-        ix[4 * q + 0] = a.x & 0xffffu;
-        ix[4 * q + 1] = a.x >> 16;
-        ix[4 * q + 2] = a.y & 0xffffu;
-        ix[4 * q + 3] = a.y >> 16;
-      } else {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&sm.idx[sl.base + 4 * q]);
-        ix[4 * q + 0] = a.x;
-        ix[4 * q + 1] = a.y;
-        ix[4 * q + 2] = a.z;
-        ix[4 * q + 3] = a.w;
-      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ix[4 * q + c] = (uint32_t)sm.idx[p0 + 64u * (uint32_t)(4 * q + c)];
     }
   }
 }
 
-static_assert(kSmallBins == kBlock, "one second-pass bin per thread");
+// The second-pass histogram is cleared by the first kSmallBins threads.
+template <int LAY>
+__device__ __forceinline__ void clear_small(Smem<LAY>& sm) {
+  static_assert(Shape<LAY>::kBlock >= kSmallBins, "one second-pass bin per thread at most");
+  const uint32_t t = tid();
+  if (Shape<LAY>::kBlock == kSmallBins || t < (uint32_t)kSmallBins) sm.hs[t] = 0u;
+}
 
 template <int LAY>
 __device__ __forceinline__ void clear_hists(Smem<LAY>& sm) {
-  for (int i = tid(); i < kBins; i += kBlock) sm.hist1[i] = 0u;
-  sm.hs[tid()] = 0u;
+  for (int i = tid(); i < kBins; i += Shape<LAY>::kBlock) sm.hist1[i] = 0u;
+  clear_small(sm);
 }
 
 // Maximum over the wavefront by DPP row shifts and row broadcasts; every
@@ -458,18 +477,25 @@ __device__ __forceinline__ void key_range(Smem<LAY>& sm, const uint32_t (&k)[S],
       }
     }
   }
+  constexpr int W = Shape<LAY>::kWaves;
   const uint32_t mn = wave_min(min(mn0, mn1));
   const uint32_t mx = wave_max(max(mx0, mx1));
   const int w = tid() >> 6;
   if ((tid() & 63) == 0) {
     sm.red[w] = mn;
-    sm.red[kWaves + w] = mx;
+    sm.red[W + w] = mx;
   }
   __syncthreads();
-  const u32x4 a = *reinterpret_cast<const u32x4*>(&sm.red[0]);
-  const u32x4 b = *reinterpret_cast<const u32x4*>(&sm.red[kWaves]);
-  lo = uni(min(min(a.x, a.y), min(a.z, a.w)));
-  hi = uni(max(max(b.x, b.y), max(b.z, b.w)));
+  uint32_t l = 0xffffffffu, h = 0u;
+#pragma unroll
+  for (int q = 0; q < W / 4; ++q) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(&sm.red[4 * q]);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(&sm.red[W + 4 * q]);
+    l = min(l, min(min(a.x, a.y), min(a.z, a.w)));
+    h = max(h, max(max(b.x, b.y), max(b.z, b.w)));
+  }
+  lo = uni(l);
+  hi = uni(h);
 }
 
 // Narrows [lo, hi] (which holds every entry) to the bin holding the keep-th
@@ -496,9 +522,9 @@ __device__ Sel range_select(Smem<LAY>& sm, const uint32_t (&k)[S], const Slice& 
     if (pass >= 2) {  // this histogram was used two passes ago
       __syncthreads();
       if (big) {
-        for (int i = tid(); i < kBins; i += kBlock) h[i] = 0u;
+        for (int i = tid(); i < kBins; i += Shape<LAY>::kBlock) h[i] = 0u;
       } else {
-        h[tid()] = 0u;
+        clear_small(sm);
       }
       __syncthreads();
     }
@@ -549,30 +575,29 @@ enum EmitMode { kToBuffer = 0, kToOut = 1 };
 // / eq_base count the entries above / inside [lo, hi] of earlier chunks of
 // the row; an entry's rank = earlier entries above + min(earlier entries
 // inside, take).  Ranks >= limit are dropped (only reachable with an
-// inconsistent workspace).  To the buffer (as fp32 bits) for kToBuffer.
-// Otherwise ibase + idx goes to out[rank]: the chosen ranks of this buffer
-// are one contiguous range (the buffer is one contiguous stretch of the
-// row), so they are staged in hist1 and copied out with coalesced stores.
-// Every thread has read its buffer slice, and every wave has finished
-// reading the histograms, before any thread writes (the scan's barrier).
+// inconsistent workspace).
 //
-// vout (kToOut only, may be null): the chosen scores' exact bits go to
-// vout[rank] beside the indices.  They are read from the buffer's fp32 bits
-// (which nothing overwrites in this mode) and staged over the index array,
-// which nobody reads after the scan's barrier.
+// Ranks come from ballots: a wavefront's slot j covers 64 consecutive
+// buffer positions, so the rank of an entry is its wavefront's base (the
+// counts of the lower wavefronts, one exchange), plus the counts of the
+// wavefront's earlier slots, plus the lanes below it in its slot.  The
+// chosen entries of one slot get consecutive ranks, so their stores are
+// coalesced.  To the buffer (fp32 bits and index at position rank) for
+// kToBuffer; otherwise ibase + index goes straight to out[rank], and with
+// vout the entry's exact fp32 bits to vout[rank].  Every wavefront has read
+// its slots and finished with the histograms before any entry moves (the
+// exchange's barrier); the histograms are cleared after it.
 template <int LAY, int MODE>
 __device__ __forceinline__ void emit_chosen(Smem<LAY>& sm, const uint32_t (&k)[Shape<LAY>::kSlots], const Slice& sl,
                                             const Sel& s, uint32_t gt_base, uint32_t eq_base, int32_t* out,
                                             uint32_t limit, uint32_t ibase, float* vout = nullptr) {
-  static_assert(!Shape<LAY>::kValues || sizeof(sm.idx) >= 4 * Shape<LAY>::kMaxK, "values staged over the index array");
-  uint32_t* vstage = reinterpret_cast<uint32_t*>(&sm.idx[0]);
   constexpr int S = Shape<LAY>::kSlots;
-  static_assert(S <= 32, "slice flags fit one word");
+  static_assert(S <= 32, "slot flags fit one word");
   const uint32_t sp = sl.sp, nv = sl.nv;
   const uint32_t width = s.hi - s.lo;
   const uint32_t take = s.take;
-  // Whole interval taken and no earlier chunks: the chosen set is simply
-  // every key >= lo.  Otherwise flags for above / inside the interval.
+  // Whole interval taken: the chosen set is every key >= lo (eqm stays 0).
+  // Otherwise flags for above / inside the interval.
   const bool whole = s.all_in && gt_base == 0u && eq_base == 0u;
   uint32_t gtm = 0, eqm = 0;
   if (whole) {
@@ -601,98 +626,49 @@ __device__ __forceinline__ void emit_chosen(Smem<LAY>& sm, const uint32_t (&k)[S
     }
   }
   // Indices (and, for a compaction, the fp32 bits) are read before the
-  // scan's barrier: a compaction then moves entries down into other threads'
-  // slices.  The bits are kept rather than rebuilt from the keys, which fold
-  // -0.0 into +0.0.
+  // exchange's barrier: a compaction then moves entries down into other
+  // wavefronts' ranges.  The bits are kept rather than rebuilt from the
+  // keys, which fold -0.0 into +0.0.
   uint32_t ix[S];
   load_idx<LAY>(sm, ix, sl);
   uint32_t rv[MODE == kToBuffer ? S : 1];
   if constexpr (MODE == kToBuffer) load_bits<LAY>(sm, rv, sl);
   uint32_t total;
-  const uint32_t excl = block_excl_scan(sm, (uint32_t)__popc(gtm) | ((uint32_t)__popc(eqm) << 16), &total);
-  uint32_t first, m;
-  if (whole) {
-    // Rank of slice position j = this thread's first rank + picks before j.
-    uint32_t pos = excl;
+  const uint32_t before =
+      wave_exclusive(sm, wave_sum((uint32_t)__popc(gtm) | ((uint32_t)__popc(eqm) << 16)), &total);
+  (void)total;
+  if constexpr (MODE != kToBuffer) clear_hists(sm);  // every wavefront is past its searches
+  uint32_t g = gt_base + (before & 0xffffu);
+  uint32_t e = eq_base + (before >> 16);
+  const uint32_t p0 = slot_pos(sl, 0);
 #pragma unroll
-    for (int q = 0; q < S / 4; ++q) {
-      if ((uint32_t)(4 * q) < sp) {
+  for (int q = 0; q < S / 4; ++q) {
+    if ((uint32_t)(4 * q) < sp) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int j = 4 * q + c;
-          if (((gtm >> j) & 1u) && pos < limit) {
-            if constexpr (MODE != kToBuffer) {
-              sm.hist1[pos] = ibase + ix[j];
-              if (vout != nullptr) vstage[pos] = sm.val[sl.base + j];
-            } else {
-              sm.val[pos] = rv[MODE == kToBuffer ? j : 0];
-              sm.idx[pos] = (typename Shape<LAY>::Idx)ix[j];
-            }
+      for (int c = 0; c < 4; ++c) {
+        const int j = 4 * q + c;
+        const bool gt = (gtm >> j) & 1u;
+        const bool eq = (eqm >> j) & 1u;
+        const uint64_t bg = ballot(gt), be = ballot(eq);
+        const uint32_t gr = g + lanes_below(bg);
+        const uint32_t er = e + lanes_below(be);
+        const bool pick = gt || (eq && er < take);
+        const uint32_t pos = gr + (er < take ? er : take);
+        if (pick && pos < limit) {
+          if constexpr (MODE != kToBuffer) {
+            out[pos] = (int32_t)(ibase + ix[j]);
+            if (vout != nullptr) vout[pos] = __uint_as_float(sm.val[p0 + 64u * (uint32_t)j]);
+          } else {
+            sm.val[pos] = rv[j];
+            sm.idx[pos] = (typename Shape<LAY>::Idx)ix[j];
           }
-          pos += (gtm >> j) & 1u;
         }
+        g += popc64(bg);
+        e += popc64(be);
       }
     }
-    first = 0u;
-    m = total < limit ? total : limit;
-  } else {
-    uint32_t g = gt_base + (excl & 0xffffu);
-    uint32_t e = eq_base + (excl >> 16);
-    first = gt_base + (eq_base < take ? eq_base : take);  // rank of the first chosen
-#pragma unroll
-    for (int q = 0; q < S / 4; ++q) {
-      if ((uint32_t)(4 * q) < sp) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int j = 4 * q + c;
-          const bool gt = (gtm >> j) & 1u;
-          const bool eq = (eqm >> j) & 1u;
-          const bool pick = gt || (eq && e < take);
-          const uint32_t pos = g + (e < take ? e : take);
-          if (pick && pos < limit) {
-            if constexpr (MODE != kToBuffer) {
-              sm.hist1[pos - first] = ibase + ix[j];
-              if (vout != nullptr) vstage[pos - first] = sm.val[sl.base + j];
-            } else {
-              sm.val[pos] = rv[MODE == kToBuffer ? j : 0];
-              sm.idx[pos] = (typename Shape<LAY>::Idx)ix[j];
-            }
-          }
-          g += gt ? 1u : 0u;
-          e += eq ? 1u : 0u;
-        }
-      }
-    }
-    const uint32_t eq_end = eq_base + (total >> 16);
-    uint32_t last = gt_base + (total & 0xffffu) + (eq_end < take ? eq_end : take);
-    last = last < limit ? last : limit;
-    m = last > first ? last - first : 0u;
   }
-  if constexpr (MODE != kToBuffer) {
-    // Copy the staged ranks [0, m) to out[first + ...], clearing as we go.
-    __syncthreads();
-    int32_t* dst = out + first;
-    if ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0u && (m & 3u) == 0u) {
-      for (uint32_t i = tid() * 4u; i < (uint32_t)Shape<LAY>::kStage; i += kBlock * 4u) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(&sm.hist1[i]);
-        *reinterpret_cast<u32x4*>(&sm.hist1[i]) = u32x4{0u, 0u, 0u, 0u};
-        if (i < m) *reinterpret_cast<u32x4*>(dst + i) = v;
-      }
-    } else {
-      for (uint32_t i = tid(); i < (uint32_t)Shape<LAY>::kStage; i += kBlock) {
-        const uint32_t v = sm.hist1[i];
-        sm.hist1[i] = 0u;
-        if (i < m) dst[i] = (int32_t)v;
-      }
-    }
-    sm.hs[tid()] = 0u;
-    if (vout != nullptr) {
-      float* vdst = vout + first;
-      for (uint32_t i = tid(); i < m; i += kBlock) vdst[i] = __uint_as_float(vstage[i]);
-    }
-  } else {
-    clear_hists(sm);
-  }
+  if constexpr (MODE == kToBuffer) clear_hists(sm);
 }
 
 // Frees buffer space when a tile would not fit (cnt > keep entries), keeping
@@ -719,7 +695,7 @@ __device__ __noinline__ uint64_t compact(Smem<LAY>& sm, uint32_t cnt, uint32_t k
   load_keys<LAY>(sm, k, sl);
   uint32_t lo, hi;
   key_range<LAY, S>(sm, k, sl, lo, hi);
-  const Sel s = range_select<LAY, S>(sm, k, sl, lo, hi, keep, CAP - kTile);
+  const Sel s = range_select<LAY, S>(sm, k, sl, lo, hi, keep, CAP - (uint32_t)Shape<LAY>::kTile);
   emit_chosen<LAY, kToBuffer>(sm, k, sl, s, 0u, 0u, nullptr, CAP, 0u);
   uint32_t Ln;
   if (s.all_in) {
@@ -793,27 +769,39 @@ __device__ __forceinline__ void load_run(const T* __restrict__ p, float (&x)[kEl
   }
 }
 
-// One full tile starting at `tile` (a wave-uniform pointer): thread t loads
-// elements u * 256 * VEC + t * VEC .. + VEC - 1, so each load instruction of a
-// wave covers one contiguous run of 64 * VEC elements.
+// Tiles are wave-major: wavefront w of the workgroup covers elements
+// [w * kWaveTile, (w + 1) * kWaveTile) of a tile, and lane l of it loads
+// elements u * 64 * VEC + l * VEC .. + VEC - 1 of that range (u < kElems /
+// VEC).  Each load instruction of a wave covers one contiguous run of 64 * VEC
+// elements, and a wavefront's elements all precede the next one's in index
+// order, so wavefronts only need each other's totals to place candidates.
+constexpr uint32_t kWaveTile = 64u * kElems;  // elements one wavefront covers per tile
+
+// One full tile starting at `tile` (a wave-uniform pointer).
 template <int VEC, typename T>
 __device__ __forceinline__ void load_full(const T* __restrict__ tile, float (&x)[kElems]) {
-  const uint32_t t = threadIdx.x;
+  const uint32_t w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
-  for (int u = 0; u < kElems / VEC; ++u) load_run<VEC>(tile + (uint32_t)u * (kBlock * VEC) + t * VEC, x, u * VEC);
+  for (int u = 0; u < kElems / VEC; ++u)
+    load_run<VEC>(tile + w * kWaveTile + (uint32_t)u * (64u * VEC) + l * VEC, x, u * VEC);
 }
 
 // The partial last tile [p0, c1): per-element bounds checks, nothing read at
 // or past c1.
 template <int VEC, typename T>
 __device__ __forceinline__ void load_tail(const T* __restrict__ rowp, uint32_t c1, uint32_t p0, float (&x)[kElems]) {
-  const uint32_t t = threadIdx.x;
+  const uint32_t w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
   for (int u = 0; u < kElems / VEC; ++u) {
-    const uint32_t pos = p0 + (uint32_t)u * (kBlock * VEC) + t * VEC;
+    const uint32_t pos = p0 + w * kWaveTile + (uint32_t)u * (64u * VEC) + l * VEC;
 #pragma unroll
     for (int c = 0; c < VEC; ++c) x[u * VEC + c] = (pos + c < c1) ? widen(rowp[pos + c]) : 0.0f;
   }
+}
+
+// Row position of this thread's first element in the tile at p0.
+__device__ __forceinline__ uint32_t tile_pbase(uint32_t p0, int vec) {
+  return p0 + (threadIdx.x >> 6) * kWaveTile + (threadIdx.x & 63) * (uint32_t)vec;
 }
 
 // Whether element e of this thread's share of a tile is accepted: inside
@@ -823,7 +811,7 @@ __device__ __forceinline__ void load_tail(const T* __restrict__ rowp, uint32_t c
 template <int VEC, bool FULL>
 __device__ __forceinline__ bool accepted(const float (&x)[kElems], int e, uint32_t pbase, uint32_t c1, float bf) {
   const int u = e / VEC, c = e % VEC;
-  const bool in = FULL || pbase + (uint32_t)u * (kBlock * VEC) + c < c1;
+  const bool in = FULL || pbase + (uint32_t)u * (64u * VEC) + c < c1;
   return in && x[e] >= bf;
 }
 
@@ -835,45 +823,47 @@ __device__ __forceinline__ void tile_accept(const float (&x)[kElems], uint32_t p
   for (int e = 0; e < kElems; ++e) bal[e] = ballot(accepted<VEC, FULL>(x, e, pbase, c1, bf));
 }
 
-// Per-wave counts of accepted elements for each load slot go through LDS
-// (double-buffered by par); returns the tile total and this wave's offset
-// for each slot, all wave-uniform.
-template <int LAY, int VEC>
+// Every wavefront's count of accepted elements goes through LDS
+// (double-buffered by par); returns the tile total, and in before the
+// counts of the lower wavefronts, both wave-uniform.
+template <int LAY>
 __device__ __forceinline__ uint32_t tile_exchange(Smem<LAY>& sm, const uint64_t (&bal)[kElems], int& par,
-                                                  uint32_t (&off)[kElems / VEC]) {
-  constexpr int NL = kElems / VEC;
-  const uint32_t lane = threadIdx.x & 63;
+                                                  uint32_t& before) {
+  constexpr int W = Shape<LAY>::kWaves;
   const uint32_t w = uni(threadIdx.x >> 6);
+  uint32_t mine = 0;
 #pragma unroll
-  for (int u = 0; u < NL; ++u) {
-    uint32_t c = 0;
-#pragma unroll
-    for (int cc = 0; cc < VEC; ++cc) c += popc64(bal[u * VEC + cc]);
-    if (lane == 0) sm.tile_cnt[par][u][w] = c;
-  }
+  for (int e = 0; e < kElems; ++e) mine += popc64(bal[e]);
+  if ((threadIdx.x & 63) == 0) sm.tile_cnt[par][0][w] = mine;
   __syncthreads();
-  uint32_t total = 0;
+  uint32_t b = 0, all = 0;
 #pragma unroll
-  for (int u = 0; u < NL; ++u) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(sm.tile_cnt[par][u]);
-    const uint32_t v0 = uni(v.x), v1 = uni(v.y), v2 = uni(v.z), v3 = uni(v.w);
-    off[u] = total + (w > 0 ? v0 : 0u) + (w > 1 ? v1 : 0u) + (w > 2 ? v2 : 0u);
-    total += v0 + v1 + v2 + v3;
+  for (int q = 0; q < W / 4; ++q) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(&sm.tile_cnt[par][0][4 * q]);
+    const uint32_t a[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      b += ((uint32_t)(4 * q + c) < w) ? a[c] : 0u;
+      all += a[c];
+    }
   }
+  before = uni(b);
   par ^= 1;
-  return total;
+  return uni(all);
 }
 
-// Appends the accepted elements of one tile, in index order, at cnt + their
-// rank in the tile: fp32 bits and the index relative to the chunk start.
+// Appends this wavefront's accepted elements of one tile, in index order,
+// at cnt + before + their rank in the wavefront's part: fp32 bits and the
+// index relative to the chunk start.
 template <int LAY, int VEC, bool FULL>
 __device__ __forceinline__ void tile_append(Smem<LAY>& sm, const float (&x)[kElems], const uint64_t (&bal)[kElems],
-                                            const uint32_t (&off)[kElems / VEC], uint32_t cnt, uint32_t pbase,
-                                            uint32_t c1, float bf, uint32_t rel) {
+                                            uint32_t before, uint32_t cnt, uint32_t pbase, uint32_t c1, float bf,
+                                            uint32_t rel) {
   constexpr int NL = kElems / VEC;
+  uint32_t r0 = cnt + before;
 #pragma unroll
   for (int u = 0; u < NL; ++u) {
-    uint32_t r = cnt + off[u];
+    uint32_t r = r0;
 #pragma unroll
     for (int c = 0; c < VEC; ++c) r = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[u * VEC + c] >> 32),
                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)bal[u * VEC + c], r));
@@ -883,10 +873,12 @@ __device__ __forceinline__ void tile_append(Smem<LAY>& sm, const float (&x)[kEle
       const bool take = accepted<VEC, FULL>(x, e, pbase, c1, bf);
       if (take) {
         sm.val[r] = __float_as_uint(x[e]);
-        sm.idx[r] = (typename Shape<LAY>::Idx)(rel + (uint32_t)u * (kBlock * VEC) + c);
+        sm.idx[r] = (typename Shape<LAY>::Idx)(rel + (uint32_t)u * (64u * VEC) + c);
       }
       r += take ? 1u : 0u;
     }
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) r0 += popc64(bal[u * VEC + c]);
   }
 }
 
@@ -905,27 +897,27 @@ struct Stream {
 template <int LAY, int VEC, bool FULL>
 __device__ __forceinline__ void process_tile(Smem<LAY>& sm, const float (&x)[kElems], uint32_t p0, uint32_t c1,
                                              uint32_t ibase, uint32_t keep, Stream& st) {
-  constexpr int NL = kElems / VEC;
-  const uint32_t pbase = p0 + threadIdx.x * VEC;
+  const uint32_t pbase = tile_pbase(p0, VEC);
   uint64_t bal[kElems];
-  uint32_t off[NL];
+  uint32_t before = 0;
   tile_accept<VEC, FULL>(x, pbase, c1, st.bf, bal);
-  uint32_t total = tile_exchange<LAY, VEC>(sm, bal, st.par, off);
+  uint32_t total = tile_exchange<LAY>(sm, bal, st.par, before);
   if (st.cnt + total > (uint32_t)Shape<LAY>::kCap) {
     const uint64_t r = compact<LAY>(sm, st.cnt, keep, st.L);
     st.L = uni((uint32_t)r);
     st.cnt = uni((uint32_t)(r >> 32));
     st.bf = accept_floor(st.L);
     tile_accept<VEC, FULL>(x, pbase, c1, st.bf, bal);
-    total = tile_exchange<LAY, VEC>(sm, bal, st.par, off);
+    total = tile_exchange<LAY>(sm, bal, st.par, before);
   }
-  if (total != 0) tile_append<LAY, VEC, FULL>(sm, x, bal, off, st.cnt, pbase, c1, st.bf, pbase - ibase);
+  if (total != 0) tile_append<LAY, VEC, FULL>(sm, x, bal, before, st.cnt, pbase, c1, st.bf, pbase - ibase);
   st.cnt += total;
 }
 
 // The speculative bound for a row of n elements whose first two tiles are
 // in x0 and x1 (n >= kSpecMinLen): the key of (about) the r-th best of those
-// 4096 elements, r = max(kSpecMinRank, ceil(kSpecNum / kSpecDen * K * 4096 / n)),
+// M = 2 * kTile elements (4096, 8192 or 16384 by workgroup width),
+// r = max(kSpecMinRank, ceil(kSpecNum / kSpecDen * K * M / n)),
 // or 0 (no bound) when r >= K.  The bin holding the r-th best is taken whole
 // when it is small, which only lowers the bound.  The caller checks at the
 // end of the row that at least K elements reached the bound and streams the
@@ -935,7 +927,7 @@ __device__ __forceinline__ void process_tile(Smem<LAY>& sm, const float (&x)[kEl
 template <int LAY>
 __device__ __forceinline__ uint32_t spec_bound(Smem<LAY>& sm, float (&x0)[kElems], float (&x1)[kElems], uint32_t n,
                                                uint32_t K) {
-  constexpr uint32_t M = 2u * kTile;
+  constexpr uint32_t M = 2u * (uint32_t)Shape<LAY>::kTile;
   const uint64_t want = ((uint64_t)kSpecNum * K * M + (uint64_t)kSpecDen * n - 1) / ((uint64_t)kSpecDen * n);
   const uint32_t r = want > kSpecMinRank ? (uint32_t)want : kSpecMinRank;
   if (r >= K) return 0u;
@@ -949,8 +941,8 @@ __device__ __forceinline__ uint32_t spec_bound(Smem<LAY>& sm, float (&x0)[kElems
     k[e] = raw_key(__float_as_uint(x0[e]));
     k[kElems + e] = raw_key(__float_as_uint(x1[e]));
   }
-  Slice sl;
-  sl.base = 0u;
+  Slice sl;  // the keys live only in registers: every lane holds 16 valid slots
+  sl.ws = 0u;
   sl.sp = 2u * kElems;
   sl.nv = 2u * kElems;
   uint32_t lo, hi;
@@ -984,6 +976,8 @@ __device__ __forceinline__ void stream_chunk(Smem<LAY>& sm, const T* __restrict_
                                              uint32_t spec, float (&x0)[kElems], float (&x1)[kElems],
                                              bool preloaded) {
   constexpr int PF = kPrefetch;
+  constexpr int NT = Shape<LAY>::kBlock;
+  constexpr uint32_t kTile = (uint32_t)Shape<LAY>::kTile;
   c0 = uni(c0);
   c1 = uni(c1);
   Stream st;
@@ -1052,31 +1046,34 @@ __device__ __forceinline__ void stream_chunk(Smem<LAY>& sm, const T* __restrict_
 // Wave-by-wave streaming of a row with a speculative bound
 //
 // Rows long enough to speculate (see spec_bound) usually end with a few
-// thousand candidates.  Each wavefront then streams its own contiguous
-// quarter of the row into its own quarter of the buffer, with positions from
-// its own ballots: no per-tile exchange between wavefronts and no per-tile
-// barrier.  The quarters are contiguous in index order, so the buffer read
-// segment by segment is in index order too.  If a wavefront's quarter of the
+// thousand candidates.  Each of the W wavefronts then streams its own
+// contiguous segment (a quarter of the row for W = 4) into its own part of
+// the buffer, with positions from its own ballots: no per-tile exchange
+// between wavefronts and no per-tile barrier.  The segments are contiguous in
+// index order, so the buffer read part by part is in index order too.  If a wavefront's quarter of the
 // buffer would overflow (or the bound turns out too high) the row is
 // streamed again on the general path.
 // ---------------------------------------------------------------------------
 
-constexpr uint32_t kWaveTile = 64u * kElems;  // elements one wavefront loads per step
 
-// Elements per wavefront quarter of a row of n: whole wave tiles.
-__device__ __forceinline__ uint32_t quarter_of(uint32_t n) {
-  const uint32_t q = (n + kWaves - 1) / kWaves;
+// Elements per wavefront segment of a row of n, W wavefronts: whole wave tiles.
+template <int W>
+__device__ __forceinline__ uint32_t segment_of(uint32_t n) {
+  const uint32_t q = (n + W - 1) / W;
   return (q + kWaveTile - 1) / kWaveTile * kWaveTile;
 }
 
 // Whether a row of n elements (n > K) goes wave by wave: long enough to
-// speculate, every quarter holding the two full wave tiles of the sample
-// (true for every n >= 8704; below that only for n = 8192), and a
-// speculative rank below K.
+// speculate, every segment holding the two full wave tiles of the sample
+// (with four wavefronts: every n >= 8704, and 8192), and a speculative rank
+// below K.
+template <int LAY>
 __device__ __forceinline__ bool wave_mode(uint32_t n, uint32_t K) {
+  constexpr uint32_t W = (uint32_t)Shape<LAY>::kWaves;
+  constexpr uint64_t M = 2u * (uint64_t)Shape<LAY>::kTile;
   if (n < kSpecMinLen) return false;
-  if (n < 3u * quarter_of(n) + 2u * kWaveTile) return false;  // short last quarter
-  const uint64_t want = ((uint64_t)kSpecNum * K * (2u * kTile) + (uint64_t)kSpecDen * n - 1) / ((uint64_t)kSpecDen * n);
+  if (n < (W - 1u) * segment_of<W>(n) + 2u * kWaveTile) return false;  // short last segment
+  const uint64_t want = ((uint64_t)kSpecNum * K * M + (uint64_t)kSpecDen * n - 1) / ((uint64_t)kSpecDen * n);
   const uint32_t r = want > kSpecMinRank ? (uint32_t)want : kSpecMinRank;
   return r < K;
 }
@@ -1109,7 +1106,7 @@ __device__ __forceinline__ void load_wave_tail(const T* __restrict__ rowp, uint3
 template <int LAY, int VEC, bool FULL>
 __device__ __forceinline__ void wave_tile(Smem<LAY>& sm, const float (&x)[kElems], uint32_t p0, uint32_t end, float bf,
                                           uint32_t sub0, uint32_t& cnt, bool& ovf) {
-  constexpr uint32_t SUB = (uint32_t)Shape<LAY>::kCap / kWaves;
+  constexpr uint32_t SUB = (uint32_t)Shape<LAY>::kCap / Shape<LAY>::kWaves;
   constexpr int NL = kElems / VEC;
   const uint32_t pbase = p0 + (threadIdx.x & 63) * VEC;
   uint64_t bal[kElems];
@@ -1149,10 +1146,42 @@ __device__ __forceinline__ void wave_tile(Smem<LAY>& sm, const float (&x)[kElems
   cnt += total;
 }
 
+// After a wave-by-wave stream: every wavefront's candidate count and overflow
+// flag are shared; returns whether any wavefront overflowed, with the sum of
+// the counts in all and the counts of lower wavefronts in before (all
+// wave-uniform).  Two barriers: sm.red is free again on return.
+template <int LAY>
+__device__ __forceinline__ bool wave_counts(Smem<LAY>& sm, uint32_t w, uint32_t cnt, bool ovf, uint32_t& all,
+                                            uint32_t& before) {
+  constexpr int W = Shape<LAY>::kWaves;
+  if ((threadIdx.x & 63) == 0) {
+    sm.red[w] = cnt;
+    sm.red[W + w] = ovf ? 1u : 0u;
+  }
+  __syncthreads();
+  uint32_t a = 0, b = 0, o = 0;
+#pragma unroll
+  for (int q = 0; q < W / 4; ++q) {
+    const u32x4 c = *reinterpret_cast<const u32x4*>(&sm.red[4 * q]);
+    const u32x4 f = *reinterpret_cast<const u32x4*>(&sm.red[W + 4 * q]);
+    const uint32_t v[4] = {uni(c.x), uni(c.y), uni(c.z), uni(c.w)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a += v[i];
+      b += ((uint32_t)(4 * q + i) < w) ? v[i] : 0u;
+    }
+    o |= uni(f.x | f.y | f.z | f.w);
+  }
+  all = a;
+  before = b;
+  __syncthreads();  // every wave has read the counts before sm.red is reused
+  return o != 0u;
+}
+
 // Streams row [0, n) wave by wave (wave_mode(n, K) holds; indices fit the
 // buffer's index type).  x0 / x1 carry each wavefront's first two wave tiles
-// (already loaded when preloaded); together they sample 4096 elements from
-// the four quarters for the speculative bound.  Returns false if the row must
+// (already loaded when preloaded); together they sample 2 * kTile elements
+// from the W segments for the speculative bound.  Returns false if the row must
 // be streamed again on the general path; otherwise mine is this
 // wavefront's number of candidates (in slots [w * SUB, w * SUB + mine)).
 template <int LAY, int VEC, typename T>
@@ -1161,11 +1190,12 @@ __device__ __forceinline__ bool stream_row_waves(Smem<LAY>& sm, const T* __restr
                                                  bool preloaded, uint32_t& mine) {
   constexpr int PF = kPrefetch;
   constexpr uint32_t WT = kWaveTile;
-  constexpr uint32_t SUB = (uint32_t)Shape<LAY>::kCap / kWaves;
+  constexpr int W = Shape<LAY>::kWaves;
+  constexpr uint32_t SUB = (uint32_t)Shape<LAY>::kCap / W;
   n = uni(n);
   K = uni(K);
   const uint32_t w = uni(threadIdx.x >> 6);
-  const uint32_t Q = quarter_of(n);
+  const uint32_t Q = segment_of<W>(n);
   const uint32_t qs = w * Q;
   const uint32_t qe = qs + Q < n ? qs + Q : n;
   const T* qp = rowp + qs;
@@ -1174,7 +1204,7 @@ __device__ __forceinline__ bool stream_row_waves(Smem<LAY>& sm, const T* __restr
     load_wave_full<VEC>(qp + WT, x1);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // wave_mode(n, K): every quarter holds at least two full wave tiles, F >= 2.
+  // wave_mode(n, K): every segment holds at least two full wave tiles, F >= 2.
   const uint32_t F = (qe - qs) / WT;
   float buf[PF][kElems];
 #pragma unroll
@@ -1211,18 +1241,10 @@ __device__ __forceinline__ bool stream_row_waves(Smem<LAY>& sm, const T* __restr
     load_wave_tail<VEC>(rowp, qe, pt, x);
     wave_tile<LAY, VEC, false>(sm, x, pt, qe, bf, sub0, cnt, ovf);
   }
-  if ((threadIdx.x & 63) == 0) {
-    sm.red[w] = cnt;
-    sm.red[kWaves + w] = ovf ? 1u : 0u;
-  }
-  __syncthreads();
-  const u32x4 c = *reinterpret_cast<const u32x4*>(&sm.red[0]);
-  const u32x4 o = *reinterpret_cast<const u32x4*>(&sm.red[kWaves]);
-  const uint32_t c0 = uni(c.x), c1 = uni(c.y), c2 = uni(c.z), c3 = uni(c.w);
-  const bool bad = uni(o.x | o.y | o.z | o.w) != 0u;
+  uint32_t all = 0, before = 0;
+  const bool bad = wave_counts<LAY>(sm, w, cnt, ovf, all, before);
   mine = cnt;
-  __syncthreads();  // every wave has read the counts before sm.red is reused
-  return !bad && c0 + c1 + c2 + c3 >= K;
+  return !bad && all >= K;
 }
 
 // Workspace traffic between the workgroups of a row goes only through
@@ -1261,8 +1283,9 @@ __device__ __forceinline__ void ws_add(uint32_t* p, uint32_t v) {
 
 // Whether a split row of n elements is processed chunk by chunk (else its
 // chunk 0 takes it whole and the other chunks have nothing to do).
+template <int LAY>
 __device__ __forceinline__ bool splits(uint32_t n, uint32_t K, uint32_t chunk) {
-  return n > chunk && wave_mode(n, K);
+  return n > chunk && wave_mode<LAY>(n, K);
 }
 
 // Streams [c0, c1) of a row of n elements wave by wave, each wavefront its
@@ -1278,20 +1301,21 @@ __device__ __forceinline__ bool stream_piece_waves(Smem<LAY>& sm, const T* __res
                                                    uint32_t& off, uint32_t& total, uint32_t& L) {
   constexpr int PF = kPrefetch;
   constexpr uint32_t WT = kWaveTile;
-  constexpr uint32_t SUB = (uint32_t)Shape<LAY>::kCap / kWaves;
+  constexpr int W = Shape<LAY>::kWaves;
+  constexpr uint32_t SUB = (uint32_t)Shape<LAY>::kCap / W;
   n = uni(n);
   K = uni(K);
   c0 = uni(c0);
   c1 = uni(c1);
   const uint32_t w = uni(threadIdx.x >> 6);
   if (!preloaded) {
-    const T* sp = rowp + w * quarter_of(n);
+    const T* sp = rowp + w * segment_of<W>(n);
     load_wave_full<VEC>(sp, x0);
     load_wave_full<VEC>(sp + WT, x1);
     __builtin_amdgcn_sched_barrier(0);
   }
-  const uint32_t q = quarter_of(c1 - c0);
-  const uint32_t qs = c0 + w * q;  // at or past c1 when the range has fewer quarters
+  const uint32_t q = segment_of<W>(c1 - c0);
+  const uint32_t qs = c0 + w * q;  // at or past c1 when the range has fewer segments
   const uint32_t qe = qs + q < c1 ? qs + q : c1;
   const uint32_t F = qe > qs ? (qe - qs) / WT : 0u;
   const T* qp = rowp + qs;
@@ -1330,19 +1354,8 @@ __device__ __forceinline__ bool stream_piece_waves(Smem<LAY>& sm, const T* __res
     load_wave_tail<VEC>(rowp, qe, pt, x);
     wave_tile<LAY, VEC, false>(sm, x, pt, qe, bf, sub0, cnt, ovf);
   }
-  if ((threadIdx.x & 63) == 0) {
-    sm.red[w] = cnt;
-    sm.red[kWaves + w] = ovf ? 1u : 0u;
-  }
-  __syncthreads();
-  const u32x4 c = *reinterpret_cast<const u32x4*>(&sm.red[0]);
-  const u32x4 o = *reinterpret_cast<const u32x4*>(&sm.red[kWaves]);
-  const uint32_t v0 = uni(c.x), v1 = uni(c.y), v2 = uni(c.z), v3 = uni(c.w);
-  const bool bad = uni(o.x | o.y | o.z | o.w) != 0u;
+  const bool bad = wave_counts<LAY>(sm, w, cnt, ovf, total, off);
   mine = cnt;
-  off = (w > 0 ? v0 : 0u) + (w > 1 ? v1 : 0u) + (w > 2 ? v2 : 0u);
-  total = v0 + v1 + v2 + v3;
-  __syncthreads();  // every wave has read the counts before sm.red is reused
   return !bad;
 }
 
@@ -1362,7 +1375,8 @@ template <int LAY>
 __device__ __forceinline__ uint32_t publish_piece(Smem<LAY>& sm, uint32_t* blk, int c, bool waved, uint32_t mine,
                                                   uint32_t off, uint32_t total, uint32_t ibase) {
   constexpr uint32_t CAP = (uint32_t)Shape<LAY>::kCap;
-  constexpr uint32_t SUB = CAP / kWaves;
+  constexpr uint32_t NT = (uint32_t)Shape<LAY>::kBlock;
+  constexpr uint32_t SUB = CAP / Shape<LAY>::kWaves;
   uint32_t* bits = blk + kSplitHead / 4 + (uint32_t)c * 2u * CAP;
   uint32_t* idxs = bits + CAP;
   const uint32_t t = tid();
@@ -1373,7 +1387,7 @@ __device__ __forceinline__ uint32_t publish_piece(Smem<LAY>& sm, uint32_t* blk, 
       ws_store(idxs + off + i, (uint32_t)sm.idx[s0 + i]);
     }
   } else {
-    for (uint32_t i = t; i < total; i += kBlock) {
+    for (uint32_t i = t; i < total; i += NT) {
       ws_store(bits + i, sm.val[i]);
       ws_store(idxs + i, (uint32_t)sm.idx[i] + ibase);
     }
@@ -1397,6 +1411,7 @@ template <int LAY>
 __device__ __forceinline__ uint32_t merge_pieces(Smem<LAY>& sm, uint32_t* blk, uint32_t geff, uint32_t K) {
   constexpr int S = Shape<LAY>::kSlots;
   constexpr uint32_t CAP = (uint32_t)Shape<LAY>::kCap;
+  constexpr uint32_t NT = (uint32_t)Shape<LAY>::kBlock;
   const uint32_t t = tid();
   if (t < 64u) {
     const uint32_t v = t < geff ? ws_load(blk + 16 + t) : 0u;
@@ -1421,7 +1436,7 @@ __device__ __forceinline__ uint32_t merge_pieces(Smem<LAY>& sm, uint32_t* blk, u
     uint32_t vb[S], vi[S];
 #pragma unroll
     for (int j = 0; j < S; ++j) {
-      const uint32_t i = t + (uint32_t)j * kBlock;
+      const uint32_t i = t + (uint32_t)j * NT;
       uint32_t ch = 0;
 #pragma unroll
       for (int g = 1; g < kMaxSplit; ++g) ch += i >= P[g] ? 1u : 0u;
@@ -1431,7 +1446,7 @@ __device__ __forceinline__ uint32_t merge_pieces(Smem<LAY>& sm, uint32_t* blk, u
     }
 #pragma unroll
     for (int j = 0; j < S; ++j) {
-      const uint32_t i = t + (uint32_t)j * kBlock;
+      const uint32_t i = t + (uint32_t)j * NT;
       if (i < total) {
         sm.val[i] = vb[j];
         sm.idx[i] = (typename Shape<LAY>::Idx)vi[j];
@@ -1442,7 +1457,7 @@ __device__ __forceinline__ uint32_t merge_pieces(Smem<LAY>& sm, uint32_t* blk, u
   for (uint32_t g = 0; g < geff; ++g) {
     const uint32_t m = uni(sm.part()[g + 1]) - uni(sm.part()[g]);
     uint32_t* bits = lists + g * 2u * CAP;
-    for (uint32_t i = t; i < m; i += kBlock) {
+    for (uint32_t i = t; i < m; i += NT) {
       ws_store(bits + i, 0u);
       ws_store(bits + CAP + i, 0u);
     }
@@ -1465,10 +1480,10 @@ __device__ __forceinline__ int64_t clamp_len(const KernelParams& p, int row) {
 
 // n <= K: every valid index (plus the row's offset), then -1.  Reads no scores.
 // With vout, the n scores themselves (read from rowp, as fp32) and -inf after them.
-template <typename T = float>
+template <int NT, typename T = float>
 __device__ __forceinline__ void write_all_then_pad(int32_t* out, int64_t n, int K, uint32_t off,
                                                    float* vout = nullptr, const T* rowp = nullptr) {
-  for (int i = threadIdx.x; i < K; i += kBlock) {
+  for (int i = threadIdx.x; i < K; i += NT) {
     out[i] = i < n ? (int32_t)(off + (uint32_t)i) : -1;
     if (vout != nullptr) vout[i] = i < n ? widen(rowp[i]) : -__builtin_huge_valf();
   }
@@ -1520,7 +1535,9 @@ __device__ __forceinline__ void unit_of(const KernelParams& p, uint32_t u, int& 
 // the same reason).
 // T: the score type (float, or uint16_t holding bf16).
 template <int VEC, int LAY, bool SPLIT, bool VALS, typename T>
-__global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_single_kernel(KernelParams p) {
+__global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd) topk_single_kernel(KernelParams p) {
+  constexpr int NT = Shape<LAY>::kBlock;
+  constexpr int W = Shape<LAY>::kWaves;
   __shared__ Smem<LAY> sm;
   zero_histograms(sm);
   __syncthreads();
@@ -1568,20 +1585,20 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_single_ker
     uint32_t cnt = 0;
     bool waved = false;  // the candidates sit wave by wave
     bool select = false;
-    const bool piece = SPLIT && c >= 0 && splits((uint32_t)n, K, CH);
+    const bool piece = SPLIT && c >= 0 && splits<LAY>((uint32_t)n, K, CH);
     if (SPLIT && c > 0 && !piece) {
       // Chunk of a row taken whole by its chunk 0: nothing to do.
     } else if (n <= (int64_t)K) {
       if constexpr (VALS)
-        write_all_then_pad<T>(out, n, p.K, off, p.out_val + (int64_t)row * p.K, row_of<T>(p, row));
+        write_all_then_pad<NT, T>(out, n, p.K, off, p.out_val + (int64_t)row * p.K, row_of<T>(p, row));
       else
-        write_all_then_pad(out, n, p.K, off);
+        write_all_then_pad<NT>(out, n, p.K, off);
     } else {
       const T* rowp = row_of<T>(p, row);
       uint32_t g0 = 0, g1 = (uint32_t)n, gL = 0;  // general path: range, starting bound
       bool general = true;
       uint32_t mine = 0, off = 0;
-      if (SPLIT && (piece || (!redo && wave_mode((uint32_t)n, K)))) {
+      if (SPLIT && (piece || (!redo && wave_mode<LAY>((uint32_t)n, K)))) {
         // One wave-by-wave streamer for chunks and whole rows alike (a second
         // inlined copy would cost the loop registers).
         if (piece) {
@@ -1604,7 +1621,7 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_single_ker
           }
           cnt = mine;
         }
-      } else if (!redo && wave_mode((uint32_t)n, K)) {
+      } else if (!redo && wave_mode<LAY>((uint32_t)n, K)) {
         waved = stream_row_waves<LAY, VEC>(sm, rowp, (uint32_t)n, K, x0, x1, have_pre, cnt);
         have_pre = false;
         if (!waved) {
@@ -1682,19 +1699,19 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_single_ker
       nc = (int)uni(sm.acc[12]) - 1;
     }
     // Prefetch for the next unit unless it is a chunk with nothing to do.
-    const bool npiece = SPLIT && nc >= 0 && splits((uint32_t)nn, K, CH);
+    const bool npiece = SPLIT && nc >= 0 && splits<LAY>((uint32_t)nn, K, CH);
     if (nunit < U && nn >= (int64_t)kSpecMinLen && nn > (int64_t)K && (nc <= 0 || npiece)) {
       // The next unit's first two tiles: per wavefront quarter (the row's
       // sample) when it will go wave by wave or is a chunk, else the row's
       // first two tiles.
       const T* nrowp = row_of<T>(p, nrow);
-      if (wave_mode((uint32_t)nn, K)) {
-        const T* qp = nrowp + uni(threadIdx.x >> 6) * quarter_of((uint32_t)nn);
+      if (wave_mode<LAY>((uint32_t)nn, K)) {
+        const T* qp = nrowp + uni(threadIdx.x >> 6) * segment_of<W>((uint32_t)nn);
         load_wave_full<VEC>(qp, x0);
         load_wave_full<VEC>(qp + kWaveTile, x1);
       } else {
         load_full<VEC>(nrowp, x0);
-        load_full<VEC>(nrowp + kTile, x1);
+        load_full<VEC>(nrowp + Shape<LAY>::kTile, x1);
       }
       have_pre = true;
     }
@@ -1740,7 +1757,8 @@ __device__ void group_barrier(uint32_t* ctr, uint32_t target, uint32_t spin_limi
 
 // Adds a complete LDS histogram into a workspace histogram (non-zero bins
 // only) and its sums over groups of 32 bins into the workspace's group sums
-// gc.  The LDS copy is left as it is.
+// gc.  The LDS copy is left as it is.  NT threads.
+template <int NT>
 __device__ __forceinline__ void merge_hist(const uint32_t* lds_hist, uint32_t* gh, uint32_t* gc) {
   const int t = threadIdx.x;
   if (t < kBins / 32) {
@@ -1753,7 +1771,7 @@ __device__ __forceinline__ void merge_hist(const uint32_t* lds_hist, uint32_t* g
     }
     if (s) ws_add(gc + t, s);
   }
-  for (int i = t; i < kBins; i += kBlock) {
+  for (int i = t; i < kBins; i += NT) {
     const uint32_t v = lds_hist[i];
     if (v) ws_add(gh + i, v);
   }
@@ -1818,12 +1836,13 @@ __device__ __forceinline__ int list_of(const uint32_t* off, int n, uint32_t i) {
 }
 
 template <int VEC, int LAY, typename E>
-__global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kernel(KernelParams p) {
+__global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd) topk_multi_kernel(KernelParams p) {
   __shared__ Smem<LAY> sm;
   __shared__ uint32_t s_off[kMaxGroup + 1];
   __shared__ uint32_t s_above[kMaxGroup];
   constexpr int S = Shape<LAY>::kSlots;
   constexpr int CAP = Shape<LAY>::kCap;
+  constexpr int NT = Shape<LAY>::kBlock;
   const int t = threadIdx.x;
   const int G = p.wg_per_row;
   // Workgroups are dispatched round-robin over the 8 XCDs.  Renumber them so
@@ -1839,7 +1858,7 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kern
   int32_t* out = p.out + (int64_t)row * p.K;
   if (n <= (int64_t)K) {
     if (g == 0)
-      write_all_then_pad<E>(out, n, p.K, offset_of(p, row),
+      write_all_then_pad<NT, E>(out, n, p.K, offset_of(p, row),
                             p.out_val != nullptr ? p.out_val + (int64_t)row * p.K : nullptr, row_of<E>(p, row));
     return;
   }
@@ -1873,8 +1892,8 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kern
   // cnt >= K kept ones; if fewer than K reached it, the chunk is streamed
   // again without one.
   const uint32_t clen = (uint32_t)(c1 - c0);
-  stream_chunk<LAY, VEC>(sm, rowp, (uint32_t)c0, (uint32_t)c1, K, cnt, L, clen >= 2u * kTile ? clen : 0u, x0, x1,
-                         false);
+  stream_chunk<LAY, VEC>(sm, rowp, (uint32_t)c0, (uint32_t)c1, K, cnt, L,
+                         clen >= 2u * (uint32_t)Shape<LAY>::kTile ? clen : 0u, x0, x1, false);
   if (cnt < K && clen > K) {
     cnt = 0u;
     L = 0u;
@@ -1903,7 +1922,7 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kern
     }
   }
   __syncthreads();
-  merge_hist(sm.hist1, h1, gs1);
+  merge_hist<NT>(sm.hist1, h1, gs1);
   group_barrier(ctr, 1u * grow, p.spin_limit, err);
   const Found f1 = ws_find(h1, gs1, K);
   uint32_t ok = f1.ok;
@@ -1914,7 +1933,7 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kern
   // Round 2: next 11 bits of the entries in the threshold bin; publish how
   // many of this chunk's entries lie above it.
   __syncthreads();  // every wave has read the row's copy
-  for (int i = t; i < kBins; i += kBlock) sm.hist1[i] = 0u;
+  for (int i = t; i < kBins; i += NT) sm.hist1[i] = 0u;
   __syncthreads();
   uint32_t n_above = 0;
 #pragma unroll
@@ -1932,7 +1951,7 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kern
   }
   wave_add(&sm.acc[0], n_above);
   __syncthreads();
-  merge_hist(sm.hist1, h2, gs2);
+  merge_hist<NT>(sm.hist1, h2, gs2);
   if (t == 0) ws_store(&slots[4 * g + 0], sm.acc[0]);
   group_barrier(ctr, 2u * grow, p.spin_limit, err);
   const Found f2 = ws_find(h2, gs2, krem);
@@ -1941,8 +1960,8 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kern
   prefix |= f2.bin << 10;
   pmask = 0xfffffc00u;
 
-  // Round 3: publish the keys still undecided after 22 bits, in index order,
-  // and the count above them.
+  // Round 3: publish the keys still undecided after 22 bits, in index order
+  // (positions from ballots, as in emit_chosen), and the count above them.
   {
     uint32_t mine = 0;
     n_above = 0;
@@ -1954,14 +1973,14 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kern
           const int j = 4 * q + c;
           const bool valid = (uint32_t)j < nv;
           const uint32_t km = k[j] & pmask;
-          mine += (valid && km == prefix) ? 1u : 0u;
+          mine += popc64(ballot(valid && km == prefix));
           n_above += popc64(ballot(valid && km > prefix));
         }
       }
     }
     wave_add(&sm.acc[1], n_above);
     uint32_t len;
-    uint32_t at = block_excl_scan(sm, mine, &len);
+    uint32_t at = wave_exclusive(sm, mine, &len);
     uint32_t* my_list = lists + (uint64_t)g * CAP;
 #pragma unroll
     for (int q = 0; q < S / 4; ++q) {
@@ -1969,8 +1988,10 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kern
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int j = 4 * q + c;
-          const bool valid = (uint32_t)j < nv;
-          if (valid && (k[j] & pmask) == prefix) ws_store(&my_list[at++], k[j]);
+          const bool und = (uint32_t)j < nv && (k[j] & pmask) == prefix;
+          const uint64_t b = ballot(und);
+          if (und) ws_store(&my_list[at + lanes_below(b)], k[j]);
+          at += popc64(b);
         }
       }
     }
@@ -1980,7 +2001,7 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kern
     }
   }
   group_barrier(ctr, 3u * grow, p.spin_limit, err);
-  for (int i = t; i < kBins; i += kBlock) sm.hist1[i] = 0u;  // round 2's local histogram was merged before the barrier
+  for (int i = t; i < kBins; i += NT) sm.hist1[i] = 0u;  // round 2's local histogram was merged before the barrier
 
   // Every chunk's list, flattened: offsets by a prefix sum over the lengths.
   if (t < 64) {
@@ -2000,7 +2021,7 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kern
   __syncthreads();
   const uint32_t total = s_off[grow];
   // Last 10 bits over all lists.
-  for (uint32_t i = t; i < total; i += kBlock) {
+  for (uint32_t i = t; i < total; i += NT) {
     const int gg = list_of(s_off, grow, i);
     const uint32_t v = ws_load(&lists[(uint64_t)gg * CAP + (i - s_off[gg])]);
     atomicAdd(&sm.hist1[v & 1023u], 1u);
@@ -2015,7 +2036,7 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kern
   {
     uint32_t gt_b = 0, eq_b = 0;
     const uint32_t lim = s_off[g];
-    for (uint32_t i0 = 0; i0 < lim; i0 += kBlock) {
+    for (uint32_t i0 = 0; i0 < lim; i0 += NT) {
       const uint32_t i = i0 + t;
       uint32_t v = 0;
       if (i < lim) {
@@ -2045,7 +2066,7 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kern
   }
   __syncthreads();
   if (sm.acc[4]) {
-    for (int i = t; i < kBins; i += kBlock) {
+    for (int i = t; i < kBins; i += NT) {
       ws_store(&h1[i], 0u);
       ws_store(&h2[i], 0u);
     }
@@ -2053,7 +2074,7 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kern
       ws_store(&gs1[t], 0u);
       ws_store(&gs2[t], 0u);
     }
-    for (uint32_t i = t; i < total; i += kBlock) {
+    for (uint32_t i = t; i < total; i += NT) {
       const int gg = list_of(s_off, grow, i);
       ws_store(&lists[(uint64_t)gg * CAP + (i - s_off[gg])], 0u);
     }
@@ -2074,187 +2095,5 @@ __global__ void __launch_bounds__(kBlock, Shape<LAY>::kResident) topk_multi_kern
   s.all_in = false;
   emit_chosen<LAY, kToOut>(sm, k, sl, s, gt_base, eq_base, out, K, (uint32_t)c0 + offset_of(p, row), vout);
 }
-
-// ---------------------------------------------------------------------------
-// Streaming-read reference (measurement only): the largest key of each row's
-// valid prefix, read with the same tiles, load width and prefetch ring as the
-// selection kernels, and no filtering.  Its rate is the ceiling the streaming
-// filter can approach on the same bytes.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t tile_max(const float (&x)[kElems], uint32_t m) {
-#pragma unroll
-  for (int e = 0; e < kElems; ++e) {
-    const uint32_t k = ord_key(__float_as_uint(x[e]));
-    m = k > m ? k : m;
-  }
-  return m;
-}
-
-template <int VEC, typename T>
-__global__ void __launch_bounds__(kBlock) read_ref_kernel(KernelParams p) {
-  __shared__ uint32_t wmax[kWaves];
-  constexpr int PF = kPrefetch;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int row = blockIdx.x; row < p.num_rows; row += gridDim.x) {
-    const uint32_t n = (uint32_t)clamp_len(p, row);
-    const T* rowp = row_of<T>(p, row);
-    const uint32_t F = n / kTile;
-    uint32_t m = 0;
-    if (F > 0) {
-      float buf[PF][kElems];
-#pragma unroll
-      for (int s = 0; s < PF - 1; ++s) {
-        load_full<VEC>(rowp + ((uint32_t)s < F ? (uint32_t)s : F - 1) * kTile, buf[s]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      const uint32_t Fr = F - F % PF;
-      for (uint32_t j0 = 0; j0 < Fr; j0 += PF) {
-#pragma unroll
-        for (int slot = 0; slot < PF; ++slot) {
-          const uint32_t j = j0 + slot;
-          const uint32_t jn = j + PF - 1 < F ? j + PF - 1 : F - 1;
-          load_full<VEC>(rowp + jn * kTile, buf[(slot + PF - 1) % PF]);
-          __builtin_amdgcn_sched_barrier(0);
-          m = tile_max(buf[slot], m);
-        }
-      }
-#pragma unroll
-      for (int slot = 0; slot < PF - 1; ++slot)
-        if (Fr + slot < F) m = tile_max(buf[slot], m);
-    }
-    const uint32_t pt = F * kTile;
-    if (pt < n) {
-      float x[kElems];
-      load_tail<VEC>(rowp, n, pt, x);
-#pragma unroll
-      for (int u = 0; u < kElems / VEC; ++u)
-#pragma unroll
-        for (int c = 0; c < VEC; ++c) {
-          const uint32_t pos = pt + (uint32_t)u * (kBlock * VEC) + threadIdx.x * VEC + c;
-          const uint32_t k = ord_key(__float_as_uint(x[u * VEC + c]));
-          if (pos < n && k > m) m = k;
-        }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const uint32_t o = (uint32_t)__shfl_xor((int)m, off);
-      m = o > m ? o : m;
-    }
-    if (lane == 0) wmax[w] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      uint32_t r = wmax[0];
-#pragma unroll
-      for (int i = 1; i < kWaves; ++i) r = wmax[i] > r ? wmax[i] : r;
-      reinterpret_cast<uint32_t*>(p.out)[row] = r;
-    }
-    __syncthreads();
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Small utility kernels
-// ---------------------------------------------------------------------------
-
-__global__ void zero_kernel(uint32_t* p, uint64_t words) {
-  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += stride) p[i] = 0u;
-}
-
-// Packs rows with a column stride into contiguous rows of num_cols:
-// packed[r * num_cols + c] = scores[r * row_stride + c * col_stride] for
-// c < clamp(lengths[r], 0, num_cols).  Nothing at or past a length is read
-// or written.  Tiles of 64 rows x 64 columns go through LDS: loaded with the
-// lanes along whichever of rows and columns is closer in memory (a
-// transposed view reads consecutive addresses), written with the lanes
-// along the packed rows.
-constexpr int kPackTile = 64;
-
-__global__ void __launch_bounds__(256) pack_kernel(const float* __restrict__ scores, int64_t row_stride,
-                                                   int64_t col_stride, int64_t num_cols,
-                                                   const int32_t* __restrict__ lengths, int32_t num_rows,
-                                                   float* __restrict__ packed) {
-  __shared__ float tile[kPackTile][kPackTile + 1];  // [column][row]
-  __shared__ int32_t len[kPackTile];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t tiles_r = (num_rows + kPackTile - 1) / kPackTile;
-  const int64_t tiles_c = (num_cols + kPackTile - 1) / kPackTile;
-  const bool rows_close = row_stride < col_stride;
-  for (int64_t tt = blockIdx.x; tt < tiles_r * tiles_c; tt += gridDim.x) {
-    const int64_t r0 = (tt % tiles_r) * kPackTile, c0 = (tt / tiles_r) * kPackTile;
-    if (threadIdx.x < kPackTile) {
-      const int64_t r = r0 + threadIdx.x;
-      int64_t n = r < num_rows ? lengths[r] : 0;
-      n = n < 0 ? 0 : (n > num_cols ? num_cols : n);
-      len[threadIdx.x] = (int32_t)(n > c0 ? (n - c0 < kPackTile ? n - c0 : kPackTile) : 0);
-    }
-    __syncthreads();
-    if (rows_close) {
-      for (int cc = w; cc < kPackTile; cc += 4)
-        if (cc < len[lane]) tile[cc][lane] = scores[(r0 + lane) * row_stride + (c0 + cc) * col_stride];
-    } else {
-      for (int rr = w; rr < kPackTile; rr += 4)
-        if (lane < len[rr]) tile[lane][rr] = scores[(r0 + rr) * row_stride + (c0 + lane) * col_stride];
-    }
-    __syncthreads();
-    for (int rr = w; rr < kPackTile; rr += 4)
-      if (lane < len[rr]) packed[(r0 + rr) * num_cols + c0 + lane] = tile[lane][rr];
-    __syncthreads();  // the tile and lengths are reused
-  }
-}
-
-__global__ void keys_kernel(const uint32_t* bits, uint32_t* keys, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) keys[i] = ord_key(bits[i]);
-}
-
-// ---------------------------------------------------------------------------
-// Instance table
-// ---------------------------------------------------------------------------
-
-template <int VEC, int LAY, typename T>
-static const void* pick_vec(int path, bool vals) {
-  if (path == 3) return reinterpret_cast<const void*>(&read_ref_kernel<VEC, T>);
-  if (path == 2) return reinterpret_cast<const void*>(&topk_multi_kernel<VEC, LAY, T>);
-  const bool sp = path == 4;
-  if constexpr (Shape<LAY>::kValues) {
-    if (sp && vals) return reinterpret_cast<const void*>(&topk_single_kernel<VEC, LAY, true, true, T>);
-    if (vals) return reinterpret_cast<const void*>(&topk_single_kernel<VEC, LAY, false, true, T>);
-  } else {
-    if (vals) return nullptr;  // no room to stage the values: the host plans another layout
-  }
-  if (sp) return reinterpret_cast<const void*>(&topk_single_kernel<VEC, LAY, true, false, T>);
-  return reinterpret_cast<const void*>(&topk_single_kernel<VEC, LAY, false, false, T>);
-}
-
-template <int LAY>
-static const void* pick(int path, int vec, bool vals, bool bf16) {
-  if (bf16) return vec == 8 ? pick_vec<8, LAY, uint16_t>(path, vals) : pick_vec<1, LAY, uint16_t>(path, vals);
-  if (vec == 4) return pick_vec<4, LAY, float>(path, vals);
-  if (vec == 2) return pick_vec<2, LAY, float>(path, vals);
-  return pick_vec<1, LAY, float>(path, vals);
-}
-
-const void* kernel_ptr(int path, int vec, bool idx16, bool vals, bool bf16, bool big_k) {
-  switch (layout_of(idx16, big_k)) {
-    case kLayIdx16: return pick<kLayIdx16>(path, vec, vals, bf16);
-    case kLayBigK: return pick<kLayBigK>(path, vec, vals, bf16);
-    case kLayIdx16 | kLayBigK: return pick<kLayIdx16 | kLayBigK>(path, vec, vals, bf16);
-    default: return pick<0>(path, vec, vals, bf16);
-  }
-}
-
-int lds_bytes_of(bool idx16, bool big_k) {
-  switch (layout_of(idx16, big_k)) {
-    case kLayIdx16: return (int)sizeof(Smem<kLayIdx16>);
-    case kLayBigK: return (int)sizeof(Smem<kLayBigK>);
-    case kLayIdx16 | kLayBigK: return (int)sizeof(Smem<kLayIdx16 | kLayBigK>);
-    default: return (int)sizeof(Smem<0>);
-  }
-}
-
-const void* zero_kernel_ptr() { return reinterpret_cast<const void*>(&zero_kernel); }
-const void* keys_kernel_ptr() { return reinterpret_cast<const void*>(&keys_kernel); }
-const void* pack_kernel_ptr() { return reinterpret_cast<const void*>(&pack_kernel); }
 
 }  // namespace rrt
