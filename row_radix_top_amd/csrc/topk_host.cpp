@@ -201,13 +201,34 @@ OccSet occ_for(const topk_device_props* p, int block) {
   return {p->occupancy_single, p->occupancy_multi, p->occupancy_single16, p->occupancy_multi16};
 }
 
+// Whether a row of n elements streams wave by wave on an instance of
+// `block` threads: long enough to speculate, every wavefront segment holding
+// the two wave tiles of the sample, and a speculative rank below K (the
+// sample is 2 * block * kElems elements).  Mirrors the kernels' rule.
+bool waves_on(int block, int64_t n, int32_t K) {
+  const int64_t W = block / 64, wave_tile = 64 * rrt::kElems;
+  if (n < (int64_t)rrt::kSpecMinLen) return false;
+  const int64_t seg = (ceil_div(n, W) + wave_tile - 1) / wave_tile * wave_tile;
+  if (n < (W - 1) * seg + 2 * wave_tile) return false;
+  const int64_t M = 2 * (int64_t)block * rrt::kElems;
+  const int64_t want = ((int64_t)rrt::kSpecNum * K * M + (int64_t)rrt::kSpecDen * n - 1) / ((int64_t)rrt::kSpecDen * n);
+  return std::max<int64_t>(want, rrt::kSpecMinRank) < K;
+}
+
 // Workgroup width of the one-workgroup path when the caller does not force
-// one.
+// one.  512 threads (8 wavefronts per row) when every row gets a resident
+// workgroup of its own and rows of row_stride elements still speculate with
+// the 512-thread sample: a row's streaming is then spread over twice the
+// wavefronts.  Measured on MI355X, 64 rows: multi-token rows 22.3 -> 18.4
+// us, decode 17.8 -> 17.3 us; 4 x 8192 rows at K = 512 cannot speculate on
+// 512 threads and stay on 256 (9.7 us against 11.5).  Batches that fill the
+// GPU stay on 256 threads: four workgroups per CU overlap one row's
+// selection with other rows' streaming (prefill-shaped batch 191-201 us on
+// 256, 210 us on 512).  1024 threads measured slower everywhere.
 int auto_block_single(const topk_device_props* p, int32_t num_rows, int64_t row_stride, int32_t K) {
-  (void)p;
-  (void)num_rows;
-  (void)row_stride;
-  (void)K;
+  const int occ512 = std::min(p->occupancy_w512[0], p->occupancy_w512[2]);
+  if (occ512 >= 1 && (int64_t)num_rows <= (int64_t)p->num_cus * occ512 && waves_on(512, row_stride, K))
+    return 512;
   return rrt::kBlock;
 }
 

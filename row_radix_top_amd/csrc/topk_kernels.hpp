@@ -733,28 +733,35 @@ __device__ __forceinline__ void final_select(Smem<LAY>& sm, const Slice& sl, uin
 __device__ __forceinline__ float widen(float v) { return v; }
 __device__ __forceinline__ float widen(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 // VEC consecutive elements at p (aligned to VEC elements) into x[o .. o + VEC).
+// Scores are read once and never again by this launch, so the loads carry
+// the nontemporal hint: they stream through the caches without displacing
+// anything (measured on the prefill-shaped batch: 211.6 -> 198.1 us, and
+// the streaming-read reference 168 -> 149 us).
 template <int VEC, typename T>
 __device__ __forceinline__ void load_run(const T* __restrict__ p, float (&x)[kElems], int o) {
   if constexpr (std::is_same<T, float>::value) {
     static_assert(VEC == 4 || VEC == 2 || VEC == 1, "fp32 loads of 16, 8 or 4 bytes");
     if constexpr (VEC == 4) {
-      const float4 v = *reinterpret_cast<const float4*>(p);
+      const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
       x[o + 0] = v.x;
       x[o + 1] = v.y;
       x[o + 2] = v.z;
       x[o + 3] = v.w;
     } else if constexpr (VEC == 2) {
-      const float2 v = *reinterpret_cast<const float2*>(p);
+      const f32x2 v = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p));
       x[o + 0] = v.x;
       x[o + 1] = v.y;
     } else {
-      x[o] = *p;
+      x[o] = __builtin_nontemporal_load(p);
     }
   } else {
     static_assert(std::is_same<T, uint16_t>::value && (VEC == 8 || VEC == 1), "bf16 loads of 16 or 2 bytes");
     if constexpr (VEC == 8) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
       x[o + 0] = __uint_as_float(v.x << 16);
       x[o + 1] = __uint_as_float(v.x & 0xffff0000u);
       x[o + 2] = __uint_as_float(v.y << 16);
@@ -764,7 +771,7 @@ __device__ __forceinline__ void load_run(const T* __restrict__ p, float (&x)[kEl
       x[o + 6] = __uint_as_float(v.w << 16);
       x[o + 7] = __uint_as_float(v.w & 0xffff0000u);
     } else {
-      x[o] = widen(*p);
+      x[o] = widen(__builtin_nontemporal_load(p));
     }
   }
 }

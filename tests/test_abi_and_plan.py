@@ -249,3 +249,51 @@ def test_plan_large_k_layout():
     # Split-row blocks and cooperative lists size with the layout's capacity.
     p = rrt.plan_for_props(256, 2, 2, 8, 65536, 4096, split_rows=8, split_g=4)
     assert p["workspace_bytes"] == 256 + 8 * ((256 + 8 * 7168 * 4 + 255) // 256 * 256)
+
+
+# ---------------------------------------------------------------------------
+# Workgroup width
+# ---------------------------------------------------------------------------
+
+WIDE = dict(occupancy_w512=(2, 2, 2, 2), occupancy_w1024=(1, 1, 1, 1))
+
+
+def test_plan_block_width_auto():
+    # Few long rows that speculate with the 512-thread sample: 512 threads.
+    p = rrt.plan_for_props(256, 3, 3, 64, 32768, 2048, occupancy_single16=4, **WIDE)
+    assert p["path"] == rrt.PATH_SINGLE and p["block"] == 512 and p["grid"] == 64
+    p = rrt.plan_for_props(256, 3, 3, 64, 65536, 2048, occupancy_single16=4, **WIDE)
+    assert p["block"] == 512 and p["lds_bytes"] > 0
+    # 4 x 8192 at K = 512: the 512-thread sample (8192) would be the whole
+    # row, no speculation there, so 256 threads.
+    p = rrt.plan_for_props(256, 3, 3, 4, 8192, 512, occupancy_single16=4, **WIDE)
+    assert p["block"] == 256
+    # A batch that fills the GPU stays on 256 threads.
+    p = rrt.plan_for_props(256, 3, 3, 4096, 65536, 2048, occupancy_single16=4, **WIDE)
+    assert p["block"] == 256 and p["grid"] == 1024
+    # More rows than 512-thread slots: 256.
+    p = rrt.plan_for_props(256, 3, 3, 600, 32768, 2048, occupancy_single16=4, **WIDE)
+    assert p["block"] == 256
+    # No wide instance on the device (zeros): 256.
+    p = rrt.plan_for_props(256, 3, 3, 64, 32768, 2048, occupancy_single16=4)
+    assert p["block"] == 256
+
+
+def test_plan_block_width_forced():
+    for b in (256, 512, 1024):
+        p = rrt.plan_for_props(256, 3, 3, 64, 32768, 2048, force_block=b, **WIDE)
+        assert p["block"] == b and p["path"] == rrt.PATH_SINGLE
+        p = rrt.plan_for_props(256, 3, 3, 16, 131072, 2048, force_block=b, force_path=2, **WIDE)
+        assert p["block"] == b and p["path"] == rrt.PATH_MULTI
+        # Chunks of the multi path are whole tiles of this width.
+        assert p["chunk"] % (b * 8) == 0
+    with pytest.raises(rrt.TopKError):
+        rrt.plan_for_props(256, 3, 3, 64, 32768, 2048, force_block=384, **WIDE)
+    # A forced width the device cannot keep resident is an error, not a silent change.
+    with pytest.raises(rrt.TopKError):
+        rrt.plan_for_props(256, 3, 3, 64, 32768, 2048, force_block=1024)
+    # Split rows run on 256 threads only.
+    with pytest.raises(rrt.TopKError):
+        rrt.plan_for_props(256, 3, 3, 64, 32768, 2048, force_block=512, split_rows=4, **WIDE)
+    p = rrt.plan_for_props(256, 3, 3, 64, 32768, 2048, split_rows=4, **WIDE)
+    assert p["block"] == 256 and p["split_rows"] == 4
