@@ -9,6 +9,10 @@ fraction of the 8 TB/s peak, the roofline of the kernel, the CPU oracle timed
 on a bounded sample of the same rows, and per-launch figures for the other
 workloads (timed over rotating input copies so the 256 MB last-level cache
 cannot serve them).
+
+`--workload NAME` makes another workload the timed one (for profiling each
+configuration on its own); workloads smaller than 1 GiB then rotate over
+copies of their input totalling at least 1 GiB, one copy per step.
 """
 
 from __future__ import annotations
@@ -28,9 +32,19 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 METRIC = "rows/sec + effective HBM GB/s (fraction of peak) for ragged per-row top-2048"
 CSRC = os.path.join(ROOT, "row_radix_top_amd", "csrc")
-KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("topk_kernels.hip", "topk_internal.h", "topk_host.cpp")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_hbm_traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 1 << 30
+POOL_BYTES = 1 << 30
+
+
+def kernel_sources() -> list[str]:
+    """Every source of the HIP library, in a fixed order."""
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                  if f.endswith((".hip", ".hpp", ".h", ".cpp")))
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"hbm_traffic_{workload}.json")
 
 
 def log(msg: str) -> None:
@@ -41,7 +55,8 @@ def kernel_source_hash() -> str:
     """Hash of the kernel and launcher sources: a stored counter reading is
     used only while this matches the hash it was taken with."""
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
+    for path in kernel_sources():
+        h.update(os.path.basename(path).encode())
         h.update(open(path, "rb").read())
     return h.hexdigest()
 
@@ -70,13 +85,14 @@ def time_launches(fn, n: int):
     return start.elapsed_time(end) / n
 
 
-def measured_traffic(per_launch_alg: int):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this workload, if it was taken on the current kernel sources; else None."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
         return None
     try:
-        d = json.load(open(TRAFFIC_FILE))
+        d = json.load(open(path))
     except (OSError, ValueError):
         return None
     if d.get("kernel_source_sha256") != kernel_source_hash():
@@ -84,16 +100,18 @@ def measured_traffic(per_launch_alg: int):
     return d.get("hbm_bytes_per_launch")
 
 
-def read_ceiling(scores, lengths, valid_bytes: int, launches: int = 20) -> float:
+def read_ceiling(pool, lengths, valid_bytes: int, launches: int = 100) -> float:
     """Effective GB/s of the library's streaming-read reference kernel, which
     reads exactly the valid bytes the selection reads (same tiles, load
-    width and prefetch ring) and selects nothing."""
+    width and prefetch ring) and selects nothing; over the same rotating
+    copies as the timed steps."""
     import torch
     import row_radix_top_amd as rrt
-    keys = torch.empty(scores.shape[0], dtype=torch.int32, device=scores.device)
-    for _ in range(3):
-        rrt.read_reference(scores, lengths, out=keys)
-    ms = time_launches(lambda i: rrt.read_reference(scores, lengths, out=keys), launches)
+    keys = torch.empty(pool.shape[1], dtype=torch.int32, device=pool.device)
+    n = pool.shape[0]
+    for i in range(3):
+        rrt.read_reference(pool[i % n], lengths, out=keys)
+    ms = time_launches(lambda i: rrt.read_reference(pool[i % n], lengths, out=keys), launches)
     return valid_bytes / (ms * 1e-3) / 1e9
 
 
@@ -108,32 +126,57 @@ def copy_calibration(dev, launches: int = 10) -> float:
     return 2 * COPY_BYTES / (ms * 1e-3) / 1e9
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, budget_s: float):
-    """Time the CPU oracle (as is) on the same workload: the first rows that
-    fit the time budget, or whole passes over all rows repeated until the
-    budget is spent when one pass is shorter."""
+    """Time the CPU oracle (as is) on the same workload, on a bounded sample:
+    the first rows that take about budget_s / 12 seconds on all threads.
+    After one warm-up run, 5 timed runs at all threads and 5 at one thread;
+    medians reported (generation and transfers excluded)."""
     from oracle import topk_ragged_oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
     probe = min(64, w.num_rows)
     topk_ragged_oracle(w.scores[:8], w.flat_lengths[:8], w.K, threads=threads)  # warm
     t0 = time.perf_counter()
     topk_ragged_oracle(w.scores[:probe], w.flat_lengths[:probe], w.K, threads=threads)
-    t_probe = time.perf_counter() - t0
-    rows = int(min(w.num_rows, max(probe, probe * budget_s / max(t_probe, 1e-6))))
-    passes, t = 0, 0.0
-    while passes == 0 or (rows == w.num_rows and t < budget_s):
-        t0 = time.perf_counter()
-        topk_ragged_oracle(w.scores[:rows], w.flat_lengths[:rows], w.K, threads=threads)
-        t += time.perf_counter() - t0
-        passes += 1
+    t_probe = max(time.perf_counter() - t0, 1e-6)
+    # One all-thread run takes about budget_s / 12, so that 6 of them plus
+    # 6 one-thread runs of a 1/threads share stay near budget_s in all.
+    rows = int(min(w.num_rows, max(probe, probe * (budget_s / 12.0) / t_probe)))
+    rows1 = max(1, min(rows, int(round(rows / threads)) or 1))
+
+    def med(nrows, nthreads):
+        topk_ragged_oracle(w.scores[:nrows], w.flat_lengths[:nrows], w.K, threads=nthreads)  # warm-up run
+        ts = []
+        for _ in range(5):
+            t0 = time.perf_counter()
+            topk_ragged_oracle(w.scores[:nrows], w.flat_lengths[:nrows], w.K, threads=nthreads)
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts)), ts
+
+    t_all, _ = med(rows, threads)
+    t_one, _ = med(rows1, 1)
     valid, _ = algorithmic_bytes(w.flat_lengths[:rows], w.row_stride, w.K)
+    valid1, _ = algorithmic_bytes(w.flat_lengths[:rows1], w.row_stride, w.K)
     return {
-        "value": rows * passes / t,
+        "value": rows / t_all,
         "unit": "rows/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"first {rows} of {w.num_rows} rows of the same workload x {passes} passes, {t:.2f} s, "
-                  f"{valid * passes / t / 1e9:.2f} effective GB/s",
+        "sample": f"first {rows} of {w.num_rows} rows of the same workload on {threads} threads, median of 5 "
+                  f"runs after 1 warm-up ({t_all:.3f} s each, {valid / t_all / 1e9:.2f} effective GB/s); "
+                  f"first {rows1} rows on 1 thread, median of 5 after 1 warm-up",
+        "cpu_model": cpu_model(),
+        "single_thread_rows_per_s": rows1 / t_one,
+        "single_thread_effective_GBps": round(valid1 / t_one / 1e9, 3),
     }
 
 
@@ -185,7 +228,7 @@ def bench_other(name: str, copies_bytes: int = 1 << 30, launches: int = 200):
     w = workloads.make_workload(name)
     dev = torch.device("cuda:0")
     one = torch.from_numpy(w.scores).to(dev)
-    ncopy = max(1, min(1024, copies_bytes // max(1, one.numel() * 4)))
+    ncopy = max(1, min(16384, copies_bytes // max(1, one.numel() * 4)))
     pool = torch.empty((ncopy,) + tuple(one.shape), dtype=torch.float32, device=dev)
     pool.copy_(one.unsqueeze(0).expand_as(pool))
     L = torch.from_numpy(w.flat_lengths).to(dev)
@@ -210,7 +253,7 @@ def bench_other(name: str, copies_bytes: int = 1 << 30, launches: int = 200):
         "effective_GBps": round(valid / (ms * 1e-3) / 1e9, 1),
         "frac_of_hbm_peak": round(valid / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "rotating_copies": ncopy,
-        "path": plan["path"], "grid": plan["grid"], "wg_per_row": plan["wg_per_row"],
+        "path": plan["path"], "block": plan["block"], "grid": plan["grid"], "wg_per_row": plan["wg_per_row"],
     }
     del pool, ws, out
     torch.cuda.empty_cache()
@@ -331,7 +374,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill")
-    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true", help="skip the other workloads")
     ap.add_argument("--check", action="store_true", help="compare sampled rows with the oracle")
@@ -354,43 +397,56 @@ def main() -> int:
 
     log(f"generating workload {args.workload}")
     w = workloads.make_workload(args.workload)
-    scores = torch.from_numpy(w.scores).to(dev)
+    one = torch.from_numpy(w.scores).to(dev)
+    # Inputs smaller than 1 GiB rotate over copies totalling at least 1 GiB,
+    # one copy per step, so that the 256 MB last-level cache cannot serve them.
+    ncopy = max(1, min(16384, -(-POOL_BYTES // max(1, one.numel() * 4)))) if one.numel() * 4 < POOL_BYTES else 1
+    if ncopy > 1:
+        pool = torch.empty((ncopy,) + tuple(one.shape), dtype=torch.float32, device=dev)
+        pool.copy_(one.unsqueeze(0).expand_as(pool))
+        del one
+    else:
+        pool = one.unsqueeze(0)
     lengths = torch.from_numpy(w.flat_lengths).to(dev)
     out = torch.empty((w.num_rows, w.K), dtype=torch.int32, device=dev)
     nbytes = rrt.workspace_size(w.num_rows, w.row_stride, w.K, device=dev)
     ws = rrt.new_workspace(nbytes, dev)
-    plan = rrt.query_plan(scores, w.K)
-    log(f"plan {plan}")
+    plan = rrt.query_plan(pool[0], w.K)
+    log(f"plan {plan}, {ncopy} input copies")
 
-    def step(_i=0):
-        rrt.topk_ragged(scores, lengths, w.K, out=out, workspace=ws, next_n=w.next_n)
+    def step(i=0):
+        rrt.topk_ragged(pool[i % ncopy], lengths, w.K, out=out, workspace=ws, next_n=w.next_n)
 
-    for _ in range(args.warmup):
-        step()
+    # The streaming-read ceiling is measured first: its launches also bring the
+    # GPU out of idle before the warmup and timed steps.
+    valid, alg = algorithmic_bytes(w.flat_lengths, w.row_stride, w.K)
+    ceiling = read_ceiling(pool, lengths, valid)
+    log(f"streaming-read reference: {ceiling:.1f} GB/s")
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms_ev = time_launches(step, args.steps)
+    ms_ev = time_launches(lambda i: step(args.warmup + i), args.steps)
     wall = time.perf_counter() - t0
     log(f"{args.steps} steps: {ms_ev:.4f} ms/step (events), wall {wall:.3f} s")
 
     if args.check:
         from oracle import topk_ragged_oracle
-        rows = np.linspace(0, w.num_rows - 1, 64).astype(int)
+        rows = np.linspace(0, w.num_rows - 1, min(64, w.num_rows)).astype(int)
         exp = topk_ragged_oracle(w.scores[rows], w.flat_lengths[rows], w.K)
         got = out.cpu().numpy()[rows]
         assert np.array_equal(got, exp), "bench output differs from the oracle"
         log("sampled rows match the oracle")
 
-    valid, alg = algorithmic_bytes(w.flat_lengths, w.row_stride, w.K)
-    ceiling = read_ceiling(scores, lengths, valid)
-    log(f"streaming-read reference: {ceiling:.1f} GB/s")
     if args.copy_calibration:
         log(f"copy calibration: {copy_calibration(dev):.1f} GB/s (read + write)")
     sec = ms_ev * 1e-3
     rows_per_s = w.num_rows / sec
     eff = valid / sec / 1e9
     achieved = alg / sec / 1e9
-    traffic = measured_traffic(alg)
+    traffic = measured_traffic(w.name)
+    kname = ("topk_single_kernel" if plan["path"] == 1 else "topk_multi_kernel") + \
+        f"<vec={plan['vec']}, block={plan['block']}, idx16={bool(plan['idx16'])}>"
     result = {
         "metric": METRIC,
         "value": rows_per_s,
@@ -413,6 +469,7 @@ def main() -> int:
         "frac_of_hbm_peak": round(eff / HBM_PEAK_GBPS, 4),
         "read_reference_GBps": round(ceiling, 1),
         "frac_of_read_reference": round(eff / ceiling, 4),
+        "input_copies": ncopy,
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
@@ -420,16 +477,18 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": ("topk_single_kernel" if plan["path"] == 1 else "topk_multi_kernel")
-                      + f"<vec={plan['vec']}, idx16={bool(plan['idx16'])}>",
+            "kernel": kname,
             "algorithmic_bytes_per_launch": alg,
         },
-        "plan": {k: plan[k] for k in ("path", "grid", "wg_per_row", "kmax", "vec", "idx16", "resident_cap")},
+        "plan": {k: plan[k] for k in ("path", "block", "grid", "wg_per_row", "kmax", "vec", "idx16", "resident_cap")},
     }
+    del pool
 
     if not args.no_others:
         others = {}
         for name in ("small", "decode", "mtp", "long_k1024", "long_k2048"):
+            if name == w.name:
+                continue
             log(f"timing {name}")
             others[name] = bench_other(name)
         result["workloads"] = others
@@ -437,7 +496,9 @@ def main() -> int:
         result["decode_latency"] = decode_latency()
         if w.name == "prefill":
             log("extended entry points")
+            scores = torch.from_numpy(w.scores).to(dev)
             result["extensions"] = extensions(w, scores, lengths)
+            del scores
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")

@@ -359,8 +359,8 @@ int topk_ragged_read_reference(const float* scores, int64_t row_stride, const in
  * allocates or frees device memory.
  *   - A launch whose plan needs more than that fails with TOPK_EWORKSPACE
  *     and launches nothing (topk_ragged_workspace_size gives the need: the
- *     prefill-shaped batches need 256 bytes, the long-row batches about
- *     0.35 MB per row).
+ *     prefill-shaped batches need 256 bytes, rows of 131072 elements at
+ *     K = 2048 about 0.41 MB per row, more for K above 2048).
  *   - The first call on a GPU also queues a fill kernel on `stream` that
  *     zeroes the array, ahead of its own launch; every launch leaves the
  *     array all-zero again (in-kernel cleanup).

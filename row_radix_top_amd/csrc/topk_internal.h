@@ -97,11 +97,14 @@ constexpr uint32_t kErrSearch = 2u;
 // Per-row block layout (bytes from the block start):
 //   0    arrival counter (u32)
 //   128  exit counter (u32)
-//   256  per-workgroup slots, 4 x u32 each: [above digit 1, above digit 2, list length, -]
+//   256  per-workgroup slots, 4 x u32 each: [above digit 1, above digit 2,
+//        list length, published count (bit 31: nothing published)]
 //   ...  digit-1 histogram, 2048 x u32
 //   ...  digit-2 histogram, 2048 x u32
 //   ...  their sums over groups of 32 bins, 64 x u32 each (digit 1, digit 2)
-//   ...  per-workgroup lists, cap x u32 each
+//   ...  per-workgroup lists, cap x u32 each: the one-round path publishes
+//        up to cap / 2 candidates there (fp32 bits in the first half, row
+//        indices in the second); the three rounds write undecided keys.
 struct GroupLayout {
   uint64_t slots, h1, h2, c1, c2, lists, bytes;
 };

@@ -498,6 +498,58 @@ __device__ __forceinline__ void key_range(Smem<LAY>& sm, const uint32_t (&k)[S],
   hi = uni(h);
 }
 
+// [mn, mx]: the smallest and largest key inside [lo, hi] (both uniform; mn >
+// mx when none is).  One barrier, as key_range.
+template <int LAY, int S>
+__device__ __forceinline__ void interval_range(Smem<LAY>& sm, const uint32_t (&k)[S], const Slice& sl, uint32_t lo,
+                                               uint32_t hi, uint32_t& mn, uint32_t& mx) {
+  constexpr int W = Shape<LAY>::kWaves;
+  const uint32_t range = hi - lo;
+  uint32_t a0 = 0xffffffffu, b0 = 0u, a1 = 0xffffffffu, b1 = 0u;
+#pragma unroll
+  for (int q = 0; q < S / 4; ++q) {
+    if ((uint32_t)(4 * q) < sl.sp) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int j = 4 * q + c;
+        const bool in = (uint32_t)j < sl.nv && k[j] - lo <= range;
+        if (c & 1) {
+          a1 = min(a1, in ? k[j] : 0xffffffffu);
+          b1 = max(b1, in ? k[j] : 0u);
+        } else {
+          a0 = min(a0, in ? k[j] : 0xffffffffu);
+          b0 = max(b0, in ? k[j] : 0u);
+        }
+      }
+    }
+  }
+  const uint32_t wa = wave_min(min(a0, a1));
+  const uint32_t wb = wave_max(max(b0, b1));
+  const int w = tid() >> 6;
+  if ((tid() & 63) == 0) {
+    sm.red[w] = wa;
+    sm.red[W + w] = wb;
+  }
+  __syncthreads();
+  uint32_t l = 0xffffffffu, h = 0u;
+#pragma unroll
+  for (int q = 0; q < W / 4; ++q) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(&sm.red[4 * q]);
+    const u32x4 y = *reinterpret_cast<const u32x4*>(&sm.red[W + 4 * q]);
+    l = min(l, min(min(x.x, x.y), min(x.z, x.w)));
+    h = max(h, max(max(y.x, y.y), max(y.z, y.w)));
+  }
+  mn = uni(l);
+  mx = uni(h);
+  __syncthreads();  // sm.red is free again
+}
+
+// A threshold bin holding more entries than this after a pass is checked
+// for being one key (ties), and otherwise narrowed to its exact range: with
+// many equal keys every further pass would send most lanes of a wavefront to
+// the same histogram word.
+constexpr uint32_t kTieCheck = 128;
+
 // Narrows [lo, hi] (which holds every entry) to the bin holding the keep-th
 // largest entry.  Stops when that bin is taken whole (its entries are
 // exactly the ones still needed, or entries above plus the bin number at
@@ -559,6 +611,15 @@ __device__ Sel range_select(Smem<LAY>& sm, const uint32_t (&k)[S], const Slice& 
     hi = hi - lo > width ? lo + width : hi;
     whole = f.in_bin == krem || r.above + f.in_bin <= stop_total;
     if (whole || sh == 0u || !f.ok) break;
+    if (f.in_bin > kTieCheck) {
+      uint32_t mn, mx;
+      interval_range<LAY, S>(sm, k, sl, lo, hi, mn, mx);
+      if (mn <= mx) {
+        lo = mn;
+        hi = mx;
+        if (mn == mx) break;  // one key: take krem of its entries, lowest index first
+      }
+    }
   }
   r.lo = lo;
   r.hi = hi;
@@ -641,6 +702,33 @@ __device__ __forceinline__ void emit_chosen(Smem<LAY>& sm, const uint32_t (&k)[S
   uint32_t g = gt_base + (before & 0xffffu);
   uint32_t e = eq_base + (before >> 16);
   const uint32_t p0 = slot_pos(sl, 0);
+  if (whole) {
+    // Every key >= lo is chosen: one ballot per slot.
+#pragma unroll
+    for (int q = 0; q < S / 4; ++q) {
+      if ((uint32_t)(4 * q) < sp) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int j = 4 * q + c;
+          const bool gt = (gtm >> j) & 1u;
+          const uint64_t bg = ballot(gt);
+          const uint32_t pos = g + lanes_below(bg);
+          if (gt && pos < limit) {
+            if constexpr (MODE != kToBuffer) {
+              out[pos] = (int32_t)(ibase + ix[j]);
+              if (vout != nullptr) vout[pos] = __uint_as_float(sm.val[p0 + 64u * (uint32_t)j]);
+            } else {
+              sm.val[pos] = rv[j];
+              sm.idx[pos] = (typename Shape<LAY>::Idx)ix[j];
+            }
+          }
+          g += popc64(bg);
+        }
+      }
+    }
+    if constexpr (MODE == kToBuffer) clear_hists(sm);
+    return;
+  }
 #pragma unroll
   for (int q = 0; q < S / 4; ++q) {
     if ((uint32_t)(4 * q) < sp) {
@@ -1762,6 +1850,86 @@ __device__ void group_barrier(uint32_t* ctr, uint32_t target, uint32_t spin_limi
   __syncthreads();
 }
 
+// The waiting half of group_barrier, for a workgroup that has already
+// arrived: one thread polls until the count reaches target (bounded as
+// above), then the workgroup proceeds.
+__device__ void group_wait(const uint32_t* ctr, uint32_t target, uint32_t spin_limit, uint32_t* err) {
+  if (threadIdx.x == 0) {
+    uint32_t polls = 0;
+    while (ws_load(ctr) < target) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++polls > spin_limit) {
+        __hip_atomic_fetch_or(err, kErrSpin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Gathers the chunks' published candidates of a row, in chunk order (so in
+// index order), into buffer positions [0, total): chunk gg's entries sit at
+// lists + gg * CAP (fp32 bits) and + pub (row indices), and go to merged
+// positions [s_off[gg], s_off[gg + 1]) (s_off ascending, s_off[0] = 0, grow
+// chunks, total = s_off[grow] <= the buffer capacity).  First every merged
+// position's source offset is written into the buffer (one short loop per
+// chunk, LDS only); then each thread reads its positions' offsets and issues
+// all its workspace loads back to back, with no branch between them, so the
+// gather costs about one round trip; the values go to the buffer last.
+template <int LAY>
+__device__ __forceinline__ void gather_union(Smem<LAY>& sm, const uint32_t* lists, uint32_t pub, const uint32_t* s_off,
+                                             int grow, uint32_t total) {
+  constexpr int S = Shape<LAY>::kSlots;
+  constexpr uint32_t NT = (uint32_t)Shape<LAY>::kBlock;
+  constexpr uint32_t CAP = (uint32_t)Shape<LAY>::kCap;
+  using Idx = typename Shape<LAY>::Idx;
+  const uint32_t t = tid();
+  // Every merged position's source word goes into the buffer's value array
+  // first (it is overwritten last).  The chunk bounds are read once, lane gg
+  // of each wavefront holding s_off[gg], so the loop waits on nothing.
+  const uint32_t lane = t & 63u;
+  const uint32_t bound = lane < (uint32_t)grow ? s_off[lane] : 0u;  // grow <= 64 chunk starts
+  for (int gg = 0; gg < grow; ++gg) {
+    const uint32_t o = lane_value(bound, gg);
+    const uint32_t e = gg + 1 < grow ? lane_value(bound, gg + 1) : total;
+    const uint32_t src = (uint32_t)gg * CAP - o;
+    for (uint32_t i = o + t; i < e; i += NT) sm.val[i] = src + i;
+  }
+  __syncthreads();
+  uint32_t vb[S], vi[S];
+#pragma unroll
+  for (int j = 0; j < S; ++j) {
+    const uint32_t i = t + (uint32_t)j * NT;
+    const uint32_t a = i < total ? sm.val[i] : 0u;
+    vb[j] = ws_load(lists + a);
+    vi[j] = ws_load(lists + a + pub);
+  }
+  __syncthreads();  // every position's address has been read before the buffer is overwritten
+#pragma unroll
+  for (int j = 0; j < S; ++j) {
+    const uint32_t i = t + (uint32_t)j * NT;
+    if (i < total) {
+      sm.val[i] = vb[j];
+      sm.idx[i] = (Idx)vi[j];
+    }
+  }
+}
+
+// Zeroes the published candidates of a row's grow chunks (positions as in
+// gather_union), chunk by chunk.
+template <int NT>
+__device__ __forceinline__ void clear_union(uint32_t* lists, uint32_t cap, uint32_t pub, const uint32_t* s_off,
+                                            int grow) {
+  for (int gg = 0; gg < grow; ++gg) {
+    const uint32_t m = s_off[gg + 1] - s_off[gg];
+    uint32_t* l = lists + (uint32_t)gg * cap;
+    for (uint32_t i = threadIdx.x; i < m; i += NT) {
+      ws_store(l + i, 0u);
+      ws_store(l + pub + i, 0u);
+    }
+  }
+}
+
 // Adds a complete LDS histogram into a workspace histogram (non-zero bins
 // only) and its sums over groups of 32 bins into the workspace's group sums
 // gc.  The LDS copy is left as it is.  NT threads.
@@ -1891,6 +2059,94 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
   const int64_t c0 = (int64_t)g * p.chunk;
   const int64_t c1 = c0 + p.chunk < n ? c0 + p.chunk : n;
   const E* rowp = row_of<E>(p, row);
+  float* vout = p.out_val != nullptr ? p.out_val + (int64_t)row * p.K : nullptr;
+  uint32_t* my_list = lists + (uint64_t)g * CAP;
+  uint32_t base = 0;  // arrivals counted on ctr before the rounds below
+
+  // One round.  Every workgroup of the row takes the same speculative bound
+  // from the same sample (the first two wave tiles of each wavefront segment
+  // of the whole row, through the same integer selection), streams its chunk
+  // wave by wave keeping the elements that reach it, publishes them with
+  // their row indices, and arrives once.  When every chunk published and at
+  // least K and at most the buffer's capacity reached the bound in all, the
+  // union holds every element of the row's K best (each is at least the K-th
+  // best key, which is at least the bound); the last workgroup to arrive
+  // gathers it and selects, and no workgroup waits for a second round.
+  // Otherwise (the bound was above the K-th best, a wavefront's part of the
+  // buffer overflowed, or too many elements passed) every workgroup falls
+  // back to the three rounds below, which need nothing from the bound.
+  if (wave_mode<LAY>((uint32_t)n, K)) {
+    constexpr uint32_t PUB = (uint32_t)CAP / 2u;  // published entries a chunk may hold
+    constexpr uint32_t SUB = (uint32_t)CAP / Shape<LAY>::kWaves;
+    uint32_t mine = 0, woff = 0, total = 0, Lr = 0;
+    float x0[kElems], x1[kElems];
+    const bool ok = stream_piece_waves<LAY, VEC>(sm, rowp, (uint32_t)n, K, (uint32_t)c0, (uint32_t)c1, x0, x1, false,
+                                                mine, woff, total, Lr);
+    const bool pub = ok && Lr != 0u && total <= PUB;
+    if (pub) {
+      const uint32_t lane = t & 63, s0 = ((uint32_t)t >> 6) * SUB;
+      for (uint32_t i = lane; i < mine; i += 64u) {
+        ws_store(my_list + woff + i, sm.val[s0 + i]);
+        ws_store(my_list + PUB + woff + i, (uint32_t)sm.idx[s0 + i]);  // row positions already
+      }
+    }
+    if (t == 0) ws_store(&slots[4 * g + 3], pub ? total : (0x80000000u | (total & 0x7fffffffu)));
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t == 0) sm.acc[5] = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const bool last = uni(sm.acc[5]) == (uint32_t)grow - 1u;
+    if (!last) group_wait(ctr, (uint32_t)grow, p.spin_limit, err);
+    // Every workgroup reads the same published counts and decides alike.
+    if (t < 64) {  // the whole of wavefront 0
+      const uint32_t v = t < grow ? ws_load(&slots[4 * t + 3]) : 0u;
+      const uint32_t c = (v & 0x80000000u) ? 0u : (v < PUB ? v : PUB);
+      const uint32_t incl = wave_incl_scan(c);
+      const uint64_t unpublished = ballot(t < grow && (v & 0x80000000u) != 0u);
+      if (t < grow) s_off[t + 1] = incl;
+      if (t == 0) {
+        s_off[0] = 0u;
+        sm.acc[6] = unpublished != 0u ? 1u : 0u;
+      }
+    }
+    __syncthreads();
+    const uint32_t sum = uni(s_off[grow]);
+    const bool fast = uni(sm.acc[6]) == 0u && sum >= K && sum <= (uint32_t)CAP;
+    if (fast) {
+      if (last) gather_union<LAY>(sm, lists, PUB, s_off, grow, sum);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();  // every gather load has completed
+      // Leave.  The last workgroup out zeroes the published lists, the slots
+      // and both counters (nobody reads them any more); the workgroup that
+      // selects does so after its selection, off its critical path.
+      if (t == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(exit_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm.acc[4] = (old == (uint32_t)grow - 1u) ? 1u : 0u;
+      }
+      __syncthreads();
+      const bool clean = uni(sm.acc[4]) != 0u;
+      if (last) final_select<LAY>(sm, plain_slice<LAY>(sum), K, out, offset_of(p, row), vout);
+      if (clean) {
+        clear_union<NT>(lists, (uint32_t)CAP, PUB, s_off, grow);
+        if (t < 4 * grow) ws_store(&slots[t], 0u);
+        if (t == 0) {
+          ws_store(ctr, 0u);
+          ws_store(exit_ctr, 0u);
+        }
+      }
+      return;
+    }
+    // Fallback: this chunk's published entries are nobody's input any more.
+    if (pub) {
+      for (uint32_t i = t; i < total; i += NT) {
+        ws_store(my_list + i, 0u);
+        ws_store(my_list + PUB + i, 0u);
+      }
+    }
+    __syncthreads();  // s_off and sm.acc are reused below
+    base = (uint32_t)grow;
+  }
+
   uint32_t cnt = 0, L = 0;
   float x0[kElems], x1[kElems];
   // The chunk speculates from its first two tiles, as a general-path row
@@ -1911,7 +2167,6 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
   const uint32_t sp = sl.sp, nv = sl.nv;
   uint32_t k[S];
   load_keys<LAY>(sm, k, sl);
-  float* vout = p.out_val != nullptr ? p.out_val + (int64_t)row * p.K : nullptr;
 
   // Round 1: the chunk's top-digit (11-bit) histogram into the row's, then
   // the row-wide threshold digit from a copy of the row's.  (Loops over the
@@ -1930,7 +2185,7 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
   }
   __syncthreads();
   merge_hist<NT>(sm.hist1, h1, gs1);
-  group_barrier(ctr, 1u * grow, p.spin_limit, err);
+  group_barrier(ctr, base + 1u * grow, p.spin_limit, err);
   const Found f1 = ws_find(h1, gs1, K);
   uint32_t ok = f1.ok;
   uint32_t krem = K - f1.above;
@@ -1960,7 +2215,7 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
   __syncthreads();
   merge_hist<NT>(sm.hist1, h2, gs2);
   if (t == 0) ws_store(&slots[4 * g + 0], sm.acc[0]);
-  group_barrier(ctr, 2u * grow, p.spin_limit, err);
+  group_barrier(ctr, base + 2u * grow, p.spin_limit, err);
   const Found f2 = ws_find(h2, gs2, krem);
   ok &= f2.ok;
   krem -= f2.above;
@@ -1988,7 +2243,6 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
     wave_add(&sm.acc[1], n_above);
     uint32_t len;
     uint32_t at = wave_exclusive(sm, mine, &len);
-    uint32_t* my_list = lists + (uint64_t)g * CAP;
 #pragma unroll
     for (int q = 0; q < S / 4; ++q) {
       if ((uint32_t)(4 * q) < sp) {
@@ -2007,7 +2261,7 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
       ws_store(&slots[4 * g + 2], len);
     }
   }
-  group_barrier(ctr, 3u * grow, p.spin_limit, err);
+  group_barrier(ctr, base + 3u * grow, p.spin_limit, err);
   for (int i = t; i < kBins; i += NT) sm.hist1[i] = 0u;  // round 2's local histogram was merged before the barrier
 
   // Every chunk's list, flattened: offsets by a prefix sum over the lengths.

@@ -126,11 +126,14 @@ def test_plan_single_when_multi_kernel_cannot_run():
 def test_plan_index_width_and_vec():
     for K in (1, 256, 1000, 2048):
         assert rrt.plan_for_props(256, 2, 2, 4, 8192, K)["kmax"] == 2048
-    # 16-bit candidate indices when a row (single path) or chunk (multi) fits them.
+    # 16-bit candidate indices when every row index fits them, on both paths:
+    # the workgroup that merges a row's chunks holds row indices.
     assert rrt.plan_for_props(256, 3, 3, 4096, 65536, 2048)["idx16"] == 1
     assert rrt.plan_for_props(256, 3, 3, 4096, 65537, 2048)["idx16"] == 0
     p = rrt.plan_for_props(256, 3, 3, 16, 131072, 2048)
-    assert p["path"] == rrt.PATH_MULTI and p["chunk"] <= 65536 and p["idx16"] == 1
+    assert p["path"] == rrt.PATH_MULTI and p["chunk"] <= 65536 and p["idx16"] == 0
+    p = rrt.plan_for_props(256, 3, 3, 16, 65536, 2048, force_path=2)
+    assert p["path"] == rrt.PATH_MULTI and p["idx16"] == 1
     p = rrt.plan_for_props(256, 3, 3, 2, 1 << 20, 2048, force_path=2, force_wg_per_row=8)
     assert p["chunk"] > 65536 and p["idx16"] == 0
     assert rrt.plan_for_props(256, 3, 3, 4, 131072, 2048, force_path=1)["idx16"] == 0

@@ -100,9 +100,12 @@ def test_mtp_rows_split_across_workgroups(G):
 
 @pytest.mark.parametrize("G", [1, 2, 3, 5, 16, 31, 64])
 def test_long_rows_group_sizes(G):
+    # 256-thread workgroups (up to 3 per CU on the cooperative path), so that
+    # every G up to 64 per row can be resident for the 16 rows or not.
     w = workloads.make_workload("long_k2048")
     exp = topk_ragged_oracle(w.scores, w.lengths, w.K)
-    got, plan = run_gpu(w.scores, w.lengths, w.K, tag=f"long G={G}", force_path=2, force_wg_per_row=G)
+    got, plan = run_gpu(w.scores, w.lengths, w.K, tag=f"long G={G}", force_path=2, force_wg_per_row=G,
+                        force_block=256)
     if plan["path"] == rrt.PATH_MULTI:
         assert plan["wg_per_row"] == G
     else:

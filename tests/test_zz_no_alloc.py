@@ -91,23 +91,22 @@ def test_noalloc_refuses_more_than_its_scratch():
     import torch
     dev = torch.device("cuda:0")
     limit = binding.NOALLOC_SCRATCH_BYTES
-    # The smallest of a few long-row shapes whose workspace exceeds the scratch.
+    # The first of a few long-row shapes whose workspace exceeds the scratch
+    # (the large-K layout has the larger per-workgroup lists).
     shape = None
-    for rows in (64, 96, 128, 192, 256, 384, 512):
-        for stride in (131072, 262144, 1 << 20):
-            need = rrt.workspace_size(rows, stride, 2048, device=dev)
-            if need > limit:
-                shape = (rows, stride, need)
-                break
-        if shape:
-            break
+    for K in (2048, 4096):
+        for rows in (16, 32, 64, 96, 128):
+            for stride in (131072, 262144, 1 << 20):
+                need = rrt.workspace_size(rows, stride, K, device=dev)
+                if need > limit and shape is None:
+                    shape = (rows, stride, K, need)
     assert shape is not None, "no shape needs more workspace than the scratch holds"
-    rows, stride, need = shape
-    note(f"noalloc refusal: rows={rows} stride={stride} needs {need} > {limit}")
+    rows, stride, K, need = shape
+    note(f"noalloc refusal: rows={rows} stride={stride} K={K} needs {need} > {limit}")
     s = torch.zeros((rows, stride), dtype=torch.float32, device=dev)
     L = torch.full((rows,), stride, dtype=torch.int32, device=dev)
-    out = torch.full((rows, 2048), -7, dtype=torch.int32, device=dev)
-    rc = _abi_noalloc(s, L, 2048, 1, out)
+    out = torch.full((rows, K), -7, dtype=torch.int32, device=dev)
+    rc = _abi_noalloc(s, L, K, 1, out)
     assert rc == -3, f"expected TOPK_EWORKSPACE, got {rc}"
     assert "scratch" in binding.last_error()
     torch.cuda.synchronize()
