@@ -2117,15 +2117,16 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();  // every gather load has completed
       // Leave.  The last workgroup out zeroes the published lists, the slots
-      // and both counters (nobody reads them any more); the workgroup that
-      // selects does so after its selection, off its critical path.
-      if (t == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(exit_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sm.acc[4] = (old == (uint32_t)grow - 1u) ? 1u : 0u;
-      }
+      // and both counters (nobody reads them any more).  The workgroup that
+      // selects issues its exit before the selection and looks at the
+      // answer after it, so neither the atomic's round trip nor a cleanup
+      // sits on its critical path.
+      uint32_t old = 0u;
+      if (t == 0) old = __hip_atomic_fetch_add(exit_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (last) final_select<LAY>(sm, plain_slice<LAY>(sum), K, out, offset_of(p, row), vout);
+      if (t == 0) sm.acc[4] = (old == (uint32_t)grow - 1u) ? 1u : 0u;
       __syncthreads();
       const bool clean = uni(sm.acc[4]) != 0u;
-      if (last) final_select<LAY>(sm, plain_slice<LAY>(sum), K, out, offset_of(p, row), vout);
       if (clean) {
         clear_union<NT>(lists, (uint32_t)CAP, PUB, s_off, grow);
         if (t < 4 * grow) ws_store(&slots[t], 0u);
