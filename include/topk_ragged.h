@@ -195,7 +195,7 @@ int topk_ragged_bf16(const uint16_t* scores, int64_t row_stride, const int32_t* 
  * rows than resident workgroups (the PR #41748 page, Motivation: rows up to
  * the radix threshold need no workspace).  With more rows than that, a
  * 256-byte workspace holds the counter that hands rows to workgroups as they
- * finish; rows split over several workgroups need a block per row on top. */
+ * finish; rows that several workgroups share need a block per row on top. */
 int topk_ragged_workspace_size(int32_t num_rows, int64_t row_stride, int32_t K,
                                hipStream_t stream, size_t* bytes);
 
@@ -269,9 +269,6 @@ typedef struct {
   int32_t fell_back;      /* 1 if a requested multi plan could not be made co-resident */
   int32_t idx16;          /* 1 if the instance keeps 16-bit candidate indices */
   uint64_t workspace_bytes;
-  int32_t split_rows;     /* single path: the last split_rows rows are split into chunks */
-  int32_t split_g;        /* chunks per split row */
-  int64_t split_chunk;    /* elements per chunk (a multiple of 2048) */
 } topk_plan;
 
 typedef struct {
@@ -282,9 +279,6 @@ typedef struct {
   int64_t force_chunk;       /* 0 auto, else elements per workgroup (multiple of 4) */
   uint32_t spin_limit;       /* 0 default; bound on a cooperative wait (polls) */
   int32_t min_chunk;         /* 0 default; smallest per-workgroup chunk the planner picks */
-  int32_t split_rows;        /* single path: 0 auto, -1 none, else split the last split_rows rows */
-  int32_t split_g;           /* 0 auto, else chunks per split row (1 .. 16) */
-  int64_t split_chunk;       /* 0 auto, else elements per chunk (a multiple of 2048) */
   int32_t max_occupancy;     /* 0 the device's, else plan as if no instance could keep more
                                 workgroups per CU resident (emulates a smaller device) */
   int32_t force_idx32;       /* 1: never keep 16-bit candidate indices (testing) */

@@ -46,8 +46,7 @@ class Plan(ctypes.Structure):
                 ("chunk", ctypes.c_int64), ("resident_cap", ctypes.c_int32),
                 ("headroom", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
                 ("fell_back", ctypes.c_int32), ("idx16", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_uint64), ("split_rows", ctypes.c_int32),
-                ("split_g", ctypes.c_int32), ("split_chunk", ctypes.c_int64)]
+                ("workspace_bytes", ctypes.c_uint64)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -57,8 +56,7 @@ class Overrides(ctypes.Structure):
     _fields_ = [("force_path", ctypes.c_int32), ("force_wg_per_row", ctypes.c_int32),
                 ("max_grid", ctypes.c_int32), ("force_vec", ctypes.c_int32),
                 ("force_chunk", ctypes.c_int64), ("spin_limit", ctypes.c_uint32),
-                ("min_chunk", ctypes.c_int32), ("split_rows", ctypes.c_int32),
-                ("split_g", ctypes.c_int32), ("split_chunk", ctypes.c_int64), ("max_occupancy", ctypes.c_int32),
+                ("min_chunk", ctypes.c_int32), ("max_occupancy", ctypes.c_int32),
                 ("force_idx32", ctypes.c_int32), ("force_block", ctypes.c_int32)]
 
     @classmethod

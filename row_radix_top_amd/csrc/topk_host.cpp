@@ -24,7 +24,6 @@ int fail(int code, const std::string& msg) {
 }
 
 constexpr int64_t kDefaultMinChunk = 8192;
-constexpr int64_t kSplitMinChunk = 8192;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -40,11 +39,10 @@ std::string describe(const topk_plan& p) {
   char buf[512];
   std::snprintf(buf, sizeof(buf),
                 "path=%d idx16=%d vec=%d block=%d grid=%d wg_per_row=%d chunk=%lld "
-                "resident_cap=%d headroom=%d lds=%d fell_back=%d workspace=%llu "
-                "split_rows=%d split_g=%d split_chunk=%lld",
+                "resident_cap=%d headroom=%d lds=%d fell_back=%d workspace=%llu",
                 p.path, p.idx16, p.vec, p.block, p.grid, p.wg_per_row, (long long)p.chunk,
                 p.resident_cap, p.headroom, p.lds_bytes, p.fell_back,
-                (unsigned long long)p.workspace_bytes, p.split_rows, p.split_g, (long long)p.split_chunk);
+                (unsigned long long)p.workspace_bytes);
   return buf;
 }
 
@@ -315,12 +313,13 @@ int topk_ragged_plan(const topk_device_props* props_in, int32_t num_rows, int64_
     return fail(TOPK_EINVAL, "force_path must be 0, 1 or 2");
 
   // Several workgroups per row only pay off when rows are long and too few
-  // to occupy the GPU one per workgroup.  The pages split rows above their
+  // to occupy the GPU one per workgroup.  The pages share rows above their
   // 32K radix threshold; here the one-workgroup path streams rows of up to
-  // 64K elements wave by wave faster than any split, so rows are split
-  // automatically only above that, and only into at least kMinSplit parts.
-  // row_stride stands in for the longest length, which lives on the device.
-  const bool long_rows = row_stride > TOPK_RAGGED_RADIX_THRESHOLD && row_stride > rrt::kSplitMinStride;
+  // 64K elements wave by wave faster than several workgroups do, so rows are
+  // shared automatically only above that, and only by at least kMinGroup
+  // workgroups.  row_stride stands in for the longest length, which lives
+  // on the device.
+  const bool long_rows = row_stride > TOPK_RAGGED_RADIX_THRESHOLD && row_stride > rrt::kMultiMinStride;
   if (want == TOPK_PATH_MULTI || (want == 0 && long_rows)) {
     int block = want_block != 0 ? want_block : auto_block_multi(props, num_rows, row_stride, K);
     OccSet os = occ_for(props, block);
@@ -374,7 +373,7 @@ int topk_ragged_plan(const topk_device_props* props_in, int32_t num_rows, int64_
         std::snprintf(buf, sizeof(buf), "wg_per_row=%lld exceeds %d", (long long)G, rrt::kMaxGroup);
         return fail(TOPK_EINVAL, buf);
       }
-      const bool usable = want == TOPK_PATH_MULTI ? G >= 1 : G >= rrt::kMinSplit;
+      const bool usable = want == TOPK_PATH_MULTI ? G >= 1 : G >= rrt::kMinGroup;
       if (usable) {
         const int64_t grid = (int64_t)num_rows * G;
         if (grid <= avail) {
@@ -404,10 +403,7 @@ int topk_ragged_plan(const topk_device_props* props_in, int32_t num_rows, int64_
   }
 
   const bool i16 = row_stride <= rrt::kIdx16Limit && !idx32_only;
-  const int32_t want_split = ov != nullptr ? ov->split_rows : 0;
-  int block = want_block != 0 ? want_block : (want_split > 0 ? rrt::kBlock : auto_block_single(props, num_rows, row_stride, K));
-  if (want_split > 0 && block != rrt::kBlock)
-    return fail(TOPK_EINVAL, "split rows run on 256-thread workgroups only");
+  int block = want_block != 0 ? want_block : auto_block_single(props, num_rows, row_stride, K);
   int occ = i16 ? occ_for(props, block).single16 : occ_for(props, block).single;
   if (occ < 1 && want_block == 0 && block != rrt::kBlock) {
     block = rrt::kBlock;  // no wider instance resident: the base one
@@ -415,37 +411,8 @@ int topk_ragged_plan(const topk_device_props* props_in, int32_t num_rows, int64_
   }
   if (occ < 1) return fail(TOPK_EDEVICE, "single-workgroup kernel cannot be resident");
   const int64_t cap = (int64_t)props->num_cus * occ;
-
-  // Split rows: the last split_rows rows are cut into split_g chunks that
-  // any workgroup takes as units of their own (no workgroup waits for
-  // another, so residency does not matter).  Only when asked for: it
-  // measured slower than whole rows on every workload.
-  int64_t split_rows = 0, split_g = 0, split_chunk = 0;
-  if (want_split > 0) split_rows = std::min<int64_t>(want_split, num_rows);
-  if (split_rows > 0) {
-    if (ov != nullptr && ov->split_g != 0) {
-      if (ov->split_g < 1 || ov->split_g > rrt::kMaxSplit) return fail(TOPK_EINVAL, "split_g must be in [1, 16]");
-      split_g = ov->split_g;
-    } else {
-      split_g = std::min<int64_t>(ceil_div(row_stride, kSplitMinChunk), rrt::kMaxSplit);
-      split_g = std::min<int64_t>(split_g, std::max<int64_t>(2, cap / std::max<int64_t>(1, split_rows)));
-    }
-    if (ov != nullptr && ov->split_chunk != 0) {
-      if (ov->split_chunk < 0 || ov->split_chunk % rrt::kTile != 0)
-        return fail(TOPK_EINVAL, "split_chunk must be a positive multiple of 2048");
-      split_chunk = ov->split_chunk;
-    } else {
-      split_chunk = (int64_t)rrt::round_up((uint64_t)ceil_div(row_stride, split_g), rrt::kTile);
-    }
-    if (split_chunk * split_g < row_stride) return fail(TOPK_EINVAL, "split_g * split_chunk must cover the row");
-  }
-  const int64_t units = (num_rows - split_rows) + split_rows * split_g;
-  if (units > UINT32_MAX / 2) return fail(TOPK_EINVAL, "too many work units");
-  int64_t grid = units < cap ? units : cap;
+  int64_t grid = num_rows < cap ? num_rows : cap;
   if (ov != nullptr && ov->max_grid > 0 && grid > ov->max_grid) grid = ov->max_grid;
-  plan->split_rows = (int32_t)split_rows;
-  plan->split_g = (int32_t)split_g;
-  plan->split_chunk = split_chunk;
   plan->path = TOPK_PATH_SINGLE;
   plan->block = block;
   plan->wg_per_row = 1;
@@ -455,12 +422,9 @@ int topk_ragged_plan(const topk_device_props* props_in, int32_t num_rows, int64_
   plan->headroom = 0;
   plan->idx16 = i16 ? 1 : 0;
   plan->lds_bytes = rrt::lds_bytes_of(i16, big, block);
-  // More units than workgroups: later units are handed out by a ticket
-  // counter in the workspace header.  Split rows add a block each.
-  plan->workspace_bytes = (units > grid || split_rows > 0) ? rrt::kWsHeader : 0;
-  if (split_rows > 0)
-    plan->workspace_bytes +=
-        (uint64_t)split_rows * rrt::split_block_bytes((int)split_g, rrt::cap_of(rrt::layout_of(i16, big)));
+  // More rows than workgroups: later rows are handed out by a ticket
+  // counter in the workspace header.
+  plan->workspace_bytes = num_rows > grid ? rrt::kWsHeader : 0;
   return TOPK_OK;
 }
 
@@ -561,20 +525,11 @@ int launch(const void* scores, int64_t row_stride, const int32_t* lengths, const
   kp.K = K;
   kp.wg_per_row = plan.wg_per_row;
   kp.spin_limit = (ov != nullptr && ov->spin_limit > 0) ? ov->spin_limit : rrt::kDefaultSpin;
-  kp.split_from = num_rows - plan.split_rows;
-  kp.split_g = plan.split_rows > 0 ? plan.split_g : 1;
-  kp.split_chunk = plan.split_rows > 0 ? plan.split_chunk : row_stride;
-  kp.split_bytes =
-      plan.split_rows > 0 ? rrt::split_block_bytes(plan.split_g, rrt::cap_of(rrt::layout_of(plan.idx16 != 0, big))) : 0;
-  kp.num_units = (uint32_t)(kp.split_from + (int64_t)plan.split_rows * kp.split_g);
 
   if (verbose()) std::fprintf(stderr, "[topk_ragged] rows=%d stride=%lld K=%d %s\n", num_rows,
                               (long long)row_stride, K, describe(plan).c_str());
   void* args[] = {&kp};
-  // Split rows run on the one-workgroup kernel's split instance (same
-  // occupancy: both are held to the same register and LDS budget).
-  const int kpath = (plan.path == TOPK_PATH_SINGLE && plan.split_rows > 0) ? 4 : plan.path;
-  const void* fn = rrt::kernel_ptr(kpath, plan.vec, plan.idx16 != 0, out_val != nullptr, bf16, big, plan.block);
+  const void* fn = rrt::kernel_ptr(plan.path, plan.vec, plan.idx16 != 0, out_val != nullptr, bf16, big, plan.block);
   if (fn == nullptr) return fail(TOPK_EINVAL, "no kernel instance for this plan (" + describe(plan) + ")");
   hipError_t e = hipLaunchKernel(fn, dim3(plan.grid), dim3(plan.block), args, 0, stream);
   if (e == hipSuccess) e = hipGetLastError();

@@ -1,5 +1,5 @@
 // Kernel instances of the 1024-thread layout (kLayW1024 | kLayBigK): fp32 scores, every
-// load width, without split rows.
+// load width.
 #include "topk_instances.hpp"
 
 namespace rrt {

@@ -1,5 +1,5 @@
 // Kernel instances of the 256-thread layout (kLayBigK): every load width, fp32
-// and bf16 scores, with and without split rows and values.
+// and bf16 scores, with and without values.
 #include "topk_instances.hpp"
 
 namespace rrt {

@@ -10,20 +10,10 @@ namespace rrt {
 
 template <int VEC, int LAY, typename T>
 static const void* pick_vec(int path, bool vals) {
-  constexpr bool kSplitOk = has_block(block_of(LAY), std::is_same<T, uint16_t>::value, true);
   if (path == 2) return reinterpret_cast<const void*>(&topk_multi_kernel<VEC, LAY, T>);
-  const bool sp = path == 4;
-  if (path != 1 && path != 4) return nullptr;
-  if constexpr (kSplitOk) {
-    if (sp && vals) return reinterpret_cast<const void*>(&topk_single_kernel<VEC, LAY, true, true, T>);
-  }
-  if (vals && !sp) return reinterpret_cast<const void*>(&topk_single_kernel<VEC, LAY, false, true, T>);
-  if (vals) return nullptr;  // no such instance
-  if constexpr (kSplitOk) {
-    if (sp) return reinterpret_cast<const void*>(&topk_single_kernel<VEC, LAY, true, false, T>);
-  }
-  if (sp) return nullptr;
-  return reinterpret_cast<const void*>(&topk_single_kernel<VEC, LAY, false, false, T>);
+  if (path != 1) return nullptr;
+  if (vals) return reinterpret_cast<const void*>(&topk_single_kernel<VEC, LAY, true, T>);
+  return reinterpret_cast<const void*>(&topk_single_kernel<VEC, LAY, false, T>);
 }
 
 // BF16: whether this file also compiles the bf16 instances of the layout.

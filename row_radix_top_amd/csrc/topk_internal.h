@@ -72,18 +72,17 @@ constexpr int resident_of(int lay) {
        : block_of(lay) == 512 ? (((lay & kLayBigK) && !(lay & kLayIdx16)) ? 1 : 2)
                               : ((lay & kLayBigK) ? 2 : ((lay & kLayIdx16) ? 4 : 3));
 }
-// Workgroup widths with instances: 256 for every load width and score type;
-// 512 for every load width of fp32 and bf16 scores, without split rows;
-// 1024 for fp32 scores only, without split rows.
-constexpr bool has_block(int block, bool bf16, bool split) {
-  return block == kBlock || (!split && (block == 512 || (block == 1024 && !bf16)));
+// Workgroup widths with instances: 256 and 512 for every load width of fp32
+// and bf16 scores; 1024 for fp32 scores only.
+constexpr bool has_block(int block, bool bf16) {
+  return block == kBlock || block == 512 || (block == 1024 && !bf16);
 }
 
-// Rows are split over several workgroups only when longer than this (the
-// one-workgroup path streams shorter rows wave by wave faster than any
-// split) and only with at least kMinSplit workgroups per row.
-constexpr int64_t kSplitMinStride = 65536;
-constexpr int64_t kMinSplit = 4;
+// The planner gives a row several workgroups only when rows are longer than
+// this (the one-workgroup path streams shorter rows wave by wave faster) and
+// only with at least kMinGroup workgroups per row.
+constexpr int64_t kMultiMinStride = 65536;
+constexpr int64_t kMinGroup = 4;
 
 // Workspace: a 256-byte header followed by one block per row of the
 // multi-workgroup path.  Header word 0: error bits; the word at byte
@@ -123,18 +122,6 @@ inline constexpr GroupLayout group_layout(int wg_per_row, int cap) {
   return L;
 }
 
-// Split rows (one-workgroup kernel): the last rows of a launch may each be
-// cut into split_g chunks of split_chunk elements that any workgroup takes
-// as separate work units.  A chunk publishes its candidates to the row's
-// block; the last chunk to arrive selects over all of them.  Block layout
-// (bytes): 0 arrival counter (u32), 64 per-chunk candidate counts (u32),
-// kSplitHead chunk lists, each cap fp32 bit patterns then cap indices.
-constexpr int kMaxSplit = 16;
-constexpr uint64_t kSplitHead = 256;
-inline constexpr uint64_t split_block_bytes(int split_g, int cap) {
-  return round_up(kSplitHead + 8ull * (uint64_t)cap * (uint64_t)split_g, 256);
-}
-
 struct KernelParams {
   const void* scores;          // fp32, or bf16 as uint16_t bits (the kernel instance says which)
   const int32_t* lengths;
@@ -149,18 +136,10 @@ struct KernelParams {
   int32_t K;
   int32_t wg_per_row;    // multi path: G
   uint32_t spin_limit;
-  // One-workgroup path: rows [split_from, num_rows) are split (see above);
-  // units = split_from + (num_rows - split_from) * split_g work units.
-  int32_t split_from;
-  int32_t split_g;
-  int64_t split_chunk;
-  uint64_t split_bytes;  // bytes per split row block, after the header
-  uint32_t num_units;
 };
 
 // Kernel lookup for the host side.  path: 1 single, 2 multi, 3 the
-// streaming-read reference (idx16, big_k and block ignored), 4 single with
-// split rows.  vals: the one-workgroup instance that also writes the chosen
+// streaming-read reference (idx16, big_k and block ignored).  vals: the one-workgroup instance that also writes the chosen
 // scores (the multi-workgroup kernel always can).  bf16: the instance that
 // reads bf16 scores (vec 8 or 1); big_k: the large layout (K up to
 // kMaxKBig); block: threads per workgroup.  nullptr if no such instance.

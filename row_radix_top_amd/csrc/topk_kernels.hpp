@@ -44,16 +44,12 @@
 //   in-kernel cleanup of the PR #41748 page, without the race its review
 //   describes: nothing is reset while another workgroup can still read it).
 //
-// * Split rows (opt-in).  Chunks of a row as separate work units that publish
-//   their candidates; the last to arrive selects over all of them, and no
-//   workgroup ever waits for another.
-//
 // Instances differ in the workgroup width (256, 512 or 1024 threads: 4, 8 or
 // 16 wavefronts share a row), the buffer layout (16-bit or 32-bit candidate
 // indices; room for K up to 2048 or 4096), the load width, the score type
-// (fp32, or bf16 widened exactly at the load), and whether the launch has
-// split rows or writes the chosen scores (compiled out otherwise, to keep the
-// row loop's registers).  This header holds the templates; the instance
+// (fp32, or bf16 widened exactly at the load), and whether the launch writes
+// the chosen scores (compiled out otherwise, to keep the row loop's
+// registers).  This header holds the templates; the instance
 // files compile groups of them in parallel.
 //
 // The key function maps fp32 bits to uint32 so that unsigned order equals
@@ -191,12 +187,6 @@ struct __align__(16) Smem {
   // Target of histogram adds that count nothing: one word per lane, so the
   // lanes of one add never collide on it (never read).
   uint32_t sink[64];
-  // Split-row merge (between streaming and selection, when tile_cnt is
-  // idle): each chunk's first slot in the buffer, and its list's offset in
-  // the row block less that slot.
-  __device__ uint32_t* part() { return &tile_cnt[0][0][0]; }
-  __device__ uint32_t* delta() { return &tile_cnt[0][0][0] + (kMaxSplit + 1); }
-  static_assert(2 * kMaxSplit + 1 <= 2 * kElems * Shape<LAY>::kWaves, "merge offsets fit the tile-count area");
 };
 
 // ---------------------------------------------------------------------------
@@ -1359,29 +1349,14 @@ __device__ __forceinline__ void ws_add(uint32_t* p, uint32_t v) {
 }
 
 // ---------------------------------------------------------------------------
-// Split rows: a chunk of a row as a unit of its own
+// A chunk of a row, wave by wave (the cooperative kernel's first pass)
 //
-// Every chunk of a row takes the same speculative bound: from the same 4096
-// elements (the first two wave tiles of each quarter of the row, the sample
-// a whole row streamed wave by wave uses) through the same integer
-// selection.  A chunk keeps every element of its range at or above the
-// bound, wave by wave; if a wavefront's part of the buffer overflows, the
-// chunk is streamed again on the general path from the same bound, whose
-// compactions keep a superset of the chunk's own K best.  Either way, every
-// element of the chunk that is among the row's K best is published once at
-// least K elements of the row reached the bound: such an element is at least
-// the K-th best key of the row, which is at least the bound, or it is among
-// its chunk's K best.  The last chunk to arrive checks that count and
-// selects over the union; failing it, it streams the whole row itself.
-// No workgroup ever waits for another, so nothing needs to be co-resident.
+// Every workgroup of a row takes the same speculative bound: from the same
+// sample (the first two wave tiles of each wave segment of the whole row,
+// the sample a row streamed wave by wave in one workgroup uses) through the
+// same integer selection.  A chunk keeps every element of its range at or
+// above the bound, wave by wave.
 // ---------------------------------------------------------------------------
-
-// Whether a split row of n elements is processed chunk by chunk (else its
-// chunk 0 takes it whole and the other chunks have nothing to do).
-template <int LAY>
-__device__ __forceinline__ bool splits(uint32_t n, uint32_t K, uint32_t chunk) {
-  return n > chunk && wave_mode<LAY>(n, K);
-}
 
 // Streams [c0, c1) of a row of n elements wave by wave, each wavefront its
 // own quarter of the range, from the row's speculative bound (returned in
@@ -1390,7 +1365,7 @@ __device__ __forceinline__ bool splits(uint32_t n, uint32_t K, uint32_t chunk) {
 // overflowed; otherwise mine / off are this wavefront's candidate count and
 // its offset among the chunk's total (in slots [w * SUB, w * SUB + mine)).
 template <int LAY, int VEC, typename T>
-__device__ __forceinline__ bool stream_piece_waves(Smem<LAY>& sm, const T* __restrict__ rowp, uint32_t n,
+__device__ __forceinline__ bool stream_range_waves(Smem<LAY>& sm, const T* __restrict__ rowp, uint32_t n,
                                                    uint32_t K, uint32_t c0, uint32_t c1, float (&x0)[kElems],
                                                    float (&x1)[kElems], bool preloaded, uint32_t& mine,
                                                    uint32_t& off, uint32_t& total, uint32_t& L) {
@@ -1454,113 +1429,6 @@ __device__ __forceinline__ bool stream_piece_waves(Smem<LAY>& sm, const T* __res
   return !bad;
 }
 
-// The block of split row `row` in the workspace (as 32-bit words).
-__device__ __forceinline__ uint32_t* split_block(const KernelParams& p, int row) {
-  return reinterpret_cast<uint32_t*>(p.ws + kWsHeader + (uint64_t)(row - p.split_from) * p.split_bytes);
-}
-
-// Writes this chunk's candidates to its list in the row block (fp32 bits,
-// row indices) and its count, then arrives.  Candidates sit wave by wave
-// (waved: this wavefront's mine at slots [w * SUB, ...), going to offset
-// off) or in slots [0, total) with indices relative to ibase.  Every store
-// is an agent-scope atomic and completes before the arrival, so the last
-// arriver, on any XCD, reads them after its own arrival without cache
-// maintenance.  Returns how many chunks arrived before this one.
-template <int LAY>
-__device__ __forceinline__ uint32_t publish_piece(Smem<LAY>& sm, uint32_t* blk, int c, bool waved, uint32_t mine,
-                                                  uint32_t off, uint32_t total, uint32_t ibase) {
-  constexpr uint32_t CAP = (uint32_t)Shape<LAY>::kCap;
-  constexpr uint32_t NT = (uint32_t)Shape<LAY>::kBlock;
-  constexpr uint32_t SUB = CAP / Shape<LAY>::kWaves;
-  uint32_t* bits = blk + kSplitHead / 4 + (uint32_t)c * 2u * CAP;
-  uint32_t* idxs = bits + CAP;
-  const uint32_t t = tid();
-  if (waved) {
-    const uint32_t lane = t & 63u, s0 = (t >> 6) * SUB;
-    for (uint32_t i = lane; i < mine; i += 64u) {
-      ws_store(bits + off + i, sm.val[s0 + i]);
-      ws_store(idxs + off + i, (uint32_t)sm.idx[s0 + i]);
-    }
-  } else {
-    for (uint32_t i = t; i < total; i += NT) {
-      ws_store(bits + i, sm.val[i]);
-      ws_store(idxs + i, (uint32_t)sm.idx[i] + ibase);
-    }
-  }
-  if (t == 0) ws_store(blk + 16 + c, total);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (t == 0) sm.acc[10] = __hip_atomic_fetch_add(blk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  return uni(sm.acc[10]);
-}
-
-// The last arriver of a split row with geff chunks: resets the arrival
-// counter and gathers every chunk's list, in chunk order (so in index
-// order), into the buffer's slots [0, total).  Returns total; the buffer is
-// filled only when K <= total <= the capacity.  All loads are issued before
-// any is used (addresses clamped into the block), so the gather costs about
-// one round trip.  Then the lists and counts it read are zeroed, so the
-// block is all-zero again when the launch ends.
-template <int LAY>
-__device__ __forceinline__ uint32_t merge_pieces(Smem<LAY>& sm, uint32_t* blk, uint32_t geff, uint32_t K) {
-  constexpr int S = Shape<LAY>::kSlots;
-  constexpr uint32_t CAP = (uint32_t)Shape<LAY>::kCap;
-  constexpr uint32_t NT = (uint32_t)Shape<LAY>::kBlock;
-  const uint32_t t = tid();
-  if (t < 64u) {
-    const uint32_t v = t < geff ? ws_load(blk + 16 + t) : 0u;
-    const uint32_t incl = wave_incl_scan(v);
-    if (t < geff) {
-      sm.part()[t + 1] = incl;
-      sm.delta()[t] = t * 2u * CAP - (incl - v);
-    }
-    if (t == 0) {
-      sm.part()[0] = 0u;
-      ws_store(blk, 0u);  // no other chunk of this row touches the counter again
-    }
-  }
-  __syncthreads();
-  const uint32_t total = uni(sm.part()[geff]);
-  uint32_t* lists = blk + kSplitHead / 4;
-  if (total >= K && total <= CAP) {
-    // Chunk boundaries as wave-uniform values (past geff: never reached).
-    uint32_t P[kMaxSplit];
-#pragma unroll
-    for (int g = 1; g < kMaxSplit; ++g) P[g] = (uint32_t)g < geff ? uni(sm.part()[g]) : 0xffffffffu;
-    uint32_t vb[S], vi[S];
-#pragma unroll
-    for (int j = 0; j < S; ++j) {
-      const uint32_t i = t + (uint32_t)j * NT;
-      uint32_t ch = 0;
-#pragma unroll
-      for (int g = 1; g < kMaxSplit; ++g) ch += i >= P[g] ? 1u : 0u;
-      const uint32_t a = i < total ? i + sm.delta()[ch] : 0u;
-      vb[j] = ws_load(lists + a);
-      vi[j] = ws_load(lists + a + CAP);
-    }
-#pragma unroll
-    for (int j = 0; j < S; ++j) {
-      const uint32_t i = t + (uint32_t)j * NT;
-      if (i < total) {
-        sm.val[i] = vb[j];
-        sm.idx[i] = (typename Shape<LAY>::Idx)vi[j];
-      }
-    }
-    __syncthreads();  // every gather load has completed before its word is cleared
-  }
-  for (uint32_t g = 0; g < geff; ++g) {
-    const uint32_t m = uni(sm.part()[g + 1]) - uni(sm.part()[g]);
-    uint32_t* bits = lists + g * 2u * CAP;
-    for (uint32_t i = t; i < m; i += NT) {
-      ws_store(bits + i, 0u);
-      ws_store(bits + CAP + i, 0u);
-    }
-  }
-  if (t < geff) ws_store(blk + 16 + t, 0u);
-  return total;
-}
-
 // Row r of the scores, as elements of type T.
 template <typename T>
 __device__ __forceinline__ const T* row_of(const KernelParams& p, int64_t r) {
@@ -1596,40 +1464,20 @@ __device__ __forceinline__ void zero_histograms(Smem<LAY>& sm) {
 }
 
 // ---------------------------------------------------------------------------
-// One workgroup per row, persistent over work units.
+// One workgroup per row, persistent over rows.
 //
-// A unit is a whole row, or one chunk of a split row (the last rows of the
-// launch, when the plan splits them).  Workgroup b takes unit b first.
-// With a workspace every later unit comes from a ticket counter, so
-// workgroups that run faster -- the hardware favours the oldest waves --
-// take more units, and the small chunk units come last, evening out the
-// end of the launch.  Each workgroup draws its next ticket when it starts a
-// unit, hiding the atomic's latency behind the unit, and stops at the first
-// ticket past the last unit.  There are exactly num_units draws per launch
-// (one per unit after the first gridDim.x, plus one failing draw per
-// workgroup), so the draw that returns num_units - 1 is the last touch of
-// the counter and resets it to zero.  Without a workspace unit b + k *
-// gridDim.x is taken in turn.
+// Workgroup b takes row b first.  With a workspace every later row comes
+// from a ticket counter, so workgroups that run faster -- the hardware
+// favours the oldest waves -- take more rows, evening out the end of the
+// launch.  Each workgroup draws its next ticket when it starts a row, hiding
+// the atomic's latency behind the row, and stops at the first ticket past
+// the last row.  Without a workspace row b + k * gridDim.x is taken in turn.
 // ---------------------------------------------------------------------------
 
-// Row and chunk of unit u (chunk -1: a whole row).
-__device__ __forceinline__ void unit_of(const KernelParams& p, uint32_t u, int& row, int& c) {
-  if (u < (uint32_t)p.split_from) {
-    row = (int)u;
-    c = -1;
-  } else {
-    const uint32_t v = u - (uint32_t)p.split_from;
-    row = p.split_from + (int)(v / (uint32_t)p.split_g);
-    c = (int)(v % (uint32_t)p.split_g);
-  }
-}
-
-// SPLIT: the launch has split rows.  Without, every unit is a whole row and
-// the split-row code is compiled out (it costs registers the row loop needs).
-// VALS: the launch also writes the chosen scores (compiled out otherwise, for
-// the same reason).
+// VALS: the launch also writes the chosen scores (compiled out otherwise: it
+// costs registers the row loop needs).
 // T: the score type (float, or uint16_t holding bf16).
-template <int VEC, int LAY, bool SPLIT, bool VALS, typename T>
+template <int VEC, int LAY, bool VALS, typename T>
 __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd) topk_single_kernel(KernelParams p) {
   constexpr int NT = Shape<LAY>::kBlock;
   constexpr int W = Shape<LAY>::kWaves;
@@ -1637,103 +1485,67 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
   zero_histograms(sm);
   __syncthreads();
   const uint32_t K = (uint32_t)p.K;
-  const uint32_t U = p.num_units;
-  const uint32_t CH = (uint32_t)p.split_chunk;
+  const uint32_t U = (uint32_t)p.num_rows;
   uint32_t* ticket = p.ws != nullptr ? reinterpret_cast<uint32_t*>(p.ws + kTicketOff) : nullptr;
   uint32_t redo = 0u;  // 1 while a row is streamed again after a failed speculation
-  uint32_t next = 0u;  // thread 0: the unit after this one
-  bool drawn = false;  // thread 0: next is set for the current unit
-  uint32_t unit = blockIdx.x;
-  bool first_unit = true;
-  // Every unit draws its successor when it starts, so the atomic's latency
-  // hides behind the unit.  The first unit's successor is fixed (unit +
-  // grid): at launch every workgroup would hit the counter at once, and at
-  // the end of the first units, which end close together, nearly as many.
-  // Tickets therefore start at two grids; U - grid draws are made in all
-  // (each workgroup with a second unit draws until it gets no unit), and the
-  // last one resets the counter.
+  uint32_t next = 0u;  // thread 0: the row after this one
+  bool drawn = false;  // thread 0: next is set for the current row
+  uint32_t row = blockIdx.x;
+  bool first_row = true;
+  // Every row draws its successor when it starts, so the atomic's latency
+  // hides behind the row.  The first row's successor is fixed (row + grid):
+  // at launch every workgroup would hit the counter at once, and at the end
+  // of the first rows, which end close together, nearly as many.  Tickets
+  // therefore start at two grids; U - grid draws are made in all (each
+  // workgroup with a second row draws until it gets no row), and the last
+  // one resets the counter.
   auto draw = [&]() {
     if (threadIdx.x == 0 && !drawn) {
-      if (ticket != nullptr && !first_unit) {
+      if (ticket != nullptr && !first_row) {
         const uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (t == U - gridDim.x - 1u) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         next = 2u * gridDim.x + t;
       } else {
-        next = unit + gridDim.x;
+        next = row + gridDim.x;
       }
       drawn = true;
     }
   };
-  // The next unit's first tiles (or its row's sample) are loaded before this
-  // unit's final selection, so that their latency hides behind it.
+  // The next row's first tiles (or its sample) are loaded before this row's
+  // final selection, so that their latency hides behind it.
   bool have_pre = false;
   float x0[kElems], x1[kElems];
-  int row = (int)unit, c = -1;
-  if constexpr (SPLIT) {
-    if (unit < U) unit_of(p, unit, row, c);
-  }
-  int64_t n = unit < U ? clamp_len(p, row) : 0;
-  uint32_t off = unit < U ? uni(offset_of(p, row)) : 0u;
-  while (unit < U) {
+  int64_t n = row < U ? clamp_len(p, (int)row) : 0;
+  uint32_t off = row < U ? uni(offset_of(p, (int)row)) : 0u;
+  while (row < U) {
     draw();
     int32_t* out = p.out + (int64_t)row * p.K;
     uint32_t cnt = 0;
     bool waved = false;  // the candidates sit wave by wave
     bool select = false;
-    const bool piece = SPLIT && c >= 0 && splits<LAY>((uint32_t)n, K, CH);
-    if (SPLIT && c > 0 && !piece) {
-      // Chunk of a row taken whole by its chunk 0: nothing to do.
-    } else if (n <= (int64_t)K) {
+    if (n <= (int64_t)K) {
       if constexpr (VALS)
         write_all_then_pad<NT, T>(out, n, p.K, off, p.out_val + (int64_t)row * p.K, row_of<T>(p, row));
       else
         write_all_then_pad<NT>(out, n, p.K, off);
     } else {
       const T* rowp = row_of<T>(p, row);
-      uint32_t g0 = 0, g1 = (uint32_t)n, gL = 0;  // general path: range, starting bound
-      bool general = true;
-      uint32_t mine = 0, off = 0;
-      if (SPLIT && (piece || (!redo && wave_mode<LAY>((uint32_t)n, K)))) {
-        // One wave-by-wave streamer for chunks and whole rows alike (a second
-        // inlined copy would cost the loop registers).
-        if (piece) {
-          g0 = (uint32_t)c * CH;
-          g1 = g0 + CH < (uint32_t)n ? g0 + CH : (uint32_t)n;
-        }
-        if (g0 < g1) {
-          waved = stream_piece_waves<LAY, VEC>(sm, rowp, (uint32_t)n, K, g0, g1, x0, x1, have_pre, mine, off, cnt,
-                                               gL);
-          general = !waved;
-        } else {
-          general = false;  // past the row's end: nothing to publish or wait for
-        }
-        have_pre = false;
-        if (!piece) {
-          if (!waved || cnt < K) {
-            // As below: stream the row again on the general path.
-            redo = 1u;
-            continue;
-          }
-          cnt = mine;
-        }
-      } else if (!redo && wave_mode<LAY>((uint32_t)n, K)) {
+      uint32_t gL = 0;  // general path: starting bound
+      if (!redo && wave_mode<LAY>((uint32_t)n, K)) {
         waved = stream_row_waves<LAY, VEC>(sm, rowp, (uint32_t)n, K, x0, x1, have_pre, cnt);
         have_pre = false;
         if (!waved) {
-          // A quarter of the buffer overflowed, or fewer than K elements
-          // reached the speculative bound: stream the row again on the
-          // general path, without speculating.
+          // A wavefront's part of the buffer overflowed, or fewer than K
+          // elements reached the speculative bound: stream the row again on
+          // the general path, without speculating.
           redo = 1u;
           continue;
         }
-        general = false;
-      }
-      if (general) {
-        cnt = 0u;  // a failed wave-by-wave attempt leaves its count behind
-        const uint32_t spec = (piece || redo || n < (int64_t)kSpecMinLen) ? 0u : (uint32_t)n;
-        stream_chunk<LAY, VEC>(sm, rowp, g0, g1, K, cnt, gL, spec, x0, x1, have_pre);
+      } else {
+        const uint32_t spec = (redo || n < (int64_t)kSpecMinLen) ? 0u : (uint32_t)n;
+        stream_chunk<LAY, VEC>(sm, rowp, 0u, (uint32_t)n, K, cnt, gL, spec, x0, x1, have_pre);
         have_pre = false;
-        if (!piece && cnt < K && !redo) {
+        if (cnt < K && !redo) {
           // Fewer than K elements reached the speculative bound: it was above
           // the K-th best.  Stream the same row again without speculating.
           redo = 1u;
@@ -1741,64 +1553,26 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
           continue;
         }
       }
-      if (SPLIT && piece) {
-        const uint32_t geff = ((uint32_t)n + CH - 1u) / CH;
-        if (g0 < g1) {
-          uint32_t* blk = split_block(p, row);
-          const uint32_t before = publish_piece<LAY>(sm, blk, c, waved, mine, off, cnt, g0);
-          if (before == geff - 1u) {
-            cnt = merge_pieces<LAY>(sm, blk, geff, K);
-            if (cnt < K || cnt > (uint32_t)Shape<LAY>::kCap) {
-              // Too few elements reached the bound, or too many to gather:
-              // this workgroup streams the whole row on the general path.
-              c = -1;
-              redo = 1u;
-              continue;
-            }
-            waved = false;
-            select = true;
-          }
-        }
-      } else {
-        select = true;
-      }
+      select = true;
       redo = 0u;
     }
     draw();
     if (threadIdx.x == 0) {
-      uint32_t nrow = next, nc = 0u, nn = 0u;
+      uint32_t nn = 0u;
       if (next < U) {
-        if constexpr (SPLIT) {
-          int r, cc;
-          unit_of(p, next, r, cc);
-          nrow = (uint32_t)r;
-          nc = (uint32_t)(cc + 1);
-        }
-        nn = (uint32_t)clamp_len(p, (int)nrow);
-        sm.acc[13] = offset_of(p, (int)nrow);
+        nn = (uint32_t)clamp_len(p, (int)next);
+        sm.acc[13] = offset_of(p, (int)next);
       }
       sm.acc[8] = next < U ? next : U;
       sm.acc[9] = nn;
-      if constexpr (SPLIT) {
-        sm.acc[11] = nrow;
-        sm.acc[12] = nc;
-      }
     }
     __syncthreads();
-    const uint32_t nunit = uni(sm.acc[8]);
+    const uint32_t nrow = uni(sm.acc[8]);
     const int64_t nn = (int64_t)uni(sm.acc[9]);
     const uint32_t noff = uni(sm.acc[13]);
-    int nrow = (int)nunit, nc = -1;
-    if constexpr (SPLIT) {
-      nrow = (int)uni(sm.acc[11]);
-      nc = (int)uni(sm.acc[12]) - 1;
-    }
-    // Prefetch for the next unit unless it is a chunk with nothing to do.
-    const bool npiece = SPLIT && nc >= 0 && splits<LAY>((uint32_t)nn, K, CH);
-    if (nunit < U && nn >= (int64_t)kSpecMinLen && nn > (int64_t)K && (nc <= 0 || npiece)) {
-      // The next unit's first two tiles: per wavefront quarter (the row's
-      // sample) when it will go wave by wave or is a chunk, else the row's
-      // first two tiles.
+    if (nrow < U && nn >= (int64_t)kSpecMinLen && nn > (int64_t)K) {
+      // The next row's first two tiles: per wave segment (the row's sample)
+      // when it will go wave by wave, else the row's first two tiles.
       const T* nrowp = row_of<T>(p, nrow);
       if (wave_mode<LAY>((uint32_t)nn, K)) {
         const T* qp = nrowp + uni(threadIdx.x >> 6) * segment_of<W>((uint32_t)nn);
@@ -1814,14 +1588,12 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
       final_select<LAY>(sm, waved ? wave_slice<LAY>(cnt) : plain_slice<LAY>(cnt), K, out, off,
                         VALS ? p.out_val + (int64_t)row * p.K : nullptr);
     }
-    first_unit = false;
+    first_row = false;
     drawn = false;
-    unit = nunit;
     row = nrow;
-    c = nc;
     n = nn;
     off = noff;
-    __syncthreads();  // every thread has read the next unit before it is overwritten
+    __syncthreads();  // every thread has read the next row before it is overwritten
   }
 }
 
@@ -2080,7 +1852,7 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
     constexpr uint32_t SUB = (uint32_t)CAP / Shape<LAY>::kWaves;
     uint32_t mine = 0, woff = 0, total = 0, Lr = 0;
     float x0[kElems], x1[kElems];
-    const bool ok = stream_piece_waves<LAY, VEC>(sm, rowp, (uint32_t)n, K, (uint32_t)c0, (uint32_t)c1, x0, x1, false,
+    const bool ok = stream_range_waves<LAY, VEC>(sm, rowp, (uint32_t)n, K, (uint32_t)c0, (uint32_t)c1, x0, x1, false,
                                                 mine, woff, total, Lr);
     const bool pub = ok && Lr != 0u && total <= PUB;
     if (pub) {

@@ -157,7 +157,7 @@ const void* read_ref_kernel_ptr(int vec) {
 
 const void* kernel_ptr(int path, int vec, bool idx16, bool vals, bool bf16, bool big_k, int block) {
   if (path == 3) return read_ref_kernel_ptr(vec);
-  if (!has_block(block, bf16, path == 4)) return nullptr;
+  if (!has_block(block, bf16)) return nullptr;
   const int lay = layout_of(idx16, big_k, block);
   switch (block) {
     case 1024:

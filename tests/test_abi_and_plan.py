@@ -57,7 +57,7 @@ def test_plan_single_path_for_short_rows():
         assert p["path"] == rrt.PATH_SINGLE, (stride, p)
     p = rrt.plan_for_props(256, 3, 3, 2, 65537, 1024)
     assert p["path"] == rrt.PATH_MULTI and p["wg_per_row"] >= 4
-    # A split into fewer than four parts is not worth it: one workgroup per row.
+    # Fewer than four workgroups per row are not worth it: one workgroup per row.
     p = rrt.plan_for_props(256, 3, 3, 200, 131072, 1024)
     assert p["path"] == rrt.PATH_SINGLE and p["fell_back"] == 0
     # Unless the caller asks for it.
@@ -111,7 +111,7 @@ def test_plan_headroom_only_when_there_is_room():
     # and a group of 2 cannot be resident -> single path.
     p = rrt.plan_for_props(1, 1, 1, 1, 131072, 2048)
     assert p["path"] == rrt.PATH_SINGLE
-    # Four slots less one of headroom leave a group of 3: below the minimum split.
+    # Four slots less one of headroom leave a group of 3: below the minimum group.
     p = rrt.plan_for_props(4, 1, 1, 1, 131072, 2048)
     assert p["path"] == rrt.PATH_SINGLE
     p = rrt.plan_for_props(8, 1, 1, 1, 131072, 2048)
@@ -186,29 +186,19 @@ def test_plan_forced_group_sizes_are_kept():
     assert p["path"] == rrt.PATH_SINGLE and p["fell_back"] == 1
 
 
-def test_plan_split_rows():
-    # Forced split of the last rows: units, grid and workspace follow.
-    p = rrt.plan_for_props(256, 4, 4, 64, 32768, 2048, split_rows=64, split_g=4)
-    assert p["path"] == rrt.PATH_SINGLE and p["split_rows"] == 64 and p["split_g"] == 4
-    assert p["split_chunk"] == 8192 and p["grid"] == 256
-    block = (256 + 8 * 5120 * 4 + 255) // 256 * 256
-    assert p["workspace_bytes"] == 256 + 64 * block
-    p = rrt.plan_for_props(256, 4, 4, 4096, 65536, 2048, split_rows=512, split_g=4)
-    assert p["split_rows"] == 512 and p["split_chunk"] == 16384 and p["grid"] == 1024
-    assert p["workspace_bytes"] == 256 + 512 * ((256 + 8 * 5120 * 4 + 255) // 256 * 256)
-    # More split rows than rows: all of them.
-    p = rrt.plan_for_props(256, 4, 4, 10, 65536, 2048, split_rows=99, split_g=2)
-    assert p["split_rows"] == 10 and p["grid"] == 20 and p["split_chunk"] == 32768
-    # Chunk given: a multiple of 2048 that covers the row with split_g chunks.
-    p = rrt.plan_for_props(256, 4, 4, 8, 65536, 2048, split_rows=8, split_g=4, split_chunk=16384)
-    assert p["split_chunk"] == 16384
-    for bad in (dict(split_g=17), dict(split_g=-1), dict(split_g=4, split_chunk=1000),
-                dict(split_g=2, split_chunk=8192)):
-        with pytest.raises(rrt.TopKError):
-            rrt.plan_for_props(256, 4, 4, 8, 65536, 2048, split_rows=8, **bad)
-    # -1: never split.
-    p = rrt.plan_for_props(256, 4, 4, 64, 32768, 2048, split_rows=-1)
-    assert p["split_rows"] == 0 and p["workspace_bytes"] == 0
+def test_plan_ticket_workspace():
+    # One workgroup per row: no workspace while every row has its own
+    # workgroup, a 256-byte header (the row ticket) once rows outnumber the grid.
+    p = rrt.plan_for_props(256, 4, 4, 1024, 32768, 2048)
+    assert p["path"] == rrt.PATH_SINGLE and p["grid"] == 1024 and p["workspace_bytes"] == 0
+    p = rrt.plan_for_props(256, 4, 4, 1025, 32768, 2048)
+    assert p["grid"] == 1024 and p["workspace_bytes"] == 256
+    p = rrt.plan_for_props(256, 4, 4, 64, 32768, 2048, max_grid=7)
+    assert p["grid"] == 7 and p["workspace_bytes"] == 256
+    # The row-splitting overrides of earlier versions are gone.
+    for bad in ("split_rows", "split_g", "split_chunk"):
+        with pytest.raises(TypeError):
+            rrt.plan_for_props(256, 4, 4, 8, 65536, 2048, **{bad: 4})
 
 
 def test_plan_occupancy_cap():
@@ -249,9 +239,10 @@ def test_plan_large_k_layout():
     p = rrt.plan_for_props(256, 2, 2, 64, 32768, 3000, force_idx32=1)
     assert p["idx16"] == 0 and p["kmax"] == 4096
     assert rrt.plan_for_props(256, 2, 2, 64, 32768, 3000)["idx16"] == 1
-    # Split-row blocks and cooperative lists size with the layout's capacity.
-    p = rrt.plan_for_props(256, 2, 2, 8, 65536, 4096, split_rows=8, split_g=4)
-    assert p["workspace_bytes"] == 256 + 8 * ((256 + 8 * 7168 * 4 + 255) // 256 * 256)
+    # Cooperative lists size with the layout's capacity.
+    ws = [rrt.plan_for_props(256, 2, 2, 8, 131072, k, force_path=2, force_wg_per_row=4)["workspace_bytes"]
+          for k in (2048, 4096)]
+    assert ws[1] - ws[0] == 8 * 4 * 4 * (7168 - 5120)
 
 
 # ---------------------------------------------------------------------------
@@ -295,8 +286,3 @@ def test_plan_block_width_forced():
     # A forced width the device cannot keep resident is an error, not a silent change.
     with pytest.raises(rrt.TopKError):
         rrt.plan_for_props(256, 3, 3, 64, 32768, 2048, force_block=1024)
-    # Split rows run on 256 threads only.
-    with pytest.raises(rrt.TopKError):
-        rrt.plan_for_props(256, 3, 3, 64, 32768, 2048, force_block=512, split_rows=4, **WIDE)
-    p = rrt.plan_for_props(256, 3, 3, 64, 32768, 2048, split_rows=4, **WIDE)
-    assert p["block"] == 256 and p["split_rows"] == 4

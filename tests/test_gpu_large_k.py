@@ -28,7 +28,7 @@ def test_large_k_workloads(name, K):
     if name != "prefill":
         paths += [dict(force_path=2), dict(force_path=1, max_grid=5), dict(force_idx32=1)]
     if name in ("mtp", "long_k2048"):
-        paths.append(dict(force_path=1, split_rows=w.num_rows, split_g=4))
+        paths.append(dict(force_path=2, force_block=512))
     for ov in paths:
         got, plan = run_gpu(w.scores, w.lengths, K, tag=f"{name} K={K} {ov}", **ov)
         assert plan["kmax"] == 4096

@@ -88,7 +88,7 @@ def test_long_rows_one_workgroup_per_row(name):
 
 
 @pytest.mark.parametrize("G", [0, 2, 4])
-def test_mtp_rows_split_across_workgroups(G):
+def test_mtp_rows_shared_by_workgroups(G):
     # The multi-token rows with the cooperative path forced on.
     w = workloads.make_workload("mtp")
     exp = topk_ragged_oracle(w.scores, w.lengths, w.K)
@@ -355,7 +355,7 @@ def test_row_offsets_flat_layout(name):
     exp = topk_ragged_offsets_oracle(w.scores, w.lengths, w.K, starts)
     paths = [{}, dict(force_path=1)]
     if name != "prefill":
-        paths += [dict(force_path=2), dict(force_path=1, split_rows=w.num_rows, split_g=4)]
+        paths += [dict(force_path=2), dict(force_path=1, force_block=512)]
     for ov in paths:
         got, _ = run_gpu(w.scores, w.lengths, w.K, tag=f"{name} offsets {ov}", row_offsets=starts, **ov)
         assert_same(got, exp, f"{name} offsets {ov}")

@@ -1,5 +1,5 @@
 """Seeded random sweep: shapes, strides (both index widths), K, value
-distributions, lengths, paths, group sizes, split rows, grid caps, load
+distributions, lengths, paths, group sizes, workgroup widths, grid caps, load
 widths, row offsets, values and bf16 scores, each case compared element by
 element with the oracle.  Every case prints its parameters first, so a
 failure names its case."""
@@ -55,9 +55,8 @@ def _case(seed: int):
         if rng.random() < 0.5:
             ov["force_wg_per_row"] = int(rng.integers(1, 17))
     elif path == 3 and stride >= 4096:
-        ov["force_path"] = 1
-        g = int(rng.integers(2, 9))
-        ov.update(split_rows=int(rng.integers(1, rows + 1)), split_g=g)
+        ov["force_path"] = int(rng.integers(1, 3))
+        ov["force_block"] = 512
     offset = int(rng.choice([0, 0, 1, 2]))
     return dict(stride=stride, rows=rows, K=K, dist=dist, s=s, L=L, ov=ov, offset=offset,
                 offsets=rng.random() < 0.3, values=rng.random() < 0.3, bf16=rng.random() < 0.2)

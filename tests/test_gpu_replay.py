@@ -38,17 +38,17 @@ def _length_patterns(rng, npat, rows, stride):
     return pats
 
 
-@pytest.mark.parametrize("path,G,grid,split", [(2, 0, 0, 0), (2, 7, 0, 0), (1, 0, 0, 0), (1, 0, 5, 0),
-                                                (1, 0, 0, 12), (1, 0, 5, 6)])
-def test_graph_replay_changing_lengths(path, G, grid, split):
+@pytest.mark.parametrize("path,G,grid,block", [(2, 0, 0, 0), (2, 7, 0, 0), (1, 0, 0, 0), (1, 0, 5, 0),
+                                                (2, 0, 0, 512), (1, 0, 5, 512)])
+def test_graph_replay_changing_lengths(path, G, grid, block):
     # grid=5 < 12 rows: the one-workgroup path hands rows out by a ticket
     # counter in the workspace, which must be back at zero after each replay.
-    # split > 0: the last rows are split into chunks, whose arrival counters,
-    # counts and candidate lists must be back at zero too.
+    # The cooperative path's counters, slots and published lists too, at both
+    # widths.
     import torch
     dev = torch.device("cuda:0")
     rows, stride, K = 12, 65536, 2048
-    rng = np.random.default_rng(50 + path + G + split)
+    rng = np.random.default_rng(50 + path + G + block)
     s_np, _ = workloads.random_rows(51, rows, stride, [stride] * rows, dist="levels", levels=4000)
     pats = _length_patterns(rng, 8, rows, stride)
     exps = [torch.from_numpy(topk_ragged_oracle(s_np, p, K)).to(dev) for p in pats]
@@ -60,8 +60,8 @@ def test_graph_replay_changing_lengths(path, G, grid, split):
     ov = dict(force_path=path, force_wg_per_row=G) if G else dict(force_path=path)
     if grid:
         ov["max_grid"] = grid
-    if split:
-        ov.update(split_rows=split, split_g=4)
+    if block:
+        ov["force_block"] = block
     plan = rrt.query_plan(scores, K, **ov)
     note(f"replay plan={plan}")
     assert plan["path"] == path

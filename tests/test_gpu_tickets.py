@@ -1,8 +1,8 @@
 """The one-workgroup path's row tickets, at the boundaries of their scheme.
 
-With G workgroups and U > G units, workgroup b takes unit b, then unit b + G,
-then units 2G, 2G + 1, ... from a counter in the workspace header, drawn when
-each unit starts; the draw that hands out the last ticket resets the counter.
+With G workgroups and U > G rows, workgroup b takes row b, then row b + G,
+then rows 2G, 2G + 1, ... from a counter in the workspace header, drawn when
+each row starts; the draw that hands out the last ticket resets the counter.
 Row counts around G, 2G and 3G, and grids from 1 to 9 workgroups, must give
 the oracle's output on every launch of a workspace reused without
 re-initialisation, and leave it all-zero each time (a counter left behind
@@ -61,9 +61,10 @@ def test_ticket_boundaries(G, U):
         assert int(ws.count_nonzero().item()) == 0, f"G={G} U={U}: workspace not all-zero after launch {launch}"
 
 
-@pytest.mark.parametrize("G,U,split", [(2, 5, 2), (3, 7, 3), (4, 9, 9)])
-def test_ticket_boundaries_split_units(G, U, split):
-    # Split rows make more units than rows: the same scheme counts units.
+@pytest.mark.parametrize("G,U,block", [(2, 5, 512), (3, 7, 1024), (4, 9, 512)])
+def test_ticket_boundaries_wide(G, U, block):
+    # The same scheme on 512- and 1024-thread workgroups, with rows longer
+    # than 16-bit indices hold.
     import torch
     dev = torch.device("cuda:0")
     stride, K = 70000, 1024
@@ -72,13 +73,13 @@ def test_ticket_boundaries_split_units(G, U, split):
     exp = topk_ragged_oracle(s_np, L_np, K)
     scores = torch.from_numpy(s_np).to(dev)
     L = torch.from_numpy(L_np).to(dev)
-    ov = dict(force_path=1, max_grid=G, split_rows=split, split_g=4)
+    ov = dict(force_path=1, max_grid=G, force_block=block)
     plan = rrt.query_plan(scores, K, **ov)
-    note(f"tickets split G={G} U={U} split={split} plan={plan}")
-    assert plan["split_rows"] == split and plan["grid"] == G
+    note(f"tickets wide G={G} U={U} block={block} plan={plan}")
+    assert plan["block"] == block and plan["grid"] == G
     ws = rrt.new_workspace(rrt.workspace_size(U, stride, K, scores=scores, **ov), dev)
     for launch in range(3):
         out = rrt.topk_ragged(scores, L, K, workspace=ws, **ov)
         torch.cuda.synchronize()
-        assert_same(out.cpu().numpy(), exp, f"split G={G} U={U} launch {launch}")
-        assert int(ws.count_nonzero().item()) == 0, f"split G={G} U={U}: workspace not all-zero"
+        assert_same(out.cpu().numpy(), exp, f"wide G={G} U={U} block={block} launch {launch}")
+        assert int(ws.count_nonzero().item()) == 0, f"wide G={G} U={U} block={block}: workspace not all-zero"
