@@ -176,8 +176,11 @@ struct Shape {
 
 template <int LAY>
 struct __align__(16) Smem {
-  uint32_t val[Shape<LAY>::kCap];                 // candidate fp32 bits, index order
-  typename Shape<LAY>::Idx idx[Shape<LAY>::kCap];  // their indices, relative to the chunk start
+  // Wide workgroups append without a branch per element: a lane with nothing
+  // to keep writes to its own word past the capacity (never read).
+  static constexpr int kDiscard = Shape<LAY>::kWaves > 4 ? 64 : 0;
+  uint32_t val[Shape<LAY>::kCap + kDiscard];                 // candidate fp32 bits, index order
+  typename Shape<LAY>::Idx idx[Shape<LAY>::kCap + kDiscard];  // their indices, relative to the chunk start
   uint32_t hist1[kBins];                          // digit histogram; all-zero outside a selection
   uint32_t hs[kSmallBins];                        // second digit histogram; all-zero outside a selection
   uint32_t red[2 * Shape<LAY>::kWaves];           // per-wave partial results
@@ -540,8 +543,9 @@ __device__ __forceinline__ void interval_range(Smem<LAY>& sm, const uint32_t (&k
 // the same histogram word.
 constexpr uint32_t kTieCheck = 128;
 
-// Narrows [lo, hi] (which holds every entry) to the bin holding the keep-th
-// largest entry.  Stops when that bin is taken whole (its entries are
+// Narrows [lo, hi] (which holds every entry at or above the keep-th largest;
+// entries below lo are not counted) to the bin holding the keep-th largest
+// entry.  Stops when that bin is taken whole (its entries are
 // exactly the ones still needed, or entries above plus the bin number at
 // most stop_total) or holds a single key; the result's take is then the
 // whole bin or the entries still needed.  stop_total = 0 asks for an exact
@@ -999,6 +1003,73 @@ __device__ __forceinline__ void process_tile(Smem<LAY>& sm, const float (&x)[kEl
   st.cnt += total;
 }
 
+// Per lane, the largest and the KK-th largest of its 2 * kElems sample keys:
+// an insertion network over a descending list of the KK largest so far.
+template <int KK>
+__device__ __forceinline__ void lane_top(const uint32_t (&k)[2 * kElems], uint32_t& kth, uint32_t& top) {
+  uint32_t t[KK];
+#pragma unroll
+  for (int i = 0; i < KK; ++i) t[i] = 0u;
+#pragma unroll
+  for (int j = 0; j < 2 * kElems; ++j) {
+#pragma unroll
+    for (int i = KK - 1; i > 0; --i) t[i] = max(t[i], min(t[i - 1], k[j]));
+    t[0] = max(t[0], k[j]);
+  }
+  kth = t[KK - 1];
+  top = t[0];
+}
+
+// The interval the speculative bound's selection starts from (both ends
+// uniform).  hi is the largest sample key.  lo is a key that at least r
+// sample keys reach, found without a selection: with kk = ceil(r / threads)
+// at most 4, the smallest over lanes of each lane's kk-th largest key (every
+// lane holds kk keys at or above it, so the workgroup holds at least r);
+// otherwise the smallest sample key.  The r-th best key is therefore at
+// least lo.  Keys below lo go to the sink, so the first pass spends its bins
+// on the upper part of the sample, where the r-th best lies, and the dense
+// middle of the sample does not crowd a few bins.  Contains one barrier.
+template <int LAY>
+__device__ __forceinline__ void sample_range(Smem<LAY>& sm, const uint32_t (&k)[2 * kElems], uint32_t r,
+                                             uint32_t& lo, uint32_t& hi) {
+  constexpr int W = Shape<LAY>::kWaves;
+  const uint32_t kk = (r + (uint32_t)Shape<LAY>::kBlock - 1u) / (uint32_t)Shape<LAY>::kBlock;
+  uint32_t a, b;
+  if (kk == 1u) {
+    lane_top<1>(k, a, b);
+  } else if (kk == 2u) {
+    lane_top<2>(k, a, b);
+  } else if (kk <= 4u) {
+    lane_top<4>(k, a, b);  // kk = 3 takes the 4th largest: a lower key that qualifies too
+  } else {
+    a = 0xffffffffu;
+    b = 0u;
+#pragma unroll
+    for (int j = 0; j < 2 * kElems; ++j) {
+      a = min(a, k[j]);
+      b = max(b, k[j]);
+    }
+  }
+  const uint32_t mn = wave_min(a);
+  const uint32_t mx = wave_max(b);
+  const int w = tid() >> 6;
+  if ((tid() & 63) == 0) {
+    sm.red[w] = mn;
+    sm.red[W + w] = mx;
+  }
+  __syncthreads();
+  uint32_t l = 0xffffffffu, h = 0u;
+#pragma unroll
+  for (int q = 0; q < W / 4; ++q) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(&sm.red[4 * q]);
+    const u32x4 y = *reinterpret_cast<const u32x4*>(&sm.red[W + 4 * q]);
+    l = min(l, min(min(x.x, x.y), min(x.z, x.w)));
+    h = max(h, max(max(y.x, y.y), max(y.z, y.w)));
+  }
+  lo = uni(l);
+  hi = uni(h);
+}
+
 // The speculative bound for a row of n elements whose first two tiles are
 // in x0 and x1 (n >= kSpecMinLen): the key of (about) the r-th best of those
 // M = 2 * kTile elements (4096, 8192 or 16384 by workgroup width),
@@ -1031,7 +1102,7 @@ __device__ __forceinline__ uint32_t spec_bound(Smem<LAY>& sm, float (&x0)[kElems
   sl.sp = 2u * kElems;
   sl.nv = 2u * kElems;
   uint32_t lo, hi;
-  key_range<LAY, 2 * kElems>(sm, k, sl, lo, hi);
+  sample_range<LAY>(sm, k, r, lo, hi);
   const Sel s = range_select<LAY, 2 * kElems>(sm, k, sl, lo, hi, r, r + r / 8u + 8u);
 #pragma unroll
   for (int e = 0; e < kElems; ++e) {
@@ -1219,7 +1290,11 @@ __device__ __forceinline__ void wave_tile(Smem<LAY>& sm, const float (&x)[kElems
       const int e = u * VEC + c;
       const uint32_t pos = pbase + (uint32_t)u * (64u * VEC) + c;
       const bool take = (FULL || pos < end) && x[e] >= bf;
-      if (take) {
+      if constexpr (Smem<LAY>::kDiscard != 0) {
+        const uint32_t dst = take ? r : (uint32_t)Shape<LAY>::kCap + (threadIdx.x & 63);
+        sm.val[dst] = __float_as_uint(x[e]);
+        sm.idx[dst] = (typename Shape<LAY>::Idx)pos;
+      } else if (take) {
         sm.val[r] = __float_as_uint(x[e]);
         sm.idx[r] = (typename Shape<LAY>::Idx)pos;
       }
