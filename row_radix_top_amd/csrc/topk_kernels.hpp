@@ -540,8 +540,11 @@ __device__ __forceinline__ void interval_range(Smem<LAY>& sm, const uint32_t (&k
 // A threshold bin holding more entries than this after a pass is checked
 // for being one key (ties), and otherwise narrowed to its exact range: with
 // many equal keys every further pass would send most lanes of a wavefront to
-// the same histogram word.
+// the same histogram word.  A selection with a stop total (a bound that may
+// take its bin whole) checks from kTieCheckSoft: a tied bin there would
+// otherwise take a pass per 8 bits of key until the bins are single keys.
 constexpr uint32_t kTieCheck = 128;
+constexpr uint32_t kTieCheckSoft = 8;
 
 // Narrows [lo, hi] (which holds every entry at or above the keep-th largest;
 // entries below lo are not counted) to the bin holding the keep-th largest
@@ -605,7 +608,7 @@ __device__ Sel range_select(Smem<LAY>& sm, const uint32_t (&k)[S], const Slice& 
     hi = hi - lo > width ? lo + width : hi;
     whole = f.in_bin == krem || r.above + f.in_bin <= stop_total;
     if (whole || sh == 0u || !f.ok) break;
-    if (f.in_bin > kTieCheck) {
+    if (f.in_bin > (stop_total != 0u ? kTieCheckSoft : kTieCheck)) {
       uint32_t mn, mx;
       interval_range<LAY, S>(sm, k, sl, lo, hi, mn, mx);
       if (mn <= mx) {
