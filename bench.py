@@ -303,15 +303,36 @@ def decode_latency(launches: int = 400):
     def py(i):
         rrt.topk_ragged(pool[i % ncopy], L, w.K, out=out)
 
+    # The C-ABI call's host cost, taken apart with calls of the same library:
+    # a call that returns a constant (the ctypes floor), and the plan alone
+    # (device lookup, occupancy cache, planning; no launch).  What remains of
+    # a launching call is hipLaunchKernel.
+    plan = binding.Plan()
+    plan_p = ctypes.byref(plan)
+    qp = lib.topk_ragged_query_plan
+    ver = lib.topk_ragged_version
+
+    def plan_only(i):
+        rc = qp(ptrs[i % ncopy], w.num_rows, w.row_stride, w.K, None, sp, plan_p)
+        if rc != 0:
+            raise rrt.TopKError(rc, "topk_ragged_query_plan", lib.topk_ragged_last_error().decode())
+
     for i in range(20):
         abi(i)
     torch.cuda.synchronize()
+    ctypes_us = host_call_us(lambda i: ver(), launches)
+    plan_us = host_call_us(plan_only, launches)
+    abi_us = host_call_us(abi, launches)
     res = {
         "config": "decode: 64 rows, row_stride 32768, lengths U{1..32768}, K=2048, no workspace",
         "eager_us_per_launch": round(time_launches(abi, launches) * 1e3, 3),
         "graph_us_per_launch": round(graph_replay_ms(py, 100) * 1e3, 3),
         "host_us_per_call_binding": round(host_call_us(py, launches), 3),
-        "host_us_per_call_c_abi": round(host_call_us(abi, launches), 3),
+        "host_us_per_call_c_abi": round(abi_us, 3),
+        "host_us_ctypes_floor": round(ctypes_us, 3),
+        "host_us_plan_only": round(plan_us, 3),
+        "host_us_library": round(plan_us - ctypes_us, 3),
+        "host_us_hip_launch": round(abi_us - plan_us, 3),
         "empty_rows_us_per_launch": round(graph_replay_ms(
             lambda i: rrt.topk_ragged(pool[i % ncopy], Z, w.K, out=out), 100) * 1e3, 3),
         "read_reference_us_per_launch": round(graph_replay_ms(

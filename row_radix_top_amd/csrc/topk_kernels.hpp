@@ -825,28 +825,38 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 // Scores are read once and never again by this launch, so the loads carry
 // the nontemporal hint: they stream through the caches without displacing
 // anything (measured on the prefill-shaped batch: 211.6 -> 198.1 us, and
-// the streaming-read reference 168 -> 149 us).
-template <int VEC, typename T>
+// the streaming-read reference 168 -> 149 us).  A sample that several
+// workgroups of one row read (NT = false) goes through the caches as usual,
+// so that the row's other workgroups find it in L2.
+template <bool NT, typename V>
+__device__ __forceinline__ V ld(const V* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
+}
+
+template <int VEC, bool NT = true, typename T>
 __device__ __forceinline__ void load_run(const T* __restrict__ p, float (&x)[kElems], int o) {
   if constexpr (std::is_same<T, float>::value) {
     static_assert(VEC == 4 || VEC == 2 || VEC == 1, "fp32 loads of 16, 8 or 4 bytes");
     if constexpr (VEC == 4) {
-      const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+      const f32x4 v = ld<NT>(reinterpret_cast<const f32x4*>(p));
       x[o + 0] = v.x;
       x[o + 1] = v.y;
       x[o + 2] = v.z;
       x[o + 3] = v.w;
     } else if constexpr (VEC == 2) {
-      const f32x2 v = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p));
+      const f32x2 v = ld<NT>(reinterpret_cast<const f32x2*>(p));
       x[o + 0] = v.x;
       x[o + 1] = v.y;
     } else {
-      x[o] = __builtin_nontemporal_load(p);
+      x[o] = ld<NT>(p);
     }
   } else {
     static_assert(std::is_same<T, uint16_t>::value && (VEC == 8 || VEC == 1), "bf16 loads of 16 or 2 bytes");
     if constexpr (VEC == 8) {
-      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+      const u32x4 v = ld<NT>(reinterpret_cast<const u32x4*>(p));
       x[o + 0] = __uint_as_float(v.x << 16);
       x[o + 1] = __uint_as_float(v.x & 0xffff0000u);
       x[o + 2] = __uint_as_float(v.y << 16);
@@ -856,7 +866,7 @@ __device__ __forceinline__ void load_run(const T* __restrict__ p, float (&x)[kEl
       x[o + 6] = __uint_as_float(v.w << 16);
       x[o + 7] = __uint_as_float(v.w & 0xffff0000u);
     } else {
-      x[o] = widen(__builtin_nontemporal_load(p));
+      x[o] = widen(ld<NT>(p));
     }
   }
 }
@@ -1239,11 +1249,12 @@ __device__ __forceinline__ bool wave_mode(uint32_t n, uint32_t K) {
 
 // One full wave tile at `tile` (wave-uniform): lane l loads elements
 // u * 64 * VEC + l * VEC .. + VEC - 1.
-template <int VEC, typename T>
+template <int VEC, bool NT = true, typename T>
 __device__ __forceinline__ void load_wave_full(const T* __restrict__ tile, float (&x)[kElems]) {
   const uint32_t l = threadIdx.x & 63;
 #pragma unroll
-  for (int u = 0; u < kElems / VEC; ++u) load_run<VEC>(tile + (uint32_t)u * (64u * VEC) + l * VEC, x, u * VEC);
+  for (int u = 0; u < kElems / VEC; ++u)
+    load_run<VEC, NT>(tile + (uint32_t)u * (64u * VEC) + l * VEC, x, u * VEC);
 }
 
 // The partial last wave tile [p0, end): nothing read at or past end.
@@ -1457,9 +1468,10 @@ __device__ __forceinline__ bool stream_range_waves(Smem<LAY>& sm, const T* __res
   c1 = uni(c1);
   const uint32_t w = uni(threadIdx.x >> 6);
   if (!preloaded) {
+    // Every workgroup of the row reads this sample: through L2.
     const T* sp = rowp + w * segment_of<W>(n);
-    load_wave_full<VEC>(sp, x0);
-    load_wave_full<VEC>(sp + WT, x1);
+    load_wave_full<VEC, false>(sp, x0);
+    load_wave_full<VEC, false>(sp + WT, x1);
     __builtin_amdgcn_sched_barrier(0);
   }
   const uint32_t q = segment_of<W>(c1 - c0);
