@@ -1016,25 +1016,29 @@ __device__ __forceinline__ void process_tile(Smem<LAY>& sm, const float (&x)[kEl
   st.cnt += total;
 }
 
-// Per lane, the largest and the KK-th largest of its 2 * kElems sample keys:
+// Per lane, the largest and the KK-th largest of its first nk sample keys
+// (uniform nk of 2 * kElems; the others count as key 0, below every key):
 // an insertion network over a descending list of the KK largest so far.
 template <int KK>
-__device__ __forceinline__ void lane_top(const uint32_t (&k)[2 * kElems], uint32_t& kth, uint32_t& top) {
+__device__ __forceinline__ void lane_top(const uint32_t (&k)[2 * kElems], uint32_t nk, uint32_t& kth,
+                                         uint32_t& top) {
   uint32_t t[KK];
 #pragma unroll
   for (int i = 0; i < KK; ++i) t[i] = 0u;
 #pragma unroll
   for (int j = 0; j < 2 * kElems; ++j) {
+    const uint32_t v = (uint32_t)j < nk ? k[j] : 0u;
 #pragma unroll
-    for (int i = KK - 1; i > 0; --i) t[i] = max(t[i], min(t[i - 1], k[j]));
-    t[0] = max(t[0], k[j]);
+    for (int i = KK - 1; i > 0; --i) t[i] = max(t[i], min(t[i - 1], v));
+    t[0] = max(t[0], v);
   }
   kth = t[KK - 1];
   top = t[0];
 }
 
 // The interval the speculative bound's selection starts from (both ends
-// uniform).  hi is the largest sample key.  lo is a key that at least r
+// uniform), over the first nk keys of every lane (all of them sample keys,
+// so kk <= nk below).  hi is the largest sample key.  lo is a key that at least r
 // sample keys reach, found without a selection: with kk = ceil(r / threads)
 // at most 4, the smallest over lanes of each lane's kk-th largest key (every
 // lane holds kk keys at or above it, so the workgroup holds at least r);
@@ -1043,24 +1047,26 @@ __device__ __forceinline__ void lane_top(const uint32_t (&k)[2 * kElems], uint32
 // on the upper part of the sample, where the r-th best lies, and the dense
 // middle of the sample does not crowd a few bins.  Contains one barrier.
 template <int LAY>
-__device__ __forceinline__ void sample_range(Smem<LAY>& sm, const uint32_t (&k)[2 * kElems], uint32_t r,
-                                             uint32_t& lo, uint32_t& hi) {
+__device__ __forceinline__ void sample_range(Smem<LAY>& sm, const uint32_t (&k)[2 * kElems], uint32_t nk,
+                                             uint32_t r, uint32_t& lo, uint32_t& hi) {
   constexpr int W = Shape<LAY>::kWaves;
   const uint32_t kk = (r + (uint32_t)Shape<LAY>::kBlock - 1u) / (uint32_t)Shape<LAY>::kBlock;
   uint32_t a, b;
   if (kk == 1u) {
-    lane_top<1>(k, a, b);
+    lane_top<1>(k, nk, a, b);
   } else if (kk == 2u) {
-    lane_top<2>(k, a, b);
+    lane_top<2>(k, nk, a, b);
   } else if (kk <= 4u) {
-    lane_top<4>(k, a, b);  // kk = 3 takes the 4th largest: a lower key that qualifies too
+    lane_top<4>(k, nk, a, b);  // kk = 3 takes the 4th largest: a lower key that qualifies too
   } else {
     a = 0xffffffffu;
     b = 0u;
 #pragma unroll
     for (int j = 0; j < 2 * kElems; ++j) {
-      a = min(a, k[j]);
-      b = max(b, k[j]);
+      if ((uint32_t)j < nk) {
+        a = min(a, k[j]);
+        b = max(b, k[j]);
+      }
     }
   }
   const uint32_t mn = wave_min(a);
@@ -1083,11 +1089,19 @@ __device__ __forceinline__ void sample_range(Smem<LAY>& sm, const uint32_t (&k)[
   hi = uni(h);
 }
 
+// Rank of the speculative bound in a sample of M elements of a row of n:
+// r = max(kSpecMinRank, ceil(kSpecNum / kSpecDen * K * M / n)).
+__device__ __forceinline__ uint32_t spec_rank(uint32_t K, uint32_t M, uint32_t n) {
+  const uint64_t want = ((uint64_t)kSpecNum * K * M + (uint64_t)kSpecDen * n - 1) / ((uint64_t)kSpecDen * n);
+  return want > kSpecMinRank ? (uint32_t)want : kSpecMinRank;
+}
+
 // The speculative bound for a row of n elements whose first two tiles are
 // in x0 and x1 (n >= kSpecMinLen): the key of (about) the r-th best of those
-// M = 2 * kTile elements (4096, 8192 or 16384 by workgroup width),
-// r = max(kSpecMinRank, ceil(kSpecNum / kSpecDen * K * M / n)),
-// or 0 (no bound) when r >= K.  The bin holding the r-th best is taken whole
+// M = 2 * kTile elements (4096, 8192 or 16384 by workgroup width), r =
+// spec_rank(K, M, n).  When that r reaches K (the two tiles are too large a
+// share of the row) the sample is the first tile alone, M = kTile, and if r
+// still reaches K there is no bound (0).  The bin holding the r-th best is taken whole
 // when it is small, which only lowers the bound.  The caller checks at the
 // end of the row that at least K elements reached the bound and streams the
 // row again without it if not; when the check passes, every element below
@@ -1097,8 +1111,9 @@ template <int LAY>
 __device__ __forceinline__ uint32_t spec_bound(Smem<LAY>& sm, float (&x0)[kElems], float (&x1)[kElems], uint32_t n,
                                                uint32_t K) {
   constexpr uint32_t M = 2u * (uint32_t)Shape<LAY>::kTile;
-  const uint64_t want = ((uint64_t)kSpecNum * K * M + (uint64_t)kSpecDen * n - 1) / ((uint64_t)kSpecDen * n);
-  const uint32_t r = want > kSpecMinRank ? (uint32_t)want : kSpecMinRank;
+  uint32_t r = spec_rank(K, M, n);
+  const bool one = r >= K;
+  if (one) r = spec_rank(K, M / 2u, n);
   if (r >= K) return 0u;
   // The keys replace the values in place (registers are scarce here) and
   // are turned back afterwards, bit for bit: raw_key keeps -0.0 apart from
@@ -1110,12 +1125,12 @@ __device__ __forceinline__ uint32_t spec_bound(Smem<LAY>& sm, float (&x0)[kElems
     k[e] = raw_key(__float_as_uint(x0[e]));
     k[kElems + e] = raw_key(__float_as_uint(x1[e]));
   }
-  Slice sl;  // the keys live only in registers: every lane holds 16 valid slots
+  Slice sl;  // the keys live only in registers: every lane holds 16 slots, 8 or 16 of them sample keys
   sl.ws = 0u;
   sl.sp = 2u * kElems;
-  sl.nv = 2u * kElems;
+  sl.nv = one ? kElems : 2u * kElems;
   uint32_t lo, hi;
-  sample_range<LAY>(sm, k, r, lo, hi);
+  sample_range<LAY>(sm, k, sl.nv, r, lo, hi);
   const Sel s = range_select<LAY, 2 * kElems>(sm, k, sl, lo, hi, r, r + r / 8u + 8u);
 #pragma unroll
   for (int e = 0; e < kElems; ++e) {
@@ -1225,26 +1240,46 @@ __device__ __forceinline__ void stream_chunk(Smem<LAY>& sm, const T* __restrict_
 // ---------------------------------------------------------------------------
 
 
-// Elements per wavefront segment of a row of n, W wavefronts: whole wave tiles.
+// Elements per wavefront segment of a chunk of n, W wavefronts: whole wave
+// tiles (the cooperative chunks; the last segments may be short or empty).
 template <int W>
 __device__ __forceinline__ uint32_t segment_of(uint32_t n) {
   const uint32_t q = (n + W - 1) / W;
   return (q + kWaveTile - 1) / kWaveTile * kWaveTile;
 }
 
+// Wave segments of a whole row of n elements.  Normally every wavefront but
+// the last takes segment_of(n) elements (whole wave tiles, rounded up) and
+// the last takes the rest: the last wavefront, issued last, gets the least
+// work, which evens out finishing times since the oldest waves of a SIMD win
+// its issue slots.  When that would leave the last segment without the two
+// full wave tiles of the sample, the row's T = n / kWaveTile full tiles are
+// dealt out evenly instead (wavefront w starts at tile ceil(w T / W)), with
+// the partial tile at the end going to the last wavefront: every segment
+// then holds at least floor(T / W) full tiles.
+template <int W>
+__device__ __forceinline__ bool even_segments(uint32_t n) {
+  return n < (uint32_t)(W - 1) * segment_of<W>(n) + 2u * kWaveTile;
+}
+template <int W>
+__device__ __forceinline__ uint32_t seg_begin(uint32_t n, uint32_t w) {
+  if (even_segments<W>(n)) return ((w * (n / kWaveTile) + (uint32_t)W - 1u) / (uint32_t)W) * kWaveTile;
+  return w * segment_of<W>(n);
+}
+template <int W>
+__device__ __forceinline__ uint32_t seg_end(uint32_t n, uint32_t w) {
+  return w + 1u == (uint32_t)W ? n : seg_begin<W>(n, w + 1u);
+}
+
 // Whether a row of n elements (n > K) goes wave by wave: long enough to
 // speculate, every segment holding the two full wave tiles of the sample
-// (with four wavefronts: every n >= 8704, and 8192), and a speculative rank
-// below K.
+// (at least 2W full wave tiles in all), and a speculative rank below K.
 template <int LAY>
 __device__ __forceinline__ bool wave_mode(uint32_t n, uint32_t K) {
   constexpr uint32_t W = (uint32_t)Shape<LAY>::kWaves;
-  constexpr uint64_t M = 2u * (uint64_t)Shape<LAY>::kTile;
   if (n < kSpecMinLen) return false;
-  if (n < (W - 1u) * segment_of<W>(n) + 2u * kWaveTile) return false;  // short last segment
-  const uint64_t want = ((uint64_t)kSpecNum * K * M + (uint64_t)kSpecDen * n - 1) / ((uint64_t)kSpecDen * n);
-  const uint32_t r = want > kSpecMinRank ? (uint32_t)want : kSpecMinRank;
-  return r < K;
+  if (n / kWaveTile < 2u * W) return false;
+  return spec_rank(K, (uint32_t)Shape<LAY>::kTile, n) < K;  // a bound from one or two tiles
 }
 
 // One full wave tile at `tile` (wave-uniform): lane l loads elements
@@ -1369,9 +1404,8 @@ __device__ __forceinline__ bool stream_row_waves(Smem<LAY>& sm, const T* __restr
   n = uni(n);
   K = uni(K);
   const uint32_t w = uni(threadIdx.x >> 6);
-  const uint32_t Q = segment_of<W>(n);
-  const uint32_t qs = w * Q;
-  const uint32_t qe = qs + Q < n ? qs + Q : n;
+  const uint32_t qs = uni(seg_begin<W>(n, w));
+  const uint32_t qe = uni(seg_end<W>(n, w));
   const T* qp = rowp + qs;
   if (!preloaded) {
     load_wave_full<VEC>(qp, x0);
@@ -1469,7 +1503,7 @@ __device__ __forceinline__ bool stream_range_waves(Smem<LAY>& sm, const T* __res
   const uint32_t w = uni(threadIdx.x >> 6);
   if (!preloaded) {
     // Every workgroup of the row reads this sample: through L2.
-    const T* sp = rowp + w * segment_of<W>(n);
+    const T* sp = rowp + seg_begin<W>(n, w);
     load_wave_full<VEC, false>(sp, x0);
     load_wave_full<VEC, false>(sp + WT, x1);
     __builtin_amdgcn_sched_barrier(0);
@@ -1665,7 +1699,7 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
       // when it will go wave by wave, else the row's first two tiles.
       const T* nrowp = row_of<T>(p, nrow);
       if (wave_mode<LAY>((uint32_t)nn, K)) {
-        const T* qp = nrowp + uni(threadIdx.x >> 6) * segment_of<W>((uint32_t)nn);
+        const T* qp = nrowp + seg_begin<W>((uint32_t)nn, uni(threadIdx.x >> 6));
         load_wave_full<VEC>(qp, x0);
         load_wave_full<VEC>(qp + kWaveTile, x1);
       } else {
@@ -1978,11 +2012,14 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
       if (last) gather_union<LAY>(sm, lists, PUB, s_off, grow, sum);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();  // every gather load has completed
-      // Leave.  The last workgroup out zeroes the published lists, the slots
-      // and both counters (nobody reads them any more).  The workgroup that
+      // The gatherer was the lists' only reader: it zeroes them now, and the
+      // stores complete while it selects.
+      if (last) clear_union<NT>(lists, (uint32_t)CAP, PUB, s_off, grow);
+      // Leave.  The last workgroup out zeroes the slots and both counters
+      // (every workgroup has read the slots by then).  The workgroup that
       // selects issues its exit before the selection and looks at the
-      // answer after it, so neither the atomic's round trip nor a cleanup
-      // sits on its critical path.
+      // answer after it, so the atomic's round trip is off its critical
+      // path.
       uint32_t old = 0u;
       if (t == 0) old = __hip_atomic_fetch_add(exit_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (last) final_select<LAY>(sm, plain_slice<LAY>(sum), K, out, offset_of(p, row), vout);
@@ -1990,7 +2027,6 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
       __syncthreads();
       const bool clean = uni(sm.acc[4]) != 0u;
       if (clean) {
-        clear_union<NT>(lists, (uint32_t)CAP, PUB, s_off, grow);
         if (t < 4 * grow) ws_store(&slots[t], 0u);
         if (t == 0) {
           ws_store(ctr, 0u);
