@@ -48,8 +48,10 @@ constexpr int kIdx16Limit = 65536;
 // (kElems per thread) for the general path, and about twice the ~1.5 K that
 // pass a speculative bound, split between the wavefronts.  256 threads:
 // 5120 (7168 for the large K), four workgroups per CU with 16-bit indices,
-// three with 32-bit ones, two for the large K.  512 threads: 6144 (8192),
-// two per CU (one for the large K with 32-bit indices).  1024 threads: 12288,
+// three with 32-bit ones, two for the large K.  512 threads: 8192 with
+// 16-bit indices (a row of up to two tiles then never compacts), 6144 with
+// 32-bit ones (8192 for the large K), two per CU (one for the large K with
+// 32-bit indices).  1024 threads: 12288,
 // one per CU.  At most 16 wavefronts per CU in every case, so each keeps
 // 128 VGPRs (256 where fewer fit).
 constexpr int kLayIdx16 = 1;
@@ -63,7 +65,7 @@ constexpr int layout_of(bool idx16, bool big_k, int block = kBlock) {
 constexpr int block_of(int lay) { return (lay & kLayW1024) ? 1024 : (lay & kLayW512) ? 512 : kBlock; }
 constexpr int tile_of(int lay) { return block_of(lay) * kElems; }
 constexpr int cap_of(int lay) {
-  return block_of(lay) == 1024 ? 12288 : block_of(lay) == 512 ? ((lay & kLayBigK) ? 8192 : 6144)
+  return block_of(lay) == 1024 ? 12288 : block_of(lay) == 512 ? ((lay & (kLayBigK | kLayIdx16)) ? 8192 : 6144)
                                                               : ((lay & kLayBigK) ? 7168 : 5120);
 }
 constexpr int kmax_of(int lay) { return (lay & kLayBigK) ? kMaxKBig : kMaxK; }
