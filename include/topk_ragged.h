@@ -283,6 +283,9 @@ typedef struct {
                                 workgroups per CU resident (emulates a smaller device) */
   int32_t force_idx32;       /* 1: never keep 16-bit candidate indices (testing) */
   int32_t force_block;       /* 0 auto, else threads per workgroup: 256, 512 or 1024 */
+  int32_t force_wait_timeout; /* 1: every cooperative wait waits for one arrival more than can come, so it
+                                 gives up after spin_limit polls and sets error bit 0 (testing the bound
+                                 on waits; the results of such a launch are undefined) */
 } topk_overrides;
 
 /* Pure planning function (host only, no GPU needed).  vec_allowed is the

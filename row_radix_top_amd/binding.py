@@ -57,7 +57,8 @@ class Overrides(ctypes.Structure):
                 ("max_grid", ctypes.c_int32), ("force_vec", ctypes.c_int32),
                 ("force_chunk", ctypes.c_int64), ("spin_limit", ctypes.c_uint32),
                 ("min_chunk", ctypes.c_int32), ("max_occupancy", ctypes.c_int32),
-                ("force_idx32", ctypes.c_int32), ("force_block", ctypes.c_int32)]
+                ("force_idx32", ctypes.c_int32), ("force_block", ctypes.c_int32),
+                ("force_wait_timeout", ctypes.c_int32)]
 
     @classmethod
     def make(cls, **kw) -> "Overrides | None":

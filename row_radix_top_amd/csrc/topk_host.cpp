@@ -525,6 +525,7 @@ int launch(const void* scores, int64_t row_stride, const int32_t* lengths, const
   kp.K = K;
   kp.wg_per_row = plan.wg_per_row;
   kp.spin_limit = (ov != nullptr && ov->spin_limit > 0) ? ov->spin_limit : rrt::kDefaultSpin;
+  kp.wait_extra = (ov != nullptr && ov->force_wait_timeout != 0) ? 1u : 0u;
 
   if (verbose()) std::fprintf(stderr, "[topk_ragged] rows=%d stride=%lld K=%d %s\n", num_rows,
                               (long long)row_stride, K, describe(plan).c_str());

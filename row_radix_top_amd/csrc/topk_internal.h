@@ -138,6 +138,7 @@ struct KernelParams {
   int32_t K;
   int32_t wg_per_row;    // multi path: G
   uint32_t spin_limit;
+  uint32_t wait_extra;  // added to every cooperative wait's target: 0, or 1 to force timeouts (testing)
 };
 
 // Kernel lookup for the host side.  path: 1 single, 2 multi, 3 the

@@ -1768,10 +1768,12 @@ __device__ void group_wait(const uint32_t* ctr, uint32_t target, uint32_t spin_l
 // lists + gg * CAP (fp32 bits) and + pub (row indices), and go to merged
 // positions [s_off[gg], s_off[gg + 1]) (s_off ascending, s_off[0] = 0, grow
 // chunks, total = s_off[grow] <= the buffer capacity).  First every merged
-// position's source offset is written into the buffer (one short loop per
-// chunk, LDS only); then each thread reads its positions' offsets and issues
-// all its workspace loads back to back, with no branch between them, so the
-// gather costs about one round trip; the values go to the buffer last.
+// position's source offset is written into the buffer (wavefront w takes
+// chunks w, w + W, ..., its lanes 64 positions at a time; the chunk bounds
+// come from registers, so nothing waits on LDS); then each thread reads its
+// positions' offsets and issues all its workspace loads back to back, with
+// no branch between them, so the gather costs about one round trip; the
+// values go to the buffer last.
 template <int LAY>
 __device__ __forceinline__ void gather_union(Smem<LAY>& sm, const uint32_t* lists, uint32_t pub, const uint32_t* s_off,
                                              int grow, uint32_t total) {
@@ -1779,17 +1781,19 @@ __device__ __forceinline__ void gather_union(Smem<LAY>& sm, const uint32_t* list
   constexpr uint32_t NT = (uint32_t)Shape<LAY>::kBlock;
   constexpr uint32_t CAP = (uint32_t)Shape<LAY>::kCap;
   using Idx = typename Shape<LAY>::Idx;
+  constexpr int W = Shape<LAY>::kWaves;
   const uint32_t t = tid();
   // Every merged position's source word goes into the buffer's value array
   // first (it is overwritten last).  The chunk bounds are read once, lane gg
   // of each wavefront holding s_off[gg], so the loop waits on nothing.
   const uint32_t lane = t & 63u;
+  const int w = (int)uni(t >> 6);
   const uint32_t bound = lane < (uint32_t)grow ? s_off[lane] : 0u;  // grow <= 64 chunk starts
-  for (int gg = 0; gg < grow; ++gg) {
+  for (int gg = w; gg < grow; gg += W) {
     const uint32_t o = lane_value(bound, gg);
     const uint32_t e = gg + 1 < grow ? lane_value(bound, gg + 1) : total;
     const uint32_t src = (uint32_t)gg * CAP - o;
-    for (uint32_t i = o + t; i < e; i += NT) sm.val[i] = src + i;
+    for (uint32_t i = o + lane; i < e; i += 64u) sm.val[i] = src + i;
   }
   __syncthreads();
   uint32_t vb[S], vi[S];
@@ -1812,14 +1816,21 @@ __device__ __forceinline__ void gather_union(Smem<LAY>& sm, const uint32_t* list
 }
 
 // Zeroes the published candidates of a row's grow chunks (positions as in
-// gather_union), chunk by chunk.
+// gather_union): wavefront w takes chunks w, w + W, ..., with the chunk
+// bounds in registers as in gather_union.
 template <int NT>
 __device__ __forceinline__ void clear_union(uint32_t* lists, uint32_t cap, uint32_t pub, const uint32_t* s_off,
                                             int grow) {
-  for (int gg = 0; gg < grow; ++gg) {
-    const uint32_t m = s_off[gg + 1] - s_off[gg];
+  constexpr int W = NT / 64;
+  const uint32_t lane = threadIdx.x & 63u;
+  const int w = (int)uni(threadIdx.x >> 6);
+  const uint32_t bound = lane < (uint32_t)grow ? s_off[lane] : 0u;  // grow <= 64 chunk starts
+  const uint32_t last = s_off[grow];
+  for (int gg = w; gg < grow; gg += W) {
+    const uint32_t o = lane_value(bound, gg);
+    const uint32_t e = gg + 1 < grow ? lane_value(bound, gg + 1) : last;
     uint32_t* l = lists + (uint32_t)gg * cap;
-    for (uint32_t i = threadIdx.x; i < m; i += NT) {
+    for (uint32_t i = lane; i < e - o; i += 64u) {
       ws_store(l + i, 0u);
       ws_store(l + pub + i, 0u);
     }
@@ -1992,7 +2003,7 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
     if (t == 0) sm.acc[5] = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     const bool last = uni(sm.acc[5]) == (uint32_t)grow - 1u;
-    if (!last) group_wait(ctr, (uint32_t)grow, p.spin_limit, err);
+    if (!last) group_wait(ctr, (uint32_t)grow + p.wait_extra, p.spin_limit, err);
     // Every workgroup reads the same published counts and decides alike.
     if (t < 64) {  // the whole of wavefront 0
       const uint32_t v = t < grow ? ws_load(&slots[4 * t + 3]) : 0u;
@@ -2084,7 +2095,7 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
   }
   __syncthreads();
   merge_hist<NT>(sm.hist1, h1, gs1);
-  group_barrier(ctr, base + 1u * grow, p.spin_limit, err);
+  group_barrier(ctr, base + 1u * grow + p.wait_extra, p.spin_limit, err);
   const Found f1 = ws_find(h1, gs1, K);
   uint32_t ok = f1.ok;
   uint32_t krem = K - f1.above;
@@ -2114,7 +2125,7 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
   __syncthreads();
   merge_hist<NT>(sm.hist1, h2, gs2);
   if (t == 0) ws_store(&slots[4 * g + 0], sm.acc[0]);
-  group_barrier(ctr, base + 2u * grow, p.spin_limit, err);
+  group_barrier(ctr, base + 2u * grow + p.wait_extra, p.spin_limit, err);
   const Found f2 = ws_find(h2, gs2, krem);
   ok &= f2.ok;
   krem -= f2.above;
@@ -2160,7 +2171,7 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
       ws_store(&slots[4 * g + 2], len);
     }
   }
-  group_barrier(ctr, base + 3u * grow, p.spin_limit, err);
+  group_barrier(ctr, base + 3u * grow + p.wait_extra, p.spin_limit, err);
   for (int i = t; i < kBins; i += NT) sm.hist1[i] = 0u;  // round 2's local histogram was merged before the barrier
 
   // Every chunk's list, flattened: offsets by a prefix sum over the lengths.

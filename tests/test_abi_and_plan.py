@@ -286,3 +286,29 @@ def test_plan_block_width_forced():
     # A forced width the device cannot keep resident is an error, not a silent change.
     with pytest.raises(rrt.TopKError):
         rrt.plan_for_props(256, 3, 3, 64, 32768, 2048, force_block=1024)
+
+
+def test_ctypes_mirrors_match_the_header():
+    # The binding's ctypes structs must list the header's fields in order,
+    # with the same widths: a mismatch would make the library read or write
+    # past the caller's struct.
+    import ctypes
+    import os
+    import re
+    from row_radix_top_amd import binding
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "topk_ragged.h")).read()
+    hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
+    widths = {"int32_t": 4, "uint32_t": 4, "int64_t": 8, "uint64_t": 8}
+    for cname, cls in (("topk_plan", binding.Plan), ("topk_overrides", binding.Overrides),
+                       ("topk_device_props", binding.DeviceProps)):
+        body = re.search(r"typedef struct \{([^{}]*)\}\s*" + cname + ";", hdr).group(1)
+        fields = []
+        for decl in body.split(";"):
+            decl = decl.strip()
+            if not decl:
+                continue
+            m = re.fullmatch(r"(\w+)\s+(\w+)(?:\[(\d+)\])?", decl)
+            assert m, (cname, decl)
+            fields.append((m.group(2), widths[m.group(1)] * int(m.group(3) or 1)))
+        mirror = [(name, ctypes.sizeof(t)) for name, t in cls._fields_]
+        assert mirror == fields, (cname, mirror, fields)
