@@ -2023,9 +2023,6 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
       if (last) gather_union<LAY>(sm, lists, PUB, s_off, grow, sum);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();  // every gather load has completed
-      // The gatherer was the lists' only reader: it zeroes them now, and the
-      // stores complete while it selects.
-      if (last) clear_union<NT>(lists, (uint32_t)CAP, PUB, s_off, grow);
       // Leave.  The last workgroup out zeroes the slots and both counters
       // (every workgroup has read the slots by then).  The workgroup that
       // selects issues its exit before the selection and looks at the
@@ -2033,7 +2030,11 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
       // path.
       uint32_t old = 0u;
       if (t == 0) old = __hip_atomic_fetch_add(exit_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (last) final_select<LAY>(sm, plain_slice<LAY>(sum), K, out, offset_of(p, row), vout);
+      if (last) {
+        final_select<LAY>(sm, plain_slice<LAY>(sum), K, out, offset_of(p, row), vout);
+        // The gatherer was the lists' only reader: it zeroes them.
+        clear_union<NT>(lists, (uint32_t)CAP, PUB, s_off, grow);
+      }
       if (t == 0) sm.acc[4] = (old == (uint32_t)grow - 1u) ? 1u : 0u;
       __syncthreads();
       const bool clean = uni(sm.acc[4]) != 0u;
