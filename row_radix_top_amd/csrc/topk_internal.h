@@ -50,10 +50,12 @@ constexpr int kIdx16Limit = 65536;
 // 5120 (7168 for the large K), four workgroups per CU with 16-bit indices,
 // three with 32-bit ones, two for the large K.  512 threads: 8192 with
 // 16-bit indices (a row of up to two tiles then never compacts), 6144 with
-// 32-bit ones (8192 for the large K), two per CU (one for the large K with
-// 32-bit indices).  1024 threads: 12288,
-// one per CU.  At most 16 wavefronts per CU in every case, so each keeps
-// 128 VGPRs (256 where fewer fit).
+// 32-bit ones (8192 for the large K), two per CU, except one for the large K
+// with 32-bit indices (LDS) and one for 16-bit indices below the large K:
+// the rows that layout serves are fewer than the CUs, and at one workgroup
+// per CU its instances keep up to 256 VGPRs instead of spilling at 128.
+// 1024 threads: 12288, one per CU.  At most 16 wavefronts per CU in every
+// case, so each keeps 128 VGPRs (more where fewer fit).
 constexpr int kLayIdx16 = 1;
 constexpr int kLayBigK = 2;
 constexpr int kLayW512 = 4;
@@ -71,7 +73,7 @@ constexpr int cap_of(int lay) {
 constexpr int kmax_of(int lay) { return (lay & kLayBigK) ? kMaxKBig : kMaxK; }
 constexpr int resident_of(int lay) {
   return block_of(lay) == 1024 ? 1
-       : block_of(lay) == 512 ? (((lay & kLayBigK) && !(lay & kLayIdx16)) ? 1 : 2)
+       : block_of(lay) == 512 ? (((lay & kLayBigK) != 0) != ((lay & kLayIdx16) != 0) ? 1 : 2)
                               : ((lay & kLayBigK) ? 2 : ((lay & kLayIdx16) ? 4 : 3));
 }
 // Workgroup widths with instances: 256 and 512 for every load width of fp32
