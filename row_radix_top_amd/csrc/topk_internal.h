@@ -39,7 +39,9 @@ constexpr uint32_t kSpecMinLen = 8192;
 // wavefronts 1280 slots when a row streams wave by wave.  With 16-bit
 // indices (rows or chunks of at most 65536 elements) an entry takes 6 bytes
 // and four workgroups fit in a CU's 160 KB of LDS; with 32-bit indices,
-// three.
+// three.  The wider workgroups keep 32-bit indices in LDS whatever the row
+// length (8 bytes per entry); their layouts with the 16-bit flag differ from
+// the others only in capacity and residency.
 constexpr int kIdx16Limit = 65536;
 
 // Buffer layout of a kernel instance (a bit set): 16-bit candidate indices,
@@ -48,12 +50,13 @@ constexpr int kIdx16Limit = 65536;
 // (kElems per thread) for the general path, and about twice the ~1.5 K that
 // pass a speculative bound, split between the wavefronts.  256 threads:
 // 5120 (7168 for the large K), four workgroups per CU with 16-bit indices,
-// three with 32-bit ones, two for the large K.  512 threads: 8192 with
-// 16-bit indices (a row of up to two tiles then never compacts), 6144 with
-// 32-bit ones (8192 for the large K), two per CU, except one for the large K
-// with 32-bit indices (LDS) and one for 16-bit indices below the large K:
-// the rows that layout serves are fewer than the CUs, and at one workgroup
-// per CU its instances keep up to 256 VGPRs instead of spilling at 128.
+// three with 32-bit ones, two for the large K.  512 threads (32-bit
+// indices in LDS either way): 8192 with the 16-bit flag (a row of up to two
+// tiles then never compacts), 6144 without it (8192 for the large K), two
+// per CU, except one for the large K without the flag (LDS) and one with the
+// flag below the large K: the rows that layout serves are fewer than the
+// CUs, and at one workgroup per CU its instances keep up to 256 VGPRs
+// instead of spilling at 128.
 // 1024 threads: 12288, one per CU.  At most 16 wavefronts per CU in every
 // case, so each keeps 128 VGPRs (more where fewer fit).
 constexpr int kLayIdx16 = 1;
