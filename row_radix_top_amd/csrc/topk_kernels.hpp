@@ -559,11 +559,13 @@ constexpr uint32_t kTieCheckSoft = 8;
 // exactly the ones still needed, or entries above plus the bin number at
 // most stop_total) or holds a single key; the result's take is then the
 // whole bin or the entries still needed.  stop_total = 0 asks for an exact
-// selection of keep entries.  Both histograms are zero on entry and hold
-// garbage on return.
+// selection of keep entries.  With open_top, hi is only an estimate of the
+// largest key: the first pass counts the keys above it in its top bin, and
+// if the wanted entry lies there the search goes on from that bin's exact
+// key range.  Both histograms are zero on entry and hold garbage on return.
 template <int LAY, int S>
 __device__ Sel range_select(Smem<LAY>& sm, const uint32_t (&k)[S], const Slice& sl, uint32_t lo, uint32_t hi,
-                            uint32_t keep, uint32_t stop_total) {
+                            uint32_t keep, uint32_t stop_total, bool open_top = false) {
   Sel r;
   r.ok = 1u;
   r.above = 0u;
@@ -592,15 +594,30 @@ __device__ Sel range_select(Smem<LAY>& sm, const uint32_t (&k)[S], const Slice& 
     // bin.  (Adding 0 to some bin would let every such lane of a wave hit the
     // same bin when the keys share their low bits, as bf16 scores do.)
     uint32_t* const sink = &sm.sink[tid() & 63];
+    if (open_top) {
 #pragma unroll
-    for (int q = 0; q < S / 4; ++q) {
-      if ((uint32_t)(4 * q) < sl.sp) {
+      for (int q = 0; q < S / 4; ++q) {
+        if ((uint32_t)(4 * q) < sl.sp) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int j = 4 * q + c;
-          const uint32_t d = k[j] - lo;
-          const bool in = (uint32_t)j < sl.nv && d <= range;
-          atomicAdd(in ? &h[d >> sh] : sink, 1u);
+          for (int c = 0; c < 4; ++c) {
+            const int j = 4 * q + c;
+            const uint32_t d = k[j] - lo;
+            const bool in = (uint32_t)j < sl.nv && k[j] >= lo;
+            atomicAdd(in ? &h[min(d, range) >> sh] : sink, 1u);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < S / 4; ++q) {
+        if ((uint32_t)(4 * q) < sl.sp) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int j = 4 * q + c;
+            const uint32_t d = k[j] - lo;
+            const bool in = (uint32_t)j < sl.nv && d <= range;
+            atomicAdd(in ? &h[d >> sh] : sink, 1u);
+          }
         }
       }
     }
@@ -610,12 +627,15 @@ __device__ Sel range_select(Smem<LAY>& sm, const uint32_t (&k)[S], const Slice& 
     krem -= f.above;
     r.above += f.above;
     r.in_bin = f.in_bin;
+    // The top bin of an open first pass holds every key from its start up.
+    const bool top = open_top && f.bin == range >> sh;
+    open_top = false;
     lo += f.bin << sh;
     const uint32_t width = (1u << sh) - 1u;
-    hi = hi - lo > width ? lo + width : hi;
+    hi = top ? 0xffffffffu : (hi - lo > width ? lo + width : hi);
     whole = f.in_bin == krem || r.above + f.in_bin <= stop_total;
-    if (whole || sh == 0u || !f.ok) break;
-    if (f.in_bin > (stop_total != 0u ? kTieCheckSoft : kTieCheck)) {
+    if (whole || (sh == 0u && !top) || !f.ok) break;
+    if (top || f.in_bin > (stop_total != 0u ? kTieCheckSoft : kTieCheck)) {
       uint32_t mn, mx;
       interval_range<LAY, S>(sm, k, sl, lo, hi, mn, mx);
       if (mn <= mx) {
@@ -799,19 +819,45 @@ __device__ __noinline__ uint64_t compact(Smem<LAY>& sm, uint32_t cnt, uint32_t k
   return ((uint64_t)(s.above + s.take) << 32) | Ln;
 }
 
+// Where the candidates of a speculative stream lie, in ord_key terms: every
+// one at or above lo (they passed the bound), the largest usually at most hi
+// (the sample's largest key), so the final selection can skip its key range.
+struct Hint {
+  uint32_t lo, hi;
+  bool on;
+};
+
+// The hint of a stream from bound L (a raw_key, > 0) and the sample's largest
+// raw key top.
+__device__ __forceinline__ Hint stream_hint(uint32_t L, uint32_t top) {
+  Hint h;
+  h.lo = ord_key(__float_as_uint(accept_floor(L)));
+  h.hi = ord_key(key_bits(top));
+  h.hi = h.hi > h.lo ? h.hi : h.lo;
+  h.on = true;
+  return h;
+}
+
 // The K best of the buffer, written to out in index order as ibase + index.
 // Inline, so that loads issued before it (the next row's first tiles) stay
-// in flight.
+// in flight.  With a hint the first pass spans [hint.lo, hint.hi] with an
+// open top instead of the entries' exact key range, saving a reduction and
+// its barrier.
 template <int LAY>
 __device__ __forceinline__ void final_select(Smem<LAY>& sm, const Slice& sl, uint32_t K, int32_t* out,
-                                             uint32_t ibase, float* vout = nullptr) {
+                                             uint32_t ibase, float* vout = nullptr, Hint hint = Hint{0u, 0u, false}) {
   constexpr int S = Shape<LAY>::kSlots;
   K = uni(K);
   uint32_t k[S];
   load_keys<LAY>(sm, k, sl);
   uint32_t lo, hi;
-  key_range<LAY, S>(sm, k, sl, lo, hi);
-  const Sel s = range_select<LAY, S>(sm, k, sl, lo, hi, K, 0u);
+  if (hint.on) {
+    lo = uni(hint.lo);
+    hi = uni(hint.hi);
+  } else {
+    key_range<LAY, S>(sm, k, sl, lo, hi);
+  }
+  const Sel s = range_select<LAY, S>(sm, k, sl, lo, hi, K, 0u, hint.on);
   emit_chosen<LAY, kToOut>(sm, k, sl, s, 0u, 0u, out, K, ibase, vout);
 }
 
@@ -1114,9 +1160,10 @@ __device__ __forceinline__ uint32_t spec_rank(uint32_t K, uint32_t M, uint32_t n
 // row again without it if not; when the check passes, every element below
 // the bound is beaten by at least K others.  Runs on register-held keys
 // while the next tiles' loads are in flight.  Leaves the histograms zero.
+// With top, also gives the sample's largest raw_key (uniform).
 template <int LAY>
 __device__ __forceinline__ uint32_t spec_bound(Smem<LAY>& sm, float (&x0)[kElems], float (&x1)[kElems], uint32_t n,
-                                               uint32_t K) {
+                                               uint32_t K, uint32_t* top = nullptr) {
   constexpr uint32_t M = 2u * (uint32_t)Shape<LAY>::kTile;
   uint32_t r = spec_rank(K, M, n);
   const bool one = r >= K;
@@ -1139,6 +1186,7 @@ __device__ __forceinline__ uint32_t spec_bound(Smem<LAY>& sm, float (&x0)[kElems
   uint32_t lo, hi;
   sample_range<LAY>(sm, k, sl.nv, r, lo, hi);
   const Sel s = range_select<LAY, 2 * kElems>(sm, k, sl, lo, hi, r, r + r / 8u + 8u);
+  if (top != nullptr) *top = hi;
 #pragma unroll
   for (int e = 0; e < kElems; ++e) {
     x0[e] = __uint_as_float(key_bits(k[e]));
@@ -1341,20 +1389,36 @@ __device__ __forceinline__ void wave_tile(Smem<LAY>& sm, const float (&x)[kElems
 #pragma unroll
     for (int c = 0; c < VEC; ++c) r = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[u * VEC + c] >> 32),
                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)bal[u * VEC + c], r));
+    if constexpr (Smem<LAY>::kDiscard != 0) {
+      // Wide workgroups: every lane stores every element, the ones it does
+      // not keep to its own discard word.  Positions are kept as byte
+      // offsets, which both arrays share (32-bit entries), so an element
+      // costs a select, its index, one paired store and the running add.
+      static_assert(sizeof(typename Shape<LAY>::Idx) == 4, "wide layouts keep 32-bit indices");
+      uint32_t rb = r * 4u;
+      const uint32_t db = ((uint32_t)Shape<LAY>::kCap + (threadIdx.x & 63)) * 4u;
 #pragma unroll
-    for (int c = 0; c < VEC; ++c) {
-      const int e = u * VEC + c;
-      const uint32_t pos = pbase + (uint32_t)u * (64u * VEC) + c;
-      const bool take = (FULL || pos < end) && x[e] >= bf;
-      if constexpr (Smem<LAY>::kDiscard != 0) {
-        const uint32_t dst = take ? r : (uint32_t)Shape<LAY>::kCap + (threadIdx.x & 63);
-        sm.val[dst] = __float_as_uint(x[e]);
-        sm.idx[dst] = (typename Shape<LAY>::Idx)pos;
-      } else if (take) {
-        sm.val[r] = __float_as_uint(x[e]);
-        sm.idx[r] = (typename Shape<LAY>::Idx)pos;
+      for (int c = 0; c < VEC; ++c) {
+        const int e = u * VEC + c;
+        const uint32_t pos = pbase + (uint32_t)u * (64u * VEC) + c;
+        const bool take = (FULL || pos < end) && x[e] >= bf;
+        const uint32_t d = take ? rb : db;
+        *reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(sm.val) + d) = __float_as_uint(x[e]);
+        *reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(sm.idx) + d) = pos;
+        rb += take ? 4u : 0u;
       }
-      r += take ? 1u : 0u;
+    } else {
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) {
+        const int e = u * VEC + c;
+        const uint32_t pos = pbase + (uint32_t)u * (64u * VEC) + c;
+        const bool take = (FULL || pos < end) && x[e] >= bf;
+        if (take) {
+          sm.val[r] = __float_as_uint(x[e]);
+          sm.idx[r] = (typename Shape<LAY>::Idx)pos;
+        }
+        r += take ? 1u : 0u;
+      }
     }
 #pragma unroll
     for (int c = 0; c < VEC; ++c) r0 += popc64(bal[u * VEC + c]);
@@ -1399,11 +1463,12 @@ __device__ __forceinline__ bool wave_counts(Smem<LAY>& sm, uint32_t w, uint32_t 
 // (already loaded when preloaded); together they sample 2 * kTile elements
 // from the W segments for the speculative bound.  Returns false if the row must
 // be streamed again on the general path; otherwise mine is this
-// wavefront's number of candidates (in slots [w * SUB, w * SUB + mine)).
+// wavefront's number of candidates (in slots [w * SUB, w * SUB + mine)) and
+// hint says where their keys lie.
 template <int LAY, int VEC, typename T>
 __device__ __forceinline__ bool stream_row_waves(Smem<LAY>& sm, const T* __restrict__ rowp, uint32_t n,
                                                  uint32_t K, float (&x0)[kElems], float (&x1)[kElems],
-                                                 bool preloaded, uint32_t& mine) {
+                                                 bool preloaded, uint32_t& mine, Hint& hint) {
   constexpr int PF = kPrefetch;
   constexpr uint32_t WT = kWaveTile;
   constexpr int W = Shape<LAY>::kWaves;
@@ -1427,7 +1492,9 @@ __device__ __forceinline__ bool stream_row_waves(Smem<LAY>& sm, const T* __restr
     load_wave_full<VEC>(qp + (2u + (uint32_t)s < F ? 2u + (uint32_t)s : F - 1) * WT, buf[s]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  const uint32_t L = uni(spec_bound<LAY>(sm, x0, x1, n, K));
+  uint32_t top = 0u;
+  const uint32_t L = uni(spec_bound<LAY>(sm, x0, x1, n, K, &top));
+  hint = stream_hint(L, uni(top));
   const float bf = accept_floor(L);
   const uint32_t sub0 = w * SUB;
   uint32_t cnt = 0;
@@ -1494,11 +1561,12 @@ __device__ __forceinline__ void ws_add(uint32_t* p, uint32_t v) {
 // unless preloaded).  Returns false if a wavefront's part of the buffer
 // overflowed; otherwise mine / off are this wavefront's candidate count and
 // its offset among the chunk's total (in slots [w * SUB, w * SUB + mine)).
+// hint says where the keys of the row's candidates lie.
 template <int LAY, int VEC, typename T>
 __device__ __forceinline__ bool stream_range_waves(Smem<LAY>& sm, const T* __restrict__ rowp, uint32_t n,
                                                    uint32_t K, uint32_t c0, uint32_t c1, float (&x0)[kElems],
                                                    float (&x1)[kElems], bool preloaded, uint32_t& mine,
-                                                   uint32_t& off, uint32_t& total, uint32_t& L) {
+                                                   uint32_t& off, uint32_t& total, uint32_t& L, Hint& hint) {
   constexpr int PF = kPrefetch;
   constexpr uint32_t WT = kWaveTile;
   constexpr int W = Shape<LAY>::kWaves;
@@ -1528,7 +1596,9 @@ __device__ __forceinline__ bool stream_range_waves(Smem<LAY>& sm, const T* __res
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  L = uni(spec_bound<LAY>(sm, x0, x1, n, K));
+  uint32_t top = 0u;
+  L = uni(spec_bound<LAY>(sm, x0, x1, n, K, &top));
+  hint = stream_hint(L, uni(top));
   const float bf = accept_floor(L);
   const uint32_t sub0 = w * SUB;
   uint32_t cnt = 0;
@@ -1653,6 +1723,7 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
     int32_t* out = p.out + (int64_t)row * p.K;
     uint32_t cnt = 0;
     bool waved = false;  // the candidates sit wave by wave
+    Hint hint{0u, 0u, false};
     bool select = false;
     if (n <= (int64_t)K) {
       if constexpr (VALS)
@@ -1663,7 +1734,7 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
       const T* rowp = row_of<T>(p, row);
       uint32_t gL = 0;  // general path: starting bound
       if (!redo && wave_mode<LAY>((uint32_t)n, K)) {
-        waved = stream_row_waves<LAY, VEC>(sm, rowp, (uint32_t)n, K, x0, x1, have_pre, cnt);
+        waved = stream_row_waves<LAY, VEC>(sm, rowp, (uint32_t)n, K, x0, x1, have_pre, cnt, hint);
         have_pre = false;
         if (!waved) {
           // A wavefront's part of the buffer overflowed, or fewer than K
@@ -1716,8 +1787,11 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
       have_pre = true;
     }
     if (select) {
+      // The hint only for the wide workgroups: the 256-thread instances are
+      // held to 128 VGPRs, and carrying it spills there.
       final_select<LAY>(sm, waved ? wave_slice<LAY>(cnt) : plain_slice<LAY>(cnt), K, out, off,
-                        VALS ? p.out_val + (int64_t)row * p.K : nullptr);
+                        VALS ? p.out_val + (int64_t)row * p.K : nullptr,
+                        W > 4 ? hint : Hint{0u, 0u, false});
     }
     first_row = false;
     drawn = false;
@@ -1994,8 +2068,9 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
     constexpr uint32_t SUB = (uint32_t)CAP / Shape<LAY>::kWaves;
     uint32_t mine = 0, woff = 0, total = 0, Lr = 0;
     float x0[kElems], x1[kElems];
+    Hint hint{0u, 0u, false};
     const bool ok = stream_range_waves<LAY, VEC>(sm, rowp, (uint32_t)n, K, (uint32_t)c0, (uint32_t)c1, x0, x1, false,
-                                                mine, woff, total, Lr);
+                                                mine, woff, total, Lr, hint);
     const bool pub = ok && Lr != 0u && total <= PUB;
     if (pub) {
       const uint32_t lane = t & 63, s0 = ((uint32_t)t >> 6) * SUB;
@@ -2038,7 +2113,7 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
       uint32_t old = 0u;
       if (t == 0) old = __hip_atomic_fetch_add(exit_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (last) {
-        final_select<LAY>(sm, plain_slice<LAY>(sum), K, out, offset_of(p, row), vout);
+        final_select<LAY>(sm, plain_slice<LAY>(sum), K, out, offset_of(p, row), vout, hint);
         // The gatherer was the lists' only reader: it zeroes them.
         clear_union<NT>(lists, (uint32_t)CAP, PUB, s_off, grow);
       }
