@@ -210,3 +210,53 @@ def test_graph_replay_wide():
             if ws is not None:
                 assert int(ws.count_nonzero().item()) == 0, f"workspace not clean after replay {rep} {c}"
     del g
+
+
+def _above_sample_rows(seed: int, rows: int, stride: int, K: int, levels: bool) -> tuple[np.ndarray, np.ndarray]:
+    """Rows whose K best all lie outside the speculative sample and above its
+    largest value: N(0, 1) everywhere, plus K + K // 2 values of 100 or more
+    at random positions p with p mod 4096 >= 2048.  The sample is at most the
+    first 1024 elements of each wave segment, and segments start at multiples
+    of 4096 in these rows, so it holds none of them; the final selection's
+    first pass then finds the K-th best in its open top bin.  With levels the
+    large values take 11 distinct values (ties at the threshold)."""
+    rng = np.random.default_rng(seed)
+    s = rng.standard_normal((rows, stride), dtype=np.float32)
+    pos = np.nonzero(np.arange(stride) % 4096 >= 2048)[0]
+    m = K + K // 2
+    for r in range(rows):
+        p = rng.choice(pos, size=m, replace=False)
+        if levels:
+            s[r, p] = np.float32(100.0) + rng.integers(0, 11, size=m).astype(np.float32)
+        else:
+            s[r, p] = np.float32(100.0) + rng.random(m, dtype=np.float32) * np.float32(50.0)
+    return s, np.full(rows, stride, np.int32)
+
+
+@pytest.mark.parametrize("levels", [False, True])
+@pytest.mark.parametrize("block", BLOCKS)
+def test_threshold_above_sample(block, levels):
+    """The final selection of a row streamed wave by wave starts from the
+    bound and the sample's largest key, with keys above that in its top bin:
+    rows whose threshold lies in that bin, one workgroup per row."""
+    s, L = _above_sample_rows(300 + block + int(levels), 6, 65536, 2048, levels)
+    for K in (1000, 2048):
+        exp = topk_ragged_oracle(s, L, K)
+        got, plan = run_gpu(s, L, K, tag=f"above sample K={K} block={block} levels={levels}", force_path=1,
+                            force_block=block)
+        assert plan["path"] == rrt.PATH_SINGLE and plan["block"] == block
+        assert_same(got, exp, f"above sample K={K} block={block} levels={levels}")
+
+
+@pytest.mark.parametrize("levels", [False, True])
+def test_threshold_above_sample_cooperative(levels):
+    """The same on the cooperative path (rows of 131072, 8 or 16 workgroups
+    per row): the union's selection starts from the shared bound and the
+    shared sample's largest key."""
+    s, L = _above_sample_rows(400 + int(levels), 4, 131072, 2048, levels)
+    for K, G in ((1024, 8), (2048, 16)):
+        exp = topk_ragged_oracle(s, L, K)
+        got, plan = run_gpu(s, L, K, tag=f"above sample coop K={K} G={G} levels={levels}", force_path=2,
+                            force_wg_per_row=G, force_block=512)
+        assert plan["path"] == rrt.PATH_MULTI and plan["wg_per_row"] == G
+        assert_same(got, exp, f"above sample coop K={K} G={G} levels={levels}")
