@@ -194,6 +194,7 @@ struct __align__(16) Smem {
   uint32_t tile_cnt[2][kElems][Shape<LAY>::kWaves];
   uint32_t wsum[Shape<LAY>::kWaves];
   uint32_t acc[16];
+  uint32_t bnd[2 * Shape<LAY>::kWaves];  // per-wave bounds and sample maxima of a speculative sample
   // Target of histogram adds that count nothing: one word per lane, so the
   // lanes of one add never collide on it (never read).
   uint32_t sink[64];
@@ -1149,6 +1150,78 @@ __device__ __forceinline__ uint32_t spec_rank(uint32_t K, uint32_t M, uint32_t n
   return want > kSpecMinRank ? (uint32_t)want : kSpecMinRank;
 }
 
+// One wavefront's part of a speculative bound: a key t that at least rw of
+// its first nk sample keys per lane (k, all lanes) reach, and the largest of
+// those keys (both uniform).  Everything stays inside the wavefront, with no
+// workgroup barrier.  The interval starts at the smallest over lanes of each
+// lane's kk-th largest key (kk = ceil(rw / 64), at most 4; else the
+// smallest key) and ends at the largest; each pass histograms it into this
+// wavefront's own kBins / W bins of hist1 and narrows it to the bin holding
+// the rw-th best, until that bin may be taken whole (at most rw + rw / 8 + 8
+// keys from it up) or holds one key; t is then the bin's lowest key.  The
+// LDS serves one wavefront's instructions in order, so its reads see its
+// adds; the bins are zero again on return.
+template <int LAY>
+__device__ __forceinline__ uint32_t wave_sample_bound(Smem<LAY>& sm, const uint32_t (&k)[2 * kElems], uint32_t nk,
+                                                      uint32_t rw, uint32_t& wmax) {
+  constexpr int W = Shape<LAY>::kWaves;
+  constexpr int NB = kBins / W;
+  constexpr uint32_t BITS = NB == 512 ? 9u : 8u;
+  static_assert(NB == 512 || NB == 256, "four or eight wavefronts");
+  const uint32_t kk = (rw + 63u) / 64u;
+  uint32_t a, b;
+  if (kk == 1u) {
+    lane_top<1>(k, nk, a, b);
+  } else if (kk == 2u) {
+    lane_top<2>(k, nk, a, b);
+  } else if (kk <= 4u) {
+    lane_top<4>(k, nk, a, b);
+  } else {
+    a = 0xffffffffu;
+    b = 0u;
+#pragma unroll
+    for (int j = 0; j < 2 * kElems; ++j) {
+      if ((uint32_t)j < nk) {
+        a = min(a, k[j]);
+        b = max(b, k[j]);
+      }
+    }
+  }
+  uint32_t lo = uni(wave_min(a));
+  uint32_t hi = uni(wave_max(b));
+  wmax = hi;
+  uint32_t* const h = sm.hist1 + uni(tid() >> 6) * (uint32_t)NB;
+  uint32_t* const sink = &sm.sink[tid() & 63];
+  const uint32_t stop = rw + rw / 8u + 8u;
+  uint32_t krem = rw, above = 0u;
+  bool ok = true;
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const uint32_t range = hi - lo;
+    const uint32_t nbit = range != 0u ? 32u - (uint32_t)__builtin_clz(range) : 0u;
+    const uint32_t sh = nbit > BITS ? nbit - BITS : 0u;
+#pragma unroll
+    for (int j = 0; j < 2 * kElems; ++j) {
+      const uint32_t d = k[j] - lo;
+      const bool in = (uint32_t)j < nk && d <= range;
+      atomicAdd(in ? &h[d >> sh] : sink, 1u);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    const Found f = wave_find<NB>(h, krem);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    for (uint32_t i = tid() & 63u; i < (uint32_t)NB; i += 64u) h[i] = 0u;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    ok = ok && f.ok != 0u;
+    lo += f.bin << sh;
+    const uint32_t width = (1u << sh) - 1u;
+    hi = hi - lo > width ? lo + width : hi;
+    if (!ok || sh == 0u || above + f.above + f.in_bin <= stop) break;
+    above += f.above;
+    krem -= f.above;
+  }
+  return ok ? lo : 0u;
+}
+
 // The speculative bound for a row of n elements whose first two tiles are
 // in x0 and x1 (n >= kSpecMinLen): the key of (about) the r-th best of those
 // M = 2 * kTile elements (4096, 8192 or 16384 by workgroup width), r =
@@ -1161,7 +1234,16 @@ __device__ __forceinline__ uint32_t spec_rank(uint32_t K, uint32_t M, uint32_t n
 // the bound is beaten by at least K others.  Runs on register-held keys
 // while the next tiles' loads are in flight.  Leaves the histograms zero.
 // With top, also gives the sample's largest raw_key (uniform).
-template <int LAY>
+//
+// WAVES (a row streamed wave by wave by one 512-thread workgroup): each
+// wavefront takes a bound from its own part of the sample instead, with no
+// workgroup barrier but the one that combines them (a lone row's decode and
+// multi-token rows 13.6 -> 13.3 us and 15.0 -> 14.8 us on MI355X).  The
+// lowest of the per-wave bounds admits about a fifth more candidates than
+// the shared selection; where rows share a CU (256 threads: prefill-shaped
+// batch 190 -> 224 us) or rows have heavy ties (cooperative long rows
+// 18.0 -> 19.7 us) that cost more than the barriers it saves.
+template <int LAY, bool WAVES = false>
 __device__ __forceinline__ uint32_t spec_bound(Smem<LAY>& sm, float (&x0)[kElems], float (&x1)[kElems], uint32_t n,
                                                uint32_t K, uint32_t* top = nullptr) {
   constexpr uint32_t M = 2u * (uint32_t)Shape<LAY>::kTile;
@@ -1178,6 +1260,36 @@ __device__ __forceinline__ uint32_t spec_bound(Smem<LAY>& sm, float (&x0)[kElems
   for (int e = 0; e < kElems; ++e) {
     k[e] = raw_key(__float_as_uint(x0[e]));
     k[kElems + e] = raw_key(__float_as_uint(x1[e]));
+  }
+  if constexpr (WAVES && Shape<LAY>::kWaves == 8) {
+    // Every wavefront finds a bound on its own part of the sample, reached
+    // by ceil(r / W) of its keys; the row's bound is the lowest of them, so
+    // at least r sample keys reach it.  One barrier in all; each wavefront
+    // cleared its own bins.
+    constexpr int W = Shape<LAY>::kWaves;
+    uint32_t wmax = 0u;
+    const uint32_t t = wave_sample_bound<LAY>(sm, k, one ? kElems : 2u * kElems, (r + W - 1u) / W, wmax);
+#pragma unroll
+    for (int e = 0; e < kElems; ++e) {
+      x0[e] = __uint_as_float(key_bits(k[e]));
+      x1[e] = __uint_as_float(key_bits(k[kElems + e]));
+    }
+    const uint32_t w = tid() >> 6;
+    if ((tid() & 63) == 0) {
+      sm.bnd[w] = t;
+      sm.bnd[W + w] = wmax;
+    }
+    __syncthreads();
+    uint32_t l = 0xffffffffu, h = 0u;
+#pragma unroll
+    for (int q = 0; q < W / 4; ++q) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(&sm.bnd[4 * q]);
+      const u32x4 y = *reinterpret_cast<const u32x4*>(&sm.bnd[W + 4 * q]);
+      l = min(l, min(min(x.x, x.y), min(x.z, x.w)));
+      h = max(h, max(max(y.x, y.y), max(y.z, y.w)));
+    }
+    if (top != nullptr) *top = uni(h);
+    return uni(l);
   }
   Slice sl;  // the keys live only in registers: every lane holds 16 slots, 8 or 16 of them sample keys
   sl.ws = 0u;
@@ -1493,7 +1605,7 @@ __device__ __forceinline__ bool stream_row_waves(Smem<LAY>& sm, const T* __restr
     __builtin_amdgcn_sched_barrier(0);
   }
   uint32_t top = 0u;
-  const uint32_t L = uni(spec_bound<LAY>(sm, x0, x1, n, K, &top));
+  const uint32_t L = uni(spec_bound<LAY, true>(sm, x0, x1, n, K, &top));
   hint = stream_hint(L, uni(top));
   const float bf = accept_floor(L);
   const uint32_t sub0 = w * SUB;
