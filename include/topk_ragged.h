@@ -258,7 +258,8 @@ typedef struct {
   int32_t path;           /* topk_path */
   int32_t kmax;           /* largest K the kernel instance handles: 2048, or 4096 for the
                              large layout that K above 2048 takes */
-  int32_t vec;            /* elements per load: 4, 2 or 1 (fp32), 8 or 1 (bf16) */
+  int32_t vec;            /* elements per load: 4, 2 or 1 (fp32), 8 or 1 (bf16); fp32 rows on 512- or
+                             1024-thread workgroups load 1 unless force_vec says otherwise */
   int32_t block;          /* threads per workgroup: 256, or 512 / 1024 (8 or 16 wavefronts per row) */
   int32_t grid;           /* workgroups launched */
   int32_t wg_per_row;     /* G (1 on the single path) */
