@@ -195,6 +195,7 @@ struct __align__(16) Smem {
   uint32_t wsum[Shape<LAY>::kWaves];
   uint32_t acc[16];
   uint32_t bnd[2 * Shape<LAY>::kWaves];  // per-wave bounds and sample maxima of a speculative sample
+  uint32_t wcnt[2 * Shape<LAY>::kWaves]; // per-wave candidate counts and overflow flags of a stream
   // Target of histogram adds that count nothing: one word per lane, so the
   // lanes of one add never collide on it (never read).
   uint32_t sink[64];
@@ -1541,21 +1542,28 @@ __device__ __forceinline__ void wave_tile(Smem<LAY>& sm, const float (&x)[kElems
 // After a wave-by-wave stream: every wavefront's candidate count and overflow
 // flag are shared; returns whether any wavefront overflowed, with the sum of
 // the counts in all and the counts of lower wavefronts in before (all
-// wave-uniform).  Two barriers: sm.red is free again on return.
-template <int LAY>
+// wave-uniform).  pre() runs before the exchange's barrier, so what it
+// writes to LDS is shared by the same barrier.  One barrier: sm.wcnt is
+// written again only by the next row's stream, after the barriers between.
+struct NoPre {
+  __device__ void operator()() const {}
+};
+
+template <int LAY, typename Pre = NoPre>
 __device__ __forceinline__ bool wave_counts(Smem<LAY>& sm, uint32_t w, uint32_t cnt, bool ovf, uint32_t& all,
-                                            uint32_t& before) {
+                                            uint32_t& before, const Pre& pre = Pre{}) {
   constexpr int W = Shape<LAY>::kWaves;
   if ((threadIdx.x & 63) == 0) {
-    sm.red[w] = cnt;
-    sm.red[W + w] = ovf ? 1u : 0u;
+    sm.wcnt[w] = cnt;
+    sm.wcnt[W + w] = ovf ? 1u : 0u;
   }
+  pre();
   __syncthreads();
   uint32_t a = 0, b = 0, o = 0;
 #pragma unroll
   for (int q = 0; q < W / 4; ++q) {
-    const u32x4 c = *reinterpret_cast<const u32x4*>(&sm.red[4 * q]);
-    const u32x4 f = *reinterpret_cast<const u32x4*>(&sm.red[W + 4 * q]);
+    const u32x4 c = *reinterpret_cast<const u32x4*>(&sm.wcnt[4 * q]);
+    const u32x4 f = *reinterpret_cast<const u32x4*>(&sm.wcnt[W + 4 * q]);
     const uint32_t v[4] = {uni(c.x), uni(c.y), uni(c.z), uni(c.w)};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1566,7 +1574,6 @@ __device__ __forceinline__ bool wave_counts(Smem<LAY>& sm, uint32_t w, uint32_t 
   }
   all = a;
   before = b;
-  __syncthreads();  // every wave has read the counts before sm.red is reused
   return o != 0u;
 }
 
@@ -1576,11 +1583,12 @@ __device__ __forceinline__ bool wave_counts(Smem<LAY>& sm, uint32_t w, uint32_t 
 // from the W segments for the speculative bound.  Returns false if the row must
 // be streamed again on the general path; otherwise mine is this
 // wavefront's number of candidates (in slots [w * SUB, w * SUB + mine)) and
-// hint says where their keys lie.
-template <int LAY, int VEC, typename T>
+// hint says where their keys lie.  pre() runs before the closing exchange's
+// barrier (see wave_counts).
+template <int LAY, int VEC, typename T, typename Pre>
 __device__ __forceinline__ bool stream_row_waves(Smem<LAY>& sm, const T* __restrict__ rowp, uint32_t n,
                                                  uint32_t K, float (&x0)[kElems], float (&x1)[kElems],
-                                                 bool preloaded, uint32_t& mine, Hint& hint) {
+                                                 bool preloaded, uint32_t& mine, Hint& hint, const Pre& pre) {
   constexpr int PF = kPrefetch;
   constexpr uint32_t WT = kWaveTile;
   constexpr int W = Shape<LAY>::kWaves;
@@ -1636,7 +1644,7 @@ __device__ __forceinline__ bool stream_row_waves(Smem<LAY>& sm, const T* __restr
     wave_tile<LAY, VEC, false>(sm, x, pt, qe, bf, sub0, cnt, ovf);
   }
   uint32_t all = 0, before = 0;
-  const bool bad = wave_counts<LAY>(sm, w, cnt, ovf, all, before);
+  const bool bad = wave_counts<LAY>(sm, w, cnt, ovf, all, before, pre);
   mine = cnt;
   return !bad && all >= K;
 }
@@ -1830,11 +1838,25 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
   float x0[kElems], x1[kElems];
   int64_t n = row < U ? clamp_len(p, (int)row) : 0;
   uint32_t off = row < U ? uni(offset_of(p, (int)row)) : 0u;
+  // Thread 0 shares the next row, its length and offset through LDS.
+  auto publish_next = [&]() {
+    draw();
+    if (threadIdx.x == 0) {
+      uint32_t nn = 0u;
+      if (next < U) {
+        nn = (uint32_t)clamp_len(p, (int)next);
+        sm.acc[13] = offset_of(p, (int)next);
+      }
+      sm.acc[8] = next < U ? next : U;
+      sm.acc[9] = nn;
+    }
+  };
   while (row < U) {
     draw();
     int32_t* out = p.out + (int64_t)row * p.K;
     uint32_t cnt = 0;
     bool waved = false;  // the candidates sit wave by wave
+    bool shared = false;  // the next row went out with the stream's closing exchange
     Hint hint{0u, 0u, false};
     bool select = false;
     if (n <= (int64_t)K) {
@@ -1846,7 +1868,8 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
       const T* rowp = row_of<T>(p, row);
       uint32_t gL = 0;  // general path: starting bound
       if (!redo && wave_mode<LAY>((uint32_t)n, K)) {
-        waved = stream_row_waves<LAY, VEC>(sm, rowp, (uint32_t)n, K, x0, x1, have_pre, cnt, hint);
+        waved = stream_row_waves<LAY, VEC>(sm, rowp, (uint32_t)n, K, x0, x1, have_pre, cnt, hint, publish_next);
+        shared = true;
         have_pre = false;
         if (!waved) {
           // A wavefront's part of the buffer overflowed, or fewer than K
@@ -1870,17 +1893,10 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
       select = true;
       redo = 0u;
     }
-    draw();
-    if (threadIdx.x == 0) {
-      uint32_t nn = 0u;
-      if (next < U) {
-        nn = (uint32_t)clamp_len(p, (int)next);
-        sm.acc[13] = offset_of(p, (int)next);
-      }
-      sm.acc[8] = next < U ? next : U;
-      sm.acc[9] = nn;
+    if (!shared) {
+      publish_next();
+      __syncthreads();
     }
-    __syncthreads();
     const uint32_t nrow = uni(sm.acc[8]);
     const int64_t nn = (int64_t)uni(sm.acc[9]);
     const uint32_t noff = uni(sm.acc[13]);
