@@ -2146,10 +2146,15 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
   if (row >= p.num_rows) return;
   const uint32_t K = (uint32_t)p.K;
   const int64_t n = clamp_len(p, row);
+  // The row's offset is read here, beside its length, and kept uniform: read
+  // at the emit, its load would still be outstanding there, and the wait for
+  // it (for all vector memory operations) would then sit before every store
+  // of the output, each waiting for the previous one.
+  const uint32_t roff = uni(offset_of(p, row));
   int32_t* out = p.out + (int64_t)row * p.K;
   if (n <= (int64_t)K) {
     if (g == 0)
-      write_all_then_pad<NT, E>(out, n, p.K, offset_of(p, row),
+      write_all_then_pad<NT, E>(out, n, p.K, roff,
                             p.out_val != nullptr ? p.out_val + (int64_t)row * p.K : nullptr, row_of<E>(p, row));
     return;
   }
@@ -2241,7 +2246,7 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
       uint32_t old = 0u;
       if (t == 0) old = __hip_atomic_fetch_add(exit_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (last) {
-        final_select<LAY>(sm, plain_slice<LAY>(sum), K, out, offset_of(p, row), vout, hint);
+        final_select<LAY>(sm, plain_slice<LAY>(sum), K, out, roff, vout, hint);
         // The gatherer was the lists' only reader: it zeroes them.
         clear_union<NT>(lists, (uint32_t)CAP, PUB, s_off, grow);
       }
@@ -2475,7 +2480,7 @@ __global__ void __launch_bounds__(Shape<LAY>::kBlock, Shape<LAY>::kWavesPerSimd)
   s.in_bin = 0u;
   s.ok = ok;
   s.all_in = false;
-  emit_chosen<LAY, kToOut>(sm, k, sl, s, gt_base, eq_base, out, K, (uint32_t)c0 + offset_of(p, row), vout);
+  emit_chosen<LAY, kToOut>(sm, k, sl, s, gt_base, eq_base, out, K, (uint32_t)c0 + roff, vout);
 }
 
 }  // namespace rrt
