@@ -1091,28 +1091,53 @@ __device__ __forceinline__ void lane_top(const uint32_t (&k)[2 * kElems], uint32
   top = t[0];
 }
 
+// The q-th largest of the wavefront's 64 values v (uniform; 1 <= q <= 64):
+// the largest t that at least q lanes reach, found bit by bit from the top
+// with one ballot per bit.  Used for q up to kKthLanes only: nearer to 64
+// it is little above the smallest value and its 32 steps do not pay
+// (decode and multi-token rows, q = 48: 13.0 -> 13.3 and 14.6 -> 15.3 us).
+constexpr uint32_t kKthLanes = 32;
+__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t v, uint32_t q) {
+  uint32_t t = 0u;
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = t | (1u << b);
+    t = popc64(ballot(v >= c)) >= q ? c : t;
+  }
+  return t;
+}
+
 // The interval the speculative bound's selection starts from (both ends
 // uniform), over the first nk keys of every lane (all of them sample keys,
-// so kk <= nk below).  hi is the largest sample key.  lo is a key that at least r
-// sample keys reach, found without a selection: with kk = ceil(r / threads)
-// at most 4, the smallest over lanes of each lane's kk-th largest key (every
-// lane holds kk keys at or above it, so the workgroup holds at least r);
-// otherwise the smallest sample key.  The r-th best key is therefore at
-// least lo.  Keys below lo go to the sink, so the first pass spends its bins
-// on the upper part of the sample, where the r-th best lies, and the dense
-// middle of the sample does not crowd a few bins.  Contains one barrier.
+// so kk <= nk below).  hi is the largest sample key.  lo is a key that at
+// least r sample keys reach, found without a selection.  Every lane takes
+// its kk-th largest key a (kk = ceil(r / threads) at most 4; else its
+// smallest key, kk = nk): it holds kk keys at or above a.  Every wavefront
+// then takes the q-th largest a over its lanes, q = ceil(r / (W kk)) (the
+// smallest when q > kKthLanes), and lo is the smallest of those: each wavefront holds
+// q lanes with kk keys at or above it, W q kk >= r in all.  The r-th best
+// key is therefore at least lo.  Keys below lo go to the sink, so the first
+// pass spends its bins on the upper part of the sample, where the r-th best
+// lies; taking the q-th largest lane instead of the smallest keeps the
+// lanes whose keys happen to be low from widening the interval (an N(0, 1)
+// sample at r = 192 keeps about 4% of its keys inside instead of 38%, and a
+// quantised one no longer crowds its adds onto a few levels).  Contains one
+// barrier.
 template <int LAY>
 __device__ __forceinline__ void sample_range(Smem<LAY>& sm, const uint32_t (&k)[2 * kElems], uint32_t nk,
                                              uint32_t r, uint32_t& lo, uint32_t& hi) {
   constexpr int W = Shape<LAY>::kWaves;
   const uint32_t kk = (r + (uint32_t)Shape<LAY>::kBlock - 1u) / (uint32_t)Shape<LAY>::kBlock;
-  uint32_t a, b;
+  uint32_t a, b, kq;
   if (kk == 1u) {
     lane_top<1>(k, nk, a, b);
+    kq = 1u;
   } else if (kk == 2u) {
     lane_top<2>(k, nk, a, b);
+    kq = 2u;
   } else if (kk <= 4u) {
     lane_top<4>(k, nk, a, b);  // kk = 3 takes the 4th largest: a lower key that qualifies too
+    kq = 4u;
   } else {
     a = 0xffffffffu;
     b = 0u;
@@ -1123,8 +1148,10 @@ __device__ __forceinline__ void sample_range(Smem<LAY>& sm, const uint32_t (&k)[
         b = max(b, k[j]);
       }
     }
+    kq = nk;
   }
-  const uint32_t mn = wave_min(a);
+  const uint32_t q = (r + (uint32_t)W * kq - 1u) / ((uint32_t)W * kq);
+  const uint32_t mn = q > kKthLanes ? wave_min(a) : wave_kth_largest(a, q);
   const uint32_t mx = wave_max(b);
   const int w = tid() >> 6;
   if ((tid() & 63) == 0) {
@@ -1154,9 +1181,10 @@ __device__ __forceinline__ uint32_t spec_rank(uint32_t K, uint32_t M, uint32_t n
 // One wavefront's part of a speculative bound: a key t that at least rw of
 // its first nk sample keys per lane (k, all lanes) reach, and the largest of
 // those keys (both uniform).  Everything stays inside the wavefront, with no
-// workgroup barrier.  The interval starts at the smallest over lanes of each
-// lane's kk-th largest key (kk = ceil(rw / 64), at most 4; else the
-// smallest key) and ends at the largest; each pass histograms it into this
+// workgroup barrier.  The interval starts at the q-th largest over lanes of
+// each lane's kk-th largest key (kk = ceil(rw / 64), at most 4; else the
+// smallest key, kk = nk; q = ceil(rw / kk)) and ends at the largest key;
+// each pass histograms it into this
 // wavefront's own kBins / W bins of hist1 and narrows it to the bin holding
 // the rw-th best, until that bin may be taken whole (at most rw + rw / 8 + 8
 // keys from it up) or holds one key; t is then the bin's lowest key.  The
@@ -1170,13 +1198,16 @@ __device__ __forceinline__ uint32_t wave_sample_bound(Smem<LAY>& sm, const uint3
   constexpr uint32_t BITS = NB == 512 ? 9u : 8u;
   static_assert(NB == 512 || NB == 256, "four or eight wavefronts");
   const uint32_t kk = (rw + 63u) / 64u;
-  uint32_t a, b;
+  uint32_t a, b, kq;
   if (kk == 1u) {
     lane_top<1>(k, nk, a, b);
+    kq = 1u;
   } else if (kk == 2u) {
     lane_top<2>(k, nk, a, b);
+    kq = 2u;
   } else if (kk <= 4u) {
     lane_top<4>(k, nk, a, b);
+    kq = 4u;
   } else {
     a = 0xffffffffu;
     b = 0u;
@@ -1187,8 +1218,11 @@ __device__ __forceinline__ uint32_t wave_sample_bound(Smem<LAY>& sm, const uint3
         b = max(b, k[j]);
       }
     }
+    kq = nk;
   }
-  uint32_t lo = uni(wave_min(a));
+  // q lanes holding kq keys each at or above lo: q kq >= rw.
+  const uint32_t q = (rw + kq - 1u) / kq;
+  uint32_t lo = uni(q > kKthLanes ? wave_min(a) : wave_kth_largest(a, q));
   uint32_t hi = uni(wave_max(b));
   wmax = hi;
   uint32_t* const h = sm.hist1 + uni(tid() >> 6) * (uint32_t)NB;
