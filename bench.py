@@ -51,13 +51,42 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def code_of(text: str) -> str:
+    """C/C++ source without its comments and with runs of whitespace folded
+    to one space: what the compiler sees, so that editing a comment does not
+    invalidate a counter reading.  String and character literals are kept
+    as written."""
+    out = []
+    i, n = 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
-    """Hash of the kernel and launcher sources: a stored counter reading is
-    used only while this matches the hash it was taken with."""
+    """Hash of the kernel and launcher sources' code (comments stripped, see
+    code_of): a stored counter reading is used only while this matches the
+    hash it was taken with."""
     h = hashlib.sha256()
     for path in kernel_sources():
         h.update(os.path.basename(path).encode())
-        h.update(open(path, "rb").read())
+        h.update(code_of(open(path, encoding="utf-8").read()).encode())
     return h.hexdigest()
 
 

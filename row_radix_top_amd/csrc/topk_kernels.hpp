@@ -8,39 +8,44 @@
 // Design (not the pages' CUDA design, which is prior art):
 //
 // * Streaming filter.  A workgroup walks its row (or its chunk of a row) once,
-//   in 2048-element tiles of coalesced vector loads kept in flight by a
-//   register ring.  It keeps an index-ordered candidate buffer in LDS (fp32
-//   bits and indices) and a lower bound L on the key of the K-th best
-//   element seen so far; an element is appended only if its key is >= L,
-//   which costs one IEEE compare per element, and appending is two LDS
-//   stores.  When a tile would overflow the buffer, the buffer is compacted
-//   and L rises (see compact()).  Each score is read from HBM exactly once.
+//   in tiles of coalesced loads kept in flight by a register ring.  It keeps
+//   an index-ordered candidate buffer in LDS (fp32 bits and indices) and a
+//   lower bound L on the key of the K-th best element seen so far; an
+//   element is appended only if it reaches L, one IEEE compare per element,
+//   and its position comes from ballots and mbcnt ranks.  When a tile would
+//   overflow the buffer, the buffer is compacted and L rises (see compact()).
+//   Each score is read from HBM once.
 //
 // * Speculative bound.  On long rows the bound starts at (about) the key of
-//   the 1.5 K * 4096 / n-th best of a 4096-element sample, so only ~1.5 K
-//   elements reach the buffer; each wavefront then streams its own quarter
-//   of the row without per-tile barriers.  A row whose bound proves too high
-//   (fewer than K reached it) is streamed again without one.
+//   the ceil(1.5 K M / n)-th best of an M-element sample (the first two wave
+//   tiles of every wavefront's segment), so only ~1.5 K elements reach the
+//   buffer; each wavefront then streams its own segment of the row into its
+//   own part of the buffer, with no per-tile barrier.  A row whose bound
+//   proves too high (fewer than K reached it), or whose part of the buffer
+//   would overflow, is streamed again without one.
 //
-// * Range select.  Over the register-held buffer: passes histogram the keys
-//   of the current interval [lo, hi] (starting from their exact range) into
-//   2048 or 256 bins with LDS atomics.  Every wavefront scans a histogram
-//   from the top with DPP prefix sums and finds the threshold bin itself, so
-//   a search costs no barrier.  Ties at the final 32-bit key go to the lower
-//   buffer position, the lower index.
+// * Range select.  Over the register-held keys: passes histogram the keys of
+//   the current interval [lo, hi] into 2048 or 256 LDS bins, starting from
+//   the keys' exact range or, after a speculative stream, from [bound, the
+//   sample's largest key] with an open top bin.  Every wavefront scans a
+//   histogram from the top with DPP prefix sums and finds the threshold bin
+//   itself, so a search costs no barrier.  Ties at the final 32-bit key go
+//   to the lower buffer position, the lower index.
 //
-// * Ordered emit.  Each thread owns a contiguous slice of the buffer; one
-//   workgroup prefix sum of the per-thread (greater, equal) counts gives every
-//   chosen entry its output rank, so output is written in ascending index
-//   order with no sort.
+// * Ordered emit.  Each wavefront owns a contiguous, index-ordered part of
+//   the buffer; one exchange of per-wavefront counts gives every chosen
+//   entry its output rank by ballots, so output is written in ascending
+//   index order with no sort.
 //
-// * Multi-workgroup rows.  G workgroups each filter a contiguous chunk, then
-//   merge digit histograms in the workspace with agent-scope atomics across
-//   three cooperative rounds (an arrival-counter barrier each; all workspace
-//   traffic is atomic, so no cache-wide fences are needed), publish the
-//   few keys left undecided after 22 bits, and derive their output offsets
-//   from per-workgroup counts.  The last workgroup to leave zeroes everything
-//   the row touched, so the workspace is all-zero when the kernel ends (the
+// * Multi-workgroup rows.  G workgroups each stream a chunk of the row from
+//   the same speculative bound (the same sample, the same selection), publish
+//   the elements that reach it to the workspace and arrive once; the last to
+//   arrive gathers the union in chunk order and selects.  If the bound fails
+//   for the row, every workgroup falls back to three cooperative rounds that
+//   merge digit histograms in the workspace.  All workspace traffic is
+//   agent-scope atomic, ordered by waits and barriers, so no cache-wide
+//   fences are needed.  The last workgroup to leave zeroes everything the
+//   row touched, so the workspace is all-zero when the kernel ends (the
 //   in-kernel cleanup of the PR #41748 page, without the race its review
 //   describes: nothing is reset while another workgroup can still read it).
 //
