@@ -312,3 +312,17 @@ def test_ctypes_mirrors_match_the_header():
             fields.append((m.group(2), widths[m.group(1)] * int(m.group(3) or 1)))
         mirror = [(name, ctypes.sizeof(t)) for name, t in cls._fields_]
         assert mirror == fields, (cname, mirror, fields)
+
+
+def test_counter_hash_ignores_comments_only():
+    """The key of a stored counter reading follows the sources' code: a
+    comment or whitespace edit keeps it, any code edit changes it, and
+    comment markers inside string literals are code."""
+    import bench
+    a = 'int x = 1; // one\n/* two\n   lines */ const char* s = "a // b /* c */";\n'
+    b = 'int x = 1;   /* other words */\nconst char* s = "a // b /* c */"; // trailing\n'
+    c = 'int x = 2; const char* s = "a // b /* c */";'
+    assert bench.code_of(a) == bench.code_of(b) == 'int x = 1; const char* s = "a // b /* c */";'
+    assert bench.code_of(c) != bench.code_of(a)
+    assert bench.code_of("char q = '\\''; // x") == "char q = '\\'';"
+    assert len(bench.kernel_source_hash()) == 64
