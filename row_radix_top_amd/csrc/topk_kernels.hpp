@@ -169,9 +169,10 @@ struct Shape {
   // where they let a fourth workgroup share the CU.  The wide layouts keep 32
   // bits: the value and the index of a kept element then go out as one
   // paired store (the two arrays sit a multiple of 256 bytes apart), where a
-  // 16-bit index costs a second store and its own address arithmetic, and
-  // their streaming loop is bound by instruction issue (multi-token rows
-  // 16.2 -> 15.3 us, decode 14.0 -> 13.7 us, measured on MI355X).
+  // 16-bit index costs a second store and its own address arithmetic, on a
+  // streaming loop that a lone workgroup runs as fast as it can issue it
+  // (multi-token rows 16.2 -> 15.3 us, decode 14.0 -> 13.7 us, measured on
+  // MI355X).
   using Idx = typename std::conditional<kIdx16 && kWaves == 4, uint16_t, uint32_t>::type;
   static_assert(kCap % kBlock == 0 && kSlots % 4 == 0, "capacity must tile the workgroup in aligned runs");
   static_assert(kCap % (kWaves * 64) == 0 && kCap / kWaves <= 64 * kSlots, "a wavefront's part fits its slices");
