@@ -326,3 +326,26 @@ def test_counter_hash_ignores_comments_only():
     assert bench.code_of(c) != bench.code_of(a)
     assert bench.code_of("char q = '\\''; // x") == "char q = '\\'';"
     assert len(bench.kernel_source_hash()) == 64
+
+
+def test_wide_plans_load_one_element_per_lane():
+    """fp32 rows on 512- (or 1024-) thread workgroups load one element per
+    lane unless a width is forced; 256-thread plans keep the widest load the
+    alignment allows, and bf16 plans keep theirs."""
+    w512 = (2, 2, 2, 2)
+    # 64 rows fitting the CUs at the 512-thread occupancy, long enough to go wave by wave.
+    p = rrt.plan_for_props(256, 4, 4, 64, 32768, 2048, occupancy_w512=w512)
+    assert p["block"] == 512 and p["vec"] == 1
+    p = rrt.plan_for_props(256, 4, 4, 64, 32768, 2048, occupancy_w512=w512, force_vec=4)
+    assert p["block"] == 512 and p["vec"] == 4
+    p = rrt.plan_for_props(256, 4, 4, 64, 32768, 2048, vec_allowed=2, occupancy_w512=w512, force_vec=2)
+    assert p["vec"] == 2
+    # Cooperative long rows on 512 threads.
+    p = rrt.plan_for_props(256, 3, 3, 16, 131072, 2048, occupancy_w512=w512)
+    assert p["path"] == rrt.PATH_MULTI and p["block"] == 512 and p["vec"] == 1
+    # A batch that fills the GPU stays on 256 threads and wide loads.
+    p = rrt.plan_for_props(256, 4, 4, 4096, 65536, 2048, occupancy_w512=w512)
+    assert p["block"] == 256 and p["vec"] == 4
+    # bf16 (8-element loads allowed) keeps its width on wide workgroups.
+    p = rrt.plan_for_props(256, 4, 4, 64, 32768, 2048, vec_allowed=8, occupancy_w512=w512)
+    assert p["block"] == 512 and p["vec"] == 8
