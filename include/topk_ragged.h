@@ -231,8 +231,10 @@ const char* topk_ragged_last_error(void);
 /* Device facts the planner uses.  occupancy_* are workgroups per CU of the
  * exact kernel instance that would run (PR #41189 page, implementation
  * notes: query the instance actually launched, not a sibling).  The "16"
- * instances keep 16-bit candidate indices (rows or chunks of at most 65536
- * elements) and a larger candidate buffer. */
+ * instances serve rows or chunks of at most 65536 elements: at 256 threads
+ * they keep 16-bit candidate indices, at 512 and 1024 threads 32-bit ones in
+ * a larger candidate buffer (one workgroup per CU at 512 threads below the
+ * large K). */
 typedef struct {
   int32_t num_cus;
   int32_t occupancy_single;    /* one workgroup per row kernel, 32-bit indices */
@@ -268,7 +270,8 @@ typedef struct {
   int32_t headroom;       /* slots left free when workgroups wait on each other */
   int32_t lds_bytes;      /* static LDS per workgroup */
   int32_t fell_back;      /* 1 if a requested multi plan could not be made co-resident */
-  int32_t idx16;          /* 1 if the instance keeps 16-bit candidate indices */
+  int32_t idx16;          /* 1 if the instance serves rows or chunks of at most 65536 elements (16-bit
+                             candidate indices at 256 threads) */
   uint64_t workspace_bytes;
 } topk_plan;
 
